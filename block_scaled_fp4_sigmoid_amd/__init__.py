@@ -1,0 +1,329 @@
+"""Python binding of the MI355X NVFP4 / FP8_DYNAMIC routed-expert MoE library.
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libbsmoe.so`` (C ABI declared in ``include/bsmoe.h``).  Tensors are torch
+CUDA tensors (device memory on the MI355X); work is enqueued on torch's current
+stream.  There is no CPU fallback: if the library is missing or no GPU is
+visible, calls raise.
+
+Exported names follow the C ABI: ``nvfp4_quantize``, ``nvfp4_dequantize``,
+``fp8_quantize``, ``route``, ``moe_expert_mlp`` (plus ``rmsnorm``,
+``scaled_residual_``, and the convenience ``quantize_expert_weights`` and
+``moe_layer`` built from those calls).
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsmoe.so")
+
+BSM_OK = 0
+BSM_BF16, BSM_F32 = 1, 2
+FMT_NVFP4, FMT_FP8 = 1, 2
+GS_DYNAMIC, GS_STATIC = 0, 1
+
+_lib = None
+
+
+class BsmError(RuntimeError):
+    pass
+
+
+class _MoeWeights(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int), ("E", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
+                ("w13_codes", ctypes.c_void_p), ("w13_scales", ctypes.c_void_p), ("w13_gs", ctypes.c_void_p),
+                ("w2_codes", ctypes.c_void_p), ("w2_scales", ctypes.c_void_p), ("w2_gs", ctypes.c_void_p)]
+
+
+class _ActQ(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p)]
+
+
+class _WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("total", "counts", "offsets", "row_pair", "pair_row", "tiles", "h_f32",
+                                                "h_codes", "h_scales", "h_gs", "y_f32", "scratch")]
+
+
+def load():
+    """Load ``libbsmoe.so`` (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise BsmError(f"HIP library not built: {LIB_PATH} missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, sz, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "bsm_abi_version": (i32, []),
+        "bsm_status_str": (ctypes.c_char_p, [i32]),
+        "bsm_last_error": (ctypes.c_char_p, []),
+        "bsm_nvfp4_quantize_workspace_size": (sz, [i64, i64, i64]),
+        "bsm_nvfp4_quantize": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32, vp, sz, vp]),
+        "bsm_nvfp4_dequantize": (i32, [vp, vp, vp, i64, i64, i64, vp, vp]),
+        "bsm_fp8_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
+        "bsm_route_workspace_size": (sz, [i64, i64, i64]),
+        "bsm_route": (i32, [vp, i32, i64, i64, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "bsm_route_diagnostics": (i32, [vp, i64, i64, i64, vp, vp]),
+        "bsm_moe_workspace_size": (sz, [i32, i64, i64, i64, i64, i32]),
+        "bsm_moe_workspace_layout": (i32, [i32, i64, i64, i64, i64, i32, ctypes.POINTER(_WsLayout)]),
+        "bsm_moe_expert_mlp": (i32, [ctypes.POINTER(_MoeWeights), ctypes.POINTER(_ActQ), i64, vp, vp, i32, f32, i32,
+                                     vp, vp, vp, sz, vp]),
+        "bsm_rmsnorm_f32": (i32, [vp, i64, i64, f32, vp, vp]),
+        "bsm_scaled_residual_f32": (i32, [vp, vp, f32, f32, i64, i64, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != BSM_OK:
+        lib = load()
+        raise BsmError(f"{lib.bsm_status_str(status).decode()}: {lib.bsm_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BSM_BF16
+    if t.dtype == torch.float32:
+        return BSM_F32
+    raise BsmError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise BsmError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise BsmError(f"{name} must be contiguous")
+    return t
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# quantizers
+# ---------------------------------------------------------------------------
+
+
+def nvfp4_quantize(x: torch.Tensor, global_scale: Optional[torch.Tensor] = None):
+    """NVFP4 of B tensors x[B, R, C] (or one tensor [R, C]).
+
+    Returns (codes uint8 [..., R, C/2], scales uint8 [..., R, C/16], global_scale f32 [B]).
+    ``global_scale`` given (f32 [B] on the device) -> static mode.
+    """
+    lib = load()
+    _dev(x, "x")
+    squeeze = x.dim() == 2
+    x3 = x.unsqueeze(0) if squeeze else x
+    B, R, C = x3.shape
+    codes = torch.empty((B, R, C // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, R, C // 16), dtype=torch.uint8, device=x.device)
+    if global_scale is None:
+        gs = torch.empty(B, dtype=torch.float32, device=x.device)
+        mode = GS_DYNAMIC
+        ws = _ws(lib.bsm_nvfp4_quantize_workspace_size(B, R, C), x.device)
+    else:
+        gs = _dev(global_scale.reshape(-1).to(torch.float32), "global_scale")
+        mode = GS_STATIC
+        ws = None
+    _check(lib.bsm_nvfp4_quantize(_ptr(x3), _dtype_code(x), B, R, C, _ptr(codes), _ptr(scales), _ptr(gs), mode,
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    if squeeze:
+        return codes[0], scales[0], gs
+    return codes, scales, gs
+
+
+def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor):
+    """float32 values fl32(fl32(q * s_b) * S_g) of NVFP4 tensors."""
+    lib = load()
+    _dev(codes, "codes")
+    squeeze = codes.dim() == 2
+    c3 = codes.unsqueeze(0) if squeeze else codes
+    B, R, C2 = c3.shape
+    out = torch.empty((B, R, C2 * 2), dtype=torch.float32, device=codes.device)
+    _check(lib.bsm_nvfp4_dequantize(_ptr(c3), _ptr(_dev(scales, "scales")), _ptr(_dev(global_scale, "gs")), B, R,
+                                    C2 * 2, _ptr(out), _stream()))
+    return out[0] if squeeze else out
+
+
+def fp8_quantize(x: torch.Tensor):
+    """Per-row FP8 E4M3 quantization of x[R, C] -> (codes uint8 [R, C], scales f32 [R])."""
+    lib = load()
+    _dev(x, "x")
+    R, C = x.shape
+    codes = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(R, dtype=torch.float32, device=x.device)
+    _check(lib.bsm_fp8_quantize(_ptr(x), _dtype_code(x), R, C, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+
+
+def route(x, w_router, n_group, topk_group, topk, return_scores=False, return_workspace=False):
+    """Group-limited sigmoid routing -> (ids int32 [T, k], weights f32 [T, k][, scores f32 [T, E]])."""
+    lib = load()
+    _dev(x, "x")
+    _dev(w_router, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    ids = torch.empty((T, topk), dtype=torch.int32, device=x.device)
+    wts = torch.empty((T, topk), dtype=torch.float32, device=x.device)
+    scores = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_scores else None
+    ws = _ws(lib.bsm_route_workspace_size(T, H, E), x.device)
+    _check(lib.bsm_route(_ptr(x), _dtype_code(x), T, H, _ptr(w_router), _dtype_code(w_router), E, n_group, topk_group,
+                         topk, _ptr(ids), _ptr(wts), _ptr(scores), _ptr(ws), ws.numel(), _stream()))
+    out = [ids, wts]
+    if return_scores:
+        out.append(scores)
+    if return_workspace:
+        out.append(ws)
+    return tuple(out)
+
+
+def route_diagnostics(ws, T, H, E):
+    """[exact-fallback logits, double-double sigmoids, 0, 0] of the last route call using ``ws``."""
+    lib = load()
+    d = torch.zeros(4, dtype=torch.int32, device=ws.device)
+    _check(lib.bsm_route_diagnostics(_ptr(ws), T, H, E, _ptr(d), _stream()))
+    return d
+
+
+# ---------------------------------------------------------------------------
+# expert MLP
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class ExpertWeights:
+    """Quantized routed-expert weights in the library's canonical layout."""
+    format: int
+    E: int
+    H: int
+    I: int
+    w13_codes: torch.Tensor
+    w13_scales: torch.Tensor
+    w13_gs: Optional[torch.Tensor]
+    w2_codes: torch.Tensor
+    w2_scales: torch.Tensor
+    w2_gs: Optional[torch.Tensor]
+
+    def _struct(self):
+        return _MoeWeights(self.format, self.E, self.H, self.I, self.w13_codes.data_ptr(), self.w13_scales.data_ptr(),
+                           None if self.w13_gs is None else self.w13_gs.data_ptr(), self.w2_codes.data_ptr(),
+                           self.w2_scales.data_ptr(), None if self.w2_gs is None else self.w2_gs.data_ptr())
+
+
+def quantize_expert_weights(w13: torch.Tensor, w2: torch.Tensor, fmt: str) -> ExpertWeights:
+    """Offline RTN quantization of bf16 masters W13 [E, 2I, H] (gate rows then up rows) and W2 [E, H, I].
+
+    NVFP4: every expert's gate, up and down is its own tensor with its own global scale.
+    FP8: one scale per output channel (row).
+    """
+    E, I2, H = w13.shape
+    I = I2 // 2
+    if fmt == "nvfp4":
+        c13, s13, g13 = nvfp4_quantize(w13.reshape(2 * E, I, H))
+        c2, s2, g2 = nvfp4_quantize(w2)
+        return ExpertWeights(FMT_NVFP4, E, H, I, c13.reshape(E, 2 * I, H // 2), s13.reshape(E, 2 * I, H // 16),
+                             g13.reshape(E, 2), c2, s2, g2)
+    if fmt == "fp8":
+        c13, s13 = fp8_quantize(w13.reshape(E * 2 * I, H))
+        c2, s2 = fp8_quantize(w2.reshape(E * H, I))
+        return ExpertWeights(FMT_FP8, E, H, I, c13.reshape(E, 2 * I, H), s13.reshape(E, 2 * I), None,
+                             c2.reshape(E, H, I), s2.reshape(E, H), None)
+    raise BsmError(f"unknown format {fmt}")
+
+
+def quantize_activations(x: torch.Tensor, fmt: str):
+    """NVFP4 (codes, scales, gs[1]) or FP8 (codes, scales[T]) of the expert input."""
+    if fmt == "nvfp4":
+        return nvfp4_quantize(x)
+    return fp8_quantize(x)
+
+
+def moe_workspace_layout(fmt, E, H, I, T, topk):
+    lib = load()
+    lay = _WsLayout()
+    _check(lib.bsm_moe_workspace_layout(FMT_NVFP4 if fmt == "nvfp4" else FMT_FP8, E, H, I, T, topk,
+                                        ctypes.byref(lay)))
+    return {n: getattr(lay, n) for n, _ in _WsLayout._fields_}
+
+
+def moe_expert_mlp(weights: ExpertWeights, xq, ids, wts, combine_scale=2.5, h_global_scale=None, out=None, ws=None,
+                   return_workspace=False):
+    """Routed-expert MLP on quantized activations ``xq`` -> out f32 [T, H]."""
+    lib = load()
+    _dev(ids, "ids")
+    _dev(wts, "wts")
+    T, topk = ids.shape
+    fmt = weights.format
+    if fmt == FMT_NVFP4:
+        codes, scales, gs = xq
+        act = _ActQ(fmt, codes.data_ptr(), scales.data_ptr(), gs.data_ptr())
+    else:
+        codes, scales = xq
+        act = _ActQ(fmt, codes.data_ptr(), scales.data_ptr(), None)
+    if out is None:
+        out = torch.empty((T, weights.H), dtype=torch.float32, device=ids.device)
+    need = lib.bsm_moe_workspace_size(fmt, weights.E, weights.H, weights.I, T, topk)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, ids.device)
+    mode = GS_STATIC if h_global_scale is not None else GS_DYNAMIC
+    wstruct = weights._struct()
+    _check(lib.bsm_moe_expert_mlp(ctypes.byref(wstruct), ctypes.byref(act), T, _ptr(ids), _ptr(wts), topk,
+                                  float(combine_scale), mode, _ptr(h_global_scale), _ptr(out), _ptr(ws), ws.numel(),
+                                  _stream()))
+    return (out, ws) if return_workspace else out
+
+
+def moe_layer(x, w_router, weights: ExpertWeights, n_group, topk_group, topk, combine_scale=2.5):
+    """Route -> quantize activations -> expert MLP.  Returns (out, ids, wts)."""
+    ids, wts = route(x, w_router, n_group, topk_group, topk)
+    fmt = "nvfp4" if weights.format == FMT_NVFP4 else "fp8"
+    xq = quantize_activations(x, fmt)
+    out = moe_expert_mlp(weights, xq, ids, wts, combine_scale)
+    return out, ids, wts
+
+
+# ---------------------------------------------------------------------------
+# norm / residual
+# ---------------------------------------------------------------------------
+
+
+def rmsnorm(x: torch.Tensor, eps=1e-6):
+    lib = load()
+    _dev(x, "x")
+    y = torch.empty_like(x)
+    _check(lib.bsm_rmsnorm_f32(_ptr(x), x.shape[0], x.shape[1], float(eps), _ptr(y), _stream()))
+    return y
+
+
+def scaled_residual_(x: torch.Tensor, m: torch.Tensor, a: float, b: float):
+    """x <- fl32(a*x + b*m) in place."""
+    lib = load()
+    _dev(x, "x")
+    _dev(m, "m")
+    _check(lib.bsm_scaled_residual_f32(_ptr(x), _ptr(m), float(a), float(b), x.shape[0], x.shape[1], _stream()))
+    return x

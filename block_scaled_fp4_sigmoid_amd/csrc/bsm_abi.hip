@@ -1,0 +1,245 @@
+// bsm_abi.hip -- extern "C" entry points declared in include/bsmoe.h:
+// argument validation on the host, workspace sizing, kernel launches.
+// Every check runs before anything is enqueued; on error nothing is launched.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/bsmoe.h"
+#include "bsm_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return BSM_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BSM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool dtype_ok(int d) { return d == BSM_BF16 || d == BSM_F32; }
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return BSM_OK;
+  if (!ws) return fail(BSM_ERR_WORKSPACE, "workspace pointer is NULL (need %zu bytes)", need);
+  if (!aligned(ws, 256)) return fail(BSM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(BSM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return BSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsm_abi_version(void) { return BSM_ABI_VERSION; }
+
+const char* bsm_status_str(int s) {
+  switch (s) {
+    case BSM_OK: return "BSM_OK";
+    case BSM_ERR_INVALID_ARG: return "BSM_ERR_INVALID_ARG";
+    case BSM_ERR_UNSUPPORTED: return "BSM_ERR_UNSUPPORTED";
+    case BSM_ERR_WORKSPACE: return "BSM_ERR_WORKSPACE";
+    case BSM_ERR_HIP: return "BSM_ERR_HIP";
+    default: return "BSM_ERR_UNKNOWN";
+  }
+}
+
+const char* bsm_last_error(void) { return g_err; }
+
+size_t bsm_nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
+  if (B < 0 || R < 0 || C < 0) return 0;
+  return bsm::nvfp4_quant_ws(B, R, C);
+}
+
+int bsm_nvfp4_quantize(const void* x, int x_dtype, int64_t B, int64_t R, int64_t C, uint8_t* codes, uint8_t* scales,
+                       float* global_scale, int gs_mode, void* ws, size_t ws_bytes, bsm_stream_t stream) {
+  if (!dtype_ok(x_dtype)) return fail(BSM_ERR_INVALID_ARG, "x_dtype must be BSM_BF16 or BSM_F32");
+  if (B < 0 || R < 0 || C < 0) return fail(BSM_ERR_INVALID_ARG, "negative shape");
+  if (C % 16 != 0) return fail(BSM_ERR_INVALID_ARG, "C (%lld) must be a multiple of 16", (long long)C);
+  if (B > 65535) return fail(BSM_ERR_UNSUPPORTED, "B (%lld) > 65535", (long long)B);
+  if (gs_mode != BSM_GS_DYNAMIC && gs_mode != BSM_GS_STATIC) return fail(BSM_ERR_INVALID_ARG, "bad gs_mode");
+  if (B * R * C == 0) return ok();
+  if (!x || !codes || !scales || !global_scale) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(x, 32) || !aligned(codes, 8)) return fail(BSM_ERR_INVALID_ARG, "x must be 32-byte and codes 8-byte aligned");
+  const size_t need = gs_mode == BSM_GS_DYNAMIC ? bsm::nvfp4_quant_ws(B, R, C) : 0;
+  if (int r = check_ws(ws, ws_bytes, need)) return r;
+  return hip_status(bsm::launch_nvfp4_quantize(x, x_dtype == BSM_BF16, B, R, C, codes, scales, global_scale,
+                                               gs_mode == BSM_GS_DYNAMIC, (float*)ws, (hipStream_t)stream),
+                    "bsm_nvfp4_quantize");
+}
+
+int bsm_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale, int64_t B, int64_t R,
+                         int64_t C, float* out, bsm_stream_t stream) {
+  if (B < 0 || R < 0 || C < 0) return fail(BSM_ERR_INVALID_ARG, "negative shape");
+  if (C % 16 != 0) return fail(BSM_ERR_INVALID_ARG, "C (%lld) must be a multiple of 16", (long long)C);
+  if (B > 65535) return fail(BSM_ERR_UNSUPPORTED, "B (%lld) > 65535", (long long)B);
+  if (B * R * C == 0) return ok();
+  if (!codes || !scales || !global_scale || !out) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(codes, 8) || !aligned(out, 16)) return fail(BSM_ERR_INVALID_ARG, "codes 8-byte / out 16-byte alignment");
+  return hip_status(bsm::launch_nvfp4_dequantize(codes, scales, global_scale, B, R, C, out, (hipStream_t)stream),
+                    "bsm_nvfp4_dequantize");
+}
+
+int bsm_fp8_quantize(const void* x, int x_dtype, int64_t R, int64_t C, uint8_t* codes, float* scales,
+                     bsm_stream_t stream) {
+  if (!dtype_ok(x_dtype)) return fail(BSM_ERR_INVALID_ARG, "x_dtype must be BSM_BF16 or BSM_F32");
+  if (R < 0 || C < 0) return fail(BSM_ERR_INVALID_ARG, "negative shape");
+  if (C % 4 != 0) return fail(BSM_ERR_INVALID_ARG, "C (%lld) must be a multiple of 4", (long long)C);
+  if (R > 0x7FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "R too large");
+  if (R * C == 0) {
+    if (R > 0 && C == 0) return fail(BSM_ERR_INVALID_ARG, "C must be positive");
+    return ok();
+  }
+  if (!x || !codes || !scales) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(x, 16) || !aligned(codes, 4)) return fail(BSM_ERR_INVALID_ARG, "x 16-byte / codes 4-byte alignment");
+  return hip_status(bsm::launch_fp8_quantize(x, x_dtype == BSM_BF16, R, C, codes, scales, (hipStream_t)stream),
+                    "bsm_fp8_quantize");
+}
+
+size_t bsm_route_workspace_size(int64_t T, int64_t H, int64_t E) {
+  if (T < 0 || H <= 0 || E <= 0) return 0;
+  return bsm::route_ws(T, H, E);
+}
+
+static int route_checks(int64_t T, int64_t H, int64_t E, int n_group, int topk_group, int topk) {
+  if (T < 0 || H <= 0 || E <= 0) return fail(BSM_ERR_INVALID_ARG, "T >= 0, H > 0, E > 0 required");
+  if (E > 1024) return fail(BSM_ERR_UNSUPPORTED, "E (%lld) > 1024", (long long)E);
+  if (n_group < 1 || n_group > 64) return fail(BSM_ERR_INVALID_ARG, "n_group must be in [1, 64]");
+  if (E % n_group != 0) return fail(BSM_ERR_INVALID_ARG, "E %% n_group != 0");
+  if (E / n_group < 2) return fail(BSM_ERR_INVALID_ARG, "groups need at least 2 experts");
+  if (topk_group < 1 || topk_group > n_group) return fail(BSM_ERR_INVALID_ARG, "topk_group must be in [1, n_group]");
+  if (topk < 1 || topk > 32) return fail(BSM_ERR_INVALID_ARG, "topk must be in [1, 32]");
+  if ((int64_t)topk > (int64_t)topk_group * (E / n_group))
+    return fail(BSM_ERR_INVALID_ARG, "topk > topk_group * E / n_group");
+  if (T * E > 0x7FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "T * E too large");
+  return BSM_OK;
+}
+
+int bsm_route(const void* x, int x_dtype, int64_t T, int64_t H, const void* w_router, int w_dtype, int64_t E,
+              int n_group, int topk_group, int topk, int32_t* topk_ids, float* topk_weights, float* scores, void* ws,
+              size_t ws_bytes, bsm_stream_t stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype)) return fail(BSM_ERR_INVALID_ARG, "dtype must be BSM_BF16 or BSM_F32");
+  if (int r = route_checks(T, H, E, n_group, topk_group, topk)) return r;
+  if (T == 0) return ok();
+  if (!x || !w_router || !topk_ids || !topk_weights) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (int r = check_ws(ws, ws_bytes, bsm::route_ws(T, H, E))) return r;
+  return hip_status(bsm::launch_route(x, x_dtype == BSM_BF16, T, H, w_router, w_dtype == BSM_BF16, E, n_group,
+                                      topk_group, topk, topk_ids, topk_weights, scores, ws, (hipStream_t)stream),
+                    "bsm_route");
+}
+
+int bsm_route_diagnostics(const void* ws, int64_t T, int64_t H, int64_t E, int32_t* diag, bsm_stream_t stream) {
+  if (T < 0 || H <= 0 || E <= 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
+  if (!ws || !diag) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  return hip_status(bsm::launch_route_diag(ws, T, H, E, diag, (hipStream_t)stream), "bsm_route_diagnostics");
+}
+
+size_t bsm_moe_workspace_size(int format, int64_t E, int64_t H, int64_t I, int64_t T, int topk) {
+  if ((format != BSM_FMT_NVFP4 && format != BSM_FMT_FP8) || E <= 0 || H <= 0 || I <= 0 || T < 0 || topk <= 0) return 0;
+  return bsm::moe_layout(format == BSM_FMT_NVFP4, E, H, I, T, topk).total;
+}
+
+int bsm_moe_workspace_layout(int format, int64_t E, int64_t H, int64_t I, int64_t T, int topk,
+                             bsm_moe_ws_layout* out) {
+  if ((format != BSM_FMT_NVFP4 && format != BSM_FMT_FP8) || E <= 0 || H <= 0 || I <= 0 || T < 0 || topk <= 0 || !out)
+    return fail(BSM_ERR_INVALID_ARG, "bad arguments");
+  const bsm::MoeLayout L = bsm::moe_layout(format == BSM_FMT_NVFP4, E, H, I, T, topk);
+  out->total = L.total;
+  out->counts = L.counts;
+  out->offsets = L.offsets;
+  out->row_pair = L.row_pair;
+  out->pair_row = L.pair_row;
+  out->tiles = L.tiles;
+  out->h_f32 = L.h_f32;
+  out->h_codes = L.h_codes;
+  out->h_scales = L.h_scales;
+  out->h_gs = L.h_gs;
+  out->y_f32 = L.y_f32;
+  out->scratch = L.scratch;
+  return ok();
+}
+
+int bsm_moe_expert_mlp(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T, const int32_t* topk_ids,
+                       const float* topk_weights, int topk, float combine_scale, int h_gs_mode, float* h_global_scale,
+                       float* out, void* ws, size_t ws_bytes, bsm_stream_t stream) {
+  if (!w || !xq) return fail(BSM_ERR_INVALID_ARG, "NULL weights / activation descriptor");
+  if (w->format != BSM_FMT_NVFP4 && w->format != BSM_FMT_FP8) return fail(BSM_ERR_INVALID_ARG, "bad weight format");
+  if (xq->format != w->format) return fail(BSM_ERR_INVALID_ARG, "activation and weight formats differ");
+  const bool nv = w->format == BSM_FMT_NVFP4;
+  const int64_t E = w->E, H = w->H, I = w->I;
+  if (E <= 0 || H <= 0 || I <= 0 || T < 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
+  if (H % 128 != 0 || I % 128 != 0) return fail(BSM_ERR_UNSUPPORTED, "H and I must be multiples of 128");
+  if (E > 1024) return fail(BSM_ERR_UNSUPPORTED, "E > 1024");
+  if (topk < 1 || topk > 32 || topk > E) return fail(BSM_ERR_INVALID_ARG, "topk must be in [1, min(32, E)]");
+  if (T * topk > 0x3FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "T * topk too large");
+  if (h_gs_mode != BSM_GS_DYNAMIC && h_gs_mode != BSM_GS_STATIC) return fail(BSM_ERR_INVALID_ARG, "bad h_gs_mode");
+  if (nv && h_gs_mode == BSM_GS_STATIC && !h_global_scale)
+    return fail(BSM_ERR_INVALID_ARG, "STATIC h global scale needs h_global_scale");
+  if (T == 0) return ok();
+  if (!w->w13_codes || !w->w13_scales || !w->w2_codes || !w->w2_scales || !xq->codes || !xq->scales || !topk_ids ||
+      !topk_weights || !out)
+    return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (nv && (!w->w13_gs || !w->w2_gs || !xq->global_scale)) return fail(BSM_ERR_INVALID_ARG, "NULL global scale");
+  if (!aligned(w->w13_codes, 16) || !aligned(w->w2_codes, 16) || !aligned(xq->codes, 16) || !aligned(out, 16))
+    return fail(BSM_ERR_INVALID_ARG, "codes and out must be 16-byte aligned");
+  if (nv && (!aligned(w->w13_scales, 2) || !aligned(w->w2_scales, 2) || !aligned(xq->scales, 2)))
+    return fail(BSM_ERR_INVALID_ARG, "NVFP4 scales must be 2-byte aligned");
+  if (int r = check_ws(ws, ws_bytes, bsm::moe_layout(nv, E, H, I, T, topk).total)) return r;
+  bsm::MoeArgs a;
+  a.nvfp4 = nv;
+  a.E = E;
+  a.H = H;
+  a.I = I;
+  a.T = T;
+  a.topk = topk;
+  a.w13_codes = w->w13_codes;
+  a.w13_scales = w->w13_scales;
+  a.w13_gs = w->w13_gs;
+  a.w2_codes = w->w2_codes;
+  a.w2_scales = w->w2_scales;
+  a.w2_gs = w->w2_gs;
+  a.x_codes = xq->codes;
+  a.x_scales = xq->scales;
+  a.x_gs = xq->global_scale;
+  a.ids = topk_ids;
+  a.wts = topk_weights;
+  a.combine_scale = combine_scale;
+  a.h_static = h_gs_mode == BSM_GS_STATIC;
+  a.h_gs_user = h_global_scale;
+  a.out = out;
+  a.ws = (uint8_t*)ws;
+  return hip_status(bsm::launch_moe(a, (hipStream_t)stream), "bsm_moe_expert_mlp");
+}
+
+int bsm_rmsnorm_f32(const float* x, int64_t T, int64_t H, float eps, float* y, bsm_stream_t stream) {
+  if (T < 0 || H <= 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
+  if (!(eps >= 0.0f)) return fail(BSM_ERR_INVALID_ARG, "eps must be >= 0");
+  if (T == 0) return ok();
+  if (!x || !y) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  return hip_status(bsm::launch_rmsnorm(x, T, H, eps, y, (hipStream_t)stream), "bsm_rmsnorm_f32");
+}
+
+int bsm_scaled_residual_f32(float* x, const float* m, float a, float b, int64_t T, int64_t H, bsm_stream_t stream) {
+  if (T < 0 || H <= 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
+  if (T == 0) return ok();
+  if (!x || !m) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  return hip_status(bsm::launch_residual(x, m, a, b, T * H, (hipStream_t)stream), "bsm_scaled_residual_f32");
+}
+
+}  // extern "C"

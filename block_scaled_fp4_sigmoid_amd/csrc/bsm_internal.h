@@ -1,0 +1,82 @@
+// bsm_internal.h -- declarations shared by the kernel translation units and
+// the C ABI layer.  Launchers assume their arguments were validated by the
+// ABI layer (shapes, alignment, workspace size) and return the HIP status of
+// the enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bsm_numerics.h"
+
+namespace bsm {
+
+constexpr int kWave = 64;
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// ---- quantizers -----------------------------------------------------------
+// per-tensor partial maxima of |x| (NVFP4 dynamic global scale)
+constexpr int kAmaxMaxParts = 1024;
+int nvfp4_amax_parts(int64_t R, int64_t C);
+size_t nvfp4_quant_ws(int64_t B, int64_t R, int64_t C);
+hipError_t launch_nvfp4_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C, uint8_t* codes,
+                                 uint8_t* scales, float* gs, bool dynamic, float* ws_partials,
+                                 hipStream_t st);
+// same, with the global amax already known (bits of a non-negative float at
+// amax_bits, one per tensor) -- used for h whose amax comes from the GEMM epilogue
+hipError_t launch_nvfp4_quantize_from_amax(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C,
+                                           uint8_t* codes, uint8_t* scales, float* gs,
+                                           const uint32_t* amax_bits, const float* static_gs,
+                                           hipStream_t st);
+hipError_t launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t B,
+                                   int64_t R, int64_t C, float* out, hipStream_t st);
+hipError_t launch_fp8_quantize(const void* x, bool x_bf16, int64_t R, int64_t C, uint8_t* codes, float* scales,
+                               hipStream_t st);
+
+// ---- router ---------------------------------------------------------------
+size_t route_ws(int64_t T, int64_t H, int64_t E);
+hipError_t launch_route(const void* x, bool x_bf16, int64_t T, int64_t H, const void* w, bool w_bf16, int64_t E,
+                        int n_group, int topk_group, int topk, int32_t* ids, float* wts, float* scores, void* ws,
+                        hipStream_t st);
+size_t route_diag_offset(int64_t T, int64_t H, int64_t E);
+hipError_t launch_route_diag(const void* ws, int64_t T, int64_t H, int64_t E, int32_t* dst, hipStream_t st);
+
+// ---- expert MLP -----------------------------------------------------------
+struct MoeLayout {
+  size_t total, counts, offsets, row_pair, pair_row, tiles, h_f32, h_codes, h_scales, h_gs, y_f32, scratch;
+  // scratch sub-buffers
+  size_t sel_masks, chunk_cnt, chunk_base, ntiles, h_amax;
+  int64_t P, n_chunks, max_tiles;
+};
+MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int topk);
+
+struct MoeArgs {
+  bool nvfp4;
+  int64_t E, H, I, T;
+  int topk;
+  const uint8_t* w13_codes;
+  const void* w13_scales;
+  const float* w13_gs;
+  const uint8_t* w2_codes;
+  const void* w2_scales;
+  const float* w2_gs;
+  const uint8_t* x_codes;
+  const void* x_scales;
+  const float* x_gs;
+  const int32_t* ids;
+  const float* wts;
+  float combine_scale;
+  bool h_static;
+  float* h_gs_user;
+  float* out;
+  uint8_t* ws;
+};
+hipError_t launch_moe(const MoeArgs& a, hipStream_t st);
+
+// ---- norm / residual ------------------------------------------------------
+hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t H, float eps, float* y, hipStream_t st);
+hipError_t launch_residual(float* x, const float* m, float a, float b, int64_t n, hipStream_t st);
+
+}  // namespace bsm

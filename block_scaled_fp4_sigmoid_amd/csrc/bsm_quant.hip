@@ -1,0 +1,305 @@
+// bsm_quant.hip -- NVFP4 and FP8_DYNAMIC quantization kernels for gfx950.
+//
+// NVFP4 ("NVFP4 quantization" page, "Quantization scheme"): E2M1 elements,
+// one E4M3 scale per 16 consecutive values, one global scale per tensor.
+// FP8_DYNAMIC ("FP8 quantization" page, "Quantization scheme" and
+// "Quantization method"): one scale per row, values divided by the scale and
+// rounded to the nearest E4M3 value.
+//
+// Arithmetic per tensor (binary32, round to nearest even, in this order):
+//   S_g = amax / 2688 ; s_b = E4M3(a_b / (6*S_g)) ; q = E2M1(x / (s_b*S_g))
+// FP8 row: s = amax / 448 ; q = E4M3(x / s).
+//
+// Layout: a tensor [R, C] with C % 16 == 0 is a flat sequence of 16-value
+// blocks; block f covers elements 16f..16f+15, its codes are bytes 8f..8f+7
+// (low nibble = even element) and its scale is byte f.  One thread handles one
+// block per iteration, so a wave reads 2 KB (bf16) / 4 KB (f32) contiguous and
+// writes 512 B of codes and 64 B of scales contiguous.
+//
+// The dynamic global scale needs max|x| of the whole tensor before any block
+// can be encoded: pass 1 writes one partial maximum per workgroup, pass 2
+// reduces those (max is order independent, so the result is deterministic)
+// and encodes.  Pass 2 walks the tensor from the end so that the blocks pass 1
+// touched last are still in the last-level cache.
+
+#include "bsm_internal.h"
+
+namespace bsm {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ inline float block_max(float v, float* lds) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) lds[wid] = v;
+  __syncthreads();
+  float r = lds[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, lds[i]);
+  __syncthreads();
+  return r;
+}
+
+// Load 16 consecutive elements of block f as floats.
+template <bool BF16>
+__device__ inline void load16(const void* x, int64_t f, float* v) {
+  if (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + f * 16);
+    const uint4 a = p[0], b = p[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = u2f(w[i] << 16);
+      v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + f * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 q = p[i];
+      v[4 * i] = q.x;
+      v[4 * i + 1] = q.y;
+      v[4 * i + 2] = q.z;
+      v[4 * i + 3] = q.w;
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_amax_parts(const void* __restrict__ x, int64_t n_blk,
+                                                          float* __restrict__ parts, int nparts) {
+  __shared__ float lds[kThreads / 64];
+  const int b = blockIdx.y;
+  const void* xb = BF16 ? (const void*)((const uint16_t*)x + (int64_t)b * n_blk * 16)
+                        : (const void*)((const float*)x + (int64_t)b * n_blk * 16);
+  float m = 0.0f;
+  for (int64_t f = (int64_t)blockIdx.x * kThreads + threadIdx.x; f < n_blk; f += (int64_t)nparts * kThreads) {
+    float v[16];
+    load16<BF16>(xb, f, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  m = block_max(m, lds);
+  if (threadIdx.x == 0) parts[(int64_t)b * kAmaxMaxParts + blockIdx.x] = m;
+}
+
+// Encode one 16-value block with global scale S (S > 0, or S == 0 -> zero scales).
+__device__ inline void encode_block(const float* v, float S, float d1, uint8_t* codes_f, uint8_t* scale_f) {
+  float ab = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
+  uint32_t sc = 0;
+  if (S != 0.0f) sc = e4m3_code_mag(ab / d1);
+  const float sv = e4m3_value_mag(sc);
+  const float d2 = sv * S;
+  uint32_t q[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t sgn = (f2u(v[i]) >> 31) << 3;
+    const uint32_t mag = (sv == 0.0f) ? 0u : e2m1_code_mag(fabsf(v[i]) / d2);
+    q[i] = sgn | mag;
+  }
+  uint2 packed;
+  packed.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) | (q[6] << 24) |
+             (q[7] << 28);
+  packed.y = q[8] | (q[9] << 4) | (q[10] << 8) | (q[11] << 12) | (q[12] << 16) | (q[13] << 20) |
+             (q[14] << 24) | (q[15] << 28);
+  *reinterpret_cast<uint2*>(codes_f) = packed;
+  *scale_f = (uint8_t)sc;
+}
+
+// mode 0: dynamic from partial maxima; mode 1: static (gs read); mode 2: amax bits given
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_nvfp4_encode(const void* __restrict__ x, int64_t n_blk,
+                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                            float* __restrict__ gs, const float* __restrict__ parts,
+                                                            int nparts1, const uint32_t* __restrict__ amax_bits,
+                                                            const float* __restrict__ static_gs, int mode,
+                                                            int nparts2) {
+  __shared__ float lds[kThreads / 64];
+  const int b = blockIdx.y;
+  float S;
+  if (mode == 0) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < nparts1; i += kThreads) m = fmaxf(m, parts[(int64_t)b * kAmaxMaxParts + i]);
+    m = block_max(m, lds);
+    S = m / 2688.0f;
+  } else if (mode == 1) {
+    S = static_gs[b];
+  } else {
+    S = static_gs ? static_gs[b] : u2f(amax_bits[b]) / 2688.0f;
+  }
+  if (gs && mode != 1 && blockIdx.x == 0 && threadIdx.x == 0) gs[b] = S;
+  const float d1 = 6.0f * S;
+  const void* xb = BF16 ? (const void*)((const uint16_t*)x + (int64_t)b * n_blk * 16)
+                        : (const void*)((const float*)x + (int64_t)b * n_blk * 16);
+  uint8_t* cb = codes + (int64_t)b * n_blk * 8;
+  uint8_t* sb = scales + (int64_t)b * n_blk;
+  // walk from the end of the tensor (the blocks pass 1 read last come first)
+  const int64_t start = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (int64_t g = start; g < n_blk; g += (int64_t)nparts2 * kThreads) {
+    const int64_t f = n_blk - 1 - g;
+    float v[16];
+    load16<BF16>(xb, f, v);
+    encode_block(v, S, d1, cb + f * 8, sb + f);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_nvfp4_decode(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           const float* __restrict__ gs, int64_t n_blk,
+                                                           float* __restrict__ out) {
+  const int b = blockIdx.y;
+  const float S = gs[b];
+  const uint8_t* cb = codes + (int64_t)b * n_blk * 8;
+  const uint8_t* sb = scales + (int64_t)b * n_blk;
+  float* ob = out + (int64_t)b * n_blk * 16;
+  for (int64_t f = (int64_t)blockIdx.x * kThreads + threadIdx.x; f < n_blk; f += (int64_t)gridDim.x * kThreads) {
+    const uint2 c = *reinterpret_cast<const uint2*>(cb + f * 8);
+    const float sv = e4m3_value_mag(sb[f]);
+    float o[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w = i < 8 ? c.x : c.y;
+      const uint32_t q = (w >> (4 * (i & 7))) & 15u;
+      const float e = e2m1_value_mag(q & 7u) * sv;  // exact: <= 6 significant bits
+      const float r = e * S;
+      o[i] = (q & 8u) ? -r : r;
+    }
+    float4* op = reinterpret_cast<float4*>(ob + f * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_fp8_rows(const void* __restrict__ x, int64_t C,
+                                                        uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ float lds[kThreads / 64];
+  const int64_t r = blockIdx.x;
+  const int64_t n4 = C / 4;
+  auto load4 = [&](int64_t j, float* v) {
+    if (BF16) {
+      const uint2 w = *reinterpret_cast<const uint2*>((const uint16_t*)x + r * C + 4 * j);
+      v[0] = u2f(w.x << 16);
+      v[1] = u2f(w.x & 0xFFFF0000u);
+      v[2] = u2f(w.y << 16);
+      v[3] = u2f(w.y & 0xFFFF0000u);
+    } else {
+      const float4 q = *reinterpret_cast<const float4*>((const float*)x + r * C + 4 * j);
+      v[0] = q.x;
+      v[1] = q.y;
+      v[2] = q.z;
+      v[3] = q.w;
+    }
+  };
+  float m = 0.0f;
+  for (int64_t j = threadIdx.x; j < n4; j += kThreads) {
+    float v[4];
+    load4(j, v);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+  m = block_max(m, lds);
+  const float s = m / 448.0f;
+  if (threadIdx.x == 0) scales[r] = s;
+  for (int64_t j = threadIdx.x; j < n4; j += kThreads) {
+    float v[4];
+    load4(j, v);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t sgn = (f2u(v[i]) >> 31) << 7;
+      const uint32_t mag = (s == 0.0f) ? 0u : e4m3_code_mag(fabsf(v[i]) / s);
+      word |= (sgn | mag) << (8 * i);
+    }
+    *reinterpret_cast<uint32_t*>(codes + r * C + 4 * j) = word;
+  }
+}
+
+}  // namespace
+
+int nvfp4_amax_parts(int64_t R, int64_t C) {
+  const int64_t n_blk = R * C / 16;
+  int64_t p = (n_blk + kThreads * 8 - 1) / (kThreads * 8);
+  if (p < 1) p = 1;
+  if (p > kAmaxMaxParts) p = kAmaxMaxParts;
+  return (int)p;
+}
+
+size_t nvfp4_quant_ws(int64_t B, int64_t, int64_t) { return align256((size_t)B * kAmaxMaxParts * sizeof(float)); }
+
+static int encode_parts(int64_t n_blk, int64_t B) {
+  int64_t p = (n_blk + kThreads * 4 - 1) / (kThreads * 4);
+  if (p < 1) p = 1;
+  const int64_t cap = B > 1 ? 256 : 4096;
+  return (int)(p > cap ? cap : p);
+}
+
+hipError_t launch_nvfp4_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C, uint8_t* codes,
+                                 uint8_t* scales, float* gs, bool dynamic, float* parts, hipStream_t st) {
+  const int64_t n_blk = R * C / 16;
+  if (n_blk == 0 || B == 0) return hipSuccess;
+  const int np1 = nvfp4_amax_parts(R, C);
+  if (dynamic) {
+    dim3 g1(np1, (unsigned)B);
+    if (x_bf16)
+      k_amax_parts<true><<<g1, kThreads, 0, st>>>(x, n_blk, parts, np1);
+    else
+      k_amax_parts<false><<<g1, kThreads, 0, st>>>(x, n_blk, parts, np1);
+  }
+  const int np2 = encode_parts(n_blk, B);
+  dim3 g2(np2, (unsigned)B);
+  if (x_bf16)
+    k_nvfp4_encode<true><<<g2, kThreads, 0, st>>>(x, n_blk, codes, scales, gs, parts, np1, nullptr, gs,
+                                                   dynamic ? 0 : 1, np2);
+  else
+    k_nvfp4_encode<false><<<g2, kThreads, 0, st>>>(x, n_blk, codes, scales, gs, parts, np1, nullptr, gs,
+                                                    dynamic ? 0 : 1, np2);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quantize_from_amax(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C,
+                                           uint8_t* codes, uint8_t* scales, float* gs, const uint32_t* amax_bits,
+                                           const float* static_gs, hipStream_t st) {
+  const int64_t n_blk = R * C / 16;
+  if (n_blk == 0 || B == 0) return hipSuccess;
+  const int np2 = encode_parts(n_blk, B);
+  dim3 g2(np2, (unsigned)B);
+  if (x_bf16)
+    k_nvfp4_encode<true><<<g2, kThreads, 0, st>>>(x, n_blk, codes, scales, gs, nullptr, 0, amax_bits, static_gs, 2,
+                                                   np2);
+  else
+    k_nvfp4_encode<false><<<g2, kThreads, 0, st>>>(x, n_blk, codes, scales, gs, nullptr, 0, amax_bits, static_gs, 2,
+                                                    np2);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t B, int64_t R,
+                                   int64_t C, float* out, hipStream_t st) {
+  const int64_t n_blk = R * C / 16;
+  if (n_blk == 0 || B == 0) return hipSuccess;
+  int64_t p = (n_blk + kThreads * 4 - 1) / (kThreads * 4);
+  if (p > 4096) p = 4096;
+  dim3 g((unsigned)p, (unsigned)B);
+  k_nvfp4_decode<<<g, kThreads, 0, st>>>(codes, scales, gs, n_blk, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize(const void* x, bool x_bf16, int64_t R, int64_t C, uint8_t* codes, float* scales,
+                               hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  if (x_bf16)
+    k_fp8_rows<true><<<(unsigned)R, kThreads, 0, st>>>(x, C, codes, scales);
+  else
+    k_fp8_rows<false><<<(unsigned)R, kThreads, 0, st>>>(x, C, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace bsm

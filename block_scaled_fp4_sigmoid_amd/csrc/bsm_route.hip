@@ -1,0 +1,380 @@
+// bsm_route.hip -- group-limited sigmoid router for gfx950.
+//
+// Method ("Reflection releases Beam" news page, "Mixture-of-Experts
+// details"): sigmoid score per expert, experts split into n_group groups,
+// keep the topk_group groups with the largest sum of their two best scores,
+// select the topk best experts inside them, weights normalized by the sum of
+// the selected scores.  The router runs in FP32 ("Residual stream and
+// numerical decisions") on unquantized inputs ("NVFP4 quantization" page,
+// "Quantization scheme").
+//
+// To make the FP32 result independent of summation order, a logit is the
+// exactly rounded binary32 value of the exact dot product, and a score the
+// exactly rounded binary32 value of 1/(1+exp(-l)):
+//
+//   k_rowstats    per row of x and w: an upper bound of the 2-norm and the
+//                 lowest set-bit exponent over the row's nonzero entries
+//   k_logits      64x64 token x expert tiles, split along H; binary64 FMA
+//                 accumulation of products that are exact in binary64
+//   k_finalize    sums the split partials in a fixed order and proves the
+//                 binary32 rounding: (a) exact -- every partial sum is a
+//                 multiple of 2^L (L = lsb(x) + lsb(w)) below
+//                 |x|_2 |w|_2 < 2^(L+53), so no addition rounded; or
+//                 (b) certified -- the binary64 error bound
+//                 (terms + splits + 4) * 2^-53 * |x|_2 |w|_2 keeps the value
+//                 away from every binary32 rounding boundary.  Otherwise the
+//                 logit is queued for
+//   k_exact       an exact fixed-point superaccumulator sum, rounded once.
+//   k_select      one wave per token: certified binary64 sigmoid (double-
+//                 double fallback), group top-2 sums, group selection,
+//                 iterative 64-bit (score, index) argmax, normalization.
+
+#include "bsm_internal.h"
+
+namespace bsm {
+
+namespace {
+
+constexpr int kTile = 64;  // tokens x experts per workgroup
+constexpr int kBK = 32;    // K step staged in LDS
+constexpr int kFbBlocks = 256;
+
+struct RouteWs {
+  size_t norm, lsb, part, logits, list, diag, total;
+  int ks, kc;
+};
+
+RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
+  RouteWs L;
+  const int64_t tiles = ((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
+  int64_t ks = (1024 + tiles - 1) / tiles;
+  const int64_t kmax = (H + 127) / 128;
+  if (ks > kmax) ks = kmax;
+  if (ks < 1) ks = 1;
+  int64_t kc = (H + ks - 1) / ks;
+  kc = (kc + kBK - 1) / kBK * kBK;
+  ks = (H + kc - 1) / kc;
+  L.ks = (int)ks;
+  L.kc = (int)kc;
+  size_t o = 0;
+  L.norm = o;
+  o += align256(sizeof(double) * (size_t)(T + E));
+  L.lsb = o;
+  o += align256(sizeof(int) * (size_t)(T + E));
+  L.part = o;
+  o += align256(sizeof(double) * (size_t)ks * (size_t)T * (size_t)E);
+  L.logits = o;
+  o += align256(sizeof(float) * (size_t)T * (size_t)E);
+  L.list = o;
+  o += align256(sizeof(int) * (size_t)T * (size_t)E);
+  L.diag = o;
+  o += align256(sizeof(int) * 4);
+  L.total = o;
+  return L;
+}
+
+template <bool BF16>
+__device__ inline float ld1(const void* p, int64_t i) {
+  if (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  return reinterpret_cast<const float*>(p)[i];
+}
+
+__global__ void k_route_prep(int* diag) {
+  if (threadIdx.x < 4) diag[threadIdx.x] = 0;
+}
+
+template <bool XB, bool WB>
+__global__ __launch_bounds__(64) void k_rowstats(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
+                                                 int64_t E, int64_t H, double* __restrict__ norm,
+                                                 int* __restrict__ lsb) {
+  const int64_t r = blockIdx.x;
+  const bool isx = r < T;
+  const void* p = isx ? x : w;
+  const int64_t row = isx ? r : r - T;
+  double ss = 0.0;
+  int lmin = 0x7FFFFFFF;
+  for (int64_t k = threadIdx.x; k < H; k += 64) {
+    const float v = isx ? ld1<XB>(p, row * H + k) : ld1<WB>(p, row * H + k);
+    const double d = (double)v;
+    ss = fma(d, d, ss);
+    if (v != 0.0f) {
+      const int l = f32_lsb_exp(v);
+      lmin = l < lmin ? l : lmin;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ss += __shfl_xor(ss, o, 64);
+    const int ol = __shfl_xor(lmin, o, 64);
+    lmin = ol < lmin ? ol : lmin;
+  }
+  if (threadIdx.x == 0) {
+    // relative error of ss is below (H + 6) * 2^-53; inflate generously
+    norm[r] = sqrt(ss * (1.0 + 0x1p-30)) * (1.0 + 0x1p-40);
+    lsb[r] = lmin;
+  }
+}
+
+template <bool XB, bool WB>
+__global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
+                                                int64_t E, int64_t H, int kc, double* __restrict__ part) {
+  __shared__ float xs[kBK][kTile + 4];
+  __shared__ float wsm[kBK][kTile + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kTile, e0 = (int64_t)blockIdx.y * kTile;
+  const int s = blockIdx.z;
+  const int64_t k0 = (int64_t)s * kc;
+  int64_t k1 = k0 + kc;
+  if (k1 > H) k1 = H;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  const int lr = tid >> 2;        // row of the tile this thread stages
+  const int lk = (tid & 3) * 8;   // first k of the 8 it stages
+  for (int64_t kb = k0; kb < k1; kb += kBK) {
+    {
+      const int64_t t = t0 + lr, e = e0 + lr;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t k = kb + lk + q;
+        const bool kin = k < k1;
+        xs[lk + q][lr] = (kin && t < T) ? ld1<XB>(x, t * H + k) : 0.0f;
+        wsm[lk + q][lr] = (kin && e < E) ? ld1<WB>(w, e * H + k) : 0.0f;
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < kBK; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(&xs[kk][ty * 4]);
+      const float4 b = *reinterpret_cast<const float4*>(&wsm[kk][tx * 4]);
+      const double av[4] = {(double)a.x, (double)a.y, (double)a.z, (double)a.w};
+      const double bv[4] = {(double)b.x, (double)b.y, (double)b.z, (double)b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t e = e0 + tx * 4 + j;
+      if (e < E) part[((int64_t)s * T + t) * E + e] = acc[i][j];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ part, int ks, int kc, int64_t T,
+                                                  int64_t E, const double* __restrict__ norm,
+                                                  const int* __restrict__ lsb, float* __restrict__ logits,
+                                                  int* __restrict__ list, int* __restrict__ diag) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * E) return;
+  const int64_t t = i / E, e = i % E;
+  double S = 0.0;
+  for (int s = 0; s < ks; ++s) S += part[((int64_t)s * T + t) * E + e];
+  const double A = norm[t] * norm[T + e] * (1.0 + 0x1p-40);  // >= sum |x_k w_k|
+  const int lx = lsb[t], lw = lsb[T + e];
+  float r = (float)S;
+  bool ok = false;
+  if (A == 0.0) {
+    ok = true;  // every product is zero
+    r = 0.0f;
+  } else if (lx != 0x7FFFFFFF && lw != 0x7FFFFFFF) {
+    const int L = lx + lw;
+    if (L + 53 > -1000 && A < ldexp(1.0, L + 53)) ok = true;  // the binary64 sum is exact
+  }
+  if (!ok) {
+    const double err = (double)(kc + ks + 4) * 0x1p-53 * A * 1.0001;
+    ok = f32_certified(S, err, &r);
+  }
+  if (ok) {
+    logits[i] = r;
+  } else {
+    const int slot = atomicAdd(&diag[0], 1);
+    list[slot] = (int)i;
+    logits[i] = 0.0f;  // replaced by k_exact
+  }
+}
+
+template <bool XB, bool WB>
+__global__ __launch_bounds__(64) void k_exact(const void* __restrict__ x, const void* __restrict__ w, int64_t E,
+                                             int64_t H, const int* __restrict__ list, const int* __restrict__ diag,
+                                             float* __restrict__ logits) {
+  __shared__ int64_t dig[64][SA_NDIG + 1];
+  __shared__ int64_t tot[SA_NDIG];
+  const int lane = threadIdx.x;
+  const int n = diag[0];
+  for (int it = blockIdx.x; it < n; it += gridDim.x) {
+    const int64_t i = list[it];
+    const int64_t t = i / E, e = i % E;
+    for (int d = 0; d < SA_NDIG; ++d) dig[lane][d] = 0;
+    for (int64_t k = lane; k < H; k += 64) {
+      const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);  // exact
+      sa_add(dig[lane], p);
+    }
+    __syncthreads();
+    if (lane < SA_NDIG) {
+      int64_t s = 0;
+      for (int l = 0; l < 64; ++l) s += dig[l][lane];
+      tot[lane] = s;
+    }
+    __syncthreads();
+    if (lane == 0) logits[i] = sa_round_f32(tot);
+    __syncthreads();
+  }
+}
+
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    const uint64_t u = ((uint64_t)hi << 32) | lo;
+    v = u > v ? u : v;
+  }
+  return v;
+}
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxPerLane = kMaxE / 64;
+
+__global__ __launch_bounds__(64) void k_select(const float* __restrict__ logits, int64_t E, int n_group,
+                                               int topk_group, int topk, int32_t* __restrict__ ids,
+                                               float* __restrict__ wts, float* __restrict__ scores,
+                                               int* __restrict__ diag) {
+  __shared__ float s_lds[kMaxE];
+  __shared__ float g_lds[64];
+  __shared__ int kept[64];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x;
+  int nslow = 0;
+  for (int64_t e = lane; e < E; e += 64) {
+    bool fast;
+    const float s = sigmoid_f32_exact(logits[t * E + e], &fast);
+    nslow += fast ? 0 : 1;
+    s_lds[e] = s;
+    if (scores) scores[t * E + e] = s;
+  }
+  if (nslow) atomicAdd(&diag[1], nslow);
+  __syncthreads();
+  const int gsz = (int)(E / n_group);
+  if (lane < n_group) {
+    float t1 = -1.0f, t2 = -1.0f;
+    for (int i = 0; i < gsz; ++i) {
+      const float v = s_lds[lane * gsz + i];
+      if (v > t1) {
+        t2 = t1;
+        t1 = v;
+      } else if (v > t2) {
+        t2 = v;
+      }
+    }
+    g_lds[lane] = t1 + t2;
+  }
+  __syncthreads();
+  if (lane < n_group) {
+    const float gj = g_lds[lane];
+    int rank = 0;
+    for (int i = 0; i < n_group; ++i) {
+      const float gi = g_lds[i];
+      rank += (gi > gj || (gi == gj && i < lane)) ? 1 : 0;
+    }
+    kept[lane] = rank < topk_group ? 1 : 0;
+  }
+  __syncthreads();
+  uint64_t key[kMaxPerLane];
+#pragma unroll
+  for (int q = 0; q < kMaxPerLane; ++q) {
+    const int e = lane + 64 * q;
+    key[q] = 0;
+    if (e < E && kept[e / gsz]) key[q] = ((uint64_t)f2u(s_lds[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+  }
+  int my_id = 0;
+  float my_s = 0.0f;
+  float ssum = 0.0f;
+  float sel_s[32];
+  int sel_id[32];
+  for (int r = 0; r < topk; ++r) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxPerLane; ++q) m = key[q] > m ? key[q] : m;
+    m = wave_max_u64(m);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
+    const float s = u2f((uint32_t)(m >> 32));
+#pragma unroll
+    for (int q = 0; q < kMaxPerLane; ++q)
+      if (lane + 64 * q == e) key[q] = 0;
+    sel_s[r] = s;
+    sel_id[r] = e;
+    ssum = (r == 0) ? s : ssum + s;
+    if (lane == r) {
+      my_id = e;
+      my_s = s;
+    }
+  }
+  (void)sel_s;
+  (void)sel_id;
+  if (lane < topk) {
+    ids[t * topk + lane] = my_id;
+    wts[t * topk + lane] = my_s / ssum;
+  }
+}
+
+__global__ void k_copy_diag(const int* src, int32_t* dst) {
+  if (threadIdx.x < 4) dst[threadIdx.x] = src[threadIdx.x];
+}
+
+}  // namespace
+
+size_t route_ws(int64_t T, int64_t H, int64_t E) { return route_layout(T, H, E).total; }
+size_t route_diag_offset(int64_t T, int64_t H, int64_t E) { return route_layout(T, H, E).diag; }
+
+hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void* w, bool wb, int64_t E, int n_group,
+                        int topk_group, int topk, int32_t* ids, float* wts, float* scores, void* ws_, hipStream_t st) {
+  const RouteWs L = route_layout(T, H, E);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(ws_);
+  double* norm = reinterpret_cast<double*>(ws + L.norm);
+  int* lsb = reinterpret_cast<int*>(ws + L.lsb);
+  double* part = reinterpret_cast<double*>(ws + L.part);
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int* list = reinterpret_cast<int*>(ws + L.list);
+  int* diag = reinterpret_cast<int*>(ws + L.diag);
+  if (T == 0) return hipSuccess;
+  k_route_prep<<<1, 64, 0, st>>>(diag);
+  const unsigned nrows = (unsigned)(T + E);
+  dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile), (unsigned)L.ks);
+  const unsigned nfin = (unsigned)((T * E + 255) / 256);
+#define BSM_ROUTE_DISPATCH(XB, WB)                                                           \
+  k_rowstats<XB, WB><<<nrows, 64, 0, st>>>(x, w, T, E, H, norm, lsb);                      \
+  k_logits<XB, WB><<<gl, 256, 0, st>>>(x, w, T, E, H, L.kc, part);                          \
+  k_finalize<<<nfin, 256, 0, st>>>(part, L.ks, L.kc, T, E, norm, lsb, logits, list, diag); \
+  k_exact<XB, WB><<<kFbBlocks, 64, 0, st>>>(x, w, E, H, list, diag, logits);
+  if (xb && wb) {
+    BSM_ROUTE_DISPATCH(true, true)
+  } else if (xb && !wb) {
+    BSM_ROUTE_DISPATCH(true, false)
+  } else if (!xb && wb) {
+    BSM_ROUTE_DISPATCH(false, true)
+  } else {
+    BSM_ROUTE_DISPATCH(false, false)
+  }
+#undef BSM_ROUTE_DISPATCH
+  k_select<<<(unsigned)T, 64, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, diag);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_diag(const void* ws, int64_t T, int64_t H, int64_t E, int32_t* dst, hipStream_t st) {
+  const int* src = reinterpret_cast<const int*>(reinterpret_cast<const uint8_t*>(ws) + route_layout(T, H, E).diag);
+  k_copy_diag<<<1, 64, 0, st>>>(src, dst);
+  return hipGetLastError();
+}
+
+}  // namespace bsm

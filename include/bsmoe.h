@@ -1,0 +1,227 @@
+/*
+ * bsmoe.h -- C ABI of the MI355X (gfx950) NVFP4 / FP8_DYNAMIC routed-expert
+ * MoE path: group-limited sigmoid routing, block-scaled activation
+ * quantization, expert-grouped gate/up/down GEMMs with a SwiGLU product, and
+ * the normalized-weight combine.
+ *
+ * Method sources (cited per function below):
+ *   [NVFP4]  "NVFP4 quantization" page, section "Quantization scheme":
+ *            W4A4; elements are 4-bit E2M1; each block of 16 values shares an
+ *            FP8 E4M3 scale; each tensor has one more global scale; only the
+ *            routed experts' gate/up/down projections are quantized, router
+ *            input and weights stay unquantized.
+ *   [FP8]    "FP8 quantization" page, sections "Quantization scheme" and
+ *            "Quantization method": FP8_DYNAMIC (W8A8), E4M3 weights with a
+ *            fixed per-output-channel scale, activation scales computed per
+ *            token at run time; values are divided by their scale and
+ *            rounded to the nearest FP8 value.
+ *   [MOE]    "Reflection releases Beam" news page, section
+ *            "Mixture-of-Experts details": sigmoid scores over 256 experts,
+ *            8 groups of 32, keep the 4 groups with the largest sum of their
+ *            two best scores, top 8 experts within them, SwiGLU experts with
+ *            intermediate 2560, outputs combined with normalized router
+ *            weights and scaled by 2.5.
+ *   [NUM]    same page, section "Residual stream and numerical decisions":
+ *            router, SwiGLU product and norms in FP32; residual step k adds
+ *            the sublayer output with weight 1/sqrt(k) and keeps the stream
+ *            with weight sqrt((k-1)/k).
+ *
+ * Conventions (all functions):
+ *   - Pointers named x, w*, codes, scales, out, ws ... are DEVICE pointers
+ *     owned by the caller; arrays are dense row-major; the library never
+ *     allocates or frees and keeps no pointer after a call returns.
+ *   - Work is enqueued on `stream` (hipStream_t, 0 = null stream) and is
+ *     asynchronous; no function synchronizes the host.
+ *   - Scratch memory is a caller-provided (ws, ws_bytes) pair, at least the
+ *     size the matching *_workspace_size() returns, 256-byte aligned.  Its
+ *     contents need no initialization and are clobbered.
+ *   - Return value: BSM_OK or an error code.  Arguments are validated on the
+ *     host before anything is enqueued; on error nothing is enqueued and no
+ *     output is touched.  bsm_last_error() returns a thread-local message
+ *     describing the most recent error of the calling thread.
+ *   - Inputs must be finite.  Results are deterministic: the same inputs give
+ *     bit-identical outputs on every run.
+ *   - Element dtypes: BSM_BF16 (bfloat16) or BSM_F32 (IEEE binary32).
+ *   - E4M3 means OCP FP8 E4M3FN (bias 7, max finite 448, no infinities).
+ */
+#ifndef BSMOE_H
+#define BSMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSM_ABI_VERSION 1
+
+typedef struct ihipStream_t* bsm_stream_t; /* identical to hipStream_t */
+
+enum bsm_status {
+  BSM_OK = 0,
+  BSM_ERR_INVALID_ARG = 1, /* null pointer, bad shape, bad enum value */
+  BSM_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  BSM_ERR_WORKSPACE = 3,   /* ws missing, misaligned or too small */
+  BSM_ERR_HIP = 4          /* a HIP runtime call failed (message in bsm_last_error) */
+};
+
+enum bsm_dtype { BSM_BF16 = 1, BSM_F32 = 2 };
+enum bsm_format { BSM_FMT_NVFP4 = 1, BSM_FMT_FP8 = 2 };
+enum bsm_gs_mode { BSM_GS_DYNAMIC = 0, BSM_GS_STATIC = 1 };
+
+/* Library version (BSM_ABI_VERSION). */
+int bsm_abi_version(void);
+
+/* Static string naming a status code. */
+const char* bsm_status_str(int status);
+
+/* Thread-local description of the calling thread's most recent error ("" if none). */
+const char* bsm_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * NVFP4 quantization [NVFP4]
+ *
+ * Quantizes B independent tensors x[b] of shape [R, C] (C % 16 == 0, blocks of
+ * 16 consecutive values along C) to
+ *   codes  uint8 [B, R, C/2]   E2M1 codes, element 2j in the low nibble of byte j
+ *   scales uint8 [B, R, C/16]  E4M3 block scales
+ *   global_scale float [B]     per-tensor decode multiplier S_g
+ * with, per tensor (IEEE binary32 arithmetic, round to nearest even):
+ *   S_g = amax / 2688                       (DYNAMIC: written; STATIC: read)
+ *   s_b = E4M3(a_b / (6*S_g)), a_b = max |x| over the block  (0 if S_g == 0)
+ *   q   = E2M1(x / (s_b*S_g)), sign = sign of x; a zero scale gives +-0 codes
+ * E4M3/E2M1 conversions round to nearest, ties to even, saturating at 448/6.
+ * Decoded value: q * s_b * S_g.  B = 1 for activations; B = n_experts for one
+ * projection of every expert (each expert's gate, up and down get their own
+ * S_g).  x: bf16 or f32 per x_dtype.  Workspace: see the size function.
+ * ------------------------------------------------------------------------ */
+size_t bsm_nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C);
+int bsm_nvfp4_quantize(const void* x, int x_dtype, int64_t B, int64_t R, int64_t C,
+                       uint8_t* codes, uint8_t* scales, float* global_scale, int gs_mode,
+                       void* ws, size_t ws_bytes, bsm_stream_t stream);
+
+/* Dequantize: out[b,r,c] = fl32(fl32(q*s_b) * S_g[b]) (q*s_b is exact), float32 output. */
+int bsm_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                         int64_t B, int64_t R, int64_t C, float* out, bsm_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * FP8_DYNAMIC quantization, one scale per row [FP8]
+ *
+ * x [R, C] -> codes uint8 [R, C] (E4M3), scales float [R]:
+ *   s = amax_row / 448 ; q = E4M3(x / s) (nearest, ties to even, saturating)
+ * A row with amax == 0 gets s = 0 and +-0 codes.  Rows are tokens for
+ * activations and output channels for weights.  Decoded value q * s.
+ * ------------------------------------------------------------------------ */
+int bsm_fp8_quantize(const void* x, int x_dtype, int64_t R, int64_t C, uint8_t* codes, float* scales,
+                     bsm_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Group-limited sigmoid router [MOE], FP32 [NUM], unquantized [NVFP4]
+ *
+ * x [T, H] (bf16 or f32), w_router [E, H] (bf16 or f32).  Per token:
+ *   l_e = exactly rounded binary32 value of the exact dot product x . w_e
+ *   s_e = exactly rounded binary32 value of 1 / (1 + exp(-l_e))
+ *   group score g_j = s(1) + s(2) (binary32 add of the group's two best)
+ *   keep the topk_group groups with the largest g (ties: lower group index)
+ *   select the topk experts with the largest s inside kept groups (ties: lower
+ *   expert index); topk_ids [T, topk] int32 ordered by (s desc, id asc)
+ *   topk_weights [T, topk] = s_j / S, S = binary32 running sum of the
+ *   selected s in output order (the combine scale is applied later).
+ * scores [T, E] (float) receives s when non-NULL.
+ * Requirements: E % n_group == 0, E/n_group >= 2, 1 <= topk_group <= n_group,
+ * 1 <= topk <= min(32, topk_group * E/n_group), E <= 1024, n_group <= 64.
+ * ------------------------------------------------------------------------ */
+size_t bsm_route_workspace_size(int64_t T, int64_t H, int64_t E);
+int bsm_route(const void* x, int x_dtype, int64_t T, int64_t H, const void* w_router, int w_dtype, int64_t E,
+              int n_group, int topk_group, int topk, int32_t* topk_ids, float* topk_weights, float* scores,
+              void* ws, size_t ws_bytes, bsm_stream_t stream);
+
+/* Route diagnostics read back from the workspace of the last bsm_route call
+ * enqueued with it: number of logits and scores that needed the exact
+ * fallback evaluation.  Copies 4 int32 from device ws to `diag` (device
+ * pointer) on `stream`. */
+int bsm_route_diagnostics(const void* ws, int64_t T, int64_t H, int64_t E, int32_t* diag, bsm_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Routed-expert MLP [MOE] [NVFP4] [FP8] [NUM]
+ *
+ * Weights (canonical layout, consumed directly):
+ *   NVFP4: w13_codes uint8 [E, 2I, H/2], w13_scales uint8 [E, 2I, H/16],
+ *          w13_gs float [E, 2] (gate, up);  rows 0..I-1 gate, I..2I-1 up.
+ *          w2_codes uint8 [E, H, I/2], w2_scales uint8 [E, H, I/16], w2_gs float [E].
+ *   FP8:   w13_codes uint8 [E, 2I, H], w13_scales float [E, 2I];
+ *          w2_codes uint8 [E, H, I],   w2_scales float [E, H]; *_gs unused (NULL).
+ * Activations xq: NVFP4 codes [T, H/2] + scales [T, H/16] + global_scale
+ *   (device float*), or FP8 codes [T, H] + scales float [T].
+ * For every pair (t, j), e = topk_ids[t, j]:
+ *   g, u = binary32-accumulated products of the decoded x[t] with gate/up of e
+ *   h    = silu(g) * u in binary32
+ *   h is re-quantized (NVFP4: one global scale over all T*topk rows, DYNAMIC
+ *   or STATIC via h_gs_mode / h_global_scale; FP8: one scale per row)
+ *   y    = decoded h times down of e
+ *   out[t] = combine_scale * sum_j topk_weights[t, j] * y(t, j)   (float [T, H])
+ * Requirements: H % 16 == 0 and I % 16 == 0 (NVFP4), H % 128 == 0, I % 128 == 0,
+ * topk <= 32, ids in [0, E).  h_global_scale: NVFP4 STATIC -> read; DYNAMIC ->
+ * written when non-NULL.  The layout of the workspace (stage buffers) is
+ * reported by bsm_moe_workspace_layout for inspection.
+ * ------------------------------------------------------------------------ */
+typedef struct bsm_moe_weights {
+  int format;
+  int64_t E, H, I;
+  const uint8_t* w13_codes;
+  const void* w13_scales;
+  const float* w13_gs;
+  const uint8_t* w2_codes;
+  const void* w2_scales;
+  const float* w2_gs;
+} bsm_moe_weights;
+
+typedef struct bsm_act_q {
+  int format;
+  const uint8_t* codes;
+  const void* scales;
+  const float* global_scale;
+} bsm_act_q;
+
+/* Byte offsets of the stage buffers inside the expert-MLP workspace. */
+typedef struct bsm_moe_ws_layout {
+  size_t total;
+  size_t counts;      /* int32 [E]        pairs per expert                                  */
+  size_t offsets;     /* int32 [E+1]      first row of each expert (rows sorted by (e, t, j)) */
+  size_t row_pair;    /* int32 [P]        pair index t*topk+j of each sorted row             */
+  size_t pair_row;    /* int32 [P]        sorted row of each pair                            */
+  size_t tiles;       /* int32 [..]       row-tile work list                                 */
+  size_t h_f32;       /* float [P, I]     h of each sorted row                               */
+  size_t h_codes;     /* uint8 [P, I/2] (NVFP4) or [P, I] (FP8)                              */
+  size_t h_scales;    /* uint8 [P, I/16] (NVFP4) or float [P] (FP8)                          */
+  size_t h_gs;        /* float [1]        NVFP4 global scale of h                            */
+  size_t y_f32;       /* float [P, H]     down-projection output of each sorted row          */
+  size_t scratch;     /* internal                                                            */
+} bsm_moe_ws_layout;
+
+size_t bsm_moe_workspace_size(int format, int64_t E, int64_t H, int64_t I, int64_t T, int topk);
+int bsm_moe_workspace_layout(int format, int64_t E, int64_t H, int64_t I, int64_t T, int topk,
+                             bsm_moe_ws_layout* layout /* host pointer */);
+int bsm_moe_expert_mlp(const bsm_moe_weights* w /* host */, const bsm_act_q* xq /* host */, int64_t T,
+                       const int32_t* topk_ids, const float* topk_weights, int topk, float combine_scale,
+                       int h_gs_mode, float* h_global_scale, float* out, void* ws, size_t ws_bytes,
+                       bsm_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * FP32 RMSNorm and depth-scaled residual [NUM]
+ *
+ * bsm_rmsnorm_f32: y[t] = fl32(x[t] * r), r = fl32(1/sqrt(fl32(mean(x[t]^2)) + eps)),
+ *   mean and root in float64; gain 1.
+ * bsm_scaled_residual_f32: x <- fl32(a*x + b*m) in place (float64 evaluation);
+ *   a = sqrt((k-1)/k), b = 1/sqrt(k) for residual step k.
+ * ------------------------------------------------------------------------ */
+int bsm_rmsnorm_f32(const float* x, int64_t T, int64_t H, float eps, float* y, bsm_stream_t stream);
+int bsm_scaled_residual_f32(float* x, const float* m, float a, float b, int64_t T, int64_t H,
+                            bsm_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSMOE_H */

@@ -1,0 +1,48 @@
+// Host build of the library's scalar numerics (bsm_numerics.h) for CPU tests:
+// the same source the gfx950 kernels use, compiled by g++ and called through
+// ctypes so the oracle can check it without a GPU.
+#include "../../block_scaled_fp4_sigmoid_amd/csrc/bsm_numerics.h"
+
+extern "C" {
+
+void hc_e4m3_code(const float* a, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)bsm::e4m3_code_mag(a[i]);
+}
+void hc_e2m1_code(const float* a, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)bsm::e2m1_code_mag(a[i]);
+}
+void hc_e4m3_value(const uint8_t* c, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bsm::e4m3_value_mag(c[i]);
+}
+void hc_e2m1_value(const uint8_t* c, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bsm::e2m1_value_mag(c[i]);
+}
+// exact dot products of float32 rows through the superaccumulator
+void hc_exact_dot(const float* x, const float* w, int64_t rows, int64_t n, float* out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    int64_t dig[bsm::SA_NDIG] = {0};
+    for (int64_t k = 0; k < n; ++k) bsm::sa_add(dig, (double)x[r * n + k] * (double)w[r * n + k]);
+    out[r] = bsm::sa_round_f32(dig);
+  }
+}
+void hc_sigmoid(const float* l, int64_t n, float* out, int32_t* fast) {
+  for (int64_t i = 0; i < n; ++i) {
+    bool f;
+    out[i] = bsm::sigmoid_f32_exact(l[i], &f);
+    fast[i] = f ? 1 : 0;
+  }
+}
+void hc_sigmoid_dd(const float* l, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double x = -(double)l[i];
+    if (x > 700.0) {
+      out[i] = 0.0f;
+      continue;
+    }
+    const bsm::dd E = bsm::dd_exp(x);
+    out[i] = bsm::dd_to_f32(bsm::dd_div(bsm::dd{1.0, 0.0}, bsm::dd_add(bsm::dd{1.0, 0.0}, E)));
+  }
+}
+int hc_f32_certified(double v, double err, float* out) { return bsm::f32_certified(v, err, out) ? 1 : 0; }
+int hc_lsb_exp(float f) { return bsm::f32_lsb_exp(f); }
+}

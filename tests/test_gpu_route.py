@@ -1,0 +1,88 @@
+"""GPU parity: group-limited sigmoid router (ids, weights and scores bit-exact)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import route as R
+from tests.helpers import np_, to_dev_bf16, to_dev_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gpu_lib, x, wr, G, kg, k, x_bf16=True, w_bf16=True):
+    xt = to_dev_bf16(x) if x_bf16 else to_dev_f32(x)
+    wt = to_dev_bf16(wr) if w_bf16 else to_dev_f32(wr)
+    ids, wts, scores, ws = gpu_lib.route(xt, wt, G, kg, k, return_scores=True, return_workspace=True)
+    diag = gpu_lib.route_diagnostics(ws, x.shape[0], x.shape[1], wr.shape[0])
+    torch.cuda.synchronize()
+    return np_(ids), np_(wts), np_(scores), np_(diag)
+
+
+def _check(gpu, x, wr, G, kg, k):
+    ids, wts, scores, diag = gpu
+    oi, ow, os_, st = R.route(x, wr, G, kg, k)
+    assert np.array_equal(scores.view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(ids, oi)
+    assert np.array_equal(wts.view(np.uint32), ow.view(np.uint32))
+    return diag, st
+
+
+def test_route_tiny_fp32_router(gpu_lib):
+    cfg = W.TINY
+    x, wr = W.activations(cfg), W.router_weights(cfg)
+    _check(_run(gpu_lib, x, wr, cfg.n_group, cfg.topk_group, cfg.topk, w_bf16=False), x, wr, 4, 2, 2)
+
+
+def test_route_decode_shape(gpu_lib):
+    cfg = W.DECODE
+    x, wr = W.activations(cfg), W.router_weights(cfg)
+    diag, st = _check(_run(gpu_lib, x, wr, 8, 4, 8), x, wr, 8, 4, 8)
+
+
+def test_route_prefill_shape_full(gpu_lib):
+    cfg = W.PREFILL
+    x, wr = W.activations(cfg), W.router_weights(cfg)
+    diag, st = _check(_run(gpu_lib, x, wr, 8, 4, 8), x, wr, 8, 4, 8)
+    print("route prefill diag", diag, "oracle refinements", st["logits_refined"], st["sigmoid_refined"])
+
+
+def test_route_fp32_stream_input(gpu_lib):
+    # the stacked layers route an FP32 residual-stream input with bf16 router weights
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((300, 5120)).astype(np.float32)
+    wr = W.router_weights(W.DECODE)
+    _check(_run(gpu_lib, x, wr, 8, 4, 8, x_bf16=False), x, wr, 8, 4, 8)
+
+
+def test_route_ties_and_saturation(gpu_lib):
+    rng = np.random.default_rng(12)
+    H, E = 256, 64
+    x = W.to_bf16_f32(rng.standard_normal((96, H)).astype(np.float32))
+    wr = W.to_bf16_f32((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
+    wr[10] = wr[3]            # identical logits -> exact score ties, lower index must win
+    wr[40] = wr[33]
+    wr[50:54] = wr[50] * 64   # large logits -> sigmoid saturates to 1.0f (ties at 1.0)
+    x[5] = 0.0                # all-zero token: every score 0.5
+    _check(_run(gpu_lib, x, wr, 8, 4, 8), x, wr, 8, 4, 8)
+    _check(_run(gpu_lib, x, wr, 8, 8, 8), x, wr, 8, 8, 8)  # all groups kept == plain top-k
+    _check(_run(gpu_lib, x, wr, 4, 1, 3), x, wr, 4, 1, 3)
+
+
+def test_route_exact_fallback_paths(gpu_lib):
+    """Cancelling dot products and float32-midpoint logits go through the exact superaccumulator."""
+    rng = np.random.default_rng(13)
+    T, H, E = 64, 512, 16
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    x[:, 0] = 2.0 ** 20
+    x[:, 1] = -(2.0 ** 20)
+    w[:, 0] = 1.0
+    w[:, 1] = 1.0  # the two large terms cancel exactly; the binary64 bound is wide
+    x[3, :] = 0.0
+    x[3, :2] = [1.0, 2.0 ** -24]
+    w[:, 2:] = w[:, 2:]  # keep
+    ids, wts, scores, diag = _run(gpu_lib, x, w, 4, 2, 4, x_bf16=False, w_bf16=False)
+    _check((ids, wts, scores, diag), x, w, 4, 2, 4)
+    assert diag[0] > 0  # the fallback ran

@@ -1,0 +1,121 @@
+"""The HIP library's scalar numerics (bsm_numerics.h, compiled for the host) against the oracle.
+
+These are the encoders and exact-rounding routines the gfx950 kernels run; a
+g++ build of the same header lets the CPU suite check them without a GPU.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import route as R
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def hc():
+    path = os.path.join(HERE, "native", "libbsm_host_checks.so")
+    if not os.path.exists(path):
+        from tests.native.build_host_checks import build
+        build()
+    lib = ctypes.CDLL(path)
+    P = np.ctypeslib.ndpointer
+    lib.hc_e4m3_code.argtypes = [P(np.float32), ctypes.c_int64, P(np.uint8)]
+    lib.hc_e2m1_code.argtypes = [P(np.float32), ctypes.c_int64, P(np.uint8)]
+    lib.hc_e4m3_value.argtypes = [P(np.uint8), ctypes.c_int64, P(np.float32)]
+    lib.hc_e2m1_value.argtypes = [P(np.uint8), ctypes.c_int64, P(np.float32)]
+    lib.hc_exact_dot.argtypes = [P(np.float32), P(np.float32), ctypes.c_int64, ctypes.c_int64, P(np.float32)]
+    lib.hc_sigmoid.argtypes = [P(np.float32), ctypes.c_int64, P(np.float32), P(np.int32)]
+    lib.hc_sigmoid_dd.argtypes = [P(np.float32), ctypes.c_int64, P(np.float32)]
+    lib.hc_lsb_exp.argtypes = [ctypes.c_float]
+    lib.hc_lsb_exp.restype = ctypes.c_int
+    return lib
+
+
+def _probe(table, rng, n):
+    t = np.asarray(table, np.float64)
+    mids = ((t[1:] + t[:-1]) / 2).astype(np.float32)
+    parts = [mids, np.nextafter(mids, np.float32(1e30)), np.nextafter(mids, np.float32(0)), t.astype(np.float32),
+             rng.uniform(0, float(t[-1]) * 1.3, n).astype(np.float32),
+             (rng.uniform(0, 1, n) * 2.0 ** rng.integers(-40, 10, n)).astype(np.float32),
+             np.float32([0.0, np.inf, 1e30, 2.0 ** -149, 2.0 ** -126])]
+    return np.concatenate(parts).astype(np.float32)
+
+
+def test_e4m3_encoder_matches_oracle(hc):
+    rng = np.random.default_rng(0)
+    a = _probe(F.E4M3_MAGNITUDES, rng, 200000)
+    out = np.empty(a.size, np.uint8)
+    hc.hc_e4m3_code(a, a.size, out)
+    assert np.array_equal(out, F.e4m3_encode_magnitude(a))
+    codes = np.arange(127, dtype=np.uint8)
+    v = np.empty(127, np.float32)
+    hc.hc_e4m3_value(codes, 127, v)
+    assert np.array_equal(v, F.E4M3_MAGNITUDES.astype(np.float32))
+
+
+def test_e2m1_encoder_matches_oracle(hc):
+    rng = np.random.default_rng(1)
+    a = _probe(F.E2M1_MAGNITUDES, rng, 200000)
+    a = np.concatenate([a, np.float32([np.nan])])
+    out = np.empty(a.size, np.uint8)
+    hc.hc_e2m1_code(a, a.size, out)
+    assert np.array_equal(out, F.e2m1_encode_magnitude(a))
+    codes = np.arange(8, dtype=np.uint8)
+    v = np.empty(8, np.float32)
+    hc.hc_e2m1_value(codes, 8, v)
+    assert np.array_equal(v, F.E2M1_MAGNITUDES.astype(np.float32))
+
+
+def test_superaccumulator_exact_dot(hc):
+    rng = np.random.default_rng(2)
+    rows, n = 300, 512
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    w = (rng.standard_normal((rows, n)) * 0.05).astype(np.float32)
+    # adversarial rows: huge cancellation, ties at float32 midpoints, tiny and subnormal products
+    x[0, :3] = [2.0 ** 30, 1.0, -2.0 ** 30]
+    w[0, :3] = [1.0, 2.0 ** -40, 1.0]
+    x[0, 3:] = 0
+    x[1, :2] = [1.0, 2.0 ** -24]
+    w[1, :2] = [1.0, 1.0]
+    x[1, 2:] = 0
+    x[2] = np.float32(2.0 ** -120)
+    w[2] = np.float32(2.0 ** -100)
+    x[3] = -x[4]
+    w[3] = w[4]
+    x[5, :] = np.float32(3e38) * np.sign(rng.standard_normal(n)).astype(np.float32)
+    w[5, :] = np.float32(1e-38)
+    out = np.empty(rows, np.float32)
+    hc.hc_exact_dot(x, w, rows, n, out)
+    ref = np.array([R.logits_exact_f32(x[r:r + 1], w[r:r + 1])[0][0, 0] for r in range(rows)], np.float32)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    assert out[0] == np.float32(2.0 ** -40) and out[1] == 1.0
+
+
+def test_sigmoid_fast_path_and_dd_path_match_oracle(hc):
+    rng = np.random.default_rng(3)
+    l = np.concatenate([rng.standard_normal(200000) * 4, rng.uniform(-110, 30, 100000),
+                        np.float32([0, -0.0, 16, 17, 17.33, 17.4, 88, -87, -103, -104, -200, 800, -800])]).astype(np.float32)
+    ref, _ = R.sigmoid_exact_f32(l)
+    out = np.empty(l.size, np.float32)
+    fast = np.empty(l.size, np.int32)
+    hc.hc_sigmoid(l, l.size, out, fast)
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    # the double-double path alone must also be exactly rounded
+    sub = l[(l > -100) & (l < 25)][:20000]
+    dd = np.empty(sub.size, np.float32)
+    hc.hc_sigmoid_dd(sub, sub.size, dd)
+    ref2, _ = R.sigmoid_exact_f32(sub)
+    assert np.array_equal(dd.view(np.uint32), ref2.view(np.uint32))
+
+
+def test_lsb_exponent(hc):
+    assert hc.hc_lsb_exp(1.0) == 0
+    assert hc.hc_lsb_exp(1.5) == -1
+    assert hc.hc_lsb_exp(2.0 ** -149) == -149
+    assert hc.hc_lsb_exp(3.0 * 2.0 ** -140) == -140
+    assert hc.hc_lsb_exp(-6.0) == 1
