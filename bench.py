@@ -1,0 +1,265 @@
+"""Benchmark of the Beam-shaped NVFP4 / FP8 routed-expert MoE layer on one MI355X.
+
+One step = the whole hot path on one batch with inputs resident in HBM:
+group-limited sigmoid routing + activation quantization + expert MLP
+(permutation, gate/up GEMM + SwiGLU, h re-quantization, down GEMM, combine).
+Offline weight quantization happens once before timing.
+
+The headline line (``value``) is the 64-token decode layer in NVFP4 (hidden
+5120, 256 experts, 8 groups of 32, keep 4, top 8, intermediate 2560); the same
+run also measures the 8192-token prefill layer (Zipf-skewed router) and reports
+it under ``prefill_8192``.  Per-kernel times come from hipEvents recorded at
+the library's stage boundaries on the launch stream.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--fmt nvfp4|fp8]
+                       [--workload decode|prefill] [--no-prefill] [--no-cpu-baseline]
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_scaled_fp4_sigmoid_amd as bsm  # noqa: E402
+import workloads as W  # noqa: E402
+
+METRIC = "MoE-layer tokens/s + TFLOP/s & HBM GB/s (% roofline), decode-64 & prefill-8192"
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "f16": 2500.0}
+NVFP4_BYTES_PER_WEIGHT = 0.5625  # 4-bit code + one 1-byte E4M3 scale per 16 values
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its launch stream)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev.append(h.value)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) == 0
+        return float(out.value)
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
+def build_layer(cfg, fmt, dev):
+    x = torch.from_numpy(W.activations(cfg)).to(dev, torch.bfloat16)
+    wr = torch.from_numpy(W.router_weights(cfg)).to(dev, torch.bfloat16)
+    w13, w2 = W.expert_weights_device(cfg, device=dev)
+    weights = bsm.quantize_expert_weights(w13, w2, fmt)
+    torch.cuda.synchronize()
+    return x, wr, w13, w2, weights
+
+
+def run_steps(cfg, fmt, x, wr, weights, steps, warmup):
+    """Time ``steps`` whole-path steps; per-stage times from library stage events."""
+    T = x.shape[0]
+    out = torch.empty((T, cfg.H), dtype=torch.float32, device=x.device)
+    ws = None
+
+    def step():
+        nonlocal ws
+        ids, wts = bsm.route(x, wr, cfg.n_group, cfg.topk_group, cfg.topk)
+        xq = bsm.quantize_activations(x, fmt)
+        o, ws = bsm.moe_expert_mlp(weights, xq, ids, wts, cfg.combine_scale, out=out, ws=ws, return_workspace=True)
+        return ids
+
+    for _ in range(warmup):
+        ids = step()
+    torch.cuda.synchronize()
+    ev = HipEvents(steps * 6 + steps * 3)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        bsm.set_stage_events(1, ev.ev[steps * 6 + 3 * i: steps * 6 + 3 * i + 3])
+        bsm.set_stage_events(0, ev.ev[6 * i: 6 * i + 6])
+        ids = step()
+    stop.record()
+    torch.cuda.synchronize()
+    bsm.set_stage_events(0, [])
+    bsm.set_stage_events(1, [])
+    total_ms = start.elapsed_time(stop)
+    stages = {k: [] for k in ("route", "route_select", "permute", "gemm1", "hquant", "gemm2", "combine")}
+    for i in range(steps):
+        b = 6 * i
+        r = steps * 6 + 3 * i
+        stages["route"].append(ev.ms(r, r + 2))
+        stages["route_select"].append(ev.ms(r + 1, r + 2))
+        stages["permute"].append(ev.ms(b, b + 1))
+        stages["gemm1"].append(ev.ms(b + 1, b + 2))
+        stages["hquant"].append(ev.ms(b + 2, b + 3))
+        stages["gemm2"].append(ev.ms(b + 3, b + 4))
+        stages["combine"].append(ev.ms(b + 4, b + 5))
+    ev.close()
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=cfg.E)
+    return total_ms / steps, {k: float(np.mean(v)) for k, v in stages.items()}, counts
+
+
+def layer_numbers(cfg, fmt, T, ms, stage_ms, counts):
+    P = T * cfg.topk
+    n_act = int((counts > 0).sum())
+    flop = 2.0 * P * 3 * cfg.H * cfg.I + 2.0 * T * cfg.E * cfg.H
+    wbytes_per_expert = 3 * cfg.H * cfg.I * (NVFP4_BYTES_PER_WEIGHT if fmt == "nvfp4" else 1.0) + \
+        (0 if fmt == "nvfp4" else 4 * (2 * cfg.I + cfg.H))
+    layer_bytes = n_act * wbytes_per_expert + T * cfg.H * 2 + cfg.E * cfg.H * 2 + T * cfg.H * 4
+    # dominant kernel: gate/up GEMM.  Algorithmic bytes per launch: the gate+up weights of
+    # every active expert, the quantized activations it reads, the FP32 h it writes.
+    g1_w = 2 * cfg.I * cfg.H * (NVFP4_BYTES_PER_WEIGHT if fmt == "nvfp4" else 1.0) + \
+        (0 if fmt == "nvfp4" else 4 * 2 * cfg.I)
+    g1_bytes = n_act * g1_w + T * cfg.H * (NVFP4_BYTES_PER_WEIGHT if fmt == "nvfp4" else 1.0) + P * cfg.I * 4
+    g1_flop = 2.0 * P * 2 * cfg.I * cfg.H
+    g1_ms = stage_ms["gemm1"]
+    return {
+        "tokens_per_s": T / (ms * 1e-3),
+        "ms_per_step": ms,
+        "tflops": flop / (ms * 1e-3) / 1e12,
+        "gbps": layer_bytes / (ms * 1e-3) / 1e9,
+        "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "active_experts": n_act,
+        "max_expert_rows": int(counts.max()),
+        "layer_flop": flop,
+        "layer_bytes": layer_bytes,
+        "stage_ms": stage_ms,
+        "gemm1": {"ms": g1_ms, "bytes": g1_bytes, "flop": g1_flop,
+                  "gbps": g1_bytes / (g1_ms * 1e-3) / 1e9, "tflops": g1_flop / (g1_ms * 1e-3) / 1e12},
+    }
+
+
+def cpu_baseline(cfg, fmt, w13, w2, x_np, wr_np):
+    """The CPU oracle, timed on a bounded sample: the full routing of the batch plus the
+    expert MLP of the first token (its experts quantized by the oracle beforehand, untimed)."""
+    from oracle import moe as OM
+    from oracle import route as OR
+
+    ids, wts, _, _ = OR.route(x_np, wr_np, cfg.n_group, cfg.topk_group, cfg.topk)
+    cls = OM.NVFP4Expert if fmt == "nvfp4" else OM.FP8Expert
+    tok = 1
+    need = sorted(set(int(e) for e in ids[:tok].ravel()))
+    experts = {}
+    for e in need:
+        experts[e] = cls(w13[e, :cfg.I].float().cpu().numpy(), w13[e, cfg.I:].float().cpu().numpy(),
+                         w2[e].float().cpu().numpy())
+    t0 = time.perf_counter()
+    OR.route(x_np, wr_np, cfg.n_group, cfg.topk_group, cfg.topk)
+    t_route = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    xq, xh = OM.quantize_activations(x_np[:tok], fmt)
+    OM.moe_expert_mlp(xh, ids[:tok], wts[:tok], experts, fmt, cfg.combine_scale)
+    t_mlp = time.perf_counter() - t1
+    per_token = t_route / x_np.shape[0] + t_mlp / tok
+    threads = len(os.sched_getaffinity(0))
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"routing of all {x_np.shape[0]} tokens ({t_route:.2f} s) + quantize and expert MLP of "
+                      f"{tok} token ({len(need)} experts, {t_mlp:.2f} s); numpy float64 on {threads} host threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "fp8"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs the MI355X"
+    dev = torch.device("cuda:0")
+    bsm.load()
+
+    main_cfg = W.DECODE if args.workload == "decode" else W.PREFILL
+    x, wr, w13, w2, weights = build_layer(main_cfg, args.fmt, dev)
+    ms, stage_ms, counts = run_steps(main_cfg, args.fmt, x, wr, weights, args.steps, args.warmup)
+    main_nums = layer_numbers(main_cfg, args.fmt, main_cfg.T, ms, stage_ms, counts)
+    print(f"[bench] {main_cfg.name} {args.fmt}: {ms:.3f} ms/step, stages {stage_ms}", file=sys.stderr, flush=True)
+
+    g1 = main_nums["gemm1"]
+    roofline = {"bound": "hbm", "achieved": round(g1["gbps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(g1["gbps"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gate/up GEMM + SwiGLU",
+                "algorithmic_bytes_per_launch": int(g1["bytes"]), "avg_launch_ms": round(g1["ms"], 4)}
+
+    prefill = None
+    if args.workload == "decode" and not args.no_prefill:
+        del weights, w13, w2
+        torch.cuda.empty_cache()
+        pcfg = W.PREFILL
+        px, pwr, pw13, pw2, pweights = build_layer(pcfg, args.fmt, dev)
+        psteps = max(3, args.steps // 4)
+        pms, pst, pcounts = run_steps(pcfg, args.fmt, px, pwr, pweights, psteps, 2)
+        pn = layer_numbers(pcfg, args.fmt, pcfg.T, pms, pst, pcounts)
+        print(f"[bench] prefill {args.fmt}: {pms:.3f} ms/step, stages {pst}", file=sys.stderr, flush=True)
+        mm = "fp4" if args.fmt == "nvfp4" else "fp8"
+        prefill = {
+            "tokens_per_s": round(pn["tokens_per_s"], 1), "ms_per_step": round(pms, 4),
+            "tflops": round(pn["tflops"], 2), "frac_fp4_or_fp8_peak": round(pn["tflops"] / PEAK_TFLOPS[mm], 4),
+            "frac_f16_mfma_peak": round(pn["tflops"] / PEAK_TFLOPS["f16"], 4), "gbps": round(pn["gbps"], 1),
+            "active_experts": pn["active_experts"], "max_expert_rows": pn["max_expert_rows"],
+            "stage_ms": {k: round(v, 4) for k, v in pst.items()},
+            "gemm1": {k: round(v, 3) for k, v in pn["gemm1"].items()},
+            "steps": psteps,
+        }
+        del pweights, pw13, pw2
+        torch.cuda.empty_cache()
+        w13 = w2 = None
+
+    cpu = None
+    if not args.no_cpu_baseline and args.workload == "decode":
+        if w13 is None:
+            w13, w2 = W.expert_weights_device(main_cfg, device=dev)
+        cpu = cpu_baseline(main_cfg, args.fmt, w13, w2, W.activations(main_cfg), W.router_weights(main_cfg))
+
+    line = {
+        "metric": METRIC,
+        "value": round(main_nums["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4-e2m1 (exact f16 mfma, f32 acc)" if args.fmt == "nvfp4" else "fp8-e4m3 (fp8 mfma, f32 acc)",
+        "data": "synthetic (seeded Beam-shaped activations, router and expert weights)",
+        "config": {"workload": f"beam-{main_cfg.name}-{main_cfg.T} {args.fmt} MoE layer", "T": main_cfg.T,
+                   "H": main_cfg.H, "I": main_cfg.I, "E": main_cfg.E, "n_group": main_cfg.n_group,
+                   "topk_group": main_cfg.topk_group, "topk": main_cfg.topk, "combine_scale": main_cfg.combine_scale,
+                   "active_experts": main_nums["active_experts"], "parallelism": "single GPU"},
+        "tflops": round(main_nums["tflops"], 3),
+        "gbps": round(main_nums["gbps"], 1),
+        "hbm_frac": round(main_nums["hbm_frac"], 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "prefill_8192": prefill,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -74,6 +74,7 @@ def load():
         "bsm_moe_workspace_layout": (i32, [i32, i64, i64, i64, i64, i32, ctypes.POINTER(_WsLayout)]),
         "bsm_moe_expert_mlp": (i32, [ctypes.POINTER(_MoeWeights), ctypes.POINTER(_ActQ), i64, vp, vp, i32, f32, i32,
                                      vp, vp, vp, sz, vp]),
+        "bsm_set_stage_events": (i32, [i32, ctypes.POINTER(vp), i32]),
         "bsm_rmsnorm_f32": (i32, [vp, i64, i64, f32, vp, vp]),
         "bsm_scaled_residual_f32": (i32, [vp, vp, f32, f32, i64, i64, vp]),
     }
@@ -305,6 +306,14 @@ def moe_layer(x, w_router, weights: ExpertWeights, n_group, topk_group, topk, co
     xq = quantize_activations(x, fmt)
     out = moe_expert_mlp(weights, xq, ids, wts, combine_scale)
     return out, ids, wts
+
+
+def set_stage_events(which: int, handles):
+    """Record caller-owned hipEvent_t ``handles`` at stage boundaries (see bsmoe.h); [] stops."""
+    lib = load()
+    n = len(handles)
+    arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(h) for h in handles])
+    _check(lib.bsm_set_stage_events(which, arr if n else None, n))
 
 
 # ---------------------------------------------------------------------------

@@ -12,6 +12,7 @@
 namespace {
 
 thread_local char g_err[512] = {0};
+thread_local bsm::StageEvents g_stage[2];
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -44,6 +45,10 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 }
 
 }  // namespace
+
+namespace bsm {
+StageEvents& stage_events(int which) { return g_stage[which]; }
+}  // namespace bsm
 
 extern "C" {
 
@@ -184,7 +189,7 @@ int bsm_moe_expert_mlp(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T,
   const bool nv = w->format == BSM_FMT_NVFP4;
   const int64_t E = w->E, H = w->H, I = w->I;
   if (E <= 0 || H <= 0 || I <= 0 || T < 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
-  if (H % 128 != 0 || I % 128 != 0) return fail(BSM_ERR_UNSUPPORTED, "H and I must be multiples of 128");
+  if (H % 256 != 0 || I % 128 != 0) return fail(BSM_ERR_UNSUPPORTED, "H must be a multiple of 256 and I of 128");
   if (E > 1024) return fail(BSM_ERR_UNSUPPORTED, "E > 1024");
   if (topk < 1 || topk > 32 || topk > E) return fail(BSM_ERR_INVALID_ARG, "topk must be in [1, min(32, E)]");
   if (T * topk > 0x3FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "T * topk too large");
@@ -225,6 +230,17 @@ int bsm_moe_expert_mlp(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T,
   a.out = out;
   a.ws = (uint8_t*)ws;
   return hip_status(bsm::launch_moe(a, (hipStream_t)stream), "bsm_moe_expert_mlp");
+}
+
+int bsm_set_stage_events(int which, void* const* events, int n) {
+  if (which != 0 && which != 1) return fail(BSM_ERR_INVALID_ARG, "which must be 0 (moe) or 1 (route)");
+  const int need = which == 0 ? 6 : 3;
+  if (n != 0 && n != need) return fail(BSM_ERR_INVALID_ARG, "n must be 0 or %d", need);
+  if (n && !events) return fail(BSM_ERR_INVALID_ARG, "NULL events");
+  bsm::StageEvents& s = bsm::stage_events(which);
+  for (int i = 0; i < n; ++i) s.ev[i] = (hipEvent_t)events[i];
+  s.n = n;
+  return ok();
 }
 
 int bsm_rmsnorm_f32(const float* x, int64_t T, int64_t H, float eps, float* y, bsm_stream_t stream) {

@@ -26,14 +26,16 @@ hipError_t launch_nvfp4_quantize(const void* x, bool x_bf16, int64_t B, int64_t 
                                  hipStream_t st);
 // same, with the global amax already known (bits of a non-negative float at
 // amax_bits, one per tensor) -- used for h whose amax comes from the GEMM epilogue
+// dec16 (optional): also writes the exact FP16 values q * s_b (global scale not applied)
 hipError_t launch_nvfp4_quantize_from_amax(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C,
                                            uint8_t* codes, uint8_t* scales, float* gs,
                                            const uint32_t* amax_bits, const float* static_gs,
-                                           hipStream_t st);
+                                           hipStream_t st, _Float16* dec16 = nullptr);
 hipError_t launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t B,
                                    int64_t R, int64_t C, float* out, hipStream_t st);
+// dec16 (optional): also writes the exact FP16 values of the E4M3 codes (row scale not applied)
 hipError_t launch_fp8_quantize(const void* x, bool x_bf16, int64_t R, int64_t C, uint8_t* codes, float* scales,
-                               hipStream_t st);
+                               hipStream_t st, _Float16* dec16 = nullptr);
 
 // ---- router ---------------------------------------------------------------
 size_t route_ws(int64_t T, int64_t H, int64_t E);
@@ -47,7 +49,7 @@ hipError_t launch_route_diag(const void* ws, int64_t T, int64_t H, int64_t E, in
 struct MoeLayout {
   size_t total, counts, offsets, row_pair, pair_row, tiles, h_f32, h_codes, h_scales, h_gs, y_f32, scratch;
   // scratch sub-buffers
-  size_t sel_masks, chunk_cnt, chunk_base, ntiles, h_amax;
+  size_t sel_masks, chunk_cnt, chunk_base, ntiles, h_amax, act_f16, h_f16;
   int64_t P, n_chunks, max_tiles;
 };
 MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int topk);
@@ -74,6 +76,18 @@ struct MoeArgs {
   uint8_t* ws;
 };
 hipError_t launch_moe(const MoeArgs& a, hipStream_t st);
+
+// ---- stage events (profiling aid) -----------------------------------------
+constexpr int kMaxStageEvents = 8;
+struct StageEvents {
+  hipEvent_t ev[kMaxStageEvents];
+  int n = 0;
+};
+StageEvents& stage_events(int which);  // thread-local, which = 0 (moe) or 1 (route)
+inline void stage_mark(int which, int i, hipStream_t st) {
+  StageEvents& s = stage_events(which);
+  if (i < s.n) (void)hipEventRecord(s.ev[i], st);
+}
 
 // ---- norm / residual ------------------------------------------------------
 hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t H, float eps, float* y, hipStream_t st);

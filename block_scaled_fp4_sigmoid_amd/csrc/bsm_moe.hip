@@ -47,37 +47,11 @@ namespace {
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
-typedef int i8v __attribute__((ext_vector_type(8)));
 
 constexpr int kRowsPerTile = 16;
 constexpr int kChunk = 64;  // tokens per permutation chunk
 
 // FP16 high bytes of the E2M1 magnitudes {0, .5, 1, 1.5 | 2, 3, 4, 6}
-constexpr uint32_t kLutLo = 0x3E3C3800u;
-constexpr uint32_t kLutHi = 0x46444240u;
-
-__device__ inline uint32_t pack_pair(uint32_t hbe, uint32_t hbo, uint32_t j) {
-  // bytes [0, hbe_j, 0, hbo_j]: FP16 (even element) low half, (odd element) high half
-  // selector bytes (LSB first): 0x0C -> 0x00, j -> byte j of hbe, 4+j -> byte j of hbo
-  return __builtin_amdgcn_perm(hbo, hbe, 0x000C000Cu | (j << 8) | ((4u + j) << 24));
-}
-
-// 8 E2M1 codes (element i in nibble i of w) times the block scale, as FP16 (exact).
-__device__ inline h8v decode8(uint32_t w, h2v s2) {
-  const uint32_t ev = w & 0x0F0F0F0Fu;
-  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;
-  const uint32_t hbe = __builtin_amdgcn_perm(kLutHi, kLutLo, ev & 0x07070707u) | ((ev & 0x08080808u) << 4);
-  const uint32_t hbo = __builtin_amdgcn_perm(kLutHi, kLutLo, od & 0x07070707u) | ((od & 0x08080808u) << 4);
-  h8v r;
-#pragma unroll
-  for (uint32_t j = 0; j < 4; ++j) {
-    const h2v p = __builtin_bit_cast(h2v, pack_pair(hbe, hbo, j)) * s2;
-    r[2 * j] = p[0];
-    r[2 * j + 1] = p[1];
-  }
-  return r;
-}
-
 __device__ inline h2v scale_pair(uint32_t code) {
   const _Float16 s = (_Float16)e4m3_value_mag(code);  // exact in FP16
   return h2v{s, s};
@@ -85,37 +59,10 @@ __device__ inline h2v scale_pair(uint32_t code) {
 
 __device__ inline f4v mfma_f16(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-__device__ inline f4v mfma_fp8(i8v a, i8v b, f4v c) {
-  // E4M3 x E4M3 (format 0 for both operands), unit E8M0 block scales (127)
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-
 __device__ inline float wave_max_f(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
-}
-
-// 32 NVFP4 values (16 code bytes + 2 scale bytes) -> 4 FP16 octets, k order preserved
-struct Nv32 {
-  h8v q[4];
-};
-__device__ inline Nv32 load_nv32(const uint8_t* codes, const uint8_t* scales) {
-  const uint4 c = *reinterpret_cast<const uint4*>(codes);
-  const uint32_t s = *reinterpret_cast<const uint16_t*>(scales);
-  const h2v s0 = scale_pair(s & 0xFFu), s1 = scale_pair(s >> 8);
-  Nv32 r;
-  r.q[0] = decode8(c.x, s0);
-  r.q[1] = decode8(c.y, s0);
-  r.q[2] = decode8(c.z, s1);
-  r.q[3] = decode8(c.w, s1);
-  return r;
-}
-
-__device__ inline i8v load_fp8_32(const uint8_t* p) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
-  return i8v{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
 __device__ inline float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
@@ -204,165 +151,243 @@ __global__ __launch_bounds__(256) void k_perm_rows(const int32_t* __restrict__ i
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4 grouped GEMMs
+// Operand decoding to FP16 (exact)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_gemm1_nvfp4(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
-                                                     const float* __restrict__ xgs, const uint8_t* __restrict__ wc,
-                                                     const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
-                                                     const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-                                                     const int* __restrict__ row_pair, int topk, int64_t H,
-                                                     int64_t I, float* __restrict__ h_out,
-                                                     uint32_t* __restrict__ h_amax) {
+// E2M1 x E4M3 block scale: the hardware FP4 -> FP16 converter (unit scale; it
+// uses only the exponent of its scale operand) gives q exactly, one packed
+// FP16 multiply by s_b gives q * s_b exactly (<= 6 significant bits, within
+// [2^-10, 2688]).  E4M3 -> FP16 is exact with the FP8 converter.
+__device__ inline h8v dec_fp4x8(uint32_t w, h2v s2) {
+  h8v r;
+  const h2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const h2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const h2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const h2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+__device__ inline h8v dec_fp8x8(uint32_t w0, uint32_t w1) {
+  h8v r;
+  const h2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const h2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const h2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const h2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Activations -> FP16 [T, H]: NVFP4 q * s_b (global scale applied later), FP8 q.
+template <bool NV>
+__global__ __launch_bounds__(256) void k_decode_act(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                    int64_t n_blk, _Float16* __restrict__ out) {
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-value block
+  if (f >= n_blk) return;
+  uint4 o0, o1;
+  if (NV) {
+    const uint2 c = *reinterpret_cast<const uint2*>(codes + f * 8);
+    const h2v s2 = scale_pair(scales[f]);
+    const h8v a = dec_fp4x8(c.x, s2), b = dec_fp4x8(c.y, s2);
+    o0 = __builtin_bit_cast(uint4, a);
+    o1 = __builtin_bit_cast(uint4, b);
+  } else {
+    const uint4 c = *reinterpret_cast<const uint4*>(codes + f * 16);
+    o0 = __builtin_bit_cast(uint4, dec_fp8x8(c.x, c.y));
+    o1 = __builtin_bit_cast(uint4, dec_fp8x8(c.z, c.w));
+  }
+  uint4* op = reinterpret_cast<uint4*>(out + f * 16);
+  op[0] = o0;
+  op[1] = o1;
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM for few rows per expert ("skinny"): weights stream from HBM
+// straight into registers, each weight element is decoded exactly once per
+// row tile.  One wave = 16 rows x 4 weight-row tiles of 16 over all of K.
+// Lane (m, g): row m of the tile, k-range [k0 + KG*g, k0 + KG*(g+1)) of each
+// super-step of 4*KG; MFMA step j feeds lane group g's values j*8 .. j*8+7 of
+// that range for both operands, so A and B agree on the k order.
+// ---------------------------------------------------------------------------
+constexpr int kNT = 4;  // weight-row tiles of 16 per wave
+
+template <bool NV, int KG>
+struct BChunk {
+  // NVFP4: KG/2 code bytes + KG/16 scale bytes per lane; FP8: KG code bytes
+  static constexpr int kCodeVec = NV ? KG / 32 : KG / 16;  // uint4 per lane
+  uint4 c[kCodeVec];
+  uint32_t s[NV ? (KG / 16 + 3) / 4 : 1];
+};
+
+template <bool NV, int KG>
+__device__ inline void load_b(const uint8_t* codes_row, const uint8_t* scales_row, int64_t k, BChunk<NV, KG>& b) {
+  const uint4* p = reinterpret_cast<const uint4*>(codes_row + (NV ? k / 2 : k));
+#pragma unroll
+  for (int i = 0; i < BChunk<NV, KG>::kCodeVec; ++i) b.c[i] = p[i];
+  if (NV) {
+    if (KG >= 64) {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(scales_row + k / 16);
+#pragma unroll
+      for (int i = 0; i < KG / 64; ++i) b.s[i] = q[i];
+    } else {
+      b.s[0] = *reinterpret_cast<const uint16_t*>(scales_row + k / 16);
+    }
+  }
+}
+
+// MFMA step j (8 k-values) of a B chunk, decoded to FP16
+template <bool NV, int KG>
+__device__ inline h8v b_step(const BChunk<NV, KG>& b, int j) {
+  if (NV) {
+    const uint4 c = b.c[j >> 2];
+    const uint32_t w = (j & 3) == 0 ? c.x : (j & 3) == 1 ? c.y : (j & 3) == 2 ? c.z : c.w;
+    const int blk = j >> 1;  // 16 values per scale
+    const uint32_t sb = (b.s[blk >> 2] >> (8 * (blk & 3))) & 0xFFu;
+    return dec_fp4x8(w, scale_pair(sb));
+  } else {
+    const uint4 c = b.c[j >> 1];
+    return (j & 1) ? dec_fp8x8(c.z, c.w) : dec_fp8x8(c.x, c.y);
+  }
+}
+
+template <int KG>
+__device__ inline void load_a(const _Float16* row, int64_t k, h8v* a) {
+  const uint4* p = reinterpret_cast<const uint4*>(row + k);
+#pragma unroll
+  for (int j = 0; j < KG / 8; ++j) a[j] = __builtin_bit_cast(h8v, p[j]);
+}
+
+// GEMM1: rows = gathered tokens of an expert; tiles 0,1 = gate rows n0..n0+31,
+// tiles 2,3 = up rows I+n0..I+n0+31.  Epilogue h = silu(g) * u.
+template <bool NV, int KG>
+__global__ __launch_bounds__(256) void k_gemm1_skinny(const _Float16* __restrict__ act, const float* __restrict__ xgs,
+                                                      const float* __restrict__ xrs, const uint8_t* __restrict__ wc,
+                                                      const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
+                                                      const int4* __restrict__ tiles, const int* __restrict__ ntiles,
+                                                      const int* __restrict__ row_pair, int topk, int64_t H, int64_t I,
+                                                      float* __restrict__ h_out, uint32_t* __restrict__ h_amax) {
   if ((int)blockIdx.y >= *ntiles) return;
   const int4 ti = tiles[blockIdx.y];
   const int e = ti.x, row0 = ti.y, nrows = ti.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 16;
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 32;
   const int m = lane & 15, g = lane >> 4;
   const int t = row_pair[row0 + (m < nrows ? m : 0)] / topk;
-  const uint8_t* ac = xc + (int64_t)t * (H / 2) + 16 * g;
-  const uint8_t* as = xs + (int64_t)t * (H / 16) + 2 * g;
-  const int64_t rg = (int64_t)e * 2 * I + n0 + m, ru = rg + I;
-  const uint8_t* gc = wc + rg * (H / 2) + 16 * g;
-  const uint8_t* gs = wsc + rg * (H / 16) + 2 * g;
-  const uint8_t* uc = wc + ru * (H / 2) + 16 * g;
-  const uint8_t* us = wsc + ru * (H / 16) + 2 * g;
-  f4v accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = 0; k0 < H; k0 += 128) {
-    const int64_t cb = k0 / 2, sb = k0 / 16;
-    const Nv32 a = load_nv32(ac + cb, as + sb);
-    const Nv32 bg = load_nv32(gc + cb, gs + sb);
-    const Nv32 bu = load_nv32(uc + cb, us + sb);
+  const _Float16* arow = act + (int64_t)t * H + KG * g;
+  const int64_t cbytes = NV ? H / 2 : H;  // code bytes per weight row
+  const uint8_t* crow[kNT];
+  const uint8_t* srow[kNT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      accg = mfma_f16(a.q[s], bg.q[s], accg);
-      accu = mfma_f16(a.q[s], bu.q[s], accu);
-    }
+  for (int j = 0; j < kNT; ++j) {
+    const int64_t r = (int64_t)e * 2 * I + (j >= 2 ? I : 0) + n0 + 16 * (j & 1) + m;
+    crow[j] = wc + r * cbytes + (NV ? KG / 2 : KG) * g;
+    srow[j] = NV ? wsc + r * (H / 16) + (KG / 16) * g : nullptr;
   }
-  const float sg = xgs[0] * wgs[2 * e], su = xgs[0] * wgs[2 * e + 1];
+  f4v acc[kNT];
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
+  for (int64_t k0 = 0; k0 < H; k0 += 4 * KG) {
+    h8v a[KG / 8];
+    BChunk<NV, KG> b[kNT];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) load_b<NV, KG>(crow[j], srow[j], k0 * 0, b[j]);
+    load_a<KG>(arow, k0, a);
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) {
+      crow[j] += NV ? 2 * KG : 4 * KG;
+      if (NV) srow[j] += KG / 4;
+    }
+#pragma unroll
+    for (int s = 0; s < KG / 8; ++s)
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) acc[j] = mfma_f16(a[s], b_step<NV, KG>(b[j], s), acc[j]);
+  }
   float hmax = 0.0f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int ro = 4 * g + r;
-    if (ro < nrows) {
-      const float h = silu_mul(accg[r] * sg, accu[r] * su);
-      h_out[(int64_t)(row0 + ro) * I + n0 + m] = h;
-      hmax = fmaxf(hmax, fabsf(h));
+    if (ro >= nrows) continue;
+    float sgx, sux, sgy, suy;
+    if (NV) {
+      sgx = sgy = xgs[0] * wgs[2 * e];
+      sux = suy = xgs[0] * wgs[2 * e + 1];
+    } else {
+      const float sx = xrs[row_pair[row0 + ro] / topk];
+      const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
+      sgx = sx * ws[n0 + m];
+      sgy = sx * ws[n0 + 16 + m];
+      sux = sx * ws[I + n0 + m];
+      suy = sx * ws[I + n0 + 16 + m];
     }
+    const float h0 = silu_mul(acc[0][r] * sgx, acc[2][r] * sux);
+    const float h1 = silu_mul(acc[1][r] * sgy, acc[3][r] * suy);
+    float* hr = h_out + (int64_t)(row0 + ro) * I + n0 + m;
+    hr[0] = h0;
+    hr[16] = h1;
+    hmax = fmaxf(hmax, fmaxf(fabsf(h0), fabsf(h1)));
   }
-  hmax = wave_max_f(hmax);
-  if (lane == 0) atomicMax(h_amax, f2u(hmax));
+  if (NV) {
+    hmax = wave_max_f(hmax);
+    if (lane == 0) atomicMax(h_amax, f2u(hmax));
+  }
 }
 
-__global__ __launch_bounds__(256) void k_gemm2_nvfp4(const uint8_t* __restrict__ hc, const uint8_t* __restrict__ hs,
-                                                     const float* __restrict__ hgs, const uint8_t* __restrict__ wc,
-                                                     const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
-                                                     const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-                                                     int64_t H, int64_t I, float* __restrict__ y) {
+// GEMM2: rows = sorted (token, slot) rows of an expert, A = decoded h; 64 output columns per wave.
+template <bool NV, int KG>
+__global__ __launch_bounds__(256) void k_gemm2_skinny(const _Float16* __restrict__ hact, const float* __restrict__ hgs,
+                                                      const float* __restrict__ hrs, const uint8_t* __restrict__ wc,
+                                                      const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
+                                                      const int4* __restrict__ tiles, const int* __restrict__ ntiles,
+                                                      int64_t H, int64_t I, float* __restrict__ y) {
   if ((int)blockIdx.y >= *ntiles) return;
   const int4 ti = tiles[blockIdx.y];
   const int e = ti.x, row0 = ti.y, nrows = ti.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 32;
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
   const int m = lane & 15, g = lane >> 4;
-  const int64_t ar = row0 + (m < nrows ? m : 0);
-  const uint8_t* ac = hc + ar * (I / 2) + 16 * g;
-  const uint8_t* as = hs + ar * (I / 16) + 2 * g;
-  const int64_t r0 = (int64_t)e * H + n0 + m, r1 = r0 + 16;
-  const uint8_t* b0c = wc + r0 * (I / 2) + 16 * g;
-  const uint8_t* b0s = wsc + r0 * (I / 16) + 2 * g;
-  const uint8_t* b1c = wc + r1 * (I / 2) + 16 * g;
-  const uint8_t* b1s = wsc + r1 * (I / 16) + 2 * g;
-  f4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = 0; k0 < I; k0 += 128) {
-    const int64_t cb = k0 / 2, sb = k0 / 16;
-    const Nv32 a = load_nv32(ac + cb, as + sb);
-    const Nv32 b0 = load_nv32(b0c + cb, b0s + sb);
-    const Nv32 b1 = load_nv32(b1c + cb, b1s + sb);
+  const _Float16* arow = hact + (int64_t)(row0 + (m < nrows ? m : 0)) * I + KG * g;
+  const int64_t cbytes = NV ? I / 2 : I;
+  const uint8_t* crow[kNT];
+  const uint8_t* srow[kNT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      acc0 = mfma_f16(a.q[s], b0.q[s], acc0);
-      acc1 = mfma_f16(a.q[s], b1.q[s], acc1);
-    }
+  for (int j = 0; j < kNT; ++j) {
+    const int64_t r = (int64_t)e * H + n0 + 16 * j + m;
+    crow[j] = wc + r * cbytes + (NV ? KG / 2 : KG) * g;
+    srow[j] = NV ? wsc + r * (I / 16) + (KG / 16) * g : nullptr;
   }
-  const float sc = hgs[0] * wgs[e];
+  f4v acc[kNT];
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
+  for (int64_t k0 = 0; k0 < I; k0 += 4 * KG) {
+    h8v a[KG / 8];
+    BChunk<NV, KG> b[kNT];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) load_b<NV, KG>(crow[j], srow[j], 0, b[j]);
+    load_a<KG>(arow, k0, a);
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) {
+      crow[j] += NV ? 2 * KG : 4 * KG;
+      if (NV) srow[j] += KG / 4;
+    }
+#pragma unroll
+    for (int s = 0; s < KG / 8; ++s)
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) acc[j] = mfma_f16(a[s], b_step<NV, KG>(b[j], s), acc[j]);
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int ro = 4 * g + r;
-    if (ro < nrows) {
-      float* yr = y + (int64_t)(row0 + ro) * H + n0 + m;
-      yr[0] = acc0[r] * sc;
-      yr[16] = acc1[r] * sc;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// FP8 grouped GEMMs
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_gemm1_fp8(const uint8_t* __restrict__ xc, const float* __restrict__ xs,
-                                                   const uint8_t* __restrict__ wc, const float* __restrict__ wsc,
-                                                   const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-                                                   const int* __restrict__ row_pair, int topk, int64_t H, int64_t I,
-                                                   float* __restrict__ h_out) {
-  if ((int)blockIdx.y >= *ntiles) return;
-  const int4 ti = tiles[blockIdx.y];
-  const int e = ti.x, row0 = ti.y, nrows = ti.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 16;
-  const int m = lane & 15, g = lane >> 4;
-  const int t = row_pair[row0 + (m < nrows ? m : 0)] / topk;
-  const uint8_t* ap = xc + (int64_t)t * H + 32 * g;
-  const int64_t rg = (int64_t)e * 2 * I + n0 + m, ru = rg + I;
-  const uint8_t* gp = wc + rg * H + 32 * g;
-  const uint8_t* up = wc + ru * H + 32 * g;
-  f4v accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = 0; k0 < H; k0 += 128) {
-    const i8v a = load_fp8_32(ap + k0);
-    accg = mfma_fp8(a, load_fp8_32(gp + k0), accg);
-    accu = mfma_fp8(a, load_fp8_32(up + k0), accu);
-  }
-  const float swg = wsc[rg], swu = wsc[ru];
+    if (ro >= nrows) continue;
+    float* yr = y + (int64_t)(row0 + ro) * H + n0 + m;
+    if (NV) {
+      const float sc = hgs[0] * wgs[e];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ro = 4 * g + r;
-    if (ro < nrows) {
-      const float sx = xs[row_pair[row0 + ro] / topk];
-      h_out[(int64_t)(row0 + ro) * I + n0 + m] = silu_mul(accg[r] * sx * swg, accu[r] * sx * swu);
-    }
-  }
-}
-
-__global__ __launch_bounds__(256) void k_gemm2_fp8(const uint8_t* __restrict__ hc, const float* __restrict__ hs,
-                                                   const uint8_t* __restrict__ wc, const float* __restrict__ wsc,
-                                                   const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-                                                   int64_t H, int64_t I, float* __restrict__ y) {
-  if ((int)blockIdx.y >= *ntiles) return;
-  const int4 ti = tiles[blockIdx.y];
-  const int e = ti.x, row0 = ti.y, nrows = ti.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 32;
-  const int m = lane & 15, g = lane >> 4;
-  const int64_t ar = row0 + (m < nrows ? m : 0);
-  const uint8_t* ap = hc + ar * I + 32 * g;
-  const int64_t r0 = (int64_t)e * H + n0 + m, r1 = r0 + 16;
-  const uint8_t* b0 = wc + r0 * I + 32 * g;
-  const uint8_t* b1 = wc + r1 * I + 32 * g;
-  f4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = 0; k0 < I; k0 += 128) {
-    const i8v a = load_fp8_32(ap + k0);
-    acc0 = mfma_fp8(a, load_fp8_32(b0 + k0), acc0);
-    acc1 = mfma_fp8(a, load_fp8_32(b1 + k0), acc1);
-  }
-  const float s0 = wsc[r0], s1 = wsc[r1];
+      for (int j = 0; j < kNT; ++j) yr[16 * j] = acc[j][r] * sc;
+    } else {
+      const float sa = hrs[row0 + ro];
+      const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * H + n0 + m;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ro = 4 * g + r;
-    if (ro < nrows) {
-      const float sa = hs[row0 + ro];
-      float* yr = y + (int64_t)(row0 + ro) * H + n0 + m;
-      yr[0] = acc0[r] * sa * s0;
-      yr[16] = acc1[r] * sa * s1;
+      for (int j = 0; j < kNT; ++j) yr[16 * j] = acc[j][r] * sa * ws[16 * j];
     }
   }
 }
@@ -416,6 +441,8 @@ MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int
   L.h_scales = take(nvfp4 ? (size_t)L.P * I / 16 : sizeof(float) * L.P);
   L.h_gs = take(sizeof(float));
   L.y_f32 = take(sizeof(float) * L.P * H);
+  L.act_f16 = take(2 * (size_t)T * H);
+  L.h_f16 = take(2 * (size_t)L.P * I);
   L.scratch = o;
   L.sel_masks = take(sizeof(uint64_t) * E * L.n_chunks);
   L.chunk_cnt = take(sizeof(int) * E * L.n_chunks);
@@ -446,35 +473,55 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   int* ntiles = reinterpret_cast<int*>(ws + L.ntiles);
   uint32_t* h_amax = reinterpret_cast<uint32_t*>(ws + L.h_amax);
 
+  stage_mark(0, 0, st);
   k_perm_masks<<<(unsigned)L.n_chunks, 64, 0, st>>>(a.ids, a.T, a.topk, a.E, L.n_chunks, masks, ccnt);
   k_perm_scan<<<1, 1024, 0, st>>>(ccnt, a.E, L.n_chunks, cbase, counts, offsets, tiles, ntiles, h_amax);
   k_perm_rows<<<(unsigned)((L.P + 255) / 256), 256, 0, st>>>(a.ids, L.P, a.topk, L.n_chunks, masks, cbase, offsets,
                                                               row_pair, pair_row);
-  const dim3 g1((unsigned)(a.I / 64), (unsigned)L.max_tiles);
-  const dim3 g2((unsigned)(a.H / 128), (unsigned)L.max_tiles);
+  const dim3 g1((unsigned)(a.I / 128), (unsigned)L.max_tiles);
+  const dim3 g2((unsigned)(a.H / 256), (unsigned)L.max_tiles);
+  _Float16* act = reinterpret_cast<_Float16*>(ws + L.act_f16);
+  _Float16* hdec = reinterpret_cast<_Float16*>(ws + L.h_f16);
+  const int64_t xblk = a.T * a.H / 16;
+  const unsigned gx = (unsigned)((xblk + 255) / 256);
+  if (a.nvfp4)
+    k_decode_act<true><<<gx, 256, 0, st>>>(a.x_codes, reinterpret_cast<const uint8_t*>(a.x_scales), xblk, act);
+  else
+    k_decode_act<false><<<gx, 256, 0, st>>>(a.x_codes, nullptr, xblk, act);
+  stage_mark(0, 1, st);
+  const uint8_t* w13s = reinterpret_cast<const uint8_t*>(a.w13_scales);
+  const uint8_t* w2s = reinterpret_cast<const uint8_t*>(a.w2_scales);
+  const float* xrs = reinterpret_cast<const float*>(a.x_scales);
+#define BSM_G1(NV, KG)                                                                                          \
+  k_gemm1_skinny<NV, KG><<<g1, 256, 0, st>>>(act, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles,   \
+                                             row_pair, a.topk, a.H, a.I, h_f32, h_amax)
+#define BSM_G2(NV, KG)                                                                                         \
+  k_gemm2_skinny<NV, KG><<<g2, 256, 0, st>>>(hdec, h_gs, reinterpret_cast<const float*>(h_scales), a.w2_codes, \
+                                             w2s, a.w2_gs, tiles, ntiles, a.H, a.I, y)
   hipError_t err;
   if (a.nvfp4) {
-    k_gemm1_nvfp4<<<g1, 256, 0, st>>>(a.x_codes, reinterpret_cast<const uint8_t*>(a.x_scales), a.x_gs, a.w13_codes,
-                                       reinterpret_cast<const uint8_t*>(a.w13_scales), a.w13_gs, tiles, ntiles,
-                                       row_pair, a.topk, a.H, a.I, h_f32, h_amax);
+    if (a.H % 512 == 0) BSM_G1(true, 128); else if (a.H % 256 == 0) BSM_G1(true, 64); else BSM_G1(true, 32);
+    stage_mark(0, 2, st);
     err = launch_nvfp4_quantize_from_amax(h_f32, false, 1, L.P, a.I, h_codes, h_scales, h_gs, h_amax,
-                                          a.h_static ? a.h_gs_user : nullptr, st);
+                                          a.h_static ? a.h_gs_user : nullptr, st, hdec);
     if (err != hipSuccess) return err;
     if (!a.h_static && a.h_gs_user) k_copy_f32<<<1, 64, 0, st>>>(h_gs, a.h_gs_user);
-    k_gemm2_nvfp4<<<g2, 256, 0, st>>>(h_codes, h_scales, h_gs, a.w2_codes,
-                                       reinterpret_cast<const uint8_t*>(a.w2_scales), a.w2_gs, tiles, ntiles, a.H,
-                                       a.I, y);
+    stage_mark(0, 3, st);
+    if (a.I % 512 == 0) BSM_G2(true, 128); else if (a.I % 256 == 0) BSM_G2(true, 64); else BSM_G2(true, 32);
   } else {
-    k_gemm1_fp8<<<g1, 256, 0, st>>>(a.x_codes, reinterpret_cast<const float*>(a.x_scales), a.w13_codes,
-                                     reinterpret_cast<const float*>(a.w13_scales), tiles, ntiles, row_pair, a.topk,
-                                     a.H, a.I, h_f32);
-    err = launch_fp8_quantize(h_f32, false, L.P, a.I, h_codes, reinterpret_cast<float*>(h_scales), st);
+    if (a.H % 256 == 0) BSM_G1(false, 64); else BSM_G1(false, 32);
+    stage_mark(0, 2, st);
+    err = launch_fp8_quantize(h_f32, false, L.P, a.I, h_codes, reinterpret_cast<float*>(h_scales), st, hdec);
     if (err != hipSuccess) return err;
-    k_gemm2_fp8<<<g2, 256, 0, st>>>(h_codes, reinterpret_cast<const float*>(h_scales), a.w2_codes,
-                                     reinterpret_cast<const float*>(a.w2_scales), tiles, ntiles, a.H, a.I, y);
+    stage_mark(0, 3, st);
+    if (a.I % 256 == 0) BSM_G2(false, 64); else BSM_G2(false, 32);
   }
+#undef BSM_G1
+#undef BSM_G2
+  stage_mark(0, 4, st);
   const dim3 gc((unsigned)((a.H / 4 + 255) / 256), (unsigned)a.T);
   k_combine<<<gc, 256, 0, st>>>(y, pair_row, a.wts, a.topk, a.H, (double)a.combine_scale, a.out);
+  stage_mark(0, 5, st);
   return hipGetLastError();
 }
 

@@ -91,7 +91,8 @@ __global__ __launch_bounds__(kThreads) void k_amax_parts(const void* __restrict_
 }
 
 // Encode one 16-value block with global scale S (S > 0, or S == 0 -> zero scales).
-__device__ inline void encode_block(const float* v, float S, float d1, uint8_t* codes_f, uint8_t* scale_f) {
+__device__ inline void encode_block(const float* v, float S, float d1, uint8_t* codes_f, uint8_t* scale_f,
+                                    _Float16* dec_f) {
   float ab = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
@@ -113,6 +114,18 @@ __device__ inline void encode_block(const float* v, float S, float d1, uint8_t* 
              (q[14] << 24) | (q[15] << 28);
   *reinterpret_cast<uint2*>(codes_f) = packed;
   *scale_f = (uint8_t)sc;
+  if (dec_f) {
+    // exact FP16 of q * s_b (at most 6 significant bits, within [2^-10, 2688])
+    _Float16 d[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float mag = e2m1_value_mag(q[i] & 7u) * sv;
+      d[i] = (_Float16)((q[i] & 8u) ? -mag : mag);
+    }
+    uint4* dp = reinterpret_cast<uint4*>(dec_f);
+    dp[0] = __builtin_bit_cast(uint4, *reinterpret_cast<const _Float16(*)[8]>(d));
+    dp[1] = __builtin_bit_cast(uint4, *reinterpret_cast<const _Float16(*)[8]>(d + 8));
+  }
 }
 
 // mode 0: dynamic from partial maxima; mode 1: static (gs read); mode 2: amax bits given
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_encode(const void* __restric
                                                             float* __restrict__ gs, const float* __restrict__ parts,
                                                             int nparts1, const uint32_t* __restrict__ amax_bits,
                                                             const float* __restrict__ static_gs, int mode,
-                                                            int nparts2) {
+                                                            int nparts2, _Float16* __restrict__ dec16) {
   __shared__ float lds[kThreads / 64];
   const int b = blockIdx.y;
   float S;
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_encode(const void* __restric
     const int64_t f = n_blk - 1 - g;
     float v[16];
     load16<BF16>(xb, f, v);
-    encode_block(v, S, d1, cb + f * 8, sb + f);
+    encode_block(v, S, d1, cb + f * 8, sb + f, dec16 ? dec16 + (int64_t)b * n_blk * 16 + f * 16 : nullptr);
   }
 }
 
@@ -181,7 +194,8 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_decode(const uint8_t* __rest
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_fp8_rows(const void* __restrict__ x, int64_t C,
-                                                        uint8_t* __restrict__ codes, float* __restrict__ scales) {
+                                                        uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                                        _Float16* __restrict__ dec16) {
   __shared__ float lds[kThreads / 64];
   const int64_t r = blockIdx.x;
   const int64_t n4 = C / 4;
@@ -213,13 +227,17 @@ __global__ __launch_bounds__(kThreads) void k_fp8_rows(const void* __restrict__ 
     float v[4];
     load4(j, v);
     uint32_t word = 0;
+    _Float16 d[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t sgn = (f2u(v[i]) >> 31) << 7;
       const uint32_t mag = (s == 0.0f) ? 0u : e4m3_code_mag(fabsf(v[i]) / s);
       word |= (sgn | mag) << (8 * i);
+      const float dv = e4m3_value_mag(mag);
+      d[i] = (_Float16)(sgn ? -dv : dv);
     }
     *reinterpret_cast<uint32_t*>(codes + r * C + 4 * j) = word;
+    if (dec16) *reinterpret_cast<uint2*>(dec16 + r * C + 4 * j) = __builtin_bit_cast(uint2, d);
   }
 }
 
@@ -258,26 +276,26 @@ hipError_t launch_nvfp4_quantize(const void* x, bool x_bf16, int64_t B, int64_t 
   dim3 g2(np2, (unsigned)B);
   if (x_bf16)
     k_nvfp4_encode<true><<<g2, kThreads, 0, st>>>(x, n_blk, codes, scales, gs, parts, np1, nullptr, gs,
-                                                   dynamic ? 0 : 1, np2);
+                                                   dynamic ? 0 : 1, np2, nullptr);
   else
     k_nvfp4_encode<false><<<g2, kThreads, 0, st>>>(x, n_blk, codes, scales, gs, parts, np1, nullptr, gs,
-                                                    dynamic ? 0 : 1, np2);
+                                                    dynamic ? 0 : 1, np2, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_quantize_from_amax(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C,
                                            uint8_t* codes, uint8_t* scales, float* gs, const uint32_t* amax_bits,
-                                           const float* static_gs, hipStream_t st) {
+                                           const float* static_gs, hipStream_t st, _Float16* dec16) {
   const int64_t n_blk = R * C / 16;
   if (n_blk == 0 || B == 0) return hipSuccess;
   const int np2 = encode_parts(n_blk, B);
   dim3 g2(np2, (unsigned)B);
   if (x_bf16)
     k_nvfp4_encode<true><<<g2, kThreads, 0, st>>>(x, n_blk, codes, scales, gs, nullptr, 0, amax_bits, static_gs, 2,
-                                                   np2);
+                                                   np2, dec16);
   else
     k_nvfp4_encode<false><<<g2, kThreads, 0, st>>>(x, n_blk, codes, scales, gs, nullptr, 0, amax_bits, static_gs, 2,
-                                                    np2);
+                                                    np2, dec16);
   return hipGetLastError();
 }
 
@@ -293,12 +311,12 @@ hipError_t launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, 
 }
 
 hipError_t launch_fp8_quantize(const void* x, bool x_bf16, int64_t R, int64_t C, uint8_t* codes, float* scales,
-                               hipStream_t st) {
+                               hipStream_t st, _Float16* dec16) {
   if (R == 0) return hipSuccess;
   if (x_bf16)
-    k_fp8_rows<true><<<(unsigned)R, kThreads, 0, st>>>(x, C, codes, scales);
+    k_fp8_rows<true><<<(unsigned)R, kThreads, 0, st>>>(x, C, codes, scales, dec16);
   else
-    k_fp8_rows<false><<<(unsigned)R, kThreads, 0, st>>>(x, C, codes, scales);
+    k_fp8_rows<false><<<(unsigned)R, kThreads, 0, st>>>(x, C, codes, scales, dec16);
   return hipGetLastError();
 }
 

@@ -348,6 +348,7 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   int* list = reinterpret_cast<int*>(ws + L.list);
   int* diag = reinterpret_cast<int*>(ws + L.diag);
   if (T == 0) return hipSuccess;
+  stage_mark(1, 0, st);
   k_route_prep<<<1, 64, 0, st>>>(diag);
   const unsigned nrows = (unsigned)(T + E);
   dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile), (unsigned)L.ks);
@@ -367,7 +368,9 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
     BSM_ROUTE_DISPATCH(false, false)
   }
 #undef BSM_ROUTE_DISPATCH
+  stage_mark(1, 1, st);
   k_select<<<(unsigned)T, 64, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, diag);
+  stage_mark(1, 2, st);
   return hipGetLastError();
 }
 

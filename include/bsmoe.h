@@ -161,7 +161,7 @@ int bsm_route_diagnostics(const void* ws, int64_t T, int64_t H, int64_t E, int32
  *   or STATIC via h_gs_mode / h_global_scale; FP8: one scale per row)
  *   y    = decoded h times down of e
  *   out[t] = combine_scale * sum_j topk_weights[t, j] * y(t, j)   (float [T, H])
- * Requirements: H % 16 == 0 and I % 16 == 0 (NVFP4), H % 128 == 0, I % 128 == 0,
+ * Requirements: H % 256 == 0, I % 128 == 0,
  * topk <= 32, ids in [0, E).  h_global_scale: NVFP4 STATIC -> read; DYNAMIC ->
  * written when non-NULL.  The layout of the workspace (stage buffers) is
  * reported by bsm_moe_workspace_layout for inspection.
@@ -207,6 +207,23 @@ int bsm_moe_expert_mlp(const bsm_moe_weights* w /* host */, const bsm_act_q* xq 
                        const int32_t* topk_ids, const float* topk_weights, int topk, float combine_scale,
                        int h_gs_mode, float* h_global_scale, float* out, void* ws, size_t ws_bytes,
                        bsm_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Profiling aid (not part of the method): stage-boundary events.
+ *
+ * After bsm_set_stage_events(which, events, n) with n > 0, every later call
+ * made by the calling thread records events[i] (hipEvent_t handles created and
+ * owned by the caller) on the call's stream at its stage boundaries, so the
+ * caller can time individual kernels with hipEventElapsedTime:
+ *   which = 0, bsm_moe_expert_mlp (n = 6): [0] start, [1] after the
+ *     permutation, [2] after the gate/up GEMM + SwiGLU, [3] after the h
+ *     quantization, [4] after the down GEMM, [5] after the combine;
+ *   which = 1, bsm_route (n = 3): [0] start, [1] after the exact logits,
+ *     [2] after sigmoid + selection.
+ * n = 0 (events may be NULL) stops recording.  The library keeps the handle
+ * values, not the events; they must stay valid while recording is on.
+ * ------------------------------------------------------------------------ */
+int bsm_set_stage_events(int which, void* const* events, int n);
 
 /* ------------------------------------------------------------------------
  * FP32 RMSNorm and depth-scaled residual [NUM]
