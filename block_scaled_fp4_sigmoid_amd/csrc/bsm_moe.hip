@@ -38,6 +38,8 @@
 // largest possible tile count (P/16 + E) and workgroups beyond the device-side
 // tile count exit at once.
 
+#include <algorithm>
+
 #include "bsm_internal.h"
 
 namespace bsm {
@@ -90,12 +92,17 @@ __global__ __launch_bounds__(64) void k_perm_masks(const int32_t* __restrict__ i
   }
 }
 
+constexpr int kSkinnyMaxRows = 32;  // experts with more rows use the wide kernel
+constexpr int kWideRows = 128;
+
 __global__ __launch_bounds__(1024) void k_perm_scan(const int* __restrict__ cnt, int64_t E, int64_t nc,
                                                     int* __restrict__ base, int* __restrict__ counts,
-                                                    int* __restrict__ offsets, int4* __restrict__ tiles,
-                                                    int* __restrict__ ntiles, uint32_t* __restrict__ h_amax) {
+                                                    int* __restrict__ offsets, int4* __restrict__ tiles_s,
+                                                    int* __restrict__ ntiles_s, int4* __restrict__ tiles_w,
+                                                    int* __restrict__ ntiles_w, uint32_t* __restrict__ h_amax) {
   __shared__ int s_cnt[1024];
-  __shared__ int s_tl[1024];
+  __shared__ int s_ts[1024];
+  __shared__ int s_tw[1024];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
@@ -105,30 +112,39 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int* __restrict__ cnt,
     }
     counts[e] = total;
   }
+  const bool skinny = total <= kSkinnyMaxRows;
+  const int nts = (e < E && skinny) ? (total + kRowsPerTile - 1) / kRowsPerTile : 0;
+  const int ntw = (e < E && !skinny) ? (total + kWideRows - 1) / kWideRows : 0;
   s_cnt[e] = (e < E) ? total : 0;
-  s_tl[e] = (e < E) ? (total + kRowsPerTile - 1) / kRowsPerTile : 0;
+  s_ts[e] = nts;
+  s_tw[e] = ntw;
   __syncthreads();
-  // inclusive scans (Hillis-Steele) over experts
   for (int o = 1; o < 1024; o <<= 1) {
     const int a = (e >= o) ? s_cnt[e - o] : 0;
-    const int b = (e >= o) ? s_tl[e - o] : 0;
+    const int b = (e >= o) ? s_ts[e - o] : 0;
+    const int c = (e >= o) ? s_tw[e - o] : 0;
     __syncthreads();
     s_cnt[e] += a;
-    s_tl[e] += b;
+    s_ts[e] += b;
+    s_tw[e] += c;
     __syncthreads();
   }
   if (e < E) {
     const int off = s_cnt[e] - total;
-    const int nt = (total + kRowsPerTile - 1) / kRowsPerTile;
-    const int toff = s_tl[e] - nt;
     offsets[e] = off;
     if (e == E - 1) {
       offsets[E] = s_cnt[e];
-      *ntiles = s_tl[e];
+      *ntiles_s = s_ts[e];
+      *ntiles_w = s_tw[e];
     }
-    for (int i = 0; i < nt; ++i) {
+    const int ts0 = s_ts[e] - nts, tw0 = s_tw[e] - ntw;
+    for (int i = 0; i < nts; ++i) {
       const int r = total - i * kRowsPerTile;
-      tiles[toff + i] = make_int4(e, off + i * kRowsPerTile, r < kRowsPerTile ? r : kRowsPerTile, 0);
+      tiles_s[ts0 + i] = make_int4(e, off + i * kRowsPerTile, r < kRowsPerTile ? r : kRowsPerTile, 0);
+    }
+    for (int i = 0; i < ntw; ++i) {
+      const int r = total - i * kWideRows;
+      tiles_w[tw0 + i] = make_int4(e, off + i * kWideRows, r < kWideRows ? r : kWideRows, 0);
     }
   }
   if (e == 0) *h_amax = 0u;
@@ -393,6 +409,169 @@ __global__ __launch_bounds__(256) void k_gemm2_skinny(const _Float16* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Grouped GEMM for many rows per expert ("wide"): 128 rows x 128 weight rows
+// per workgroup, K in steps of 64 staged through LDS (double buffered).  The
+// weight tile is decoded to FP16 once per K step and reused by all 128 rows;
+// each wave computes 64 rows x 64 weight rows with 16 MFMA 16x16x32 tiles.
+// GEMM1 workgroup: weight rows = 64 gate rows c0.. and the 64 matching up
+// rows, so each wave holds g and u of the same 32 h columns (SwiGLU fused).
+// ---------------------------------------------------------------------------
+constexpr int kWBM = 128, kWBN = 128, kWBK = 64, kLds = kWBK + 8;  // +8 f16 pad: conflict-free b128 reads
+
+template <bool NV, bool G1>
+__global__ __launch_bounds__(256, 2) void k_gemm_wide(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
+                                                      int topk, const float* __restrict__ a_gs,
+                                                      const float* __restrict__ a_rs, const uint8_t* __restrict__ wc,
+                                                      const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
+                                                      const int4* __restrict__ tiles, const int* __restrict__ ntiles,
+                                                      int64_t K, int64_t H, int64_t I, float* __restrict__ out,
+                                                      uint32_t* __restrict__ h_amax) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][kWBM][kLds];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kWBN][kLds];
+  if ((int)blockIdx.y >= *ntiles) return;
+  const int4 ti = tiles[blockIdx.y];
+  const int e = ti.x, row0 = ti.y, nrows = ti.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, g = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  // output column base: GEMM1 -> h columns c0..c0+63, GEMM2 -> y columns c0..c0+127
+  const int64_t c0 = (int64_t)blockIdx.x * (G1 ? 64 : 128);
+  // staging roles: row r of the A and B tiles, k half kh (32 values)
+  const int sr = tid >> 1, kh = tid & 1;
+  const int ar = sr < nrows ? sr : nrows - 1;
+  const _Float16* asrc = G1 ? act + (int64_t)(row_pair[row0 + ar] / topk) * K + 32 * kh
+                            : act + (int64_t)(row0 + ar) * K + 32 * kh;
+  int64_t wrow;
+  if (G1) wrow = (int64_t)e * 2 * I + (sr < 64 ? c0 + sr : I + c0 + (sr - 64));
+  else wrow = (int64_t)e * H + c0 + sr;
+  const int64_t cbytes = NV ? K / 2 : K;
+  const uint8_t* bsrc = wc + wrow * cbytes + (NV ? 16 : 32) * kh;
+  const uint8_t* ssrc = NV ? wsc + wrow * (K / 16) + 2 * kh : nullptr;
+
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1;
+  uint32_t rs = 0;
+#define BSM_WIDE_GLOAD(k0)                                                          \
+  {                                                                                 \
+    const uint4* pa = reinterpret_cast<const uint4*>(asrc + (k0));                  \
+    ra0 = pa[0];                                                                    \
+    ra1 = pa[1];                                                                    \
+    ra2 = pa[2];                                                                    \
+    ra3 = pa[3];                                                                    \
+    if (NV) {                                                                       \
+      rb0 = *reinterpret_cast<const uint4*>(bsrc + (k0) / 2);                       \
+      rs = *reinterpret_cast<const uint16_t*>(ssrc + (k0) / 16);                    \
+    } else {                                                                        \
+      const uint4* pb = reinterpret_cast<const uint4*>(bsrc + (k0));                \
+      rb0 = pb[0];                                                                  \
+      rb1 = pb[1];                                                                  \
+    }                                                                               \
+  }
+#define BSM_WIDE_LSTORE(buf)                                                        \
+  {                                                                                 \
+    uint4* da = reinterpret_cast<uint4*>(&As[buf][sr][32 * kh]);                    \
+    da[0] = ra0;                                                                    \
+    da[1] = ra1;                                                                    \
+    da[2] = ra2;                                                                    \
+    da[3] = ra3;                                                                    \
+    uint4* db = reinterpret_cast<uint4*>(&Bs[buf][sr][32 * kh]);                    \
+    if (NV) {                                                                       \
+      const h2v s0 = scale_pair(rs & 0xFFu), s1 = scale_pair(rs >> 8);              \
+      db[0] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.x, s0));                      \
+      db[1] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.y, s0));                      \
+      db[2] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.z, s1));                      \
+      db[3] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.w, s1));                      \
+    } else {                                                                        \
+      db[0] = __builtin_bit_cast(uint4, dec_fp8x8(rb0.x, rb0.y));                   \
+      db[1] = __builtin_bit_cast(uint4, dec_fp8x8(rb0.z, rb0.w));                   \
+      db[2] = __builtin_bit_cast(uint4, dec_fp8x8(rb1.x, rb1.y));                   \
+      db[3] = __builtin_bit_cast(uint4, dec_fp8x8(rb1.z, rb1.w));                   \
+    }                                                                               \
+  }
+  // B rows of this wave's 4 column tiles: GEMM1 gate 0,1 / up 2,3; GEMM2 4 consecutive
+#define BSM_WIDE_BROW(j) (G1 ? (((j) < 2) ? wn * 32 + 16 * (j) : 64 + wn * 32 + 16 * ((j) - 2)) : wn * 64 + 16 * (j))
+
+  f4v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f4v{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (int)(K / kWBK);
+  BSM_WIDE_GLOAD(0)
+  BSM_WIDE_LSTORE(0)
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) BSM_WIDE_GLOAD((int64_t)(ks + 1) * kWBK)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      h8v a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const h8v*>(&As[buf][wm * 64 + 16 * i + m][32 * s + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const h8v*>(&Bs[buf][BSM_WIDE_BROW(j) + m][32 * s + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
+    }
+    if (ks + 1 < nk) BSM_WIDE_LSTORE(buf ^ 1)
+    __syncthreads();
+  }
+#undef BSM_WIDE_GLOAD
+#undef BSM_WIDE_LSTORE
+#undef BSM_WIDE_BROW
+
+  float hmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ro = wm * 64 + 16 * i + 4 * g + r;
+      if (ro >= nrows) continue;
+      if (G1) {
+        float sg0, su0, sg1, su1;
+        const int64_t col0 = c0 + wn * 32 + m, col1 = col0 + 16;
+        if (NV) {
+          sg0 = sg1 = a_gs[0] * wgs[2 * e];
+          su0 = su1 = a_gs[0] * wgs[2 * e + 1];
+        } else {
+          const float sx = a_rs[row_pair[row0 + ro] / topk];
+          const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
+          sg0 = sx * ws[col0];
+          sg1 = sx * ws[col1];
+          su0 = sx * ws[I + col0];
+          su1 = sx * ws[I + col1];
+        }
+        const float h0 = silu_mul(acc[i][0][r] * sg0, acc[i][2][r] * su0);
+        const float h1 = silu_mul(acc[i][1][r] * sg1, acc[i][3][r] * su1);
+        float* hr = out + (int64_t)(row0 + ro) * I;
+        hr[col0] = h0;
+        hr[col1] = h1;
+        hmax = fmaxf(hmax, fmaxf(fabsf(h0), fabsf(h1)));
+      } else {
+        float* yr = out + (int64_t)(row0 + ro) * H + c0 + wn * 64 + m;
+        if (NV) {
+          const float sc = a_gs[0] * wgs[e];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][r] * sc;
+        } else {
+          const float sa = a_rs[row0 + ro];
+          const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * H + c0 + wn * 64 + m;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][r] * sa * ws[16 * j];
+        }
+      }
+    }
+  }
+  if (G1 && NV) {
+    hmax = wave_max_f(hmax);
+    if (lane == 0) atomicMax(h_amax, f2u(hmax));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const int* __restrict__ pair_row,
@@ -424,7 +603,8 @@ MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int
   MoeLayout L{};
   L.P = T * topk;
   L.n_chunks = (T + kChunk - 1) / kChunk;
-  L.max_tiles = L.P / kRowsPerTile + E + 1;
+  L.max_tiles = std::min<int64_t>(2 * E, L.P / kRowsPerTile + E) + 1;       // skinny: <= 2 tiles per expert
+  L.max_tiles_w = L.P / kWideRows + L.P / (kSkinnyMaxRows + 1) + 1;         // wide: experts with > 32 rows
   size_t o = 0;
   auto take = [&](size_t n) {
     const size_t r = o;
@@ -448,6 +628,8 @@ MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int
   L.chunk_cnt = take(sizeof(int) * E * L.n_chunks);
   L.chunk_base = take(sizeof(int) * E * L.n_chunks);
   L.ntiles = take(sizeof(int));
+  L.tiles_w = take(sizeof(int4) * L.max_tiles_w);
+  L.ntiles_w = take(sizeof(int));
   L.h_amax = take(sizeof(uint32_t));
   L.total = o;
   return L;
@@ -471,15 +653,20 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   int* ccnt = reinterpret_cast<int*>(ws + L.chunk_cnt);
   int* cbase = reinterpret_cast<int*>(ws + L.chunk_base);
   int* ntiles = reinterpret_cast<int*>(ws + L.ntiles);
+  int4* tiles_w = reinterpret_cast<int4*>(ws + L.tiles_w);
+  int* ntiles_w = reinterpret_cast<int*>(ws + L.ntiles_w);
   uint32_t* h_amax = reinterpret_cast<uint32_t*>(ws + L.h_amax);
 
   stage_mark(0, 0, st);
   k_perm_masks<<<(unsigned)L.n_chunks, 64, 0, st>>>(a.ids, a.T, a.topk, a.E, L.n_chunks, masks, ccnt);
-  k_perm_scan<<<1, 1024, 0, st>>>(ccnt, a.E, L.n_chunks, cbase, counts, offsets, tiles, ntiles, h_amax);
+  k_perm_scan<<<1, 1024, 0, st>>>(ccnt, a.E, L.n_chunks, cbase, counts, offsets, tiles, ntiles, tiles_w, ntiles_w,
+                                   h_amax);
   k_perm_rows<<<(unsigned)((L.P + 255) / 256), 256, 0, st>>>(a.ids, L.P, a.topk, L.n_chunks, masks, cbase, offsets,
                                                               row_pair, pair_row);
   const dim3 g1((unsigned)(a.I / 128), (unsigned)L.max_tiles);
   const dim3 g2((unsigned)(a.H / 256), (unsigned)L.max_tiles);
+  const dim3 w1((unsigned)(a.I / 64), (unsigned)L.max_tiles_w);
+  const dim3 w2((unsigned)(a.H / 128), (unsigned)L.max_tiles_w);
   _Float16* act = reinterpret_cast<_Float16*>(ws + L.act_f16);
   _Float16* hdec = reinterpret_cast<_Float16*>(ws + L.h_f16);
   const int64_t xblk = a.T * a.H / 16;
@@ -494,27 +681,51 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   const float* xrs = reinterpret_cast<const float*>(a.x_scales);
 #define BSM_G1(NV, KG)                                                                                          \
   k_gemm1_skinny<NV, KG><<<g1, 256, 0, st>>>(act, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles,   \
-                                             row_pair, a.topk, a.H, a.I, h_f32, h_amax)
+                                             row_pair, a.topk, a.H, a.I, h_f32, h_amax);                        \
+  k_gemm_wide<NV, true><<<w1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,  \
+                                            tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
 #define BSM_G2(NV, KG)                                                                                         \
   k_gemm2_skinny<NV, KG><<<g2, 256, 0, st>>>(hdec, h_gs, reinterpret_cast<const float*>(h_scales), a.w2_codes, \
-                                             w2s, a.w2_gs, tiles, ntiles, a.H, a.I, y)
+                                             w2s, a.w2_gs, tiles, ntiles, a.H, a.I, y);                         \
+  k_gemm_wide<NV, false><<<w2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
+                                             a.w2_codes, w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
   hipError_t err;
   if (a.nvfp4) {
-    if (a.H % 512 == 0) BSM_G1(true, 128); else if (a.H % 256 == 0) BSM_G1(true, 64); else BSM_G1(true, 32);
+    if (a.H % 512 == 0) {
+      BSM_G1(true, 128);
+    } else if (a.H % 256 == 0) {
+      BSM_G1(true, 64);
+    } else {
+      BSM_G1(true, 32);
+    }
     stage_mark(0, 2, st);
     err = launch_nvfp4_quantize_from_amax(h_f32, false, 1, L.P, a.I, h_codes, h_scales, h_gs, h_amax,
                                           a.h_static ? a.h_gs_user : nullptr, st, hdec);
     if (err != hipSuccess) return err;
     if (!a.h_static && a.h_gs_user) k_copy_f32<<<1, 64, 0, st>>>(h_gs, a.h_gs_user);
     stage_mark(0, 3, st);
-    if (a.I % 512 == 0) BSM_G2(true, 128); else if (a.I % 256 == 0) BSM_G2(true, 64); else BSM_G2(true, 32);
+    if (a.I % 512 == 0) {
+      BSM_G2(true, 128);
+    } else if (a.I % 256 == 0) {
+      BSM_G2(true, 64);
+    } else {
+      BSM_G2(true, 32);
+    }
   } else {
-    if (a.H % 256 == 0) BSM_G1(false, 64); else BSM_G1(false, 32);
+    if (a.H % 256 == 0) {
+      BSM_G1(false, 64);
+    } else {
+      BSM_G1(false, 32);
+    }
     stage_mark(0, 2, st);
     err = launch_fp8_quantize(h_f32, false, L.P, a.I, h_codes, reinterpret_cast<float*>(h_scales), st, hdec);
     if (err != hipSuccess) return err;
     stage_mark(0, 3, st);
-    if (a.I % 256 == 0) BSM_G2(false, 64); else BSM_G2(false, 32);
+    if (a.I % 256 == 0) {
+      BSM_G2(false, 64);
+    } else {
+      BSM_G2(false, 32);
+    }
   }
 #undef BSM_G1
 #undef BSM_G2

@@ -217,3 +217,87 @@ def test_moe_decode_full_size_sampled(gpu_lib, fmt):
     e2e = rel_l2(np_(out)[t], ref_out)
     print(f"decode {fmt} token {t}: end-to-end rel L2 {e2e:.3e}")
     assert e2e <= 1e-3
+
+
+@pytest.mark.parametrize("fmt,T", [("nvfp4", 300), ("nvfp4", 1000), ("fp8", 300), ("fp8", 1000)])
+def test_moe_tiny_shapes_many_tokens(gpu_lib, fmt, T):
+    """Tiny layer with many tokens: experts get > 32 rows (LDS-tiled kernel) next to small ones, ragged tiles."""
+    cfg = W.TINY
+    x, wr = W.activations(cfg, T=T), W.router_weights(cfg)
+    masters, w13, w2 = host_masters(cfg)
+    gw = gpu_lib.quantize_expert_weights(w13, w2, fmt)
+    experts = oracle_experts(masters, fmt)
+    xt = to_dev_bf16(x)
+    ids, wts = gpu_lib.route(xt, to_dev_f32(wr), cfg.n_group, cfg.topk_group, cfg.topk)
+    xq = gpu_lib.quantize_activations(xt, fmt)
+    out, ws = gpu_lib.moe_expert_mlp(gw, xq, ids, wts, cfg.combine_scale, return_workspace=True)
+    torch.cuda.synchronize()
+    ref = OM.moe_layer(x, wr, experts, fmt, cfg.n_group, cfg.topk_group, cfg.topk, cfg.combine_scale)
+    assert np.array_equal(np_(ids), ref["ids"])
+    counts = np.bincount(ref["ids"].ravel(), minlength=cfg.E)
+    assert counts.max() > 32
+    P = T * cfg.topk
+    st = _stages(gpu_lib, fmt, cfg, T, ws, P)
+    _, offsets, row_of_pair, _ = OM.permute(ref["ids"], cfg.E)
+    assert rel_l2(st["h"][row_of_pair], ref["h"]) <= H_TOL[fmt]
+    if fmt == "nvfp4":
+        oc, os_, og = Q.nvfp4_quantize(st["h"])
+        hh = Q.nvfp4_dequantize_exact(oc, os_, og)
+    else:
+        oc, os_ = Q.fp8_quantize(st["h"])
+        hh = Q.fp8_dequantize_exact(oc, os_)
+    assert np.array_equal(st["hc"], oc) and np.array_equal(st["hs"], os_)
+    y_ref = np.zeros_like(st["y"])
+    for e in np.unique(ref["ids"]):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        y_ref[rows] = OM.gemm_f32(hh[rows], experts[int(e)].decoded()[2])
+    assert rel_l2(st["y"], y_ref) <= H_TOL[fmt]
+    e2e = rel_l2(np_(out), ref["out"])
+    print(f"tiny {fmt} T={T}: max rows {counts.max()}, end-to-end rel L2 {e2e:.3e}")
+    assert e2e <= 1e-3
+
+
+def test_moe_prefill_full_size_sampled(gpu_lib):
+    """Beam prefill shape (8192 tokens, Zipf-skewed router) in NVFP4: full GPU layer, oracle on sampled rows."""
+    cfg = W.PREFILL
+    x, wr = W.activations(cfg), W.router_weights(cfg)
+    w13, w2 = W.expert_weights_device(cfg)
+    gw = gpu_lib.quantize_expert_weights(w13, w2, "nvfp4")
+    xt = to_dev_bf16(x)
+    ids, wts = gpu_lib.route(xt, to_dev_bf16(wr), 8, 4, 8)
+    xq = gpu_lib.quantize_activations(xt, "nvfp4")
+    out, ws = gpu_lib.moe_expert_mlp(gw, xq, ids, wts, 2.5, return_workspace=True)
+    torch.cuda.synchronize()
+    oi, ow, _, _ = OR.route(x, wr, 8, 4, 8)
+    assert np.array_equal(np_(ids), oi)
+    P = cfg.T * cfg.topk
+    st = _stages(gpu_lib, "nvfp4", cfg, cfg.T, ws, P)
+    counts, offsets, row_of_pair, pair_of_row = OM.permute(oi, cfg.E)
+    assert np.array_equal(st["row_pair"], pair_of_row) and np.array_equal(st["counts"], counts)
+    assert counts.max() > 1000
+    # global h scale from all rows; sampled rows' codes bit-exact
+    og = np.float32(np.float32(np.abs(st["h"]).max()) / np.float32(2688))
+    assert st["hg"] == og
+    rng = np.random.default_rng(3)
+    big = int(np.argmax(counts))
+    tok = [int(np.nonzero((oi == big).any(1))[0][5]), int(rng.integers(cfg.T))]
+    sx = Q.nvfp4_global_scale(x)
+    assert np_(xq[2])[0] == sx
+    xq_o, xh = OM.quantize_activations(x[tok], "nvfp4", global_scale=sx)
+    assert np.array_equal(np_(xq[0])[tok], xq_o[0]) and np.array_equal(np_(xq[1])[tok], xq_o[1])
+    for t_i, t in enumerate(tok):
+        es = [int(e) for e in oi[t]]
+        rows = [int(row_of_pair[t * 8 + j]) for j in range(8)]
+        oc, os_, _ = Q.nvfp4_quantize(st["h"][rows], global_scale=og)
+        assert np.array_equal(st["hc"][rows], oc) and np.array_equal(st["hs"][rows], os_)
+        hh = Q.nvfp4_dequantize_exact(oc, os_, og)
+        ys = []
+        for j, e in enumerate(es[:4]):  # 4 of the token's experts (oracle weight quantization is slow)
+            ex = OM.NVFP4Expert(w13[e, :cfg.I].float().cpu().numpy(), w13[e, cfg.I:].float().cpu().numpy(),
+                                w2[e].float().cpu().numpy())
+            wg, wu, wd = ex.decoded()
+            h = OM.swiglu_f32(OM.gemm_f32(xh[t_i:t_i + 1], wg), OM.gemm_f32(xh[t_i:t_i + 1], wu))
+            assert rel_l2(st["h"][rows[j]], h[0]) <= 1e-5
+            assert rel_l2(st["y"][rows[j]], OM.gemm_f32(hh[j:j + 1], wd)[0]) <= 1e-5
+        comb = OM.combine_f32(st["y"][rows][None], np_(wts)[t:t + 1], 2.5)[0]
+        assert rel_l2(np_(out)[t], comb) <= 1e-6
