@@ -72,23 +72,28 @@ __device__ inline float silu_mul(float g, float u) { return (g / (1.0f + expf(-g
 // ---------------------------------------------------------------------------
 // permutation
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_perm_masks(const int32_t* __restrict__ ids, int64_t T, int topk, int64_t E,
-                                                   int64_t nc, uint64_t* __restrict__ masks,
-                                                   int* __restrict__ cnt) {
+// One workgroup per 64-token chunk: every (token, slot) pair ORs its token bit
+// into the chunk's LDS mask of its expert (order independent), then the masks
+// and their popcounts are written out.
+__global__ __launch_bounds__(256) void k_perm_masks(const int32_t* __restrict__ ids, int64_t T, int topk, int64_t E,
+                                                    int64_t nc, uint64_t* __restrict__ masks,
+                                                    int* __restrict__ cnt) {
+  __shared__ unsigned long long lm[1024];
   const int64_t c = blockIdx.x;
-  const int64_t t = c * kChunk + threadIdx.x;
-  int my[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) my[j] = (t < T && j < topk) ? ids[t * topk + j] : -1;
-  for (int64_t e = 0; e < E; ++e) {
-    bool hit = false;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) hit |= (my[j] == (int)e);
-    const uint64_t m = __ballot(hit);
-    if (threadIdx.x == (e & 63)) {
-      masks[e * nc + c] = m;
-      cnt[e * nc + c] = __popcll(m);
-    }
+  for (int e = threadIdx.x; e < E; e += 256) lm[e] = 0ull;
+  __syncthreads();
+  const int64_t t0 = c * kChunk;
+  const int64_t tn = (T - t0) < kChunk ? (T - t0) : kChunk;
+  for (int64_t i = threadIdx.x; i < tn * topk; i += 256) {
+    const int64_t t = t0 + i / topk;
+    const int e = ids[t0 * topk + i];
+    atomicOr(&lm[e], 1ull << (t - t0));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const uint64_t m = lm[e];
+    masks[e * nc + c] = m;
+    cnt[e * nc + c] = __popcll(m);
   }
 }
 
@@ -658,7 +663,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   uint32_t* h_amax = reinterpret_cast<uint32_t*>(ws + L.h_amax);
 
   stage_mark(0, 0, st);
-  k_perm_masks<<<(unsigned)L.n_chunks, 64, 0, st>>>(a.ids, a.T, a.topk, a.E, L.n_chunks, masks, ccnt);
+  k_perm_masks<<<(unsigned)L.n_chunks, 256, 0, st>>>(a.ids, a.T, a.topk, a.E, L.n_chunks, masks, ccnt);
   k_perm_scan<<<1, 1024, 0, st>>>(ccnt, a.E, L.n_chunks, cbase, counts, offsets, tiles, ntiles, tiles_w, ntiles_w,
                                    h_amax);
   k_perm_rows<<<(unsigned)((L.P + 255) / 256), 256, 0, st>>>(a.ids, L.P, a.topk, L.n_chunks, masks, cbase, offsets,

@@ -227,6 +227,86 @@ BSM_HD float sa_round_f32(int64_t* dig) {
 }
 
 // ---------------------------------------------------------------------------
+// Fixed-point window for the exact sum of binary64 products (fast path).
+// Five signed digits of 48 bits; bit 0 of digit 0 has weight 2^base.  With
+// base = (lsb of the largest product) - 120 every product whose lowest bit is
+// >= 2^base lands in digits 0..4 and a sum of up to 2^10 * 4 (thread) terms
+// cannot overflow a digit.  win_add returns false for a product below the
+// window (the caller then uses the general superaccumulator).
+// ---------------------------------------------------------------------------
+constexpr int WIN_DIGITS = 5;
+
+BSM_HD int win_base(int emax_biased) { return emax_biased - 1075 - 120; }
+
+BSM_HD bool win_add(int64_t* dig, double p, int base) {
+  if (p == 0.0) return true;
+  const uint64_t b = d2u(p);
+  const int ef = (int)((b >> 52) & 0x7FF);
+  const uint64_t M = (b & 0xFFFFFFFFFFFFFull) | (ef ? (1ull << 52) : 0ull);
+  const int lsb = (ef ? ef : 1) - 1075;
+  const int shift = lsb - base;
+  if (shift < 0 || shift > 120) return false;
+  const int d = shift / 48, r = shift % 48;
+  const uint64_t lo = M << r;
+  const uint64_t hi = r ? (M >> (64 - r)) : 0ull;
+  const uint64_t mask = (1ull << 48) - 1;
+  const int64_t c0 = (int64_t)(lo & mask);
+  const int64_t c1 = (int64_t)(((lo >> 48) | (hi << 16)) & mask);
+  const int64_t c2 = (int64_t)(hi >> 32);
+  const int64_t sg = (b >> 63) ? -1 : 1;
+  dig[0] += sg * (d == 0 ? c0 : 0);
+  dig[1] += sg * (d == 0 ? c1 : (d == 1 ? c0 : 0));
+  dig[2] += sg * (d == 0 ? c2 : (d == 1 ? c1 : c0));
+  dig[3] += sg * (d == 1 ? c2 : (d == 2 ? c1 : 0));
+  dig[4] += sg * (d == 2 ? c2 : 0);
+  return true;
+}
+
+// Round the window value sum_q D[q] * 2^(base + 48 q) to binary32 (D is modified).
+BSM_HD float win_round_f32(int64_t* D, int base) {
+  for (int q = 0; q < WIN_DIGITS - 1; ++q) {
+    const int64_t c = D[q] >> 48;  // floor division by 2^48
+    D[q] -= c * (int64_t)(1ll << 48);
+    D[q + 1] += c;
+  }
+  const bool neg = D[WIN_DIGITS - 1] < 0;
+  if (neg) {
+    for (int q = 0; q < WIN_DIGITS; ++q) D[q] = -D[q];
+    for (int q = 0; q < WIN_DIGITS - 1; ++q) {
+      const int64_t c = D[q] >> 48;
+      D[q] -= c * (int64_t)(1ll << 48);
+      D[q + 1] += c;
+    }
+  }
+  int h = WIN_DIGITS - 1;
+  while (h > 0 && D[h] == 0) --h;
+  uint64_t W;
+  bool sticky = false;
+  int wexp;
+  if (h == 0) {
+    W = (uint64_t)D[0];
+    wexp = base;
+  } else {
+    // W keeps at least 33 leading bits exactly: enough to round to 24 bits
+    const uint64_t dh = (uint64_t)D[h], dl = (uint64_t)D[h - 1];  // dh < 2^48 except in the top digit
+    for (int q = 0; q < h - 1; ++q) sticky |= D[q] != 0;
+    if (dh < (1ull << 16)) {
+      W = (dh << 48) | dl;
+      wexp = base + 48 * (h - 1);
+    } else if (dh < (1ull << 48)) {
+      W = (dh << 16) | (dl >> 32);
+      sticky |= (dl & 0xFFFFFFFFull) != 0;
+      wexp = base + 48 * (h - 1) + 32;
+    } else {  // top digit beyond 48 bits (only possible in digit 4)
+      W = dh;
+      sticky |= dl != 0;
+      wexp = base + 48 * h;
+    }
+  }
+  return round_u64_to_f32(W, sticky, wexp, neg);
+}
+
+// ---------------------------------------------------------------------------
 // double-double arithmetic (error-free transforms, Dekker / Knuth)
 // ---------------------------------------------------------------------------
 struct dd {

@@ -37,7 +37,7 @@ namespace {
 
 constexpr int kTile = 64;  // tokens x experts per workgroup
 constexpr int kBK = 32;    // K step staged in LDS
-constexpr int kFbBlocks = 256;
+constexpr int kFbBlocks = 1024;
 
 struct RouteWs {
   size_t norm, lsb, part, logits, list, diag, total;
@@ -84,16 +84,18 @@ __global__ void k_route_prep(int* diag) {
 }
 
 template <bool XB, bool WB>
-__global__ __launch_bounds__(64) void k_rowstats(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
-                                                 int64_t E, int64_t H, double* __restrict__ norm,
-                                                 int* __restrict__ lsb) {
+__global__ __launch_bounds__(256) void k_rowstats(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
+                                                  int64_t E, int64_t H, double* __restrict__ norm,
+                                                  int* __restrict__ lsb) {
+  __shared__ double s_ss[4];
+  __shared__ int s_l[4];
   const int64_t r = blockIdx.x;
   const bool isx = r < T;
   const void* p = isx ? x : w;
   const int64_t row = isx ? r : r - T;
   double ss = 0.0;
   int lmin = 0x7FFFFFFF;
-  for (int64_t k = threadIdx.x; k < H; k += 64) {
+  for (int64_t k = threadIdx.x; k < H; k += 256) {
     const float v = isx ? ld1<XB>(p, row * H + k) : ld1<WB>(p, row * H + k);
     const double d = (double)v;
     ss = fma(d, d, ss);
@@ -108,10 +110,18 @@ __global__ __launch_bounds__(64) void k_rowstats(const void* __restrict__ x, con
     const int ol = __shfl_xor(lmin, o, 64);
     lmin = ol < lmin ? ol : lmin;
   }
+  if ((threadIdx.x & 63) == 0) {
+    s_ss[threadIdx.x >> 6] = ss;
+    s_l[threadIdx.x >> 6] = lmin;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    // relative error of ss is below (H + 6) * 2^-53; inflate generously
-    norm[r] = sqrt(ss * (1.0 + 0x1p-30)) * (1.0 + 0x1p-40);
-    lsb[r] = lmin;
+    const double tot = ((s_ss[0] + s_ss[1]) + s_ss[2]) + s_ss[3];
+    int lm = s_l[0];
+    for (int i = 1; i < 4; ++i) lm = s_l[i] < lm ? s_l[i] : lm;
+    // relative error of the sum of squares is below (H + 8) * 2^-53; inflate generously
+    norm[r] = sqrt(tot * (1.0 + 0x1p-30)) * (1.0 + 0x1p-40);
+    lsb[r] = lm;
   }
 }
 
@@ -204,30 +214,85 @@ __global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ par
   }
 }
 
+// Exact dot product of one (token, expert) pair.  Every product is exact in
+// binary64.  Fast path: a fixed-point window of five signed 48-bit digits
+// anchored 172 bits below the largest product's leading bit; a product whose
+// lowest bit falls below the window sends the pair to the general
+// superaccumulator (22 digits of 32 bits in LDS), which covers every product
+// of two binary32 values.
+constexpr int kExactThreads = 256;
+
+__device__ inline int dbl_exp(double p) { return (int)((d2u(p) >> 52) & 0x7FF); }
+
 template <bool XB, bool WB>
-__global__ __launch_bounds__(64) void k_exact(const void* __restrict__ x, const void* __restrict__ w, int64_t E,
-                                             int64_t H, const int* __restrict__ list, const int* __restrict__ diag,
-                                             float* __restrict__ logits) {
-  __shared__ int64_t dig[64][SA_NDIG + 1];
-  __shared__ int64_t tot[SA_NDIG];
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kExactThreads) void k_exact(const void* __restrict__ x, const void* __restrict__ w,
+                                                         int64_t E, int64_t H, const int* __restrict__ list,
+                                                         const int* __restrict__ diag, float* __restrict__ logits) {
+  __shared__ int s_i[4];
+  __shared__ long long s_d[4][WIN_DIGITS];
+  __shared__ int s_bad;
+  __shared__ long long s_sa[SA_NDIG];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = diag[0];
   for (int it = blockIdx.x; it < n; it += gridDim.x) {
     const int64_t i = list[it];
     const int64_t t = i / E, e = i % E;
-    for (int d = 0; d < SA_NDIG; ++d) dig[lane][d] = 0;
-    for (int64_t k = lane; k < H; k += 64) {
-      const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);  // exact
-      sa_add(dig[lane], p);
+    // largest biased exponent among the products
+    int emax = 0;
+    for (int64_t k = tid; k < H; k += kExactThreads) {
+      const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
+      const int ex = dbl_exp(p);
+      emax = ex > emax ? ex : emax;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int v = __shfl_xor(emax, o, 64);
+      emax = v > emax ? v : emax;
+    }
+    if (lane == 0) s_i[wv] = emax;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    emax = s_i[0];
+    for (int q = 1; q < 4; ++q) emax = s_i[q] > emax ? s_i[q] : emax;
+    const int base = win_base(emax);
+    int64_t dig[WIN_DIGITS] = {0, 0, 0, 0, 0};
+    bool bad = false;
+    for (int64_t k = tid; k < H; k += kExactThreads) {
+      const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
+      bad |= !win_add(dig, p, base);
+    }
+    if (bad) atomicOr(&s_bad, 1);
+#pragma unroll
+    for (int q = 0; q < WIN_DIGITS; ++q) {
+      long long v = dig[q];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0) s_d[wv][q] = v;
     }
     __syncthreads();
-    if (lane < SA_NDIG) {
-      int64_t s = 0;
-      for (int l = 0; l < 64; ++l) s += dig[l][lane];
-      tot[lane] = s;
+    if (!s_bad) {
+      if (tid == 0) {
+        int64_t D[WIN_DIGITS];
+        for (int q = 0; q < WIN_DIGITS; ++q) D[q] = ((s_d[0][q] + s_d[1][q]) + s_d[2][q]) + s_d[3][q];
+        logits[i] = win_round_f32(D, base);
+      }
+    } else {
+      // general path: 22 digits of 32 bits in LDS, one accumulation per product
+      if (tid < SA_NDIG) s_sa[tid] = 0;
+      __syncthreads();
+      int64_t loc[SA_NDIG];
+      for (int q = 0; q < SA_NDIG; ++q) loc[q] = 0;
+      for (int64_t k = tid; k < H; k += kExactThreads)
+        sa_add(loc, (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k));
+      for (int q = 0; q < SA_NDIG; ++q)
+        if (loc[q]) atomicAdd(reinterpret_cast<unsigned long long*>(&s_sa[q]), (unsigned long long)loc[q]);
+      __syncthreads();
+      if (tid == 0) {
+        int64_t dg[SA_NDIG];
+        for (int q = 0; q < SA_NDIG; ++q) dg[q] = s_sa[q];
+        logits[i] = sa_round_f32(dg);
+      }
     }
-    __syncthreads();
-    if (lane == 0) logits[i] = sa_round_f32(tot);
     __syncthreads();
   }
 }
@@ -354,10 +419,10 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile), (unsigned)L.ks);
   const unsigned nfin = (unsigned)((T * E + 255) / 256);
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                           \
-  k_rowstats<XB, WB><<<nrows, 64, 0, st>>>(x, w, T, E, H, norm, lsb);                      \
+  k_rowstats<XB, WB><<<nrows, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                     \
   k_logits<XB, WB><<<gl, 256, 0, st>>>(x, w, T, E, H, L.kc, part);                          \
   k_finalize<<<nfin, 256, 0, st>>>(part, L.ks, L.kc, T, E, norm, lsb, logits, list, diag); \
-  k_exact<XB, WB><<<kFbBlocks, 64, 0, st>>>(x, w, E, H, list, diag, logits);
+  k_exact<XB, WB><<<kFbBlocks, kExactThreads, 0, st>>>(x, w, E, H, list, diag, logits);
   if (xb && wb) {
     BSM_ROUTE_DISPATCH(true, true)
   } else if (xb && !wb) {

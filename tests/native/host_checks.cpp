@@ -25,6 +25,23 @@ void hc_exact_dot(const float* x, const float* w, int64_t rows, int64_t n, float
     out[r] = bsm::sa_round_f32(dig);
   }
 }
+// exact dot products through the fixed-point window (returns -1 in ok[r] when a product fell below it)
+void hc_window_dot(const float* x, const float* w, int64_t rows, int64_t n, float* out, int32_t* ok) {
+  for (int64_t r = 0; r < rows; ++r) {
+    int emax = 0;
+    for (int64_t k = 0; k < n; ++k) {
+      const double p = (double)x[r * n + k] * (double)w[r * n + k];
+      const int ex = (int)((bsm::d2u(p) >> 52) & 0x7FF);
+      emax = ex > emax ? ex : emax;
+    }
+    const int base = bsm::win_base(emax);
+    int64_t dig[bsm::WIN_DIGITS] = {0, 0, 0, 0, 0};
+    bool good = true;
+    for (int64_t k = 0; k < n; ++k) good &= bsm::win_add(dig, (double)x[r * n + k] * (double)w[r * n + k], base);
+    ok[r] = good ? 1 : 0;
+    out[r] = good ? bsm::win_round_f32(dig, base) : 0.0f;
+  }
+}
 void hc_sigmoid(const float* l, int64_t n, float* out, int32_t* fast) {
   for (int64_t i = 0; i < n; ++i) {
     bool f;

@@ -29,6 +29,8 @@ def hc():
     lib.hc_e4m3_value.argtypes = [P(np.uint8), ctypes.c_int64, P(np.float32)]
     lib.hc_e2m1_value.argtypes = [P(np.uint8), ctypes.c_int64, P(np.float32)]
     lib.hc_exact_dot.argtypes = [P(np.float32), P(np.float32), ctypes.c_int64, ctypes.c_int64, P(np.float32)]
+    lib.hc_window_dot.argtypes = [P(np.float32), P(np.float32), ctypes.c_int64, ctypes.c_int64, P(np.float32),
+                                  P(np.int32)]
     lib.hc_sigmoid.argtypes = [P(np.float32), ctypes.c_int64, P(np.float32), P(np.int32)]
     lib.hc_sigmoid_dd.argtypes = [P(np.float32), ctypes.c_int64, P(np.float32)]
     lib.hc_lsb_exp.argtypes = [ctypes.c_float]
@@ -94,6 +96,49 @@ def test_superaccumulator_exact_dot(hc):
     ref = np.array([R.logits_exact_f32(x[r:r + 1], w[r:r + 1])[0][0, 0] for r in range(rows)], np.float32)
     assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
     assert out[0] == np.float32(2.0 ** -40) and out[1] == 1.0
+
+
+def test_window_exact_dot(hc):
+    rng = np.random.default_rng(21)
+    rows, n = 400, 640
+    x = W_bf16(rng.standard_normal((rows, n)))
+    w = W_bf16(rng.standard_normal((rows, n)) * 0.05)
+    # exact ties, cancellation, carries across digit boundaries, negative totals, zero rows
+    x[0, :2] = [1.0, 2.0 ** -24]
+    w[0, :2] = [1.0, 1.0]
+    x[0, 2:] = 0
+    x[1] = -x[2]
+    w[1] = w[2]
+    x[3, :] = 0
+    x[4, ::2] = 3.0
+    x[4, 1::2] = -3.0
+    w[4, :] = 0.5
+    x[5, 0] = 1.0
+    w[5, 0] = 1.0
+    x[5, 1:] = 2.0 ** -40
+    w[5, 1:] = -1.0
+    xf = rng.standard_normal((rows, n)).astype(np.float32)  # full binary32 inputs too
+    for xa, wa in ((x, w), (xf, w)):
+        out = np.empty(rows, np.float32)
+        ok = np.empty(rows, np.int32)
+        hc.hc_window_dot(np.ascontiguousarray(xa), np.ascontiguousarray(wa), rows, n, out, ok)
+        ref = np.array([R.logits_exact_f32(xa[r:r + 1], wa[r:r + 1])[0][0, 0] for r in range(rows)], np.float32)
+        assert ok.all()
+        assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    # a product 2^-130 below the largest falls outside the window and is reported
+    x2 = np.zeros((1, 4), np.float32)
+    w2 = np.zeros((1, 4), np.float32)
+    x2[0, :2] = [1.0, 2.0 ** -70]
+    w2[0, :2] = [1.0, 2.0 ** -70]
+    out = np.empty(1, np.float32)
+    ok = np.empty(1, np.int32)
+    hc.hc_window_dot(x2, w2, 1, 4, out, ok)
+    assert ok[0] == 0
+
+
+def W_bf16(a):
+    import torch
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).float().numpy()
 
 
 def test_sigmoid_fast_path_and_dd_path_match_oracle(hc):
