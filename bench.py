@@ -174,13 +174,56 @@ def cpu_baseline(cfg, fmt, w13, w2, x_np, wr_np):
                       f"{tok} token ({len(need)} experts, {t_mlp:.2f} s); numpy float64 on {threads} host threads"}
 
 
+def run_stack(args, dev):
+    """Four Beam-shaped MoE layers on a 4096-token FP32 stream, NVFP4 and FP8 side by side."""
+    cfg = W.STACK
+    x1 = torch.from_numpy(W.activations(cfg)).to(dev)
+    res = {}
+    for fmt in ("nvfp4", "fp8"):
+        layers = []
+        for li in range(cfg.layers):
+            w13, w2 = W.expert_weights_device(cfg, layer=li, device=dev)
+            wr = torch.from_numpy(W.router_weights(cfg, layer=li)).to(dev, torch.bfloat16)
+            layers.append((wr, bsm.quantize_expert_weights(w13, w2, fmt)))
+            del w13, w2
+            torch.cuda.empty_cache()
+        for _ in range(args.warmup):
+            bsm.moe_stack(x1, layers, cfg.n_group, cfg.topk_group, cfg.topk)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(args.steps):
+            bsm.moe_stack(x1, layers, cfg.n_group, cfg.topk_group, cfg.topk)
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / args.steps
+        flop = cfg.layers * (2.0 * cfg.T * cfg.topk * 3 * cfg.H * cfg.I + 2.0 * cfg.T * cfg.E * cfg.H)
+        res[fmt] = {"tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+                    "tflops": round(flop / (ms * 1e-3) / 1e12, 2)}
+        print(f"[bench] stack {fmt}: {ms:.3f} ms per 4-layer step", file=sys.stderr, flush=True)
+        del layers
+        torch.cuda.empty_cache()
+    line = {
+        "metric": METRIC, "value": res["nvfp4"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["nvfp4"]["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4-e2m1 (exact f16 mfma, f32 acc); fp8 alongside",
+        "data": "synthetic (seeded Beam-shaped activations, router and expert weights)",
+        "config": {"workload": "beam-stack-4x4096: 4 MoE layers, FP32 RMSNorm + depth-scaled residual",
+                   "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "layers": cfg.layers, "topk": cfg.topk},
+        "stack": res,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "fp8"])
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "stack"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -192,6 +235,9 @@ def main():
     dev = torch.device("cuda:0")
     bsm.load()
 
+    if args.workload == "stack":
+        run_stack(args, dev)
+        return
     main_cfg = W.DECODE if args.workload == "decode" else W.PREFILL
     x, wr, w13, w2, weights = build_layer(main_cfg, args.fmt, dev)
     ms, stage_ms, counts = run_steps(main_cfg, args.fmt, x, wr, weights, args.steps, args.warmup)

@@ -321,6 +321,30 @@ def set_stage_events(which: int, handles):
 # ---------------------------------------------------------------------------
 
 
+def moe_stack(x1: torch.Tensor, layers, n_group, topk_group, topk, eps=1e-6, combine_scale=2.5, keep=False):
+    """Stack of MoE layers on an FP32 residual stream whose input is residual step 1.
+
+    Layer i (1-based) is residual step k = i + 1:  n = RMSNorm(x);  m = MoE_i(n);
+    x <- fl32(sqrt((k-1)/k) * x + (1/sqrt(k)) * m).  ``layers``: list of
+    (w_router, ExpertWeights).  Returns the final stream (and, with keep=True, the
+    per-layer (stream input, normed, ids, weights, moe output)).
+    """
+    import math
+
+    x = x1.clone().float().contiguous()
+    trace = []
+    for i, (wr, weights) in enumerate(layers, start=1):
+        k = i + 1
+        n = rmsnorm(x, eps)
+        m, ids, wts = moe_layer(n, wr, weights, n_group, topk_group, topk, combine_scale)
+        if keep:
+            trace.append((x.clone(), n, ids, wts, m))
+        a = float(torch.tensor(math.sqrt((k - 1) / k), dtype=torch.float32))
+        b = float(torch.tensor(1.0 / math.sqrt(k), dtype=torch.float32))
+        scaled_residual_(x, m, a, b)
+    return (x, trace) if keep else x
+
+
 def rmsnorm(x: torch.Tensor, eps=1e-6):
     lib = load()
     _dev(x, "x")
