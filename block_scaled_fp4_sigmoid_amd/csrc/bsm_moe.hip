@@ -59,6 +59,14 @@ __device__ inline h2v scale_pair(uint32_t code) {
   return h2v{s, s};
 }
 
+// (s, s) in FP16 for E4M3 scale byte K of w, through the hardware FP8 -> FP16
+// converter (exact; unit scale): the byte is replicated into the low two bytes.
+template <int K>
+__device__ inline h2v scale_pair_hw(uint32_t w) {
+  const uint32_t rep = __builtin_amdgcn_perm(w, w, (uint32_t)(K | (K << 8)));
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rep, 1.0f, false);
+}
+
 __device__ inline f4v mfma_f16(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
 __device__ inline float wave_max_f(float v) {
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(256) void k_decode_act(const uint8_t* __restrict__ 
   uint4 o0, o1;
   if (NV) {
     const uint2 c = *reinterpret_cast<const uint2*>(codes + f * 8);
-    const h2v s2 = scale_pair(scales[f]);
+    const h2v s2 = scale_pair_hw<0>(scales[f]);
     const h8v a = dec_fp4x8(c.x, s2), b = dec_fp4x8(c.y, s2);
     o0 = __builtin_bit_cast(uint4, a);
     o1 = __builtin_bit_cast(uint4, b);
@@ -223,193 +231,201 @@ __global__ __launch_bounds__(256) void k_decode_act(const uint8_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM for few rows per expert ("skinny"): weights stream from HBM
-// straight into registers, each weight element is decoded exactly once per
-// row tile.  One wave = 16 rows x 4 weight-row tiles of 16 over all of K.
-// Lane (m, g): row m of the tile, k-range [k0 + KG*g, k0 + KG*(g+1)) of each
-// super-step of 4*KG; MFMA step j feeds lane group g's values j*8 .. j*8+7 of
-// that range for both operands, so A and B agree on the k order.
+// Grouped GEMM for few rows per expert ("skinny", decode-sized): one
+// workgroup = 16 rows (one row tile of an expert) x 4 waves; each wave owns
+// 64 weight rows (4 tiles of 16) and streams them from HBM straight into
+// registers, decoding every weight element exactly once per row tile.  The
+// 16 activation rows of a K step go through LDS once for all 4 waves.  K is
+// walked in super-steps of 4*KB; lane (m, g) holds k-range [KB*g, KB*(g+1))
+// of a super-step, and MFMA step j feeds values 8j..8j+7 of that range for
+// both operands, so A and B agree on the k order.  The next super-step's
+// weights are loaded while the current one is multiplied (two register sets).
 // ---------------------------------------------------------------------------
-constexpr int kNT = 4;  // weight-row tiles of 16 per wave
 
-template <bool NV, int KG>
-struct BChunk {
-  // NVFP4: KG/2 code bytes + KG/16 scale bytes per lane; FP8: KG code bytes
-  static constexpr int kCodeVec = NV ? KG / 32 : KG / 16;  // uint4 per lane
-  uint4 c[kCodeVec];
-  uint32_t s[NV ? (KG / 16 + 3) / 4 : 1];
+template <bool NV, int KB>
+struct BRegs {
+  static constexpr int kVec = NV ? KB / 32 : KB / 16;  // uint4 of codes per lane and tile
+  uint4 c[kVec];
+  uint32_t s0, s1;  // NVFP4: KB/16 scale bytes (up to 8)
 };
 
-template <bool NV, int KG>
-__device__ inline void load_b(const uint8_t* codes_row, const uint8_t* scales_row, int64_t k, BChunk<NV, KG>& b) {
-  const uint4* p = reinterpret_cast<const uint4*>(codes_row + (NV ? k / 2 : k));
+template <bool NV, int KB>
+__device__ inline void b_load(const uint8_t* codes, const uint8_t* scales, BRegs<NV, KB>& b) {
+  const uint4* p = reinterpret_cast<const uint4*>(codes);
 #pragma unroll
-  for (int i = 0; i < BChunk<NV, KG>::kCodeVec; ++i) b.c[i] = p[i];
+  for (int i = 0; i < BRegs<NV, KB>::kVec; ++i) b.c[i] = p[i];
   if (NV) {
-    if (KG >= 64) {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(scales_row + k / 16);
-#pragma unroll
-      for (int i = 0; i < KG / 64; ++i) b.s[i] = q[i];
+    if (KB >= 128) {
+      const uint2 v = *reinterpret_cast<const uint2*>(scales);
+      b.s0 = v.x;
+      b.s1 = v.y;
+    } else if (KB >= 64) {
+      b.s0 = *reinterpret_cast<const uint32_t*>(scales);
     } else {
-      b.s[0] = *reinterpret_cast<const uint16_t*>(scales_row + k / 16);
+      b.s0 = *reinterpret_cast<const uint16_t*>(scales);
     }
   }
 }
 
-// MFMA step j (8 k-values) of a B chunk, decoded to FP16
-template <bool NV, int KG>
-__device__ inline h8v b_step(const BChunk<NV, KG>& b, int j) {
+template <bool NV, int KB, int J>
+__device__ inline h8v b_dec(const BRegs<NV, KB>& b) {
+  constexpr int j = J;
   if (NV) {
     const uint4 c = b.c[j >> 2];
     const uint32_t w = (j & 3) == 0 ? c.x : (j & 3) == 1 ? c.y : (j & 3) == 2 ? c.z : c.w;
-    const int blk = j >> 1;  // 16 values per scale
-    const uint32_t sb = (b.s[blk >> 2] >> (8 * (blk & 3))) & 0xFFu;
-    return dec_fp4x8(w, scale_pair(sb));
+    constexpr int blk = j >> 1;  // 16 values per scale byte
+    return dec_fp4x8(w, scale_pair_hw<(blk & 3)>(blk < 4 ? b.s0 : b.s1));
   } else {
     const uint4 c = b.c[j >> 1];
     return (j & 1) ? dec_fp8x8(c.z, c.w) : dec_fp8x8(c.x, c.y);
   }
 }
 
-template <int KG>
-__device__ inline void load_a(const _Float16* row, int64_t k, h8v* a) {
-  const uint4* p = reinterpret_cast<const uint4*>(row + k);
+template <bool NV, int KB, int NT, int J>
+__device__ inline void sk_mma_step(const _Float16* arow, const BRegs<NV, KB>* b, f4v* acc) {
+  const h8v a = *reinterpret_cast<const h8v*>(arow + 8 * J);
 #pragma unroll
-  for (int j = 0; j < KG / 8; ++j) a[j] = __builtin_bit_cast(h8v, p[j]);
+  for (int t = 0; t < NT; ++t) acc[t] = mfma_f16(a, b_dec<NV, KB, J>(b[t]), acc[t]);
+  if constexpr (J + 1 < KB / 8) sk_mma_step<NV, KB, NT, J + 1>(arow, b, acc);
+}
+template <bool NV, int KB, int NT>
+__device__ inline void sk_mma(const _Float16* arow, const BRegs<NV, KB>* b, f4v* acc) {
+  sk_mma_step<NV, KB, NT, 0>(arow, b, acc);
 }
 
-// GEMM1: rows = gathered tokens of an expert; tiles 0,1 = gate rows n0..n0+31,
-// tiles 2,3 = up rows I+n0..I+n0+31.  Epilogue h = silu(g) * u.
-template <bool NV, int KG>
-__global__ __launch_bounds__(256) void k_gemm1_skinny(const _Float16* __restrict__ act, const float* __restrict__ xgs,
-                                                      const float* __restrict__ xrs, const uint8_t* __restrict__ wc,
-                                                      const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
-                                                      const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-                                                      const int* __restrict__ row_pair, int topk, int64_t H, int64_t I,
-                                                      float* __restrict__ h_out, uint32_t* __restrict__ h_amax) {
+template <bool NV, bool G1, int KB, int NT>
+__global__ __launch_bounds__(256) void k_skinny(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
+                                                int topk, const float* __restrict__ a_gs,
+                                                const float* __restrict__ a_rs, const uint8_t* __restrict__ wc,
+                                                const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
+                                                const int4* __restrict__ tiles, const int* __restrict__ ntiles,
+                                                int64_t K, int64_t H, int64_t I, float* __restrict__ out,
+                                                uint32_t* __restrict__ h_amax) {
+  constexpr int KS = 4 * KB;         // k per super-step
+  constexpr int kAs = KS + 8;        // LDS row stride (f16), +8 pad
+  constexpr int kAv = KS / 16 / 8;   // uint4 of A staged per thread (16 threads per row)
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][16][kAs];
   if ((int)blockIdx.y >= *ntiles) return;
   const int4 ti = tiles[blockIdx.y];
   const int e = ti.x, row0 = ti.y, nrows = ti.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 32;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, g = lane >> 4;
-  const int t = row_pair[row0 + (m < nrows ? m : 0)] / topk;
-  const _Float16* arow = act + (int64_t)t * H + KG * g;
-  const int64_t cbytes = NV ? H / 2 : H;  // code bytes per weight row
-  const uint8_t* crow[kNT];
-  const uint8_t* srow[kNT];
+  // activation staging: 16 threads per row
+  const int sr = tid >> 4, sseg = tid & 15;
+  const int ar = sr < nrows ? sr : nrows - 1;
+  const _Float16* asrc = (G1 ? act + (int64_t)(row_pair[row0 + ar] / topk) * K : act + (int64_t)(row0 + ar) * K) +
+                         sseg * (KS / 16);
+  // weight rows of this wave
+  // GEMM1: NT/2 gate tiles + NT/2 up tiles -> 8*NT h columns per wave; GEMM2: 16*NT y columns
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * (G1 ? 8 * NT : 16 * NT);
+  const int64_t cbytes = NV ? K / 2 : K;
+  const uint8_t* crow[NT];
+  const uint8_t* srow[NT];
 #pragma unroll
-  for (int j = 0; j < kNT; ++j) {
-    const int64_t r = (int64_t)e * 2 * I + (j >= 2 ? I : 0) + n0 + 16 * (j & 1) + m;
-    crow[j] = wc + r * cbytes + (NV ? KG / 2 : KG) * g;
-    srow[j] = NV ? wsc + r * (H / 16) + (KG / 16) * g : nullptr;
+  for (int j = 0; j < NT; ++j) {
+    const int64_t r = G1 ? (int64_t)e * 2 * I + (j >= NT / 2 ? I : 0) + n0 + 16 * (j % (NT / 2)) + m
+                         : (int64_t)e * H + n0 + 16 * j + m;
+    crow[j] = wc + r * cbytes + (NV ? KB / 2 : KB) * g;
+    srow[j] = NV ? wsc + r * (K / 16) + (KB / 16) * g : nullptr;
   }
-  f4v acc[kNT];
+  constexpr int cstep = NV ? KS / 2 : KS;  // code bytes per super-step
+  f4v acc[NT];
 #pragma unroll
-  for (int j = 0; j < kNT; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = 0; k0 < H; k0 += 4 * KG) {
-    h8v a[KG / 8];
-    BChunk<NV, KG> b[kNT];
-#pragma unroll
-    for (int j = 0; j < kNT; ++j) load_b<NV, KG>(crow[j], srow[j], k0 * 0, b[j]);
-    load_a<KG>(arow, k0, a);
-#pragma unroll
-    for (int j = 0; j < kNT; ++j) {
-      crow[j] += NV ? 2 * KG : 4 * KG;
-      if (NV) srow[j] += KG / 4;
-    }
-#pragma unroll
-    for (int s = 0; s < KG / 8; ++s)
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) acc[j] = mfma_f16(a[s], b_step<NV, KG>(b[j], s), acc[j]);
+  for (int j = 0; j < NT; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
+
+  static_assert(kAv == 1 || kAv == 2 || kAv == 4, "activation staging: 1, 2 or 4 uint4 per thread");
+  BRegs<NV, KB> b0[NT], b1[NT];
+  uint4 ra0, ra1, ra2, ra3;
+  const int nsteps = (int)(K / KS);
+  // prologue: super-step 0
+  ra0 = reinterpret_cast<const uint4*>(asrc)[0];
+  if constexpr (kAv >= 2) ra1 = reinterpret_cast<const uint4*>(asrc)[1];
+  if constexpr (kAv >= 4) {
+    ra2 = reinterpret_cast<const uint4*>(asrc)[2];
+    ra3 = reinterpret_cast<const uint4*>(asrc)[3];
   }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) b_load<NV, KB>(crow[j], srow[j], b0[j]);
+  reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[0] = ra0;
+  if constexpr (kAv >= 2) reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[1] = ra1;
+  if constexpr (kAv >= 4) {
+    reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[2] = ra2;
+    reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[3] = ra3;
+  }
+  __syncthreads();
+  // two super-steps per iteration so the register set of each step is static
+#define BSM_SK_STEP(ST, CUR, BC, BN)                                                                      \
+  {                                                                                                       \
+    const bool more = (ST) + 1 < nsteps;                                                                  \
+    if (more) {                                                                                           \
+      const int64_t ko = (int64_t)((ST) + 1) * KS;                                                        \
+      ra0 = reinterpret_cast<const uint4*>(asrc + ko)[0];                                                 \
+      if constexpr (kAv >= 2) ra1 = reinterpret_cast<const uint4*>(asrc + ko)[1];                         \
+      if constexpr (kAv >= 4) {                                                                           \
+        ra2 = reinterpret_cast<const uint4*>(asrc + ko)[2];                                               \
+        ra3 = reinterpret_cast<const uint4*>(asrc + ko)[3];                                               \
+      }                                                                                                   \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                     \
+        b_load<NV, KB>(crow[j] + ((ST) + 1) * (int64_t)cstep,                                             \
+                       NV ? srow[j] + ((ST) + 1) * (int64_t)(KS / 16) : nullptr, BN[j]);                  \
+    }                                                                                                     \
+    sk_mma<NV, KB, NT>(&As[CUR][m][KB * g], BC, acc);                                                     \
+    if (more) {                                                                                           \
+      reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[0] = ra0;                            \
+      if constexpr (kAv >= 2) reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[1] = ra1;    \
+      if constexpr (kAv >= 4) {                                                                           \
+        reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[2] = ra2;                          \
+        reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[3] = ra3;                          \
+      }                                                                                                   \
+    }                                                                                                     \
+    __syncthreads();                                                                                      \
+  }
+  for (int st = 0; st < nsteps; st += 2) {
+    BSM_SK_STEP(st, 0, b0, b1)
+    if (st + 1 < nsteps) BSM_SK_STEP(st + 1, 1, b1, b0)
+  }
+#undef BSM_SK_STEP
+
   float hmax = 0.0f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int ro = 4 * g + r;
     if (ro >= nrows) continue;
-    float sgx, sux, sgy, suy;
-    if (NV) {
-      sgx = sgy = xgs[0] * wgs[2 * e];
-      sux = suy = xgs[0] * wgs[2 * e + 1];
+    if (G1) {
+#pragma unroll
+      for (int q = 0; q < NT / 2; ++q) {
+        const int64_t col = n0 + 16 * q + m;
+        float sg, su;
+        if (NV) {
+          sg = a_gs[0] * wgs[2 * e];
+          su = a_gs[0] * wgs[2 * e + 1];
+        } else {
+          const float sx = a_rs[row_pair[row0 + ro] / topk];
+          const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
+          sg = sx * ws[col];
+          su = sx * ws[I + col];
+        }
+        const float h = silu_mul(acc[q][r] * sg, acc[NT / 2 + q][r] * su);
+        out[(int64_t)(row0 + ro) * I + col] = h;
+        hmax = fmaxf(hmax, fabsf(h));
+      }
     } else {
-      const float sx = xrs[row_pair[row0 + ro] / topk];
-      const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
-      sgx = sx * ws[n0 + m];
-      sgy = sx * ws[n0 + 16 + m];
-      sux = sx * ws[I + n0 + m];
-      suy = sx * ws[I + n0 + 16 + m];
+      float* yr = out + (int64_t)(row0 + ro) * H + n0 + m;
+      if (NV) {
+        const float sc = a_gs[0] * wgs[e];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) yr[16 * j] = acc[j][r] * sc;
+      } else {
+        const float sa = a_rs[row0 + ro];
+        const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * H + n0 + m;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) yr[16 * j] = acc[j][r] * sa * ws[16 * j];
+      }
     }
-    const float h0 = silu_mul(acc[0][r] * sgx, acc[2][r] * sux);
-    const float h1 = silu_mul(acc[1][r] * sgy, acc[3][r] * suy);
-    float* hr = h_out + (int64_t)(row0 + ro) * I + n0 + m;
-    hr[0] = h0;
-    hr[16] = h1;
-    hmax = fmaxf(hmax, fmaxf(fabsf(h0), fabsf(h1)));
   }
-  if (NV) {
+  if (G1 && NV) {
     hmax = wave_max_f(hmax);
     if (lane == 0) atomicMax(h_amax, f2u(hmax));
-  }
-}
-
-// GEMM2: rows = sorted (token, slot) rows of an expert, A = decoded h; 64 output columns per wave.
-template <bool NV, int KG>
-__global__ __launch_bounds__(256) void k_gemm2_skinny(const _Float16* __restrict__ hact, const float* __restrict__ hgs,
-                                                      const float* __restrict__ hrs, const uint8_t* __restrict__ wc,
-                                                      const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
-                                                      const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-                                                      int64_t H, int64_t I, float* __restrict__ y) {
-  if ((int)blockIdx.y >= *ntiles) return;
-  const int4 ti = tiles[blockIdx.y];
-  const int e = ti.x, row0 = ti.y, nrows = ti.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
-  const int m = lane & 15, g = lane >> 4;
-  const _Float16* arow = hact + (int64_t)(row0 + (m < nrows ? m : 0)) * I + KG * g;
-  const int64_t cbytes = NV ? I / 2 : I;
-  const uint8_t* crow[kNT];
-  const uint8_t* srow[kNT];
-#pragma unroll
-  for (int j = 0; j < kNT; ++j) {
-    const int64_t r = (int64_t)e * H + n0 + 16 * j + m;
-    crow[j] = wc + r * cbytes + (NV ? KG / 2 : KG) * g;
-    srow[j] = NV ? wsc + r * (I / 16) + (KG / 16) * g : nullptr;
-  }
-  f4v acc[kNT];
-#pragma unroll
-  for (int j = 0; j < kNT; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = 0; k0 < I; k0 += 4 * KG) {
-    h8v a[KG / 8];
-    BChunk<NV, KG> b[kNT];
-#pragma unroll
-    for (int j = 0; j < kNT; ++j) load_b<NV, KG>(crow[j], srow[j], 0, b[j]);
-    load_a<KG>(arow, k0, a);
-#pragma unroll
-    for (int j = 0; j < kNT; ++j) {
-      crow[j] += NV ? 2 * KG : 4 * KG;
-      if (NV) srow[j] += KG / 4;
-    }
-#pragma unroll
-    for (int s = 0; s < KG / 8; ++s)
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) acc[j] = mfma_f16(a[s], b_step<NV, KG>(b[j], s), acc[j]);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ro = 4 * g + r;
-    if (ro >= nrows) continue;
-    float* yr = y + (int64_t)(row0 + ro) * H + n0 + m;
-    if (NV) {
-      const float sc = hgs[0] * wgs[e];
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) yr[16 * j] = acc[j][r] * sc;
-    } else {
-      const float sa = hrs[row0 + ro];
-      const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * H + n0 + m;
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) yr[16 * j] = acc[j][r] * sa * ws[16 * j];
-    }
   }
 }
 
@@ -480,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(const _Float16* __restrict
     da[3] = ra3;                                                                    \
     uint4* db = reinterpret_cast<uint4*>(&Bs[buf][sr][32 * kh]);                    \
     if (NV) {                                                                       \
-      const h2v s0 = scale_pair(rs & 0xFFu), s1 = scale_pair(rs >> 8);              \
+      const h2v s0 = scale_pair_hw<0>(rs), s1 = scale_pair_hw<1>(rs);              \
       db[0] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.x, s0));                      \
       db[1] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.y, s0));                      \
       db[2] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.z, s1));                      \
@@ -668,8 +684,11 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
                                    h_amax);
   k_perm_rows<<<(unsigned)((L.P + 255) / 256), 256, 0, st>>>(a.ids, L.P, a.topk, L.n_chunks, masks, cbase, offsets,
                                                               row_pair, pair_row);
-  const dim3 g1((unsigned)(a.I / 128), (unsigned)L.max_tiles);
-  const dim3 g2((unsigned)(a.H / 256), (unsigned)L.max_tiles);
+#ifndef BSM_SKINNY_NT
+#define BSM_SKINNY_NT 2
+#endif
+  const dim3 g1((unsigned)(a.I / (32 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 8*NT h columns
+  const dim3 g2((unsigned)(a.H / (64 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 16*NT y columns
   const dim3 w1((unsigned)(a.I / 64), (unsigned)L.max_tiles_w);
   const dim3 w2((unsigned)(a.H / 128), (unsigned)L.max_tiles_w);
   _Float16* act = reinterpret_cast<_Float16*>(ws + L.act_f16);
@@ -684,22 +703,24 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   const uint8_t* w13s = reinterpret_cast<const uint8_t*>(a.w13_scales);
   const uint8_t* w2s = reinterpret_cast<const uint8_t*>(a.w2_scales);
   const float* xrs = reinterpret_cast<const float*>(a.x_scales);
-#define BSM_G1(NV, KG)                                                                                          \
-  k_gemm1_skinny<NV, KG><<<g1, 256, 0, st>>>(act, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles,   \
-                                             row_pair, a.topk, a.H, a.I, h_f32, h_amax);                        \
+#define BSM_G1(NV, KB)                                                                                          \
+  k_skinny<NV, true, KB, BSM_SKINNY_NT><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes,  \
+                                                            w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I,     \
+                                                            h_f32, h_amax);                                   \
   k_gemm_wide<NV, true><<<w1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,  \
                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
-#define BSM_G2(NV, KG)                                                                                         \
-  k_gemm2_skinny<NV, KG><<<g2, 256, 0, st>>>(hdec, h_gs, reinterpret_cast<const float*>(h_scales), a.w2_codes, \
-                                             w2s, a.w2_gs, tiles, ntiles, a.H, a.I, y);                         \
+#define BSM_G2(NV, KB)                                                                                         \
+  k_skinny<NV, false, KB, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
+                                              a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
   k_gemm_wide<NV, false><<<w2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
                                              a.w2_codes, w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
   hipError_t err;
   if (a.nvfp4) {
-    if (a.H % 512 == 0) {
-      BSM_G1(true, 128);
-    } else if (a.H % 256 == 0) {
-      BSM_G1(true, 64);
+#ifndef BSM_NV_KB
+#define BSM_NV_KB 128
+#endif
+    if (a.H % (4 * BSM_NV_KB) == 0) {
+      BSM_G1(true, BSM_NV_KB);
     } else {
       BSM_G1(true, 32);
     }
@@ -709,16 +730,17 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     if (err != hipSuccess) return err;
     if (!a.h_static && a.h_gs_user) k_copy_f32<<<1, 64, 0, st>>>(h_gs, a.h_gs_user);
     stage_mark(0, 3, st);
-    if (a.I % 512 == 0) {
-      BSM_G2(true, 128);
-    } else if (a.I % 256 == 0) {
-      BSM_G2(true, 64);
+    if (a.I % (4 * BSM_NV_KB) == 0) {
+      BSM_G2(true, BSM_NV_KB);
     } else {
       BSM_G2(true, 32);
     }
   } else {
-    if (a.H % 256 == 0) {
-      BSM_G1(false, 64);
+#ifndef BSM_FP8_KB
+#define BSM_FP8_KB 64
+#endif
+    if (a.H % (4 * BSM_FP8_KB) == 0) {
+      BSM_G1(false, BSM_FP8_KB);
     } else {
       BSM_G1(false, 32);
     }
@@ -726,8 +748,8 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     err = launch_fp8_quantize(h_f32, false, L.P, a.I, h_codes, reinterpret_cast<float*>(h_scales), st, hdec);
     if (err != hipSuccess) return err;
     stage_mark(0, 3, st);
-    if (a.I % 256 == 0) {
-      BSM_G2(false, 64);
+    if (a.I % (4 * BSM_FP8_KB) == 0) {
+      BSM_G2(false, BSM_FP8_KB);
     } else {
       BSM_G2(false, 32);
     }
