@@ -365,6 +365,7 @@ BSM_HD dd dd_exp(double x) {
   r = dd_add(r, two_prod(-k, LN2_MID));
   r = dd_add(r, dd{-k * LN2_LO, 0.0});
   dd t = {1.0, 0.0};
+#pragma unroll 1
   for (int n = 27; n >= 1; --n) {
     t = dd_mul(t, r);
     t = dd_div(t, dd{(double)n, 0.0});

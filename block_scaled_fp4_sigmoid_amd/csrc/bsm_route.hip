@@ -16,18 +16,18 @@
 //                 lowest set-bit exponent over the row's nonzero entries
 //   k_logits      64x64 token x expert tiles, split along H; binary64 FMA
 //                 accumulation of products that are exact in binary64
-//   k_finalize    sums the split partials in a fixed order and proves the
-//                 binary32 rounding: (a) exact -- every partial sum is a
-//                 multiple of 2^L (L = lsb(x) + lsb(w)) below
-//                 |x|_2 |w|_2 < 2^(L+53), so no addition rounded; or
-//                 (b) certified -- the binary64 error bound
-//                 (terms + splits + 4) * 2^-53 * |x|_2 |w|_2 keeps the value
-//                 away from every binary32 rounding boundary.  Otherwise the
-//                 logit is queued for
-//   k_exact       an exact fixed-point superaccumulator sum, rounded once.
-//   k_select      one wave per token: certified binary64 sigmoid (double-
-//                 double fallback), group top-2 sums, group selection,
-//                 iterative 64-bit (score, index) argmax, normalization.
+//   k_select      one workgroup per token: sums the split partials in a fixed
+//                 order and proves the binary32 rounding of every logit:
+//                 (a) exact -- every partial sum is a multiple of 2^L
+//                 (L = lsb(x) + lsb(w)) below |x|_2 |w|_2 < 2^(L+53), so no
+//                 addition rounded; or (b) certified -- the binary64 error
+//                 bound (terms + splits + 4) * 2^-53 * |x|_2 |w|_2 keeps the
+//                 value away from every binary32 rounding boundary.  A logit
+//                 proven neither way is recomputed exactly by the workgroup
+//                 (fixed-point window / superaccumulator, rounded once).
+//                 Then: certified binary64 sigmoid (double-double fallback),
+//                 group top-2 sums, group selection, iterative 64-bit
+//                 (score, index) argmax, normalization.
 
 #include "bsm_internal.h"
 
@@ -37,10 +37,9 @@ namespace {
 
 constexpr int kTile = 64;  // tokens x experts per workgroup
 constexpr int kBK = 32;    // K step staged in LDS
-constexpr int kFbBlocks = 1024;
 
 struct RouteWs {
-  size_t norm, lsb, part, logits, list, diag, total;
+  size_t norm, lsb, part, logits, diag, total;
   int ks, kc;
 };
 
@@ -65,8 +64,6 @@ RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
   o += align256(sizeof(double) * (size_t)ks * (size_t)T * (size_t)E);
   L.logits = o;
   o += align256(sizeof(float) * (size_t)T * (size_t)E);
-  L.list = o;
-  o += align256(sizeof(int) * (size_t)T * (size_t)E);
   L.diag = o;
   o += align256(sizeof(int) * 4);
   L.total = o;
@@ -181,120 +178,75 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, cons
   }
 }
 
-__global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ part, int ks, int kc, int64_t T,
-                                                  int64_t E, const double* __restrict__ norm,
-                                                  const int* __restrict__ lsb, float* __restrict__ logits,
-                                                  int* __restrict__ list, int* __restrict__ diag) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * E) return;
-  const int64_t t = i / E, e = i % E;
-  double S = 0.0;
-  for (int s = 0; s < ks; ++s) S += part[((int64_t)s * T + t) * E + e];
-  const double A = norm[t] * norm[T + e] * (1.0 + 0x1p-40);  // >= sum |x_k w_k|
-  const int lx = lsb[t], lw = lsb[T + e];
-  float r = (float)S;
-  bool ok = false;
-  if (A == 0.0) {
-    ok = true;  // every product is zero
-    r = 0.0f;
-  } else if (lx != 0x7FFFFFFF && lw != 0x7FFFFFFF) {
-    const int L = lx + lw;
-    if (L + 53 > -1000 && A < ldexp(1.0, L + 53)) ok = true;  // the binary64 sum is exact
-  }
-  if (!ok) {
-    const double err = (double)(kc + ks + 4) * 0x1p-53 * A * 1.0001;
-    ok = f32_certified(S, err, &r);
-  }
-  if (ok) {
-    logits[i] = r;
-  } else {
-    const int slot = atomicAdd(&diag[0], 1);
-    list[slot] = (int)i;
-    logits[i] = 0.0f;  // replaced by k_exact
-  }
-}
-
-// Exact dot product of one (token, expert) pair.  Every product is exact in
-// binary64.  Fast path: a fixed-point window of five signed 48-bit digits
-// anchored 172 bits below the largest product's leading bit; a product whose
-// lowest bit falls below the window sends the pair to the general
-// superaccumulator (22 digits of 32 bits in LDS), which covers every product
-// of two binary32 values.
-constexpr int kExactThreads = 256;
-
-__device__ inline int dbl_exp(double p) { return (int)((d2u(p) >> 52) & 0x7FF); }
-
-template <bool XB, bool WB>
-__global__ __launch_bounds__(kExactThreads) void k_exact(const void* __restrict__ x, const void* __restrict__ w,
-                                                         int64_t E, int64_t H, const int* __restrict__ list,
-                                                         const int* __restrict__ diag, float* __restrict__ logits) {
-  __shared__ int s_i[4];
-  __shared__ long long s_d[4][WIN_DIGITS];
-  __shared__ int s_bad;
-  __shared__ long long s_sa[SA_NDIG];
+// Exact binary32 logit of one (token, expert) pair, computed by the whole
+// workgroup (every thread must call it).  Every product is exact in binary64;
+// fast path: fixed-point window anchored at the largest product (bsm_numerics.h),
+// general path: 22-digit superaccumulator for products below the window.
+template <bool XB, bool WB, int NT>
+__device__ float exact_logit_wg(const void* __restrict__ x, const void* __restrict__ w, int64_t t, int64_t e,
+                                int64_t H, int* s_i, long long (*s_d)[WIN_DIGITS], int* s_bad, long long* s_sa) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n = diag[0];
-  for (int it = blockIdx.x; it < n; it += gridDim.x) {
-    const int64_t i = list[it];
-    const int64_t t = i / E, e = i % E;
-    // largest biased exponent among the products
-    int emax = 0;
-    for (int64_t k = tid; k < H; k += kExactThreads) {
-      const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
-      const int ex = dbl_exp(p);
-      emax = ex > emax ? ex : emax;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const int v = __shfl_xor(emax, o, 64);
-      emax = v > emax ? v : emax;
-    }
-    if (lane == 0) s_i[wv] = emax;
-    if (tid == 0) s_bad = 0;
-    __syncthreads();
-    emax = s_i[0];
-    for (int q = 1; q < 4; ++q) emax = s_i[q] > emax ? s_i[q] : emax;
-    const int base = win_base(emax);
-    int64_t dig[WIN_DIGITS] = {0, 0, 0, 0, 0};
-    bool bad = false;
-    for (int64_t k = tid; k < H; k += kExactThreads) {
-      const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
-      bad |= !win_add(dig, p, base);
-    }
-    if (bad) atomicOr(&s_bad, 1);
-#pragma unroll
-    for (int q = 0; q < WIN_DIGITS; ++q) {
-      long long v = dig[q];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-      if (lane == 0) s_d[wv][q] = v;
-    }
-    __syncthreads();
-    if (!s_bad) {
-      if (tid == 0) {
-        int64_t D[WIN_DIGITS];
-        for (int q = 0; q < WIN_DIGITS; ++q) D[q] = ((s_d[0][q] + s_d[1][q]) + s_d[2][q]) + s_d[3][q];
-        logits[i] = win_round_f32(D, base);
-      }
-    } else {
-      // general path: 22 digits of 32 bits in LDS, one accumulation per product
-      if (tid < SA_NDIG) s_sa[tid] = 0;
-      __syncthreads();
-      int64_t loc[SA_NDIG];
-      for (int q = 0; q < SA_NDIG; ++q) loc[q] = 0;
-      for (int64_t k = tid; k < H; k += kExactThreads)
-        sa_add(loc, (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k));
-      for (int q = 0; q < SA_NDIG; ++q)
-        if (loc[q]) atomicAdd(reinterpret_cast<unsigned long long*>(&s_sa[q]), (unsigned long long)loc[q]);
-      __syncthreads();
-      if (tid == 0) {
-        int64_t dg[SA_NDIG];
-        for (int q = 0; q < SA_NDIG; ++q) dg[q] = s_sa[q];
-        logits[i] = sa_round_f32(dg);
-      }
-    }
-    __syncthreads();
+  int emax = 0;
+  for (int64_t k = tid; k < H; k += NT) {
+    const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
+    const int ex = (int)((d2u(p) >> 52) & 0x7FF);
+    emax = ex > emax ? ex : emax;
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int v = __shfl_xor(emax, o, 64);
+    emax = v > emax ? v : emax;
+  }
+  if (lane == 0) s_i[wv] = emax;
+  if (tid == 0) *s_bad = 0;
+  __syncthreads();
+  emax = s_i[0];
+  for (int q = 1; q < NW; ++q) emax = s_i[q] > emax ? s_i[q] : emax;
+  const int base = win_base(emax);
+  int64_t dig[WIN_DIGITS] = {0, 0, 0, 0, 0};
+  bool bad = false;
+  for (int64_t k = tid; k < H; k += NT) {
+    const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
+    bad |= !win_add(dig, p, base);
+  }
+  if (bad) atomicOr(s_bad, 1);
+#pragma unroll
+  for (int q = 0; q < WIN_DIGITS; ++q) {
+    long long v = dig[q];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) s_d[wv][q] = v;
+  }
+  __syncthreads();
+  float r = 0.0f;
+  if (!*s_bad) {
+    if (tid == 0) {
+      int64_t D[WIN_DIGITS];
+      for (int q = 0; q < WIN_DIGITS; ++q) {
+        long long acc = 0;
+        for (int ww = 0; ww < NW; ++ww) acc += s_d[ww][q];
+        D[q] = acc;
+      }
+      r = win_round_f32(D, base);
+    }
+  } else {
+    if (tid < SA_NDIG) s_sa[tid] = 0;
+    __syncthreads();
+    int64_t loc[SA_NDIG];
+    for (int q = 0; q < SA_NDIG; ++q) loc[q] = 0;
+    for (int64_t k = tid; k < H; k += NT) sa_add(loc, (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k));
+    for (int q = 0; q < SA_NDIG; ++q)
+      if (loc[q]) atomicAdd(reinterpret_cast<unsigned long long*>(&s_sa[q]), (unsigned long long)loc[q]);
+    __syncthreads();
+    if (tid == 0) {
+      int64_t dg[SA_NDIG];
+      for (int q = 0; q < SA_NDIG; ++q) dg[q] = s_sa[q];
+      r = sa_round_f32(dg);
+    }
+  }
+  __syncthreads();
+  return r;  // valid in thread 0
 }
 
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
@@ -309,32 +261,85 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
 }
 
 constexpr int kMaxE = 1024;
-constexpr int kMaxPerLane = kMaxE / 64;
+constexpr int kSelThreads = 256;
 
-__global__ __launch_bounds__(64) void k_select(const float* __restrict__ logits, int64_t E, int n_group,
-                                               int topk_group, int topk, int32_t* __restrict__ ids,
-                                               float* __restrict__ wts, float* __restrict__ scores,
-                                               int* __restrict__ diag) {
+// One workgroup per token: sums the split partials of every logit and proves
+// its binary32 rounding (exact-sum or error-bound argument, see the header of
+// this file); logits it cannot prove are recomputed exactly by the whole
+// workgroup.  Then: exactly rounded sigmoid (binary64 certified, double-double
+// fallback), group top-2 sums, group selection, iterative (score, index)
+// argmax in wave 0, normalization.
+template <bool XB, bool WB>
+__global__ __launch_bounds__(kSelThreads) void k_final(const void* __restrict__ x, const void* __restrict__ w,
+                                                       int64_t H, const double* __restrict__ part, int ks, int kc,
+                                                       int64_t T, int64_t E, const double* __restrict__ norm,
+                                                       const int* __restrict__ lsb, float* __restrict__ logits,
+                                                       int* __restrict__ diag) {
+  __shared__ int unc[kMaxE];
+  __shared__ int n_unc;
+  __shared__ int s_i[kSelThreads / 64];
+  __shared__ long long s_d[kSelThreads / 64][WIN_DIGITS];
+  __shared__ int s_bad;
+  __shared__ long long s_sa[SA_NDIG];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) n_unc = 0;
+  __syncthreads();
+  const double nx = norm[t];
+  const int lx = lsb[t];
+  for (int64_t e = tid; e < E; e += kSelThreads) {
+    double S = 0.0;
+    for (int s = 0; s < ks; ++s) S += part[((int64_t)s * T + t) * E + e];
+    const double A = nx * norm[T + e] * (1.0 + 0x1p-40);  // >= sum |x_k w_k|
+    const int lw = lsb[T + e];
+    float r = (float)S;
+    bool ok = false;
+    if (A == 0.0) {
+      ok = true;
+      r = 0.0f;
+    } else if (lx != 0x7FFFFFFF && lw != 0x7FFFFFFF) {
+      const int L = lx + lw;
+      if (L + 53 > -1000 && A < ldexp(1.0, L + 53)) ok = true;  // the binary64 sum is exact
+    }
+    if (!ok) ok = f32_certified(S, (double)(kc + ks + 4) * 0x1p-53 * A * 1.0001, &r);
+    if (!ok) unc[atomicAdd(&n_unc, 1)] = (int)e;
+    logits[t * E + e] = r;
+  }
+  __syncthreads();
+  const int nu = n_unc;
+  if (nu && tid == 0) atomicAdd(&diag[0], nu);
+  for (int u = 0; u < nu; ++u) {
+    const int e = unc[u];
+    const float r = exact_logit_wg<XB, WB, kSelThreads>(x, w, t, e, H, s_i, s_d, &s_bad, s_sa);
+    if (tid == 0) logits[t * E + e] = r;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ logits, int64_t E, int n_group,
+                                                        int topk_group, int topk, int32_t* __restrict__ ids,
+                                                        float* __restrict__ wts, float* __restrict__ scores,
+                                                        int* __restrict__ diag) {
   __shared__ float s_lds[kMaxE];
   __shared__ float g_lds[64];
   __shared__ int kept[64];
+  __shared__ unsigned long long keys[kMaxE];
   const int64_t t = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   int nslow = 0;
-  for (int64_t e = lane; e < E; e += 64) {
+  for (int64_t e = tid; e < E; e += kSelThreads) {
     bool fast;
-    const float s = sigmoid_f32_exact(logits[t * E + e], &fast);
+    const float sv = sigmoid_f32_exact(logits[t * E + e], &fast);
     nslow += fast ? 0 : 1;
-    s_lds[e] = s;
-    if (scores) scores[t * E + e] = s;
+    s_lds[e] = sv;
+    if (scores) scores[t * E + e] = sv;
   }
   if (nslow) atomicAdd(&diag[1], nslow);
   __syncthreads();
   const int gsz = (int)(E / n_group);
-  if (lane < n_group) {
+  if (tid < n_group) {
     float t1 = -1.0f, t2 = -1.0f;
     for (int i = 0; i < gsz; ++i) {
-      const float v = s_lds[lane * gsz + i];
+      const float v = s_lds[tid * gsz + i];
       if (v > t1) {
         t2 = t1;
         t1 = v;
@@ -342,51 +347,42 @@ __global__ __launch_bounds__(64) void k_select(const float* __restrict__ logits,
         t2 = v;
       }
     }
-    g_lds[lane] = t1 + t2;
+    g_lds[tid] = t1 + t2;
   }
   __syncthreads();
-  if (lane < n_group) {
-    const float gj = g_lds[lane];
+  if (tid < n_group) {
+    const float gj = g_lds[tid];
     int rank = 0;
     for (int i = 0; i < n_group; ++i) {
       const float gi = g_lds[i];
-      rank += (gi > gj || (gi == gj && i < lane)) ? 1 : 0;
+      rank += (gi > gj || (gi == gj && i < tid)) ? 1 : 0;
     }
-    kept[lane] = rank < topk_group ? 1 : 0;
+    kept[tid] = rank < topk_group ? 1 : 0;
   }
   __syncthreads();
-  uint64_t key[kMaxPerLane];
-#pragma unroll
-  for (int q = 0; q < kMaxPerLane; ++q) {
-    const int e = lane + 64 * q;
-    key[q] = 0;
-    if (e < E && kept[e / gsz]) key[q] = ((uint64_t)f2u(s_lds[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-  }
+  // (score, index) keys: larger score first, then lower index; 0 = not a candidate
+  for (int64_t e = tid; e < E; e += kSelThreads)
+    keys[e] = kept[e / gsz] ? ((uint64_t)f2u(s_lds[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  __syncthreads();
+  if (tid >= 64) return;  // wave 0 selects; no barrier follows
   int my_id = 0;
   float my_s = 0.0f;
   float ssum = 0.0f;
-  float sel_s[32];
-  int sel_id[32];
   for (int r = 0; r < topk; ++r) {
     uint64_t m = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxPerLane; ++q) m = key[q] > m ? key[q] : m;
+    for (int64_t e = lane; e < E; e += 64) m = keys[e] > m ? keys[e] : m;
     m = wave_max_u64(m);
     const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
-    const float s = u2f((uint32_t)(m >> 32));
-#pragma unroll
-    for (int q = 0; q < kMaxPerLane; ++q)
-      if (lane + 64 * q == e) key[q] = 0;
-    sel_s[r] = s;
-    sel_id[r] = e;
-    ssum = (r == 0) ? s : ssum + s;
+    const float sv = u2f((uint32_t)(m >> 32));
+    if (lane == (e & 63)) keys[e] = 0ull;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    ssum = (r == 0) ? sv : ssum + sv;
     if (lane == r) {
       my_id = e;
-      my_s = s;
+      my_s = sv;
     }
   }
-  (void)sel_s;
-  (void)sel_id;
   if (lane < topk) {
     ids[t * topk + lane] = my_id;
     wts[t * topk + lane] = my_s / ssum;
@@ -410,19 +406,19 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   int* lsb = reinterpret_cast<int*>(ws + L.lsb);
   double* part = reinterpret_cast<double*>(ws + L.part);
   float* logits = reinterpret_cast<float*>(ws + L.logits);
-  int* list = reinterpret_cast<int*>(ws + L.list);
   int* diag = reinterpret_cast<int*>(ws + L.diag);
   if (T == 0) return hipSuccess;
   stage_mark(1, 0, st);
   k_route_prep<<<1, 64, 0, st>>>(diag);
   const unsigned nrows = (unsigned)(T + E);
   dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile), (unsigned)L.ks);
-  const unsigned nfin = (unsigned)((T * E + 255) / 256);
-#define BSM_ROUTE_DISPATCH(XB, WB)                                                           \
-  k_rowstats<XB, WB><<<nrows, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                     \
-  k_logits<XB, WB><<<gl, 256, 0, st>>>(x, w, T, E, H, L.kc, part);                          \
-  k_finalize<<<nfin, 256, 0, st>>>(part, L.ks, L.kc, T, E, norm, lsb, logits, list, diag); \
-  k_exact<XB, WB><<<kFbBlocks, kExactThreads, 0, st>>>(x, w, E, H, list, diag, logits);
+#define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
+  k_rowstats<XB, WB><<<nrows, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                                     \
+  k_logits<XB, WB><<<gl, 256, 0, st>>>(x, w, T, E, H, L.kc, part);                                         \
+  k_final<XB, WB><<<(unsigned)T, kSelThreads, 0, st>>>(x, w, H, part, L.ks, L.kc, T, E, norm, lsb, logits,   \
+                                                      diag);                                               \
+  stage_mark(1, 1, st);                                                                                    \
+  k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, diag);
   if (xb && wb) {
     BSM_ROUTE_DISPATCH(true, true)
   } else if (xb && !wb) {
@@ -433,8 +429,6 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
     BSM_ROUTE_DISPATCH(false, false)
   }
 #undef BSM_ROUTE_DISPATCH
-  stage_mark(1, 1, st);
-  k_select<<<(unsigned)T, 64, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, diag);
   stage_mark(1, 2, st);
   return hipGetLastError();
 }
