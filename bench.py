@@ -290,7 +290,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4-e2m1 (exact f16 mfma, f32 acc)" if args.fmt == "nvfp4" else "fp8-e4m3 (fp8 mfma, f32 acc)",
+        "dtype": "nvfp4-e2m1 (exact f16 mfma, f32 acc)" if args.fmt == "nvfp4" else "fp8-e4m3 (exact f16 mfma, f32 acc)",
         "data": "synthetic (seeded Beam-shaped activations, router and expert weights)",
         "config": {"workload": f"beam-{main_cfg.name}-{main_cfg.T} {args.fmt} MoE layer", "T": main_cfg.T,
                    "H": main_cfg.H, "I": main_cfg.I, "E": main_cfg.E, "n_group": main_cfg.n_group,

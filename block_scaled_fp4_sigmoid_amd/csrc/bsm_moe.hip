@@ -11,32 +11,37 @@
 // E4M3 operands, per-output-channel weight scales, per-token activation
 // scales ("FP8 quantization" page, "Quantization scheme").
 //
-// Exactness of the NVFP4 operands on the matrix cores: a decoded element
+// Exactness of the operands on the matrix cores: a decoded NVFP4 element
 // q * s_b has at most 6 significant bits (E2M1: 2, E4M3: 4) and lies in
-// [2^-10, 2688], so it is exact in FP16.  The kernels decode codes and block
-// scales to FP16 in registers and run v_mfma_f32_16x16x32_f16 with FP32
-// accumulation; the two global scales multiply the FP32 accumulator in the
-// epilogue.  The FP8 path feeds E4M3 codes straight to
-// v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales) and applies the
-// per-row x per-column scales as a rank-1 epilogue.
+// [2^-10, 2688]; an E4M3 element has 4 significant bits and lies in
+// [2^-9, 448].  Both are exact in FP16, so every GEMM decodes its operands to
+// FP16 and runs v_mfma_f32_16x16x32_f16 with FP32 accumulation; the global
+// scales (NVFP4) or the per-row x per-column scales (FP8) multiply the FP32
+// accumulator in the epilogue.  (The FP8 matrix-core instructions were not
+// used: their internal accumulation measured about 2^-13 relative error on
+// sums that FP16 inputs with FP32 accumulation carry exactly.)
 //
 // Pipeline (all on the caller's stream, no host synchronization):
-//   k_perm_masks   per 64-token chunk and expert: ballot mask of the tokens
-//                  that selected the expert
-//   k_perm_scan    per expert: prefix counts over chunks, counts, offsets,
-//                  16-row tile work list; clears the h amax word
-//   k_perm_rows    row of every (token, slot) pair: rows of an expert are in
+//   k_perm_masks   per 64-token chunk: LDS bit mask of the chunk's tokens for
+//                  every expert (atomicOr, order independent) and its popcount
+//   k_perm_scan    per expert: prefix counts over chunks, counts, offsets, and
+//                  two device-side tile lists: experts with <= 32 rows get
+//                  16-row tiles (skinny kernel), larger ones 128-row tiles
+//                  (wide kernel); clears the h amax word
+//   k_perm_rows    row of every (token, slot) pair; rows of an expert are in
 //                  token order (stable)
-//   k_gemm1_*      one wave = 16 rows x (16 gate + 16 up) columns over all of
-//                  H; epilogue h = silu(g) * u, FP32 h to the workspace, wave
+//   k_decode_act   activation codes -> FP16 q * s_b (once per call)
+//   k_skinny<G1>   gate/up: epilogue h = silu(g) * u (FP32) to the workspace,
 //                  max |h| into one atomicMax word (order independent)
-//   h quantize     NVFP4 with one global scale over all rows / FP8 per row
-//   k_gemm2_*      one wave = 16 rows x 32 output columns over all of I
-//   k_combine      out[t] = scale * sum_j w[t,j] * y[row(t,j)] (binary64 sum)
+//   k_gemm_wide<G1> the same for 128-row tiles, LDS-staged
+//   h quantize     NVFP4 with one global scale over all rows / FP8 per row,
+//                  plus the FP16 decoded copy the down GEMM reads
+//   k_skinny<!G1>, k_gemm_wide<!G1>  down projection -> y (FP32)
+//   k_combine      out[t] = scale * sum_j w[t,j] * y[row(t,j)] (binary64 sum
+//                  in slot order, rounded once)
 //
-// Rows of an expert are split into 16-row tiles; the grid is sized for the
-// largest possible tile count (P/16 + E) and workgroups beyond the device-side
-// tile count exit at once.
+// The grids are sized for the largest possible tile counts and workgroups
+// beyond the device-side tile count exit at once.
 
 #include <algorithm>
 

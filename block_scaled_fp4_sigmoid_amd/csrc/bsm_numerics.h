@@ -144,6 +144,7 @@ BSM_HD void sa_add(int64_t* dig, double p) {
   if (p == 0.0) return;
   const uint64_t b = d2u(p);
   const int ef = (int)((b >> 52) & 0x7FF);
+  if (ef == 0x7FF) return;  // Inf/NaN input: the result is unspecified, the digit index must stay in range
   uint64_t m = b & 0xFFFFFFFFFFFFFull;
   int e;
   if (ef == 0) {
@@ -242,6 +243,7 @@ BSM_HD bool win_add(int64_t* dig, double p, int base) {
   if (p == 0.0) return true;
   const uint64_t b = d2u(p);
   const int ef = (int)((b >> 52) & 0x7FF);
+  if (ef == 0x7FF) return true;  // Inf/NaN input: ignored, the result is unspecified
   const uint64_t M = (b & 0xFFFFFFFFFFFFFull) | (ef ? (1ull << 52) : 0ull);
   const int lsb = (ef ? ef : 1) - 1075;
   const int shift = lsb - base;

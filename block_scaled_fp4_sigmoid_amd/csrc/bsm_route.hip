@@ -14,18 +14,15 @@
 //
 //   k_rowstats    per row of x and w: an upper bound of the 2-norm and the
 //                 lowest set-bit exponent over the row's nonzero entries
-//   k_logits      64x64 token x expert tiles, split along H; binary64 FMA
-//                 accumulation of products that are exact in binary64
-//   k_select      one workgroup per token: sums the split partials in a fixed
-//                 order and proves the binary32 rounding of every logit:
-//                 (a) exact -- every partial sum is a multiple of 2^L
-//                 (L = lsb(x) + lsb(w)) below |x|_2 |w|_2 < 2^(L+53), so no
-//                 addition rounded; or (b) certified -- the binary64 error
-//                 bound (terms + splits + 4) * 2^-53 * |x|_2 |w|_2 keeps the
-//                 value away from every binary32 rounding boundary.  A logit
-//                 proven neither way is recomputed exactly by the workgroup
-//                 (fixed-point window / superaccumulator, rounded once).
-//                 Then: certified binary64 sigmoid (double-double fallback),
+//   k_logits_rb   small batches: 4 tokens x 8 experts per workgroup over the
+//   / k_logits    whole row (lanes own K slices) / large batches: 64x64 LDS
+//                 tiles.  Binary64 FMA accumulation of products that are
+//                 exact in binary64; the epilogue proves the binary32
+//                 rounding of each logit (exact sum, or error bound away from
+//                 every rounding boundary) and marks the rest with NaN
+//   k_select      one workgroup per token: exact recomputation of marked
+//                 logits (fixed-point window / superaccumulator, rounded
+//                 once), certified binary64 sigmoid (double-double fallback),
 //                 group top-2 sums, group selection, iterative 64-bit
 //                 (score, index) argmax, normalization.
 
@@ -35,33 +32,30 @@ namespace bsm {
 
 namespace {
 
-constexpr int kTile = 64;  // tokens x experts per workgroup
+constexpr int kTile = 64;  // tokens x experts per workgroup of the tiled logits kernel
 constexpr int kBK = 32;    // K step staged in LDS
+constexpr int kRbT = 4;    // tokens per workgroup of the small-batch logits kernel
+constexpr int kRbE = 8;    // experts per workgroup of the small-batch logits kernel
+constexpr int kRbK = 2048; // K covered by one pass of a small-batch workgroup (256 lanes x 8)
 
 struct RouteWs {
-  size_t norm, lsb, part, logits, diag, total;
-  int ks, kc;
+  size_t norm, lsb, logits, diag, total;
+  bool rb;   // small-batch kernel (full K per workgroup, lanes own K slices)
+  int nadd;  // roundings along the longest summation path of one logit
 };
 
 RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
   RouteWs L;
   const int64_t tiles = ((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
-  int64_t ks = (1024 + tiles - 1) / tiles;
-  const int64_t kmax = (H + 127) / 128;
-  if (ks > kmax) ks = kmax;
-  if (ks < 1) ks = 1;
-  int64_t kc = (H + ks - 1) / ks;
-  kc = (kc + kBK - 1) / kBK * kBK;
-  ks = (H + kc - 1) / kc;
-  L.ks = (int)ks;
-  L.kc = (int)kc;
+  L.rb = (H % 8 == 0) && tiles < 128;
+  // small batch: one FMA chain of 8 per pass, 6 shuffle levels, 3 cross-wave adds;
+  // tiled: an FMA chain of kBK per LDS step, added to the running sum
+  L.nadd = L.rb ? (int)(((H + kRbK - 1) / kRbK) * 8 + 9) : (int)(kBK + (H + kBK - 1) / kBK + 1);
   size_t o = 0;
   L.norm = o;
   o += align256(sizeof(double) * (size_t)(T + E));
   L.lsb = o;
   o += align256(sizeof(int) * (size_t)(T + E));
-  L.part = o;
-  o += align256(sizeof(double) * (size_t)ks * (size_t)T * (size_t)E);
   L.logits = o;
   o += align256(sizeof(float) * (size_t)T * (size_t)E);
   L.diag = o;
@@ -76,29 +70,68 @@ __device__ inline float ld1(const void* p, int64_t i) {
   return reinterpret_cast<const float*>(p)[i];
 }
 
+// 8 consecutive values (16-byte aligned start) as binary32
+template <bool BF16>
+__device__ inline void ld8(const void* p, int64_t i, float* v) {
+  if (BF16) {
+    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = u2f(d[j] << 16);
+      v[2 * j + 1] = u2f(d[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
 __global__ void k_route_prep(int* diag) {
   if (threadIdx.x < 4) diag[threadIdx.x] = 0;
 }
 
-template <bool XB, bool WB>
+// Per row of x (rows 0..T-1) and of w (rows T..T+E-1), one wave per row: an
+// upper bound of the 2-norm and the lowest set-bit exponent of the row's
+// nonzero entries.
+template <bool XB, bool WB, bool VEC>
 __global__ __launch_bounds__(256) void k_rowstats(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
                                                   int64_t E, int64_t H, double* __restrict__ norm,
                                                   int* __restrict__ lsb) {
-  __shared__ double s_ss[4];
-  __shared__ int s_l[4];
-  const int64_t r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= T + E) return;
   const bool isx = r < T;
   const void* p = isx ? x : w;
   const int64_t row = isx ? r : r - T;
   double ss = 0.0;
   int lmin = 0x7FFFFFFF;
-  for (int64_t k = threadIdx.x; k < H; k += 256) {
-    const float v = isx ? ld1<XB>(p, row * H + k) : ld1<WB>(p, row * H + k);
-    const double d = (double)v;
-    ss = fma(d, d, ss);
-    if (v != 0.0f) {
-      const int l = f32_lsb_exp(v);
-      lmin = l < lmin ? l : lmin;
+  if (VEC) {
+    for (int64_t k = (int64_t)lane * 8; k < H; k += 512) {
+      float v[8];
+      if (isx) ld8<XB>(p, row * H + k, v);
+      else ld8<WB>(p, row * H + k, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const double d = (double)v[q];
+        ss = fma(d, d, ss);
+        if (v[q] != 0.0f) {
+          const int l = f32_lsb_exp(v[q]);
+          lmin = l < lmin ? l : lmin;
+        }
+      }
+    }
+  } else {
+    for (int64_t k = lane; k < H; k += 64) {
+      const float v = isx ? ld1<XB>(p, row * H + k) : ld1<WB>(p, row * H + k);
+      const double d = (double)v;
+      ss = fma(d, d, ss);
+      if (v != 0.0f) {
+        const int l = f32_lsb_exp(v);
+        lmin = l < lmin ? l : lmin;
+      }
     }
   }
 #pragma unroll
@@ -107,33 +140,136 @@ __global__ __launch_bounds__(256) void k_rowstats(const void* __restrict__ x, co
     const int ol = __shfl_xor(lmin, o, 64);
     lmin = ol < lmin ? ol : lmin;
   }
-  if ((threadIdx.x & 63) == 0) {
-    s_ss[threadIdx.x >> 6] = ss;
-    s_l[threadIdx.x >> 6] = lmin;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const double tot = ((s_ss[0] + s_ss[1]) + s_ss[2]) + s_ss[3];
-    int lm = s_l[0];
-    for (int i = 1; i < 4; ++i) lm = s_l[i] < lm ? s_l[i] : lm;
+  if (lane == 0) {
     // relative error of the sum of squares is below (H + 8) * 2^-53; inflate generously
-    norm[r] = sqrt(tot * (1.0 + 0x1p-30)) * (1.0 + 0x1p-40);
-    lsb[r] = lm;
+    norm[r] = sqrt(ss * (1.0 + 0x1p-30)) * (1.0 + 0x1p-40);
+    lsb[r] = lmin;
   }
 }
 
+// Binary32 rounding of a binary64 dot-product estimate S, when it can be
+// proven: (a) exact -- every partial sum is a multiple of 2^L (L = lsb(x) +
+// lsb(w)) below |x|_2 |w|_2 < 2^(L+53), so no addition rounded; or (b)
+// certified -- the error bound (nadd + 4) * 2^-53 * |x|_2 |w|_2 keeps S away
+// from every binary32 rounding boundary.  Otherwise NaN marks the logit for an
+// exact recomputation.
+__device__ inline float certify_logit(double S, double nx, double nw, int lx, int lw, int nadd) {
+  const double A = nx * nw * (1.0 + 0x1p-40);  // >= sum |x_k w_k|
+  if (A == 0.0) return 0.0f;
+  if (lx != 0x7FFFFFFF && lw != 0x7FFFFFFF) {
+    const int L = lx + lw;
+    if (L + 53 > -1000 && A < ldexp(1.0, L + 53)) return (float)S;
+  }
+  float r;
+  if (f32_certified(S, (double)(nadd + 4) * 0x1p-53 * A * 1.0001, &r)) return r;
+  return __builtin_nanf("");
+}
+
+// Small batches: a workgroup owns kRbT tokens x kRbE experts over the whole
+// row; each lane accumulates 8-wide K slices of all kRbT x kRbE products in
+// binary64 registers, then a fixed-order reduce-scatter across the wave and a
+// fixed-order sum of the four waves.  Consecutive workgroups land on
+// different XCDs; each XCD gets a contiguous range of expert tiles so its L2
+// holds all of x and one eighth of w.
+template <bool XB, bool WB>
+__global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
+                                                   int64_t E, int64_t H, const double* __restrict__ norm,
+                                                   const int* __restrict__ lsb, int nadd, float* __restrict__ logits) {
+  constexpr int TT = kRbT, TE = kRbE, NV = TT * TE;
+  static_assert(NV == 32, "reduce-scatter below assumes 32 outputs per workgroup");
+  __shared__ double s_red[4][NV];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t nte = (E + TE - 1) / TE;
+  const int64_t b = blockIdx.x;
+  int64_t te, tt;
+  if (nte % 8 == 0) {
+    const int64_t per = nte / 8, loc = b >> 3;
+    te = (b & 7) * per + loc % per;
+    tt = loc / per;
+  } else {
+    te = b % nte;
+    tt = b / nte;
+  }
+  const int64_t t0 = tt * TT, e0 = te * TE;
+  double acc[TT][TE];
+#pragma unroll
+  for (int i = 0; i < TT; ++i)
+#pragma unroll
+    for (int j = 0; j < TE; ++j) acc[i][j] = 0.0;
+  for (int64_t k = (int64_t)tid * 8; k < H; k += kRbK) {
+    float xv[TT][8], wv8[TE][8];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      if (t0 + i < T) {
+        ld8<XB>(x, (t0 + i) * H + k, xv[i]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xv[i][q] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      if (e0 + j < E) {
+        ld8<WB>(w, (e0 + j) * H + k, wv8[j]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) wv8[j][q] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      double wd[TE];
+#pragma unroll
+      for (int j = 0; j < TE; ++j) wd[j] = (double)wv8[j][q];
+#pragma unroll
+      for (int i = 0; i < TT; ++i) {
+        const double xd = (double)xv[i][q];
+#pragma unroll
+        for (int j = 0; j < TE; ++j) acc[i][j] = fma(xd, wd[j], acc[i][j]);
+      }
+    }
+  }
+  double v[NV];
+#pragma unroll
+  for (int i = 0; i < TT; ++i)
+#pragma unroll
+    for (int j = 0; j < TE; ++j) v[i * TE + j] = acc[i][j];
+  // reduce-scatter: after the offset-32..2 steps lane l holds output l >> 1
+  // summed over the 32 lanes that share bit 0; the offset-1 step completes it
+#pragma unroll
+  for (int s = 0; s < 5; ++s) {
+    const int off = 32 >> s, h = NV >> (s + 1);
+    const bool up = (lane & off) != 0;
+#pragma unroll
+    for (int q = 0; q < NV / 2; ++q) {
+      if (q < h) {
+        const double send = up ? v[q] : v[q + h];
+        const double keep = up ? v[q + h] : v[q];
+        v[q] = keep + __shfl_xor(send, off, 64);
+      }
+    }
+  }
+  v[0] += __shfl_xor(v[0], 1, 64);
+  if ((lane & 1) == 0) s_red[wv][lane >> 1] = v[0];
+  __syncthreads();
+  if (tid < NV) {
+    const double S = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+    const int64_t t = t0 + tid / TE, e = e0 + tid % TE;
+    if (t < T && e < E) logits[t * E + e] = certify_logit(S, norm[t], norm[T + e], lsb[t], lsb[T + e], nadd);
+  }
+}
+
+// Large batches: 64x64 token x expert tiles staged through LDS, 4x4 outputs
+// per thread; binary64 FMA chains of kBK products added to running sums.
 template <bool XB, bool WB>
 __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
-                                                int64_t E, int64_t H, int kc, double* __restrict__ part) {
+                                                int64_t E, int64_t H, const double* __restrict__ norm,
+                                                const int* __restrict__ lsb, int nadd, float* __restrict__ logits) {
   __shared__ float xs[kBK][kTile + 4];
   __shared__ float wsm[kBK][kTile + 4];
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * kTile, e0 = (int64_t)blockIdx.y * kTile;
-  const int s = blockIdx.z;
-  const int64_t k0 = (int64_t)s * kc;
-  int64_t k1 = k0 + kc;
-  if (k1 > H) k1 = H;
   double acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -141,18 +277,23 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, cons
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
   const int lr = tid >> 2;        // row of the tile this thread stages
   const int lk = (tid & 3) * 8;   // first k of the 8 it stages
-  for (int64_t kb = k0; kb < k1; kb += kBK) {
+  for (int64_t kb = 0; kb < H; kb += kBK) {
     {
       const int64_t t = t0 + lr, e = e0 + lr;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int64_t k = kb + lk + q;
-        const bool kin = k < k1;
+        const bool kin = k < H;
         xs[lk + q][lr] = (kin && t < T) ? ld1<XB>(x, t * H + k) : 0.0f;
         wsm[lk + q][lr] = (kin && e < E) ? ld1<WB>(w, e * H + k) : 0.0f;
       }
     }
     __syncthreads();
+    double blk[4][4];  // chain of kBK products per step, then one add: depth kBK + H / kBK
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) blk[i][j] = 0.0;
 #pragma unroll 4
     for (int kk = 0; kk < kBK; ++kk) {
       const float4 a = *reinterpret_cast<const float4*>(&xs[kk][ty * 4]);
@@ -162,18 +303,24 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, cons
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(av[i], bv[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) blk[i][j] = fma(av[i], bv[j], blk[i][j]);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += blk[i][j];
     __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t t = t0 + ty * 4 + i;
     if (t >= T) continue;
+    const double nx = norm[t];
+    const int lx = lsb[t];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t e = e0 + tx * 4 + j;
-      if (e < E) part[((int64_t)s * T + t) * E + e] = acc[i][j];
+      if (e < E) logits[t * E + e] = certify_logit(acc[i][j], nx, norm[T + e], lx, lsb[T + e], nadd);
     }
   }
 }
@@ -263,72 +410,50 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
 constexpr int kMaxE = 1024;
 constexpr int kSelThreads = 256;
 
-// One workgroup per token: sums the split partials of every logit and proves
-// its binary32 rounding (exact-sum or error-bound argument, see the header of
-// this file); logits it cannot prove are recomputed exactly by the whole
-// workgroup.  Then: exactly rounded sigmoid (binary64 certified, double-double
-// fallback), group top-2 sums, group selection, iterative (score, index)
-// argmax in wave 0, normalization.
+// One workgroup per token: logits the logits kernel could not prove are
+// recomputed exactly by the whole workgroup; then exactly rounded sigmoid
+// (binary64 certified, double-double fallback), group top-2 sums, group
+// selection, iterative (score, index) argmax in wave 0, normalization.
 template <bool XB, bool WB>
-__global__ __launch_bounds__(kSelThreads) void k_final(const void* __restrict__ x, const void* __restrict__ w,
-                                                       int64_t H, const double* __restrict__ part, int ks, int kc,
-                                                       int64_t T, int64_t E, const double* __restrict__ norm,
-                                                       const int* __restrict__ lsb, float* __restrict__ logits,
-                                                       int* __restrict__ diag) {
+__global__ __launch_bounds__(kSelThreads) void k_select(const void* __restrict__ x, const void* __restrict__ w,
+                                                        int64_t H, const float* __restrict__ logits, int64_t E,
+                                                        int n_group, int topk_group, int topk,
+                                                        int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                        float* __restrict__ scores, int* __restrict__ diag) {
+  __shared__ float s_lds[kMaxE];
+  __shared__ unsigned long long keys[kMaxE];
   __shared__ int unc[kMaxE];
+  __shared__ float g_lds[64];
+  __shared__ int kept[64];
   __shared__ int n_unc;
   __shared__ int s_i[kSelThreads / 64];
   __shared__ long long s_d[kSelThreads / 64][WIN_DIGITS];
   __shared__ int s_bad;
   __shared__ long long s_sa[SA_NDIG];
   const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   if (tid == 0) n_unc = 0;
   __syncthreads();
-  const double nx = norm[t];
-  const int lx = lsb[t];
   for (int64_t e = tid; e < E; e += kSelThreads) {
-    double S = 0.0;
-    for (int s = 0; s < ks; ++s) S += part[((int64_t)s * T + t) * E + e];
-    const double A = nx * norm[T + e] * (1.0 + 0x1p-40);  // >= sum |x_k w_k|
-    const int lw = lsb[T + e];
-    float r = (float)S;
-    bool ok = false;
-    if (A == 0.0) {
-      ok = true;
-      r = 0.0f;
-    } else if (lx != 0x7FFFFFFF && lw != 0x7FFFFFFF) {
-      const int L = lx + lw;
-      if (L + 53 > -1000 && A < ldexp(1.0, L + 53)) ok = true;  // the binary64 sum is exact
-    }
-    if (!ok) ok = f32_certified(S, (double)(kc + ks + 4) * 0x1p-53 * A * 1.0001, &r);
-    if (!ok) unc[atomicAdd(&n_unc, 1)] = (int)e;
-    logits[t * E + e] = r;
+    const float l = logits[t * E + e];
+    s_lds[e] = l;
+    if (l != l) unc[atomicAdd(&n_unc, 1)] = (int)e;
   }
   __syncthreads();
   const int nu = n_unc;
-  if (nu && tid == 0) atomicAdd(&diag[0], nu);
-  for (int u = 0; u < nu; ++u) {
-    const int e = unc[u];
-    const float r = exact_logit_wg<XB, WB, kSelThreads>(x, w, t, e, H, s_i, s_d, &s_bad, s_sa);
-    if (tid == 0) logits[t * E + e] = r;
+  if (nu) {
+    if (tid == 0) atomicAdd(&diag[0], nu);
+    for (int u = 0; u < nu; ++u) {
+      const int e = unc[u];
+      const float r = exact_logit_wg<XB, WB, kSelThreads>(x, w, t, e, H, s_i, s_d, &s_bad, s_sa);
+      if (tid == 0) s_lds[e] = r;
+    }
+    __syncthreads();
   }
-}
-
-__global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ logits, int64_t E, int n_group,
-                                                        int topk_group, int topk, int32_t* __restrict__ ids,
-                                                        float* __restrict__ wts, float* __restrict__ scores,
-                                                        int* __restrict__ diag) {
-  __shared__ float s_lds[kMaxE];
-  __shared__ float g_lds[64];
-  __shared__ int kept[64];
-  __shared__ unsigned long long keys[kMaxE];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
   int nslow = 0;
   for (int64_t e = tid; e < E; e += kSelThreads) {
     bool fast;
-    const float sv = sigmoid_f32_exact(logits[t * E + e], &fast);
+    const float sv = sigmoid_f32_exact(s_lds[e], &fast);
     nslow += fast ? 0 : 1;
     s_lds[e] = sv;
     if (scores) scores[t * E + e] = sv;
@@ -404,21 +529,27 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   uint8_t* ws = reinterpret_cast<uint8_t*>(ws_);
   double* norm = reinterpret_cast<double*>(ws + L.norm);
   int* lsb = reinterpret_cast<int*>(ws + L.lsb);
-  double* part = reinterpret_cast<double*>(ws + L.part);
   float* logits = reinterpret_cast<float*>(ws + L.logits);
   int* diag = reinterpret_cast<int*>(ws + L.diag);
   if (T == 0) return hipSuccess;
   stage_mark(1, 0, st);
   k_route_prep<<<1, 64, 0, st>>>(diag);
-  const unsigned nrows = (unsigned)(T + E);
-  dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile), (unsigned)L.ks);
+  const unsigned nrs = (unsigned)((T + E + 3) / 4);
+  const unsigned nrb = (unsigned)(((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE));
+  dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
+  const bool vec = (H % 8) == 0;
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
-  k_rowstats<XB, WB><<<nrows, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                                     \
-  k_logits<XB, WB><<<gl, 256, 0, st>>>(x, w, T, E, H, L.kc, part);                                         \
-  k_final<XB, WB><<<(unsigned)T, kSelThreads, 0, st>>>(x, w, H, part, L.ks, L.kc, T, E, norm, lsb, logits,   \
-                                                      diag);                                               \
+  if (vec)                                                                                                 \
+    k_rowstats<XB, WB, true><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                               \
+  else                                                                                                     \
+    k_rowstats<XB, WB, false><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                              \
+  if (L.rb)                                                                                                \
+    k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits);                    \
+  else                                                                                                     \
+    k_logits<XB, WB><<<gl, 256, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits);                        \
   stage_mark(1, 1, st);                                                                                    \
-  k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, diag);
+  k_select<XB, WB><<<(unsigned)T, kSelThreads, 0, st>>>(x, w, H, logits, E, n_group, topk_group, topk, ids, \
+                                                       wts, scores, diag);
   if (xb && wb) {
     BSM_ROUTE_DISPATCH(true, true)
   } else if (xb && !wb) {

@@ -39,8 +39,9 @@
  *     host before anything is enqueued; on error nothing is enqueued and no
  *     output is touched.  bsm_last_error() returns a thread-local message
  *     describing the most recent error of the calling thread.
- *   - Inputs must be finite.  Results are deterministic: the same inputs give
- *     bit-identical outputs on every run.
+ *   - Inputs must be finite; non-finite inputs give unspecified output values
+ *     (never an out-of-range access).  Results are deterministic: the same
+ *     inputs give bit-identical outputs on every run.
  *   - Element dtypes: BSM_BF16 (bfloat16) or BSM_F32 (IEEE binary32).
  *   - E4M3 means OCP FP8 E4M3FN (bias 7, max finite 448, no infinities).
  */
@@ -218,8 +219,9 @@ int bsm_moe_expert_mlp(const bsm_moe_weights* w /* host */, const bsm_act_q* xq 
  *   which = 0, bsm_moe_expert_mlp (n = 6): [0] start, [1] after the
  *     permutation, [2] after the gate/up GEMM + SwiGLU, [3] after the h
  *     quantization, [4] after the down GEMM, [5] after the combine;
- *   which = 1, bsm_route (n = 3): [0] start, [1] after the exact logits,
- *     [2] after sigmoid + selection.
+ *   which = 1, bsm_route (n = 3): [0] start, [1] after the logits kernel
+ *     (row statistics, dot products, rounding proofs), [2] after the exact
+ *     fallback of unproven logits, sigmoid and selection.
  * n = 0 (events may be NULL) stops recording.  The library keeps the handle
  * values, not the events; they must stay valid while recording is on.
  * ------------------------------------------------------------------------ */

@@ -164,3 +164,16 @@ def test_lsb_exponent(hc):
     assert hc.hc_lsb_exp(2.0 ** -149) == -149
     assert hc.hc_lsb_exp(3.0 * 2.0 ** -140) == -140
     assert hc.hc_lsb_exp(-6.0) == 1
+
+
+def test_exact_dot_nonfinite_inputs_stay_in_range(hc):
+    # non-finite inputs give unspecified logits; the accumulators must not index out of range
+    x = np.ones((3, 64), np.float32)
+    w = np.ones((3, 64), np.float32)
+    x[0, 5] = np.inf
+    x[1, 7] = np.nan
+    w[2, 0] = -np.inf
+    out = np.empty(3, np.float32)
+    ok = np.empty(3, np.int32)
+    hc.hc_exact_dot(x, w, 3, 64, out)
+    hc.hc_window_dot(x, w, 3, 64, out, ok)
