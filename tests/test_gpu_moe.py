@@ -13,11 +13,12 @@ from tests.helpers import host_masters, np_, oracle_experts, rel_l2, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
-# Stage tolerances (relative L2).  NVFP4 runs exact FP16 operands through the
-# FP16 MFMA with FP32 accumulation: 1e-5.  The FP8 path feeds E4M3 codes to the
-# gfx950 FP8 MFMA, whose internal accumulation of each 128-product block is
-# coarser than FP32 (measured ~2e-5 relative on h): 1e-4.
-H_TOL = {"nvfp4": 1e-5, "fp8": 1e-4}
+# Stage tolerances (relative L2).  Both formats decode their operands exactly to
+# FP16 (NVFP4 q * s_b: <= 6 significant bits; E4M3: 4) and accumulate in FP32
+# on the FP16 MFMA.  A K-term FP32 sum of products with random signs carries a
+# relative error of order sqrt(K) * 2^-24 (about 4e-6 at K = 5120) per element,
+# so the relative L2 over a stage sits near 1e-6; the gate is 1e-5.
+H_TOL = {"nvfp4": 1e-5, "fp8": 1e-5}
 
 
 def _weights_match(gpu_w, experts, fmt, ids):
