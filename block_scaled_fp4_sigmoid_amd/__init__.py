@@ -309,7 +309,7 @@ def moe_layer(x, w_router, weights: ExpertWeights, n_group, topk_group, topk, co
 
 
 def set_stage_events(which: int, handles):
-    """Record caller-owned hipEvent_t ``handles`` at stage boundaries (see bsmoe.h); [] stops."""
+    """Record caller-owned hipEvent_t ``handles`` at stage boundaries (see bsmoe.h); None skips one; [] stops."""
     lib = load()
     n = len(handles)
     arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(h) for h in handles])

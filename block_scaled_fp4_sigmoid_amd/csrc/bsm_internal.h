@@ -86,7 +86,7 @@ struct StageEvents {
 StageEvents& stage_events(int which);  // thread-local, which = 0 (moe) or 1 (route)
 inline void stage_mark(int which, int i, hipStream_t st) {
   StageEvents& s = stage_events(which);
-  if (i < s.n) (void)hipEventRecord(s.ev[i], st);
+  if (i < s.n && s.ev[i]) (void)hipEventRecord(s.ev[i], st);
 }
 
 // ---- norm / residual ------------------------------------------------------

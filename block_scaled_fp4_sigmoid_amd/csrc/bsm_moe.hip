@@ -30,6 +30,7 @@
 //                  (wide kernel); clears the h amax word
 //   k_perm_rows    row of every (token, slot) pair; rows of an expert are in
 //                  token order (stable)
+//   k_perm_small   all three in one workgroup when the batch is one chunk
 //   k_decode_act   activation codes -> FP16 q * s_b (once per call)
 //   k_skinny<G1>   gate/up: epilogue h = silu(g) * u (FP32) to the workspace,
 //                  max |h| into one atomicMax word (order independent)
@@ -237,69 +238,111 @@ __global__ __launch_bounds__(256) void k_decode_act(const uint8_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Grouped GEMM for few rows per expert ("skinny", decode-sized): one
-// workgroup = 16 rows (one row tile of an expert) x 4 waves; each wave owns
-// 64 weight rows (4 tiles of 16) and streams them from HBM straight into
-// registers, decoding every weight element exactly once per row tile.  The
-// 16 activation rows of a K step go through LDS once for all 4 waves.  K is
-// walked in super-steps of 4*KB; lane (m, g) holds k-range [KB*g, KB*(g+1))
-// of a super-step, and MFMA step j feeds values 8j..8j+7 of that range for
-// both operands, so A and B agree on the k order.  The next super-step's
-// weights are loaded while the current one is multiplied (two register sets).
+// workgroup = 16 rows (one row tile of an expert) x 4 waves; each wave owns NT
+// tiles of 16 weight rows (GEMM1: NT/2 gate + NT/2 up tiles of the same h
+// columns) and streams them from HBM straight into registers, decoding every
+// weight element once per row tile.  The 16 activation rows of a K step go
+// through LDS once for all 4 waves.
+//
+// K is walked in super-steps of KS = 4*KB values; a row's codes of one
+// super-step are one contiguous span, read by the row's 4 lanes (g = 0..3) as
+// uint4 i = 0..KB/VPU-1 at byte i*64 + g*16, so every load instruction covers
+// 64 contiguous bytes of each of its 16 rows.  Lane g thus holds values
+// i*4*VPU + g*VPU .. +VPU-1 (VPU values per uint4); MFMA step J feeds 8 of
+// them and reads the activations at the same k, so A and B agree on the k
+// order.  NVFP4 block scales: lane g holds the whole scale span of its row for
+// super-step 4q+g (the 4 lanes of a row together hold one cache line per 4
+// super-steps); at super-step 4q+i every lane fetches its scale bytes from
+// lane group i with ds_bpermute, and group i then loads its span of
+// super-step 4q+4+i.  The next super-step's codes are loaded while the
+// current one is multiplied (two register sets).
 // ---------------------------------------------------------------------------
 
-template <bool NV, int KB>
-struct BRegs {
-  static constexpr int kVec = NV ? KB / 32 : KB / 16;  // uint4 of codes per lane and tile
-  uint4 c[kVec];
-  uint32_t s0, s1;  // NVFP4: KB/16 scale bytes (up to 8)
+template <bool NV>
+struct SkGeom {
+  static constexpr int VPU = NV ? 32 : 16;  // values per uint4 of codes
+  static constexpr int SPU = VPU / 8;       // MFMA steps per uint4
 };
 
 template <bool NV, int KB>
-__device__ inline void b_load(const uint8_t* codes, const uint8_t* scales, BRegs<NV, KB>& b) {
-  const uint4* p = reinterpret_cast<const uint4*>(codes);
+struct BRegs {
+  static constexpr int kVec = KB / SkGeom<NV>::VPU;  // uint4 of codes per lane and tile
+  uint4 c[kVec];
+};
+
+template <bool NV, int KB>
+__device__ inline void b_load(const uint8_t* codes, BRegs<NV, KB>& b) {
 #pragma unroll
-  for (int i = 0; i < BRegs<NV, KB>::kVec; ++i) b.c[i] = p[i];
-  if (NV) {
-    if (KB >= 128) {
-      const uint2 v = *reinterpret_cast<const uint2*>(scales);
-      b.s0 = v.x;
-      b.s1 = v.y;
-    } else if (KB >= 64) {
-      b.s0 = *reinterpret_cast<const uint32_t*>(scales);
-    } else {
-      b.s0 = *reinterpret_cast<const uint16_t*>(scales);
+  for (int i = 0; i < BRegs<NV, KB>::kVec; ++i) b.c[i] = *reinterpret_cast<const uint4*>(codes + 64 * i);
+}
+
+// scale span of one super-step (KB/4 bytes) held by a lane
+template <int KB>
+struct SRegs {
+  static constexpr int kDw = KB / 16;
+  uint32_t d[kDw];
+};
+
+template <int KB>
+__device__ inline void s_load(const uint8_t* p, bool in, SRegs<KB>& s) {
+  if constexpr (SRegs<KB>::kDw >= 4) {
+#pragma unroll
+    for (int q = 0; q < SRegs<KB>::kDw; q += 4) {
+      const uint4 v = in ? *reinterpret_cast<const uint4*>(p + 4 * q) : make_uint4(0u, 0u, 0u, 0u);
+      s.d[q] = v.x;
+      s.d[q + 1] = v.y;
+      s.d[q + 2] = v.z;
+      s.d[q + 3] = v.w;
     }
+  } else {
+    const uint2 v = in ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
+    s.d[0] = v.x;
+    s.d[1] = v.y;
   }
 }
 
+// This lane's scale dwords of the current super-step from lane group i:
+// dword 2u + (g >> 1) of the span carries the lane's 2 bytes for uint4 u.
+template <int KB>
+__device__ inline void s_fetch(const SRegs<KB>& s, int src_addr, int ghi, uint32_t* out) {
+  constexpr int kVec = KB / 32;
+#pragma unroll
+  for (int u = 0; u < kVec; ++u) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)s.d[2 * u]);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr, (int)s.d[2 * u + 1]);
+    out[u] = ghi ? hi : lo;
+  }
+}
+
+__device__ inline h2v scale_pair_sel(uint32_t w, uint32_t sel) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w, w, sel), 1.0f, false);
+}
+
 template <bool NV, int KB, int J>
-__device__ inline h8v b_dec(const BRegs<NV, KB>& b) {
-  constexpr int j = J;
-  if (NV) {
-    const uint4 c = b.c[j >> 2];
-    const uint32_t w = (j & 3) == 0 ? c.x : (j & 3) == 1 ? c.y : (j & 3) == 2 ? c.z : c.w;
-    constexpr int blk = j >> 1;  // 16 values per scale byte
-    return dec_fp4x8(w, scale_pair_hw<(blk & 3)>(blk < 4 ? b.s0 : b.s1));
+__device__ inline h8v b_dec(const BRegs<NV, KB>& b, const uint32_t* sdw, uint32_t selA, uint32_t selB) {
+  constexpr int SPU = SkGeom<NV>::SPU;
+  const uint4 c = b.c[J / SPU];
+  if constexpr (NV) {
+    const uint32_t w = (J & 3) == 0 ? c.x : (J & 3) == 1 ? c.y : (J & 3) == 2 ? c.z : c.w;
+    return dec_fp4x8(w, scale_pair_sel(sdw[J / SPU], ((J & 3) >> 1) ? selB : selA));
   } else {
-    const uint4 c = b.c[j >> 1];
-    return (j & 1) ? dec_fp8x8(c.z, c.w) : dec_fp8x8(c.x, c.y);
+    return (J & 1) ? dec_fp8x8(c.z, c.w) : dec_fp8x8(c.x, c.y);
   }
 }
 
 template <bool NV, int KB, int NT, int J>
-__device__ inline void sk_mma_step(const _Float16* arow, const BRegs<NV, KB>* b, f4v* acc) {
-  const h8v a = *reinterpret_cast<const h8v*>(arow + 8 * J);
+__device__ inline void sk_mma_step(const _Float16* arow, const BRegs<NV, KB>* b, const uint32_t (*sdw)[KB / 32 > 0 ? KB / 32 : 1],
+                                   uint32_t selA, uint32_t selB, f4v* acc) {
+  constexpr int VPU = SkGeom<NV>::VPU, SPU = SkGeom<NV>::SPU;
+  constexpr int col = (J / SPU) * 4 * VPU + (J % SPU) * 8;  // plus g * VPU, folded into arow
+  const h8v a = *reinterpret_cast<const h8v*>(arow + col);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = mfma_f16(a, b_dec<NV, KB, J>(b[t]), acc[t]);
-  if constexpr (J + 1 < KB / 8) sk_mma_step<NV, KB, NT, J + 1>(arow, b, acc);
-}
-template <bool NV, int KB, int NT>
-__device__ inline void sk_mma(const _Float16* arow, const BRegs<NV, KB>* b, f4v* acc) {
-  sk_mma_step<NV, KB, NT, 0>(arow, b, acc);
+  for (int t = 0; t < NT; ++t) acc[t] = mfma_f16(a, b_dec<NV, KB, J>(b[t], sdw[t], selA, selB), acc[t]);
+  if constexpr (J + 1 < KB / 8) sk_mma_step<NV, KB, NT, J + 1>(arow, b, sdw, selA, selB, acc);
 }
 
 template <bool NV, bool G1, int KB, int NT>
-__global__ __launch_bounds__(256) void k_skinny(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
+__global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
                                                 int topk, const float* __restrict__ a_gs,
                                                 const float* __restrict__ a_rs, const uint8_t* __restrict__ wc,
                                                 const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
@@ -309,6 +352,8 @@ __global__ __launch_bounds__(256) void k_skinny(const _Float16* __restrict__ act
   constexpr int KS = 4 * KB;         // k per super-step
   constexpr int kAs = KS + 8;        // LDS row stride (f16), +8 pad
   constexpr int kAv = KS / 16 / 8;   // uint4 of A staged per thread (16 threads per row)
+  constexpr int VPU = SkGeom<NV>::VPU;
+  constexpr int kSV = KB / 32 > 0 ? KB / 32 : 1;  // scale dwords per lane and tile per super-step
   __shared__ __attribute__((aligned(16))) _Float16 As[2][16][kAs];
   if ((int)blockIdx.y >= *ntiles) return;
   const int4 ti = tiles[blockIdx.y];
@@ -324,25 +369,31 @@ __global__ __launch_bounds__(256) void k_skinny(const _Float16* __restrict__ act
   // GEMM1: NT/2 gate tiles + NT/2 up tiles -> 8*NT h columns per wave; GEMM2: 16*NT y columns
   const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * (G1 ? 8 * NT : 16 * NT);
   const int64_t cbytes = NV ? K / 2 : K;
+  constexpr int cstep = NV ? KS / 2 : KS;  // code bytes per row and super-step
+  constexpr int sstep = KS / 16;           // NVFP4 scale bytes per row and super-step
+  const int nsteps = (int)(K / KS);
   const uint8_t* crow[NT];
   const uint8_t* srow[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int64_t r = G1 ? (int64_t)e * 2 * I + (j >= NT / 2 ? I : 0) + n0 + 16 * (j % (NT / 2)) + m
                          : (int64_t)e * H + n0 + 16 * j + m;
-    crow[j] = wc + r * cbytes + (NV ? KB / 2 : KB) * g;
-    srow[j] = NV ? wsc + r * (K / 16) + (KB / 16) * g : nullptr;
+    crow[j] = wc + r * cbytes + 16 * g;
+    srow[j] = NV ? wsc + r * (K / 16) + (int64_t)sstep * g : nullptr;  // lane g: super-step 4q + g
   }
-  constexpr int cstep = NV ? KS / 2 : KS;  // code bytes per super-step
   f4v acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
+  // scale byte selectors: lane g's two bytes sit in half (g & 1) of each fetched dword
+  const uint32_t selA = (uint32_t)((g & 1) * 2) * 0x0101u, selB = selA + 0x0101u;
+  const int ghi = g >> 1;
 
   static_assert(kAv == 1 || kAv == 2 || kAv == 4, "activation staging: 1, 2 or 4 uint4 per thread");
   BRegs<NV, KB> b0[NT], b1[NT];
+  SRegs<KB> sc[NT];  // NVFP4 scale span of super-step 4q + g (this lane's share of the current group)
+  uint32_t sdw[NT][kSV];
   uint4 ra0, ra1, ra2, ra3;
-  const int nsteps = (int)(K / KS);
-  // prologue: super-step 0
+  // prologue: super-step 0 codes and activations, scale groups 0 and 1
   ra0 = reinterpret_cast<const uint4*>(asrc)[0];
   if constexpr (kAv >= 2) ra1 = reinterpret_cast<const uint4*>(asrc)[1];
   if constexpr (kAv >= 4) {
@@ -350,7 +401,11 @@ __global__ __launch_bounds__(256) void k_skinny(const _Float16* __restrict__ act
     ra3 = reinterpret_cast<const uint4*>(asrc)[3];
   }
 #pragma unroll
-  for (int j = 0; j < NT; ++j) b_load<NV, KB>(crow[j], srow[j], b0[j]);
+  for (int j = 0; j < NT; ++j) b_load<NV, KB>(crow[j], b0[j]);
+  if constexpr (NV) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) s_load<KB>(srow[j], g < nsteps, sc[j]);
+  }
   reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[0] = ra0;
   if constexpr (kAv >= 2) reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[1] = ra1;
   if constexpr (kAv >= 4) {
@@ -358,10 +413,20 @@ __global__ __launch_bounds__(256) void k_skinny(const _Float16* __restrict__ act
     reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[3] = ra3;
   }
   __syncthreads();
-  // two super-steps per iteration so the register set of each step is static
+  // two super-steps per iteration so the code register set of each step is static
 #define BSM_SK_STEP(ST, CUR, BC, BN)                                                                      \
   {                                                                                                       \
     const bool more = (ST) + 1 < nsteps;                                                                  \
+    if constexpr (NV) {                                                                                   \
+      /* every lane takes its scale bytes of this super-step from lane group gi, which then */           \
+      /* loads its span of super-step ST + 4 (needed four super-steps later) */                          \
+      const int gi = (ST) & 3;                                                                            \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j) s_fetch<KB>(sc[j], (m + 16 * gi) * 4, ghi, sdw[j]);  \
+      if (g == gi && (ST) + 4 < nsteps) {                                                                 \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                   \
+          s_load<KB>(srow[j] + (int64_t)((ST) + 4 - g) * sstep, true, sc[j]);                             \
+      }                                                                                                   \
+    }                                                                                                     \
     if (more) {                                                                                           \
       const int64_t ko = (int64_t)((ST) + 1) * KS;                                                        \
       ra0 = reinterpret_cast<const uint4*>(asrc + ko)[0];                                                 \
@@ -371,10 +436,9 @@ __global__ __launch_bounds__(256) void k_skinny(const _Float16* __restrict__ act
         ra3 = reinterpret_cast<const uint4*>(asrc + ko)[3];                                               \
       }                                                                                                   \
       _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                     \
-        b_load<NV, KB>(crow[j] + ((ST) + 1) * (int64_t)cstep,                                             \
-                       NV ? srow[j] + ((ST) + 1) * (int64_t)(KS / 16) : nullptr, BN[j]);                  \
+        b_load<NV, KB>(crow[j] + ((ST) + 1) * (int64_t)cstep, BN[j]);                                     \
     }                                                                                                     \
-    sk_mma<NV, KB, NT>(&As[CUR][m][KB * g], BC, acc);                                                     \
+    sk_mma_step<NV, KB, NT, 0>(&As[CUR][m][VPU * g], BC, sdw, selA, selB, acc);                           \
     if (more) {                                                                                           \
       reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[0] = ra0;                            \
       if constexpr (kAv >= 2) reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[1] = ra1;    \
@@ -607,13 +671,30 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
   const int64_t c4 = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 column index
   if (c4 * 4 >= H) return;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int j = 0; j < topk; ++j) {
-    const double w = (double)wts[t * topk + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + (int64_t)pair_row[t * topk + j] * H + c4 * 4);
-    acc[0] += w * (double)v.x;
-    acc[1] += w * (double)v.y;
-    acc[2] += w * (double)v.z;
-    acc[3] += w * (double)v.w;
+  for (int j0 = 0; j0 < topk; j0 += 8) {
+    // all row indices, then all y loads of up to 8 slots in flight; the sum stays in slot order
+    int row[8];
+    double w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool in = j0 + q < topk;
+      row[q] = in ? pair_row[t * topk + j0 + q] : 0;
+      w[q] = in ? (double)wts[t * topk + j0 + q] : 0.0;
+    }
+    float4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      v[q] = (j0 + q < topk) ? *reinterpret_cast<const float4*>(y + (int64_t)row[q] * H + c4 * 4)
+                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (j0 + q < topk) {
+        acc[0] += w[q] * (double)v[q].x;
+        acc[1] += w[q] * (double)v[q].y;
+        acc[2] += w[q] * (double)v[q].z;
+        acc[3] += w[q] * (double)v[q].w;
+      }
+    }
   }
   *reinterpret_cast<float4*>(out + t * H + c4 * 4) =
       make_float4((float)(scale * acc[0]), (float)(scale * acc[1]), (float)(scale * acc[2]), (float)(scale * acc[3]));
@@ -621,6 +702,74 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
 
 __global__ void k_copy_f32(const float* src, float* dst) {
   if (threadIdx.x == 0) dst[0] = src[0];
+}
+
+// Batches of at most one 64-token chunk (decode): masks, counts, offsets,
+// tile lists and rows in one workgroup.  Same results as the three kernels
+// above with a single chunk.
+__global__ __launch_bounds__(1024) void k_perm_small(const int32_t* __restrict__ ids, int64_t T, int topk, int64_t E,
+                                                     int* __restrict__ counts, int* __restrict__ offsets,
+                                                     int4* __restrict__ tiles_s, int* __restrict__ ntiles_s,
+                                                     int4* __restrict__ tiles_w, int* __restrict__ ntiles_w,
+                                                     int* __restrict__ row_pair, int* __restrict__ pair_row,
+                                                     uint32_t* __restrict__ h_amax) {
+  __shared__ unsigned long long lm[1024];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_ts[1024];
+  __shared__ int s_tw[1024];
+  const int e = threadIdx.x;
+  lm[e] = 0ull;
+  __syncthreads();
+  const int64_t P = T * topk;
+  for (int64_t p = threadIdx.x; p < P; p += 1024) atomicOr(&lm[ids[p]], 1ull << (p / topk));
+  __syncthreads();
+  const int total = (e < E) ? __popcll(lm[e]) : 0;
+  if (e < E) counts[e] = total;
+  const bool skinny = total <= kSkinnyMaxRows;
+  const int nts = (e < E && skinny) ? (total + kRowsPerTile - 1) / kRowsPerTile : 0;
+  const int ntw = (e < E && !skinny) ? (total + kWideRows - 1) / kWideRows : 0;
+  s_cnt[e] = total;
+  s_ts[e] = nts;
+  s_tw[e] = ntw;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int a = (e >= o) ? s_cnt[e - o] : 0;
+    const int b = (e >= o) ? s_ts[e - o] : 0;
+    const int c = (e >= o) ? s_tw[e - o] : 0;
+    __syncthreads();
+    s_cnt[e] += a;
+    s_ts[e] += b;
+    s_tw[e] += c;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int off = s_cnt[e] - total;
+    offsets[e] = off;
+    if (e == E - 1) {
+      offsets[E] = s_cnt[e];
+      *ntiles_s = s_ts[e];
+      *ntiles_w = s_tw[e];
+    }
+    const int ts0 = s_ts[e] - nts, tw0 = s_tw[e] - ntw;
+    for (int i = 0; i < nts; ++i) {
+      const int r = total - i * kRowsPerTile;
+      tiles_s[ts0 + i] = make_int4(e, off + i * kRowsPerTile, r < kRowsPerTile ? r : kRowsPerTile, 0);
+    }
+    for (int i = 0; i < ntw; ++i) {
+      const int r = total - i * kWideRows;
+      tiles_w[tw0 + i] = make_int4(e, off + i * kWideRows, r < kWideRows ? r : kWideRows, 0);
+    }
+  }
+  if (e == 0) *h_amax = 0u;
+  __syncthreads();  // s_cnt holds inclusive prefix counts
+  for (int64_t p = threadIdx.x; p < P; p += 1024) {
+    const int ex = ids[p];
+    const uint32_t bit = (uint32_t)(p / topk);
+    const uint64_t below = bit ? (lm[ex] & ((1ull << bit) - 1ull)) : 0ull;
+    const int pos = s_cnt[ex] - __popcll(lm[ex]) + __popcll(below);
+    row_pair[pos] = (int)p;
+    pair_row[p] = pos;
+  }
 }
 
 }  // namespace
@@ -684,11 +833,16 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   uint32_t* h_amax = reinterpret_cast<uint32_t*>(ws + L.h_amax);
 
   stage_mark(0, 0, st);
-  k_perm_masks<<<(unsigned)L.n_chunks, 256, 0, st>>>(a.ids, a.T, a.topk, a.E, L.n_chunks, masks, ccnt);
-  k_perm_scan<<<1, 1024, 0, st>>>(ccnt, a.E, L.n_chunks, cbase, counts, offsets, tiles, ntiles, tiles_w, ntiles_w,
-                                   h_amax);
-  k_perm_rows<<<(unsigned)((L.P + 255) / 256), 256, 0, st>>>(a.ids, L.P, a.topk, L.n_chunks, masks, cbase, offsets,
-                                                              row_pair, pair_row);
+  if (L.n_chunks == 1) {
+    k_perm_small<<<1, 1024, 0, st>>>(a.ids, a.T, a.topk, a.E, counts, offsets, tiles, ntiles, tiles_w, ntiles_w,
+                                     row_pair, pair_row, h_amax);
+  } else {
+    k_perm_masks<<<(unsigned)L.n_chunks, 256, 0, st>>>(a.ids, a.T, a.topk, a.E, L.n_chunks, masks, ccnt);
+    k_perm_scan<<<1, 1024, 0, st>>>(ccnt, a.E, L.n_chunks, cbase, counts, offsets, tiles, ntiles, tiles_w, ntiles_w,
+                                     h_amax);
+    k_perm_rows<<<(unsigned)((L.P + 255) / 256), 256, 0, st>>>(a.ids, L.P, a.topk, L.n_chunks, masks, cbase,
+                                                                offsets, row_pair, pair_row);
+  }
 #ifndef BSM_SKINNY_NT
 #define BSM_SKINNY_NT 2
 #endif

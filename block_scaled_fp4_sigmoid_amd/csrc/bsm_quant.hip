@@ -245,7 +245,9 @@ __global__ __launch_bounds__(kThreads) void k_fp8_rows(const void* __restrict__ 
 
 int nvfp4_amax_parts(int64_t R, int64_t C) {
   const int64_t n_blk = R * C / 16;
-  int64_t p = (n_blk + kThreads * 8 - 1) / (kThreads * 8);
+  // one block per thread while that fits: small tensors (decode-sized x and h)
+  // then cost one load latency instead of a serial chain of them
+  int64_t p = (n_blk + kThreads - 1) / kThreads;
   if (p < 1) p = 1;
   if (p > kAmaxMaxParts) p = kAmaxMaxParts;
   return (int)p;
@@ -254,7 +256,7 @@ int nvfp4_amax_parts(int64_t R, int64_t C) {
 size_t nvfp4_quant_ws(int64_t B, int64_t, int64_t) { return align256((size_t)B * kAmaxMaxParts * sizeof(float)); }
 
 static int encode_parts(int64_t n_blk, int64_t B) {
-  int64_t p = (n_blk + kThreads * 4 - 1) / (kThreads * 4);
+  int64_t p = (n_blk + kThreads - 1) / kThreads;
   if (p < 1) p = 1;
   const int64_t cap = B > 1 ? 256 : 4096;
   return (int)(p > cap ? cap : p);

@@ -89,18 +89,15 @@ __device__ inline void ld8(const void* p, int64_t i, float* v) {
   }
 }
 
-__global__ void k_route_prep(int* diag) {
-  if (threadIdx.x < 4) diag[threadIdx.x] = 0;
-}
-
 // Per row of x (rows 0..T-1) and of w (rows T..T+E-1), one wave per row: an
 // upper bound of the 2-norm and the lowest set-bit exponent of the row's
 // nonzero entries.
 template <bool XB, bool WB, bool VEC>
 __global__ __launch_bounds__(256) void k_rowstats(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
                                                   int64_t E, int64_t H, double* __restrict__ norm,
-                                                  int* __restrict__ lsb) {
+                                                  int* __restrict__ lsb, int* __restrict__ diag) {
   const int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && threadIdx.x < 4) diag[threadIdx.x] = 0;  // route diagnostics of this call
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= T + E) return;
   const bool isx = r < T;
@@ -147,6 +144,72 @@ __global__ __launch_bounds__(256) void k_rowstats(const void* __restrict__ x, co
   }
 }
 
+// Exact binary32 logit of one (token, expert) pair, computed by the whole
+// workgroup (every thread calls it; the result is valid in thread 0).  Every
+// product is exact in binary64.  Fast path: the fixed-point window of
+// bsm_numerics.h anchored one binade above A = |x|_2 |w|_2, which bounds every
+// product; a product more than 120 bits below it switches the workgroup to the
+// 22-digit superaccumulator.
+struct ExactLds {
+  long long d[4][WIN_DIGITS];
+  long long sa[SA_NDIG];
+  int bad;
+};
+
+template <bool XB, bool WB, int NT>
+__device__ float exact_logit_wg(const void* __restrict__ x, const void* __restrict__ w, int64_t t, int64_t e,
+                                int64_t H, double A, ExactLds* L) {
+  static_assert(NT == 256, "four waves");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int base = win_base((int)((d2u(A) >> 52) & 0x7FF) + 1);
+  if (tid == 0) L->bad = 0;
+  __syncthreads();
+  int64_t dig[WIN_DIGITS] = {0, 0, 0, 0, 0};
+  bool bad = false;
+  for (int64_t k = tid; k < H; k += NT) {
+    const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
+    bad |= !win_add(dig, p, base);
+  }
+  if (bad) atomicOr(&L->bad, 1);
+#pragma unroll
+  for (int q = 0; q < WIN_DIGITS; ++q) {
+    long long v = dig[q];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) L->d[wv][q] = v;
+  }
+  __syncthreads();
+  float r = 0.0f;
+  if (!L->bad) {
+    if (tid == 0) {
+      int64_t D[WIN_DIGITS];
+      for (int q = 0; q < WIN_DIGITS; ++q) {
+        long long acc = 0;
+        for (int ww = 0; ww < NW; ++ww) acc += L->d[ww][q];
+        D[q] = acc;
+      }
+      r = win_round_f32(D, base);
+    }
+  } else {
+    if (tid < SA_NDIG) L->sa[tid] = 0;
+    __syncthreads();
+    int64_t loc[SA_NDIG];
+    for (int q = 0; q < SA_NDIG; ++q) loc[q] = 0;
+    for (int64_t k = tid; k < H; k += NT) sa_add(loc, (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k));
+    for (int q = 0; q < SA_NDIG; ++q)
+      if (loc[q]) atomicAdd(reinterpret_cast<unsigned long long*>(&L->sa[q]), (unsigned long long)loc[q]);
+    __syncthreads();
+    if (tid == 0) {
+      int64_t dg[SA_NDIG];
+      for (int q = 0; q < SA_NDIG; ++q) dg[q] = L->sa[q];
+      r = sa_round_f32(dg);
+    }
+  }
+  __syncthreads();
+  return r;
+}
+
 // Binary32 rounding of a binary64 dot-product estimate S, when it can be
 // proven: (a) exact -- every partial sum is a multiple of 2^L (L = lsb(x) +
 // lsb(w)) below |x|_2 |w|_2 < 2^(L+53), so no addition rounded; or (b)
@@ -174,10 +237,14 @@ __device__ inline float certify_logit(double S, double nx, double nw, int lx, in
 template <bool XB, bool WB>
 __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
                                                    int64_t E, int64_t H, const double* __restrict__ norm,
-                                                   const int* __restrict__ lsb, int nadd, float* __restrict__ logits) {
+                                                   const int* __restrict__ lsb, int nadd, float* __restrict__ logits,
+                                                   int* __restrict__ diag) {
   constexpr int TT = kRbT, TE = kRbE, NV = TT * TE;
   static_assert(NV == 32, "reduce-scatter below assumes 32 outputs per workgroup");
   __shared__ double s_red[4][NV];
+  __shared__ int unc[NV];
+  __shared__ int n_unc;
+  __shared__ ExactLds xl;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t nte = (E + TE - 1) / TE;
   const int64_t b = blockIdx.x;
@@ -196,38 +263,60 @@ __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, c
   for (int i = 0; i < TT; ++i)
 #pragma unroll
     for (int j = 0; j < TE; ++j) acc[i][j] = 0.0;
-  for (int64_t k = (int64_t)tid * 8; k < H; k += kRbK) {
-    float xv[TT][8], wv8[TE][8];
+  // raw 8-value slices of the TT x rows and TE w rows; the next pass's slices
+  // are loaded before the current pass is multiplied
+  constexpr int XW = XB ? 4 : 8, WW = WB ? 4 : 8;  // dwords per 8-value slice
+  uint32_t xr[TT][XW], wr[TE][WW], xn[TT][XW], wn[TE][WW];
+  auto load_pass = [&](int64_t k, uint32_t (*xo)[XW], uint32_t (*wo)[WW]) {
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
-      if (t0 + i < T) {
-        ld8<XB>(x, (t0 + i) * H + k, xv[i]);
-      } else {
+      const bool in = (t0 + i < T) && (k < H);
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(x) + ((t0 + i) * H + k) / (XB ? 2 : 1);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) xv[i][q] = 0.0f;
+      for (int q = 0; q < XW; q += 4) {
+        const uint4 v = in ? *reinterpret_cast<const uint4*>(p + q) : make_uint4(0u, 0u, 0u, 0u);
+        xo[i][q] = v.x; xo[i][q + 1] = v.y; xo[i][q + 2] = v.z; xo[i][q + 3] = v.w;
       }
     }
 #pragma unroll
     for (int j = 0; j < TE; ++j) {
-      if (e0 + j < E) {
-        ld8<WB>(w, (e0 + j) * H + k, wv8[j]);
-      } else {
+      const bool in = (e0 + j < E) && (k < H);
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(w) + ((e0 + j) * H + k) / (WB ? 2 : 1);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) wv8[j][q] = 0.0f;
+      for (int q = 0; q < WW; q += 4) {
+        const uint4 v = in ? *reinterpret_cast<const uint4*>(p + q) : make_uint4(0u, 0u, 0u, 0u);
+        wo[j][q] = v.x; wo[j][q + 1] = v.y; wo[j][q + 2] = v.z; wo[j][q + 3] = v.w;
       }
     }
+  };
+  auto val = [](const uint32_t* r, int q, bool bf) -> double {
+    if (bf) return (double)u2f((q & 1) ? (r[q >> 1] & 0xFFFF0000u) : (r[q >> 1] << 16));
+    return (double)u2f(r[q]);
+  };
+  int64_t k = (int64_t)tid * 8;
+  load_pass(k, xr, wr);
+  for (; k < H; k += kRbK) {
+    load_pass(k + kRbK, xn, wn);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       double wd[TE];
 #pragma unroll
-      for (int j = 0; j < TE; ++j) wd[j] = (double)wv8[j][q];
+      for (int j = 0; j < TE; ++j) wd[j] = val(wr[j], q, WB);
 #pragma unroll
       for (int i = 0; i < TT; ++i) {
-        const double xd = (double)xv[i][q];
+        const double xd = val(xr[i], q, XB);
 #pragma unroll
         for (int j = 0; j < TE; ++j) acc[i][j] = fma(xd, wd[j], acc[i][j]);
       }
     }
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+#pragma unroll
+      for (int q = 0; q < XW; ++q) xr[i][q] = xn[i][q];
+#pragma unroll
+    for (int j = 0; j < TE; ++j)
+#pragma unroll
+      for (int q = 0; q < WW; ++q) wr[j][q] = wn[j][q];
   }
   double v[NV];
 #pragma unroll
@@ -251,11 +340,24 @@ __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, c
   }
   v[0] += __shfl_xor(v[0], 1, 64);
   if ((lane & 1) == 0) s_red[wv][lane >> 1] = v[0];
+  if (tid == 0) n_unc = 0;
   __syncthreads();
   if (tid < NV) {
     const double S = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
     const int64_t t = t0 + tid / TE, e = e0 + tid % TE;
-    if (t < T && e < E) logits[t * E + e] = certify_logit(S, norm[t], norm[T + e], lsb[t], lsb[T + e], nadd);
+    if (t < T && e < E) {
+      const float r = certify_logit(S, norm[t], norm[T + e], lsb[t], lsb[T + e], nadd);
+      logits[t * E + e] = r;
+      if (r != r) unc[atomicAdd(&n_unc, 1)] = tid;
+    }
+  }
+  __syncthreads();
+  const int nu = n_unc;
+  if (nu && tid == 0) atomicAdd(&diag[0], nu);
+  for (int u = 0; u < nu; ++u) {
+    const int64_t t = t0 + unc[u] / TE, e = e0 + unc[u] % TE;
+    const float r = exact_logit_wg<XB, WB, 256>(x, w, t, e, H, norm[t] * norm[T + e] * (1.0 + 0x1p-40), &xl);
+    if (tid == 0) logits[t * E + e] = r;
   }
 }
 
@@ -264,9 +366,13 @@ __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, c
 template <bool XB, bool WB>
 __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
                                                 int64_t E, int64_t H, const double* __restrict__ norm,
-                                                const int* __restrict__ lsb, int nadd, float* __restrict__ logits) {
+                                                const int* __restrict__ lsb, int nadd, float* __restrict__ logits,
+                                                int* __restrict__ diag) {
   __shared__ float xs[kBK][kTile + 4];
   __shared__ float wsm[kBK][kTile + 4];
+  __shared__ int unc[kTile * kTile];
+  __shared__ int n_unc;
+  __shared__ ExactLds xl;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * kTile, e0 = (int64_t)blockIdx.y * kTile;
@@ -311,6 +417,8 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, cons
       for (int j = 0; j < 4; ++j) acc[i][j] += blk[i][j];
     __syncthreads();
   }
+  if (tid == 0) n_unc = 0;
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t t = t0 + ty * 4 + i;
@@ -320,80 +428,21 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, cons
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t e = e0 + tx * 4 + j;
-      if (e < E) logits[t * E + e] = certify_logit(acc[i][j], nx, norm[T + e], lx, lsb[T + e], nadd);
-    }
-  }
-}
-
-// Exact binary32 logit of one (token, expert) pair, computed by the whole
-// workgroup (every thread must call it).  Every product is exact in binary64;
-// fast path: fixed-point window anchored at the largest product (bsm_numerics.h),
-// general path: 22-digit superaccumulator for products below the window.
-template <bool XB, bool WB, int NT>
-__device__ float exact_logit_wg(const void* __restrict__ x, const void* __restrict__ w, int64_t t, int64_t e,
-                                int64_t H, int* s_i, long long (*s_d)[WIN_DIGITS], int* s_bad, long long* s_sa) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int emax = 0;
-  for (int64_t k = tid; k < H; k += NT) {
-    const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
-    const int ex = (int)((d2u(p) >> 52) & 0x7FF);
-    emax = ex > emax ? ex : emax;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int v = __shfl_xor(emax, o, 64);
-    emax = v > emax ? v : emax;
-  }
-  if (lane == 0) s_i[wv] = emax;
-  if (tid == 0) *s_bad = 0;
-  __syncthreads();
-  emax = s_i[0];
-  for (int q = 1; q < NW; ++q) emax = s_i[q] > emax ? s_i[q] : emax;
-  const int base = win_base(emax);
-  int64_t dig[WIN_DIGITS] = {0, 0, 0, 0, 0};
-  bool bad = false;
-  for (int64_t k = tid; k < H; k += NT) {
-    const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
-    bad |= !win_add(dig, p, base);
-  }
-  if (bad) atomicOr(s_bad, 1);
-#pragma unroll
-  for (int q = 0; q < WIN_DIGITS; ++q) {
-    long long v = dig[q];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if (lane == 0) s_d[wv][q] = v;
-  }
-  __syncthreads();
-  float r = 0.0f;
-  if (!*s_bad) {
-    if (tid == 0) {
-      int64_t D[WIN_DIGITS];
-      for (int q = 0; q < WIN_DIGITS; ++q) {
-        long long acc = 0;
-        for (int ww = 0; ww < NW; ++ww) acc += s_d[ww][q];
-        D[q] = acc;
+      if (e < E) {
+        const float r = certify_logit(acc[i][j], nx, norm[T + e], lx, lsb[T + e], nadd);
+        logits[t * E + e] = r;
+        if (r != r) unc[atomicAdd(&n_unc, 1)] = (ty * 4 + i) * kTile + tx * 4 + j;
       }
-      r = win_round_f32(D, base);
-    }
-  } else {
-    if (tid < SA_NDIG) s_sa[tid] = 0;
-    __syncthreads();
-    int64_t loc[SA_NDIG];
-    for (int q = 0; q < SA_NDIG; ++q) loc[q] = 0;
-    for (int64_t k = tid; k < H; k += NT) sa_add(loc, (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k));
-    for (int q = 0; q < SA_NDIG; ++q)
-      if (loc[q]) atomicAdd(reinterpret_cast<unsigned long long*>(&s_sa[q]), (unsigned long long)loc[q]);
-    __syncthreads();
-    if (tid == 0) {
-      int64_t dg[SA_NDIG];
-      for (int q = 0; q < SA_NDIG; ++q) dg[q] = s_sa[q];
-      r = sa_round_f32(dg);
     }
   }
   __syncthreads();
-  return r;  // valid in thread 0
+  const int nu = n_unc;
+  if (nu && tid == 0) atomicAdd(&diag[0], nu);
+  for (int u = 0; u < nu; ++u) {
+    const int64_t t = t0 + unc[u] / kTile, e = e0 + unc[u] % kTile;
+    const float r = exact_logit_wg<XB, WB, 256>(x, w, t, e, H, norm[t] * norm[T + e] * (1.0 + 0x1p-40), &xl);
+    if (tid == 0) logits[t * E + e] = r;
+  }
 }
 
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
@@ -410,50 +459,23 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
 constexpr int kMaxE = 1024;
 constexpr int kSelThreads = 256;
 
-// One workgroup per token: logits the logits kernel could not prove are
-// recomputed exactly by the whole workgroup; then exactly rounded sigmoid
-// (binary64 certified, double-double fallback), group top-2 sums, group
-// selection, iterative (score, index) argmax in wave 0, normalization.
-template <bool XB, bool WB>
-__global__ __launch_bounds__(kSelThreads) void k_select(const void* __restrict__ x, const void* __restrict__ w,
-                                                        int64_t H, const float* __restrict__ logits, int64_t E,
-                                                        int n_group, int topk_group, int topk,
-                                                        int32_t* __restrict__ ids, float* __restrict__ wts,
-                                                        float* __restrict__ scores, int* __restrict__ diag) {
+// One workgroup per token: exactly rounded sigmoid (binary64 certified,
+// double-double fallback), group top-2 sums, group selection, iterative
+// (score, index) argmax in wave 0, normalization.
+__global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ logits, int64_t E, int n_group,
+                                                        int topk_group, int topk, int32_t* __restrict__ ids,
+                                                        float* __restrict__ wts, float* __restrict__ scores,
+                                                        int* __restrict__ diag) {
   __shared__ float s_lds[kMaxE];
   __shared__ unsigned long long keys[kMaxE];
-  __shared__ int unc[kMaxE];
   __shared__ float g_lds[64];
   __shared__ int kept[64];
-  __shared__ int n_unc;
-  __shared__ int s_i[kSelThreads / 64];
-  __shared__ long long s_d[kSelThreads / 64][WIN_DIGITS];
-  __shared__ int s_bad;
-  __shared__ long long s_sa[SA_NDIG];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
-  if (tid == 0) n_unc = 0;
-  __syncthreads();
-  for (int64_t e = tid; e < E; e += kSelThreads) {
-    const float l = logits[t * E + e];
-    s_lds[e] = l;
-    if (l != l) unc[atomicAdd(&n_unc, 1)] = (int)e;
-  }
-  __syncthreads();
-  const int nu = n_unc;
-  if (nu) {
-    if (tid == 0) atomicAdd(&diag[0], nu);
-    for (int u = 0; u < nu; ++u) {
-      const int e = unc[u];
-      const float r = exact_logit_wg<XB, WB, kSelThreads>(x, w, t, e, H, s_i, s_d, &s_bad, s_sa);
-      if (tid == 0) s_lds[e] = r;
-    }
-    __syncthreads();
-  }
   int nslow = 0;
   for (int64_t e = tid; e < E; e += kSelThreads) {
     bool fast;
-    const float sv = sigmoid_f32_exact(s_lds[e], &fast);
+    const float sv = sigmoid_f32_exact(logits[t * E + e], &fast);
     nslow += fast ? 0 : 1;
     s_lds[e] = sv;
     if (scores) scores[t * E + e] = sv;
@@ -533,23 +555,21 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   int* diag = reinterpret_cast<int*>(ws + L.diag);
   if (T == 0) return hipSuccess;
   stage_mark(1, 0, st);
-  k_route_prep<<<1, 64, 0, st>>>(diag);
   const unsigned nrs = (unsigned)((T + E + 3) / 4);
   const unsigned nrb = (unsigned)(((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE));
   dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
   const bool vec = (H % 8) == 0;
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
   if (vec)                                                                                                 \
-    k_rowstats<XB, WB, true><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                               \
+    k_rowstats<XB, WB, true><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb, diag);                               \
   else                                                                                                     \
-    k_rowstats<XB, WB, false><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                              \
+    k_rowstats<XB, WB, false><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb, diag);                              \
   if (L.rb)                                                                                                \
-    k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits);                    \
+    k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, diag);                    \
   else                                                                                                     \
-    k_logits<XB, WB><<<gl, 256, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits);                        \
+    k_logits<XB, WB><<<gl, 256, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, diag);                        \
   stage_mark(1, 1, st);                                                                                    \
-  k_select<XB, WB><<<(unsigned)T, kSelThreads, 0, st>>>(x, w, H, logits, E, n_group, topk_group, topk, ids, \
-                                                       wts, scores, diag);
+  k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, diag);
   if (xb && wb) {
     BSM_ROUTE_DISPATCH(true, true)
   } else if (xb && !wb) {

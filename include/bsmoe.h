@@ -163,7 +163,7 @@ int bsm_route_diagnostics(const void* ws, int64_t T, int64_t H, int64_t E, int32
  *   y    = decoded h times down of e
  *   out[t] = combine_scale * sum_j topk_weights[t, j] * y(t, j)   (float [T, H])
  * Requirements: H % 256 == 0, I % 128 == 0,
- * topk <= 32, ids in [0, E).  h_global_scale: NVFP4 STATIC -> read; DYNAMIC ->
+ * topk <= 32, ids in [0, E) and distinct within a token.  h_global_scale: NVFP4 STATIC -> read; DYNAMIC ->
  * written when non-NULL.  The layout of the workspace (stage buffers) is
  * reported by bsm_moe_workspace_layout for inspection.
  * ------------------------------------------------------------------------ */
@@ -222,6 +222,7 @@ int bsm_moe_expert_mlp(const bsm_moe_weights* w /* host */, const bsm_act_q* xq 
  *   which = 1, bsm_route (n = 3): [0] start, [1] after the logits kernel
  *     (row statistics, dot products, rounding proofs), [2] after the exact
  *     fallback of unproven logits, sigmoid and selection.
+ * A NULL entry skips its boundary (each recorded event costs GPU time).
  * n = 0 (events may be NULL) stops recording.  The library keeps the handle
  * values, not the events; they must stay valid while recording is on.
  * ------------------------------------------------------------------------ */

@@ -82,7 +82,11 @@ def test_route_exact_fallback_paths(gpu_lib):
     w[:, 1] = 1.0  # the two large terms cancel exactly; the binary64 bound is wide
     x[3, :] = 0.0
     x[3, :2] = [1.0, 2.0 ** -24]
-    w[:, 2:] = w[:, 2:]  # keep
+    # products spanning more than 120 bits (2^30 against about 2^-125): past the
+    # fixed-point window, into the superaccumulator
+    x[5, 0] = 2.0 ** 30
+    x[5, 1] = -(2.0 ** 30)
+    x[5, 2] = 2.0 ** -120
     ids, wts, scores, diag = _run(gpu_lib, x, w, 4, 2, 4, x_bf16=False, w_bf16=False)
     _check((ids, wts, scores, diag), x, w, 4, 2, 4)
     assert diag[0] > 0  # the fallback ran
