@@ -61,6 +61,72 @@ class HipEvents:
             self.hip.hipEventDestroy(h)
 
 
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "moe_decode64_nvfp4_traffic.json")
+GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_scaled_fp4_sigmoid_amd", "csrc", "bsm_moe.hip")
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read and 1 GiB written
+
+
+def _source_digest():
+    import hashlib
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def copy_calibration(dev):
+    """A plain elementwise copy of known size (1 GiB in, 1 GiB out) for scaling the HBM counters."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def _pmc_per_kernel(path):
+    """{kernel name: [counter value per dispatch]} from a rocprofv3 counter-collection CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch_csv, write_csv, command):
+    """Turn the FETCH_SIZE and WRITE_SIZE runs into HBM bytes per gate/up GEMM launch."""
+    fetch, write = _pmc_per_kernel(fetch_csv), _pmc_per_kernel(write_csv)
+
+    def pick(d, pred):
+        keys = [k for k in d if pred(k)]
+        assert keys, "kernel not found in the counter CSV"
+        return max(keys, key=lambda k: len(d[k]))
+
+    gemm = pick(fetch, lambda k: "k_skinny" in k and "ILb1ELb1ELi128" in k)
+    copyk = max((k for k in fetch if "elementwise" in k or "vectorized" in k), key=lambda k: max(fetch[k]))
+    f_copy, w_copy = max(fetch[copyk]), max(write[copyk])
+    sf, sw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    fb = float(np.mean(fetch[gemm])) * sf
+    wb = float(np.mean(write[gemm])) * sw
+    res = {"kernel": "k_skinny<NVFP4, gate/up> (decode-64)", "dispatches": len(fetch[gemm]),
+           "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "traffic_bytes_per_launch": fb + wb,
+           "copy_kernel": copyk[:80], "copy_counter_fetch": f_copy, "copy_counter_write": w_copy,
+           "scale_fetch": sf, "scale_write": sw, "gemm_source_sha256": _source_digest(), "command": command}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter runs, if they match this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t["traffic_bytes_per_launch"] if t.get("gemm_source_sha256") == _source_digest() else None
+
+
 def build_layer(cfg, fmt, dev):
     x = torch.from_numpy(W.activations(cfg)).to(dev, torch.bfloat16)
     wr = torch.from_numpy(W.router_weights(cfg)).to(dev, torch.bfloat16)
@@ -241,7 +307,14 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "stack"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB elementwise copy (reference for the HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write the gate/up GEMM HBM traffic from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -260,9 +333,14 @@ def main():
     print(f"[bench] {main_cfg.name} {args.fmt}: {ms:.3f} ms/step, stages {stage_ms}", file=sys.stderr, flush=True)
 
     g1 = main_nums["gemm1"]
+    traffic = measured_traffic() if (args.workload == "decode" and args.fmt == "nvfp4") else None
     roofline = {"bound": "hbm", "achieved": round(g1["gbps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(g1["gbps"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gate/up GEMM + SwiGLU",
+                "frac": round(g1["gbps"] / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else int(traffic), "traffic_unit": "bytes per launch",
+                "kernel": "gate/up GEMM + SwiGLU",
                 "algorithmic_bytes_per_launch": int(g1["bytes"]), "avg_launch_ms": round(g1["ms"], 4)}
+    if args.copy_calibration:
+        copy_calibration(dev)
 
     prefill = None
     if args.workload == "decode" and not args.no_prefill:
