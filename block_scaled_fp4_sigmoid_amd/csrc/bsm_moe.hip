@@ -500,16 +500,23 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Grouped GEMM for many rows per expert ("wide"): 128 rows x 128 weight rows
-// per workgroup, K in steps of 64 staged through LDS (double buffered).  The
-// weight tile is decoded to FP16 once per K step and reused by all 128 rows;
-// each wave computes 64 rows x 64 weight rows with 16 MFMA 16x16x32 tiles.
-// GEMM1 workgroup: weight rows = 64 gate rows c0.. and the 64 matching up
-// rows, so each wave holds g and u of the same 32 h columns (SwiGLU fused).
+// per workgroup, K in steps of 64 staged through LDS (double buffered).  The activation tile is staged as FP16; the weight
+// tile is staged as its raw codes (and NVFP4 scale bytes), a quarter (half,
+// FP8) of the FP16 bytes, and each wave decodes its B fragments after reading
+// them, which keeps LDS traffic below the matrix cores' demand.  Each wave
+// computes 64 rows x 64 weight rows with 16 MFMA 16x16x32 tiles.  GEMM1
+// workgroup: weight rows = 64 gate rows c0.. and the 64 matching up rows, so
+// each wave holds g and u of the same 32 h columns (SwiGLU fused).
 // ---------------------------------------------------------------------------
 constexpr int kWBM = 128, kWBN = 128, kWBK = 64, kLds = kWBK + 8;  // +8 f16 pad: conflict-free b128 reads
+// raw weight rows in LDS: NVFP4 32 B of codes per row and K step (+4 pad), FP8 64 B (+8 pad)
+template <bool NV>
+struct WideB {
+  static constexpr int kRow = NV ? 36 : 72;
+};
 
 template <bool NV, bool G1>
-__global__ __launch_bounds__(256, 2) void k_gemm_wide(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
+__global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
                                                       int topk, const float* __restrict__ a_gs,
                                                       const float* __restrict__ a_rs, const uint8_t* __restrict__ wc,
                                                       const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
@@ -517,7 +524,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(const _Float16* __restrict
                                                       int64_t K, int64_t H, int64_t I, float* __restrict__ out,
                                                       uint32_t* __restrict__ h_amax) {
   __shared__ __attribute__((aligned(16))) _Float16 As[2][kWBM][kLds];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kWBN][kLds];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kWBN][WideB<NV>::kRow];
+  __shared__ uint32_t Bsc[2][kWBN];  // NVFP4: the 4 scale bytes of a row and K step
   if ((int)blockIdx.y >= *ntiles) return;
   const int4 ti = tiles[blockIdx.y];
   const int e = ti.x, row0 = ti.y, nrows = ti.z;
@@ -538,43 +546,48 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(const _Float16* __restrict
   const uint8_t* bsrc = wc + wrow * cbytes + (NV ? 16 : 32) * kh;
   const uint8_t* ssrc = NV ? wsc + wrow * (K / 16) + 2 * kh : nullptr;
 
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1;
-  uint32_t rs = 0;
-#define BSM_WIDE_GLOAD(k0)                                                          \
+  // one register set holds the global loads of the next K step
+  uint4 raX0, raX1, raX2, raX3, rbX0, rbX1;
+  uint32_t rsX = 0;
+#define BSM_WIDE_GLOAD(k0, S)                                                       \
   {                                                                                 \
     const uint4* pa = reinterpret_cast<const uint4*>(asrc + (k0));                  \
-    ra0 = pa[0];                                                                    \
-    ra1 = pa[1];                                                                    \
-    ra2 = pa[2];                                                                    \
-    ra3 = pa[3];                                                                    \
+    ra##S##0 = pa[0];                                                               \
+    ra##S##1 = pa[1];                                                               \
+    ra##S##2 = pa[2];                                                               \
+    ra##S##3 = pa[3];                                                               \
     if (NV) {                                                                       \
-      rb0 = *reinterpret_cast<const uint4*>(bsrc + (k0) / 2);                       \
-      rs = *reinterpret_cast<const uint16_t*>(ssrc + (k0) / 16);                    \
+      rb##S##0 = *reinterpret_cast<const uint4*>(bsrc + (k0) / 2);                  \
+      rs##S = *reinterpret_cast<const uint16_t*>(ssrc + (k0) / 16);                 \
     } else {                                                                        \
       const uint4* pb = reinterpret_cast<const uint4*>(bsrc + (k0));                \
-      rb0 = pb[0];                                                                  \
-      rb1 = pb[1];                                                                  \
+      rb##S##0 = pb[0];                                                             \
+      rb##S##1 = pb[1];                                                             \
     }                                                                               \
   }
-#define BSM_WIDE_LSTORE(buf)                                                        \
+#define BSM_WIDE_LSTORE(buf, S)                                                     \
   {                                                                                 \
     uint4* da = reinterpret_cast<uint4*>(&As[buf][sr][32 * kh]);                    \
-    da[0] = ra0;                                                                    \
-    da[1] = ra1;                                                                    \
-    da[2] = ra2;                                                                    \
-    da[3] = ra3;                                                                    \
-    uint4* db = reinterpret_cast<uint4*>(&Bs[buf][sr][32 * kh]);                    \
+    da[0] = ra##S##0;                                                               \
+    da[1] = ra##S##1;                                                               \
+    da[2] = ra##S##2;                                                               \
+    da[3] = ra##S##3;                                                               \
+    uint32_t* db = reinterpret_cast<uint32_t*>(&Bs[buf][sr][0]);                    \
     if (NV) {                                                                       \
-      const h2v s0 = scale_pair_hw<0>(rs), s1 = scale_pair_hw<1>(rs);              \
-      db[0] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.x, s0));                      \
-      db[1] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.y, s0));                      \
-      db[2] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.z, s1));                      \
-      db[3] = __builtin_bit_cast(uint4, dec_fp4x8(rb0.w, s1));                      \
+      db[4 * kh + 0] = (rb##S##0).x;                                                \
+      db[4 * kh + 1] = (rb##S##0).y;                                                \
+      db[4 * kh + 2] = (rb##S##0).z;                                                \
+      db[4 * kh + 3] = (rb##S##0).w;                                                \
+      reinterpret_cast<uint16_t*>(&Bsc[buf][sr])[kh] = (uint16_t)rs##S;             \
     } else {                                                                        \
-      db[0] = __builtin_bit_cast(uint4, dec_fp8x8(rb0.x, rb0.y));                   \
-      db[1] = __builtin_bit_cast(uint4, dec_fp8x8(rb0.z, rb0.w));                   \
-      db[2] = __builtin_bit_cast(uint4, dec_fp8x8(rb1.x, rb1.y));                   \
-      db[3] = __builtin_bit_cast(uint4, dec_fp8x8(rb1.z, rb1.w));                   \
+      db[8 * kh + 0] = (rb##S##0).x;                                                \
+      db[8 * kh + 1] = (rb##S##0).y;                                                \
+      db[8 * kh + 2] = (rb##S##0).z;                                                \
+      db[8 * kh + 3] = (rb##S##0).w;                                                \
+      db[8 * kh + 4] = (rb##S##1).x;                                                \
+      db[8 * kh + 5] = (rb##S##1).y;                                                \
+      db[8 * kh + 6] = (rb##S##1).z;                                                \
+      db[8 * kh + 7] = (rb##S##1).w;                                                \
     }                                                                               \
   }
   // B rows of this wave's 4 column tiles: GEMM1 gate 0,1 / up 2,3; GEMM2 4 consecutive
@@ -585,30 +598,40 @@ __global__ __launch_bounds__(256, 2) void k_gemm_wide(const _Float16* __restrict
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f4v{0.f, 0.f, 0.f, 0.f};
+  // NVFP4 block of this lane's 8 values in sub-step s: 2s + (g >> 1) of the row's 4 scale bytes
+  const uint32_t selA = (uint32_t)(g >> 1) * 0x0101u, selB = selA + 0x0202u;
 
   const int nk = (int)(K / kWBK);
-  BSM_WIDE_GLOAD(0)
-  BSM_WIDE_LSTORE(0)
+  BSM_WIDE_GLOAD(0, X)
+  BSM_WIDE_LSTORE(0, X)
   __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) BSM_WIDE_GLOAD((int64_t)(ks + 1) * kWBK)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      h8v a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const h8v*>(&As[buf][wm * 64 + 16 * i + m][32 * s + 8 * g]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const h8v*>(&Bs[buf][BSM_WIDE_BROW(j) + m][32 * s + 8 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]);
-    }
-    if (ks + 1 < nk) BSM_WIDE_LSTORE(buf ^ 1)
-    __syncthreads();
+  // step ks: load step ks + 1, multiply from LDS, store step ks + 1 into the other buffer
+#define BSM_WIDE_STEP(ks)                                                           \
+  {                                                                                 \
+    const int buf = (ks) & 1;                                                       \
+    if ((ks) + 1 < nk) BSM_WIDE_GLOAD((int64_t)((ks) + 1) * kWBK, X)               \
+    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                 \
+      h8v a[4], b[4];                                                               \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                 \
+        a[i] = *reinterpret_cast<const h8v*>(&As[buf][wm * 64 + 16 * i + m][32 * s + 8 * g]); \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                               \
+        const uint8_t* brow = &Bs[buf][BSM_WIDE_BROW(j) + m][0];                    \
+        if (NV) {                                                                   \
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(brow + 16 * s + 4 * g); \
+          b[j] = dec_fp4x8(w, scale_pair_sel(Bsc[buf][BSM_WIDE_BROW(j) + m], s ? selB : selA)); \
+        } else {                                                                    \
+          const uint2 w = *reinterpret_cast<const uint2*>(brow + 32 * s + 8 * g);  \
+          b[j] = dec_fp8x8(w.x, w.y);                                               \
+        }                                                                           \
+      }                                                                             \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                 \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]); \
+    }                                                                               \
+    if ((ks) + 1 < nk) BSM_WIDE_LSTORE(buf ^ 1, X)                                  \
+    __syncthreads();                                                                \
   }
+  for (int ks = 0; ks < nk; ++ks) BSM_WIDE_STEP(ks)
+#undef BSM_WIDE_STEP
 #undef BSM_WIDE_GLOAD
 #undef BSM_WIDE_LSTORE
 #undef BSM_WIDE_BROW
