@@ -21,8 +21,12 @@ magnitude saturate to it.  Encoders here are written as "nearest entry of the
 value table", which makes that reading explicit; tests pin them against a
 brute-force argmin over the whole table.
 
+* BF16 (weight-only path's activations): the upper 16 bits of binary32;
+  rounding binary32 -> BF16 is round to nearest, ties to even.
+
 Parity: pinned (exhaustive decode vs. the bit-level definition, brute-force
-nearest encode over all midpoints +-1 ulp and random inputs).
+nearest encode over all midpoints +-1 ulp and random inputs; BF16 rounding
+against torch's conversion and constructed ties).
 """
 
 from fractions import Fraction
@@ -154,3 +158,16 @@ def f32_rounding_certified(v, err):
     mhi = (r64 + hi) / 2.0
     ok = (v - err > mlo) & (v + err < mhi) & np.isfinite(r64)
     return r, ok
+
+
+def bf16_round(a):
+    """binary32 -> nearest BF16 value (ties to even), returned as float32.
+
+    BF16 keeps the sign, the 8 exponent bits and the top 7 mantissa bits of
+    binary32; the dropped 16 bits round to nearest, ties to the even kept
+    mantissa.  Finite inputs only (the callers' values are finite).
+    """
+    b = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    keep_lsb = (b >> 16) & 1
+    r = ((b + 0x7FFF + keep_lsb) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)

@@ -14,6 +14,11 @@ Sources:
   and down projections are quantized.
 * "FP8 quantization" page, "Quantization scheme": W8A8 with per-output-channel
   weight scales and per-token activation scales.
+* "Beam-1.0 auf 4x NVIDIA RTX PRO 6000 Blackwell Server Edition" page,
+  section "NVFP4 auf Blackwell gegen FP8 auf Hopper" (and the H100 line of the
+  "NVFP4 quantization" page, "Hardware compatibility and serving"): without
+  FP4 arithmetic the NVFP4 experts run weight-only (W4A16) -- FP4 weights,
+  BF16 activations, 16-bit arithmetic speed.
 
 Readings (listed with the others in the design notes):
 * SwiGLU h = fl32(silu(g) * u), silu(g) = g / (1 + exp(-g)), evaluated in
@@ -23,6 +28,9 @@ Readings (listed with the others in the design notes):
   the comparison tolerance);
 * the intermediate h of the NVFP4 path carries ONE dynamic global scale over
   all (token, expert) rows of the call; the FP8 path quantizes h per row;
+* weight-only W4A16: the activations are the BF16 inputs themselves (no
+  activation quantization) and h is rounded to BF16 (nearest, ties to even)
+  before the down projection, the 16-bit activation type of the layer;
 * out[t] = fl32(2.5 * sum_j w[t, j] * y[t, j]) in float64, output float32;
 * rows of expert e are ordered by (token, slot) -- the stable order.
 * RMSNorm: ms = fl32(mean(x^2)) with the mean in float64, r = fl32(1 /
@@ -40,7 +48,7 @@ against a direct float64 evaluation only (tolerance parity).
 
 import numpy as np
 
-from . import quant
+from . import formats, quant
 from .route import route as _route
 
 F32 = np.float32
@@ -130,7 +138,14 @@ class FP8Expert:
 
 
 def quantize_activations(x, fmt, global_scale=None):
-    """Quantize activations and return (packed quantities, exact decoded float64)."""
+    """Quantize activations and return (packed quantities, exact decoded float64).
+
+    Weight-only W4A16 keeps the BF16 activations: (None, x) with x BF16-exact.
+    """
+    if fmt == "w4a16":
+        x = np.asarray(x, np.float32)
+        assert np.array_equal(formats.bf16_round(x), x), "W4A16 activations must be BF16 values"
+        return None, x.astype(np.float64)
     if fmt == "nvfp4":
         q = quant.nvfp4_quantize(x, global_scale)
         return q, quant.nvfp4_dequantize_exact(*q)
@@ -141,9 +156,10 @@ def quantize_activations(x, fmt, global_scale=None):
 def moe_expert_mlp(x_hat, ids, w, experts, fmt, combine_scale=2.5, h_global_scale=None):
     """Expert MLP on decoded activations.
 
-    x_hat: [T, H] exactly decoded (float64) quantized activations.
-    ids, w: [T, k] router output.  experts: mapping e -> NVFP4Expert / FP8Expert
-    (only the experts that appear in ids are touched).
+    x_hat: [T, H] exactly decoded (float64) quantized activations (W4A16: the
+    BF16 activations).  ids, w: [T, k] router output.  experts: mapping
+    e -> NVFP4Expert (NVFP4, W4A16) / FP8Expert (only the experts that appear
+    in ids are touched).  fmt: "nvfp4", "fp8" or "w4a16".
     Returns a dict with the stages in pair order p = t*k + j:
       g, u, h: [P, I] float32; hq: quantized h; y: [P, H] float32; out: [T, H].
     """
@@ -173,6 +189,9 @@ def moe_expert_mlp(x_hat, ids, w, experts, fmt, combine_scale=2.5, h_global_scal
     if fmt == "nvfp4":
         hq = quant.nvfp4_quantize(h, h_global_scale)
         h_hat = quant.nvfp4_dequantize_exact(*hq)
+    elif fmt == "w4a16":
+        hq = None
+        h_hat = formats.bf16_round(h).astype(np.float64)
     else:
         hq = quant.fp8_quantize(h)
         h_hat = quant.fp8_dequantize_exact(*hq)

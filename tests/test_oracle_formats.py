@@ -134,3 +134,20 @@ def test_round_fraction_to_f32_and_certification():
 def test_round_fraction_sign_symmetry(sign):
     q = Fraction(sign * 7, 3)
     assert F.round_fraction_to_f32(q) == sign * np.float32(7.0 / 3.0)
+
+
+def test_bf16_round_matches_torch_and_ties_to_even():
+    import torch
+    rng = np.random.default_rng(5)
+    a = np.concatenate([rng.standard_normal(50000) * 1e3, rng.standard_normal(50000) * 1e-30,
+                        rng.uniform(-7, 7, 50000)]).astype(np.float32)
+    # exact ties: low 16 bits 0x8000 with even and odd kept LSB
+    base = rng.integers(0, 0x7F00, 1000, dtype=np.uint32) << 16
+    ties = np.concatenate([base | 0x8000, (base | 0x10000) | 0x8000]).view(np.float32)
+    for v in (a, ties):
+        got = F.bf16_round(v)
+        ref = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # tie cases by hand: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> the even 1.0
+    assert F.bf16_round(np.float32([1 + 2.0 ** -8]))[0] == 1.0
+    assert F.bf16_round(np.float32([1 + 3 * 2.0 ** -8]))[0] == np.float32(1 + 2 * 2.0 ** -7)

@@ -20,7 +20,7 @@ def _bf16(a):
 
 def _experts(E, H, I, seed, fmt="nvfp4"):
     rng = np.random.default_rng(seed)
-    cls = M.NVFP4Expert if fmt == "nvfp4" else M.FP8Expert
+    cls = M.FP8Expert if fmt == "fp8" else M.NVFP4Expert
     out = {}
     for e in range(E):
         wg = _bf16(rng.standard_normal((I, H)) * 0.02)
@@ -76,7 +76,7 @@ def test_swiglu_reference_values():
     assert abs(h[1] - 2 * 0.7310585786300049) < 1e-6
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8", "w4a16"])
 def test_identical_experts_make_output_routing_independent(fmt):
     rng = np.random.default_rng(2)
     T, H, I, E, k = 16, 64, 32, 6, 3
@@ -161,3 +161,34 @@ def test_layer_tiny_runs_and_is_deterministic():
     r2 = M.moe_layer(x, wr, experts, "nvfp4", 4, 2, 2)
     assert np.array_equal(r1["out"], r2["out"])
     assert np.isfinite(r1["out"]).all() and np.abs(r1["out"]).max() > 0
+
+
+def test_weight_only_single_expert_matches_textbook_mlp():
+    """W4A16, k = 1, weight 1: out = 2.5 * W_d . bf16(silu(W_g x) * (W_u x)) on the raw BF16 x,
+    written with plain numpy and torch's BF16 conversion."""
+    import torch
+    rng = np.random.default_rng(8)
+    T, H, I, E = 10, 64, 32, 3
+    experts = _experts(E, H, I, 9)
+    x = _bf16(rng.standard_normal((T, H)))
+    xq, xh = M.quantize_activations(x, "w4a16")
+    assert xq is None and np.array_equal(xh, x.astype(np.float64))
+    ids = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    w = np.ones((T, 1), np.float32)
+    res = M.moe_expert_mlp(xh, ids, w, experts, "w4a16")
+    out = np.zeros((T, H), np.float32)
+    for t in range(T):
+        wg, wu, wd = experts[int(ids[t, 0])].decoded()
+        g = np.float64(np.float32(wg @ x[t].astype(np.float64)))
+        u = np.float64(np.float32(wu @ x[t].astype(np.float64)))
+        h = np.float32(g / (1 + np.exp(-g)) * u)
+        hb = torch.from_numpy(h).to(torch.bfloat16).double().numpy()
+        out[t] = np.float32(2.5 * np.float32(wd @ hb))
+    assert np.array_equal(out, res["out"])
+    assert res["hq"] is None
+
+
+def test_weight_only_rejects_non_bf16_activations():
+    x = np.float32([[1.0 + 2.0 ** -12, 1.0]])
+    with pytest.raises(AssertionError):
+        M.quantize_activations(x, "w4a16")
