@@ -11,7 +11,7 @@ run also measures the 8192-token prefill layer (Zipf-skewed router) and reports
 it under ``prefill_8192``.  Per-kernel times come from hipEvents recorded at
 the library's stage boundaries on the launch stream.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--fmt nvfp4|fp8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--fmt nvfp4|fp8|w4a16]
                        [--workload decode|prefill] [--no-prefill] [--no-cpu-baseline]
 """
 
@@ -131,7 +131,7 @@ def build_layer(cfg, fmt, dev):
     x = torch.from_numpy(W.activations(cfg)).to(dev, torch.bfloat16)
     wr = torch.from_numpy(W.router_weights(cfg)).to(dev, torch.bfloat16)
     w13, w2 = W.expert_weights_device(cfg, device=dev)
-    weights = bsm.quantize_expert_weights(w13, w2, fmt)
+    weights = bsm.quantize_expert_weights(w13, w2, "fp8" if fmt == "fp8" else "nvfp4")
     torch.cuda.synchronize()
     return x, wr, w13, w2, weights
 
@@ -152,6 +152,10 @@ def run_steps(cfg, fmt, x, wr, weights, steps, warmup):
     def step():
         nonlocal ws
         ids, wts = bsm.route(x, wr, cfg.n_group, cfg.topk_group, cfg.topk)
+        if fmt == "w4a16":  # weight-only: the BF16 activations go in as they are
+            o, ws = bsm.moe_expert_mlp_w4a16(weights, x, ids, wts, cfg.combine_scale, out=out, ws=ws,
+                                             return_workspace=True)
+            return ids
         xq = bsm.quantize_activations(x, fmt)
         o, ws = bsm.moe_expert_mlp(weights, xq, ids, wts, cfg.combine_scale, out=out, ws=ws, return_workspace=True)
         return ids
@@ -202,14 +206,15 @@ def layer_numbers(cfg, fmt, T, ms, stage_ms, g1_ms, counts):
     P = T * cfg.topk
     n_act = int((counts > 0).sum())
     flop = 2.0 * P * 3 * cfg.H * cfg.I + 2.0 * T * cfg.E * cfg.H
-    wbytes_per_expert = 3 * cfg.H * cfg.I * (NVFP4_BYTES_PER_WEIGHT if fmt == "nvfp4" else 1.0) + \
-        (0 if fmt == "nvfp4" else 4 * (2 * cfg.I + cfg.H))
+    nv = fmt != "fp8"  # NVFP4 weights (W4A4 and weight-only W4A16)
+    wbytes_per_expert = 3 * cfg.H * cfg.I * (NVFP4_BYTES_PER_WEIGHT if nv else 1.0) + \
+        (0 if nv else 4 * (2 * cfg.I + cfg.H))
     layer_bytes = n_act * wbytes_per_expert + T * cfg.H * 2 + cfg.E * cfg.H * 2 + T * cfg.H * 4
     # dominant kernel: gate/up GEMM.  Algorithmic bytes per launch: the gate+up weights of
     # every active expert, the quantized activations it reads, the FP32 h it writes.
-    g1_w = 2 * cfg.I * cfg.H * (NVFP4_BYTES_PER_WEIGHT if fmt == "nvfp4" else 1.0) + \
-        (0 if fmt == "nvfp4" else 4 * 2 * cfg.I)
-    g1_bytes = n_act * g1_w + T * cfg.H * (NVFP4_BYTES_PER_WEIGHT if fmt == "nvfp4" else 1.0) + P * cfg.I * 4
+    g1_w = 2 * cfg.I * cfg.H * (NVFP4_BYTES_PER_WEIGHT if nv else 1.0) + (0 if nv else 4 * 2 * cfg.I)
+    x_b = {"nvfp4": NVFP4_BYTES_PER_WEIGHT, "fp8": 1.0, "w4a16": 2.0}[fmt]
+    g1_bytes = n_act * g1_w + T * cfg.H * x_b + P * cfg.I * 4
     g1_flop = 2.0 * P * 2 * cfg.I * cfg.H
     return {
         "tokens_per_s": T / (ms * 1e-3),
@@ -234,7 +239,7 @@ def cpu_baseline(cfg, fmt, w13, w2, x_np, wr_np):
     from oracle import route as OR
 
     ids, wts, _, _ = OR.route(x_np, wr_np, cfg.n_group, cfg.topk_group, cfg.topk)
-    cls = OM.NVFP4Expert if fmt == "nvfp4" else OM.FP8Expert
+    cls = OM.FP8Expert if fmt == "fp8" else OM.NVFP4Expert
     tok = 1
     need = sorted(set(int(e) for e in ids[:tok].ravel()))
     experts = {}
@@ -303,7 +308,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "fp8"])
+    ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "fp8", "w4a16"])
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "stack"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -352,7 +357,7 @@ def main():
         pms, pst, pg1, pcounts = run_steps(pcfg, args.fmt, px, pwr, pweights, psteps, 2)
         pn = layer_numbers(pcfg, args.fmt, pcfg.T, pms, pst, pg1, pcounts)
         print(f"[bench] prefill {args.fmt}: {pms:.3f} ms/step, stages {pst}", file=sys.stderr, flush=True)
-        mm = "fp4" if args.fmt == "nvfp4" else "fp8"
+        mm = {"nvfp4": "fp4", "fp8": "fp8", "w4a16": "f16"}[args.fmt]
         prefill = {
             "tokens_per_s": round(pn["tokens_per_s"], 1), "ms_per_step": round(pms, 4),
             "tflops": round(pn["tflops"], 2), "frac_fp4_or_fp8_peak": round(pn["tflops"] / PEAK_TFLOPS[mm], 4),
@@ -383,7 +388,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4-e2m1 (exact f16 mfma, f32 acc)" if args.fmt == "nvfp4" else "fp8-e4m3 (exact f16 mfma, f32 acc)",
+        "dtype": {"nvfp4": "nvfp4-e2m1 (exact f16 mfma, f32 acc)", "fp8": "fp8-e4m3 (exact f16 mfma, f32 acc)",
+                  "w4a16": "nvfp4 weights, bf16 activations (exact bf16 mfma, f32 acc)"}[args.fmt],
         "data": "synthetic (seeded Beam-shaped activations, router and expert weights)",
         "config": {"workload": f"beam-{main_cfg.name}-{main_cfg.T} {args.fmt} MoE layer", "T": main_cfg.T,
                    "H": main_cfg.H, "I": main_cfg.I, "E": main_cfg.E, "n_group": main_cfg.n_group,

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libbsmoe.so")
 
 BSM_OK = 0
 BSM_BF16, BSM_F32 = 1, 2
-FMT_NVFP4, FMT_FP8 = 1, 2
+FMT_NVFP4, FMT_FP8, FMT_W4A16 = 1, 2, 3
 GS_DYNAMIC, GS_STATIC = 0, 1
 
 _lib = None
@@ -74,6 +74,7 @@ def load():
         "bsm_moe_workspace_layout": (i32, [i32, i64, i64, i64, i64, i32, ctypes.POINTER(_WsLayout)]),
         "bsm_moe_expert_mlp": (i32, [ctypes.POINTER(_MoeWeights), ctypes.POINTER(_ActQ), i64, vp, vp, i32, f32, i32,
                                      vp, vp, vp, sz, vp]),
+        "bsm_moe_expert_mlp_w4a16": (i32, [ctypes.POINTER(_MoeWeights), vp, i64, vp, vp, i32, f32, vp, vp, sz, vp]),
         "bsm_set_stage_events": (i32, [i32, ctypes.POINTER(vp), i32]),
         "bsm_rmsnorm_f32": (i32, [vp, i64, i64, f32, vp, vp]),
         "bsm_scaled_residual_f32": (i32, [vp, vp, f32, f32, i64, i64, vp]),
@@ -267,8 +268,8 @@ def quantize_activations(x: torch.Tensor, fmt: str):
 def moe_workspace_layout(fmt, E, H, I, T, topk):
     lib = load()
     lay = _WsLayout()
-    _check(lib.bsm_moe_workspace_layout(FMT_NVFP4 if fmt == "nvfp4" else FMT_FP8, E, H, I, T, topk,
-                                        ctypes.byref(lay)))
+    code = {"nvfp4": FMT_NVFP4, "fp8": FMT_FP8, "w4a16": FMT_W4A16}[fmt]
+    _check(lib.bsm_moe_workspace_layout(code, E, H, I, T, topk, ctypes.byref(lay)))
     return {n: getattr(lay, n) for n, _ in _WsLayout._fields_}
 
 
@@ -296,6 +297,29 @@ def moe_expert_mlp(weights: ExpertWeights, xq, ids, wts, combine_scale=2.5, h_gl
     _check(lib.bsm_moe_expert_mlp(ctypes.byref(wstruct), ctypes.byref(act), T, _ptr(ids), _ptr(wts), topk,
                                   float(combine_scale), mode, _ptr(h_global_scale), _ptr(out), _ptr(ws), ws.numel(),
                                   _stream()))
+    return (out, ws) if return_workspace else out
+
+
+def moe_expert_mlp_w4a16(weights: ExpertWeights, x, ids, wts, combine_scale=2.5, out=None, ws=None,
+                         return_workspace=False):
+    """Weight-only routed-expert MLP: NVFP4 ``weights``, BF16 activations ``x`` [T, H] -> out f32 [T, H]."""
+    lib = load()
+    _dev(x, "x")
+    _dev(ids, "ids")
+    _dev(wts, "wts")
+    if x.dtype != torch.bfloat16:
+        raise BsmError("the weight-only path takes BF16 activations")
+    if weights.format != FMT_NVFP4:
+        raise BsmError("the weight-only path takes NVFP4 weights")
+    T, topk = ids.shape
+    if out is None:
+        out = torch.empty((T, weights.H), dtype=torch.float32, device=ids.device)
+    need = lib.bsm_moe_workspace_size(FMT_W4A16, weights.E, weights.H, weights.I, T, topk)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, ids.device)
+    wstruct = weights._struct()
+    _check(lib.bsm_moe_expert_mlp_w4a16(ctypes.byref(wstruct), _ptr(x), T, _ptr(ids), _ptr(wts), topk,
+                                        float(combine_scale), _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return (out, ws) if return_workspace else out
 
 

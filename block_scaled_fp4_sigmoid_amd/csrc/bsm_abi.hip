@@ -155,16 +155,18 @@ int bsm_route_diagnostics(const void* ws, int64_t T, int64_t H, int64_t E, int32
   return hip_status(bsm::launch_route_diag(ws, T, H, E, diag, (hipStream_t)stream), "bsm_route_diagnostics");
 }
 
+static bool known_format(int f) { return f == BSM_FMT_NVFP4 || f == BSM_FMT_FP8 || f == BSM_FMT_W4A16; }
+
 size_t bsm_moe_workspace_size(int format, int64_t E, int64_t H, int64_t I, int64_t T, int topk) {
-  if ((format != BSM_FMT_NVFP4 && format != BSM_FMT_FP8) || E <= 0 || H <= 0 || I <= 0 || T < 0 || topk <= 0) return 0;
-  return bsm::moe_layout(format == BSM_FMT_NVFP4, E, H, I, T, topk).total;
+  if (!known_format(format) || E <= 0 || H <= 0 || I <= 0 || T < 0 || topk <= 0) return 0;
+  return bsm::moe_layout(format != BSM_FMT_FP8, E, H, I, T, topk).total;
 }
 
 int bsm_moe_workspace_layout(int format, int64_t E, int64_t H, int64_t I, int64_t T, int topk,
                              bsm_moe_ws_layout* out) {
-  if ((format != BSM_FMT_NVFP4 && format != BSM_FMT_FP8) || E <= 0 || H <= 0 || I <= 0 || T < 0 || topk <= 0 || !out)
+  if (!known_format(format) || E <= 0 || H <= 0 || I <= 0 || T < 0 || topk <= 0 || !out)
     return fail(BSM_ERR_INVALID_ARG, "bad arguments");
-  const bsm::MoeLayout L = bsm::moe_layout(format == BSM_FMT_NVFP4, E, H, I, T, topk);
+  const bsm::MoeLayout L = bsm::moe_layout(format != BSM_FMT_FP8, E, H, I, T, topk);
   out->total = L.total;
   out->counts = L.counts;
   out->offsets = L.offsets;
@@ -230,6 +232,53 @@ int bsm_moe_expert_mlp(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T,
   a.out = out;
   a.ws = (uint8_t*)ws;
   return hip_status(bsm::launch_moe(a, (hipStream_t)stream), "bsm_moe_expert_mlp");
+}
+
+int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w, const void* x, int64_t T, const int32_t* topk_ids,
+                             const float* topk_weights, int topk, float combine_scale, float* out, void* ws,
+                             size_t ws_bytes, bsm_stream_t stream) {
+  if (!w) return fail(BSM_ERR_INVALID_ARG, "NULL weights");
+  if (w->format != BSM_FMT_NVFP4) return fail(BSM_ERR_INVALID_ARG, "weight-only path needs NVFP4 weights");
+  const int64_t E = w->E, H = w->H, I = w->I;
+  if (E <= 0 || H <= 0 || I <= 0 || T < 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
+  if (H % 256 != 0 || I % 128 != 0) return fail(BSM_ERR_UNSUPPORTED, "H must be a multiple of 256 and I of 128");
+  if (E > 1024) return fail(BSM_ERR_UNSUPPORTED, "E > 1024");
+  if (topk < 1 || topk > 32 || topk > E) return fail(BSM_ERR_INVALID_ARG, "topk must be in [1, min(32, E)]");
+  if (T * topk > 0x3FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "T * topk too large");
+  if (T == 0) return ok();
+  if (!w->w13_codes || !w->w13_scales || !w->w2_codes || !w->w2_scales || !w->w13_gs || !w->w2_gs || !x ||
+      !topk_ids || !topk_weights || !out)
+    return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(w->w13_codes, 16) || !aligned(w->w2_codes, 16) || !aligned(x, 16) || !aligned(out, 16))
+    return fail(BSM_ERR_INVALID_ARG, "codes, x and out must be 16-byte aligned");
+  if (!aligned(w->w13_scales, 2) || !aligned(w->w2_scales, 2))
+    return fail(BSM_ERR_INVALID_ARG, "NVFP4 scales must be 2-byte aligned");
+  if (int r = check_ws(ws, ws_bytes, bsm::moe_layout(true, E, H, I, T, topk).total)) return r;
+  bsm::MoeArgs a;
+  a.nvfp4 = true;
+  a.a16 = true;
+  a.E = E;
+  a.H = H;
+  a.I = I;
+  a.T = T;
+  a.topk = topk;
+  a.w13_codes = w->w13_codes;
+  a.w13_scales = w->w13_scales;
+  a.w13_gs = w->w13_gs;
+  a.w2_codes = w->w2_codes;
+  a.w2_scales = w->w2_scales;
+  a.w2_gs = w->w2_gs;
+  a.x_codes = reinterpret_cast<const uint8_t*>(x);
+  a.x_scales = nullptr;
+  a.x_gs = nullptr;
+  a.ids = topk_ids;
+  a.wts = topk_weights;
+  a.combine_scale = combine_scale;
+  a.h_static = false;
+  a.h_gs_user = nullptr;
+  a.out = out;
+  a.ws = reinterpret_cast<uint8_t*>(ws);
+  return hip_status(bsm::launch_moe(a, (hipStream_t)stream), "bsm_moe_expert_mlp_w4a16");
 }
 
 int bsm_set_stage_events(int which, void* const* events, int n) {

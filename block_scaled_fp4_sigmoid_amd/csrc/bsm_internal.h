@@ -56,6 +56,7 @@ MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int
 
 struct MoeArgs {
   bool nvfp4;
+  bool a16 = false;  // weight-only W4A16: x_codes is BF16 x [T, H]; NVFP4 weights
   int64_t E, H, I, T;
   int topk;
   const uint8_t* w13_codes;

@@ -75,6 +75,17 @@ __device__ inline h2v scale_pair_hw(uint32_t w) {
 
 __device__ inline f4v mfma_f16(h8v a, h8v b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
+// Weight-only (W4A16) operands: BF16 bits carried in the same 8 x 16-bit containers.
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+template <bool A16>
+__device__ inline f4v mfma_ab(h8v a, h8v b, f4v c) {
+  if constexpr (A16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b), c, 0, 0, 0);
+  else
+    return mfma_f16(a, b, c);
+}
+
 __device__ inline float wave_max_f(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -202,6 +213,19 @@ __device__ inline h8v dec_fp4x8(uint32_t w, h2v s2) {
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
 }
+// E2M1 x E4M3 block scale -> BF16 (weight-only path): q exactly in FP32 from
+// the hardware converter, times s_b in FP32 (exact, <= 6 significant bits),
+// whose upper 16 bits are then the exact BF16 value.
+__device__ inline h8v dec_fp4x8_bf16(uint32_t w, float s) {
+  const f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  return __builtin_bit_cast(h8v, make_uint4(__builtin_amdgcn_perm(f2u(p0[1] * s), f2u(p0[0] * s), 0x07060302u),
+                                            __builtin_amdgcn_perm(f2u(p1[1] * s), f2u(p1[0] * s), 0x07060302u),
+                                            __builtin_amdgcn_perm(f2u(p2[1] * s), f2u(p2[0] * s), 0x07060302u),
+                                            __builtin_amdgcn_perm(f2u(p3[1] * s), f2u(p3[0] * s), 0x07060302u)));
+}
 __device__ inline h8v dec_fp8x8(uint32_t w0, uint32_t w1) {
   h8v r;
   const h2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
@@ -318,30 +342,32 @@ __device__ inline h2v scale_pair_sel(uint32_t w, uint32_t sel) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(w, w, sel), 1.0f, false);
 }
 
-template <bool NV, int KB, int J>
+template <bool NV, int KB, int J, bool A16>
 __device__ inline h8v b_dec(const BRegs<NV, KB>& b, const uint32_t* sdw, uint32_t selA, uint32_t selB) {
   constexpr int SPU = SkGeom<NV>::SPU;
   const uint4 c = b.c[J / SPU];
   if constexpr (NV) {
     const uint32_t w = (J & 3) == 0 ? c.x : (J & 3) == 1 ? c.y : (J & 3) == 2 ? c.z : c.w;
-    return dec_fp4x8(w, scale_pair_sel(sdw[J / SPU], ((J & 3) >> 1) ? selB : selA));
+    const h2v s2 = scale_pair_sel(sdw[J / SPU], ((J & 3) >> 1) ? selB : selA);
+    if constexpr (A16) return dec_fp4x8_bf16(w, (float)s2[0]);
+    return dec_fp4x8(w, s2);
   } else {
     return (J & 1) ? dec_fp8x8(c.z, c.w) : dec_fp8x8(c.x, c.y);
   }
 }
 
-template <bool NV, int KB, int NT, int J>
+template <bool NV, int KB, int NT, int J, bool A16>
 __device__ inline void sk_mma_step(const _Float16* arow, const BRegs<NV, KB>* b, const uint32_t (*sdw)[KB / 32 > 0 ? KB / 32 : 1],
                                    uint32_t selA, uint32_t selB, f4v* acc) {
   constexpr int VPU = SkGeom<NV>::VPU, SPU = SkGeom<NV>::SPU;
   constexpr int col = (J / SPU) * 4 * VPU + (J % SPU) * 8;  // plus g * VPU, folded into arow
   const h8v a = *reinterpret_cast<const h8v*>(arow + col);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = mfma_f16(a, b_dec<NV, KB, J>(b[t], sdw[t], selA, selB), acc[t]);
-  if constexpr (J + 1 < KB / 8) sk_mma_step<NV, KB, NT, J + 1>(arow, b, sdw, selA, selB, acc);
+  for (int t = 0; t < NT; ++t) acc[t] = mfma_ab<A16>(a, b_dec<NV, KB, J, A16>(b[t], sdw[t], selA, selB), acc[t]);
+  if constexpr (J + 1 < KB / 8) sk_mma_step<NV, KB, NT, J + 1, A16>(arow, b, sdw, selA, selB, acc);
 }
 
-template <bool NV, bool G1, int KB, int NT>
+template <bool NV, bool G1, int KB, int NT, bool A16 = false>
 __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
                                                 int topk, const float* __restrict__ a_gs,
                                                 const float* __restrict__ a_rs, const uint8_t* __restrict__ wc,
@@ -438,7 +464,7 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
       _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                     \
         b_load<NV, KB>(crow[j] + ((ST) + 1) * (int64_t)cstep, BN[j]);                                     \
     }                                                                                                     \
-    sk_mma_step<NV, KB, NT, 0>(&As[CUR][m][VPU * g], BC, sdw, selA, selB, acc);                           \
+    sk_mma_step<NV, KB, NT, 0, A16>(&As[CUR][m][VPU * g], BC, sdw, selA, selB, acc);                      \
     if (more) {                                                                                           \
       reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[0] = ra0;                            \
       if constexpr (kAv >= 2) reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[1] = ra1;    \
@@ -466,8 +492,9 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
         const int64_t col = n0 + 16 * q + m;
         float sg, su;
         if (NV) {
-          sg = a_gs[0] * wgs[2 * e];
-          su = a_gs[0] * wgs[2 * e + 1];
+          const float ag = A16 ? 1.0f : a_gs[0];  // weight-only: BF16 activations carry no scale
+          sg = ag * wgs[2 * e];
+          su = ag * wgs[2 * e + 1];
         } else {
           const float sx = a_rs[row_pair[row0 + ro] / topk];
           const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
@@ -481,7 +508,7 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
     } else {
       float* yr = out + (int64_t)(row0 + ro) * H + n0 + m;
       if (NV) {
-        const float sc = a_gs[0] * wgs[e];
+        const float sc = (A16 ? 1.0f : a_gs[0]) * wgs[e];
 #pragma unroll
         for (int j = 0; j < NT; ++j) yr[16 * j] = acc[j][r] * sc;
       } else {
@@ -515,7 +542,7 @@ struct WideB {
   static constexpr int kRow = NV ? 36 : 72;
 };
 
-template <bool NV, bool G1>
+template <bool NV, bool G1, bool A16 = false>
 __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
                                                       int topk, const float* __restrict__ a_gs,
                                                       const float* __restrict__ a_rs, const uint8_t* __restrict__ wc,
@@ -618,14 +645,15 @@ __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict
         const uint8_t* brow = &Bs[buf][BSM_WIDE_BROW(j) + m][0];                    \
         if (NV) {                                                                   \
           const uint32_t w = *reinterpret_cast<const uint32_t*>(brow + 16 * s + 4 * g); \
-          b[j] = dec_fp4x8(w, scale_pair_sel(Bsc[buf][BSM_WIDE_BROW(j) + m], s ? selB : selA)); \
+          const h2v s2 = scale_pair_sel(Bsc[buf][BSM_WIDE_BROW(j) + m], s ? selB : selA); \
+          b[j] = A16 ? dec_fp4x8_bf16(w, (float)s2[0]) : dec_fp4x8(w, s2);          \
         } else {                                                                    \
           const uint2 w = *reinterpret_cast<const uint2*>(brow + 32 * s + 8 * g);  \
           b[j] = dec_fp8x8(w.x, w.y);                                               \
         }                                                                           \
       }                                                                             \
       _Pragma("unroll") for (int i = 0; i < 4; ++i)                                 \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(a[i], b[j], acc[i][j]); \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma_ab<A16>(a[i], b[j], acc[i][j]); \
     }                                                                               \
     if ((ks) + 1 < nk) BSM_WIDE_LSTORE(buf ^ 1, X)                                  \
     __syncthreads();                                                                \
@@ -647,8 +675,9 @@ __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict
         float sg0, su0, sg1, su1;
         const int64_t col0 = c0 + wn * 32 + m, col1 = col0 + 16;
         if (NV) {
-          sg0 = sg1 = a_gs[0] * wgs[2 * e];
-          su0 = su1 = a_gs[0] * wgs[2 * e + 1];
+          const float ag = A16 ? 1.0f : a_gs[0];
+          sg0 = sg1 = ag * wgs[2 * e];
+          su0 = su1 = ag * wgs[2 * e + 1];
         } else {
           const float sx = a_rs[row_pair[row0 + ro] / topk];
           const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
@@ -666,7 +695,7 @@ __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict
       } else {
         float* yr = out + (int64_t)(row0 + ro) * H + c0 + wn * 64 + m;
         if (NV) {
-          const float sc = a_gs[0] * wgs[e];
+          const float sc = (A16 ? 1.0f : a_gs[0]) * wgs[e];
 #pragma unroll
           for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][r] * sc;
         } else {
@@ -795,6 +824,21 @@ __global__ __launch_bounds__(1024) void k_perm_small(const int32_t* __restrict__
   }
 }
 
+// h (FP32) -> BF16, round to nearest even (weight-only path's 16-bit activations); finite inputs
+__global__ __launch_bounds__(256) void k_h_to_bf16(const float* __restrict__ h, int64_t n4, uint16_t* __restrict__ o) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = reinterpret_cast<const float4*>(h)[i];
+  const float f[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t b = f2u(f[q]);
+    r[q] = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  }
+  reinterpret_cast<uint2*>(o)[i] = make_uint2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
+}
+
 }  // namespace
 
 MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int topk) {
@@ -877,7 +921,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   _Float16* hdec = reinterpret_cast<_Float16*>(ws + L.h_f16);
   const int64_t xblk = a.T * a.H / 16;
   const unsigned gx = (unsigned)((xblk + 255) / 256);
-  if (a.nvfp4)
+  if (a.a16)
+    act = reinterpret_cast<_Float16*>(const_cast<uint8_t*>(a.x_codes));  // BF16 x, read as 16-bit containers
+  else if (a.nvfp4)
     k_decode_act<true><<<gx, 256, 0, st>>>(a.x_codes, reinterpret_cast<const uint8_t*>(a.x_scales), xblk, act);
   else
     k_decode_act<false><<<gx, 256, 0, st>>>(a.x_codes, nullptr, xblk, act);
@@ -896,11 +942,33 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
                                               a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
   k_gemm_wide<NV, false><<<w2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
                                              a.w2_codes, w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
-  hipError_t err;
-  if (a.nvfp4) {
 #ifndef BSM_NV_KB
 #define BSM_NV_KB 128
 #endif
+  hipError_t err;
+  if (a.a16) {
+    // weight-only W4A16: BF16 activations, NVFP4 weights decoded to BF16, h rounded to BF16
+#define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K, KB)                                               \
+  k_skinny<true, G, KB, BSM_SKINNY_NT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, \
+                                                                   tiles, ntiles, K, a.H, a.I, OUT, h_amax);   \
+  k_gemm_wide<true, G, true><<<WGRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,     \
+                                                    ntiles_w, K, a.H, a.I, OUT, h_amax)
+    if (a.H % (4 * BSM_NV_KB) == 0) {
+      BSM_A16_G(true, act, xrs, a.w13_codes, w13s, a.w13_gs, h_f32, g1, w1, a.H, BSM_NV_KB);
+    } else {
+      BSM_A16_G(true, act, xrs, a.w13_codes, w13s, a.w13_gs, h_f32, g1, w1, a.H, 32);
+    }
+    stage_mark(0, 2, st);
+    const int64_t n4 = L.P * a.I / 4;
+    k_h_to_bf16<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(h_f32, n4, reinterpret_cast<uint16_t*>(hdec));
+    stage_mark(0, 3, st);
+    if (a.I % (4 * BSM_NV_KB) == 0) {
+      BSM_A16_G(false, hdec, nullptr, a.w2_codes, w2s, a.w2_gs, y, g2, w2, a.I, BSM_NV_KB);
+    } else {
+      BSM_A16_G(false, hdec, nullptr, a.w2_codes, w2s, a.w2_gs, y, g2, w2, a.I, 32);
+    }
+#undef BSM_A16_G
+  } else if (a.nvfp4) {
     if (a.H % (4 * BSM_NV_KB) == 0) {
       BSM_G1(true, BSM_NV_KB);
     } else {

@@ -368,8 +368,8 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, cons
                                                 int64_t E, int64_t H, const double* __restrict__ norm,
                                                 const int* __restrict__ lsb, int nadd, float* __restrict__ logits,
                                                 int* __restrict__ diag) {
-  __shared__ float xs[kBK][kTile + 4];
-  __shared__ float wsm[kBK][kTile + 4];
+  __shared__ double xs[kBK][kTile + 2];  // converted to binary64 once per staged element
+  __shared__ double wsm[kBK][kTile + 2];
   __shared__ int unc[kTile * kTile];
   __shared__ int n_unc;
   __shared__ ExactLds xl;
@@ -390,8 +390,8 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, cons
       for (int q = 0; q < 8; ++q) {
         const int64_t k = kb + lk + q;
         const bool kin = k < H;
-        xs[lk + q][lr] = (kin && t < T) ? ld1<XB>(x, t * H + k) : 0.0f;
-        wsm[lk + q][lr] = (kin && e < E) ? ld1<WB>(w, e * H + k) : 0.0f;
+        xs[lk + q][lr] = (kin && t < T) ? (double)ld1<XB>(x, t * H + k) : 0.0;
+        wsm[lk + q][lr] = (kin && e < E) ? (double)ld1<WB>(w, e * H + k) : 0.0;
       }
     }
     __syncthreads();
@@ -402,10 +402,12 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, cons
       for (int j = 0; j < 4; ++j) blk[i][j] = 0.0;
 #pragma unroll 4
     for (int kk = 0; kk < kBK; ++kk) {
-      const float4 a = *reinterpret_cast<const float4*>(&xs[kk][ty * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&wsm[kk][tx * 4]);
-      const double av[4] = {(double)a.x, (double)a.y, (double)a.z, (double)a.w};
-      const double bv[4] = {(double)b.x, (double)b.y, (double)b.z, (double)b.w};
+      const double2 a01 = *reinterpret_cast<const double2*>(&xs[kk][ty * 4]);
+      const double2 a23 = *reinterpret_cast<const double2*>(&xs[kk][ty * 4 + 2]);
+      const double2 b01 = *reinterpret_cast<const double2*>(&wsm[kk][tx * 4]);
+      const double2 b23 = *reinterpret_cast<const double2*>(&wsm[kk][tx * 4 + 2]);
+      const double av[4] = {a01.x, a01.y, a23.x, a23.y};
+      const double bv[4] = {b01.x, b01.y, b23.x, b23.y};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll

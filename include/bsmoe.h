@@ -21,7 +21,12 @@
  *            two best scores, top 8 experts within them, SwiGLU experts with
  *            intermediate 2560, outputs combined with normalized router
  *            weights and scaled by 2.5.
- *   [NUM]    same page, section "Residual stream and numerical decisions":
+ *   [WO]     "Beam-1.0 auf 4x NVIDIA RTX PRO 6000 Blackwell Server Edition"
+ *            page, section "NVFP4 auf Blackwell gegen FP8 auf Hopper" (and
+ *            the H100 line of the [NVFP4] page's "Hardware compatibility and
+ *            serving"): without FP4 arithmetic the NVFP4 experts run
+ *            weight-only, FP4 weights with BF16 activations (W4A16).
+ *   [NUM]    same page as [MOE], section "Residual stream and numerical decisions":
  *            router, SwiGLU product and norms in FP32; residual step k adds
  *            the sublayer output with weight 1/sqrt(k) and keeps the stream
  *            with weight sqrt((k-1)/k).
@@ -68,7 +73,7 @@ enum bsm_status {
 };
 
 enum bsm_dtype { BSM_BF16 = 1, BSM_F32 = 2 };
-enum bsm_format { BSM_FMT_NVFP4 = 1, BSM_FMT_FP8 = 2 };
+enum bsm_format { BSM_FMT_NVFP4 = 1, BSM_FMT_FP8 = 2, BSM_FMT_W4A16 = 3 /* workspace sizing only */ };
 enum bsm_gs_mode { BSM_GS_DYNAMIC = 0, BSM_GS_STATIC = 1 };
 
 /* Library version (BSM_ABI_VERSION). */
@@ -210,15 +215,37 @@ int bsm_moe_expert_mlp(const bsm_moe_weights* w /* host */, const bsm_act_q* xq 
                        bsm_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Weight-only W4A16 routed-expert MLP [WO] [MOE] [NUM]
+ *
+ * w: NVFP4 weights in the canonical layout above (format BSM_FMT_NVFP4).
+ * x: BF16 [T, H] (device), the layer input itself; no activation
+ * quantization.  For every pair (t, j), e = topk_ids[t, j]:
+ *   g, u = binary32-accumulated products of x[t] with the exactly decoded
+ *          gate / up rows (q * s_b * S_g; q * s_b is exact in BF16)
+ *   h    = silu(g) * u in binary32, rounded to BF16 (nearest, ties to even)
+ *   y    = binary32-accumulated products of h with the decoded down rows
+ *   out[t] = combine_scale * sum_j topk_weights[t, j] * y(t, j)  (float [T, H])
+ * Requirements as bsm_moe_expert_mlp (H % 256 == 0, I % 128 == 0, topk <= 32,
+ * ids in [0, E) and distinct within a token); x 16-byte aligned.  Workspace:
+ * bsm_moe_workspace_size(BSM_FMT_W4A16, ...); its layout
+ * (bsm_moe_workspace_layout with BSM_FMT_W4A16) has h_f32 as above, h_codes
+ * and h_scales unused.
+ * ------------------------------------------------------------------------ */
+int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w /* host */, const void* x, int64_t T,
+                             const int32_t* topk_ids, const float* topk_weights, int topk, float combine_scale,
+                             float* out, void* ws, size_t ws_bytes, bsm_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Profiling aid (not part of the method): stage-boundary events.
  *
  * After bsm_set_stage_events(which, events, n) with n > 0, every later call
  * made by the calling thread records events[i] (hipEvent_t handles created and
  * owned by the caller) on the call's stream at its stage boundaries, so the
  * caller can time individual kernels with hipEventElapsedTime:
- *   which = 0, bsm_moe_expert_mlp (n = 6): [0] start, [1] after the
- *     permutation, [2] after the gate/up GEMM + SwiGLU, [3] after the h
- *     quantization, [4] after the down GEMM, [5] after the combine;
+ *   which = 0, bsm_moe_expert_mlp / _w4a16 (n = 6): [0] start, [1] after
+ *     the permutation, [2] after the gate/up GEMM + SwiGLU, [3] after the h
+ *     quantization (W4A16: BF16 rounding), [4] after the down GEMM, [5]
+ *     after the combine;
  *   which = 1, bsm_route (n = 3): [0] start, [1] after the logits kernel
  *     (row statistics, dot products, rounding proofs), [2] after the exact
  *     fallback of unproven logits, sigmoid and selection.

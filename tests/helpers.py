@@ -39,7 +39,7 @@ def host_masters(cfg, layer=0):
 
 
 def oracle_experts(masters, fmt, ids=None):
-    cls = OM.NVFP4Expert if fmt == "nvfp4" else OM.FP8Expert
+    cls = OM.FP8Expert if fmt == "fp8" else OM.NVFP4Expert  # W4A16 uses the NVFP4 weights
     keep = range(len(masters)) if ids is None else sorted(set(int(e) for e in np.asarray(ids).ravel()))
     return {e: cls(*masters[e]) for e in keep}
 

@@ -104,3 +104,21 @@ def test_norm_validation(lib):
     assert lib.bsm_rmsnorm_f32(FAKE, 4, 16, -1.0, FAKE, None) == 1
     assert lib.bsm_scaled_residual_f32(None, FAKE, 1.0, 1.0, 4, 16, None) == 1
     assert lib.bsm_rmsnorm_f32(None, 0, 16, 1e-6, None, None) == 0
+
+
+def test_weight_only_moe_validation(lib):
+    w = bsm._MoeWeights(1, 256, 5120, 2560, 0x100000, 0x100000, 0x100000, 0x100000, 0x100000, 0x100000)
+    ref = ctypes.byref
+    f = lib.bsm_moe_expert_mlp_w4a16
+    assert f(ref(w), FAKE, 64, FAKE, FAKE, 8, 2.5, FAKE, None, 0, None) == 3   # no workspace
+    w8 = bsm._MoeWeights(2, 256, 5120, 2560, 0x100000, 0x100000, None, 0x100000, 0x100000, None)
+    assert f(ref(w8), FAKE, 64, FAKE, FAKE, 8, 2.5, FAKE, None, 0, None) == 1  # FP8 weights
+    bad = bsm._MoeWeights(1, 256, 5120, 2500, 0x100000, 0x100000, 0x100000, 0x100000, 0x100000, 0x100000)
+    assert f(ref(bad), FAKE, 64, FAKE, FAKE, 8, 2.5, FAKE, None, 0, None) == 2  # I % 128
+    assert f(ref(w), None, 64, FAKE, FAKE, 8, 2.5, FAKE, None, 0, None) == 1     # NULL x
+    assert f(ref(w), 0x100008, 64, FAKE, FAKE, 8, 2.5, FAKE, None, 0, None) == 1  # x misaligned
+    assert f(ref(w), FAKE, 64, FAKE, FAKE, 33, 2.5, FAKE, None, 0, None) == 1   # topk > 32
+    assert f(ref(w), FAKE, 0, None, None, 8, 2.5, None, None, 0, None) == 0     # empty batch
+    assert lib.bsm_moe_workspace_size(3, 256, 5120, 2560, 64, 8) == lib.bsm_moe_workspace_size(1, 256, 5120, 2560,
+                                                                                             64, 8)
+    assert lib.bsm_moe_workspace_size(4, 256, 5120, 2560, 64, 8) == 0
