@@ -303,13 +303,63 @@ def run_stack(args, dev):
     print(json.dumps(line))
 
 
+def run_dense_fp8(args, dev):
+    """Dense FP8_DYNAMIC block at decode (64 tokens): attention q/k/v/gate/o projections and the dense
+    SwiGLU MLP (hidden 5120, intermediate 20480), all W8A8 with per-channel / per-token scales."""
+    T, H, I, NQ, NKV = 64, 5120, 20480, 6144, 1024
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5120)
+
+    def w(n, k):
+        return bsm.fp8_quantize((torch.randn((n, k), generator=gen, device=dev) * 0.02).to(torch.bfloat16))
+
+    proj = {"q": w(NQ, H), "k": w(NKV, H), "v": w(NKV, H), "gate": w(NQ, H), "o": w(H, NQ)}
+    w13 = (torch.randn((1, 2 * I, H), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn((1, H, I), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    mlp = bsm.quantize_expert_weights(w13, w2, "fp8")
+    del w13, w2
+    x = torch.from_numpy(W.activations(W.DECODE)).to(dev, torch.bfloat16)
+    outs = {k: torch.empty((T, v[0].shape[0]), dtype=torch.float32, device=dev) for k, v in proj.items()}
+    mlp_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+    def step():
+        xq = bsm.fp8_quantize(x)
+        for k in ("q", "k", "v", "gate"):
+            bsm.fp8_linear(xq, proj[k], out=outs[k])
+        bsm.fp8_linear(bsm.fp8_quantize(outs["q"]), proj["o"], out=outs["o"])
+        bsm.fp8_dense_mlp(mlp, x, out=mlp_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    wbytes = sum(v[0].numel() + 4 * v[1].numel() for v in proj.values()) + \
+        mlp.w13_codes.numel() + mlp.w2_codes.numel() + 4 * (mlp.w13_scales.numel() + mlp.w2_scales.numel())
+    gbps = wbytes / (ms * 1e-3) / 1e9
+    print(f"[bench] dense fp8 block: {ms:.3f} ms/step, {gbps:.0f} GB/s of weights", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "dense FP8_DYNAMIC block tokens/s (attention projections + dense MLP), decode-64",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8-e4m3 (exact f16 mfma, f32 acc)", "data": "synthetic",
+        "config": {"workload": "beam dense fp8 block: q/k/v/gate/o projections + dense SwiGLU MLP, 64 tokens",
+                   "T": T, "H": H, "I_dense": I, "q_heads": 48, "kv_heads": 8, "head_dim": 128},
+        "gbps_weights": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBS, 4), "weight_bytes": int(wbytes)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "fp8", "w4a16"])
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "stack"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "stack", "dense-fp8"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -330,6 +380,9 @@ def main():
 
     if args.workload == "stack":
         run_stack(args, dev)
+        return
+    if args.workload == "dense-fp8":
+        run_dense_fp8(args, dev)
         return
     main_cfg = W.DECODE if args.workload == "decode" else W.PREFILL
     x, wr, w13, w2, weights = build_layer(main_cfg, args.fmt, dev)

@@ -75,6 +75,8 @@ def load():
         "bsm_moe_expert_mlp": (i32, [ctypes.POINTER(_MoeWeights), ctypes.POINTER(_ActQ), i64, vp, vp, i32, f32, i32,
                                      vp, vp, vp, sz, vp]),
         "bsm_moe_expert_mlp_w4a16": (i32, [ctypes.POINTER(_MoeWeights), vp, i64, vp, vp, i32, f32, vp, vp, sz, vp]),
+        "bsm_fp8_linear_workspace_size": (sz, [i64, i64, i64]),
+        "bsm_fp8_linear": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         "bsm_set_stage_events": (i32, [i32, ctypes.POINTER(vp), i32]),
         "bsm_rmsnorm_f32": (i32, [vp, i64, i64, f32, vp, vp]),
         "bsm_scaled_residual_f32": (i32, [vp, vp, f32, f32, i64, i64, vp]),
@@ -321,6 +323,37 @@ def moe_expert_mlp_w4a16(weights: ExpertWeights, x, ids, wts, combine_scale=2.5,
     _check(lib.bsm_moe_expert_mlp_w4a16(ctypes.byref(wstruct), _ptr(x), T, _ptr(ids), _ptr(wts), topk,
                                         float(combine_scale), _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return (out, ws) if return_workspace else out
+
+
+def fp8_linear(xq, wq, out=None, ws=None):
+    """Dense FP8_DYNAMIC linear: xq = fp8_quantize(x [T, K]), wq = fp8_quantize(W [N, K]) -> out f32 [T, N]."""
+    lib = load()
+    xc, xs = xq
+    wc, wsc = wq
+    for t, n in ((xc, "x codes"), (xs, "x scales"), (wc, "w codes"), (wsc, "w scales")):
+        _dev(t, n)
+    T, K = xc.shape
+    N = wc.shape[0]
+    if wc.shape[1] != K:
+        raise BsmError("x and W disagree on K")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=xc.device)
+    need = lib.bsm_fp8_linear_workspace_size(T, K, N)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, xc.device)
+    _check(lib.bsm_fp8_linear(_ptr(xc), _ptr(xs), _ptr(wc), _ptr(wsc), T, K, N, _ptr(out), _ptr(ws), ws.numel(),
+                              _stream()))
+    return out
+
+
+def fp8_dense_mlp(weights: ExpertWeights, x, out=None):
+    """Dense FP8 SwiGLU MLP: one-expert weights (E = 1), every token routed to it with weight 1, scale 1."""
+    if weights.format != FMT_FP8 or weights.E != 1:
+        raise BsmError("dense MLP weights: FP8 with E = 1")
+    T = x.shape[0]
+    ids = torch.zeros((T, 1), dtype=torch.int32, device=x.device)
+    wts = torch.ones((T, 1), dtype=torch.float32, device=x.device)
+    return moe_expert_mlp(weights, quantize_activations(x, "fp8"), ids, wts, combine_scale=1.0, out=out)
 
 
 def moe_layer(x, w_router, weights: ExpertWeights, n_group, topk_group, topk, combine_scale=2.5):

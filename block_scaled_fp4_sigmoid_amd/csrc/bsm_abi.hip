@@ -281,6 +281,26 @@ int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w, const void* x, int64_t T,
   return hip_status(bsm::launch_moe(a, (hipStream_t)stream), "bsm_moe_expert_mlp_w4a16");
 }
 
+size_t bsm_fp8_linear_workspace_size(int64_t T, int64_t K, int64_t N) {
+  if (T < 0 || K <= 0 || N <= 0) return 0;
+  return bsm::fp8_linear_ws(T, K);
+}
+
+int bsm_fp8_linear(const uint8_t* x_codes, const float* x_scales, const uint8_t* w_codes, const float* w_scales,
+                   int64_t T, int64_t K, int64_t N, float* out, void* ws, size_t ws_bytes, bsm_stream_t stream) {
+  if (T < 0 || K <= 0 || N <= 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
+  if (K % 128 != 0 || N % 128 != 0) return fail(BSM_ERR_UNSUPPORTED, "K and N must be multiples of 128");
+  if (T > 0x3FFFFFFF || K > 0x3FFFFFFF || N > 0x3FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "shape too large");
+  if (T == 0) return ok();
+  if (!x_codes || !x_scales || !w_codes || !w_scales || !out) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(x_codes, 16) || !aligned(w_codes, 16) || !aligned(out, 16))
+    return fail(BSM_ERR_INVALID_ARG, "codes and out must be 16-byte aligned");
+  if (int r = check_ws(ws, ws_bytes, bsm::fp8_linear_ws(T, K))) return r;
+  return hip_status(bsm::launch_fp8_linear(x_codes, x_scales, w_codes, w_scales, T, K, N, out,
+                                           reinterpret_cast<uint8_t*>(ws), (hipStream_t)stream),
+                    "bsm_fp8_linear");
+}
+
 int bsm_set_stage_events(int which, void* const* events, int n) {
   if (which != 0 && which != 1) return fail(BSM_ERR_INVALID_ARG, "which must be 0 (moe) or 1 (route)");
   const int need = which == 0 ? 6 : 3;

@@ -78,6 +78,11 @@ struct MoeArgs {
 };
 hipError_t launch_moe(const MoeArgs& a, hipStream_t st);
 
+// ---- dense FP8 linear ------------------------------------------------------
+size_t fp8_linear_ws(int64_t T, int64_t K);
+hipError_t launch_fp8_linear(const uint8_t* xc, const float* xs, const uint8_t* wc, const float* wsc, int64_t T,
+                             int64_t K, int64_t N, float* out, uint8_t* ws, hipStream_t st);
+
 // ---- stage events (profiling aid) -----------------------------------------
 constexpr int kMaxStageEvents = 8;
 struct StageEvents {

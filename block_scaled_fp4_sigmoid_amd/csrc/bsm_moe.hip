@@ -25,7 +25,7 @@
 //   k_perm_masks   per 64-token chunk: LDS bit mask of the chunk's tokens for
 //                  every expert (atomicOr, order independent) and its popcount
 //   k_perm_scan    per expert: prefix counts over chunks, counts, offsets, and
-//                  two device-side tile lists: experts with <= 32 rows get
+//                  two device-side tile lists: experts with <= 64 rows get
 //                  16-row tiles (skinny kernel), larger ones 128-row tiles
 //                  (wide kernel); clears the h amax word
 //   k_perm_rows    row of every (token, slot) pair; rows of an expert are in
@@ -47,6 +47,11 @@
 #include <algorithm>
 
 #include "bsm_internal.h"
+
+// skinny kernel: 16-row weight tiles per wave (2 x 16 rows = 32 weight rows)
+#ifndef BSM_SKINNY_NT
+#define BSM_SKINNY_NT 2
+#endif
 
 namespace bsm {
 
@@ -122,7 +127,10 @@ __global__ __launch_bounds__(256) void k_perm_masks(const int32_t* __restrict__ 
   }
 }
 
-constexpr int kSkinnyMaxRows = 32;  // experts with more rows use the wide kernel
+// experts with more rows use the wide kernel; up to 4 row tiles of one expert
+// run side by side on one XCD (consecutive grid rows), so their weight
+// re-reads hit L2
+constexpr int kSkinnyMaxRows = 64;
 constexpr int kWideRows = 128;
 
 __global__ __launch_bounds__(1024) void k_perm_scan(const int* __restrict__ cnt, int64_t E, int64_t nc,
@@ -839,14 +847,100 @@ __global__ __launch_bounds__(256) void k_h_to_bf16(const float* __restrict__ h, 
   reinterpret_cast<uint2*>(o)[i] = make_uint2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
 }
 
+// Dense linear: all T rows belong to one weight matrix ("expert" 0).  At most
+// kSkinnyMaxRows rows use 16-row tiles of the register-streaming kernel, more
+// use 128-row tiles of the LDS-tiled kernel (weights read once per 128 rows).
+__global__ void k_dense_tiles(int64_t T, int4* __restrict__ tiles_s, int* __restrict__ ntiles_s,
+                              int4* __restrict__ tiles_w, int* __restrict__ ntiles_w, uint32_t* __restrict__ amax) {
+  const bool skinny = T <= kSkinnyMaxRows;
+  const int nts = skinny ? (int)((T + kRowsPerTile - 1) / kRowsPerTile) : 0;
+  const int ntw = skinny ? 0 : (int)((T + kWideRows - 1) / kWideRows);
+  for (int i = threadIdx.x; i < nts; i += blockDim.x) {
+    const int64_t r = T - (int64_t)i * kRowsPerTile;
+    tiles_s[i] = make_int4(0, i * kRowsPerTile, r < kRowsPerTile ? (int)r : kRowsPerTile, 0);
+  }
+  for (int i = threadIdx.x; i < ntw; i += blockDim.x) {
+    const int64_t r = T - (int64_t)i * kWideRows;
+    tiles_w[i] = make_int4(0, i * kWideRows, r < kWideRows ? (int)r : kWideRows, 0);
+  }
+  if (threadIdx.x == 0) {
+    *ntiles_s = nts;
+    *ntiles_w = ntw;
+    *amax = 0u;
+  }
+}
+
+struct LinLayout {
+  size_t act, tiles_s, ntiles_s, tiles_w, ntiles_w, amax, total;
+  int64_t max_s, max_w;
+};
+
+LinLayout lin_layout(int64_t T, int64_t K) {
+  LinLayout L{};
+  L.max_s = (kSkinnyMaxRows + kRowsPerTile - 1) / kRowsPerTile;
+  L.max_w = (T + kWideRows - 1) / kWideRows;
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    const size_t r = o;
+    o += align256(n);
+    return r;
+  };
+  L.act = take(2 * (size_t)T * (size_t)K);
+  L.tiles_s = take(sizeof(int4) * L.max_s);
+  L.ntiles_s = take(sizeof(int));
+  L.tiles_w = take(sizeof(int4) * (L.max_w > 0 ? L.max_w : 1));
+  L.ntiles_w = take(sizeof(int));
+  L.amax = take(sizeof(uint32_t));
+  L.total = o;
+  return L;
+}
+
 }  // namespace
+
+size_t fp8_linear_ws(int64_t T, int64_t K) { return lin_layout(T, K).total; }
+
+hipError_t launch_fp8_linear(const uint8_t* xc, const float* xs, const uint8_t* wc, const float* wsc, int64_t T,
+                             int64_t K, int64_t N, float* out, uint8_t* ws, hipStream_t st) {
+  const LinLayout L = lin_layout(T, K);
+  if (T == 0) return hipSuccess;
+  _Float16* act = reinterpret_cast<_Float16*>(ws + L.act);
+  int4* tiles_s = reinterpret_cast<int4*>(ws + L.tiles_s);
+  int* ntiles_s = reinterpret_cast<int*>(ws + L.ntiles_s);
+  int4* tiles_w = reinterpret_cast<int4*>(ws + L.tiles_w);
+  int* ntiles_w = reinterpret_cast<int*>(ws + L.ntiles_w);
+  uint32_t* amax = reinterpret_cast<uint32_t*>(ws + L.amax);
+  k_dense_tiles<<<1, 64, 0, st>>>(T, tiles_s, ntiles_s, tiles_w, ntiles_w, amax);
+  const int64_t xblk = T * K / 16;
+  k_decode_act<false><<<(unsigned)((xblk + 255) / 256), 256, 0, st>>>(xc, nullptr, xblk, act);
+#ifndef BSM_FP8_KB
+#define BSM_FP8_KB 64
+#endif
+  const dim3 gs((unsigned)(N / (64 * BSM_SKINNY_NT)), (unsigned)L.max_s);
+  const dim3 gw((unsigned)(N / 128), (unsigned)(L.max_w > 0 ? L.max_w : 1));
+  if (T <= kSkinnyMaxRows) {
+    if (K % (4 * BSM_FP8_KB) == 0)
+      k_skinny<false, false, BSM_FP8_KB, BSM_SKINNY_NT><<<gs, 256, 0, st>>>(
+          act, nullptr, 1, nullptr, xs, wc, reinterpret_cast<const uint8_t*>(wsc), nullptr, tiles_s, ntiles_s, K, N, 0,
+          out, amax);
+    else
+      k_skinny<false, false, 32, BSM_SKINNY_NT><<<gs, 256, 0, st>>>(
+          act, nullptr, 1, nullptr, xs, wc, reinterpret_cast<const uint8_t*>(wsc), nullptr, tiles_s, ntiles_s, K, N, 0,
+          out, amax);
+  } else {
+    k_gemm_wide<false, false><<<gw, 256, 0, st>>>(act, nullptr, 1, nullptr, xs, wc,
+                                                  reinterpret_cast<const uint8_t*>(wsc), nullptr, tiles_w, ntiles_w, K,
+                                                  N, 0, out, amax);
+  }
+  return hipGetLastError();
+}
 
 MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int topk) {
   MoeLayout L{};
   L.P = T * topk;
   L.n_chunks = (T + kChunk - 1) / kChunk;
-  L.max_tiles = std::min<int64_t>(2 * E, L.P / kRowsPerTile + E) + 1;       // skinny: <= 2 tiles per expert
-  L.max_tiles_w = L.P / kWideRows + L.P / (kSkinnyMaxRows + 1) + 1;         // wide: experts with > 32 rows
+  constexpr int64_t kMaxSkinnyTiles = (kSkinnyMaxRows + kRowsPerTile - 1) / kRowsPerTile;
+  L.max_tiles = std::min<int64_t>(kMaxSkinnyTiles * E, L.P / kRowsPerTile + E) + 1;  // skinny tiles
+  L.max_tiles_w = L.P / kWideRows + L.P / (kSkinnyMaxRows + 1) + 1;  // wide: experts above kSkinnyMaxRows rows
   size_t o = 0;
   auto take = [&](size_t n) {
     const size_t r = o;

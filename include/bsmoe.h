@@ -236,6 +236,24 @@ int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w /* host */, const void* x,
                              float* out, void* ws, size_t ws_bytes, bsm_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Dense FP8_DYNAMIC (W8A8) linear projection [FP8]
+ *
+ * The FP8 checkpoint also quantizes the attention query, key, value, output
+ * and gate projections and the dense MLPs ([FP8] "Quantization scheme").
+ *   x_codes uint8 [T, K] E4M3, x_scales float [T]   (bsm_fp8_quantize of x)
+ *   w_codes uint8 [N, K] E4M3, w_scales float [N]   (bsm_fp8_quantize of W)
+ *   out[t, n] = x_scales[t] * w_scales[n] * sum_k q_x[t,k] q_w[n,k]
+ *               (binary32 accumulation of exactly decoded operands), float [T, N]
+ * Requirements: K % 128 == 0, N % 128 == 0; codes and out 16-byte aligned.
+ * Workspace: bsm_fp8_linear_workspace_size(T, K, N) bytes.  A dense FP8
+ * SwiGLU MLP is bsm_moe_expert_mlp with one expert (E = 1), every token's id
+ * 0 with weight 1 (topk = 1) and combine_scale 1.
+ * ------------------------------------------------------------------------ */
+size_t bsm_fp8_linear_workspace_size(int64_t T, int64_t K, int64_t N);
+int bsm_fp8_linear(const uint8_t* x_codes, const float* x_scales, const uint8_t* w_codes, const float* w_scales,
+                   int64_t T, int64_t K, int64_t N, float* out, void* ws, size_t ws_bytes, bsm_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Profiling aid (not part of the method): stage-boundary events.
  *
  * After bsm_set_stage_events(which, events, n) with n > 0, every later call

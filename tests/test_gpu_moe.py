@@ -222,7 +222,8 @@ def test_moe_decode_full_size_sampled(gpu_lib, fmt):
 
 @pytest.mark.parametrize("fmt,T", [("nvfp4", 300), ("nvfp4", 1000), ("fp8", 300), ("fp8", 1000)])
 def test_moe_tiny_shapes_many_tokens(gpu_lib, fmt, T):
-    """Tiny layer with many tokens: experts get > 32 rows (LDS-tiled kernel) next to small ones, ragged tiles."""
+    """Tiny layer with many tokens: experts with 33-64 rows (up to four 16-row tiles, T = 300) and above 64 rows
+    (LDS-tiled kernel, T = 1000) next to small ones, ragged tiles."""
     cfg = W.TINY
     x, wr = W.activations(cfg, T=T), W.router_weights(cfg)
     masters, w13, w2 = host_masters(cfg)
@@ -236,7 +237,7 @@ def test_moe_tiny_shapes_many_tokens(gpu_lib, fmt, T):
     ref = OM.moe_layer(x, wr, experts, fmt, cfg.n_group, cfg.topk_group, cfg.topk, cfg.combine_scale)
     assert np.array_equal(np_(ids), ref["ids"])
     counts = np.bincount(ref["ids"].ravel(), minlength=cfg.E)
-    assert counts.max() > 32
+    assert counts.max() > (64 if T >= 1000 else 32)
     P = T * cfg.topk
     st = _stages(gpu_lib, fmt, cfg, T, ws, P)
     _, offsets, row_of_pair, _ = OM.permute(ref["ids"], cfg.E)
