@@ -23,6 +23,8 @@ Every function follows the method as the source pages state it:
   residual weights 1/sqrt(k) and sqrt((k-1)/k).
 * "FP8 quantization" page, "Quantization scheme": the attention projections
   and the dense MLPs are FP8_DYNAMIC too (``linear``).
+* "NVFP4 quantization" page, "Quantization method": the Local Hessian
+  block-scale search of the offline weight quantizer (``hessian``).
 
 Where the pages leave a step open the reading taken is stated in the function
 that implements it.  Floating point is evaluated in float64 (exact where the
@@ -31,4 +33,4 @@ docstrings say so) and rounded to float32 where the method fixes FP32.
 Parity status of each function (what pins it) is listed in each module header.
 """
 
-from . import formats, quant, route, moe, linear  # noqa: F401
+from . import formats, quant, route, moe, linear, hessian  # noqa: F401
