@@ -66,6 +66,8 @@ def load():
         "bsm_nvfp4_quantize_workspace_size": (sz, [i64, i64, i64]),
         "bsm_nvfp4_quantize": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32, vp, sz, vp]),
         "bsm_nvfp4_dequantize": (i32, [vp, vp, vp, i64, i64, i64, vp, vp]),
+        "bsm_local_hessian_blocks": (i32, [vp, i32, i64, i64, vp, vp]),
+        "bsm_nvfp4_quantize_local_hessian": (i32, [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp, sz, vp]),
         "bsm_fp8_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "bsm_route_workspace_size": (sz, [i64, i64, i64]),
         "bsm_route": (i32, [vp, i32, i64, i64, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
@@ -167,6 +169,34 @@ def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, global_scale: to
     _check(lib.bsm_nvfp4_dequantize(_ptr(c3), _ptr(_dev(scales, "scales")), _ptr(_dev(global_scale, "gs")), B, R,
                                     C2 * 2, _ptr(out), _stream()))
     return out[0] if squeeze else out
+
+
+def local_hessian_blocks(x: torch.Tensor):
+    """x [N, C] -> [C/16, 16, 16] float64 diagonal blocks of x^T x (the local Hessians of a weight's blocks)."""
+    lib = load()
+    _dev(x, "x")
+    N, C = x.shape
+    out = torch.empty((C // 16, 16, 16), dtype=torch.float64, device=x.device)
+    _check(lib.bsm_local_hessian_blocks(_ptr(x), _dtype_code(x), N, C, _ptr(out), _stream()))
+    return out
+
+
+def nvfp4_quantize_local_hessian(w: torch.Tensor, hess_blocks: torch.Tensor, radius: int = 8):
+    """Offline NVFP4 quantization of w [R, C] with the Local-Hessian block-scale search -> (codes, scales, gs[1])."""
+    lib = load()
+    _dev(w, "w")
+    _dev(hess_blocks, "hess_blocks")
+    R, C = w.shape
+    if hess_blocks.dtype != torch.float64 or tuple(hess_blocks.shape) != (C // 16, 16, 16):
+        raise BsmError("hess_blocks must be float64 [C/16, 16, 16]")
+    codes = torch.empty((R, C // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((R, C // 16), dtype=torch.uint8, device=w.device)
+    gs = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws = _ws(lib.bsm_nvfp4_quantize_workspace_size(1, R, C), w.device)
+    _check(lib.bsm_nvfp4_quantize_local_hessian(_ptr(w), _dtype_code(w), R, C, _ptr(hess_blocks), int(radius),
+                                                _ptr(codes), _ptr(scales), _ptr(gs), _ptr(ws), ws.numel(),
+                                                _stream()))
+    return codes, scales, gs
 
 
 def fp8_quantize(x: torch.Tensor):

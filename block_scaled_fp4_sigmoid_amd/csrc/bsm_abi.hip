@@ -89,6 +89,35 @@ int bsm_nvfp4_quantize(const void* x, int x_dtype, int64_t B, int64_t R, int64_t
                     "bsm_nvfp4_quantize");
 }
 
+int bsm_local_hessian_blocks(const void* x, int x_dtype, int64_t N, int64_t C, double* hess_blocks,
+                             bsm_stream_t stream) {
+  if (!dtype_ok(x_dtype)) return fail(BSM_ERR_INVALID_ARG, "x_dtype must be BSM_BF16 or BSM_F32");
+  if (N < 0 || C < 0) return fail(BSM_ERR_INVALID_ARG, "negative shape");
+  if (C % 16 != 0) return fail(BSM_ERR_INVALID_ARG, "C (%lld) must be a multiple of 16", (long long)C);
+  if (C == 0) return ok();
+  if (!hess_blocks || (N > 0 && !x)) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(hess_blocks, 8)) return fail(BSM_ERR_INVALID_ARG, "hess_blocks must be 8-byte aligned");
+  return hip_status(bsm::launch_local_hessian(x, x_dtype == BSM_BF16, N, C, hess_blocks, (hipStream_t)stream),
+                    "bsm_local_hessian_blocks");
+}
+
+int bsm_nvfp4_quantize_local_hessian(const void* w, int w_dtype, int64_t R, int64_t C, const double* hess_blocks,
+                                     int radius, uint8_t* codes, uint8_t* scales, float* global_scale, void* ws,
+                                     size_t ws_bytes, bsm_stream_t stream) {
+  if (!dtype_ok(w_dtype)) return fail(BSM_ERR_INVALID_ARG, "w_dtype must be BSM_BF16 or BSM_F32");
+  if (R < 0 || C < 0) return fail(BSM_ERR_INVALID_ARG, "negative shape");
+  if (C % 16 != 0) return fail(BSM_ERR_INVALID_ARG, "C (%lld) must be a multiple of 16", (long long)C);
+  if (radius < 0 || radius > 125) return fail(BSM_ERR_INVALID_ARG, "radius must be in [0, 125]");
+  if (R * C == 0) return ok();
+  if (!w || !hess_blocks || !codes || !scales || !global_scale) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(w, 32) || !aligned(codes, 8) || !aligned(hess_blocks, 8))
+    return fail(BSM_ERR_INVALID_ARG, "w 32-byte, codes and hess_blocks 8-byte alignment");
+  if (int r = check_ws(ws, ws_bytes, bsm::nvfp4_quant_ws(1, R, C))) return r;
+  return hip_status(bsm::launch_nvfp4_quantize_lh(w, w_dtype == BSM_BF16, R, C, hess_blocks, radius, codes, scales,
+                                                  global_scale, (float*)ws, (hipStream_t)stream),
+                    "bsm_nvfp4_quantize_local_hessian");
+}
+
 int bsm_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale, int64_t B, int64_t R,
                          int64_t C, float* out, bsm_stream_t stream) {
   if (B < 0 || R < 0 || C < 0) return fail(BSM_ERR_INVALID_ARG, "negative shape");

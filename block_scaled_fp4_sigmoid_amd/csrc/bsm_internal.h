@@ -21,6 +21,9 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 constexpr int kAmaxMaxParts = 1024;
 int nvfp4_amax_parts(int64_t R, int64_t C);
 size_t nvfp4_quant_ws(int64_t B, int64_t R, int64_t C);
+hipError_t launch_local_hessian(const void* x, bool x_bf16, int64_t N, int64_t C, double* out, hipStream_t st);
+hipError_t launch_nvfp4_quantize_lh(const void* w, bool w_bf16, int64_t R, int64_t C, const double* hb, int radius,
+                                    uint8_t* codes, uint8_t* scales, float* gs, float* parts, hipStream_t st);
 hipError_t launch_nvfp4_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C, uint8_t* codes,
                                  uint8_t* scales, float* gs, bool dynamic, float* ws_partials,
                                  hipStream_t st);

@@ -241,6 +241,112 @@ __global__ __launch_bounds__(kThreads) void k_fp8_rows(const void* __restrict__ 
   }
 }
 
+// Local Hessian blocks of the inputs x [N, C]: out[b][i][j] = sum_t x[t, 16b+i] x[t, 16b+j]
+// (binary64, t ascending).  One thread per (b, i, j).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_local_hessian(const void* __restrict__ x, int64_t N, int64_t C,
+                                                             double* __restrict__ out) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= (C / 16) * 256) return;
+  const int64_t b = gid >> 8;
+  const int i = (int)((gid >> 4) & 15), j = (int)(gid & 15);
+  const int64_t ci = 16 * b + i, cj = 16 * b + j;
+  double acc = 0.0;
+  for (int64_t t = 0; t < N; ++t) {
+    float a, c;
+    if (BF16) {
+      a = u2f((uint32_t)reinterpret_cast<const uint16_t*>(x)[t * C + ci] << 16);
+      c = u2f((uint32_t)reinterpret_cast<const uint16_t*>(x)[t * C + cj] << 16);
+    } else {
+      a = reinterpret_cast<const float*>(x)[t * C + ci];
+      c = reinterpret_cast<const float*>(x)[t * C + cj];
+    }
+    const double p = (double)a * (double)c;
+    acc = acc + p;
+  }
+  out[gid] = acc;
+}
+
+// Local-Hessian block-scale search ("NVFP4 quantization" page, "Quantization
+// method"): per 16-value block, among the E4M3 scale codes c0 - radius ..
+// c0 + radius (c0 = round-to-nearest code, admissible codes 1..126) keep the
+// one minimizing dw^T H_b dw, dw = w - q * s * S_g, evaluated in binary64 in a
+// fixed order (t_i = sum_j H_ij dw_j, j ascending; e = sum_i dw_i t_i); ties go
+// to the lower code.  The elements of a block quantize exactly as in the RTN
+// encoder.  One thread per (block column b, row r); a wave shares b, so the
+// 16 x 16 block of H is read once per wave.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_nvfp4_lh_encode(const void* __restrict__ w, int64_t R, int64_t C,
+                                                               const double* __restrict__ hb,
+                                                               const float* __restrict__ gs, int radius,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales) {
+  const int64_t nb = C / 16;
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= R * nb) return;
+  const int64_t b = gid / R, r = gid % R;
+  const int64_t f = r * nb + b;  // block index in the row-major block sequence
+  float v[16];
+  load16<BF16>(w, f, v);
+  const float S = gs[0];
+  const float d1 = 6.0f * S;
+  float ab = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) ab = fmaxf(ab, fabsf(v[k]));
+  const int c0 = (S != 0.0f) ? (int)e4m3_code_mag(ab / d1) : 0;
+  int best = c0;
+  if (c0 > 0) {
+    const double* H = hb + b * 256;
+    double best_e = __builtin_inf();
+    for (int c = c0 - radius; c <= c0 + radius; ++c) {
+      if (c < 1 || c > 126) continue;
+      const float sv = e4m3_value_mag((uint32_t)c);
+      const float d2 = sv * S;
+      double dw[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t mag = e2m1_code_mag(fabsf(v[k]) / d2);
+        const double qm = (f2u(v[k]) >> 31) ? -(double)e2m1_value_mag(mag) : (double)e2m1_value_mag(mag);
+        const double val = (qm * (double)sv) * (double)S;
+        dw[k] = (double)v[k] - val;
+      }
+      double e = 0.0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        double t = 0.0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const double p = H[i * 16 + j] * dw[j];
+          t = t + p;
+        }
+        const double p = dw[i] * t;
+        e = e + p;
+      }
+      if (e < best_e) {
+        best_e = e;
+        best = c;
+      }
+    }
+  }
+  // encode with the chosen scale exactly as the RTN encoder does
+  const float sv = e4m3_value_mag((uint32_t)best);
+  const float d2 = sv * S;
+  uint32_t q[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t sgn = (f2u(v[k]) >> 31) << 3;
+    const uint32_t mag = (sv == 0.0f) ? 0u : e2m1_code_mag(fabsf(v[k]) / d2);
+    q[k] = sgn | mag;
+  }
+  uint2 packed;
+  packed.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) | (q[6] << 24) |
+             (q[7] << 28);
+  packed.y = q[8] | (q[9] << 4) | (q[10] << 8) | (q[11] << 12) | (q[12] << 16) | (q[13] << 20) |
+             (q[14] << 24) | (q[15] << 28);
+  *reinterpret_cast<uint2*>(codes + f * 8) = packed;
+  scales[f] = (uint8_t)best;
+}
+
 }  // namespace
 
 int nvfp4_amax_parts(int64_t R, int64_t C) {
@@ -298,6 +404,32 @@ hipError_t launch_nvfp4_quantize_from_amax(const void* x, bool x_bf16, int64_t B
   else
     k_nvfp4_encode<false><<<g2, kThreads, 0, st>>>(x, n_blk, codes, scales, gs, nullptr, 0, amax_bits, static_gs, 2,
                                                     np2, dec16);
+  return hipGetLastError();
+}
+
+hipError_t launch_local_hessian(const void* x, bool x_bf16, int64_t N, int64_t C, double* out, hipStream_t st) {
+  const int64_t n = (C / 16) * 256;
+  if (n == 0) return hipSuccess;
+  const unsigned g = (unsigned)((n + kThreads - 1) / kThreads);
+  if (x_bf16)
+    k_local_hessian<true><<<g, kThreads, 0, st>>>(x, N, C, out);
+  else
+    k_local_hessian<false><<<g, kThreads, 0, st>>>(x, N, C, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quantize_lh(const void* w, bool w_bf16, int64_t R, int64_t C, const double* hb, int radius,
+                                    uint8_t* codes, uint8_t* scales, float* gs, float* parts, hipStream_t st) {
+  const int64_t nblk = R * (C / 16);
+  if (nblk == 0) return hipSuccess;
+  // round-to-nearest pass: the dynamic global scale (and a complete encoding the search then overwrites)
+  hipError_t err = launch_nvfp4_quantize(w, w_bf16, 1, R, C, codes, scales, gs, true, parts, st);
+  if (err != hipSuccess) return err;
+  const unsigned g = (unsigned)((nblk + kThreads - 1) / kThreads);
+  if (w_bf16)
+    k_nvfp4_lh_encode<true><<<g, kThreads, 0, st>>>(w, R, C, hb, gs, radius, codes, scales);
+  else
+    k_nvfp4_lh_encode<false><<<g, kThreads, 0, st>>>(w, R, C, hb, gs, radius, codes, scales);
   return hipGetLastError();
 }
 

@@ -107,6 +107,32 @@ int bsm_nvfp4_quantize(const void* x, int x_dtype, int64_t B, int64_t R, int64_t
                        uint8_t* codes, uint8_t* scales, float* global_scale, int gs_mode,
                        void* ws, size_t ws_bytes, bsm_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Local-Hessian block-scale search (offline weight quantizer) [NVFP4]
+ * ("NVFP4 quantization" page, "Quantization method": per block, candidate
+ * scales are searched and the one minimizing the Hessian-weighted error
+ * dW^T H dW kept, H computed from the tokens routed to the expert).
+ *
+ * bsm_local_hessian_blocks: x [N, C] (the inputs the weight multiplies, bf16
+ *   or f32) -> hess_blocks double [C/16][16][16], block b = the 16 x 16
+ *   diagonal block of x^T x over input features 16b..16b+15 (binary64, tokens
+ *   summed in order).
+ * bsm_nvfp4_quantize_local_hessian: one tensor w [R, C] -> codes [R, C/2],
+ *   scales [R, C/16], global_scale [1] like bsm_nvfp4_quantize (DYNAMIC global
+ *   scale), except that each block's E4M3 scale is the code among
+ *   c0 - radius .. c0 + radius (c0 = the round-to-nearest code, admissible
+ *   codes 1..126; a zero block keeps 0) minimizing dw^T H_b dw with
+ *   dw = w - q * s * S_g, evaluated in binary64 as t_i = sum_j H_ij dw_j
+ *   (j ascending), e = sum_i dw_i t_i (i ascending); ties go to the lower
+ *   code.  radius 0 is round-to-nearest.  w 32-byte, codes and hess_blocks
+ *   8-byte aligned.  Workspace: bsm_nvfp4_quantize_workspace_size(1, R, C).
+ * ------------------------------------------------------------------------ */
+int bsm_local_hessian_blocks(const void* x, int x_dtype, int64_t N, int64_t C, double* hess_blocks,
+                             bsm_stream_t stream);
+int bsm_nvfp4_quantize_local_hessian(const void* w, int w_dtype, int64_t R, int64_t C, const double* hess_blocks,
+                                     int radius, uint8_t* codes, uint8_t* scales, float* global_scale, void* ws,
+                                     size_t ws_bytes, bsm_stream_t stream);
+
 /* Dequantize: out[b,r,c] = fl32(fl32(q*s_b) * S_g[b]) (q*s_b is exact), float32 output. */
 int bsm_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                          int64_t B, int64_t R, int64_t C, float* out, bsm_stream_t stream);

@@ -71,14 +71,17 @@ def _quantize_block(blk, sb, S_g):
     return q, val
 
 
-def nvfp4_quantize_local_hessian(w, hblocks, radius=8):
-    """w [R, C], hblocks [C/16, 16, 16] -> (codes [R, C/2], scales [R, C/16], S_g, objective of the pick)."""
+def nvfp4_quantize_local_hessian(w, hblocks, radius=8, global_scale=None):
+    """w [R, C], hblocks [C/16, 16, 16] -> (codes [R, C/2], scales [R, C/16], S_g, objective of the pick).
+
+    ``global_scale``: the tensor's S_g when w holds only some of its rows (rows quantize independently).
+    """
     w32 = _as_f32_exact(w)
     R, C = w32.shape
     nb = C // NVFP4_BLOCK
     hb = np.asarray(hblocks, np.float64)
     assert hb.shape == (nb, NVFP4_BLOCK, NVFP4_BLOCK)
-    S_g = nvfp4_global_scale(w32)
+    S_g = nvfp4_global_scale(w32) if global_scale is None else F32(global_scale)
     blk = w32.reshape(R, nb, NVFP4_BLOCK)
     a_b = np.max(np.abs(blk), axis=-1)
     d1 = F32(F32(6.0) * S_g)

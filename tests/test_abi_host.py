@@ -122,3 +122,18 @@ def test_weight_only_moe_validation(lib):
     assert lib.bsm_moe_workspace_size(3, 256, 5120, 2560, 64, 8) == lib.bsm_moe_workspace_size(1, 256, 5120, 2560,
                                                                                              64, 8)
     assert lib.bsm_moe_workspace_size(4, 256, 5120, 2560, 64, 8) == 0
+
+
+def test_local_hessian_validation(lib):
+    f = lib.bsm_nvfp4_quantize_local_hessian
+    assert f(FAKE, 1, 64, 250, FAKE, 8, FAKE, FAKE, FAKE, None, 0, None) == 1     # C % 16
+    assert f(FAKE, 1, 64, 256, FAKE, -1, FAKE, FAKE, FAKE, None, 0, None) == 1    # radius < 0
+    assert f(FAKE, 1, 64, 256, FAKE, 126, FAKE, FAKE, FAKE, None, 0, None) == 1   # radius > 125
+    assert f(FAKE, 3, 64, 256, FAKE, 8, FAKE, FAKE, FAKE, None, 0, None) == 1     # dtype
+    assert f(FAKE, 1, 64, 256, None, 8, FAKE, FAKE, FAKE, None, 0, None) == 1     # NULL H
+    assert f(FAKE, 1, 64, 256, FAKE, 8, FAKE, FAKE, FAKE, None, 0, None) == 3     # no workspace
+    assert f(None, 1, 0, 256, None, 8, None, None, None, None, 0, None) == 0      # empty
+    h = lib.bsm_local_hessian_blocks
+    assert h(FAKE, 1, 100, 250, FAKE, None) == 1
+    assert h(FAKE, 1, 100, 256, None, None) == 1
+    assert h(FAKE, 1, 100, 256, ctypes.c_void_p(0x100004), None) == 1            # misaligned output
