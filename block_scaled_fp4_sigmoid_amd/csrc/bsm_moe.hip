@@ -427,18 +427,19 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
   SRegs<KB> sc[NT];  // NVFP4 scale span of super-step 4q + g (this lane's share of the current group)
   uint32_t sdw[NT][kSV];
   uint4 ra0, ra1, ra2, ra3;
-  // prologue: super-step 0 codes and activations, scale groups 0 and 1
-  ra0 = reinterpret_cast<const uint4*>(asrc)[0];
-  if constexpr (kAv >= 2) ra1 = reinterpret_cast<const uint4*>(asrc)[1];
-  if constexpr (kAv >= 4) {
-    ra2 = reinterpret_cast<const uint4*>(asrc)[2];
-    ra3 = reinterpret_cast<const uint4*>(asrc)[3];
-  }
+  // prologue: super-step 0 weights and scale group 0 first (their addresses depend only on the
+  // tile descriptor), then the activations (GEMM1 gathers them through row_pair)
 #pragma unroll
   for (int j = 0; j < NT; ++j) b_load<NV, KB>(crow[j], b0[j]);
   if constexpr (NV) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) s_load<KB>(srow[j], g < nsteps, sc[j]);
+  }
+  ra0 = reinterpret_cast<const uint4*>(asrc)[0];
+  if constexpr (kAv >= 2) ra1 = reinterpret_cast<const uint4*>(asrc)[1];
+  if constexpr (kAv >= 4) {
+    ra2 = reinterpret_cast<const uint4*>(asrc)[2];
+    ra3 = reinterpret_cast<const uint4*>(asrc)[3];
   }
   reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[0] = ra0;
   if constexpr (kAv >= 2) reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[1] = ra1;
@@ -711,6 +712,202 @@ __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict
           const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * H + c0 + wn * 64 + m;
 #pragma unroll
           for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][r] * sa * ws[16 * j];
+        }
+      }
+    }
+  }
+  if (G1 && NV) {
+    hmax = wave_max_f(hmax);
+    if (lane == 0) atomicMax(h_amax, f2u(hmax));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM for many rows per expert on the 32x32x16 matrix cores ("big"):
+// 128 rows x 256 weight rows per workgroup, 4 waves of 64 rows x 128 weight
+// rows (2 x 4 MFMA tiles of 32 x 32, 128 accumulators per lane), K in steps
+// of 64 staged through LDS (double buffered; the next step's global loads go
+// to registers during the current step).  The activation tile is staged as
+// FP16 (W4A16: BF16); the weight tile as raw codes and scale bytes, decoded
+// by the wave that uses each fragment.  GEMM1 workgroup: weight rows = 128
+// gate rows c0.. and the 128 matching up rows; each wave holds g and u of the
+// same 64 h columns, so SwiGLU fuses into the epilogue.
+// MFMA 32x32x16 operands: lane l carries row / column l % 32 and k values
+// 8 (l / 32) .. +7 of the 16; result register 4q + j of lane l is row
+// 8q + 4 (l / 32) + j, column l % 32.
+// ---------------------------------------------------------------------------
+constexpr int kGBM = 128, kGBN = 256, kGBK = 64;
+template <bool NV>
+struct BigB {
+  static constexpr int kRow = NV ? 36 : 72;  // LDS bytes per weight row and K step (+4 / +8 pad)
+};
+typedef float f16v __attribute__((ext_vector_type(16)));
+template <bool A16>
+__device__ inline f16v mfma32(h8v a, h8v b, f16v c) {
+  if constexpr (A16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+template <bool NV, bool G1, bool A16 = false>
+__global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
+                                                     int topk, const float* __restrict__ a_gs,
+                                                     const float* __restrict__ a_rs, const uint8_t* __restrict__ wc,
+                                                     const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
+                                                     const int4* __restrict__ tiles, const int* __restrict__ ntiles,
+                                                     int64_t K, int64_t H, int64_t I, float* __restrict__ out,
+                                                     uint32_t* __restrict__ h_amax) {
+  constexpr int kBRow = BigB<NV>::kRow;
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][kGBM][kGBK + 8];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGBN][kBRow];
+  __shared__ uint32_t Bsc[2][kGBN];
+  if ((int)blockIdx.y >= *ntiles) return;
+  const int4 ti = tiles[blockIdx.y];
+  const int e = ti.x, row0 = ti.y, nrows = ti.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t c0 = (int64_t)blockIdx.x * (G1 ? kGBN / 2 : kGBN);
+  // staging: A row sr, half kh (32 values); B row br (the whole K step)
+  const int sr = tid >> 1, kh = tid & 1, br = tid;
+  const int ar = sr < nrows ? sr : nrows - 1;
+  const _Float16* asrc = G1 ? act + (int64_t)(row_pair[row0 + ar] / topk) * K + 32 * kh
+                            : act + (int64_t)(row0 + ar) * K + 32 * kh;
+  int64_t wrow;
+  if (G1) wrow = (int64_t)e * 2 * I + (br < kGBN / 2 ? c0 + br : I + c0 + (br - kGBN / 2));
+  else wrow = (int64_t)e * H + c0 + br;
+  const int64_t cbytes = NV ? K / 2 : K;
+  const uint8_t* bsrc = wc + wrow * cbytes;
+  const uint8_t* ssrc = NV ? wsc + wrow * (K / 16) : nullptr;
+
+  // one register set holds the global loads of the next K step
+  uint4 raX0, raX1, raX2, raX3, rbX0, rbX1, rbX2, rbX3;
+  uint32_t rsX = 0;
+#define BSM_BIG_GLOAD(k0, S)                                                        \
+  {                                                                                 \
+    const uint4* pa = reinterpret_cast<const uint4*>(asrc + (k0));                  \
+    ra##S##0 = pa[0];                                                               \
+    ra##S##1 = pa[1];                                                               \
+    ra##S##2 = pa[2];                                                               \
+    ra##S##3 = pa[3];                                                               \
+    const uint4* pb = reinterpret_cast<const uint4*>(bsrc + (NV ? (k0) / 2 : (k0))); \
+    rb##S##0 = pb[0];                                                               \
+    rb##S##1 = pb[1];                                                               \
+    if (!NV) {                                                                      \
+      rb##S##2 = pb[2];                                                             \
+      rb##S##3 = pb[3];                                                             \
+    }                                                                               \
+    if (NV) rs##S = *reinterpret_cast<const uint32_t*>(ssrc + (k0) / 16);           \
+  }
+#define BSM_BIG_LSTORE(buf, S)                                                      \
+  {                                                                                 \
+    uint4* da = reinterpret_cast<uint4*>(&As[buf][sr][32 * kh]);                    \
+    da[0] = ra##S##0;                                                               \
+    da[1] = ra##S##1;                                                               \
+    da[2] = ra##S##2;                                                               \
+    da[3] = ra##S##3;                                                               \
+    uint32_t* db = reinterpret_cast<uint32_t*>(&Bs[buf][br][0]);                    \
+    db[0] = (rb##S##0).x; db[1] = (rb##S##0).y; db[2] = (rb##S##0).z; db[3] = (rb##S##0).w; \
+    db[4] = (rb##S##1).x; db[5] = (rb##S##1).y; db[6] = (rb##S##1).z; db[7] = (rb##S##1).w; \
+    if (!NV) {                                                                      \
+      db[8] = (rb##S##2).x; db[9] = (rb##S##2).y; db[10] = (rb##S##2).z; db[11] = (rb##S##2).w; \
+      db[12] = (rb##S##3).x; db[13] = (rb##S##3).y; db[14] = (rb##S##3).z; db[15] = (rb##S##3).w; \
+    }                                                                               \
+    if (NV) Bsc[buf][br] = rs##S;                                                   \
+  }
+  // LDS weight row of this wave's N tile t: GEMM1 gate tiles 0,1 / up tiles 2,3; GEMM2 4 consecutive
+#define BSM_BIG_BROW(t) (G1 ? (((t) < 2) ? wn * 64 + 32 * (t) : kGBN / 2 + wn * 64 + 32 * ((t) - 2)) : wn * 128 + 32 * (t))
+
+  f16v acc[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mt][t][q] = 0.0f;
+
+  const int nk = (int)(K / kGBK);
+  BSM_BIG_GLOAD(0, X)
+  BSM_BIG_LSTORE(0, X)
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) BSM_BIG_GLOAD((int64_t)(ks + 1) * kGBK, X)
+#pragma unroll
+    for (int k16 = 0; k16 < kGBK / 16; ++k16) {
+      h8v a[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        a[mt] = *reinterpret_cast<const h8v*>(&As[buf][wm * 64 + mt * 32 + l32][k16 * 16 + lh * 8]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int brow = BSM_BIG_BROW(t) + l32;
+        h8v b;
+        if constexpr (NV) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(&Bs[buf][brow][k16 * 8 + lh * 4]);
+          const h2v s2 = scale_pair_sel(Bsc[buf][brow], (uint32_t)k16 * 0x0101u);
+          if constexpr (A16)
+            b = dec_fp4x8_bf16(w, (float)s2[0]);
+          else
+            b = dec_fp4x8(w, s2);
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2*>(&Bs[buf][brow][k16 * 16 + lh * 8]);
+          b = dec_fp8x8(w.x, w.y);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[mt][t] = mfma32<A16>(a[mt], b, acc[mt][t]);
+      }
+    }
+    if (ks + 1 < nk) BSM_BIG_LSTORE(buf ^ 1, X)
+    __syncthreads();
+  }
+#undef BSM_BIG_GLOAD
+#undef BSM_BIG_LSTORE
+#undef BSM_BIG_BROW
+
+  float hmax = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ro = wm * 64 + mt * 32 + 8 * q + 4 * lh + j;
+        if (ro >= nrows) continue;
+        const int r = 4 * q + j;
+        if (G1) {
+          float* hr = out + (int64_t)(row0 + ro) * I;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int64_t col = c0 + wn * 64 + 32 * t + l32;
+            float sg, su;
+            if (NV) {
+              const float ag = A16 ? 1.0f : a_gs[0];
+              sg = ag * wgs[2 * e];
+              su = ag * wgs[2 * e + 1];
+            } else {
+              const float sx = a_rs[row_pair[row0 + ro] / topk];
+              const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
+              sg = sx * ws[col];
+              su = sx * ws[I + col];
+            }
+            const float h = silu_mul(acc[mt][t][r] * sg, acc[mt][t + 2][r] * su);
+            hr[col] = h;
+            hmax = fmaxf(hmax, fabsf(h));
+          }
+        } else {
+          float* yr = out + (int64_t)(row0 + ro) * H;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int64_t col = c0 + wn * 128 + 32 * t + l32;
+            if (NV) {
+              yr[col] = acc[mt][t][r] * ((A16 ? 1.0f : a_gs[0]) * wgs[e]);
+            } else {
+              const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * H;
+              yr[col] = acc[mt][t][r] * a_rs[row0 + ro] * ws[col];
+            }
+          }
         }
       }
     }
@@ -1009,8 +1206,11 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #endif
   const dim3 g1((unsigned)(a.I / (32 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 8*NT h columns
   const dim3 g2((unsigned)(a.H / (64 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 16*NT y columns
-  const dim3 w1((unsigned)(a.I / 64), (unsigned)L.max_tiles_w);
-  const dim3 w2((unsigned)(a.H / 128), (unsigned)L.max_tiles_w);
+#ifndef BSM_PREFILL_BIG
+#define BSM_PREFILL_BIG 1  // many-row experts on the 32x32x16 kernel (0: the 16x16x32 one)
+#endif
+  const dim3 w1((unsigned)(a.I / (BSM_PREFILL_BIG ? kGBN / 2 : 64)), (unsigned)L.max_tiles_w);
+  const dim3 w2((unsigned)(a.H / (BSM_PREFILL_BIG ? kGBN : 128)), (unsigned)L.max_tiles_w);
   _Float16* act = reinterpret_cast<_Float16*>(ws + L.act_f16);
   _Float16* hdec = reinterpret_cast<_Float16*>(ws + L.h_f16);
   const int64_t xblk = a.T * a.H / 16;
@@ -1029,12 +1229,14 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   k_skinny<NV, true, KB, BSM_SKINNY_NT><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes,  \
                                                             w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I,     \
                                                             h_f32, h_amax);                                   \
-  k_gemm_wide<NV, true><<<w1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,  \
+  (BSM_PREFILL_BIG ? k_gemm_big<NV, true> : k_gemm_wide<NV, true>)<<<w1, 256, 0, st>>>(                      \
+      act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,                                        \
                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
 #define BSM_G2(NV, KB)                                                                                         \
   k_skinny<NV, false, KB, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
                                               a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
-  k_gemm_wide<NV, false><<<w2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
+  (BSM_PREFILL_BIG ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                    \
+      hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales),                                \
                                              a.w2_codes, w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
 #ifndef BSM_NV_KB
 #define BSM_NV_KB 128
@@ -1045,7 +1247,8 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K, KB)                                               \
   k_skinny<true, G, KB, BSM_SKINNY_NT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, \
                                                                    tiles, ntiles, K, a.H, a.I, OUT, h_amax);   \
-  k_gemm_wide<true, G, true><<<WGRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,     \
+  (BSM_PREFILL_BIG ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(        \
+      A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,                                                  \
                                                     ntiles_w, K, a.H, a.I, OUT, h_amax)
     if (a.H % (4 * BSM_NV_KB) == 0) {
       BSM_A16_G(true, act, xrs, a.w13_codes, w13s, a.w13_gs, h_f32, g1, w1, a.H, BSM_NV_KB);
