@@ -724,14 +724,15 @@ __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict
 
 // ---------------------------------------------------------------------------
 // Grouped GEMM for many rows per expert on the 32x32x16 matrix cores ("big"):
-// 128 rows x 256 weight rows per workgroup, 4 waves of 64 rows x 128 weight
-// rows (2 x 4 MFMA tiles of 32 x 32, 128 accumulators per lane), K in steps
+// 128 rows x 256 weight rows per workgroup, 4 waves of 128 rows x 64 weight
+// rows (4 x 2 MFMA tiles of 32 x 32, 128 accumulators per lane), K in steps
 // of 64 staged through LDS (double buffered; the next step's global loads go
 // to registers during the current step).  The activation tile is staged as
-// FP16 (W4A16: BF16); the weight tile as raw codes and scale bytes, decoded
-// by the wave that uses each fragment.  GEMM1 workgroup: weight rows = 128
-// gate rows c0.. and the 128 matching up rows; each wave holds g and u of the
-// same 64 h columns, so SwiGLU fuses into the epilogue.
+// FP16 (W4A16: BF16); the weight tile as raw codes and scale bytes.  Each
+// weight fragment is used by exactly one wave, which decodes it once for all
+// 128 rows.  GEMM1 workgroup: weight rows = 128 gate rows c0.. and the 128
+// matching up rows; each wave holds g and u of the same 32 h columns, so
+// SwiGLU fuses into the epilogue.
 // MFMA 32x32x16 operands: lane l carries row / column l % 32 and k values
 // 8 (l / 32) .. +7 of the 16; result register 4q + j of lane l is row
 // 8q + 4 (l / 32) + j, column l % 32.
@@ -767,81 +768,107 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   const int e = ti.x, row0 = ti.y, nrows = ti.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, lh = lane >> 5;
-  const int wm = wave & 1, wn = wave >> 1;
   const int64_t c0 = (int64_t)blockIdx.x * (G1 ? kGBN / 2 : kGBN);
-  // staging: A row sr, half kh (32 values); B row br (the whole K step)
-  const int sr = tid >> 1, kh = tid & 1, br = tid;
-  const int ar = sr < nrows ? sr : nrows - 1;
-  const _Float16* asrc = G1 ? act + (int64_t)(row_pair[row0 + ar] / topk) * K + 32 * kh
-                            : act + (int64_t)(row0 + ar) * K + 32 * kh;
-  int64_t wrow;
-  if (G1) wrow = (int64_t)e * 2 * I + (br < kGBN / 2 ? c0 + br : I + c0 + (br - kGBN / 2));
-  else wrow = (int64_t)e * H + c0 + br;
+  // Staging: each load instruction covers whole row segments with consecutive
+  // lanes (8 lanes per 128-byte activation row segment, 2 (FP8: 4) lanes per
+  // weight row segment), so one instruction touches few cache lines.
+  // Activation rows ar(i) = 32 i + tid / 8, 16-byte part tid % 8.
+  constexpr int kBI = NV ? 2 : 4;  // weight rows per thread: kGBN / (256 / (16-byte parts per row))
+  constexpr int kBP = NV ? 2 : 4;  // 16-byte parts per weight row and K step
+  const int apart = tid & 7, bpart = tid & (kBP - 1);
+  auto arow = [&](int i) -> const _Float16* {
+    const int r = 32 * i + (tid >> 3);
+    const int ar = r < nrows ? r : nrows - 1;
+    return (G1 ? act + (int64_t)(row_pair[row0 + ar] / topk) * K : act + (int64_t)(row0 + ar) * K) + 8 * apart;
+  };
+  const _Float16 *as0 = arow(0), *as1 = arow(1), *as2 = arow(2), *as3 = arow(3);
+  // weight row r of the tile: GEMM1 gate rows c0.. then the matching up rows
+  auto wrow_of = [&](int r) -> int64_t {
+    if (G1) return (int64_t)e * 2 * I + (r < kGBN / 2 ? c0 + r : I + c0 + (r - kGBN / 2));
+    return (int64_t)e * H + c0 + r;
+  };
   const int64_t cbytes = NV ? K / 2 : K;
-  const uint8_t* bsrc = wc + wrow * cbytes;
-  const uint8_t* ssrc = NV ? wsc + wrow * (K / 16) : nullptr;
+  // weight rows as 32-bit byte offsets from the tile's first row (within one expert)
+  const uint8_t* bbase = wc + wrow_of(0) * cbytes + 16 * bpart;
+  auto boff_of = [&](int i) -> uint32_t {
+    return (uint32_t)((wrow_of((256 / kBP) * i + tid / kBP) - wrow_of(0)) * cbytes);
+  };
+  const uint32_t bo0 = boff_of(0), bo1 = boff_of(1), bo2 = kBI > 2 ? boff_of(2) : 0u, bo3 = kBI > 2 ? boff_of(3) : 0u;
+  // scale bytes: thread tid holds weight row tid; 16 bytes (4 K steps) per load when rows are 16-byte aligned
+  const uint8_t* ssrc = NV ? wsc + wrow_of(tid) * (K / 16) : nullptr;
+  const bool s4 = (K % 256) == 0;
 
-  // one register set holds the global loads of the next K step
-  uint4 raX0, raX1, raX2, raX3, rbX0, rbX1, rbX2, rbX3;
-  uint32_t rsX = 0;
-#define BSM_BIG_GLOAD(k0, S)                                                        \
-  {                                                                                 \
-    const uint4* pa = reinterpret_cast<const uint4*>(asrc + (k0));                  \
-    ra##S##0 = pa[0];                                                               \
-    ra##S##1 = pa[1];                                                               \
-    ra##S##2 = pa[2];                                                               \
-    ra##S##3 = pa[3];                                                               \
-    const uint4* pb = reinterpret_cast<const uint4*>(bsrc + (NV ? (k0) / 2 : (k0))); \
-    rb##S##0 = pb[0];                                                               \
-    rb##S##1 = pb[1];                                                               \
-    if (!NV) {                                                                      \
-      rb##S##2 = pb[2];                                                             \
-      rb##S##3 = pb[3];                                                             \
-    }                                                                               \
-    if (NV) rs##S = *reinterpret_cast<const uint32_t*>(ssrc + (k0) / 16);           \
-  }
-#define BSM_BIG_LSTORE(buf, S)                                                      \
-  {                                                                                 \
-    uint4* da = reinterpret_cast<uint4*>(&As[buf][sr][32 * kh]);                    \
-    da[0] = ra##S##0;                                                               \
-    da[1] = ra##S##1;                                                               \
-    da[2] = ra##S##2;                                                               \
-    da[3] = ra##S##3;                                                               \
-    uint32_t* db = reinterpret_cast<uint32_t*>(&Bs[buf][br][0]);                    \
-    db[0] = (rb##S##0).x; db[1] = (rb##S##0).y; db[2] = (rb##S##0).z; db[3] = (rb##S##0).w; \
-    db[4] = (rb##S##1).x; db[5] = (rb##S##1).y; db[6] = (rb##S##1).z; db[7] = (rb##S##1).w; \
-    if (!NV) {                                                                      \
-      db[8] = (rb##S##2).x; db[9] = (rb##S##2).y; db[10] = (rb##S##2).z; db[11] = (rb##S##2).w; \
-      db[12] = (rb##S##3).x; db[13] = (rb##S##3).y; db[14] = (rb##S##3).z; db[15] = (rb##S##3).w; \
-    }                                                                               \
-    if (NV) Bsc[buf][br] = rs##S;                                                   \
-  }
-  // LDS weight row of this wave's N tile t: GEMM1 gate tiles 0,1 / up tiles 2,3; GEMM2 4 consecutive
-#define BSM_BIG_BROW(t) (G1 ? (((t) < 2) ? wn * 64 + 32 * (t) : kGBN / 2 + wn * 64 + 32 * ((t) - 2)) : wn * 128 + 32 * (t))
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3, sc4 = make_uint4(0, 0, 0, 0);
+  uint32_t rs1 = 0;
+  auto gload = [&](int s) {  // global loads of K step s into registers
+    ra0 = *reinterpret_cast<const uint4*>(as0 + s * kGBK);
+    ra1 = *reinterpret_cast<const uint4*>(as1 + s * kGBK);
+    ra2 = *reinterpret_cast<const uint4*>(as2 + s * kGBK);
+    ra3 = *reinterpret_cast<const uint4*>(as3 + s * kGBK);
+    const uint8_t* bs = bbase + s * (NV ? kGBK / 2 : kGBK);
+    rb0 = *reinterpret_cast<const uint4*>(bs + bo0);
+    rb1 = *reinterpret_cast<const uint4*>(bs + bo1);
+    if constexpr (kBI > 2) {
+      rb2 = *reinterpret_cast<const uint4*>(bs + bo2);
+      rb3 = *reinterpret_cast<const uint4*>(bs + bo3);
+    }
+    if constexpr (NV) {
+      if (s4) {
+        if ((s & 3) == 0) sc4 = *reinterpret_cast<const uint4*>(ssrc + 4 * s);
+      } else {
+        rs1 = *reinterpret_cast<const uint32_t*>(ssrc + 4 * s);
+      }
+    }
+  };
+  auto lstore = [&](int buf, int s) {  // registers of K step s into LDS buffer buf
+    *reinterpret_cast<uint4*>(&As[buf][(tid >> 3)][8 * apart]) = ra0;
+    *reinterpret_cast<uint4*>(&As[buf][32 + (tid >> 3)][8 * apart]) = ra1;
+    *reinterpret_cast<uint4*>(&As[buf][64 + (tid >> 3)][8 * apart]) = ra2;
+    *reinterpret_cast<uint4*>(&As[buf][96 + (tid >> 3)][8 * apart]) = ra3;
+    auto bst = [&](int i, uint4 v) {
+      uint32_t* d = reinterpret_cast<uint32_t*>(&Bs[buf][(256 / kBP) * i + tid / kBP][16 * bpart]);
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
+    };
+    bst(0, rb0);
+    bst(1, rb1);
+    if constexpr (kBI > 2) {
+      bst(2, rb2);
+      bst(3, rb3);
+    }
+    if constexpr (NV) {
+      const int j = s & 3;
+      Bsc[buf][tid] = !s4 ? rs1 : j == 0 ? sc4.x : j == 1 ? sc4.y : j == 2 ? sc4.z : sc4.w;
+    }
+  };
+  // LDS weight row of this wave's N tile t: GEMM1 gate tile 0 / up tile 1; GEMM2 2 consecutive
+#define BSM_BIG_BROW(t) (G1 ? ((t) == 0 ? 32 * wave : kGBN / 2 + 32 * wave) : 64 * wave + 32 * (t))
 
-  f16v acc[2][4];
+  f16v acc[4][2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mt][t][q] = 0.0f;
 
   const int nk = (int)(K / kGBK);
-  BSM_BIG_GLOAD(0, X)
-  BSM_BIG_LSTORE(0, X)
+  gload(0);
+  lstore(0, 0);
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
     const int buf = ks & 1;
-    if (ks + 1 < nk) BSM_BIG_GLOAD((int64_t)(ks + 1) * kGBK, X)
+    if (ks + 1 < nk) gload(ks + 1);
 #pragma unroll
     for (int k16 = 0; k16 < kGBK / 16; ++k16) {
-      h8v a[2];
+      h8v a[4];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        a[mt] = *reinterpret_cast<const h8v*>(&As[buf][wm * 64 + mt * 32 + l32][k16 * 16 + lh * 8]);
+      for (int mt = 0; mt < 4; ++mt)
+        a[mt] = *reinterpret_cast<const h8v*>(&As[buf][mt * 32 + l32][k16 * 16 + lh * 8]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 2; ++t) {
         const int brow = BSM_BIG_BROW(t) + l32;
         h8v b;
         if constexpr (NV) {
@@ -856,51 +883,46 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
           b = dec_fp8x8(w.x, w.y);
         }
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[mt][t] = mfma32<A16>(a[mt], b, acc[mt][t]);
+        for (int mt = 0; mt < 4; ++mt) acc[mt][t] = mfma32<A16>(a[mt], b, acc[mt][t]);
       }
     }
-    if (ks + 1 < nk) BSM_BIG_LSTORE(buf ^ 1, X)
+    if (ks + 1 < nk) lstore(buf ^ 1, ks + 1);
     __syncthreads();
   }
-#undef BSM_BIG_GLOAD
-#undef BSM_BIG_LSTORE
 #undef BSM_BIG_BROW
 
   float hmax = 0.0f;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int ro = wm * 64 + mt * 32 + 8 * q + 4 * lh + j;
+        const int ro = mt * 32 + 8 * q + 4 * lh + j;
         if (ro >= nrows) continue;
         const int r = 4 * q + j;
         if (G1) {
           float* hr = out + (int64_t)(row0 + ro) * I;
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int64_t col = c0 + wn * 64 + 32 * t + l32;
-            float sg, su;
-            if (NV) {
-              const float ag = A16 ? 1.0f : a_gs[0];
-              sg = ag * wgs[2 * e];
-              su = ag * wgs[2 * e + 1];
-            } else {
-              const float sx = a_rs[row_pair[row0 + ro] / topk];
-              const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
-              sg = sx * ws[col];
-              su = sx * ws[I + col];
-            }
-            const float h = silu_mul(acc[mt][t][r] * sg, acc[mt][t + 2][r] * su);
-            hr[col] = h;
-            hmax = fmaxf(hmax, fabsf(h));
+          const int64_t col = c0 + 32 * wave + l32;
+          float sg, su;
+          if (NV) {
+            const float ag = A16 ? 1.0f : a_gs[0];
+            sg = ag * wgs[2 * e];
+            su = ag * wgs[2 * e + 1];
+          } else {
+            const float sx = a_rs[row_pair[row0 + ro] / topk];
+            const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
+            sg = sx * ws[col];
+            su = sx * ws[I + col];
           }
+          const float h = silu_mul(acc[mt][0][r] * sg, acc[mt][1][r] * su);
+          hr[col] = h;
+          hmax = fmaxf(hmax, fabsf(h));
         } else {
           float* yr = out + (int64_t)(row0 + ro) * H;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int64_t col = c0 + wn * 128 + 32 * t + l32;
+          for (int t = 0; t < 2; ++t) {
+            const int64_t col = c0 + 64 * wave + 32 * t + l32;
             if (NV) {
               yr[col] = acc[mt][t][r] * ((A16 ? 1.0f : a_gs[0]) * wgs[e]);
             } else {
