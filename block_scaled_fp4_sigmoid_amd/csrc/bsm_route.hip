@@ -15,8 +15,8 @@
 //   k_rowstats    per row of x and w: an upper bound of the 2-norm and the
 //                 lowest set-bit exponent over the row's nonzero entries
 //   k_logits_rb   small batches: 4 tokens x 8 experts per workgroup over the
-//   / k_logits    whole row (lanes own K slices) / large batches: 64x64 LDS
-//                 tiles.  Binary64 FMA accumulation of products that are
+//   / k_logits    whole row (lanes own K slices) / large batches: 64x64
+//                 double-buffered LDS tiles, 8x4 logits per thread.  Binary64 FMA accumulation of products that are
 //                 exact in binary64; the epilogue proves the binary32
 //                 rounding of each logit (exact sum, or error bound away from
 //                 every rounding boundary) and marks the rest with NaN
@@ -159,7 +159,7 @@ struct ExactLds {
 template <bool XB, bool WB, int NT>
 __device__ float exact_logit_wg(const void* __restrict__ x, const void* __restrict__ w, int64_t t, int64_t e,
                                 int64_t H, double A, ExactLds* L) {
-  static_assert(NT == 256, "four waves");
+  static_assert(NT % 64 == 0 && NT <= 256, "one to four waves");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int base = win_base((int)((d2u(A) >> 52) & 0x7FF) + 1);
@@ -363,77 +363,110 @@ __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, c
 
 // Large batches: 64x64 token x expert tiles staged through LDS, 4x4 outputs
 // per thread; binary64 FMA chains of kBK products added to running sums.
-template <bool XB, bool WB>
-__global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
+// Large batches: a workgroup of 128 threads owns 64 tokens x 64 experts; each
+// thread accumulates 8 tokens x 4 experts.  K steps of kBK are staged through
+// double-buffered LDS as binary64 (converted once per element), laid out
+// [k][row] so a wave's staging stores and its expert reads are contiguous and
+// its token reads are broadcasts.  Per logit: an FMA chain over the kBK
+// products of a step (k ascending), added to the running sum (steps
+// ascending).
+template <bool XB, bool WB, bool VEC>
+__global__ __launch_bounds__(128) void k_logits(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
                                                 int64_t E, int64_t H, const double* __restrict__ norm,
                                                 const int* __restrict__ lsb, int nadd, float* __restrict__ logits,
                                                 int* __restrict__ diag) {
-  __shared__ double xs[kBK][kTile + 2];  // converted to binary64 once per staged element
-  __shared__ double wsm[kBK][kTile + 2];
-  __shared__ int unc[kTile * kTile];
+  __shared__ __attribute__((aligned(16))) double tl[2][2][kBK][kTile];  // [buffer][x, w][k][row]
   __shared__ int n_unc;
   __shared__ ExactLds xl;
+  int* unc = reinterpret_cast<int*>(&tl[0][0][0][0]);  // after the main loop: the tile's uncertain logits
+  static_assert(sizeof(tl) >= sizeof(int) * kTile * kTile, "uncertain-logit list fits the staging buffers");
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
+  const int tx = tid & 15, ty = tid >> 4;  // experts {2tx, 2tx+1, 32+2tx, 33+2tx}; tokens {4ty+i, 32+4ty+i}
   const int64_t t0 = (int64_t)blockIdx.x * kTile, e0 = (int64_t)blockIdx.y * kTile;
-  double acc[4][4];
+  // staging: row sr of the x and w tiles, k values 16 sh .. +15 of the step.  Rows past T or E
+  // repeat the last row: their logits are never stored, and no other logit reads them.
+  const int sr = tid & 63, sh = tid >> 6;
+  const int64_t xr = t0 + sr < T ? t0 + sr : T - 1, wr = e0 + sr < E ? e0 + sr : E - 1;
+  const int64_t xo = xr * H + 16 * sh, wo = wr * H + 16 * sh;
+  float xv[16], wv[16];
+  auto gload = [&](int64_t kb) {
+    if constexpr (VEC) {  // H % kBK == 0: every k of the step is in range
+      ld8<XB>(x, xo + kb, xv);
+      ld8<XB>(x, xo + kb + 8, xv + 8);
+      ld8<WB>(w, wo + kb, wv);
+      ld8<WB>(w, wo + kb + 8, wv + 8);
+    } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  const int lr = tid >> 2;        // row of the tile this thread stages
-  const int lk = (tid & 3) * 8;   // first k of the 8 it stages
-  for (int64_t kb = 0; kb < H; kb += kBK) {
-    {
-      const int64_t t = t0 + lr, e = e0 + lr;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int64_t k = kb + lk + q;
-        const bool kin = k < H;
-        xs[lk + q][lr] = (kin && t < T) ? (double)ld1<XB>(x, t * H + k) : 0.0;
-        wsm[lk + q][lr] = (kin && e < E) ? (double)ld1<WB>(w, e * H + k) : 0.0;
+      for (int q = 0; q < 16; ++q) {
+        const bool kin = kb + 16 * sh + q < H;
+        xv[q] = kin ? ld1<XB>(x, xo + kb + q) : 0.0f;
+        wv[q] = kin ? ld1<WB>(w, wo + kb + q) : 0.0f;
       }
     }
-    __syncthreads();
-    double blk[4][4];  // chain of kBK products per step, then one add: depth kBK + H / kBK
+  };
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 16; ++q) {
+      tl[buf][0][16 * sh + q][sr] = (double)xv[q];
+      tl[buf][1][16 * sh + q][sr] = (double)wv[q];
+    }
+  };
+  double acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  const int nst = (int)((H + kBK - 1) / kBK);
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nst) gload((int64_t)(s + 1) * kBK);
+    double blk[8][4];  // chain of kBK products per step, then one add: depth kBK + H / kBK
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) blk[i][j] = 0.0;
-#pragma unroll 4
+#pragma unroll 2
     for (int kk = 0; kk < kBK; ++kk) {
-      const double2 a01 = *reinterpret_cast<const double2*>(&xs[kk][ty * 4]);
-      const double2 a23 = *reinterpret_cast<const double2*>(&xs[kk][ty * 4 + 2]);
-      const double2 b01 = *reinterpret_cast<const double2*>(&wsm[kk][tx * 4]);
-      const double2 b23 = *reinterpret_cast<const double2*>(&wsm[kk][tx * 4 + 2]);
-      const double av[4] = {a01.x, a01.y, a23.x, a23.y};
-      const double bv[4] = {b01.x, b01.y, b23.x, b23.y};
+      const double2 a0 = *reinterpret_cast<const double2*>(&tl[buf][0][kk][4 * ty]);
+      const double2 a1 = *reinterpret_cast<const double2*>(&tl[buf][0][kk][4 * ty + 2]);
+      const double2 a2 = *reinterpret_cast<const double2*>(&tl[buf][0][kk][32 + 4 * ty]);
+      const double2 a3 = *reinterpret_cast<const double2*>(&tl[buf][0][kk][32 + 4 * ty + 2]);
+      const double2 b0 = *reinterpret_cast<const double2*>(&tl[buf][1][kk][2 * tx]);
+      const double2 b1 = *reinterpret_cast<const double2*>(&tl[buf][1][kk][32 + 2 * tx]);
+      const double av[8] = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+      const double bv[4] = {b0.x, b0.y, b1.x, b1.y};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) blk[i][j] = fma(av[i], bv[j], blk[i][j]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] += blk[i][j];
+    if (s + 1 < nst) lstore(buf ^ 1);
     __syncthreads();
   }
   if (tid == 0) n_unc = 0;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = t0 + ty * 4 + i;
+  for (int i = 0; i < 8; ++i) {
+    const int tr = (i < 4 ? 0 : 32) + 4 * ty + (i & 3);
+    const int64_t t = t0 + tr;
     if (t >= T) continue;
     const double nx = norm[t];
     const int lx = lsb[t];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t e = e0 + tx * 4 + j;
+      const int ec = (j < 2 ? 0 : 32) + 2 * tx + (j & 1);
+      const int64_t e = e0 + ec;
       if (e < E) {
         const float r = certify_logit(acc[i][j], nx, norm[T + e], lx, lsb[T + e], nadd);
         logits[t * E + e] = r;
-        if (r != r) unc[atomicAdd(&n_unc, 1)] = (ty * 4 + i) * kTile + tx * 4 + j;
+        if (r != r) unc[atomicAdd(&n_unc, 1)] = tr * kTile + ec;
       }
     }
   }
@@ -442,7 +475,7 @@ __global__ __launch_bounds__(256) void k_logits(const void* __restrict__ x, cons
   if (nu && tid == 0) atomicAdd(&diag[0], nu);
   for (int u = 0; u < nu; ++u) {
     const int64_t t = t0 + unc[u] / kTile, e = e0 + unc[u] % kTile;
-    const float r = exact_logit_wg<XB, WB, 256>(x, w, t, e, H, norm[t] * norm[T + e] * (1.0 + 0x1p-40), &xl);
+    const float r = exact_logit_wg<XB, WB, 128>(x, w, t, e, H, norm[t] * norm[T + e] * (1.0 + 0x1p-40), &xl);
     if (tid == 0) logits[t * E + e] = r;
   }
 }
@@ -568,8 +601,10 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
     k_rowstats<XB, WB, false><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb, diag);                              \
   if (L.rb)                                                                                                \
     k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, diag);                    \
+  else if (H % kBK == 0)                                                                                   \
+    k_logits<XB, WB, true><<<gl, 128, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, diag);                  \
   else                                                                                                     \
-    k_logits<XB, WB><<<gl, 256, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, diag);                        \
+    k_logits<XB, WB, false><<<gl, 128, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, diag);                 \
   stage_mark(1, 1, st);                                                                                    \
   k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, diag);
   if (xb && wb) {

@@ -90,3 +90,23 @@ def test_route_exact_fallback_paths(gpu_lib):
     ids, wts, scores, diag = _run(gpu_lib, x, w, 4, 2, 4, x_bf16=False, w_bf16=False)
     _check((ids, wts, scores, diag), x, w, 4, 2, 4)
     assert diag[0] > 0  # the fallback ran
+
+
+@pytest.mark.parametrize("T,H,E,x_bf16", [(1000, 200, 520, False), (4100, 256, 200, True)])
+def test_route_tiled_ragged_with_fallbacks(gpu_lib, T, H, E, x_bf16):
+    """At least 128 tiles of 64 x 64 select the tiled logits kernel: ragged token and expert tiles, H with
+    (256) and without (200) whole K steps of 32, and cancelling rows that need the exact recomputation."""
+    rng = np.random.default_rng(T + H)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    if x_bf16:
+        x = W.to_bf16_f32(x)
+    w = W.to_bf16_f32(w)
+    rows = np.arange(7, T, 97)
+    x[rows, 0] = 2.0 ** 20
+    x[rows, 1] = -(2.0 ** 20)
+    w[:, 0] = 1.0
+    w[:, 1] = 1.0
+    ids, wts, scores, diag = _run(gpu_lib, x, w, 8, 4, 8, x_bf16=x_bf16)
+    _check((ids, wts, scores, diag), x, w, 8, 4, 8)
+    assert diag[0] > 0  # the tiled kernel's exact fallback ran
