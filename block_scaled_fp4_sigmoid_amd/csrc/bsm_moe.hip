@@ -941,6 +941,130 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// FP8_DYNAMIC down projection for many rows per expert on the FP8 matrix
+// cores ("f8"): the E4M3 codes of h and of the weights go into
+// v_mfma_scale_f32_32x32x64_f8f6f4 as they are (both operands E4M3, block
+// scale 2^0), and the per-row and per-channel scales multiply the FP32 result
+// in the epilogue, where they factor out of the sum.  Products of two E4M3
+// values are exact; the matrix core adds each group of 64 of them with a
+// fixed-point alignment to the largest before the FP32 accumulator, which
+// carries more rounding than an FP32 chain (relative L2 about 1.4e-5 per
+// 64-product block on normal data).  y is combined, never requantized, so
+// that error reaches the layer output unamplified.  (The gate/up projection
+// stays on exactly decoded FP16 operands: h is requantized to E4M3 per row,
+// and an error of that size flips codes near rounding boundaries, each by up
+// to 1/8 of the value.)  128 rows x 256 weight rows per workgroup, 4 waves of
+// 128 rows x 64 weight rows (4 x 2 tiles of 32 x 32), K in steps of 64 (one
+// MFMA K) through double-buffered LDS.  Operand layout: lane l carries row /
+// column l % 32 and k bytes 32 (l / 32) .. +31 of the step.
+// ---------------------------------------------------------------------------
+typedef int i8v __attribute__((ext_vector_type(8)));
+constexpr int kF8Row = 80;  // LDS bytes per row and K step: 64 + 16 pad (conflict-free 16-byte reads)
+
+__global__ __launch_bounds__(256, 2) void k_gemm_f8_down(const uint8_t* __restrict__ ac, const float* __restrict__ a_rs,
+                                                         const uint8_t* __restrict__ wc, const float* __restrict__ wsc,
+                                                         const int4* __restrict__ tiles, const int* __restrict__ ntiles,
+                                                         int64_t K, int64_t H, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][kGBM][kF8Row];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGBN][kF8Row];
+  if ((int)blockIdx.y >= *ntiles) return;
+  const int4 ti = tiles[blockIdx.y];
+  const int e = ti.x, row0 = ti.y, nrows = ti.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int64_t c0 = (int64_t)blockIdx.x * kGBN;
+  // staging: 4 lanes per 64-byte row segment; h rows 64 i + tid / 4 (i < 2), weight rows 64 i + tid / 4 (i < 4)
+  const int part = tid & 3, srow = tid >> 2;
+  auto arow = [&](int i) -> const uint8_t* {
+    const int r = 64 * i + srow;
+    const int ar = r < nrows ? r : nrows - 1;
+    return ac + (int64_t)(row0 + ar) * K + 16 * part;
+  };
+  const uint8_t *as0 = arow(0), *as1 = arow(1);
+  const uint8_t* bbase = wc + ((int64_t)e * H + c0) * K + 16 * part;
+  auto boff = [&](int i) -> uint32_t { return (uint32_t)((64 * i + srow) * K); };
+  const uint32_t bo0 = boff(0), bo1 = boff(1), bo2 = boff(2), bo3 = boff(3);
+  uint4 ra0, ra1, rb0, rb1, rb2, rb3;
+  auto gload = [&](int s) {
+    const int64_t k0 = (int64_t)s * kGBK;
+    ra0 = *reinterpret_cast<const uint4*>(as0 + k0);
+    ra1 = *reinterpret_cast<const uint4*>(as1 + k0);
+    const uint8_t* bs = bbase + k0;
+    rb0 = *reinterpret_cast<const uint4*>(bs + bo0);
+    rb1 = *reinterpret_cast<const uint4*>(bs + bo1);
+    rb2 = *reinterpret_cast<const uint4*>(bs + bo2);
+    rb3 = *reinterpret_cast<const uint4*>(bs + bo3);
+  };
+  auto lstore = [&](int buf) {
+    *reinterpret_cast<uint4*>(&As[buf][srow][16 * part]) = ra0;
+    *reinterpret_cast<uint4*>(&As[buf][64 + srow][16 * part]) = ra1;
+    *reinterpret_cast<uint4*>(&Bs[buf][srow][16 * part]) = rb0;
+    *reinterpret_cast<uint4*>(&Bs[buf][64 + srow][16 * part]) = rb1;
+    *reinterpret_cast<uint4*>(&Bs[buf][128 + srow][16 * part]) = rb2;
+    *reinterpret_cast<uint4*>(&Bs[buf][192 + srow][16 * part]) = rb3;
+  };
+  auto frag = [](const uint8_t* p) -> i8v {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(p);
+    const uint4 u1 = *reinterpret_cast<const uint4*>(p + 16);
+    i8v v;
+    v[0] = (int)u0.x; v[1] = (int)u0.y; v[2] = (int)u0.z; v[3] = (int)u0.w;
+    v[4] = (int)u1.x; v[5] = (int)u1.y; v[6] = (int)u1.z; v[7] = (int)u1.w;
+    return v;
+  };
+  // LDS weight row of this wave's N tile t
+  auto brow0 = [&](int t) -> int { return 64 * wave + 32 * t; };
+
+  f16v acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mt][t][q] = 0.0f;
+
+  const int nk = (int)(K / kGBK);
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) gload(ks + 1);
+    i8v a[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) a[mt] = frag(&As[buf][mt * 32 + l32][32 * lh]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const i8v b = frag(&Bs[buf][brow0(t) + l32][32 * lh]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt], b, acc[mt][t], 0, 0, 0, 127, 0, 127);
+    }
+    if (ks + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ro = mt * 32 + 8 * q + 4 * lh + j;
+        if (ro >= nrows) continue;
+        const int r = 4 * q + j;
+        float* yr = out + (int64_t)(row0 + ro) * H;
+        const float* ws = wsc + (int64_t)e * H;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int64_t col = c0 + 64 * wave + 32 * t + l32;
+          yr[col] = acc[mt][t][r] * a_rs[row0 + ro] * ws[col];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const int* __restrict__ pair_row,
@@ -1308,6 +1432,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #ifndef BSM_FP8_KB
 #define BSM_FP8_KB 64
 #endif
+#ifndef BSM_FP8_MFMA
+#define BSM_FP8_MFMA 1  // down projection of many-row experts on the FP8 matrix cores (0: decoded to FP16)
+#endif
     if (a.H % (4 * BSM_FP8_KB) == 0) {
       BSM_G1(false, BSM_FP8_KB);
     } else {
@@ -1317,10 +1444,23 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     err = launch_fp8_quantize(h_f32, false, L.P, a.I, h_codes, reinterpret_cast<float*>(h_scales), st, hdec);
     if (err != hipSuccess) return err;
     stage_mark(0, 3, st);
-    if (a.I % (4 * BSM_FP8_KB) == 0) {
-      BSM_G2(false, BSM_FP8_KB);
+    if (!BSM_FP8_MFMA) {
+      if (a.I % (4 * BSM_FP8_KB) == 0) {
+        BSM_G2(false, BSM_FP8_KB);
+      } else {
+        BSM_G2(false, 32);
+      }
     } else {
-      BSM_G2(false, 32);
+      // few-row experts: E4M3 decoded to FP16 next to the weight stream; many-row experts: FP8 matrix cores
+      const float* hsc = reinterpret_cast<const float*>(h_scales);
+      if (a.I % (4 * BSM_FP8_KB) == 0)
+        k_skinny<false, false, BSM_FP8_KB, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(
+            hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
+      else
+        k_skinny<false, false, 32, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(
+            hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
+      k_gemm_f8_down<<<dim3((unsigned)(a.H / kGBN), (unsigned)L.max_tiles_w), 256, 0, st>>>(
+          h_codes, hsc, a.w2_codes, reinterpret_cast<const float*>(a.w2_scales), tiles_w, ntiles_w, a.I, a.H, y);
     }
   }
 #undef BSM_G1

@@ -13,12 +13,18 @@ from tests.helpers import host_masters, np_, oracle_experts, rel_l2, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
-# Stage tolerances (relative L2).  Both formats decode their operands exactly to
-# FP16 (NVFP4 q * s_b: <= 6 significant bits; E4M3: 4) and accumulate in FP32
-# on the FP16 MFMA.  A K-term FP32 sum of products with random signs carries a
-# relative error of order sqrt(K) * 2^-24 (about 4e-6 at K = 5120) per element,
-# so the relative L2 over a stage sits near 1e-6; the gate is 1e-5.
-H_TOL = {"nvfp4": 1e-5, "fp8": 1e-5}
+# Stage tolerances (relative L2).  NVFP4, and FP8 experts with few rows, decode
+# their operands exactly to FP16 (NVFP4 q * s_b: <= 6 significant bits; E4M3:
+# 4) and accumulate in FP32 on the FP16 MFMA.  A K-term FP32 sum of products
+# with random signs carries a relative error of order sqrt(K) * 2^-24 (about
+# 4e-6 at K = 5120) per element, so the relative L2 over a stage sits near
+# 1e-7..1e-6; the gate is 1e-5.  The FP8 down projection of experts with many
+# rows multiplies the E4M3 codes on the FP8 matrix cores, which add each group
+# of 64 exact products with a fixed-point alignment to the largest before the
+# FP32 accumulator: measured on one 32x32x64 block of normal data, relative L2
+# 1.4e-5; over the y stage about 2e-5.  The FP8 gate is 1e-4 (layer outputs:
+# 1e-3).
+H_TOL = {"nvfp4": 1e-5, "fp8": 1e-4}
 
 
 def _weights_match(gpu_w, experts, fmt, ids):
@@ -220,11 +226,24 @@ def test_moe_decode_full_size_sampled(gpu_lib, fmt):
     assert e2e <= 1e-3
 
 
+# hidden 1024, intermediate 512, 8 experts: two column tiles of the many-row kernels in both GEMMs
+MID = W.LayerConfig("mid", 7, T=700, H=1024, I=512, E=8, n_group=2, topk_group=1, topk=2, router_fp32=True)
+
+
 @pytest.mark.parametrize("fmt,T", [("nvfp4", 300), ("nvfp4", 1000), ("fp8", 300), ("fp8", 1000)])
 def test_moe_tiny_shapes_many_tokens(gpu_lib, fmt, T):
     """Tiny layer with many tokens: experts with 33-64 rows (up to four 16-row tiles, T = 300) and above 64 rows
     (LDS-tiled kernel, T = 1000) next to small ones, ragged tiles."""
-    cfg = W.TINY
+    _many_tokens(gpu_lib, W.TINY, fmt, T)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_moe_mid_shapes_many_rows(gpu_lib, fmt):
+    """Every expert above 64 rows in ragged 128-row tiles, several column tiles per GEMM; every row checked."""
+    _many_tokens(gpu_lib, MID, fmt, MID.T)
+
+
+def _many_tokens(gpu_lib, cfg, fmt, T):
     x, wr = W.activations(cfg, T=T), W.router_weights(cfg)
     masters, w13, w2 = host_masters(cfg)
     gw = gpu_lib.quantize_expert_weights(w13, w2, fmt)
@@ -237,11 +256,13 @@ def test_moe_tiny_shapes_many_tokens(gpu_lib, fmt, T):
     ref = OM.moe_layer(x, wr, experts, fmt, cfg.n_group, cfg.topk_group, cfg.topk, cfg.combine_scale)
     assert np.array_equal(np_(ids), ref["ids"])
     counts = np.bincount(ref["ids"].ravel(), minlength=cfg.E)
-    assert counts.max() > (64 if T >= 1000 else 32)
+    assert counts.max() > (64 if T >= 700 else 32)
     P = T * cfg.topk
     st = _stages(gpu_lib, fmt, cfg, T, ws, P)
     _, offsets, row_of_pair, _ = OM.permute(ref["ids"], cfg.E)
-    assert rel_l2(st["h"][row_of_pair], ref["h"]) <= H_TOL[fmt]
+    h_err = rel_l2(st["h"][row_of_pair], ref["h"])
+    print(f"{cfg.name} {fmt} T={T}: h rel L2 {h_err:.3e}")
+    assert h_err <= H_TOL[fmt]
     if fmt == "nvfp4":
         oc, os_, og = Q.nvfp4_quantize(st["h"])
         hh = Q.nvfp4_dequantize_exact(oc, os_, og)
@@ -253,9 +274,11 @@ def test_moe_tiny_shapes_many_tokens(gpu_lib, fmt, T):
     for e in np.unique(ref["ids"]):
         rows = np.arange(offsets[e], offsets[e + 1])
         y_ref[rows] = OM.gemm_f32(hh[rows], experts[int(e)].decoded()[2])
-    assert rel_l2(st["y"], y_ref) <= H_TOL[fmt]
+    y_err = rel_l2(st["y"], y_ref)
+    print(f"{cfg.name} {fmt} T={T}: y rel L2 {y_err:.3e}")
+    assert y_err <= H_TOL[fmt]
     e2e = rel_l2(np_(out), ref["out"])
-    print(f"tiny {fmt} T={T}: max rows {counts.max()}, end-to-end rel L2 {e2e:.3e}")
+    print(f"{cfg.name} {fmt} T={T}: max rows {counts.max()}, end-to-end rel L2 {e2e:.3e}")
     assert e2e <= 1e-3
 
 

@@ -69,6 +69,16 @@ def test_w4a16_tiny_layer(gpu_lib, T):
         assert counts.max() > 64
 
 
+def test_w4a16_mid_shapes_many_rows(gpu_lib):
+    """Hidden 1024, intermediate 512, 8 experts, 700 tokens: every expert in ragged 128-row tiles."""
+    cfg = W.LayerConfig("mid", 7, T=700, H=1024, I=512, E=8, n_group=2, topk_group=1, topk=2, router_fp32=True)
+    x, wr = W.activations(cfg), W.router_weights(cfg)
+    masters, w13, w2 = host_masters(cfg)
+    gw = gpu_lib.quantize_expert_weights(w13, w2, "nvfp4")
+    counts = _check_layer(gpu_lib, cfg, cfg.T, x, wr, to_dev_f32(wr), oracle_experts(masters, "w4a16"), gw)
+    assert counts.min() > 64
+
+
 def test_w4a16_deterministic_and_matches_w4a4_weights(gpu_lib):
     cfg = W.TINY
     x, wr = W.activations(cfg), W.router_weights(cfg)
