@@ -394,9 +394,12 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
   const int e = ti.x, row0 = ti.y, nrows = ti.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, g = lane >> 4;
-  // activation staging: 16 threads per row
+  // activation staging: 16 threads per row.  Only the tile's nrows rows are staged: an MFMA output row
+  // depends on its own A row only, and the rows past nrows are never stored, so their LDS rows may hold
+  // anything (an expert at decode has about 2 of its 16 rows).
   const int sr = tid >> 4, sseg = tid & 15;
-  const int ar = sr < nrows ? sr : nrows - 1;
+  const bool stage = sr < nrows;
+  const int ar = stage ? sr : nrows - 1;
   const _Float16* asrc = (G1 ? act + (int64_t)(row_pair[row0 + ar] / topk) * K : act + (int64_t)(row0 + ar) * K) +
                          sseg * (KS / 16);
   // weight rows of this wave
@@ -435,17 +438,19 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
 #pragma unroll
     for (int j = 0; j < NT; ++j) s_load<KB>(srow[j], g < nsteps, sc[j]);
   }
-  ra0 = reinterpret_cast<const uint4*>(asrc)[0];
-  if constexpr (kAv >= 2) ra1 = reinterpret_cast<const uint4*>(asrc)[1];
-  if constexpr (kAv >= 4) {
-    ra2 = reinterpret_cast<const uint4*>(asrc)[2];
-    ra3 = reinterpret_cast<const uint4*>(asrc)[3];
-  }
-  reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[0] = ra0;
-  if constexpr (kAv >= 2) reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[1] = ra1;
-  if constexpr (kAv >= 4) {
-    reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[2] = ra2;
-    reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[3] = ra3;
+  if (stage) {
+    ra0 = reinterpret_cast<const uint4*>(asrc)[0];
+    if constexpr (kAv >= 2) ra1 = reinterpret_cast<const uint4*>(asrc)[1];
+    if constexpr (kAv >= 4) {
+      ra2 = reinterpret_cast<const uint4*>(asrc)[2];
+      ra3 = reinterpret_cast<const uint4*>(asrc)[3];
+    }
+    reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[0] = ra0;
+    if constexpr (kAv >= 2) reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[1] = ra1;
+    if constexpr (kAv >= 4) {
+      reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[2] = ra2;
+      reinterpret_cast<uint4*>(&As[0][sr][sseg * (KS / 16)])[3] = ra3;
+    }
   }
   __syncthreads();
   // two super-steps per iteration so the code register set of each step is static
@@ -464,17 +469,19 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
     }                                                                                                     \
     if (more) {                                                                                           \
       const int64_t ko = (int64_t)((ST) + 1) * KS;                                                        \
-      ra0 = reinterpret_cast<const uint4*>(asrc + ko)[0];                                                 \
-      if constexpr (kAv >= 2) ra1 = reinterpret_cast<const uint4*>(asrc + ko)[1];                         \
-      if constexpr (kAv >= 4) {                                                                           \
-        ra2 = reinterpret_cast<const uint4*>(asrc + ko)[2];                                               \
-        ra3 = reinterpret_cast<const uint4*>(asrc + ko)[3];                                               \
+      if (stage) {                                                                                        \
+        ra0 = reinterpret_cast<const uint4*>(asrc + ko)[0];                                               \
+        if constexpr (kAv >= 2) ra1 = reinterpret_cast<const uint4*>(asrc + ko)[1];                       \
+        if constexpr (kAv >= 4) {                                                                         \
+          ra2 = reinterpret_cast<const uint4*>(asrc + ko)[2];                                             \
+          ra3 = reinterpret_cast<const uint4*>(asrc + ko)[3];                                             \
+        }                                                                                                 \
       }                                                                                                   \
       _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                     \
         b_load<NV, KB>(crow[j] + ((ST) + 1) * (int64_t)cstep, BN[j]);                                     \
     }                                                                                                     \
     sk_mma_step<NV, KB, NT, 0, A16>(&As[CUR][m][VPU * g], BC, sdw, selA, selB, acc);                      \
-    if (more) {                                                                                           \
+    if (more && stage) {                                                                                  \
       reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[0] = ra0;                            \
       if constexpr (kAv >= 2) reinterpret_cast<uint4*>(&As[(CUR) ^ 1][sr][sseg * (KS / 16)])[1] = ra1;    \
       if constexpr (kAv >= 4) {                                                                           \
@@ -1355,6 +1362,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #ifndef BSM_PREFILL_BIG
 #define BSM_PREFILL_BIG 1  // many-row experts on the 32x32x16 kernel (0: the 16x16x32 one)
 #endif
+  // One permutation chunk (T <= kChunk) counts an expert's rows over a kChunk-bit token mask, so no
+  // expert exceeds kSkinnyMaxRows rows and the many-row kernels have no tiles: they are not launched.
+  static_assert(kChunk <= kSkinnyMaxRows, "a single chunk never yields a many-row expert");
+  const bool many = L.n_chunks > 1;
   const dim3 w1((unsigned)(a.I / (BSM_PREFILL_BIG ? kGBN / 2 : 64)), (unsigned)L.max_tiles_w);
   const dim3 w2((unsigned)(a.H / (BSM_PREFILL_BIG ? kGBN : 128)), (unsigned)L.max_tiles_w);
   _Float16* act = reinterpret_cast<_Float16*>(ws + L.act_f16);
@@ -1375,13 +1386,13 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   k_skinny<NV, true, KB, BSM_SKINNY_NT><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes,  \
                                                             w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I,     \
                                                             h_f32, h_amax);                                   \
-  (BSM_PREFILL_BIG ? k_gemm_big<NV, true> : k_gemm_wide<NV, true>)<<<w1, 256, 0, st>>>(                      \
+  if (many) (BSM_PREFILL_BIG ? k_gemm_big<NV, true> : k_gemm_wide<NV, true>)<<<w1, 256, 0, st>>>(                      \
       act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,                                        \
                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
 #define BSM_G2(NV, KB)                                                                                         \
   k_skinny<NV, false, KB, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
                                               a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
-  (BSM_PREFILL_BIG ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                    \
+  if (many) (BSM_PREFILL_BIG ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                    \
       hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales),                                \
                                              a.w2_codes, w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
 #ifndef BSM_NV_KB
@@ -1393,7 +1404,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K, KB)                                               \
   k_skinny<true, G, KB, BSM_SKINNY_NT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, \
                                                                    tiles, ntiles, K, a.H, a.I, OUT, h_amax);   \
-  (BSM_PREFILL_BIG ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(        \
+  if (many) (BSM_PREFILL_BIG ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(        \
       A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,                                                  \
                                                     ntiles_w, K, a.H, a.I, OUT, h_amax)
     if (a.H % (4 * BSM_NV_KB) == 0) {
@@ -1459,7 +1470,8 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
       else
         k_skinny<false, false, 32, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(
             hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
-      k_gemm_f8_down<<<dim3((unsigned)(a.H / kGBN), (unsigned)L.max_tiles_w), 256, 0, st>>>(
+      if (many)
+        k_gemm_f8_down<<<dim3((unsigned)(a.H / kGBN), (unsigned)L.max_tiles_w), 256, 0, st>>>(
           h_codes, hsc, a.w2_codes, reinterpret_cast<const float*>(a.w2_scales), tiles_w, ntiles_w, a.I, a.H, y);
     }
   }
