@@ -375,8 +375,8 @@ __device__ inline void sk_mma_step(const _Float16* arow, const BRegs<NV, KB>* b,
   if constexpr (J + 1 < KB / 8) sk_mma_step<NV, KB, NT, J + 1, A16>(arow, b, sdw, selA, selB, acc);
 }
 
-template <bool NV, bool G1, int KB, int NT, bool A16 = false>
-__global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
+template <bool NV, bool G1, int KB, int NT, bool A16 = false, int DEPTH = 1>
+__global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
                                                 int topk, const float* __restrict__ a_gs,
                                                 const float* __restrict__ a_rs, const uint8_t* __restrict__ wc,
                                                 const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
@@ -426,7 +426,9 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
   const int ghi = g >> 1;
 
   static_assert(kAv == 1 || kAv == 2 || kAv == 4, "activation staging: 1, 2 or 4 uint4 per thread");
-  BRegs<NV, KB> b0[NT], b1[NT];
+  // DEPTH + 1 register sets of codes: the codes of super-step s + DEPTH load while s is multiplied
+  static_assert(DEPTH == 1 || DEPTH == 2, "weight prefetch depth 1 or 2 super-steps");
+  BRegs<NV, KB> b0[NT], b1[NT], b2[DEPTH > 1 ? NT : 1];
   SRegs<KB> sc[NT];  // NVFP4 scale span of super-step 4q + g (this lane's share of the current group)
   uint32_t sdw[NT][kSV];
   uint4 ra0, ra1, ra2, ra3;
@@ -434,6 +436,12 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
   // tile descriptor), then the activations (GEMM1 gathers them through row_pair)
 #pragma unroll
   for (int j = 0; j < NT; ++j) b_load<NV, KB>(crow[j], b0[j]);
+  if constexpr (DEPTH > 1) {
+    if (nsteps > 1) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) b_load<NV, KB>(crow[j] + cstep, b1[j]);
+    }
+  }
   if constexpr (NV) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) s_load<KB>(srow[j], g < nsteps, sc[j]);
@@ -453,7 +461,6 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
     }
   }
   __syncthreads();
-  // two super-steps per iteration so the code register set of each step is static
 #define BSM_SK_STEP(ST, CUR, BC, BN)                                                                      \
   {                                                                                                       \
     const bool more = (ST) + 1 < nsteps;                                                                  \
@@ -477,8 +484,10 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
           ra3 = reinterpret_cast<const uint4*>(asrc + ko)[3];                                             \
         }                                                                                                 \
       }                                                                                                   \
+    }                                                                                                     \
+    if ((ST) + DEPTH < nsteps) {                                                                          \
       _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                     \
-        b_load<NV, KB>(crow[j] + ((ST) + 1) * (int64_t)cstep, BN[j]);                                     \
+        b_load<NV, KB>(crow[j] + ((ST) + DEPTH) * (int64_t)cstep, BN[j]);                                 \
     }                                                                                                     \
     sk_mma_step<NV, KB, NT, 0, A16>(&As[CUR][m][VPU * g], BC, sdw, selA, selB, acc);                      \
     if (more && stage) {                                                                                  \
@@ -491,9 +500,18 @@ __global__ __launch_bounds__(256, 3) void k_skinny(const _Float16* __restrict__ 
     }                                                                                                     \
     __syncthreads();                                                                                      \
   }
-  for (int st = 0; st < nsteps; st += 2) {
-    BSM_SK_STEP(st, 0, b0, b1)
-    if (st + 1 < nsteps) BSM_SK_STEP(st + 1, 1, b1, b0)
+  if constexpr (DEPTH == 1) {
+    // two super-steps per iteration so the code register set of each step is static
+    for (int st = 0; st < nsteps; st += 2) {
+      BSM_SK_STEP(st, 0, b0, b1)
+      if (st + 1 < nsteps) BSM_SK_STEP(st + 1, 1, b1, b0)
+    }
+  } else {
+    for (int st = 0; st < nsteps; st += 3) {
+      BSM_SK_STEP(st, st & 1, b0, b2)
+      if (st + 1 < nsteps) BSM_SK_STEP(st + 1, (st + 1) & 1, b1, b0)
+      if (st + 2 < nsteps) BSM_SK_STEP(st + 2, st & 1, b2, b1)
+    }
   }
 #undef BSM_SK_STEP
 
@@ -1357,6 +1375,14 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #ifndef BSM_SKINNY_NT
 #define BSM_SKINNY_NT 2
 #endif
+// super-steps of weight codes in flight per lane (measured at decode-64: NVFP4 gate/up 0.62 ms at depth 1,
+// 0.66 ms at depth 2 with occupancy 3 -> 2; FP8 1.01 -> 0.995 ms with depth 2, occupancy 4 -> 3)
+#ifndef BSM_SKINNY_DEPTH
+#define BSM_SKINNY_DEPTH 1
+#endif
+#ifndef BSM_SKINNY_DEPTH_FP8
+#define BSM_SKINNY_DEPTH_FP8 2
+#endif
   const dim3 g1((unsigned)(a.I / (32 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 8*NT h columns
   const dim3 g2((unsigned)(a.H / (64 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 16*NT y columns
 #ifndef BSM_PREFILL_BIG
@@ -1383,14 +1409,14 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   const uint8_t* w2s = reinterpret_cast<const uint8_t*>(a.w2_scales);
   const float* xrs = reinterpret_cast<const float*>(a.x_scales);
 #define BSM_G1(NV, KB)                                                                                          \
-  k_skinny<NV, true, KB, BSM_SKINNY_NT><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes,  \
+  k_skinny<NV, true, KB, BSM_SKINNY_NT, false, NV ? BSM_SKINNY_DEPTH : BSM_SKINNY_DEPTH_FP8><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes,  \
                                                             w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I,     \
                                                             h_f32, h_amax);                                   \
   if (many) (BSM_PREFILL_BIG ? k_gemm_big<NV, true> : k_gemm_wide<NV, true>)<<<w1, 256, 0, st>>>(                      \
       act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,                                        \
                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
 #define BSM_G2(NV, KB)                                                                                         \
-  k_skinny<NV, false, KB, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
+  k_skinny<NV, false, KB, BSM_SKINNY_NT, false, NV ? BSM_SKINNY_DEPTH : BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
                                               a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
   if (many) (BSM_PREFILL_BIG ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                    \
       hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales),                                \
@@ -1402,7 +1428,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   if (a.a16) {
     // weight-only W4A16: BF16 activations, NVFP4 weights decoded to BF16, h rounded to BF16
 #define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K, KB)                                               \
-  k_skinny<true, G, KB, BSM_SKINNY_NT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, \
+  k_skinny<true, G, KB, BSM_SKINNY_NT, true, BSM_SKINNY_DEPTH><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, \
                                                                    tiles, ntiles, K, a.H, a.I, OUT, h_amax);   \
   if (many) (BSM_PREFILL_BIG ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(        \
       A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,                                                  \
@@ -1465,10 +1491,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
       // few-row experts: E4M3 decoded to FP16 next to the weight stream; many-row experts: FP8 matrix cores
       const float* hsc = reinterpret_cast<const float*>(h_scales);
       if (a.I % (4 * BSM_FP8_KB) == 0)
-        k_skinny<false, false, BSM_FP8_KB, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(
+        k_skinny<false, false, BSM_FP8_KB, BSM_SKINNY_NT, false, BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(
             hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
       else
-        k_skinny<false, false, 32, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(
+        k_skinny<false, false, 32, BSM_SKINNY_NT, false, BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(
             hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
       if (many)
         k_gemm_f8_down<<<dim3((unsigned)(a.H / kGBN), (unsigned)L.max_tiles_w), 256, 0, st>>>(
