@@ -12,19 +12,24 @@
 // exactly rounded binary32 value of the exact dot product, and a score the
 // exactly rounded binary32 value of 1/(1+exp(-l)):
 //
-//   k_rowstats    per row of x and w: an upper bound of the 2-norm and the
-//                 lowest set-bit exponent over the row's nonzero entries
 //   k_logits_rb   small batches: 4 tokens x 8 experts per workgroup over the
-//   / k_logits    whole row (lanes own K slices) / large batches: 64x64
-//                 double-buffered LDS tiles, 8x4 logits per thread.  Binary64 FMA accumulation of products that are
-//                 exact in binary64; the epilogue proves the binary32
-//                 rounding of each logit (exact sum, or error bound away from
-//                 every rounding boundary) and marks the rest with NaN
-//   k_select      one workgroup per token: exact recomputation of marked
-//                 logits (fixed-point window / superaccumulator, rounded
-//                 once), certified binary64 sigmoid (double-double fallback),
-//                 group top-2 sums, group selection, iterative 64-bit
-//                 (score, index) argmax, normalization.
+//                 whole row (lanes own K slices); binary64 FMA accumulation of
+//                 products that are exact in binary64, and binary64 sums of
+//                 squares of the workgroup's rows (an upper bound of each
+//                 2-norm).  The epilogue proves the binary32 rounding of each
+//                 logit by an error bound away from every rounding boundary;
+//                 for the rest, by exactness (lowest set bits of its two
+//                 rows); failing both, the workgroup recomputes it
+//                 exactly (fixed-point window / superaccumulator, rounded once)
+//   k_rowstats    large batches: per row of x and w, an upper bound of the
+//                 2-norm and the lowest set-bit exponent of its nonzero entries
+//   k_logits      large batches: 64x64 double-buffered LDS tiles, 8x4 logits
+//                 per thread; the epilogue tries exactness first, then the
+//                 error bound, then recomputes the rest exactly
+//   k_select      one workgroup per token: certified binary64 sigmoid
+//                 (double-double fallback), group top-2 sums, group
+//                 selection, iterative 64-bit (score, index) argmax,
+//                 normalization.
 
 #include "bsm_internal.h"
 
@@ -39,9 +44,10 @@ constexpr int kRbE = 8;    // experts per workgroup of the small-batch logits ke
 constexpr int kRbK = 2048; // K covered by one pass of a small-batch workgroup (256 lanes x 8)
 
 struct RouteWs {
-  size_t norm, lsb, logits, diag, total;
-  bool rb;   // small-batch kernel (full K per workgroup, lanes own K slices)
-  int nadd;  // roundings along the longest summation path of one logit
+  size_t norm, lsb, logits, blk, diag, total;  // norm, lsb: tiled path only
+  bool rb;    // small-batch kernel (full K per workgroup, lanes own K slices)
+  int nadd;   // roundings along the longest summation path of one logit
+  int64_t nblk;  // logits workgroups (one exact-recomputation count each)
 };
 
 RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
@@ -51,13 +57,16 @@ RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
   // small batch: one FMA chain of 8 per pass, 6 shuffle levels, 3 cross-wave adds;
   // tiled: an FMA chain of kBK per LDS step, added to the running sum
   L.nadd = L.rb ? (int)(((H + kRbK - 1) / kRbK) * 8 + 9) : (int)(kBK + (H + kBK - 1) / kBK + 1);
+  L.nblk = L.rb ? ((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE) : tiles;
   size_t o = 0;
   L.norm = o;
-  o += align256(sizeof(double) * (size_t)(T + E));
+  if (!L.rb) o += align256(sizeof(double) * (size_t)(T + E));
   L.lsb = o;
-  o += align256(sizeof(int) * (size_t)(T + E));
+  if (!L.rb) o += align256(sizeof(int) * (size_t)(T + E));
   L.logits = o;
   o += align256(sizeof(float) * (size_t)T * (size_t)E);
+  L.blk = o;
+  o += align256(sizeof(int) * (size_t)(L.nblk > 0 ? L.nblk : 1));
   L.diag = o;
   o += align256(sizeof(int) * 4);
   L.total = o;
@@ -86,61 +95,6 @@ __device__ inline void ld8(const void* p, int64_t i, float* v) {
     const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i + 4);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-}
-
-// Per row of x (rows 0..T-1) and of w (rows T..T+E-1), one wave per row: an
-// upper bound of the 2-norm and the lowest set-bit exponent of the row's
-// nonzero entries.
-template <bool XB, bool WB, bool VEC>
-__global__ __launch_bounds__(256) void k_rowstats(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
-                                                  int64_t E, int64_t H, double* __restrict__ norm,
-                                                  int* __restrict__ lsb, int* __restrict__ diag) {
-  const int lane = threadIdx.x & 63;
-  if (blockIdx.x == 0 && threadIdx.x < 4) diag[threadIdx.x] = 0;  // route diagnostics of this call
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= T + E) return;
-  const bool isx = r < T;
-  const void* p = isx ? x : w;
-  const int64_t row = isx ? r : r - T;
-  double ss = 0.0;
-  int lmin = 0x7FFFFFFF;
-  if (VEC) {
-    for (int64_t k = (int64_t)lane * 8; k < H; k += 512) {
-      float v[8];
-      if (isx) ld8<XB>(p, row * H + k, v);
-      else ld8<WB>(p, row * H + k, v);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const double d = (double)v[q];
-        ss = fma(d, d, ss);
-        if (v[q] != 0.0f) {
-          const int l = f32_lsb_exp(v[q]);
-          lmin = l < lmin ? l : lmin;
-        }
-      }
-    }
-  } else {
-    for (int64_t k = lane; k < H; k += 64) {
-      const float v = isx ? ld1<XB>(p, row * H + k) : ld1<WB>(p, row * H + k);
-      const double d = (double)v;
-      ss = fma(d, d, ss);
-      if (v != 0.0f) {
-        const int l = f32_lsb_exp(v);
-        lmin = l < lmin ? l : lmin;
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    ss += __shfl_xor(ss, o, 64);
-    const int ol = __shfl_xor(lmin, o, 64);
-    lmin = ol < lmin ? ol : lmin;
-  }
-  if (lane == 0) {
-    // relative error of the sum of squares is below (H + 8) * 2^-53; inflate generously
-    norm[r] = sqrt(ss * (1.0 + 0x1p-30)) * (1.0 + 0x1p-40);
-    lsb[r] = lmin;
   }
 }
 
@@ -210,22 +164,99 @@ __device__ float exact_logit_wg(const void* __restrict__ x, const void* __restri
   return r;
 }
 
-// Binary32 rounding of a binary64 dot-product estimate S, when it can be
-// proven: (a) exact -- every partial sum is a multiple of 2^L (L = lsb(x) +
-// lsb(w)) below |x|_2 |w|_2 < 2^(L+53), so no addition rounded; or (b)
-// certified -- the error bound (nadd + 4) * 2^-53 * |x|_2 |w|_2 keeps S away
-// from every binary32 rounding boundary.  Otherwise NaN marks the logit for an
-// exact recomputation.
-__device__ inline float certify_logit(double S, double nx, double nw, int lx, int lw, int nadd) {
-  const double A = nx * nw * (1.0 + 0x1p-40);  // >= sum |x_k w_k|
+// Upper bound of a row's 2-norm from its binary64 sum of squares: along any
+// summation chain of n <= 2^22 terms the relative error of the sum is below
+// (n + 8) * 2^-53; the inflation is generous.
+__device__ inline double norm_bound(double ss) { return sqrt(ss * (1.0 + 0x1p-30)) * (1.0 + 0x1p-40); }
+
+// A >= sum_k |x_k w_k| from the two rows' norm bounds.
+__device__ inline double abs_bound(double nx, double nw) { return nx * nw * (1.0 + 0x1p-40); }
+
+// Binary32 rounding of a binary64 dot-product estimate S.  (b) certified: the
+// error bound (nadd + 4) * 2^-53 * A keeps S away from every binary32 rounding
+// boundary; NaN when it does not.  A zero bound means every product is zero.
+__device__ inline float certify_bound(double S, double A, int nadd) {
   if (A == 0.0) return 0.0f;
-  if (lx != 0x7FFFFFFF && lw != 0x7FFFFFFF) {
-    const int L = lx + lw;
-    if (L + 53 > -1000 && A < ldexp(1.0, L + 53)) return (float)S;
-  }
   float r;
   if (f32_certified(S, (double)(nadd + 4) * 0x1p-53 * A * 1.0001, &r)) return r;
   return __builtin_nanf("");
+}
+
+// (a) exact: every product is a multiple of 2^L (L = lsb(x) + lsb(w)) and
+// every partial sum lies below A < 2^(L+53) in magnitude, so no addition
+// rounded and S is the exact sum.
+__device__ inline bool certify_exact(double S, double A, int lx, int lw, float* r) {
+  if (lx == 0x7FFFFFFF || lw == 0x7FFFFFFF) return false;
+  const int L = lx + lw;
+  if (L + 53 > -1000 && A < ldexp(1.0, L + 53)) {
+    *r = (float)S;
+    return true;
+  }
+  return false;
+}
+
+// Large batches: per row of x (rows 0..T-1) and of w (rows T..T+E-1), one
+// wave per row: an upper bound of the 2-norm and the lowest set-bit exponent
+// of the row's nonzero entries, read by the tiled logits kernel.
+template <bool XB, bool WB, bool VEC>
+__global__ __launch_bounds__(256) void k_rowstats(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
+                                                  int64_t E, int64_t H, double* __restrict__ norm,
+                                                  int* __restrict__ lsb) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= T + E) return;
+  const bool isx = r < T;
+  const void* p = isx ? x : w;
+  const int64_t row = isx ? r : r - T;
+  double ss = 0.0;
+  int lmin = 0x7FFFFFFF;
+  if (VEC) {
+    for (int64_t k = (int64_t)lane * 8; k < H; k += 512) {
+      float v[8];
+      if (isx) ld8<XB>(p, row * H + k, v);
+      else ld8<WB>(p, row * H + k, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const double d = (double)v[q];
+        ss = fma(d, d, ss);
+        if (v[q] != 0.0f) {
+          const int l = f32_lsb_exp(v[q]);
+          lmin = l < lmin ? l : lmin;
+        }
+      }
+    }
+  } else {
+    for (int64_t k = lane; k < H; k += 64) {
+      const float v = isx ? ld1<XB>(p, row * H + k) : ld1<WB>(p, row * H + k);
+      const double d = (double)v;
+      ss = fma(d, d, ss);
+      if (v != 0.0f) {
+        const int l = f32_lsb_exp(v);
+        lmin = l < lmin ? l : lmin;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ss += __shfl_xor(ss, o, 64);
+    const int ol = __shfl_xor(lmin, o, 64);
+    lmin = ol < lmin ? ol : lmin;
+  }
+  if (lane == 0) {
+    // relative error of the sum of squares is below (H + 8) * 2^-53; inflate generously
+    norm[r] = norm_bound(ss);
+    lsb[r] = lmin;
+  }
+}
+
+// Both tests with precomputed row statistics (norm bounds and lowest set bits):
+// exactness first, then the error bound; NaN when neither proves the rounding.
+__device__ inline float certify_logit(double S, double nx, double nw, int lx, int lw, int nadd) {
+  const double A = abs_bound(nx, nw);
+  if (A == 0.0) return 0.0f;
+  float r;
+  if (certify_exact(S, A, lx, lw, &r)) return r;
+  return certify_bound(S, A, nadd);
 }
 
 // Small batches: a workgroup owns kRbT tokens x kRbE experts over the whole
@@ -236,16 +267,20 @@ __device__ inline float certify_logit(double S, double nx, double nw, int lx, in
 // holds all of x and one eighth of w.
 template <bool XB, bool WB>
 __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
-                                                   int64_t E, int64_t H, const double* __restrict__ norm,
-                                                   const int* __restrict__ lsb, int nadd, float* __restrict__ logits,
-                                                   int* __restrict__ diag) {
+                                                   int64_t E, int64_t H, int nadd, float* __restrict__ logits,
+                                                   int* __restrict__ blk, int* __restrict__ diag) {
   constexpr int TT = kRbT, TE = kRbE, NV = TT * TE;
   static_assert(NV == 32, "reduce-scatter below assumes 32 outputs per workgroup");
   __shared__ double s_red[4][NV];
+  __shared__ double s_ss[4][TT + TE];  // per wave: sums of squares of the TT x rows and TE w rows
+  __shared__ double s_n[TT + TE];      // norm bounds of those rows
   __shared__ int unc[NV];
+  __shared__ double uS[NV];
+  __shared__ int s_lo[4][2];  // per wave: lowest set-bit exponents of one x row and one w row
   __shared__ int n_unc;
   __shared__ ExactLds xl;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (blockIdx.x == 0 && tid >= 1 && tid < 4) diag[tid] = 0;  // counters of the selection kernel that follows
   const int64_t nte = (E + TE - 1) / TE;
   const int64_t b = blockIdx.x;
   int64_t te, tt;
@@ -258,11 +293,15 @@ __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, c
     tt = b / nte;
   }
   const int64_t t0 = tt * TT, e0 = te * TE;
-  double acc[TT][TE];
+  double acc[TT][TE], ssx[TT], ssw[TE];
 #pragma unroll
-  for (int i = 0; i < TT; ++i)
+  for (int i = 0; i < TT; ++i) {
+    ssx[i] = 0.0;
 #pragma unroll
     for (int j = 0; j < TE; ++j) acc[i][j] = 0.0;
+  }
+#pragma unroll
+  for (int j = 0; j < TE; ++j) ssw[j] = 0.0;
   // raw 8-value slices of the TT x rows and TE w rows; the next pass's slices
   // are loaded before the current pass is multiplied
   constexpr int XW = XB ? 4 : 8, WW = WB ? 4 : 8;  // dwords per 8-value slice
@@ -301,10 +340,14 @@ __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, c
     for (int q = 0; q < 8; ++q) {
       double wd[TE];
 #pragma unroll
-      for (int j = 0; j < TE; ++j) wd[j] = val(wr[j], q, WB);
+      for (int j = 0; j < TE; ++j) {
+        wd[j] = val(wr[j], q, WB);
+        ssw[j] = fma(wd[j], wd[j], ssw[j]);
+      }
 #pragma unroll
       for (int i = 0; i < TT; ++i) {
         const double xd = val(xr[i], q, XB);
+        ssx[i] = fma(xd, xd, ssx[i]);
 #pragma unroll
         for (int j = 0; j < TE; ++j) acc[i][j] = fma(xd, wd[j], acc[i][j]);
       }
@@ -340,25 +383,77 @@ __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, c
   }
   v[0] += __shfl_xor(v[0], 1, 64);
   if ((lane & 1) == 0) s_red[wv][lane >> 1] = v[0];
+  // sums of squares: butterfly over the wave, then the four waves in a fixed order
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+    for (int i = 0; i < TT; ++i) ssx[i] += __shfl_xor(ssx[i], o, 64);
+#pragma unroll
+    for (int j = 0; j < TE; ++j) ssw[j] += __shfl_xor(ssw[j], o, 64);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < TT; ++i) s_ss[wv][i] = ssx[i];
+#pragma unroll
+    for (int j = 0; j < TE; ++j) s_ss[wv][TT + j] = ssw[j];
+  }
   if (tid == 0) n_unc = 0;
+  __syncthreads();
+  if (tid < TT + TE) s_n[tid] = norm_bound(((s_ss[0][tid] + s_ss[1][tid]) + s_ss[2][tid]) + s_ss[3][tid]);
   __syncthreads();
   if (tid < NV) {
     const double S = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
     const int64_t t = t0 + tid / TE, e = e0 + tid % TE;
     if (t < T && e < E) {
-      const float r = certify_logit(S, norm[t], norm[T + e], lsb[t], lsb[T + e], nadd);
+      const float r = certify_bound(S, abs_bound(s_n[tid / TE], s_n[TT + tid % TE]), nadd);
       logits[t * E + e] = r;
-      if (r != r) unc[atomicAdd(&n_unc, 1)] = tid;
+      if (r != r) {
+        const int u = atomicAdd(&n_unc, 1);
+        unc[u] = tid;
+        uS[u] = S;
+      }
     }
   }
   __syncthreads();
   const int nu = n_unc;
-  if (nu && tid == 0) atomicAdd(&diag[0], nu);
+  int nexact = 0;
   for (int u = 0; u < nu; ++u) {
-    const int64_t t = t0 + unc[u] / TE, e = e0 + unc[u] % TE;
-    const float r = exact_logit_wg<XB, WB, 256>(x, w, t, e, H, norm[t] * norm[T + e] * (1.0 + 0x1p-40), &xl);
+    // exactness test: lowest set-bit exponents of the two rows (8-value loads; H % 8 == 0 on this path)
+    const int i = unc[u] / TE, j = unc[u] % TE;
+    const int64_t t = t0 + i, e = e0 + j;
+    int a = 0x7FFFFFFF, c = 0x7FFFFFFF;
+    for (int64_t k = (int64_t)tid * 8; k < H; k += 256 * 8) {
+      float xv[8], wv[8];
+      ld8<XB>(x, t * H + k, xv);
+      ld8<WB>(w, e * H + k, wv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (xv[q] != 0.0f) a = min(a, f32_lsb_exp(xv[q]));
+        if (wv[q] != 0.0f) c = min(c, f32_lsb_exp(wv[q]));
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      a = min(a, __shfl_xor(a, o, 64));
+      c = min(c, __shfl_xor(c, o, 64));
+    }
+    if (lane == 0) {
+      s_lo[wv][0] = a;
+      s_lo[wv][1] = c;
+    }
+    __syncthreads();
+    const int lx = min(min(s_lo[0][0], s_lo[1][0]), min(s_lo[2][0], s_lo[3][0]));
+    const int lw = min(min(s_lo[0][1], s_lo[1][1]), min(s_lo[2][1], s_lo[3][1]));
+    __syncthreads();
+    const double A = abs_bound(s_n[i], s_n[TT + j]);
+    float r;
+    if (!certify_exact(uS[u], A, lx, lw, &r)) {  // uniform across the workgroup
+      r = exact_logit_wg<XB, WB, 256>(x, w, t, e, H, A, &xl);
+      ++nexact;
+    }
     if (tid == 0) logits[t * E + e] = r;
   }
+  if (tid == 0) blk[blockIdx.x] = nexact;
 }
 
 // Large batches: 64x64 token x expert tiles staged through LDS, 4x4 outputs
@@ -374,13 +469,14 @@ template <bool XB, bool WB, bool VEC>
 __global__ __launch_bounds__(128) void k_logits(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
                                                 int64_t E, int64_t H, const double* __restrict__ norm,
                                                 const int* __restrict__ lsb, int nadd, float* __restrict__ logits,
-                                                int* __restrict__ diag) {
+                                                int* __restrict__ blk, int* __restrict__ diag) {
   __shared__ __attribute__((aligned(16))) double tl[2][2][kBK][kTile];  // [buffer][x, w][k][row]
   __shared__ int n_unc;
   __shared__ ExactLds xl;
   int* unc = reinterpret_cast<int*>(&tl[0][0][0][0]);  // after the main loop: the tile's uncertain logits
   static_assert(sizeof(tl) >= sizeof(int) * kTile * kTile, "uncertain-logit list fits the staging buffers");
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid >= 1 && tid < 4) diag[tid] = 0;  // selection-kernel counters
   const int tx = tid & 15, ty = tid >> 4;  // experts {2tx, 2tx+1, 32+2tx, 33+2tx}; tokens {4ty+i, 32+4ty+i}
   const int64_t t0 = (int64_t)blockIdx.x * kTile, e0 = (int64_t)blockIdx.y * kTile;
   // staging: row sr of the x and w tiles, k values 16 sh .. +15 of the step.  Rows past T or E
@@ -472,12 +568,12 @@ __global__ __launch_bounds__(128) void k_logits(const void* __restrict__ x, cons
   }
   __syncthreads();
   const int nu = n_unc;
-  if (nu && tid == 0) atomicAdd(&diag[0], nu);
   for (int u = 0; u < nu; ++u) {
     const int64_t t = t0 + unc[u] / kTile, e = e0 + unc[u] % kTile;
-    const float r = exact_logit_wg<XB, WB, 128>(x, w, t, e, H, norm[t] * norm[T + e] * (1.0 + 0x1p-40), &xl);
+    const float r = exact_logit_wg<XB, WB, 128>(x, w, t, e, H, abs_bound(norm[t], norm[T + e]), &xl);
     if (tid == 0) logits[t * E + e] = r;
   }
+  if (tid == 0) blk[blockIdx.y * gridDim.x + blockIdx.x] = nu;
 }
 
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
@@ -500,13 +596,24 @@ constexpr int kSelThreads = 256;
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ logits, int64_t E, int n_group,
                                                         int topk_group, int topk, int32_t* __restrict__ ids,
                                                         float* __restrict__ wts, float* __restrict__ scores,
+                                                        const int* __restrict__ blk, int64_t nblk,
                                                         int* __restrict__ diag) {
   __shared__ float s_lds[kMaxE];
   __shared__ unsigned long long keys[kMaxE];
   __shared__ float g_lds[64];
   __shared__ int kept[64];
+  __shared__ int s_cnt;
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
+  if (t == 0) {  // diagnostics: exact recomputations of all logits workgroups
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    int c = 0;
+    for (int64_t i = tid; i < nblk; i += kSelThreads) c += blk[i];
+    if (c) atomicAdd(&s_cnt, c);
+    __syncthreads();
+    if (tid == 0) diag[0] = s_cnt;
+  }
   int nslow = 0;
   for (int64_t e = tid; e < E; e += kSelThreads) {
     bool fast;
@@ -584,29 +691,33 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
                         int topk_group, int topk, int32_t* ids, float* wts, float* scores, void* ws_, hipStream_t st) {
   const RouteWs L = route_layout(T, H, E);
   uint8_t* ws = reinterpret_cast<uint8_t*>(ws_);
-  double* norm = reinterpret_cast<double*>(ws + L.norm);
-  int* lsb = reinterpret_cast<int*>(ws + L.lsb);
   float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int* blk = reinterpret_cast<int*>(ws + L.blk);
   int* diag = reinterpret_cast<int*>(ws + L.diag);
+  double* norm = L.rb ? nullptr : reinterpret_cast<double*>(ws + L.norm);
+  int* lsb = L.rb ? nullptr : reinterpret_cast<int*>(ws + L.lsb);
   if (T == 0) return hipSuccess;
   stage_mark(1, 0, st);
   const unsigned nrs = (unsigned)((T + E + 3) / 4);
+  const bool vec = (H % 8) == 0;
   const unsigned nrb = (unsigned)(((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE));
   dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
-  const bool vec = (H % 8) == 0;
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
-  if (vec)                                                                                                 \
-    k_rowstats<XB, WB, true><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb, diag);                               \
-  else                                                                                                     \
-    k_rowstats<XB, WB, false><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb, diag);                              \
-  if (L.rb)                                                                                                \
-    k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, diag);                    \
-  else if (H % kBK == 0)                                                                                   \
-    k_logits<XB, WB, true><<<gl, 128, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, diag);                  \
-  else                                                                                                     \
-    k_logits<XB, WB, false><<<gl, 128, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, diag);                 \
+  if (L.rb) {                                                                                              \
+    k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, L.nadd, logits, blk, diag);                    \
+  } else {                                                                                                 \
+    if (vec)                                                                                               \
+      k_rowstats<XB, WB, true><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                             \
+    else                                                                                                   \
+      k_rowstats<XB, WB, false><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                            \
+    if (H % kBK == 0)                                                                                      \
+      k_logits<XB, WB, true><<<gl, 128, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, blk, diag);     \
+    else                                                                                                   \
+      k_logits<XB, WB, false><<<gl, 128, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, blk, diag);    \
+  }                                                                                                        \
   stage_mark(1, 1, st);                                                                                    \
-  k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, diag);
+  k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, blk,    \
+                                                L.nblk, diag);
   if (xb && wb) {
     BSM_ROUTE_DISPATCH(true, true)
   } else if (xb && !wb) {
