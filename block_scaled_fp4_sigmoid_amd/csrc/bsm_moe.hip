@@ -785,8 +785,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
                                                      int64_t K, int64_t H, int64_t I, float* __restrict__ out,
                                                      uint32_t* __restrict__ h_amax) {
   constexpr int kBRow = BigB<NV>::kRow;
+  // NVFP4 weights come in groups of 4 K steps: 128 code bytes per row (one cache line, loaded by 8
+  // lanes) into one LDS buffer that the group's 4 steps read (K % 256 == 0); FP8 weights per step,
+  // double buffered
+  constexpr int kGP = 132;  // LDS bytes per weight row of a group (+4 pad: conflict-free dword reads)
   __shared__ __attribute__((aligned(16))) _Float16 As[2][kGBM][kGBK + 8];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGBN][kBRow];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[NV ? 1 : 2][NV ? 1 : kGBN][kBRow];
+  __shared__ __attribute__((aligned(16))) uint8_t Bg[NV ? kGBN : 1][kGP];
   __shared__ uint32_t Bsc[2][kGBN];
   if ((int)blockIdx.y >= *ntiles) return;
   const int4 ti = tiles[blockIdx.y];
@@ -798,8 +803,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   // lanes (8 lanes per 128-byte activation row segment, 2 (FP8: 4) lanes per
   // weight row segment), so one instruction touches few cache lines.
   // Activation rows ar(i) = 32 i + tid / 8, 16-byte part tid % 8.
-  constexpr int kBI = NV ? 2 : 4;  // weight rows per thread: kGBN / (256 / (16-byte parts per row))
-  constexpr int kBP = NV ? 2 : 4;  // 16-byte parts per weight row and K step
+  constexpr int kBI = NV ? 8 : 4;  // weight rows per thread: kGBN / (256 / (16-byte parts per row))
+  constexpr int kBP = NV ? 8 : 4;  // 16-byte parts per weight row and load (NVFP4: a group of 4 K steps)
   const int apart = tid & 7, bpart = tid & (kBP - 1);
   auto arow = [&](int i) -> const _Float16* {
     const int r = 32 * i + (tid >> 3);
@@ -818,54 +823,46 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   auto boff_of = [&](int i) -> uint32_t {
     return (uint32_t)((wrow_of((256 / kBP) * i + tid / kBP) - wrow_of(0)) * cbytes);
   };
-  const uint32_t bo0 = boff_of(0), bo1 = boff_of(1), bo2 = kBI > 2 ? boff_of(2) : 0u, bo3 = kBI > 2 ? boff_of(3) : 0u;
-  // scale bytes: thread tid holds weight row tid; 16 bytes (4 K steps) per load when rows are 16-byte aligned
+  uint32_t bo[kBI];
+#pragma unroll
+  for (int i = 0; i < kBI; ++i) bo[i] = boff_of(i);
+  // scale bytes: thread tid holds weight row tid; 16 bytes (the 4 K steps of a group) per load
   const uint8_t* ssrc = NV ? wsc + wrow_of(tid) * (K / 16) : nullptr;
-  const bool s4 = (K % 256) == 0;
 
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3, sc4 = make_uint4(0, 0, 0, 0);
-  uint32_t rs1 = 0;
-  auto gload = [&](int s) {  // global loads of K step s into registers
+  uint4 ra0, ra1, ra2, ra3, rb[kBI], sc4 = make_uint4(0, 0, 0, 0);
+  auto gload = [&](int s) {  // global loads of K step s into registers (NVFP4 weights: whole groups)
     ra0 = *reinterpret_cast<const uint4*>(as0 + s * kGBK);
     ra1 = *reinterpret_cast<const uint4*>(as1 + s * kGBK);
     ra2 = *reinterpret_cast<const uint4*>(as2 + s * kGBK);
     ra3 = *reinterpret_cast<const uint4*>(as3 + s * kGBK);
-    const uint8_t* bs = bbase + s * (NV ? kGBK / 2 : kGBK);
-    rb0 = *reinterpret_cast<const uint4*>(bs + bo0);
-    rb1 = *reinterpret_cast<const uint4*>(bs + bo1);
-    if constexpr (kBI > 2) {
-      rb2 = *reinterpret_cast<const uint4*>(bs + bo2);
-      rb3 = *reinterpret_cast<const uint4*>(bs + bo3);
-    }
-    if constexpr (NV) {
-      if (s4) {
-        if ((s & 3) == 0) sc4 = *reinterpret_cast<const uint4*>(ssrc + 4 * s);
-      } else {
-        rs1 = *reinterpret_cast<const uint32_t*>(ssrc + 4 * s);
-      }
+    if (!NV || (s & 3) == 0) {
+      const uint8_t* bs = bbase + s * (NV ? kGBK / 2 : kGBK);
+#pragma unroll
+      for (int i = 0; i < kBI; ++i) rb[i] = *reinterpret_cast<const uint4*>(bs + bo[i]);
+      if constexpr (NV) sc4 = *reinterpret_cast<const uint4*>(ssrc + 4 * s);
     }
   };
-  auto lstore = [&](int buf, int s) {  // registers of K step s into LDS buffer buf
+  auto bstore = [&](int buf) {  // weight registers into LDS (NVFP4: the group buffer)
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) {
+      uint32_t* d = reinterpret_cast<uint32_t*>(NV ? &Bg[(256 / kBP) * i + tid / kBP][16 * bpart]
+                                                   : &Bs[buf][(256 / kBP) * i + tid / kBP][16 * bpart]);
+      d[0] = rb[i].x;
+      d[1] = rb[i].y;
+      d[2] = rb[i].z;
+      d[3] = rb[i].w;
+    }
+  };
+  auto lstore = [&](int buf, int s) {  // activation registers (and the step's scale dword) of K step s
     *reinterpret_cast<uint4*>(&As[buf][(tid >> 3)][8 * apart]) = ra0;
     *reinterpret_cast<uint4*>(&As[buf][32 + (tid >> 3)][8 * apart]) = ra1;
     *reinterpret_cast<uint4*>(&As[buf][64 + (tid >> 3)][8 * apart]) = ra2;
     *reinterpret_cast<uint4*>(&As[buf][96 + (tid >> 3)][8 * apart]) = ra3;
-    auto bst = [&](int i, uint4 v) {
-      uint32_t* d = reinterpret_cast<uint32_t*>(&Bs[buf][(256 / kBP) * i + tid / kBP][16 * bpart]);
-      d[0] = v.x;
-      d[1] = v.y;
-      d[2] = v.z;
-      d[3] = v.w;
-    };
-    bst(0, rb0);
-    bst(1, rb1);
-    if constexpr (kBI > 2) {
-      bst(2, rb2);
-      bst(3, rb3);
-    }
     if constexpr (NV) {
       const int j = s & 3;
-      Bsc[buf][tid] = !s4 ? rs1 : j == 0 ? sc4.x : j == 1 ? sc4.y : j == 2 ? sc4.z : sc4.w;
+      Bsc[buf][tid] = j == 0 ? sc4.x : j == 1 ? sc4.y : j == 2 ? sc4.z : sc4.w;
+    } else {
+      bstore(buf);
     }
   };
   // LDS weight row of this wave's N tile t: GEMM1 gate tile 0 / up tile 1; GEMM2 2 consecutive
@@ -881,6 +878,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
 
   const int nk = (int)(K / kGBK);
   gload(0);
+  if constexpr (NV) bstore(0);
   lstore(0, 0);
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
@@ -897,7 +895,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
         const int brow = BSM_BIG_BROW(t) + l32;
         h8v b;
         if constexpr (NV) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(&Bs[buf][brow][k16 * 8 + lh * 4]);
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(&Bg[brow][(ks & 3) * 32 + k16 * 8 + lh * 4]);
           const h2v s2 = scale_pair_sel(Bsc[buf][brow], (uint32_t)k16 * 0x0101u);
           if constexpr (A16)
             b = dec_fp4x8_bf16(w, (float)s2[0]);
@@ -911,7 +909,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
         for (int mt = 0; mt < 4; ++mt) acc[mt][t] = mfma32<A16>(a[mt], b, acc[mt][t]);
       }
     }
-    if (ks + 1 < nk) lstore(buf ^ 1, ks + 1);
+    if (ks + 1 < nk) {
+      if constexpr (NV) {
+        if (((ks + 1) & 3) == 0) {  // next group: every wave has finished reading the current one
+          __syncthreads();
+          bstore(0);
+        }
+      }
+      lstore(buf ^ 1, ks + 1);
+    }
     __syncthreads();
   }
 #undef BSM_BIG_BROW
@@ -1392,8 +1398,11 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   // expert exceeds kSkinnyMaxRows rows and the many-row kernels have no tiles: they are not launched.
   static_assert(kChunk <= kSkinnyMaxRows, "a single chunk never yields a many-row expert");
   const bool many = L.n_chunks > 1;
+  // the NVFP4 many-row kernel reads weights in groups of 4 K steps (K % 256 == 0): always for the gate/up
+  // projection (H % 256 == 0), for the down projection when I % 256 == 0 (else the 16x16x32 kernel)
+  const bool big_dn = BSM_PREFILL_BIG && a.I % 256 == 0;
   const dim3 w1((unsigned)(a.I / (BSM_PREFILL_BIG ? kGBN / 2 : 64)), (unsigned)L.max_tiles_w);
-  const dim3 w2((unsigned)(a.H / (BSM_PREFILL_BIG ? kGBN : 128)), (unsigned)L.max_tiles_w);
+  const dim3 w2((unsigned)(a.H / (big_dn ? kGBN : 128)), (unsigned)L.max_tiles_w);
   _Float16* act = reinterpret_cast<_Float16*>(ws + L.act_f16);
   _Float16* hdec = reinterpret_cast<_Float16*>(ws + L.h_f16);
   const int64_t xblk = a.T * a.H / 16;
@@ -1418,7 +1427,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #define BSM_G2(NV, KB)                                                                                         \
   k_skinny<NV, false, KB, BSM_SKINNY_NT, false, NV ? BSM_SKINNY_DEPTH : BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
                                               a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
-  if (many) (BSM_PREFILL_BIG ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                    \
+  if (many) (big_dn ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                    \
       hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales),                                \
                                              a.w2_codes, w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
 #ifndef BSM_NV_KB
@@ -1430,7 +1439,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K, KB)                                               \
   k_skinny<true, G, KB, BSM_SKINNY_NT, true, BSM_SKINNY_DEPTH><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, \
                                                                    tiles, ntiles, K, a.H, a.I, OUT, h_amax);   \
-  if (many) (BSM_PREFILL_BIG ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(        \
+  if (many) ((G ? BSM_PREFILL_BIG : big_dn) ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(        \
       A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,                                                  \
                                                     ntiles_w, K, a.H, a.I, OUT, h_amax)
     if (a.H % (4 * BSM_NV_KB) == 0) {
