@@ -785,13 +785,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
                                                      int64_t K, int64_t H, int64_t I, float* __restrict__ out,
                                                      uint32_t* __restrict__ h_amax) {
   constexpr int kBRow = BigB<NV>::kRow;
-  // NVFP4 weights come in groups of 4 K steps: 128 code bytes per row (one cache line, loaded by 8
-  // lanes) into one LDS buffer that the group's 4 steps read (K % 256 == 0); FP8 weights per step,
-  // double buffered
-  constexpr int kGP = 132;  // LDS bytes per weight row of a group (+4 pad: conflict-free dword reads)
+  // Weights come in groups of GS K steps, 128 code bytes per row (one cache line, loaded by 8 lanes;
+  // NVFP4 4 steps with K % 256 == 0, FP8 2 steps with K % 128 == 0), into one LDS buffer that the
+  // group's steps read.  Per-step pieces of 32 or 64 bytes left the lines to be evicted between steps.
+  constexpr int GS = NV ? 4 : 2;               // K steps per weight group
+  constexpr int kSB = NV ? kGBK / 2 : kGBK;    // code bytes per row and K step
+  constexpr int kGP = NV ? 132 : 136;          // LDS bytes per weight row of a group (+pad: conflict-free reads)
+  (void)kBRow;
   __shared__ __attribute__((aligned(16))) _Float16 As[2][kGBM][kGBK + 8];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[NV ? 1 : 2][NV ? 1 : kGBN][kBRow];
-  __shared__ __attribute__((aligned(16))) uint8_t Bg[NV ? kGBN : 1][kGP];
+  __shared__ __attribute__((aligned(16))) uint8_t Bg[kGBN][kGP];
   __shared__ uint32_t Bsc[2][kGBN];
   if ((int)blockIdx.y >= *ntiles) return;
   const int4 ti = tiles[blockIdx.y];
@@ -803,8 +805,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   // lanes (8 lanes per 128-byte activation row segment, 2 (FP8: 4) lanes per
   // weight row segment), so one instruction touches few cache lines.
   // Activation rows ar(i) = 32 i + tid / 8, 16-byte part tid % 8.
-  constexpr int kBI = NV ? 8 : 4;  // weight rows per thread: kGBN / (256 / (16-byte parts per row))
-  constexpr int kBP = NV ? 8 : 4;  // 16-byte parts per weight row and load (NVFP4: a group of 4 K steps)
+  constexpr int kBI = 8;  // weight rows per thread and group: kGBN / (256 / kBP)
+  constexpr int kBP = 8;  // 16-byte parts per weight row and group
   const int apart = tid & 7, bpart = tid & (kBP - 1);
   auto arow = [&](int i) -> const _Float16* {
     const int r = 32 * i + (tid >> 3);
@@ -835,18 +837,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
     ra1 = *reinterpret_cast<const uint4*>(as1 + s * kGBK);
     ra2 = *reinterpret_cast<const uint4*>(as2 + s * kGBK);
     ra3 = *reinterpret_cast<const uint4*>(as3 + s * kGBK);
-    if (!NV || (s & 3) == 0) {
-      const uint8_t* bs = bbase + s * (NV ? kGBK / 2 : kGBK);
+    if (s % GS == 0) {
+      const uint8_t* bs = bbase + s * kSB;
 #pragma unroll
       for (int i = 0; i < kBI; ++i) rb[i] = *reinterpret_cast<const uint4*>(bs + bo[i]);
       if constexpr (NV) sc4 = *reinterpret_cast<const uint4*>(ssrc + 4 * s);
     }
   };
-  auto bstore = [&](int buf) {  // weight registers into LDS (NVFP4: the group buffer)
+  auto bstore = [&]() {  // weight registers of a group into the group buffer
 #pragma unroll
     for (int i = 0; i < kBI; ++i) {
-      uint32_t* d = reinterpret_cast<uint32_t*>(NV ? &Bg[(256 / kBP) * i + tid / kBP][16 * bpart]
-                                                   : &Bs[buf][(256 / kBP) * i + tid / kBP][16 * bpart]);
+      uint32_t* d = reinterpret_cast<uint32_t*>(&Bg[(256 / kBP) * i + tid / kBP][16 * bpart]);
       d[0] = rb[i].x;
       d[1] = rb[i].y;
       d[2] = rb[i].z;
@@ -861,8 +862,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
     if constexpr (NV) {
       const int j = s & 3;
       Bsc[buf][tid] = j == 0 ? sc4.x : j == 1 ? sc4.y : j == 2 ? sc4.z : sc4.w;
-    } else {
-      bstore(buf);
     }
   };
   // LDS weight row of this wave's N tile t: GEMM1 gate tile 0 / up tile 1; GEMM2 2 consecutive
@@ -878,7 +877,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
 
   const int nk = (int)(K / kGBK);
   gload(0);
-  if constexpr (NV) bstore(0);
+  bstore();
   lstore(0, 0);
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
@@ -902,7 +901,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
           else
             b = dec_fp4x8(w, s2);
         } else {
-          const uint2 w = *reinterpret_cast<const uint2*>(&Bs[buf][brow][k16 * 16 + lh * 8]);
+          const uint2 w = *reinterpret_cast<const uint2*>(&Bg[brow][(ks & 1) * 64 + k16 * 16 + lh * 8]);
           b = dec_fp8x8(w.x, w.y);
         }
 #pragma unroll
@@ -910,11 +909,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
       }
     }
     if (ks + 1 < nk) {
-      if constexpr (NV) {
-        if (((ks + 1) & 3) == 0) {  // next group: every wave has finished reading the current one
-          __syncthreads();
-          bstore(0);
-        }
+      if ((ks + 1) % GS == 0) {  // next group: every wave has finished reading the current one
+        __syncthreads();
+        bstore();
       }
       lstore(buf ^ 1, ks + 1);
     }
