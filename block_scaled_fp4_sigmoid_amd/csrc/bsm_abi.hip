@@ -312,7 +312,7 @@ int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w, const void* x, int64_t T,
 
 size_t bsm_fp8_linear_workspace_size(int64_t T, int64_t K, int64_t N) {
   if (T < 0 || K <= 0 || N <= 0) return 0;
-  return bsm::fp8_linear_ws(T, K);
+  return bsm::fp8_linear_ws(T, K, N);
 }
 
 int bsm_fp8_linear(const uint8_t* x_codes, const float* x_scales, const uint8_t* w_codes, const float* w_scales,
@@ -324,7 +324,7 @@ int bsm_fp8_linear(const uint8_t* x_codes, const float* x_scales, const uint8_t*
   if (!x_codes || !x_scales || !w_codes || !w_scales || !out) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
   if (!aligned(x_codes, 16) || !aligned(w_codes, 16) || !aligned(out, 16))
     return fail(BSM_ERR_INVALID_ARG, "codes and out must be 16-byte aligned");
-  if (int r = check_ws(ws, ws_bytes, bsm::fp8_linear_ws(T, K))) return r;
+  if (int r = check_ws(ws, ws_bytes, bsm::fp8_linear_ws(T, K, N))) return r;
   return hip_status(bsm::launch_fp8_linear(x_codes, x_scales, w_codes, w_scales, T, K, N, out,
                                            reinterpret_cast<uint8_t*>(ws), (hipStream_t)stream),
                     "bsm_fp8_linear");

@@ -52,7 +52,7 @@ hipError_t launch_route_diag(const void* ws, int64_t T, int64_t H, int64_t E, in
 struct MoeLayout {
   size_t total, counts, offsets, row_pair, pair_row, tiles, h_f32, h_codes, h_scales, h_gs, y_f32, scratch;
   // scratch sub-buffers
-  size_t sel_masks, chunk_cnt, chunk_base, ntiles, h_amax, act_f16, h_f16, tiles_w, ntiles_w;
+  size_t sel_masks, chunk_cnt, chunk_base, ntiles, h_amax, act_f16, h_f16, tiles_w, ntiles_w, part;
   int64_t P, n_chunks, max_tiles, max_tiles_w;
 };
 MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int topk);
@@ -82,7 +82,7 @@ struct MoeArgs {
 hipError_t launch_moe(const MoeArgs& a, hipStream_t st);
 
 // ---- dense FP8 linear ------------------------------------------------------
-size_t fp8_linear_ws(int64_t T, int64_t K);
+size_t fp8_linear_ws(int64_t T, int64_t K, int64_t N);
 hipError_t launch_fp8_linear(const uint8_t* xc, const float* xs, const uint8_t* wc, const float* wsc, int64_t T,
                              int64_t K, int64_t N, float* out, uint8_t* ws, hipStream_t st);
 

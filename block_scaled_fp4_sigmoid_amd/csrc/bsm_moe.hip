@@ -560,6 +560,200 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny(const _Float
 }
 
 // ---------------------------------------------------------------------------
+// Dense FP8 GEMM for at most 64 rows (decode-sized dense projections and the
+// dense SwiGLU MLP, one weight matrix): every workgroup covers all rows, so
+// each weight byte is streamed from HBM once (the 16-row tiles of k_skinny
+// would stream it once per tile).  The weights stream HBM -> registers as in
+// k_skinny (lane g of a row holds the 16-byte pieces i*64 + g*16 of the
+// row's super-step span), decoded once per workgroup and fed to up to 4
+// row-tile MFMAs; the rows' E4M3 codes of a super-step are decoded to FP16
+// once, into LDS.  Narrow outputs split K over gridDim.z (fixed ranges of
+// super-steps); the partial sums go to a workspace and k_dense_reduce adds
+// them in split order and applies the scales (and SwiGLU).
+// ---------------------------------------------------------------------------
+constexpr int kDenseRows = 64;
+
+template <bool G1, int KB>
+__global__ __launch_bounds__(256, 2) void k_dense_f8(const uint8_t* __restrict__ xc, const float* __restrict__ xs,
+                                                     int64_t T, int64_t K, const uint8_t* __restrict__ wc,
+                                                     const float* __restrict__ wsc, int64_t N, int64_t I,
+                                                     float* __restrict__ out, float* __restrict__ part) {
+  constexpr int NT = 2;              // 16-row weight tiles per wave (GEMM1: one gate, one up)
+  constexpr int KS = 4 * KB;         // k per super-step
+  constexpr int kAs = KS + 8;        // LDS row stride (f16), +8 pad
+  constexpr int VPU = 16, SPU = 2;   // FP8 values per uint4 of codes; MFMA steps per uint4
+  constexpr int kAq = KS / 4 / 16;   // uint4 of codes staged per thread (4 threads per row)
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][kDenseRows][kAs];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, g = lane >> 4;
+  const int nrt = (int)((T + 15) / 16);
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * (G1 ? 8 * NT : 16 * NT);
+  const uint8_t* crow[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int64_t r = G1 ? (j == 1 ? I : 0) + n0 + m : n0 + 16 * j + m;
+    crow[j] = wc + r * K + 16 * g;
+  }
+  const int nss = (int)(K / KS), nsplit = (int)gridDim.z, sp = (int)blockIdx.z;
+  const int ss0 = (int)((int64_t)sp * nss / nsplit), ss1 = (int)((int64_t)(sp + 1) * nss / nsplit);
+  // activation staging: row sr, quarter sq of the super-step (only the T real rows)
+  const int sr = tid >> 2, sq = tid & 3;
+  const bool stage = sr < T;
+  const uint8_t* asrc = xc + (int64_t)(stage ? sr : 0) * K + sq * (KS / 4);
+  uint4 ra[kAq];
+  auto aload = [&](int ss) {
+    if (stage) {
+#pragma unroll
+      for (int q = 0; q < kAq; ++q) ra[q] = reinterpret_cast<const uint4*>(asrc + (int64_t)ss * KS)[q];
+    }
+  };
+  auto astore = [&](int buf) {
+    if (stage) {
+#pragma unroll
+      for (int q = 0; q < kAq; ++q) {
+        uint4* d = reinterpret_cast<uint4*>(&As[buf][sr][sq * (KS / 4) + 16 * q]);
+        d[0] = __builtin_bit_cast(uint4, dec_fp8x8(ra[q].x, ra[q].y));
+        d[1] = __builtin_bit_cast(uint4, dec_fp8x8(ra[q].z, ra[q].w));
+      }
+    }
+  };
+  BRegs<false, KB> b0[NT], b1[NT];
+  f4v acc[4][NT];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[rt][j] = f4v{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](int buf, const BRegs<false, KB>* bc) {
+#pragma unroll
+    for (int J = 0; J < KB / 8; ++J) {
+      const int col = (J / SPU) * 4 * VPU + (J % SPU) * 8 + g * VPU;
+      h8v bd[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const uint4 c = bc[j].c[J / SPU];
+        bd[j] = (J & 1) ? dec_fp8x8(c.z, c.w) : dec_fp8x8(c.x, c.y);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        if (rt < nrt) {
+          const h8v a = *reinterpret_cast<const h8v*>(&As[buf][16 * rt + m][col]);
+#pragma unroll
+          for (int j = 0; j < NT; ++j) acc[rt][j] = mfma_ab<false>(a, bd[j], acc[rt][j]);
+        }
+      }
+    }
+  };
+  if (ss0 < ss1) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) b_load<false, KB>(crow[j] + (int64_t)ss0 * KS, b0[j]);
+    aload(ss0);
+    astore(0);
+    __syncthreads();
+    for (int ss = ss0; ss < ss1; ss += 2) {
+      // two super-steps per iteration so the code register set of each step is static
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int cur = ss + h;
+        if (cur < ss1) {
+          const bool more = cur + 1 < ss1;
+          if (more) {
+            aload(cur + 1);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) b_load<false, KB>(crow[j] + (int64_t)(cur + 1) * KS, h ? b0[j] : b1[j]);
+          }
+          mma((cur - ss0) & 1, h ? b1 : b0);
+          if (more) astore(((cur - ss0) & 1) ^ 1);
+          __syncthreads();
+        }
+      }
+    }
+  }
+  // epilogue: result register r of lane (m, g) is row 16 rt + 4 g + r, column m of the tile
+  const int64_t ncols = G1 ? 2 * I : N;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = 16 * rt + 4 * g + r;
+      if (t >= T) continue;
+      if (nsplit > 1) {
+        float* pr = part + ((int64_t)sp * T + t) * ncols;
+        if (G1) {
+          pr[n0 + m] = acc[rt][0][r];
+          pr[I + n0 + m] = acc[rt][1][r];
+        } else {
+#pragma unroll
+          for (int j = 0; j < NT; ++j) pr[n0 + 16 * j + m] = acc[rt][j][r];
+        }
+      } else if (G1) {
+        const int64_t col = n0 + m;
+        const float sx = xs[t];
+        out[t * I + col] = silu_mul(acc[rt][0][r] * (sx * wsc[col]), acc[rt][1][r] * (sx * wsc[I + col]));
+      } else {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int64_t col = n0 + 16 * j + m;
+          out[t * N + col] = acc[rt][j][r] * xs[t] * wsc[col];
+        }
+      }
+    }
+  }
+}
+
+// Split-K partial sums of k_dense_f8, added in split order, then its epilogue.
+template <bool G1>
+__global__ __launch_bounds__(256) void k_dense_reduce(const float* __restrict__ part, int nsplit, int64_t T,
+                                                      int64_t N, int64_t I, const float* __restrict__ xs,
+                                                      const float* __restrict__ wsc, float* __restrict__ out) {
+  const int64_t nout = G1 ? I : N, ncols = G1 ? 2 * I : N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * nout) return;
+  const int64_t t = i / nout, col = i % nout;
+  float a = 0.0f, b = 0.0f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* pr = part + ((int64_t)sp * T + t) * ncols;
+    a += pr[col];
+    if (G1) b += pr[I + col];
+  }
+  if (G1) {
+    const float sx = xs[t];
+    out[i] = silu_mul(a * (sx * wsc[col]), b * (sx * wsc[I + col]));
+  } else {
+    out[i] = a * xs[t] * wsc[col];
+  }
+}
+
+// Split count of k_dense_f8: the grid stays within one round of resident workgroups (two per CU: the LDS
+// tile takes 66 KB), since a partly filled second round leaves most CUs idle; at least one super-step per
+// split, at most 16 splits.
+inline int dense_splits(int64_t ncb, int64_t nss) {
+  int64_t sp = 512 / ncb;
+  if (sp > 16) sp = 16;
+  if (sp > nss) sp = nss;
+  return (int)(sp < 1 ? 1 : sp);
+}
+constexpr int kDenseMaxSplits = 16;
+
+template <bool G1>
+hipError_t launch_dense_f8(const uint8_t* xc, const float* xs, int64_t T, int64_t K, const uint8_t* wc,
+                           const float* wsc, int64_t N, int64_t I, float* out, float* part, hipStream_t st) {
+  const int64_t ncb = G1 ? I / 64 : N / 128;  // 4 waves x 16 h columns / 32 output columns
+  const bool kb64 = K % 256 == 0;
+  const int64_t nss = K / (kb64 ? 256 : 128);
+  const int sp = dense_splits(ncb, nss);
+  const dim3 grid((unsigned)ncb, 1, (unsigned)sp);
+  if (kb64)
+    k_dense_f8<G1, 64><<<grid, 256, 0, st>>>(xc, xs, T, K, wc, wsc, N, I, out, part);
+  else
+    k_dense_f8<G1, 32><<<grid, 256, 0, st>>>(xc, xs, T, K, wc, wsc, N, I, out, part);
+  if (sp > 1) {
+    const int64_t n = T * (G1 ? I : N);
+    k_dense_reduce<G1><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(part, sp, T, N, I, xs, wsc, out);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Grouped GEMM for many rows per expert ("wide"): 128 rows x 128 weight rows
 // per workgroup, K in steps of 64 staged through LDS (double buffered).  The activation tile is staged as FP16; the weight
 // tile is staged as its raw codes (and NVFP4 scale bytes), a quarter (half,
@@ -1242,11 +1436,11 @@ __global__ void k_dense_tiles(int64_t T, int4* __restrict__ tiles_s, int* __rest
 }
 
 struct LinLayout {
-  size_t act, tiles_s, ntiles_s, tiles_w, ntiles_w, amax, total;
+  size_t act, tiles_s, ntiles_s, tiles_w, ntiles_w, amax, part, total;
   int64_t max_s, max_w;
 };
 
-LinLayout lin_layout(int64_t T, int64_t K) {
+LinLayout lin_layout(int64_t T, int64_t K, int64_t N) {
   LinLayout L{};
   L.max_s = (kSkinnyMaxRows + kRowsPerTile - 1) / kRowsPerTile;
   L.max_w = (T + kWideRows - 1) / kWideRows;
@@ -1262,18 +1456,22 @@ LinLayout lin_layout(int64_t T, int64_t K) {
   L.tiles_w = take(sizeof(int4) * (L.max_w > 0 ? L.max_w : 1));
   L.ntiles_w = take(sizeof(int));
   L.amax = take(sizeof(uint32_t));
+  // split-K partial sums of the dense kernel (T <= kDenseRows)
+  L.part = take(T <= kDenseRows ? sizeof(float) * kDenseMaxSplits * (size_t)T * (size_t)N : 16);
   L.total = o;
   return L;
 }
 
 }  // namespace
 
-size_t fp8_linear_ws(int64_t T, int64_t K) { return lin_layout(T, K).total; }
+size_t fp8_linear_ws(int64_t T, int64_t K, int64_t N) { return lin_layout(T, K, N).total; }
 
 hipError_t launch_fp8_linear(const uint8_t* xc, const float* xs, const uint8_t* wc, const float* wsc, int64_t T,
                              int64_t K, int64_t N, float* out, uint8_t* ws, hipStream_t st) {
-  const LinLayout L = lin_layout(T, K);
+  const LinLayout L = lin_layout(T, K, N);
   if (T == 0) return hipSuccess;
+  if (T <= kDenseRows)  // every workgroup covers all rows; weights streamed once
+    return launch_dense_f8<false>(xc, xs, T, K, wc, wsc, N, 0, out, reinterpret_cast<float*>(ws + L.part), st);
   _Float16* act = reinterpret_cast<_Float16*>(ws + L.act);
   int4* tiles_s = reinterpret_cast<int4*>(ws + L.tiles_s);
   int* ntiles_s = reinterpret_cast<int*>(ws + L.ntiles_s);
@@ -1338,6 +1536,9 @@ MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int
   L.tiles_w = take(sizeof(int4) * L.max_tiles_w);
   L.ntiles_w = take(sizeof(int));
   L.h_amax = take(sizeof(uint32_t));
+  // split-K partial sums of the dense FP8 kernel (one expert, top-1, at most kDenseRows tokens)
+  const bool dense = !nvfp4 && E == 1 && topk == 1 && T <= kDenseRows;
+  L.part = take(dense ? sizeof(float) * kDenseMaxSplits * (size_t)T * (size_t)std::max<int64_t>(2 * I, H) : 16);
   L.total = o;
   return L;
 }
@@ -1395,6 +1596,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   // expert exceeds kSkinnyMaxRows rows and the many-row kernels have no tiles: they are not launched.
   static_assert(kChunk <= kSkinnyMaxRows, "a single chunk never yields a many-row expert");
   const bool many = L.n_chunks > 1;
+  // dense FP8 MLP (one expert, top-1, at most kDenseRows tokens): every workgroup covers all rows
+  const bool dense = !a.nvfp4 && !a.a16 && a.E == 1 && a.topk == 1 && a.T <= kDenseRows;
+  float* part = reinterpret_cast<float*>(ws + L.part);
   // the NVFP4 many-row kernel reads weights in groups of 4 K steps (K % 256 == 0): always for the gate/up
   // projection (H % 256 == 0), for the down projection when I % 256 == 0 (else the 16x16x32 kernel)
   const bool big_dn = BSM_PREFILL_BIG && a.I % 256 == 0;
@@ -1408,7 +1612,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     act = reinterpret_cast<_Float16*>(const_cast<uint8_t*>(a.x_codes));  // BF16 x, read as 16-bit containers
   else if (a.nvfp4)
     k_decode_act<true><<<gx, 256, 0, st>>>(a.x_codes, reinterpret_cast<const uint8_t*>(a.x_scales), xblk, act);
-  else
+  else if (!dense)
     k_decode_act<false><<<gx, 256, 0, st>>>(a.x_codes, nullptr, xblk, act);
   stage_mark(0, 1, st);
   const uint8_t* w13s = reinterpret_cast<const uint8_t*>(a.w13_scales);
@@ -1478,7 +1682,12 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #ifndef BSM_FP8_MFMA
 #define BSM_FP8_MFMA 1  // down projection of many-row experts on the FP8 matrix cores (0: decoded to FP16)
 #endif
-    if (a.H % (4 * BSM_FP8_KB) == 0) {
+    const float* w13f = reinterpret_cast<const float*>(a.w13_scales);
+    const float* w2f = reinterpret_cast<const float*>(a.w2_scales);
+    if (dense) {
+      err = launch_dense_f8<true>(a.x_codes, xrs, a.T, a.H, a.w13_codes, w13f, 0, a.I, h_f32, part, st);
+      if (err != hipSuccess) return err;
+    } else if (a.H % (4 * BSM_FP8_KB) == 0) {
       BSM_G1(false, BSM_FP8_KB);
     } else {
       BSM_G1(false, 32);
@@ -1487,7 +1696,11 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     err = launch_fp8_quantize(h_f32, false, L.P, a.I, h_codes, reinterpret_cast<float*>(h_scales), st, hdec);
     if (err != hipSuccess) return err;
     stage_mark(0, 3, st);
-    if (!BSM_FP8_MFMA) {
+    if (dense) {
+      err = launch_dense_f8<false>(h_codes, reinterpret_cast<const float*>(h_scales), L.P, a.I, a.w2_codes, w2f,
+                                   a.H, 0, y, part, st);
+      if (err != hipSuccess) return err;
+    } else if (!BSM_FP8_MFMA) {
       if (a.I % (4 * BSM_FP8_KB) == 0) {
         BSM_G2(false, BSM_FP8_KB);
       } else {
@@ -1504,7 +1717,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
             hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
       if (many)
         k_gemm_f8_down<<<dim3((unsigned)(a.H / kGBN), (unsigned)L.max_tiles_w), 256, 0, st>>>(
-          h_codes, hsc, a.w2_codes, reinterpret_cast<const float*>(a.w2_scales), tiles_w, ntiles_w, a.I, a.H, y);
+          h_codes, hsc, a.w2_codes, w2f, tiles_w, ntiles_w, a.I, a.H, y);
     }
   }
 #undef BSM_G1

@@ -214,18 +214,44 @@ __global__ __launch_bounds__(kThreads) void k_fp8_rows(const void* __restrict__ 
       v[3] = q.w;
     }
   };
+  // rows of up to kCache * 4 * kThreads values stay in registers between the amax and the encode pass
+  constexpr int kCache = 8;
+  const bool cached = n4 <= (int64_t)kCache * kThreads;
+  float cv[kCache][4];
   float m = 0.0f;
-  for (int64_t j = threadIdx.x; j < n4; j += kThreads) {
-    float v[4];
-    load4(j, v);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  if (cached) {
+#pragma unroll
+    for (int q = 0; q < kCache; ++q) {
+      const int64_t j = threadIdx.x + (int64_t)q * kThreads;
+      if (j < n4) {
+        load4(j, cv[q]);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(cv[q][0]), fabsf(cv[q][1])), fmaxf(fabsf(cv[q][2]), fabsf(cv[q][3]))));
+      }
+    }
+  } else {
+    for (int64_t j = threadIdx.x; j < n4; j += kThreads) {
+      float v[4];
+      load4(j, v);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
   }
   m = block_max(m, lds);
   const float s = m / 448.0f;
   if (threadIdx.x == 0) scales[r] = s;
-  for (int64_t j = threadIdx.x; j < n4; j += kThreads) {
+  for (int64_t j = threadIdx.x, q = 0; j < n4; j += kThreads, ++q) {
     float v[4];
-    load4(j, v);
+    if (cached) {
+#pragma unroll
+      for (int qq = 0; qq < kCache; ++qq)
+        if (qq == q) {
+          v[0] = cv[qq][0];
+          v[1] = cv[qq][1];
+          v[2] = cv[qq][2];
+          v[3] = cv[qq][3];
+        }
+    } else {
+      load4(j, v);
+    }
     uint32_t word = 0;
     _Float16 d[4];
 #pragma unroll
