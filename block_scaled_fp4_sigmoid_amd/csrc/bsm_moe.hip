@@ -988,7 +988,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   (void)kBRow;
   __shared__ __attribute__((aligned(16))) _Float16 As[2][kGBM][kGBK + 8];
   __shared__ __attribute__((aligned(16))) uint8_t Bg[kGBN][kGP];
-  __shared__ uint32_t Bsc[2][kGBN];
+  __shared__ uint32_t Bsc[GS][kGBN];  // NVFP4: scale dwords of the group's weight rows, by K step
   if ((int)blockIdx.y >= *ntiles) return;
   const int4 ti = tiles[blockIdx.y];
   const int e = ti.x, row0 = ti.y, nrows = ti.z;
@@ -1026,19 +1026,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   const uint8_t* ssrc = NV ? wsc + wrow_of(tid) * (K / 16) : nullptr;
 
   uint4 ra0, ra1, ra2, ra3, rb[kBI], sc4 = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int s) {  // global loads of K step s into registers (NVFP4 weights: whole groups)
+  auto aload = [&](int s) {  // activations of K step s into registers
     ra0 = *reinterpret_cast<const uint4*>(as0 + s * kGBK);
     ra1 = *reinterpret_cast<const uint4*>(as1 + s * kGBK);
     ra2 = *reinterpret_cast<const uint4*>(as2 + s * kGBK);
     ra3 = *reinterpret_cast<const uint4*>(as3 + s * kGBK);
-    if (s % GS == 0) {
-      const uint8_t* bs = bbase + s * kSB;
-#pragma unroll
-      for (int i = 0; i < kBI; ++i) rb[i] = *reinterpret_cast<const uint4*>(bs + bo[i]);
-      if constexpr (NV) sc4 = *reinterpret_cast<const uint4*>(ssrc + 4 * s);
-    }
   };
-  auto bstore = [&]() {  // weight registers of a group into the group buffer
+  auto bload = [&](int s) {  // weight codes (and NVFP4 scale bytes) of the group that starts at K step s
+    const uint8_t* bs = bbase + s * kSB;
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) rb[i] = *reinterpret_cast<const uint4*>(bs + bo[i]);
+    if constexpr (NV) sc4 = *reinterpret_cast<const uint4*>(ssrc + 4 * s);
+  };
+  auto bstore = [&]() {  // weight registers of a group into the group buffer, scale dwords by K step
 #pragma unroll
     for (int i = 0; i < kBI; ++i) {
       uint32_t* d = reinterpret_cast<uint32_t*>(&Bg[(256 / kBP) * i + tid / kBP][16 * bpart]);
@@ -1047,16 +1047,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
       d[2] = rb[i].z;
       d[3] = rb[i].w;
     }
+    if constexpr (NV) {
+      Bsc[0][tid] = sc4.x;
+      Bsc[1][tid] = sc4.y;
+      Bsc[2][tid] = sc4.z;
+      Bsc[3][tid] = sc4.w;
+    }
   };
-  auto lstore = [&](int buf, int s) {  // activation registers (and the step's scale dword) of K step s
+  auto lstore = [&](int buf) {  // activation registers into LDS buffer buf
     *reinterpret_cast<uint4*>(&As[buf][(tid >> 3)][8 * apart]) = ra0;
     *reinterpret_cast<uint4*>(&As[buf][32 + (tid >> 3)][8 * apart]) = ra1;
     *reinterpret_cast<uint4*>(&As[buf][64 + (tid >> 3)][8 * apart]) = ra2;
     *reinterpret_cast<uint4*>(&As[buf][96 + (tid >> 3)][8 * apart]) = ra3;
-    if constexpr (NV) {
-      const int j = s & 3;
-      Bsc[buf][tid] = j == 0 ? sc4.x : j == 1 ? sc4.y : j == 2 ? sc4.z : sc4.w;
-    }
   };
   // LDS weight row of this wave's N tile t: GEMM1 gate tile 0 / up tile 1; GEMM2 2 consecutive
 #define BSM_BIG_BROW(t) (G1 ? ((t) == 0 ? 32 * wave : kGBN / 2 + 32 * wave) : 64 * wave + 32 * (t))
@@ -1069,14 +1071,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mt][t][q] = 0.0f;
 
-  const int nk = (int)(K / kGBK);
-  gload(0);
-  bstore();
-  lstore(0, 0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
+  // K step j of the current group from LDS buffer buf
+  auto mma_step = [&](int j, int buf) {
 #pragma unroll
     for (int k16 = 0; k16 < kGBK / 16; ++k16) {
       h8v a[4];
@@ -1088,28 +1084,48 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
         const int brow = BSM_BIG_BROW(t) + l32;
         h8v b;
         if constexpr (NV) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(&Bg[brow][(ks & 3) * 32 + k16 * 8 + lh * 4]);
-          const h2v s2 = scale_pair_sel(Bsc[buf][brow], (uint32_t)k16 * 0x0101u);
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(&Bg[brow][j * 32 + k16 * 8 + lh * 4]);
+          const h2v s2 = scale_pair_sel(Bsc[j][brow], (uint32_t)k16 * 0x0101u);
           if constexpr (A16)
             b = dec_fp4x8_bf16(w, (float)s2[0]);
           else
             b = dec_fp4x8(w, s2);
         } else {
-          const uint2 w = *reinterpret_cast<const uint2*>(&Bg[brow][(ks & 1) * 64 + k16 * 16 + lh * 8]);
+          const uint2 w = *reinterpret_cast<const uint2*>(&Bg[brow][j * 64 + k16 * 16 + lh * 8]);
           b = dec_fp8x8(w.x, w.y);
         }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) acc[mt][t] = mfma32<A16>(a[mt], b, acc[mt][t]);
       }
     }
-    if (ks + 1 < nk) {
-      if ((ks + 1) % GS == 0) {  // next group: every wave has finished reading the current one
+  };
+
+  // The K loop runs over weight groups with the group's steps unrolled, so no load sits under a
+  // branch (indices past the end are clamped to the last step or group and their data is never
+  // read) and the wait counts stay exact.  A step's activations load one step ahead; a group's
+  // weights load two steps ahead, after the activations of that step, so that the activation
+  // store of the step before the group boundary does not wait for them.
+  const int nk = (int)(K / kGBK), ng = nk / GS;
+  aload(0);
+  bload(0);
+  bstore();
+  lstore(0);
+  __syncthreads();
+  for (int gi = 0; gi < ng; ++gi) {
+#pragma unroll
+    for (int j = 0; j < GS; ++j) {
+      const int ks = gi * GS + j;  // GS is even, so ks & 1 == j & 1
+      aload(ks + 1 < nk ? ks + 1 : ks);
+      if (j == GS - 2) bload(gi + 1 < ng ? (gi + 1) * GS : gi * GS);
+      __builtin_amdgcn_sched_barrier(0);  // the scheduler would otherwise sink the loads to their stores
+      mma_step(j, j & 1);
+      if (j == GS - 1) {  // next group: every wave has finished reading the current one
         __syncthreads();
         bstore();
       }
-      lstore(buf ^ 1, ks + 1);
+      lstore((j & 1) ^ 1);
+      __syncthreads();
     }
-    __syncthreads();
   }
 #undef BSM_BIG_BROW
 
