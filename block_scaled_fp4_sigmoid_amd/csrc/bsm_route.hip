@@ -24,8 +24,10 @@
 //   k_rowstats    large batches: per row of x and w, an upper bound of the
 //                 2-norm and the lowest set-bit exponent of its nonzero entries
 //   k_logits      large batches: 64x64 double-buffered LDS tiles, 8x4 logits
-//                 per thread; the epilogue tries exactness first, then the
-//                 error bound, then recomputes the rest exactly
+//                 per thread, K cut into slices (binary64 partial sums)
+//   k_logits_fin  large batches: adds the slices in order, tries exactness
+//                 first, then the error bound, then recomputes the rest
+//                 exactly
 //   k_select      one workgroup per token: certified binary64 sigmoid
 //                 (double-double fallback), group top-2 sums, group
 //                 selection, iterative 64-bit (score, index) argmax,
@@ -38,31 +40,45 @@ namespace bsm {
 namespace {
 
 constexpr int kTile = 64;  // tokens x experts per workgroup of the tiled logits kernel
-constexpr int kBK = 32;    // K step staged in LDS
+constexpr int kBK = 16;    // K step of the tiled logits kernel staged in LDS (32 KB double-buffered)
 constexpr int kRbT = 4;    // tokens per workgroup of the small-batch logits kernel
 constexpr int kRbE = 8;    // experts per workgroup of the small-batch logits kernel
 constexpr int kRbK = 2048; // K covered by one pass of a small-batch workgroup (256 lanes x 8)
 
 struct RouteWs {
-  size_t norm, lsb, logits, blk, diag, total;  // norm, lsb: tiled path only
+  size_t norm, lsb, part, logits, blk, diag, total;  // norm, lsb, part: tiled path only
   bool rb;    // small-batch kernel (full K per workgroup, lanes own K slices)
   int nadd;   // roundings along the longest summation path of one logit
   int64_t nblk;  // logits workgroups (one exact-recomputation count each)
+  int ks;        // tiled path: K slices (one binary64 partial sum per logit each)
+  int64_t kslice;  // tiled path: K per slice (a multiple of kBK)
 };
 
 RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
   RouteWs L;
   const int64_t tiles = ((T + kTile - 1) / kTile) * ((E + kTile - 1) / kTile);
   L.rb = (H % 8 == 0) && tiles < 128;
+  // Tiled path: K is cut into slices so that the grid holds about 16 waves per CU (a 64 x 64 tile
+  // is two waves, 32 KB of LDS); every slice holds at least one LDS step.
+  const int64_t nst = (H + kBK - 1) / kBK;
+  int64_t ks = (2048 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  ks = ks < 1 ? 1 : ks > 8 ? 8 : ks;
+  ks = ks > nst ? (nst > 0 ? nst : 1) : ks;
+  const int64_t sps = (nst + ks - 1) / ks;  // LDS steps per slice
+  L.ks = (int)(sps > 0 ? (nst + sps - 1) / sps : 1);
+  L.kslice = sps * kBK;
   // small batch: one FMA chain of 8 per pass, 6 shuffle levels, 3 cross-wave adds;
-  // tiled: an FMA chain of kBK per LDS step, added to the running sum
-  L.nadd = L.rb ? (int)(((H + kRbK - 1) / kRbK) * 8 + 9) : (int)(kBK + (H + kBK - 1) / kBK + 1);
+  // tiled: an FMA chain of kBK per LDS step, added to the slice's running sum, then the slices
+  // added in order
+  L.nadd = L.rb ? (int)(((H + kRbK - 1) / kRbK) * 8 + 9) : (int)(kBK + sps + L.ks + 1);
   L.nblk = L.rb ? ((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE) : tiles;
   size_t o = 0;
   L.norm = o;
   if (!L.rb) o += align256(sizeof(double) * (size_t)(T + E));
   L.lsb = o;
   if (!L.rb) o += align256(sizeof(int) * (size_t)(T + E));
+  L.part = o;
+  if (!L.rb) o += align256(sizeof(double) * (size_t)L.ks * (size_t)T * (size_t)E);
   L.logits = o;
   o += align256(sizeof(float) * (size_t)T * (size_t)E);
   L.blk = o;
@@ -458,43 +474,42 @@ __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, c
 
 // Large batches: 64x64 token x expert tiles staged through LDS, 4x4 outputs
 // per thread; binary64 FMA chains of kBK products added to running sums.
-// Large batches: a workgroup of 128 threads owns 64 tokens x 64 experts; each
-// thread accumulates 8 tokens x 4 experts.  K steps of kBK are staged through
-// double-buffered LDS as binary64 (converted once per element), laid out
-// [k][row] so a wave's staging stores and its expert reads are contiguous and
-// its token reads are broadcasts.  Per logit: an FMA chain over the kBK
-// products of a step (k ascending), added to the running sum (steps
-// ascending).
+// Large batches: a workgroup of 128 threads owns 64 tokens x 64 experts and
+// one K slice (blockIdx.z); each thread accumulates 8 tokens x 4 experts.  K
+// steps of kBK are staged through double-buffered LDS as binary64 (converted
+// once per element), laid out [k][row] so a wave's staging stores and its
+// expert reads are contiguous and its token reads are broadcasts.  Per logit
+// and slice: an FMA chain over the kBK products of a step (k ascending),
+// added to the slice's running sum (steps ascending), stored as a binary64
+// partial sum.
 template <bool XB, bool WB, bool VEC>
 __global__ __launch_bounds__(128) void k_logits(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
-                                                int64_t E, int64_t H, const double* __restrict__ norm,
-                                                const int* __restrict__ lsb, int nadd, float* __restrict__ logits,
-                                                int* __restrict__ blk, int* __restrict__ diag) {
+                                                int64_t E, int64_t H, int64_t kslice, double* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) double tl[2][2][kBK][kTile];  // [buffer][x, w][k][row]
-  __shared__ int n_unc;
-  __shared__ ExactLds xl;
-  int* unc = reinterpret_cast<int*>(&tl[0][0][0][0]);  // after the main loop: the tile's uncertain logits
-  static_assert(sizeof(tl) >= sizeof(int) * kTile * kTile, "uncertain-logit list fits the staging buffers");
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid >= 1 && tid < 4) diag[tid] = 0;  // selection-kernel counters
   const int tx = tid & 15, ty = tid >> 4;  // experts {2tx, 2tx+1, 32+2tx, 33+2tx}; tokens {4ty+i, 32+4ty+i}
   const int64_t t0 = (int64_t)blockIdx.x * kTile, e0 = (int64_t)blockIdx.y * kTile;
-  // staging: row sr of the x and w tiles, k values 16 sh .. +15 of the step.  Rows past T or E
-  // repeat the last row: their logits are never stored, and no other logit reads them.
+  const int64_t k0 = (int64_t)blockIdx.z * kslice;
+  const int64_t k1 = k0 + kslice < H ? k0 + kslice : H;  // k0 < H: every slice holds at least one step
+  // staging: row sr of the x and w tiles, k values kPer sh .. + kPer - 1 of the step.  Rows past
+  // T or E repeat the last row: their logits are never stored, and no other logit reads them.
+  constexpr int kPer = kBK / 2;  // values of each operand per thread and step
+  static_assert(kPer % 8 == 0, "staging in 8-value loads");
   const int sr = tid & 63, sh = tid >> 6;
   const int64_t xr = t0 + sr < T ? t0 + sr : T - 1, wr = e0 + sr < E ? e0 + sr : E - 1;
-  const int64_t xo = xr * H + 16 * sh, wo = wr * H + 16 * sh;
-  float xv[16], wv[16];
+  const int64_t xo = xr * H + kPer * sh, wo = wr * H + kPer * sh;
+  float xv[kPer], wv[kPer];
   auto gload = [&](int64_t kb) {
     if constexpr (VEC) {  // H % kBK == 0: every k of the step is in range
-      ld8<XB>(x, xo + kb, xv);
-      ld8<XB>(x, xo + kb + 8, xv + 8);
-      ld8<WB>(w, wo + kb, wv);
-      ld8<WB>(w, wo + kb + 8, wv + 8);
+#pragma unroll
+      for (int q = 0; q < kPer; q += 8) {
+        ld8<XB>(x, xo + kb + q, xv + q);
+        ld8<WB>(w, wo + kb + q, wv + q);
+      }
     } else {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const bool kin = kb + 16 * sh + q < H;
+      for (int q = 0; q < kPer; ++q) {
+        const bool kin = kb + kPer * sh + q < H;
         xv[q] = kin ? ld1<XB>(x, xo + kb + q) : 0.0f;
         wv[q] = kin ? ld1<WB>(w, wo + kb + q) : 0.0f;
       }
@@ -502,9 +517,9 @@ __global__ __launch_bounds__(128) void k_logits(const void* __restrict__ x, cons
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      tl[buf][0][16 * sh + q][sr] = (double)xv[q];
-      tl[buf][1][16 * sh + q][sr] = (double)wv[q];
+    for (int q = 0; q < kPer; ++q) {
+      tl[buf][0][kPer * sh + q][sr] = (double)xv[q];
+      tl[buf][1][kPer * sh + q][sr] = (double)wv[q];
     }
   };
   double acc[8][4];
@@ -512,14 +527,14 @@ __global__ __launch_bounds__(128) void k_logits(const void* __restrict__ x, cons
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  const int nst = (int)((H + kBK - 1) / kBK);
-  gload(0);
+  const int nst = (int)((k1 - k0 + kBK - 1) / kBK);
+  gload(k0);
   lstore(0);
   __syncthreads();
   for (int s = 0; s < nst; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nst) gload((int64_t)(s + 1) * kBK);
-    double blk[8][4];  // chain of kBK products per step, then one add: depth kBK + H / kBK
+    if (s + 1 < nst) gload(k0 + (int64_t)(s + 1) * kBK);
+    double blk[8][4];  // chain of kBK products per step, then one add
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -546,25 +561,45 @@ __global__ __launch_bounds__(128) void k_logits(const void* __restrict__ x, cons
     if (s + 1 < nst) lstore(buf ^ 1);
     __syncthreads();
   }
-  if (tid == 0) n_unc = 0;
-  __syncthreads();
+  double* pz = part + (int64_t)blockIdx.z * T * E;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int tr = (i < 4 ? 0 : 32) + 4 * ty + (i & 3);
-    const int64_t t = t0 + tr;
+    const int64_t t = t0 + (i < 4 ? 0 : 32) + 4 * ty + (i & 3);
     if (t >= T) continue;
-    const double nx = norm[t];
-    const int lx = lsb[t];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int ec = (j < 2 ? 0 : 32) + 2 * tx + (j & 1);
-      const int64_t e = e0 + ec;
-      if (e < E) {
-        const float r = certify_logit(acc[i][j], nx, norm[T + e], lx, lsb[T + e], nadd);
-        logits[t * E + e] = r;
-        if (r != r) unc[atomicAdd(&n_unc, 1)] = tr * kTile + ec;
-      }
+      const int64_t e = e0 + (j < 2 ? 0 : 32) + 2 * tx + (j & 1);
+      if (e < E) pz[t * E + e] = acc[i][j];
     }
+  }
+}
+
+// Large batches, per 64 x 64 tile: the K slices' partial sums added in slice
+// order, then exactness first, the error bound second, and an exact
+// recomputation of the logits neither proves.
+template <bool XB, bool WB>
+__global__ __launch_bounds__(128) void k_logits_fin(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
+                                                    int64_t E, int64_t H, int ks, const double* __restrict__ part,
+                                                    const double* __restrict__ norm, const int* __restrict__ lsb,
+                                                    int nadd, float* __restrict__ logits, int* __restrict__ blk,
+                                                    int* __restrict__ diag) {
+  __shared__ int unc[kTile * kTile];  // the tile's uncertain logits
+  __shared__ int n_unc;
+  __shared__ ExactLds xl;
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid >= 1 && tid < 4) diag[tid] = 0;  // selection-kernel counters
+  const int64_t t0 = (int64_t)blockIdx.x * kTile, e0 = (int64_t)blockIdx.y * kTile;
+  if (tid == 0) n_unc = 0;
+  __syncthreads();
+  for (int q = tid; q < kTile * kTile; q += 128) {
+    const int tr = q / kTile, ec = q % kTile;
+    const int64_t t = t0 + tr, e = e0 + ec;
+    if (t >= T || e >= E) continue;
+    double S = part[t * E + e];
+    for (int z = 1; z < ks; ++z) S += part[(int64_t)z * T * E + t * E + e];
+    const float r = certify_logit(S, norm[t], norm[T + e], lsb[t], lsb[T + e], nadd);
+    logits[t * E + e] = r;
+    if (r != r) unc[atomicAdd(&n_unc, 1)] = q;
   }
   __syncthreads();
   const int nu = n_unc;
@@ -696,12 +731,14 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   int* diag = reinterpret_cast<int*>(ws + L.diag);
   double* norm = L.rb ? nullptr : reinterpret_cast<double*>(ws + L.norm);
   int* lsb = L.rb ? nullptr : reinterpret_cast<int*>(ws + L.lsb);
+  double* part = L.rb ? nullptr : reinterpret_cast<double*>(ws + L.part);
   if (T == 0) return hipSuccess;
   stage_mark(1, 0, st);
   const unsigned nrs = (unsigned)((T + E + 3) / 4);
   const bool vec = (H % 8) == 0;
   const unsigned nrb = (unsigned)(((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE));
-  dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
+  const dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
+  const dim3 glz(gl.x, gl.y, (unsigned)L.ks);
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
   if (L.rb) {                                                                                              \
     k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, L.nadd, logits, blk, diag);                    \
@@ -711,9 +748,10 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
     else                                                                                                   \
       k_rowstats<XB, WB, false><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                            \
     if (H % kBK == 0)                                                                                      \
-      k_logits<XB, WB, true><<<gl, 128, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, blk, diag);     \
+      k_logits<XB, WB, true><<<glz, 128, 0, st>>>(x, w, T, E, H, L.kslice, part);                          \
     else                                                                                                   \
-      k_logits<XB, WB, false><<<gl, 128, 0, st>>>(x, w, T, E, H, norm, lsb, L.nadd, logits, blk, diag);    \
+      k_logits<XB, WB, false><<<glz, 128, 0, st>>>(x, w, T, E, H, L.kslice, part);                         \
+    k_logits_fin<XB, WB><<<gl, 128, 0, st>>>(x, w, T, E, H, L.ks, part, norm, lsb, L.nadd, logits, blk, diag); \
   }                                                                                                        \
   stage_mark(1, 1, st);                                                                                    \
   k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, blk,    \
