@@ -26,8 +26,9 @@
 //   k_logits      large batches: 64x64 double-buffered LDS tiles, 8x4 logits
 //                 per thread, K cut into slices (binary64 partial sums)
 //   k_logits_fin  large batches: adds the slices in order, tries exactness
-//                 first, then the error bound, then recomputes the rest
-//                 exactly
+//                 first, then the error bound, and lists the rest
+//   k_exact_list  large batches: the listed logits recomputed exactly, one
+//                 workgroup per logit
 //   k_select      one workgroup per token: certified binary64 sigmoid
 //                 (double-double fallback), group top-2 sums, group
 //                 selection, iterative 64-bit (score, index) argmax,
@@ -44,9 +45,10 @@ constexpr int kBK = 16;    // K step of the tiled logits kernel staged in LDS (3
 constexpr int kRbT = 4;    // tokens per workgroup of the small-batch logits kernel
 constexpr int kRbE = 8;    // experts per workgroup of the small-batch logits kernel
 constexpr int kRbK = 2048; // K covered by one pass of a small-batch workgroup (256 lanes x 8)
+constexpr int kExactWgs = 1024;  // workgroups sharing the list of logits recomputed exactly
 
 struct RouteWs {
-  size_t norm, lsb, part, logits, blk, diag, total;  // norm, lsb, part: tiled path only
+  size_t norm, lsb, part, ulist, logits, blk, diag, total;  // norm, lsb, part, ulist: tiled path only
   bool rb;    // small-batch kernel (full K per workgroup, lanes own K slices)
   int nadd;   // roundings along the longest summation path of one logit
   int64_t nblk;  // logits workgroups (one exact-recomputation count each)
@@ -79,6 +81,8 @@ RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
   if (!L.rb) o += align256(sizeof(int) * (size_t)(T + E));
   L.part = o;
   if (!L.rb) o += align256(sizeof(double) * (size_t)L.ks * (size_t)T * (size_t)E);
+  L.ulist = o;  // count, then the flat indices of the logits left for exact recomputation
+  if (!L.rb) o += align256(sizeof(int) * (size_t)(T * E + 1));
   L.logits = o;
   o += align256(sizeof(float) * (size_t)T * (size_t)E);
   L.blk = o;
@@ -484,9 +488,11 @@ __global__ __launch_bounds__(256) void k_logits_rb(const void* __restrict__ x, c
 // partial sum.
 template <bool XB, bool WB, bool VEC>
 __global__ __launch_bounds__(128) void k_logits(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
-                                                int64_t E, int64_t H, int64_t kslice, double* __restrict__ part) {
+                                                int64_t E, int64_t H, int64_t kslice, double* __restrict__ part,
+                                                int* __restrict__ ulist) {
   __shared__ __attribute__((aligned(16))) double tl[2][2][kBK][kTile];  // [buffer][x, w][k][row]
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *ulist = 0;  // read by the finalize kernel
   const int tx = tid & 15, ty = tid >> 4;  // experts {2tx, 2tx+1, 32+2tx, 33+2tx}; tokens {4ty+i, 32+4ty+i}
   const int64_t t0 = (int64_t)blockIdx.x * kTile, e0 = (int64_t)blockIdx.y * kTile;
   const int64_t k0 = (int64_t)blockIdx.z * kslice;
@@ -575,23 +581,19 @@ __global__ __launch_bounds__(128) void k_logits(const void* __restrict__ x, cons
 }
 
 // Large batches, per 64 x 64 tile: the K slices' partial sums added in slice
-// order, then exactness first, the error bound second, and an exact
-// recomputation of the logits neither proves.
-template <bool XB, bool WB>
-__global__ __launch_bounds__(128) void k_logits_fin(const void* __restrict__ x, const void* __restrict__ w, int64_t T,
-                                                    int64_t E, int64_t H, int ks, const double* __restrict__ part,
+// order, then exactness first and the error bound second.  The logits neither
+// proves go to a list (ulist[0] counts them) for k_exact_list.
+__global__ __launch_bounds__(256) void k_logits_fin(int64_t T, int64_t E, int ks, const double* __restrict__ part,
                                                     const double* __restrict__ norm, const int* __restrict__ lsb,
-                                                    int nadd, float* __restrict__ logits, int* __restrict__ blk,
-                                                    int* __restrict__ diag) {
-  __shared__ int unc[kTile * kTile];  // the tile's uncertain logits
+                                                    int nadd, float* __restrict__ logits, int* __restrict__ ulist,
+                                                    int* __restrict__ blk, int* __restrict__ diag) {
   __shared__ int n_unc;
-  __shared__ ExactLds xl;
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && blockIdx.y == 0 && tid >= 1 && tid < 4) diag[tid] = 0;  // selection-kernel counters
   const int64_t t0 = (int64_t)blockIdx.x * kTile, e0 = (int64_t)blockIdx.y * kTile;
   if (tid == 0) n_unc = 0;
   __syncthreads();
-  for (int q = tid; q < kTile * kTile; q += 128) {
+  for (int q = tid; q < kTile * kTile; q += 256) {
     const int tr = q / kTile, ec = q % kTile;
     const int64_t t = t0 + tr, e = e0 + ec;
     if (t >= T || e >= E) continue;
@@ -599,16 +601,29 @@ __global__ __launch_bounds__(128) void k_logits_fin(const void* __restrict__ x, 
     for (int z = 1; z < ks; ++z) S += part[(int64_t)z * T * E + t * E + e];
     const float r = certify_logit(S, norm[t], norm[T + e], lsb[t], lsb[T + e], nadd);
     logits[t * E + e] = r;
-    if (r != r) unc[atomicAdd(&n_unc, 1)] = q;
+    if (r != r) {
+      atomicAdd(&n_unc, 1);
+      ulist[1 + atomicAdd(ulist, 1)] = (int)(t * E + e);
+    }
   }
   __syncthreads();
-  const int nu = n_unc;
-  for (int u = 0; u < nu; ++u) {
-    const int64_t t = t0 + unc[u] / kTile, e = e0 + unc[u] % kTile;
+  if (tid == 0) blk[blockIdx.y * gridDim.x + blockIdx.x] = n_unc;
+}
+
+// The listed logits, exactly: each workgroup takes list entries blockIdx.x,
+// blockIdx.x + gridDim.x, ... (the list order does not matter: every entry's
+// value is exact).
+template <bool XB, bool WB>
+__global__ __launch_bounds__(128) void k_exact_list(const void* __restrict__ x, const void* __restrict__ w, int64_t E,
+                                                    int64_t H, const double* __restrict__ norm, int64_t T,
+                                                    const int* __restrict__ ulist, float* __restrict__ logits) {
+  __shared__ ExactLds xl;
+  const int n = ulist[0];
+  for (int u = blockIdx.x; u < n; u += gridDim.x) {
+    const int64_t i = ulist[1 + u], t = i / E, e = i % E;
     const float r = exact_logit_wg<XB, WB, 128>(x, w, t, e, H, abs_bound(norm[t], norm[T + e]), &xl);
-    if (tid == 0) logits[t * E + e] = r;
+    if (threadIdx.x == 0) logits[i] = r;
   }
-  if (tid == 0) blk[blockIdx.y * gridDim.x + blockIdx.x] = nu;
 }
 
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
@@ -732,6 +747,7 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   double* norm = L.rb ? nullptr : reinterpret_cast<double*>(ws + L.norm);
   int* lsb = L.rb ? nullptr : reinterpret_cast<int*>(ws + L.lsb);
   double* part = L.rb ? nullptr : reinterpret_cast<double*>(ws + L.part);
+  int* ulist = L.rb ? nullptr : reinterpret_cast<int*>(ws + L.ulist);
   if (T == 0) return hipSuccess;
   stage_mark(1, 0, st);
   const unsigned nrs = (unsigned)((T + E + 3) / 4);
@@ -748,12 +764,13 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
     else                                                                                                   \
       k_rowstats<XB, WB, false><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                            \
     if (H % kBK == 0)                                                                                      \
-      k_logits<XB, WB, true><<<glz, 128, 0, st>>>(x, w, T, E, H, L.kslice, part);                          \
+      k_logits<XB, WB, true><<<glz, 128, 0, st>>>(x, w, T, E, H, L.kslice, part, ulist);                   \
     else                                                                                                   \
-      k_logits<XB, WB, false><<<glz, 128, 0, st>>>(x, w, T, E, H, L.kslice, part);                         \
-    k_logits_fin<XB, WB><<<gl, 128, 0, st>>>(x, w, T, E, H, L.ks, part, norm, lsb, L.nadd, logits, blk, diag); \
+      k_logits<XB, WB, false><<<glz, 128, 0, st>>>(x, w, T, E, H, L.kslice, part, ulist);                  \
+    k_logits_fin<<<gl, 256, 0, st>>>(T, E, L.ks, part, norm, lsb, L.nadd, logits, ulist, blk, diag);        \
   }                                                                                                        \
   stage_mark(1, 1, st);                                                                                    \
+  if (!L.rb) k_exact_list<XB, WB><<<kExactWgs, 128, 0, st>>>(x, w, E, H, norm, T, ulist, logits);          \
   k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, blk,    \
                                                 L.nblk, diag);
   if (xb && wb) {
