@@ -144,9 +144,20 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int* __restrict__ cnt,
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
-    for (int64_t c = 0; c < nc; ++c) {
-      base[e * nc + c] = total;
-      total += cnt[e * nc + c];
+    // 32 chunk counts in flight per batch (independent loads, clamped in range), then their prefix
+    const int* ce = cnt + (int64_t)e * nc;
+    int* be = base + (int64_t)e * nc;
+    for (int64_t c0 = 0; c0 < nc; c0 += 32) {
+      int v[32];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) v[q] = ce[c0 + q < nc ? c0 + q : nc - 1];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        if (c0 + q < nc) {
+          be[c0 + q] = total;
+          total += v[q];
+        }
+      }
     }
     counts[e] = total;
   }
