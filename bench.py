@@ -16,6 +16,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--fmt nvfp4|fp8|w4a1
 """
 
 import argparse
+import dataclasses
 import ctypes
 import json
 import os
@@ -136,9 +137,21 @@ def build_layer(cfg, fmt, dev):
     return x, wr, w13, w2, weights
 
 
-def run_steps(cfg, fmt, x, wr, weights, steps, warmup):
+def second_copy(x, wr, weights):
+    """A second, separately allocated copy of a layer's inputs and weights.
+
+    Steps alternate between the two copies, so a step never finds its inputs in
+    the 256 MB Infinity Cache from the step before (the layer reads several GB).
+    """
+    w2 = dataclasses.replace(weights, **{f.name: getattr(weights, f.name).clone() for f in dataclasses.fields(weights)
+                                         if isinstance(getattr(weights, f.name), torch.Tensor)})
+    return x.clone(), wr.clone(), w2
+
+
+def run_steps(cfg, fmt, x, wr, weights, steps, warmup, copies=None):
     """Time ``steps`` whole-path steps.
 
+    ``copies``: optional further (x, wr, weights) copies; step i uses copy i mod n.
     Timed pass: the library records only the two stage events around the gate/up
     GEMM (its per-launch duration, for the roofline) on its launch stream.  A
     second, untimed pass records every stage boundary for the per-stage
@@ -148,9 +161,13 @@ def run_steps(cfg, fmt, x, wr, weights, steps, warmup):
     T = x.shape[0]
     out = torch.empty((T, cfg.H), dtype=torch.float32, device=x.device)
     ws = None
+    sets = [(x, wr, weights)] + list(copies or [])
+    it = [0]
 
     def step():
         nonlocal ws
+        x, wr, weights = sets[it[0] % len(sets)]
+        it[0] += 1
         ids, wts = bsm.route(x, wr, cfg.n_group, cfg.topk_group, cfg.topk)
         if fmt == "w4a16":  # weight-only: the BF16 activations go in as they are
             o, ws = bsm.moe_expert_mlp_w4a16(weights, x, ids, wts, cfg.combine_scale, out=out, ws=ws,
@@ -386,7 +403,8 @@ def main():
         return
     main_cfg = W.DECODE if args.workload == "decode" else W.PREFILL
     x, wr, w13, w2, weights = build_layer(main_cfg, args.fmt, dev)
-    ms, stage_ms, g1_ms, counts = run_steps(main_cfg, args.fmt, x, wr, weights, args.steps, args.warmup)
+    ms, stage_ms, g1_ms, counts = run_steps(main_cfg, args.fmt, x, wr, weights, args.steps, args.warmup,
+                                            copies=[second_copy(x, wr, weights)])
     main_nums = layer_numbers(main_cfg, args.fmt, main_cfg.T, ms, stage_ms, g1_ms, counts)
     print(f"[bench] {main_cfg.name} {args.fmt}: {ms:.3f} ms/step, stages {stage_ms}", file=sys.stderr, flush=True)
 
@@ -407,7 +425,8 @@ def main():
         pcfg = W.PREFILL
         px, pwr, pw13, pw2, pweights = build_layer(pcfg, args.fmt, dev)
         psteps = max(3, args.steps // 4)
-        pms, pst, pg1, pcounts = run_steps(pcfg, args.fmt, px, pwr, pweights, psteps, 2)
+        pms, pst, pg1, pcounts = run_steps(pcfg, args.fmt, px, pwr, pweights, psteps, 2,
+                                           copies=[second_copy(px, pwr, pweights)])
         pn = layer_numbers(pcfg, args.fmt, pcfg.T, pms, pst, pg1, pcounts)
         print(f"[bench] prefill {args.fmt}: {pms:.3f} ms/step, stages {pst}", file=sys.stderr, flush=True)
         mm = {"nvfp4": "fp4", "fp8": "fp8", "w4a16": "f16"}[args.fmt]
