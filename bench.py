@@ -94,8 +94,53 @@ def _pmc_per_kernel(path):
     return out
 
 
-def summarize_pmc(fetch_csv, write_csv, command):
-    """Turn the FETCH_SIZE and WRITE_SIZE runs into HBM bytes per gate/up GEMM launch."""
+def _kernel_label(name):
+    """Library kernel name with its template arguments, from a demangled or mangled name; None otherwise."""
+    import re
+    m = re.search(r'bsm::\(anonymous namespace\)::(k_[a-z0-9_]+)(<([^>]*)>)?', name)
+    if m:
+        args = m.group(3).replace(' ', '') if m.group(3) else ''
+        return m.group(1) + (f"<{args}>" if args else "")
+    m = re.search(r'\d+(k_[a-z0-9_]+)(I(.*?E)EE|E)', name)
+    if not m or not name.startswith('_ZN3bsm'):
+        return None
+    args = []
+    if m.group(3):
+        for kind, val in re.findall(r'L([bi])(\d+)E', m.group(3)):
+            args.append(('true' if val == '1' else 'false') if kind == 'b' else val)
+    return m.group(1) + (f"<{','.join(args)}>" if args else "")
+
+
+def summarize_trace(trace_csv, title, command, notes=()):
+    """Print a rocprofv3 kernel_trace.csv as library kernels grouped by (name, template arguments, grid)."""
+    import csv
+    from collections import defaultdict
+    groups = defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            k = _kernel_label(r['Kernel_Name'])
+            if not k:
+                continue
+            grid = f"{int(r['Grid_Size_X']) // int(r['Workgroup_Size_X'])}x{r['Grid_Size_Y']}x{r['Grid_Size_Z']}"
+            groups[(k, grid)].append((int(r['End_Timestamp']) - int(r['Start_Timestamp'])) / 1e3)
+    print(f"# {title}")
+    print(f"# command: {command}")
+    print(f"# summary: python3 bench.py --summarize-trace <kernel_trace.csv> '<title>' '<command>'")
+    print("# rocprofv3 kernel trace, library kernels grouped by kernel, template arguments and grid (workgroups);")
+    print("# torch kernels of input generation omitted.  Durations in microseconds.")
+    for n in notes:
+        print(f"# {n}")
+    print(f"{'kernel':40s} {'grid':>14s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+    for (k, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{k:40s} {grid:>14s} {len(v):6d} {sum(v) / len(v):10.2f} {min(v):10.2f} {max(v):10.2f}")
+
+
+def summarize_pmc(fetch_csv, write_csv, command, bench_json=None):
+    """Turn the FETCH_SIZE and WRITE_SIZE runs into HBM bytes per gate/up GEMM launch.
+
+    Writes the JSON record that bench.py reads back and a text summary beside it;
+    ``bench_json`` (a default bench run's output line) supplies the algorithmic bytes.
+    """
     fetch, write = _pmc_per_kernel(fetch_csv), _pmc_per_kernel(write_csv)
 
     def pick(d, pred):
@@ -115,6 +160,34 @@ def summarize_pmc(fetch_csv, write_csv, command):
            "scale_fetch": sf, "scale_write": sw, "gemm_source_sha256": _source_digest(), "command": command}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)
+    alg = None
+    if bench_json:
+        with open(bench_json) as f:
+            alg = json.loads(f.readline())["roofline"]["algorithmic_bytes_per_launch"]
+    lines = [
+        "# HBM traffic of the gate/up GEMM (k_skinny<true,true,128,2,false,1>) at decode-64 NVFP4, MI355X",
+        "# command (two runs, one counter each):",
+        "#   " + command.replace(" (then WRITE_SIZE)", "").replace("fetch|write", "fetch"),
+        "#   " + command.replace("FETCH_SIZE (then WRITE_SIZE)", "WRITE_SIZE").replace("fetch|write", "write"),
+        "#   python3 bench.py --summarize-pmc <fetch counter_collection.csv> <write counter_collection.csv> "
+        "'<command>' <bench.py output line>",
+        "# scaling: the same counters on a 1 GiB elementwise copy (torch.add(src, 0, out=dst), 1 GiB read + 1 GiB "
+        "written)",
+        f"copy kernel FETCH_SIZE counter      {f_copy:.1f}  -> {sf:.2f} bytes per unit",
+        f"copy kernel WRITE_SIZE counter      {w_copy:.1f}  -> {sw:.2f} bytes per unit",
+        f"gate/up dispatches measured          {len(fetch[gemm])}",
+        f"fetched bytes per launch             {fb:.4g}",
+        f"written bytes per launch             {wb:.4g}",
+        f"HBM traffic per launch               {fb + wb:.4g}",
+    ]
+    if alg:
+        lines += [f"algorithmic bytes per launch         {alg:.4g}  (active experts x 14,745,600 B of gate/up "
+                  "weights + x codes/scales + h written)",
+                  f"traffic / algorithmic                {(fb + wb) / alg:.3f}"]
+    lines.append("# FETCH_SIZE counts what L2 requests from the memory fabric, so Infinity Cache hits are included "
+                 "in it.")
+    with open(TRAFFIC_FILE[:-len(".json")] + ".txt", "w") as f:
+        f.write("\n".join(lines) + "\n")
     print(json.dumps(res, indent=1))
 
 
@@ -381,11 +454,23 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB elementwise copy (reference for the HBM byte counters)")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
-                    help="write the gate/up GEMM HBM traffic from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
+                    help="FETCH_CSV WRITE_CSV COMMAND [BENCH_JSON]: write the gate/up GEMM HBM traffic from two "
+                         "rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="ARG",
+                    help="KERNEL_TRACE_CSV TITLE COMMAND [NOTE ...]: print the kernel summary of a rocprofv3 "
+                         "--kernel-trace run and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
+        if len(args.summarize_pmc) not in (3, 4):
+            ap.error("--summarize-pmc needs FETCH_CSV WRITE_CSV COMMAND [BENCH_JSON]")
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        if len(args.summarize_trace) < 3:
+            ap.error("--summarize-trace needs KERNEL_TRACE_CSV TITLE COMMAND")
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.summarize_trace[2],
+                        args.summarize_trace[3:])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
