@@ -972,6 +972,9 @@ __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict
 // 8q + 4 (l / 32) + j, column l % 32.
 // ---------------------------------------------------------------------------
 constexpr int kGBM = 128, kGBN = 256, kGBK = 64;
+#ifndef BSM_BIG_ADMA
+#define BSM_BIG_ADMA 1  // activation tiles by direct-to-LDS loads (0: through registers)
+#endif
 template <bool NV>
 struct BigB {
   static constexpr int kRow = NV ? 36 : 72;  // LDS bytes per weight row and K step (+4 / +8 pad)
@@ -1001,7 +1004,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   constexpr int kSB = NV ? kGBK / 2 : kGBK;    // code bytes per row and K step
   constexpr int kGP = NV ? 132 : 136;          // LDS bytes per weight row of a group (+pad: conflict-free reads)
   (void)kBRow;
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][kGBM][kGBK + 8];
+  // NVFP4 (and W4A16): the activation tile is written by direct-to-LDS loads (lane l of a load -> 16
+  // bytes at base + 16 l, so a load fills 8 whole 128-byte rows): unpadded rows, 16-byte chunk c of
+  // row r stored at chunk c ^ ((r >> 1) & 7), which keeps the fragment reads of 16 consecutive rows
+  // on distinct banks.  FP8 (measured slower that way) stages it through registers into padded rows.
+  // Two separate arrays, so the compiler sees that loads into one do not alias reads of the other.
+  constexpr bool kAdma = BSM_BIG_ADMA && NV;
+  constexpr int kAS = kAdma ? kGBK : kGBK + 8;  // LDS row stride (f16)
+  __shared__ __attribute__((aligned(16))) _Float16 As0[kGBM][kAS];
+  __shared__ __attribute__((aligned(16))) _Float16 As1[kGBM][kAS];
+  _Float16* const Ab[2] = {&As0[0][0], &As1[0][0]};
   __shared__ __attribute__((aligned(16))) uint8_t Bg[kGBN][kGP];
   __shared__ uint32_t Bsc[GS][kGBN];  // NVFP4: scale dwords of the group's weight rows, by K step
   if ((int)blockIdx.y >= *ntiles) return;
@@ -1017,10 +1029,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   constexpr int kBI = 8;  // weight rows per thread and group: kGBN / (256 / kBP)
   constexpr int kBP = 8;  // 16-byte parts per weight row and group
   const int apart = tid & 7, bpart = tid & (kBP - 1);
+  // direct-to-LDS: load i of wave w fills rows 32 w + 8 i .. + 7; lane l writes chunk l % 8 of row
+  // 32 w + 8 i + l / 8, which holds the row's logical chunk (l % 8) ^ ((row >> 1) & 7).
+  // Through registers: rows 32 i + tid / 8, 16-byte part tid % 8.
   auto arow = [&](int i) -> const _Float16* {
-    const int r = 32 * i + (tid >> 3);
+    const int r = kAdma ? 32 * wave + 8 * i + (lane >> 3) : 32 * i + (tid >> 3);
     const int ar = r < nrows ? r : nrows - 1;
-    return (G1 ? act + (int64_t)(row_pair[row0 + ar] / topk) * K : act + (int64_t)(row0 + ar) * K) + 8 * apart;
+    const int c = kAdma ? (lane & 7) ^ ((r >> 1) & 7) : apart;
+    return (G1 ? act + (int64_t)(row_pair[row0 + ar] / topk) * K : act + (int64_t)(row0 + ar) * K) + 8 * c;
   };
   const _Float16 *as0 = arow(0), *as1 = arow(1), *as2 = arow(2), *as3 = arow(3);
   // weight row r of the tile: GEMM1 gate rows c0.. then the matching up rows
@@ -1041,11 +1057,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   const uint8_t* ssrc = NV ? wsc + wrow_of(tid) * (K / 16) : nullptr;
 
   uint4 ra0, ra1, ra2, ra3, rb[kBI], sc4 = make_uint4(0, 0, 0, 0);
-  auto aload = [&](int s) {  // activations of K step s into registers
-    ra0 = *reinterpret_cast<const uint4*>(as0 + s * kGBK);
-    ra1 = *reinterpret_cast<const uint4*>(as1 + s * kGBK);
-    ra2 = *reinterpret_cast<const uint4*>(as2 + s * kGBK);
-    ra3 = *reinterpret_cast<const uint4*>(as3 + s * kGBK);
+  auto aload = [&](int s, _Float16* __restrict__ wr) {  // activations of K step s (into LDS tile wr)
+    if constexpr (kAdma) {
+      __builtin_amdgcn_global_load_lds(as0 + s * kGBK, wr + (32 * wave) * kGBK, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(as1 + s * kGBK, wr + (32 * wave + 8) * kGBK, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(as2 + s * kGBK, wr + (32 * wave + 16) * kGBK, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(as3 + s * kGBK, wr + (32 * wave + 24) * kGBK, 16, 0, 0);
+    } else {
+      ra0 = *reinterpret_cast<const uint4*>(as0 + s * kGBK);
+      ra1 = *reinterpret_cast<const uint4*>(as1 + s * kGBK);
+      ra2 = *reinterpret_cast<const uint4*>(as2 + s * kGBK);
+      ra3 = *reinterpret_cast<const uint4*>(as3 + s * kGBK);
+    }
   };
   auto bload = [&](int s) {  // weight codes (and NVFP4 scale bytes) of the group that starts at K step s
     const uint8_t* bs = bbase + s * kSB;
@@ -1069,11 +1092,37 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
       Bsc[3][tid] = sc4.w;
     }
   };
-  auto lstore = [&](int buf) {  // activation registers into LDS buffer buf
-    *reinterpret_cast<uint4*>(&As[buf][(tid >> 3)][8 * apart]) = ra0;
-    *reinterpret_cast<uint4*>(&As[buf][32 + (tid >> 3)][8 * apart]) = ra1;
-    *reinterpret_cast<uint4*>(&As[buf][64 + (tid >> 3)][8 * apart]) = ra2;
-    *reinterpret_cast<uint4*>(&As[buf][96 + (tid >> 3)][8 * apart]) = ra3;
+  // Direct-to-LDS: this wave's loads are complete once at most n later loads are in flight (loads
+  // complete in issue order); the barrier after it publishes every wave's rows.  Through
+  // registers: the activation registers into LDS tile buf.
+  auto lstore = [&](int buf, int n) {
+    if constexpr (kAdma) {
+      if (n == 0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited for
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kBI + 1));  // vmcnt(the group's weight and scale loads)
+    } else {
+      _Float16* d = Ab[buf] + (tid >> 3) * kAS + 8 * apart;
+      *reinterpret_cast<uint4*>(d) = ra0;
+      *reinterpret_cast<uint4*>(d + 32 * kAS) = ra1;
+      *reinterpret_cast<uint4*>(d + 64 * kAS) = ra2;
+      *reinterpret_cast<uint4*>(d + 96 * kAS) = ra3;
+    }
+  };
+  // Workgroup barrier.  With direct-to-LDS loads, __syncthreads() (also a workgroup release fence)
+  // would make the compiler wait for every load in flight, the next weight group's included, since
+  // such a load writes LDS.  There: this wave's LDS accesses complete (lgkmcnt(0)), the barrier, and
+  // compiler-only fences that keep memory accesses on their side of it; the direct-to-LDS loads are
+  // waited for explicitly in lstore.
+  auto lds_barrier = []() {
+    if constexpr (kAdma) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt(63), expcnt(7): not waited for
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    } else {
+      __syncthreads();
+    }
   };
   // LDS weight row of this wave's N tile t: GEMM1 gate tile 0 / up tile 1; GEMM2 2 consecutive
 #define BSM_BIG_BROW(t) (G1 ? ((t) == 0 ? 32 * wave : kGBN / 2 + 32 * wave) : 64 * wave + 32 * (t))
@@ -1087,13 +1136,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
       for (int q = 0; q < 16; ++q) acc[mt][t][q] = 0.0f;
 
   // K step j of the current group from LDS buffer buf
-  auto mma_step = [&](int j, int buf) {
+  // rd: the activation tile of this K step (rows of kAS; swizzled chunks with direct-to-LDS staging)
+  auto mma_step = [&](int j, const _Float16* __restrict__ rd) {
 #pragma unroll
     for (int k16 = 0; k16 < kGBK / 16; ++k16) {
       h8v a[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        a[mt] = *reinterpret_cast<const h8v*>(&As[buf][mt * 32 + l32][k16 * 16 + lh * 8]);
+        a[mt] = *reinterpret_cast<const h8v*>(
+            rd + (mt * 32 + l32) * kAS + (kAdma ? 8 * ((2 * k16 + lh) ^ ((l32 >> 1) & 7)) : k16 * 16 + lh * 8));
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int brow = BSM_BIG_BROW(t) + l32;
@@ -1121,25 +1172,33 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   // weights load two steps ahead, after the activations of that step, so that the activation
   // store of the step before the group boundary does not wait for them.
   const int nk = (int)(K / kGBK), ng = nk / GS;
-  aload(0);
+  // The step's loads and multiplies in one function whose two tile pointers are restrict-qualified:
+  // the compiler then knows the direct-to-LDS writes into one buffer do not alias the reads of the
+  // other, and does not make the reads wait for the writes.
+  auto issue_and_multiply = [&](int j, int snext, int gnext, _Float16* __restrict__ wr,
+                                const _Float16* __restrict__ rd) {
+    aload(snext, wr);
+    if (j == GS - 2) bload(gnext);
+    __builtin_amdgcn_sched_barrier(0);  // the scheduler would otherwise sink the loads to their stores
+    mma_step(j, rd);
+  };
+  aload(0, Ab[0]);
   bload(0);
   bstore();
-  lstore(0);
+  lstore(0, 0);
   __syncthreads();
   for (int gi = 0; gi < ng; ++gi) {
 #pragma unroll
     for (int j = 0; j < GS; ++j) {
       const int ks = gi * GS + j;  // GS is even, so ks & 1 == j & 1
-      aload(ks + 1 < nk ? ks + 1 : ks);
-      if (j == GS - 2) bload(gi + 1 < ng ? (gi + 1) * GS : gi * GS);
-      __builtin_amdgcn_sched_barrier(0);  // the scheduler would otherwise sink the loads to their stores
-      mma_step(j, j & 1);
+      issue_and_multiply(j, ks + 1 < nk ? ks + 1 : ks, gi + 1 < ng ? (gi + 1) * GS : gi * GS,
+                         Ab[(j & 1) ^ 1], Ab[j & 1]);
       if (j == GS - 1) {  // next group: every wave has finished reading the current one
-        __syncthreads();
+        lds_barrier();
         bstore();
       }
-      lstore((j & 1) ^ 1);
-      __syncthreads();
+      lstore((j & 1) ^ 1, j == GS - 2);
+      lds_barrier();
     }
   }
 #undef BSM_BIG_BROW
