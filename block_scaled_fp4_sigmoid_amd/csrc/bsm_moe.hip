@@ -1374,6 +1374,136 @@ __global__ __launch_bounds__(256, 2) void k_gemm_f8_down(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// FP8 down projection, three-stage direct-to-LDS pipeline: the same tile,
+// waves and MFMA as k_gemm_f8_down, with each K step's E4M3 h rows (128 x 64 B)
+// and weight rows (256 x 64 B) loaded straight into LDS
+// (global_load_lds_dwordx4: a load fills 16 unpadded 64-byte rows) two steps
+// ahead, into three buffers.  Chunk c of row r sits at chunk c ^ ((r >> 2) & 3),
+// which keeps the 16-byte fragment reads of 16 consecutive rows on distinct
+// banks.  Each buffer is its own LDS array and a step's loads and multiplies
+// sit in one function with restrict-qualified tile pointers, so the compiler
+// sees that the loads do not alias the reads; the barriers are LDS-only and
+// the loads are waited for explicitly (a workgroup fence would wait for all).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void k_gemm_f8_down3(const uint8_t* __restrict__ ac, const float* __restrict__ a_rs,
+                                                          const uint8_t* __restrict__ wc, const float* __restrict__ wsc,
+                                                          const int4* __restrict__ tiles, const int* __restrict__ ntiles,
+                                                          int64_t K, int64_t H, float* __restrict__ out) {
+  constexpr int kR = kGBK;  // LDS bytes per row and K step (unpadded)
+  __shared__ __attribute__((aligned(16))) uint8_t A0[kGBM * kR];
+  __shared__ __attribute__((aligned(16))) uint8_t A1[kGBM * kR];
+  __shared__ __attribute__((aligned(16))) uint8_t A2[kGBM * kR];
+  __shared__ __attribute__((aligned(16))) uint8_t B0[kGBN * kR];
+  __shared__ __attribute__((aligned(16))) uint8_t B1[kGBN * kR];
+  __shared__ __attribute__((aligned(16))) uint8_t B2[kGBN * kR];
+  if ((int)blockIdx.y >= *ntiles) return;
+  const int4 ti = tiles[blockIdx.y];
+  const int e = ti.x, row0 = ti.y, nrows = ti.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int64_t c0 = (int64_t)blockIdx.x * kGBN;
+  // load i of wave w fills rows 16 (n w + i) .. + 15 (n = 2 for h, 4 for weights); lane l writes
+  // chunk l % 4 of row 16 (n w + i) + l / 4, which holds the row's logical chunk (l % 4) ^ ((row >> 2) & 3)
+  auto src_chunk = [&](int r) { return (lane & 3) ^ ((r >> 2) & 3); };
+  const uint8_t* ap[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (2 * wave + i) + (lane >> 2);
+    const int ar = r < nrows ? r : nrows - 1;
+    ap[i] = ac + (int64_t)(row0 + ar) * K + 16 * src_chunk(r);
+  }
+  const uint8_t* bp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * (4 * wave + i) + (lane >> 2);
+    bp[i] = wc + ((int64_t)e * H + c0 + r) * K + 16 * src_chunk(r);
+  }
+  auto load = [&](int s, uint8_t* __restrict__ a, uint8_t* __restrict__ b) {
+    const int64_t k0 = (int64_t)s * kGBK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(ap[i] + k0, a + 16 * (2 * wave + i) * kR, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds(bp[i] + k0, b + 16 * (4 * wave + i) * kR, 16, 0, 0);
+  };
+  // fragment of row r: logical chunks 2 lh, 2 lh + 1 (32 bytes), swizzle (r >> 2) & 3 = (l32 >> 2) & 3
+  const int sw = (l32 >> 2) & 3;
+  const int p0 = 16 * ((2 * lh) ^ sw), p1 = 16 * ((2 * lh + 1) ^ sw);
+  auto frag = [&](const uint8_t* row) -> i8v {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(row + p0);
+    const uint4 u1 = *reinterpret_cast<const uint4*>(row + p1);
+    i8v v;
+    v[0] = (int)u0.x; v[1] = (int)u0.y; v[2] = (int)u0.z; v[3] = (int)u0.w;
+    v[4] = (int)u1.x; v[5] = (int)u1.y; v[6] = (int)u1.z; v[7] = (int)u1.w;
+    return v;
+  };
+  f16v acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mt][t][q] = 0.0f;
+  const int nk = (int)(K / kGBK);
+  // loads of step snext into (wa, wb), then the multiplies of step s from (ra, rb) unless s is past the end
+  auto step = [&](int s, int snext, uint8_t* __restrict__ wa, uint8_t* __restrict__ wb,
+                  const uint8_t* __restrict__ ra, const uint8_t* __restrict__ rb) {
+    load(snext < nk ? snext : nk - 1, wa, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s < nk) {
+      i8v a[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt] = frag(ra + (mt * 32 + l32) * kR);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const i8v b = frag(rb + (64 * wave + 32 * t + l32) * kR);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt], b, acc[mt][t], 0, 0, 0, 127, 0, 127);
+      }
+    }
+    // the loads of step s + 1 (issued one step earlier) are complete once at most this step's 6 are
+    // in flight; then the barrier publishes every wave's rows
+    __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6), expcnt and lgkmcnt not waited for
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  load(0, A0, B0);
+  load(1 < nk ? 1 : 0, A1, B1);
+  __builtin_amdgcn_s_waitcnt(0x0F76);  // step 0's loads complete
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  for (int s = 0; s < nk; s += 3) {
+    step(s, s + 2, A2, B2, A0, B0);
+    step(s + 1, s + 3, A0, B0, A1, B1);
+    step(s + 2, s + 4, A1, B1, A2, B2);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no load in flight at the end
+
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ro = mt * 32 + 8 * q + 4 * lh + j;
+        if (ro >= nrows) continue;
+        const int r = 4 * q + j;
+        float* yr = out + (int64_t)(row0 + ro) * H;
+        const float* ws = wsc + (int64_t)e * H;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int64_t col = c0 + 64 * wave + 32 * t + l32;
+          yr[col] = acc[mt][t][r] * a_rs[row0 + ro] * ws[col];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const int* __restrict__ pair_row,
@@ -1766,6 +1896,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #ifndef BSM_FP8_KB
 #define BSM_FP8_KB 64
 #endif
+#ifndef BSM_F8_DOWN3
+#define BSM_F8_DOWN3 1  // FP8 down projection: three-stage direct-to-LDS pipeline (0: register staging)
+#endif
 #ifndef BSM_FP8_MFMA
 #define BSM_FP8_MFMA 1  // down projection of many-row experts on the FP8 matrix cores (0: decoded to FP16)
 #endif
@@ -1803,8 +1936,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
         k_skinny<false, false, 32, BSM_SKINNY_NT, false, BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(
             hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
       if (many)
-        k_gemm_f8_down<<<dim3((unsigned)(a.H / kGBN), (unsigned)L.max_tiles_w), 256, 0, st>>>(
-          h_codes, hsc, a.w2_codes, w2f, tiles_w, ntiles_w, a.I, a.H, y);
+        (BSM_F8_DOWN3 ? k_gemm_f8_down3 : k_gemm_f8_down)<<<dim3((unsigned)(a.H / kGBN), (unsigned)L.max_tiles_w),
+                                                           256, 0, st>>>(h_codes, hsc, a.w2_codes, w2f, tiles_w,
+                                                                         ntiles_w, a.I, a.H, y);
     }
   }
 #undef BSM_G1
