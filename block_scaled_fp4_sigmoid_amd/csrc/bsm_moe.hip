@@ -578,6 +578,124 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny(const _Float
 }
 
 // ---------------------------------------------------------------------------
+// NVFP4 grouped GEMM for few rows per expert, activation rows staged in large
+// chunks of K ("rows"): the lane mapping, weight streaming (two register sets
+// of codes, one super-step ahead), scale handling and MFMA steps of k_skinny,
+// but the tile's activation rows go to LDS for kc super-steps at a time
+// (kc from the rows and kRowsLds bytes of LDS; the whole K when the tile has
+// few rows, as at decode), so the waves run those super-steps without a
+// barrier: a wave waiting for its weights does not hold the other three.
+// ---------------------------------------------------------------------------
+constexpr int kRowsLds = 44 * 1024;  // LDS bytes for the staged rows (three workgroups per CU)
+
+template <bool G1, int NT, bool A16 = false>
+__global__ __launch_bounds__(256, 3) void k_skinny_rows(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
+                                                        int topk, const float* __restrict__ a_gs,
+                                                        const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc,
+                                                        const float* __restrict__ wgs, const int4* __restrict__ tiles,
+                                                        const int* __restrict__ ntiles, int64_t K, int64_t H, int64_t I,
+                                                        float* __restrict__ out, uint32_t* __restrict__ h_amax) {
+  constexpr int KB = 128;
+  constexpr int KS = 4 * KB;  // k per super-step
+  constexpr int VPU = SkGeom<true>::VPU;
+  constexpr int kSV = KB / 32;
+  constexpr int cstep = KS / 2, sstep = KS / 16;
+  __shared__ __attribute__((aligned(16))) _Float16 Ar[kRowsLds / 2];
+  if ((int)blockIdx.y >= *ntiles) return;
+  const int4 ti = tiles[blockIdx.y];
+  const int e = ti.x, row0 = ti.y, nrows = ti.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, g = lane >> 4;
+  const int nsteps = (int)(K / KS);
+  // super-steps per chunk (even, at least 2): nrows rows of kc * KS values, +8 f16 per row so the
+  // fragment reads of different rows start on different banks
+  int kc = (int)((kRowsLds / nrows / 2 - 8) / KS) & ~1;
+  kc = kc < 2 ? 2 : kc;
+  const int rstride = kc * KS + 8;  // f16
+  // this lane's A row (rows past nrows read the last real row: their outputs are never stored)
+  const _Float16* arow = Ar + (m < nrows ? m : nrows - 1) * rstride + VPU * g;
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * (G1 ? 8 * NT : 16 * NT);
+  const uint8_t* crow[NT];
+  const uint8_t* srow[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int64_t r = G1 ? (int64_t)e * 2 * I + (j >= NT / 2 ? I : 0) + n0 + 16 * (j % (NT / 2)) + m
+                         : (int64_t)e * H + n0 + 16 * j + m;
+    crow[j] = wc + r * (K / 2) + 16 * g;
+    srow[j] = wsc + r * (K / 16) + (int64_t)sstep * g;  // lane g: super-step 4q + g
+  }
+  f4v acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
+  const uint32_t selA = (uint32_t)((g & 1) * 2) * 0x0101u, selB = selA + 0x0101u;
+  const int ghi = g >> 1;
+  BRegs<true, KB> b0[NT], b1[NT];
+  SRegs<KB> sc[NT];
+  uint32_t sdw[NT][kSV];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) b_load<true, KB>(crow[j], b0[j]);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) s_load<KB>(srow[j], g < nsteps, sc[j]);
+  // one super-step: scale bytes from lane group (ST & 3) (which reloads its span for ST + 4), the next
+  // super-step's codes into BN, the multiplies from the staged rows
+#define BSM_SKR_STEP(ST, BC, BN)                                                                       \
+  {                                                                                                    \
+    const int gi = (ST) & 3;                                                                           \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j) s_fetch<KB>(sc[j], (m + 16 * gi) * 4, ghi, sdw[j]); \
+    if (g == gi && (ST) + 4 < nsteps) {                                                                \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                  \
+        s_load<KB>(srow[j] + (int64_t)((ST) + 4 - g) * sstep, true, sc[j]);                            \
+    }                                                                                                  \
+    if ((ST) + 1 < nsteps) {                                                                           \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                  \
+        b_load<true, KB>(crow[j] + ((ST) + 1) * (int64_t)cstep, BN[j]);                                \
+    }                                                                                                  \
+    sk_mma_step<true, KB, NT, 0, A16>(arow + ((ST) - c0) * KS, BC, sdw, selA, selB, acc);               \
+  }
+  for (int c0 = 0; c0 < nsteps; c0 += kc) {
+    const int c1 = c0 + kc < nsteps ? c0 + kc : nsteps;
+    // stage rows x [c0 KS, c1 KS): 16-byte pieces, consecutive threads along a row
+    if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
+    const int pr = (c1 - c0) * KS / 8;  // pieces per row
+    for (int q = tid; q < nrows * pr; q += 256) {
+      const int r = q / pr, p = q - r * pr;
+      const _Float16* src = (G1 ? act + (int64_t)(row_pair[row0 + r] / topk) * K : act + (int64_t)(row0 + r) * K) +
+                            (int64_t)c0 * KS + 8 * p;
+      *reinterpret_cast<uint4*>(Ar + r * rstride + 8 * p) = *reinterpret_cast<const uint4*>(src);
+    }
+    __syncthreads();
+    for (int st = c0; st < c1; st += 2) {
+      BSM_SKR_STEP(st, b0, b1)
+      if (st + 1 < c1) BSM_SKR_STEP(st + 1, b1, b0)
+    }
+  }
+#undef BSM_SKR_STEP
+
+  float hmax = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ro = 4 * g + r;
+    if (ro >= nrows) continue;
+    if (G1) {
+#pragma unroll
+      for (int q = 0; q < NT / 2; ++q) {
+        const int64_t col = n0 + 16 * q + m;
+        const float ag = A16 ? 1.0f : a_gs[0];  // weight-only: BF16 activations carry no scale
+        const float h = silu_mul(acc[q][r] * (ag * wgs[2 * e]), acc[NT / 2 + q][r] * (ag * wgs[2 * e + 1]));
+        out[(int64_t)(row0 + ro) * I + col] = h;
+        hmax = fmaxf(hmax, fabsf(h));
+      }
+    } else {
+      float* yr = out + (int64_t)(row0 + ro) * H + n0 + m;
+      const float sc = (A16 ? 1.0f : a_gs[0]) * wgs[e];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) yr[16 * j] = acc[j][r] * sc;
+    }
+  }
+  if constexpr (G1) wg_amax_atomic(hmax, h_amax);
+}
+
+// ---------------------------------------------------------------------------
 // Dense FP8 GEMM for at most 64 rows (decode-sized dense projections and the
 // dense SwiGLU MLP, one weight matrix): every workgroup covers all rows, so
 // each weight byte is streamed from HBM once (the 16-row tiles of k_skinny
@@ -1804,6 +1922,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #ifndef BSM_SKINNY_DEPTH_FP8
 #define BSM_SKINNY_DEPTH_FP8 2
 #endif
+#ifndef BSM_SKINNY_ROWS
+#define BSM_SKINNY_ROWS 1  // NVFP4 / W4A16: activation rows staged in chunks of K, no barrier per super-step
+#endif
   const dim3 g1((unsigned)(a.I / (32 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 8*NT h columns
   const dim3 g2((unsigned)(a.H / (64 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 16*NT y columns
 #ifndef BSM_PREFILL_BIG
@@ -1836,6 +1957,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   const uint8_t* w2s = reinterpret_cast<const uint8_t*>(a.w2_scales);
   const float* xrs = reinterpret_cast<const float*>(a.x_scales);
 #define BSM_G1(NV, KB)                                                                                          \
+  if (BSM_SKINNY_ROWS && NV && KB == 128)                                                                       \
+    k_skinny_rows<true, BSM_SKINNY_NT><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, a.w13_codes, w13s,    \
+                                                           a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32, h_amax); \
+  else                                                                                                          \
   k_skinny<NV, true, KB, BSM_SKINNY_NT, false, NV ? BSM_SKINNY_DEPTH : BSM_SKINNY_DEPTH_FP8><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes,  \
                                                             w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I,     \
                                                             h_f32, h_amax);                                   \
@@ -1843,6 +1968,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
       act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,                                        \
                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
 #define BSM_G2(NV, KB)                                                                                         \
+  if (BSM_SKINNY_ROWS && NV && KB == 128)                                                                      \
+    k_skinny_rows<false, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, a.w2_codes, w2s,      \
+                                                            a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);  \
+  else                                                                                                         \
   k_skinny<NV, false, KB, BSM_SKINNY_NT, false, NV ? BSM_SKINNY_DEPTH : BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
                                               a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
   if (many) (big_dn ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                    \
@@ -1855,6 +1984,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   if (a.a16) {
     // weight-only W4A16: BF16 activations, NVFP4 weights decoded to BF16, h rounded to BF16
 #define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K, KB)                                               \
+  if (BSM_SKINNY_ROWS && KB == 128)                                                                            \
+    k_skinny_rows<G, BSM_SKINNY_NT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, W, WS, WGS, tiles, \
+                                                                ntiles, K, a.H, a.I, OUT, h_amax);             \
+  else                                                                                                         \
   k_skinny<true, G, KB, BSM_SKINNY_NT, true, BSM_SKINNY_DEPTH><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, \
                                                                    tiles, ntiles, K, a.H, a.I, OUT, h_amax);   \
   if (many) ((G ? BSM_PREFILL_BIG : big_dn) ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(        \
