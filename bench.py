@@ -148,13 +148,16 @@ def summarize_pmc(fetch_csv, write_csv, command, bench_json=None):
         assert keys, "kernel not found in the counter CSV"
         return max(keys, key=lambda k: len(d[k]))
 
-    gemm = pick(fetch, lambda k: "k_skinny" in k and "ILb1ELb1ELi128" in k)
+    # the decode gate/up kernel: the chunk-staged NVFP4 one, else the per-super-step one
+    rows = [k for k in fetch if "k_skinny_rowsILb1ELi2ELb0E" in k]
+    gemm = pick(fetch, (lambda k: k in rows) if rows else (lambda k: "k_skinny" in k and "ILb1ELb1ELi128" in k))
+    label = "k_skinny_rows<true,2,false>" if rows else "k_skinny<true,true,128,2,false,1>"
     copyk = max((k for k in fetch if "elementwise" in k or "vectorized" in k), key=lambda k: max(fetch[k]))
     f_copy, w_copy = max(fetch[copyk]), max(write[copyk])
     sf, sw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     fb = float(np.mean(fetch[gemm])) * sf
     wb = float(np.mean(write[gemm])) * sw
-    res = {"kernel": "k_skinny<NVFP4, gate/up> (decode-64)", "dispatches": len(fetch[gemm]),
+    res = {"kernel": label + " gate/up (decode-64 NVFP4)", "dispatches": len(fetch[gemm]),
            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "traffic_bytes_per_launch": fb + wb,
            "copy_kernel": copyk[:80], "copy_counter_fetch": f_copy, "copy_counter_write": w_copy,
            "scale_fetch": sf, "scale_write": sw, "gemm_source_sha256": _source_digest(), "command": command}
@@ -165,7 +168,7 @@ def summarize_pmc(fetch_csv, write_csv, command, bench_json=None):
         with open(bench_json) as f:
             alg = json.loads(f.readline())["roofline"]["algorithmic_bytes_per_launch"]
     lines = [
-        "# HBM traffic of the gate/up GEMM (k_skinny<true,true,128,2,false,1>) at decode-64 NVFP4, MI355X",
+        f"# HBM traffic of the gate/up GEMM ({label}) at decode-64 NVFP4, MI355X",
         "# command (two runs, one counter each):",
         "#   " + command.replace(" (then WRITE_SIZE)", "").replace("fetch|write", "fetch"),
         "#   " + command.replace("FETCH_SIZE (then WRITE_SIZE)", "WRITE_SIZE").replace("fetch|write", "write"),
