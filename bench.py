@@ -68,9 +68,16 @@ COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read and 1 GiB written
 
 
 def _source_digest():
+    """SHA-256 of the kernel source's code: comments and blank space are dropped, so editing only
+    comments keeps the counter record valid (the source holds no string literal with //)."""
     import hashlib
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(GEMM_SOURCE) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    code = "\n".join(" ".join(line.split()) for line in src.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()
 
 
 def copy_calibration(dev):

@@ -14,30 +14,38 @@
 // Exactness of the operands on the matrix cores: a decoded NVFP4 element
 // q * s_b has at most 6 significant bits (E2M1: 2, E4M3: 4) and lies in
 // [2^-10, 2688]; an E4M3 element has 4 significant bits and lies in
-// [2^-9, 448].  Both are exact in FP16, so every GEMM decodes its operands to
-// FP16 and runs v_mfma_f32_16x16x32_f16 with FP32 accumulation; the global
+// [2^-9, 448].  Both are exact in FP16, so the GEMMs decode their operands to
+// FP16 (weight-only W4A16: BF16) and run FP16 MFMA with FP32 accumulation
+// (16x16x32 in the few-row kernels, 32x32x16 in the many-row one); the global
 // scales (NVFP4) or the per-row x per-column scales (FP8) multiply the FP32
-// accumulator in the epilogue.  (The FP8 matrix-core instructions were not
-// used: their internal accumulation measured about 2^-13 relative error on
-// sums that FP16 inputs with FP32 accumulation carry exactly.)
+// accumulator in the epilogue.  One exception: the FP8 down projection of
+// many-row experts runs the FP8 matrix cores on the raw E4M3 codes.  Their
+// block accumulation is not exact (about 2^-13 relative per 64 products), which
+// y, never re-quantized, absorbs; the gate/up projection, whose h is
+// re-quantized, stays on FP16.
 //
 // Pipeline (all on the caller's stream, no host synchronization):
 //   k_perm_masks   per 64-token chunk: LDS bit mask of the chunk's tokens for
 //                  every expert (atomicOr, order independent) and its popcount
 //   k_perm_scan    per expert: prefix counts over chunks, counts, offsets, and
 //                  two device-side tile lists: experts with <= 64 rows get
-//                  16-row tiles (skinny kernel), larger ones 128-row tiles
-//                  (wide kernel); clears the h amax word
+//                  16-row tiles (skinny kernels), larger ones 128-row tiles
+//                  (many-row kernels); clears the h amax word
 //   k_perm_rows    row of every (token, slot) pair; rows of an expert are in
 //                  token order (stable)
 //   k_perm_small   all three in one workgroup when the batch is one chunk
 //   k_decode_act   activation codes -> FP16 q * s_b (once per call)
-//   k_skinny<G1>   gate/up: epilogue h = silu(g) * u (FP32) to the workspace,
-//                  max |h| into one atomicMax word (order independent)
-//   k_gemm_wide<G1> the same for 128-row tiles, LDS-staged
+//   k_skinny_rows<G1> (NVFP4, W4A16) / k_skinny<G1> (FP8)
+//                  gate/up for 16-row tiles: epilogue h = silu(g) * u (FP32)
+//                  to the workspace, max |h| into one atomicMax word (order
+//                  independent)
+//   k_gemm_big<G1> the same for 128-row tiles (128 x 256 per workgroup,
+//                  32x32x16 MFMA; k_gemm_wide is the 16x16x32 fallback)
+//   k_dense_f8<G1> FP8 with one expert and at most 64 rows (dense layers)
 //   h quantize     NVFP4 with one global scale over all rows / FP8 per row,
 //                  plus the FP16 decoded copy the down GEMM reads
-//   k_skinny<!G1>, k_gemm_wide<!G1>  down projection -> y (FP32)
+//   k_skinny_rows<!G1> / k_skinny<!G1>, k_gemm_big<!G1> (FP8: k_gemm_f8_down3)
+//                  down projection -> y (FP32)
 //   k_combine      out[t] = scale * sum_j w[t,j] * y[row(t,j)] (binary64 sum
 //                  in slot order, rounded once)
 //
