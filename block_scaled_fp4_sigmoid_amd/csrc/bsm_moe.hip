@@ -867,14 +867,29 @@ __global__ __launch_bounds__(256) void k_dense_reduce(const float* __restrict__ 
   }
 }
 
-// Split count of k_dense_f8: the grid stays within one round of resident workgroups (two per CU: the LDS
-// tile takes 66 KB), since a partly filled second round leaves most CUs idle; at least one super-step per
-// split, at most 16 splits.
+// Split count of k_dense_f8 (at least one super-step per split, at most 16).  A workgroup streams its
+// weights at a roughly fixed rate, so the time goes as (rounds of 512 resident workgroups: two per CU,
+// the LDS tile takes 66 KB) / splits, and a partly filled last round costs a whole round.  Up to 256
+// column blocks: as many splits as fill one round.  More (the dense MLP's gate/up, 320 blocks): the
+// count with the fewest rounds per split, charging 1 % per split for the partial sums the reduction
+// reads (320 blocks: 3 splits, 960 workgroups in two rounds).
 inline int dense_splits(int64_t ncb, int64_t nss) {
-  int64_t sp = 512 / ncb;
-  if (sp > 16) sp = 16;
-  if (sp > nss) sp = nss;
-  return (int)(sp < 1 ? 1 : sp);
+  if (ncb <= 256) {
+    int64_t sp = 512 / ncb;
+    if (sp > 16) sp = 16;
+    if (sp > nss) sp = nss;
+    return (int)(sp < 1 ? 1 : sp);
+  }
+  int best = 1;
+  double best_t = 1e30;
+  for (int sp = 1; sp <= 16 && sp <= nss; ++sp) {
+    const double t = (double)((ncb * sp + 511) / 512) / sp + 0.01 * sp;
+    if (t < best_t - 1e-9) {
+      best_t = t;
+      best = sp;
+    }
+  }
+  return best;
 }
 constexpr int kDenseMaxSplits = 16;
 
