@@ -596,18 +596,18 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny(const _Float
 // ---------------------------------------------------------------------------
 constexpr int kRowsLds = 44 * 1024;  // LDS bytes for the staged rows (three workgroups per CU)
 
-template <bool G1, int NT, bool A16 = false>
-__global__ __launch_bounds__(256, 3) void k_skinny_rows(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
-                                                        int topk, const float* __restrict__ a_gs,
-                                                        const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc,
-                                                        const float* __restrict__ wgs, const int4* __restrict__ tiles,
-                                                        const int* __restrict__ ntiles, int64_t K, int64_t H, int64_t I,
-                                                        float* __restrict__ out, uint32_t* __restrict__ h_amax) {
-  constexpr int KB = 128;
+template <bool NV, bool G1, int NT, bool A16 = false, int DEPTH = 1>
+__global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
+    const _Float16* __restrict__ act, const int* __restrict__ row_pair, int topk, const float* __restrict__ a_gs,
+    const float* __restrict__ a_rs, const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc,
+    const float* __restrict__ wgs, const int4* __restrict__ tiles, const int* __restrict__ ntiles, int64_t K, int64_t H,
+    int64_t I, float* __restrict__ out, uint32_t* __restrict__ h_amax) {
+  constexpr int KB = NV ? 128 : 64;
   constexpr int KS = 4 * KB;  // k per super-step
-  constexpr int VPU = SkGeom<true>::VPU;
+  constexpr int VPU = SkGeom<NV>::VPU;
   constexpr int kSV = KB / 32;
-  constexpr int cstep = KS / 2, sstep = KS / 16;
+  constexpr int cstep = NV ? KS / 2 : KS, sstep = KS / 16;  // code (NVFP4: and scale) bytes per row and super-step
+  constexpr int kU = DEPTH + 1;  // super-steps per unrolled iteration (one per register set)
   __shared__ __attribute__((aligned(16))) _Float16 Ar[kRowsLds / 2];
   if ((int)blockIdx.y >= *ntiles) return;
   const int4 ti = tiles[blockIdx.y];
@@ -615,50 +615,61 @@ __global__ __launch_bounds__(256, 3) void k_skinny_rows(const _Float16* __restri
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, g = lane >> 4;
   const int nsteps = (int)(K / KS);
-  // super-steps per chunk (even, at least 2): nrows rows of kc * KS values, +8 f16 per row so the
+  // super-steps per chunk (a multiple of kU): nrows rows of kc * KS values, +8 f16 per row so the
   // fragment reads of different rows start on different banks
-  int kc = (int)((kRowsLds / nrows / 2 - 8) / KS) & ~1;
-  kc = kc < 2 ? 2 : kc;
+  int kc = (int)((kRowsLds / nrows / 2 - 8) / KS) / kU * kU;
+  kc = kc < kU ? kU : kc;
   const int rstride = kc * KS + 8;  // f16
   // this lane's A row (rows past nrows read the last real row: their outputs are never stored)
   const _Float16* arow = Ar + (m < nrows ? m : nrows - 1) * rstride + VPU * g;
   const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * (G1 ? 8 * NT : 16 * NT);
+  const int64_t cbytes = NV ? K / 2 : K;
   const uint8_t* crow[NT];
   const uint8_t* srow[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int64_t r = G1 ? (int64_t)e * 2 * I + (j >= NT / 2 ? I : 0) + n0 + 16 * (j % (NT / 2)) + m
                          : (int64_t)e * H + n0 + 16 * j + m;
-    crow[j] = wc + r * (K / 2) + 16 * g;
-    srow[j] = wsc + r * (K / 16) + (int64_t)sstep * g;  // lane g: super-step 4q + g
+    crow[j] = wc + r * cbytes + 16 * g;
+    srow[j] = NV ? wsc + r * (K / 16) + (int64_t)sstep * g : nullptr;  // lane g: super-step 4q + g
   }
   f4v acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f4v{0.f, 0.f, 0.f, 0.f};
   const uint32_t selA = (uint32_t)((g & 1) * 2) * 0x0101u, selB = selA + 0x0101u;
   const int ghi = g >> 1;
-  BRegs<true, KB> b0[NT], b1[NT];
+  BRegs<NV, KB> b0[NT], b1[NT], b2[DEPTH > 1 ? NT : 1];
   SRegs<KB> sc[NT];
-  uint32_t sdw[NT][kSV];
+  uint32_t sdw[NT][kSV > 0 ? kSV : 1];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) b_load<true, KB>(crow[j], b0[j]);
+  for (int j = 0; j < NT; ++j) b_load<NV, KB>(crow[j], b0[j]);
+  if constexpr (DEPTH > 1) {
+    if (nsteps > 1) {
 #pragma unroll
-  for (int j = 0; j < NT; ++j) s_load<KB>(srow[j], g < nsteps, sc[j]);
-  // one super-step: scale bytes from lane group (ST & 3) (which reloads its span for ST + 4), the next
-  // super-step's codes into BN, the multiplies from the staged rows
+      for (int j = 0; j < NT; ++j) b_load<NV, KB>(crow[j] + cstep, b1[j]);
+    }
+  }
+  if constexpr (NV) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) s_load<KB>(srow[j], g < nsteps, sc[j]);
+  }
+  // one super-step: NVFP4 scale bytes from lane group (ST & 3) (which reloads its span for ST + 4), the
+  // codes of super-step ST + DEPTH into BN, the multiplies from the staged rows
 #define BSM_SKR_STEP(ST, BC, BN)                                                                       \
   {                                                                                                    \
-    const int gi = (ST) & 3;                                                                           \
-    _Pragma("unroll") for (int j = 0; j < NT; ++j) s_fetch<KB>(sc[j], (m + 16 * gi) * 4, ghi, sdw[j]); \
-    if (g == gi && (ST) + 4 < nsteps) {                                                                \
-      _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                  \
-        s_load<KB>(srow[j] + (int64_t)((ST) + 4 - g) * sstep, true, sc[j]);                            \
+    if constexpr (NV) {                                                                                \
+      const int gi = (ST) & 3;                                                                         \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j) s_fetch<KB>(sc[j], (m + 16 * gi) * 4, ghi, sdw[j]); \
+      if (g == gi && (ST) + 4 < nsteps) {                                                              \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                \
+          s_load<KB>(srow[j] + (int64_t)((ST) + 4 - g) * sstep, true, sc[j]);                          \
+      }                                                                                                \
     }                                                                                                  \
-    if ((ST) + 1 < nsteps) {                                                                           \
+    if ((ST) + DEPTH < nsteps) {                                                                       \
       _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                  \
-        b_load<true, KB>(crow[j] + ((ST) + 1) * (int64_t)cstep, BN[j]);                                \
+        b_load<NV, KB>(crow[j] + ((ST) + DEPTH) * (int64_t)cstep, BN[j]);                              \
     }                                                                                                  \
-    sk_mma_step<true, KB, NT, 0, A16>(arow + ((ST) - c0) * KS, BC, sdw, selA, selB, acc);               \
+    sk_mma_step<NV, KB, NT, 0, A16>(arow + ((ST) - c0) * KS, BC, sdw, selA, selB, acc);                 \
   }
   for (int c0 = 0; c0 < nsteps; c0 += kc) {
     const int c1 = c0 + kc < nsteps ? c0 + kc : nsteps;
@@ -672,9 +683,17 @@ __global__ __launch_bounds__(256, 3) void k_skinny_rows(const _Float16* __restri
       *reinterpret_cast<uint4*>(Ar + r * rstride + 8 * p) = *reinterpret_cast<const uint4*>(src);
     }
     __syncthreads();
-    for (int st = c0; st < c1; st += 2) {
-      BSM_SKR_STEP(st, b0, b1)
-      if (st + 1 < c1) BSM_SKR_STEP(st + 1, b1, b0)
+    if constexpr (DEPTH == 1) {
+      for (int st = c0; st < c1; st += 2) {
+        BSM_SKR_STEP(st, b0, b1)
+        if (st + 1 < c1) BSM_SKR_STEP(st + 1, b1, b0)
+      }
+    } else {  // super-step st multiplies set st % 3 and loads st + 2 into set (st + 2) % 3
+      for (int st = c0; st < c1; st += 3) {
+        BSM_SKR_STEP(st, b0, b2)
+        if (st + 1 < c1) BSM_SKR_STEP(st + 1, b1, b0)
+        if (st + 2 < c1) BSM_SKR_STEP(st + 2, b2, b1)
+      }
     }
   }
 #undef BSM_SKR_STEP
@@ -688,19 +707,36 @@ __global__ __launch_bounds__(256, 3) void k_skinny_rows(const _Float16* __restri
 #pragma unroll
       for (int q = 0; q < NT / 2; ++q) {
         const int64_t col = n0 + 16 * q + m;
-        const float ag = A16 ? 1.0f : a_gs[0];  // weight-only: BF16 activations carry no scale
-        const float h = silu_mul(acc[q][r] * (ag * wgs[2 * e]), acc[NT / 2 + q][r] * (ag * wgs[2 * e + 1]));
+        float sg, su;
+        if (NV) {
+          const float ag = A16 ? 1.0f : a_gs[0];  // weight-only: BF16 activations carry no scale
+          sg = ag * wgs[2 * e];
+          su = ag * wgs[2 * e + 1];
+        } else {
+          const float sx = a_rs[row_pair[row0 + ro] / topk];
+          const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
+          sg = sx * ws[col];
+          su = sx * ws[I + col];
+        }
+        const float h = silu_mul(acc[q][r] * sg, acc[NT / 2 + q][r] * su);
         out[(int64_t)(row0 + ro) * I + col] = h;
         hmax = fmaxf(hmax, fabsf(h));
       }
     } else {
       float* yr = out + (int64_t)(row0 + ro) * H + n0 + m;
-      const float sc = (A16 ? 1.0f : a_gs[0]) * wgs[e];
+      if (NV) {
+        const float sc = (A16 ? 1.0f : a_gs[0]) * wgs[e];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) yr[16 * j] = acc[j][r] * sc;
+        for (int j = 0; j < NT; ++j) yr[16 * j] = acc[j][r] * sc;
+      } else {
+        const float sa = a_rs[row0 + ro];
+        const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * H + n0 + m;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) yr[16 * j] = acc[j][r] * sa * ws[16 * j];
+      }
     }
   }
-  if constexpr (G1) wg_amax_atomic(hmax, h_amax);
+  if constexpr (G1 && NV) wg_amax_atomic(hmax, h_amax);
 }
 
 // ---------------------------------------------------------------------------
@@ -1946,7 +1982,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #define BSM_SKINNY_DEPTH_FP8 2
 #endif
 #ifndef BSM_SKINNY_ROWS
-#define BSM_SKINNY_ROWS 1  // NVFP4 / W4A16: activation rows staged in chunks of K, no barrier per super-step
+#define BSM_SKINNY_ROWS 1  // few-row experts: activation rows staged in chunks of K, no barrier per super-step
+#endif
+#ifndef BSM_SKR_DEPTH_FP8
+#define BSM_SKR_DEPTH_FP8 2  // FP8: super-steps of weight codes in flight per lane in k_skinny_rows
 #endif
   const dim3 g1((unsigned)(a.I / (32 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 8*NT h columns
   const dim3 g2((unsigned)(a.H / (64 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 16*NT y columns
@@ -1980,9 +2019,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   const uint8_t* w2s = reinterpret_cast<const uint8_t*>(a.w2_scales);
   const float* xrs = reinterpret_cast<const float*>(a.x_scales);
 #define BSM_G1(NV, KB)                                                                                          \
-  if (BSM_SKINNY_ROWS && NV && KB == 128)                                                                       \
-    k_skinny_rows<true, BSM_SKINNY_NT><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, a.w13_codes, w13s,    \
-                                                           a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32, h_amax); \
+  if (BSM_SKINNY_ROWS && KB == (NV ? 128 : BSM_FP8_KB))                                                        \
+    k_skinny_rows<NV, true, BSM_SKINNY_NT, false, NV ? 1 : BSM_SKR_DEPTH_FP8><<<g1, 256, 0, st>>>(                               \
+        act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32,    \
+        h_amax);                                                                                                \
   else                                                                                                          \
   k_skinny<NV, true, KB, BSM_SKINNY_NT, false, NV ? BSM_SKINNY_DEPTH : BSM_SKINNY_DEPTH_FP8><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes,  \
                                                             w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I,     \
@@ -1991,9 +2031,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
       act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,                                        \
                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
 #define BSM_G2(NV, KB)                                                                                         \
-  if (BSM_SKINNY_ROWS && NV && KB == 128)                                                                      \
-    k_skinny_rows<false, BSM_SKINNY_NT><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, a.w2_codes, w2s,      \
-                                                            a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);  \
+  if (BSM_SKINNY_ROWS && KB == (NV ? 128 : BSM_FP8_KB))                                                       \
+    k_skinny_rows<NV, false, BSM_SKINNY_NT, false, NV ? 1 : BSM_SKR_DEPTH_FP8><<<g2, 256, 0, st>>>(                             \
+        hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), a.w2_codes, w2s, a.w2_gs, tiles, \
+        ntiles, a.I, a.H, a.I, y, h_amax);                                                                     \
   else                                                                                                         \
   k_skinny<NV, false, KB, BSM_SKINNY_NT, false, NV ? BSM_SKINNY_DEPTH : BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
                                               a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
@@ -2008,8 +2049,8 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     // weight-only W4A16: BF16 activations, NVFP4 weights decoded to BF16, h rounded to BF16
 #define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K, KB)                                               \
   if (BSM_SKINNY_ROWS && KB == 128)                                                                            \
-    k_skinny_rows<G, BSM_SKINNY_NT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, W, WS, WGS, tiles, \
-                                                                ntiles, K, a.H, a.I, OUT, h_amax);             \
+    k_skinny_rows<true, G, BSM_SKINNY_NT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS,   \
+                                                                      WGS, tiles, ntiles, K, a.H, a.I, OUT, h_amax); \
   else                                                                                                         \
   k_skinny<true, G, KB, BSM_SKINNY_NT, true, BSM_SKINNY_DEPTH><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, \
                                                                    tiles, ntiles, K, a.H, a.I, OUT, h_amax);   \
@@ -2085,7 +2126,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     } else {
       // few-row experts: E4M3 decoded to FP16 next to the weight stream; many-row experts: FP8 matrix cores
       const float* hsc = reinterpret_cast<const float*>(h_scales);
-      if (a.I % (4 * BSM_FP8_KB) == 0)
+      if (a.I % (4 * BSM_FP8_KB) == 0 && BSM_SKINNY_ROWS && BSM_FP8_KB == 64)
+        k_skinny_rows<false, false, BSM_SKINNY_NT, false, BSM_SKR_DEPTH_FP8><<<g2, 256, 0, st>>>(
+            hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
+      else if (a.I % (4 * BSM_FP8_KB) == 0)
         k_skinny<false, false, BSM_FP8_KB, BSM_SKINNY_NT, false, BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(
             hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
       else
