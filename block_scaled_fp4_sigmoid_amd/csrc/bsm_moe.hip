@@ -35,7 +35,7 @@
 //                  token order (stable)
 //   k_perm_small   all three in one workgroup when the batch is one chunk
 //   k_decode_act   activation codes -> FP16 q * s_b (once per call)
-//   k_skinny_rows<G1> (NVFP4, W4A16) / k_skinny<G1> (FP8)
+//   k_skinny_rows<G1> (k_skinny<G1> when K is not a multiple of the super-step)
 //                  gate/up for 16-row tiles: epilogue h = silu(g) * u (FP32)
 //                  to the workspace, max |h| into one atomicMax word (order
 //                  independent)
