@@ -156,9 +156,9 @@ def summarize_pmc(fetch_csv, write_csv, command, bench_json=None):
         return max(keys, key=lambda k: len(d[k]))
 
     # the decode gate/up kernel: the chunk-staged NVFP4 one, else the per-super-step one
-    rows = [k for k in fetch if "k_skinny_rowsILb1ELi2ELb0E" in k]
+    rows = [k for k in fetch if "k_skinny_rowsILb1ELb1ELi2ELb0E" in k]  # <NVFP4, gate/up, NT 2, not W4A16>
     gemm = pick(fetch, (lambda k: k in rows) if rows else (lambda k: "k_skinny" in k and "ILb1ELb1ELi128" in k))
-    label = "k_skinny_rows<true,2,false>" if rows else "k_skinny<true,true,128,2,false,1>"
+    label = "k_skinny_rows<true,true,2,false,1>" if rows else "k_skinny<true,true,128,2,false,1>"
     copyk = max((k for k in fetch if "elementwise" in k or "vectorized" in k), key=lambda k: max(fetch[k]))
     f_copy, w_copy = max(fetch[copyk]), max(write[copyk])
     sf, sw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
