@@ -243,6 +243,19 @@ def test_moe_mid_shapes_many_rows(gpu_lib, fmt):
     _many_tokens(gpu_lib, MID, fmt, MID.T)
 
 
+# Every expert has 35-61 rows here, so the few-row kernel gets full 16-row tiles; with K = 2048 (gate/up)
+# and 1024 (down) their staged activation rows come in several chunks of K (NVFP4: 2 super-steps of 512
+# per chunk at 16 rows, FP8: 3 of 256).
+SKC = W.LayerConfig("skinny-chunks", 8, T=200, H=2048, I=1024, E=8, n_group=2, topk_group=1, topk=2,
+                    router_fp32=True)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_moe_skinny_tiles_in_chunks(gpu_lib, fmt):
+    """Few-row experts with full 16-row tiles whose activation rows are staged in several chunks of K."""
+    _many_tokens(gpu_lib, SKC, fmt, SKC.T)
+
+
 def _many_tokens(gpu_lib, cfg, fmt, T):
     x, wr = W.activations(cfg, T=T), W.router_weights(cfg)
     masters, w13, w2 = host_masters(cfg)
