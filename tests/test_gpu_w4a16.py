@@ -79,6 +79,18 @@ def test_w4a16_mid_shapes_many_rows(gpu_lib):
     assert counts.min() > 64
 
 
+def test_w4a16_skinny_tiles_in_chunks(gpu_lib):
+    """Hidden 2048, intermediate 1024, 8 experts, 200 tokens: every expert at 35-61 rows, so the few-row
+    kernel gets full 16-row tiles whose BF16 activation rows are staged in several chunks of K."""
+    cfg = W.LayerConfig("skinny-chunks", 8, T=200, H=2048, I=1024, E=8, n_group=2, topk_group=1, topk=2,
+                        router_fp32=True)
+    x, wr = W.activations(cfg), W.router_weights(cfg)
+    masters, w13, w2 = host_masters(cfg)
+    gw = gpu_lib.quantize_expert_weights(w13, w2, "nvfp4")
+    counts = _check_layer(gpu_lib, cfg, cfg.T, x, wr, to_dev_f32(wr), oracle_experts(masters, "w4a16"), gw)
+    assert counts.max() <= 64 and counts.max() > 32
+
+
 def test_w4a16_deterministic_and_matches_w4a4_weights(gpu_lib):
     cfg = W.TINY
     x, wr = W.activations(cfg), W.router_weights(cfg)
