@@ -33,8 +33,14 @@
 //                 (double-double fallback), group top-2 sums, group
 //                 selection, iterative 64-bit (score, index) argmax,
 //                 normalization.
+//   k_select256   256 experts: the same selection, one wave per token with
+//                 four experts per lane and shuffles in place of LDS.
 
 #include "bsm_internal.h"
+
+#ifndef BSM_SELECT_WAVE
+#define BSM_SELECT_WAVE 1
+#endif
 
 namespace bsm {
 
@@ -728,6 +734,98 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
   }
 }
 
+// 256 experts, groups of a multiple of 4: one wave per token, four
+// consecutive experts per lane, so a group is gsz / 4 consecutive lanes.
+// Same results as k_select (the same exactly rounded sigmoid, binary32 sum of
+// the group's two best, (score, index) keys, binary32 running sum in output
+// order), with shuffles in place of LDS and barriers.
+constexpr int kSel4Tokens = 4;  // waves (tokens) per workgroup
+
+__device__ inline void top2_merge(float& a1, float& a2, float b1, float b2) {
+  // the two largest (as a multiset) of {a1 >= a2} and {b1 >= b2}
+  const bool ah = a1 >= b1;
+  const float n2 = ah ? (a2 >= b1 ? a2 : b1) : (a1 >= b2 ? a1 : b2);
+  a1 = ah ? a1 : b1;
+  a2 = n2;
+}
+
+__global__ __launch_bounds__(64 * kSel4Tokens) void k_select256(
+    const float* __restrict__ logits, int64_t T, int lpg, int topk_group, int topk, int32_t* __restrict__ ids,
+    float* __restrict__ wts, float* __restrict__ scores, const int* __restrict__ blk, int64_t nblk,
+    int* __restrict__ diag) {
+  constexpr int64_t E = 256;
+  __shared__ int s_cnt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (blockIdx.x == 0) {  // diagnostics: exact recomputations of all logits workgroups
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    int c = 0;
+    for (int64_t i = tid; i < nblk; i += 64 * kSel4Tokens) c += blk[i];
+    if (c) atomicAdd(&s_cnt, c);
+    __syncthreads();
+    if (tid == 0) diag[0] = s_cnt;
+  }
+  const int64_t t = (int64_t)blockIdx.x * kSel4Tokens + (tid >> 6);
+  if (t >= T) return;  // whole waves leave; no barrier follows
+  const float4 l4 = *reinterpret_cast<const float4*>(logits + t * E + 4 * lane);
+  bool f0, f1, f2, f3;
+  float sv[4] = {sigmoid_f32_exact(l4.x, &f0), sigmoid_f32_exact(l4.y, &f1), sigmoid_f32_exact(l4.z, &f2),
+                 sigmoid_f32_exact(l4.w, &f3)};
+  const int nslow = (f0 ? 0 : 1) + (f1 ? 0 : 1) + (f2 ? 0 : 1) + (f3 ? 0 : 1);
+  if (nslow) atomicAdd(&diag[1], nslow);
+  if (scores) *reinterpret_cast<float4*>(scores + t * E + 4 * lane) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+  // the group's two best: this lane's four, then a butterfly over the group's lanes
+  float t1 = -1.0f, t2 = -1.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (sv[i] > t1) {
+      t2 = t1;
+      t1 = sv[i];
+    } else if (sv[i] > t2) {
+      t2 = sv[i];
+    }
+  }
+  for (int o = 1; o < lpg; o <<= 1) {
+    const float b1 = __shfl_xor(t1, o, 64), b2 = __shfl_xor(t2, o, 64);
+    top2_merge(t1, t2, b1, b2);
+  }
+  const float gj = t1 + t2;
+  const int ng = 64 / lpg, my_g = lane / lpg;
+  int rank = 0;
+  for (int i = 0; i < ng; ++i) {
+    const float gi = __shfl(gj, i * lpg, 64);
+    rank += (gi > gj || (gi == gj && i < my_g)) ? 1 : 0;
+  }
+  const bool kept = rank < topk_group;
+  // (score, index) keys: larger score first, then lower index; 0 = not a candidate
+  uint64_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    key[i] = kept ? ((uint64_t)f2u(sv[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(4 * lane + i)) : 0ull;
+  int my_id = 0;
+  float my_s = 0.0f, ssum = 0.0f;
+  for (int r = 0; r < topk; ++r) {
+    uint64_t m = key[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) m = key[i] > m ? key[i] : m;
+    m = wave_max_u64(m);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
+    const float s = u2f((uint32_t)(m >> 32));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * lane + i == e) key[i] = 0ull;
+    ssum = (r == 0) ? s : ssum + s;
+    if (lane == r) {
+      my_id = e;
+      my_s = s;
+    }
+  }
+  if (lane < topk) {
+    ids[t * topk + lane] = my_id;
+    wts[t * topk + lane] = my_s / ssum;
+  }
+}
+
 __global__ void k_copy_diag(const int* src, int32_t* dst) {
   if (threadIdx.x < 4) dst[threadIdx.x] = src[threadIdx.x];
 }
@@ -755,6 +853,9 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   const unsigned nrb = (unsigned)(((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE));
   const dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
   const dim3 glz(gl.x, gl.y, (unsigned)L.ks);
+  // one wave per token needs 256 experts, groups of a multiple of 4 and an aligned scores row
+  const bool sel4 = BSM_SELECT_WAVE && E == 256 && (E / n_group) % 4 == 0 && topk <= 64 &&
+                    ((uintptr_t)scores & 15) == 0;
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
   if (L.rb) {                                                                                              \
     k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, L.nadd, logits, blk, diag);                    \
@@ -771,8 +872,12 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   }                                                                                                        \
   stage_mark(1, 1, st);                                                                                    \
   if (!L.rb) k_exact_list<XB, WB><<<kExactWgs, 128, 0, st>>>(x, w, E, H, norm, T, ulist, logits);          \
-  k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores, blk,    \
-                                                L.nblk, diag);
+  if (sel4)                                                                                                \
+    k_select256<<<(unsigned)((T + kSel4Tokens - 1) / kSel4Tokens), 64 * kSel4Tokens, 0, st>>>(                \
+        logits, T, (int)(E / n_group) / 4, topk_group, topk, ids, wts, scores, blk, L.nblk, diag);             \
+  else                                                                                                     \
+    k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores,     \
+                                                  blk, L.nblk, diag);
   if (xb && wb) {
     BSM_ROUTE_DISPATCH(true, true)
   } else if (xb && !wb) {

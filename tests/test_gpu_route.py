@@ -110,3 +110,19 @@ def test_route_tiled_ragged_with_fallbacks(gpu_lib, T, H, E, x_bf16):
     ids, wts, scores, diag = _run(gpu_lib, x, w, 8, 4, 8, x_bf16=x_bf16)
     _check((ids, wts, scores, diag), x, w, 8, 4, 8)
     assert diag[0] > 0  # the tiled kernel's exact fallback ran
+
+
+@pytest.mark.parametrize("G,kg,k", [(8, 4, 8), (1, 1, 32), (2, 1, 5), (16, 3, 8), (32, 32, 32), (64, 2, 8)])
+def test_route_256_experts_group_sizes(gpu_lib, G, kg, k):
+    """256 experts take the one-wave-per-token selection: groups of 4 to 256 experts (1 to 64 lanes), a ragged
+    last workgroup of tokens, equal logits in different groups, saturated scores and an all-zero token whose
+    group sums all tie."""
+    rng = np.random.default_rng(14 + G)
+    T, H, E = 37, 256, 256
+    x = W.to_bf16_f32(rng.standard_normal((T, H)).astype(np.float32))
+    wr = W.to_bf16_f32((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
+    wr[200] = wr[7]
+    wr[131] = wr[129]
+    wr[64:68] = wr[64] * 64
+    x[5] = 0.0
+    _check(_run(gpu_lib, x, wr, G, kg, k), x, wr, G, kg, k)
