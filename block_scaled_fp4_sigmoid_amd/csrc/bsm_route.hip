@@ -33,11 +33,21 @@
 //                 (double-double fallback), group top-2 sums, group
 //                 selection, iterative 64-bit (score, index) argmax,
 //                 normalization.
+//   k_slice8      large batches, bf16 x and w: per row an exponent bound, a
+//                 truncation residual, a norm bound, and four int8 digits of
+//                 every value
+//   k_logits_i8   large batches, bf16 x and w: the dot products as exact
+//                 int32 digit sums on the int8 matrix cores, rounded once;
+//                 rows with a residual prove the rounding by a bound or list
+//                 the logit for k_exact_list
 //   k_select256   256 experts: the same selection, one wave per token with
 //                 four experts per lane and shuffles in place of LDS.
 
 #include "bsm_internal.h"
 
+#ifndef BSM_ROUTE_I8
+#define BSM_ROUTE_I8 1
+#endif
 #ifndef BSM_SELECT_WAVE
 #define BSM_SELECT_WAVE 1
 #endif
@@ -53,8 +63,19 @@ constexpr int kRbE = 8;    // experts per workgroup of the small-batch logits ke
 constexpr int kRbK = 2048; // K covered by one pass of a small-batch workgroup (256 lanes x 8)
 constexpr int kExactWgs = 1024;  // workgroups sharing the list of logits recomputed exactly
 
+// bf16 x bf16 tiled path on the int8 matrix cores (see k_slice8 below)
+constexpr int kI8Rows = 64;       // tokens and experts per workgroup
+constexpr int kI8ChunkB = 128;    // digit bytes per row and chunk of 32 k: [half of 16 k][digit][16 values]
+constexpr int kI8Stage = 2;       // chunks per LDS stage
+constexpr int kI8Ld = kI8Stage * kI8ChunkB + 16;  // LDS bytes per row and stage (16-byte pad)
+constexpr int kI8MaxH = 16384;    // keeps every int32 diagonal sum below 2^31
+constexpr int kI8ZeroRow = -4096; // exponent bound recorded for a row without finite nonzero values
+
 struct RouteWs {
   size_t norm, lsb, part, ulist, logits, blk, diag, total;  // norm, lsb, part, ulist: tiled path only
+  size_t rexp, rres;  // int8 path: per-row exponent bound and truncation residual (dig shares part's space)
+  bool i8ok;          // the int8 path fits this shape (the launch also needs bf16 x and w)
+  int64_t ncp;        // int8 path: chunks of 32 k per row, rounded up to whole stages
   bool rb;    // small-batch kernel (full K per workgroup, lanes own K slices)
   int nadd;   // roundings along the longest summation path of one logit
   int64_t nblk;  // logits workgroups (one exact-recomputation count each)
@@ -85,8 +106,18 @@ RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
   if (!L.rb) o += align256(sizeof(double) * (size_t)(T + E));
   L.lsb = o;
   if (!L.rb) o += align256(sizeof(int) * (size_t)(T + E));
-  L.part = o;
-  if (!L.rb) o += align256(sizeof(double) * (size_t)L.ks * (size_t)T * (size_t)E);
+  L.i8ok = !L.rb && H % 16 == 0 && H <= kI8MaxH;
+  L.ncp = (((H + 31) / 32 + kI8Stage - 1) / kI8Stage) * kI8Stage;
+  L.part = o;  // binary64 partial sums, or the int8 path's digits of every row of x and w
+  if (!L.rb) {
+    const size_t pb = sizeof(double) * (size_t)L.ks * (size_t)T * (size_t)E;
+    const size_t db = L.i8ok ? (size_t)(T + E) * (size_t)L.ncp * kI8ChunkB : 0;
+    o += align256(pb > db ? pb : db);
+  }
+  L.rexp = o;
+  if (L.i8ok) o += align256(sizeof(int) * (size_t)(T + E));
+  L.rres = o;
+  if (L.i8ok) o += align256(sizeof(double) * (size_t)(T + E));
   L.ulist = o;  // count, then the flat indices of the logits left for exact recomputation
   if (!L.rb) o += align256(sizeof(int) * (size_t)(T * E + 1));
   L.logits = o;
@@ -616,6 +647,256 @@ __global__ __launch_bounds__(256) void k_logits_fin(int64_t T, int64_t E, int ks
   if (tid == 0) blk[blockIdx.y * gridDim.x + blockIdx.x] = n_unc;
 }
 
+// ---------------------------------------------------------------------------
+// Large batches with bf16 x and w: the dot products in exact integer
+// arithmetic on the int8 matrix cores.
+//
+// Every bf16 value is m * 2^l with an integer m < 2^8.  For a row (of x or of
+// w) with every |v_k| < 2^X, N_k = trunc(v_k * 2^(30 - X)) is an integer with
+// |N_k| < 2^30, equal to v_k * 2^(30 - X) unless v_k has bits below 2^(X - 30)
+// (then |v_k - N_k 2^(X - 30)| is recorded in the row's residual).  N_k is
+// written as four balanced base-256 digits, N = d0 2^24 + d1 2^16 + d2 2^8 + d3
+// with d1..d3 in [-128, 127] and d0 in [-64, 64], each one int8.  For a token
+// row x and an expert row w,
+//   sum_k N_k M_k = sum_{j=0..6} D_j 2^(8 (6 - j)),   D_j = sum_k sum_{a+b=j} d_a[k] e_b[k],
+// and every D_j is an exact int32 sum (|D_j| <= 4 H 2^14 < 2^31 for H <= 16384),
+// whatever order the matrix cores add in.  The logit is then rounded once from
+// the exact integer.  When a row has a residual, the truncated sum is off by at
+// most rx 2^Xw + 2^Xx rw; the binary32 rounding is taken only when that bound
+// keeps the value away from every rounding boundary, else the logit goes to the
+// exact-recomputation list like the binary64 path's.
+// ---------------------------------------------------------------------------
+
+// One wave per row (x rows 0..T-1, then w rows): the row's exponent bound X,
+// its residual, a norm bound (for the exact recomputation), and its digits,
+// laid out per chunk of 32 k as [half of 16 k][digit][16 values], ncp chunks
+// per row (zero past H).
+__global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                int64_t T, int64_t E, int64_t H, int64_t ncp,
+                                                int8_t* __restrict__ dig, int* __restrict__ rexp,
+                                                double* __restrict__ rres, double* __restrict__ norm,
+                                                int* __restrict__ ulist, int* __restrict__ diag) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (blockIdx.x == 0 && tid < 4) {  // the list filled by k_logits_i8; the selection kernel's counters
+    if (tid == 0) *ulist = 0;
+    else diag[tid] = 0;
+  }
+  const int64_t r = (int64_t)blockIdx.x * 4 + (tid >> 6);
+  if (r >= T + E) return;
+  const uint16_t* p = r < T ? x + r * H : w + (r - T) * H;
+  const int nh = (int)(H / 16), nhp = (int)(ncp * 2);
+  double ss = 0.0;
+  int ex = kI8ZeroRow;
+  int bad = 0;
+  for (int j = lane; j < nh; j += 64) {
+    const uint4 q0 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j + 8);
+    const uint32_t u[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t b = (i & 1) ? (u[i >> 1] >> 16) : (u[i >> 1] & 0xFFFFu);
+      const double d = (double)u2f(b << 16);
+      ss = fma(d, d, ss);
+      const int eb = (int)((b >> 7) & 0xFFu);
+      const uint32_t m = b & 0x7Fu;
+      if (eb == 0xFF) bad = 1;
+      else if (eb) ex = max(ex, eb - 126);                       // (1 + m/128) 2^(eb-127) < 2^(eb-126)
+      else if (m) ex = max(ex, -133 + (32 - __builtin_clz(m)));  // m 2^-133
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ss += __shfl_xor(ss, o, 64);
+    ex = max(ex, __shfl_xor(ex, o, 64));
+    bad |= __shfl_xor(bad, o, 64);
+  }
+  const int ue = ex - 30;  // weight of N's unit
+  double res = 0.0;
+  int8_t* drow = dig + r * ncp * kI8ChunkB;
+  for (int j = lane; j < nhp; j += 64) {
+    uint32_t pk[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pk[a][c] = 0u;
+    if (j < nh) {
+      const uint4 q0 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j);
+      const uint4 q1 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j + 8);
+      const uint32_t u[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t b = (i & 1) ? (u[i >> 1] >> 16) : (u[i >> 1] & 0xFFFFu);
+        const int eb = (int)((b >> 7) & 0xFFu);
+        int n = 0;
+        if (eb != 0xFF && (b & 0x7FFFu)) {
+          const int el = eb ? eb - 134 : -133;  // value = mi 2^el
+          const uint32_t mi = eb ? ((b & 0x7Fu) | 0x80u) : (b & 0x7Fu);
+          const int sh = el - ue;
+          uint32_t a;
+          if (sh >= 0) {
+            a = mi << sh;  // < 2^30
+          } else if (sh > -32) {
+            a = mi >> -sh;
+            const uint32_t lo = mi & ((1u << -sh) - 1u);
+            if (lo) res += ldexp((double)lo, el);
+          } else {
+            a = 0u;
+            res += ldexp((double)mi, el);
+          }
+          n = (b & 0x8000u) ? -(int)a : (int)a;
+        }
+        const int d3 = (int)(int8_t)(n & 0xFF);
+        const int n1 = (n - d3) >> 8;
+        const int d2 = (int)(int8_t)(n1 & 0xFF);
+        const int n2 = (n1 - d2) >> 8;
+        const int d1 = (int)(int8_t)(n2 & 0xFF);
+        const int d0 = (n2 - d1) >> 8;
+        const int sb = 8 * (i & 3);
+        pk[0][i >> 2] |= ((uint32_t)d0 & 0xFFu) << sb;
+        pk[1][i >> 2] |= ((uint32_t)d1 & 0xFFu) << sb;
+        pk[2][i >> 2] |= ((uint32_t)d2 & 0xFFu) << sb;
+        pk[3][i >> 2] |= ((uint32_t)d3 & 0xFFu) << sb;
+      }
+    }
+    uint4* o = reinterpret_cast<uint4*>(drow + 64 * (int64_t)j);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) o[a] = make_uint4(pk[a][0], pk[a][1], pk[a][2], pk[a][3]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) res += __shfl_xor(res, o, 64);
+  if (lane == 0) {
+    rexp[r] = ex;
+    // fewer than 2^15 nonnegative terms: the binary64 sum is within a factor 1 + 2^-30 of the exact one
+    rres[r] = bad ? (double)INFINITY : res * (1.0 + 0x1p-30);
+    norm[r] = norm_bound(ss);
+  }
+}
+
+// Round hi 2^(base + 48) + lo 2^base (exact integers) once to binary32.
+__device__ inline float round_i128_f32(int64_t hi, int64_t lo, int base) {
+  const __int128 v = ((__int128)hi << 48) + (__int128)lo;
+  if (v == 0) return 0.0f;
+  const bool neg = v < 0;
+  const unsigned __int128 m = neg ? (unsigned __int128)(-v) : (unsigned __int128)v;
+  const uint64_t mh = (uint64_t)(m >> 64), ml = (uint64_t)m;
+  if (mh == 0) return round_u64_to_f32(ml, false, base, neg);
+  const int lz = __builtin_clzll(mh);
+  const uint64_t W = lz ? ((mh << lz) | (ml >> (64 - lz))) : mh;
+  return round_u64_to_f32(W, (ml << lz) != 0ull, base + 64 - lz, neg);
+}
+
+typedef int i8x16_t __attribute__((ext_vector_type(4)));   // 16 int8 digits
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+// A workgroup owns 64 tokens x 64 experts, each of its 4 waves 32 x 32 on
+// v_mfma_i32_32x32x32_i8 with seven accumulators (one per digit diagonal j).
+// K goes in stages of two chunks through double-buffered LDS (rows padded by
+// 16 bytes).  Lane l of an operand carries row l % 32 and half l / 32 of a
+// chunk (the same k for both operands, which is all the sum needs); result
+// register 4q + i of lane l is token row 8q + 4 (l / 32) + i, expert l % 32.
+// With a multiple of 8 workgroups, the expert tiles of one token tile run on
+// one XCD, so the token digits are read from HBM once.
+__global__ __launch_bounds__(256, 2) void k_logits_i8(const int8_t* __restrict__ dig, int64_t T, int64_t E,
+                                                      int64_t ncp, const int* __restrict__ rexp,
+                                                      const double* __restrict__ rres, float* __restrict__ logits,
+                                                      int* __restrict__ ulist, int* __restrict__ blk) {
+  __shared__ __attribute__((aligned(16))) int8_t tl[2][2][kI8Rows * kI8Ld];  // [buffer][x, w]
+  __shared__ int n_unc;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t ne = (E + kI8Rows - 1) / kI8Rows, nwg = ((T + kI8Rows - 1) / kI8Rows) * ne;
+  const int64_t b = blockIdx.x;
+  const int64_t lt = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + b / 8 : b;
+  const int64_t t0 = (lt / ne) * kI8Rows, e0 = (lt % ne) * kI8Rows;
+  if (tid == 0) n_unc = 0;
+  // staging: 8 loads of 16 bytes per thread and stage; rows past T or E repeat the last row
+  const int64_t rowb = ncp * kI8ChunkB;
+  const int8_t* src[8];
+  int dst[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int idx = q * 256 + tid, op = idx >> 10, rr = (idx >> 4) & 63, seg = idx & 15;
+    const int64_t row = op == 0 ? (t0 + rr < T ? t0 + rr : T - 1) : T + (e0 + rr < E ? e0 + rr : E - 1);
+    src[q] = dig + row * rowb + seg * 16;
+    dst[q] = op * (kI8Rows * kI8Ld) + rr * kI8Ld + seg * 16;
+  }
+  i8x16_t stg[8];
+  auto gload = [&](int64_t s) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) stg[q] = *reinterpret_cast<const i8x16_t*>(src[q] + s * (kI8Stage * kI8ChunkB));
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) *reinterpret_cast<i8x16_t*>(&tl[buf][0][0] + dst[q]) = stg[q];
+  };
+  i32x16_t acc[7];
+#pragma unroll
+  for (int d = 0; d < 7; ++d)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[d][i] = 0;
+  const int ar = (wv & 1) * 32 + (lane & 31), br = (wv >> 1) * 32 + (lane & 31), hoff = (lane >> 5) * 64;
+  const int64_t nst = ncp / kI8Stage;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int64_t s = 0; s < nst; ++s) {
+    const int buf = (int)(s & 1);
+    if (s + 1 < nst) gload(s + 1);
+    const int8_t* A = &tl[buf][0][ar * kI8Ld + hoff];
+    const int8_t* B = &tl[buf][1][br * kI8Ld + hoff];
+#pragma unroll
+    for (int cc = 0; cc < kI8Stage; ++cc) {
+      i8x16_t a[4], bb[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        a[d] = *reinterpret_cast<const i8x16_t*>(A + cc * kI8ChunkB + d * 16);
+        bb[d] = *reinterpret_cast<const i8x16_t*>(B + cc * kI8ChunkB + d * 16);
+      }
+#pragma unroll
+      for (int d1 = 0; d1 < 4; ++d1)
+#pragma unroll
+        for (int d2 = 0; d2 < 4; ++d2)
+          acc[d1 + d2] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[d1], bb[d2], acc[d1 + d2], 0, 0, 0);
+    }
+    if (s + 1 < nst) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  int nu = 0;
+  const int64_t e = e0 + (wv >> 1) * 32 + (lane & 31);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + (wv & 1) * 32 + 8 * q + 4 * (lane >> 5) + i;
+      if (t >= T || e >= E) continue;
+      const int g = 4 * q + i;
+      // sum_j D_j 2^(8 (6 - j)) = hi 2^48 + lo, both exact in int64
+      const int64_t D0 = acc[0][g], D1 = acc[1][g], D2 = acc[2][g], D3 = acc[3][g];
+      const int64_t hi = D0 + (D1 >> 8) + (D2 >> 16) + (D3 >> 24);
+      const int64_t lo = (int64_t)acc[6][g] + ((int64_t)acc[5][g] << 8) + ((int64_t)acc[4][g] << 16) +
+                         ((D3 & 0xFFFFFF) << 24) + ((D2 & 0xFFFF) << 32) + ((D1 & 0xFF) << 40);
+      const int xe = rexp[t], we = rexp[T + e];
+      const double rx = rres[t], rw = rres[T + e];
+      const int base = (xe - 30) + (we - 30);
+      float r;
+      if (rx == 0.0 && rw == 0.0) {
+        r = round_i128_f32(hi, lo, base);
+      } else {
+        const double S = ldexp((double)hi, base + 48) + ldexp((double)lo, base);  // one rounding
+        const double err = rx * ldexp(1.0, we) + ldexp(1.0, xe) * rw + fabs(S) * 0x1p-52;
+        if (!f32_certified(S, err, &r)) r = __builtin_nanf("");
+      }
+      logits[t * E + e] = r;
+      if (r != r) {
+        ++nu;
+        ulist[1 + atomicAdd(ulist, 1)] = (int)(t * E + e);
+      }
+    }
+  }
+  if (nu) atomicAdd(&n_unc, nu);
+  __syncthreads();
+  if (tid == 0) blk[b] = n_unc;
+}
+
 // The listed logits, exactly: each workgroup takes list entries blockIdx.x,
 // blockIdx.x + gridDim.x, ... (the list order does not matter: every entry's
 // value is exact).
@@ -853,12 +1134,21 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   const unsigned nrb = (unsigned)(((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE));
   const dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
   const dim3 glz(gl.x, gl.y, (unsigned)L.ks);
+  // bf16 x and w at large batches: exact integer dot products on the int8 matrix cores
+  const bool i8 = BSM_ROUTE_I8 && L.i8ok && xb && wb;
+  int8_t* dig = reinterpret_cast<int8_t*>(ws + L.part);
+  int* rexp = L.i8ok ? reinterpret_cast<int*>(ws + L.rexp) : nullptr;
+  double* rres = L.i8ok ? reinterpret_cast<double*>(ws + L.rres) : nullptr;
   // one wave per token needs 256 experts, groups of a multiple of 4 and an aligned scores row
   const bool sel4 = BSM_SELECT_WAVE && E == 256 && (E / n_group) % 4 == 0 && topk <= 64 &&
                     ((uintptr_t)scores & 15) == 0;
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
   if (L.rb) {                                                                                              \
     k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, L.nadd, logits, blk, diag);                    \
+  } else if (i8) {                                                                                         \
+    k_slice8<<<nrs, 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), \
+                                  T, E, H, L.ncp, dig, rexp, rres, norm, ulist, diag);                      \
+    k_logits_i8<<<gl.x * gl.y, 256, 0, st>>>(dig, T, E, L.ncp, rexp, rres, logits, ulist, blk);             \
   } else {                                                                                                 \
     if (vec)                                                                                               \
       k_rowstats<XB, WB, true><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                             \
