@@ -75,7 +75,7 @@ struct RouteWs {
   size_t norm, lsb, part, ulist, logits, blk, diag, total;  // norm, lsb, part, ulist: tiled path only
   size_t rexp, rres;  // int8 path: per-row exponent bound and truncation residual (dig shares part's space)
   bool i8ok;          // the int8 path fits this shape (the launch also needs bf16 x and w)
-  int64_t ncp;        // int8 path: chunks of 32 k per row, rounded up to whole stages
+  int64_t ncp;        // int8 path: chunks of 32 k per row, rounded up to an even number of stages
   bool rb;    // small-batch kernel (full K per workgroup, lanes own K slices)
   int nadd;   // roundings along the longest summation path of one logit
   int64_t nblk;  // logits workgroups (one exact-recomputation count each)
@@ -107,7 +107,7 @@ RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
   L.lsb = o;
   if (!L.rb) o += align256(sizeof(int) * (size_t)(T + E));
   L.i8ok = !L.rb && H % 16 == 0 && H <= kI8MaxH;
-  L.ncp = (((H + 31) / 32 + kI8Stage - 1) / kI8Stage) * kI8Stage;
+  L.ncp = (((H + 31) / 32 + 2 * kI8Stage - 1) / (2 * kI8Stage)) * (2 * kI8Stage);  // an even number of stages
   L.part = o;  // binary64 partial sums, or the int8 path's digits of every row of x and w
   if (!L.rb) {
     const size_t pb = sizeof(double) * (size_t)L.ks * (size_t)T * (size_t)E;
@@ -667,10 +667,82 @@ __global__ __launch_bounds__(256) void k_logits_fin(int64_t T, int64_t E, int ks
 // exact-recomputation list like the binary64 path's.
 // ---------------------------------------------------------------------------
 
-// One wave per row (x rows 0..T-1, then w rows): the row's exponent bound X,
-// its residual, a norm bound (for the exact recomputation), and its digits,
-// laid out per chunk of 32 k as [half of 16 k][digit][16 values], ncp chunks
-// per row (zero past H).
+// One wave per row (x rows 0..T-1, then w rows): the row's exponent bound X
+// (from the largest magnitude's bits: bf16 magnitudes order like their bit
+// patterns), its residual, a norm bound sqrt(H) max|v| (for the exact
+// recomputation), and its digits, laid out per chunk of 32 k as
+// [half of 16 k][digit][16 values], ncp chunks per row (zero past H).
+// N = trunc(v 2^(30 - X)) comes from a binary32 scaling (exact: the result is
+// below 2^30) and a truncating conversion; v - N 2^(X - 30) is exact in
+// binary32 (the low bits of v's 8-bit significand), so a nonzero difference
+// flags a truncated value.  For rows with X < -100 that difference could fall
+// below the binary32 range, and the digits come from the integer fields.
+// Balanced digits: with M = N + 0x808080, the low three bytes of M xor 0x80
+// are d3, d2, d1 and the top byte is d0 = M >> 24.
+__device__ inline uint32_t slice_n(uint32_t b, int ex, bool flt, double& res) {
+  if (flt) {
+    const float f = u2f(b << 16);
+    const int n = (int)ldexpf(f, 30 - ex);
+    const float back = ldexpf((float)n, ex - 30);
+    const float r = f - back;
+    if (r != 0.0f) res += fabs((double)r);
+    return (uint32_t)n;
+  }
+  const int eb = (int)((b >> 7) & 0xFFu);
+  if (!(b & 0x7FFFu)) return 0u;
+  const int el = eb ? eb - 134 : -133;  // value = mi 2^el
+  const uint32_t mi = eb ? ((b & 0x7Fu) | 0x80u) : (b & 0x7Fu);
+  const int sh = el - (ex - 30);
+  uint32_t a;
+  if (sh >= 0) {
+    a = mi << sh;  // < 2^30
+  } else if (sh > -32) {
+    a = mi >> -sh;
+    const uint32_t lo = mi & ((1u << -sh) - 1u);
+    if (lo) res += ldexp((double)lo, el);
+  } else {
+    a = 0u;
+    res += ldexp((double)mi, el);
+  }
+  return (b & 0x8000u) ? (uint32_t)(-(int)a) : a;
+}
+
+// Digits of 16 values (a half chunk) for digit-major storage.
+__device__ inline void slice16(const uint32_t* u, int ex, bool flt, double& res, uint32_t (*o4)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {  // values 4c .. 4c+3
+    uint32_t P[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t word = u[(4 * c + i) >> 1];
+      const uint32_t b = (i & 1) ? (word >> 16) : (word & 0xFFFFu);
+      P[i] = slice_n(b, ex, flt, res) + 0x808080u;
+    }
+    // byte transpose: row k holds byte k of P[0..3]
+    const uint32_t A = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);  // P0b0 P1b0 P0b1 P1b1
+    const uint32_t B = __builtin_amdgcn_perm(P[1], P[0], 0x07030602u);  // P0b2 P1b2 P0b3 P1b3
+    const uint32_t C = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
+    const uint32_t D = __builtin_amdgcn_perm(P[3], P[2], 0x07030602u);
+    o4[3][c] = __builtin_amdgcn_perm(C, A, 0x05040100u) ^ 0x80808080u;  // byte 0: d3
+    o4[2][c] = __builtin_amdgcn_perm(C, A, 0x07060302u) ^ 0x80808080u;  // byte 1: d2
+    o4[1][c] = __builtin_amdgcn_perm(D, B, 0x05040100u) ^ 0x80808080u;  // byte 2: d1
+    o4[0][c] = __builtin_amdgcn_perm(D, B, 0x07060302u);                 // byte 3: d0
+  }
+}
+
+__device__ inline uint32_t max_mag16(const uint32_t* u) {
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t m = u[i] & 0x7FFF7FFFu;
+    mx = max(mx, max(m & 0xFFFFu, m >> 16));
+  }
+  return mx;
+}
+
+// NC > 0: the row (at most 64 NC half chunks) stays in registers between the
+// exponent pass and the digit pass; NC == 0: the digit pass reads it again.
+template <int NC>
 __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                 int64_t T, int64_t E, int64_t H, int64_t ncp,
                                                 int8_t* __restrict__ dig, int* __restrict__ rexp,
@@ -685,82 +757,63 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
   if (r >= T + E) return;
   const uint16_t* p = r < T ? x + r * H : w + (r - T) * H;
   const int nh = (int)(H / 16), nhp = (int)(ncp * 2);
-  double ss = 0.0;
-  int ex = kI8ZeroRow;
-  int bad = 0;
-  for (int j = lane; j < nh; j += 64) {
+  auto load16 = [&](int j, uint32_t* u) {
     const uint4 q0 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j);
     const uint4 q1 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j + 8);
-    const uint32_t u[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    u[0] = q0.x; u[1] = q0.y; u[2] = q0.z; u[3] = q0.w;
+    u[4] = q1.x; u[5] = q1.y; u[6] = q1.z; u[7] = q1.w;
+  };
+  constexpr int NCC = NC > 0 ? NC : 1;
+  uint32_t cu[NCC][8];
+  uint32_t mx = 0u;  // largest magnitude bit pattern
+  if constexpr (NC > 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t b = (i & 1) ? (u[i >> 1] >> 16) : (u[i >> 1] & 0xFFFFu);
-      const double d = (double)u2f(b << 16);
-      ss = fma(d, d, ss);
-      const int eb = (int)((b >> 7) & 0xFFu);
-      const uint32_t m = b & 0x7Fu;
-      if (eb == 0xFF) bad = 1;
-      else if (eb) ex = max(ex, eb - 126);                       // (1 + m/128) 2^(eb-127) < 2^(eb-126)
-      else if (m) ex = max(ex, -133 + (32 - __builtin_clz(m)));  // m 2^-133
+    for (int c = 0; c < NC; ++c) {  // clamped loads: no load under a branch
+      const int j = lane + 64 * c;
+      load16(j < nh ? j : nh - 1, cu[c]);
+      if (j >= nh)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cu[c][i] = 0u;
+      mx = max(mx, max_mag16(cu[c]));
+    }
+  } else {
+    for (int j = lane; j < nh; j += 64) {
+      load16(j, cu[0]);
+      mx = max(mx, max_mag16(cu[0]));
     }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    ss += __shfl_xor(ss, o, 64);
-    ex = max(ex, __shfl_xor(ex, o, 64));
-    bad |= __shfl_xor(bad, o, 64);
-  }
-  const int ue = ex - 30;  // weight of N's unit
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  const bool bad = mx >= 0x7F80u;  // Inf or NaN in the row
+  const int meb = (int)(mx >> 7);
+  const int ex = mx == 0u ? kI8ZeroRow : meb ? meb - 126 : -133 + (32 - __builtin_clz(mx));
+  const bool flt = ex >= -100, live = !bad && mx != 0u;
   double res = 0.0;
   int8_t* drow = dig + r * ncp * kI8ChunkB;
-  for (int j = lane; j < nhp; j += 64) {
-    uint32_t pk[4][4];
+  auto emit = [&](int j, const uint32_t* u, bool data) {
+    uint32_t o4[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) pk[a][c] = 0u;
-    if (j < nh) {
-      const uint4 q0 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j);
-      const uint4 q1 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j + 8);
-      const uint32_t u[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t b = (i & 1) ? (u[i >> 1] >> 16) : (u[i >> 1] & 0xFFFFu);
-        const int eb = (int)((b >> 7) & 0xFFu);
-        int n = 0;
-        if (eb != 0xFF && (b & 0x7FFFu)) {
-          const int el = eb ? eb - 134 : -133;  // value = mi 2^el
-          const uint32_t mi = eb ? ((b & 0x7Fu) | 0x80u) : (b & 0x7Fu);
-          const int sh = el - ue;
-          uint32_t a;
-          if (sh >= 0) {
-            a = mi << sh;  // < 2^30
-          } else if (sh > -32) {
-            a = mi >> -sh;
-            const uint32_t lo = mi & ((1u << -sh) - 1u);
-            if (lo) res += ldexp((double)lo, el);
-          } else {
-            a = 0u;
-            res += ldexp((double)mi, el);
-          }
-          n = (b & 0x8000u) ? -(int)a : (int)a;
-        }
-        const int d3 = (int)(int8_t)(n & 0xFF);
-        const int n1 = (n - d3) >> 8;
-        const int d2 = (int)(int8_t)(n1 & 0xFF);
-        const int n2 = (n1 - d2) >> 8;
-        const int d1 = (int)(int8_t)(n2 & 0xFF);
-        const int d0 = (n2 - d1) >> 8;
-        const int sb = 8 * (i & 3);
-        pk[0][i >> 2] |= ((uint32_t)d0 & 0xFFu) << sb;
-        pk[1][i >> 2] |= ((uint32_t)d1 & 0xFFu) << sb;
-        pk[2][i >> 2] |= ((uint32_t)d2 & 0xFFu) << sb;
-        pk[3][i >> 2] |= ((uint32_t)d3 & 0xFFu) << sb;
-      }
-    }
+      for (int c = 0; c < 4; ++c) o4[a][c] = 0u;
+    if (data && live) slice16(u, ex, flt, res, o4);
     uint4* o = reinterpret_cast<uint4*>(drow + 64 * (int64_t)j);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) o[a] = make_uint4(pk[a][0], pk[a][1], pk[a][2], pk[a][3]);
+    for (int a = 0; a < 4; ++a) o[a] = make_uint4(o4[a][0], o4[a][1], o4[a][2], o4[a][3]);
+  };
+  int j0 = lane;
+  if constexpr (NC > 0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int j = lane + 64 * c;
+      if (j < nhp) emit(j, cu[c], j < nh);
+    }
+    j0 = lane + 64 * NC;
+  }
+  for (int j = j0; j < nhp; j += 64) {  // NC == 0: every half chunk; NC > 0: the zero padding past them
+    const bool data = j < nh;
+    if (data) load16(j, cu[0]);
+    emit(j, cu[0], data);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) res += __shfl_xor(res, o, 64);
@@ -768,7 +821,8 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
     rexp[r] = ex;
     // fewer than 2^15 nonnegative terms: the binary64 sum is within a factor 1 + 2^-30 of the exact one
     rres[r] = bad ? (double)INFINITY : res * (1.0 + 0x1p-30);
-    norm[r] = norm_bound(ss);
+    // sqrt(H) max|v| >= the 2-norm; max|v| < 2^X
+    norm[r] = mx == 0u ? 0.0 : sqrt((double)H) * ldexp(1.0, ex) * (1.0 + 0x1p-40);
   }
 }
 
@@ -819,14 +873,18 @@ __global__ __launch_bounds__(256, 2) void k_logits_i8(const int8_t* __restrict__
     src[q] = dig + row * rowb + seg * 16;
     dst[q] = op * (kI8Rows * kI8Ld) + rr * kI8Ld + seg * 16;
   }
-  i8x16_t stg[8];
-  auto gload = [&](int64_t s) {
+  // two register sets: a stage's digits are loaded two stages before they are multiplied; indices past
+  // the last stage are clamped (those loads are never stored), so no load sits under a branch
+  i8x16_t ga[8], gb[8];
+  const int64_t nst = ncp / kI8Stage;  // even
+  auto gload = [&](i8x16_t* g, int64_t s) {
+    const int64_t sc = s < nst ? s : nst - 1;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) stg[q] = *reinterpret_cast<const i8x16_t*>(src[q] + s * (kI8Stage * kI8ChunkB));
+    for (int q = 0; q < 8; ++q) g[q] = *reinterpret_cast<const i8x16_t*>(src[q] + sc * (kI8Stage * kI8ChunkB));
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const i8x16_t* g, int buf) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) *reinterpret_cast<i8x16_t*>(&tl[buf][0][0] + dst[q]) = stg[q];
+    for (int q = 0; q < 8; ++q) *reinterpret_cast<i8x16_t*>(&tl[buf][0][0] + dst[q]) = g[q];
   };
   i32x16_t acc[7];
 #pragma unroll
@@ -834,13 +892,7 @@ __global__ __launch_bounds__(256, 2) void k_logits_i8(const int8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[d][i] = 0;
   const int ar = (wv & 1) * 32 + (lane & 31), br = (wv >> 1) * 32 + (lane & 31), hoff = (lane >> 5) * 64;
-  const int64_t nst = ncp / kI8Stage;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int64_t s = 0; s < nst; ++s) {
-    const int buf = (int)(s & 1);
-    if (s + 1 < nst) gload(s + 1);
+  auto multiply = [&](int buf) {
     const int8_t* A = &tl[buf][0][ar * kI8Ld + hoff];
     const int8_t* B = &tl[buf][1][br * kI8Ld + hoff];
 #pragma unroll
@@ -857,9 +909,24 @@ __global__ __launch_bounds__(256, 2) void k_logits_i8(const int8_t* __restrict__
         for (int d2 = 0; d2 < 4; ++d2)
           acc[d1 + d2] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[d1], bb[d2], acc[d1 + d2], 0, 0, 0);
     }
-    if (s + 1 < nst) lstore(buf ^ 1);
+  };
+  gload(ga, 0);
+  gload(gb, 1);
+  lstore(ga, 0);
+  __syncthreads();
+  for (int64_t s = 0; s < nst; s += 2) {
+    gload(ga, s + 2);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiplies
+    multiply(0);
+    lstore(gb, 1);
+    __syncthreads();
+    gload(gb, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(1);
+    lstore(ga, 0);
     __syncthreads();
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the clamped loads of the last stages have landed
   int nu = 0;
   const int64_t e = e0 + (wv >> 1) * 32 + (lane & 31);
 #pragma unroll
@@ -1107,6 +1174,25 @@ __global__ __launch_bounds__(64 * kSel4Tokens) void k_select256(
   }
 }
 
+void launch_slice8(const uint16_t* x, const uint16_t* w, int64_t T, int64_t E, int64_t H, int64_t ncp, int8_t* dig,
+                   int* rexp, double* rres, double* norm, int* ulist, int* diag, hipStream_t st) {
+  const unsigned g = (unsigned)((T + E + 3) / 4);
+  const int64_t nc = (H / 16 + 63) / 64;  // half chunks per lane
+#define BSM_SLICE8(N) k_slice8<N><<<g, 256, 0, st>>>(x, w, T, E, H, ncp, dig, rexp, rres, norm, ulist, diag)
+  switch (nc) {
+    case 1: BSM_SLICE8(1); break;
+    case 2: BSM_SLICE8(2); break;
+    case 3: BSM_SLICE8(3); break;
+    case 4: BSM_SLICE8(4); break;
+    case 5: BSM_SLICE8(5); break;
+    case 6: BSM_SLICE8(6); break;
+    case 7: BSM_SLICE8(7); break;
+    case 8: BSM_SLICE8(8); break;
+    default: BSM_SLICE8(0); break;
+  }
+#undef BSM_SLICE8
+}
+
 __global__ void k_copy_diag(const int* src, int32_t* dst) {
   if (threadIdx.x < 4) dst[threadIdx.x] = src[threadIdx.x];
 }
@@ -1146,8 +1232,8 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   if (L.rb) {                                                                                              \
     k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, L.nadd, logits, blk, diag);                    \
   } else if (i8) {                                                                                         \
-    k_slice8<<<nrs, 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), \
-                                  T, E, H, L.ncp, dig, rexp, rres, norm, ulist, diag);                      \
+    launch_slice8(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), T, E, H, L.ncp,  \
+                  dig, rexp, rres, norm, ulist, diag, st);                                                 \
     k_logits_i8<<<gl.x * gl.y, 256, 0, st>>>(dig, T, E, L.ncp, rexp, rres, logits, ulist, blk);             \
   } else {                                                                                                 \
     if (vec)                                                                                               \
