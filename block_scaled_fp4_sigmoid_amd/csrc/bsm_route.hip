@@ -178,9 +178,19 @@ __device__ float exact_logit_wg(const void* __restrict__ x, const void* __restri
   __syncthreads();
   int64_t dig[WIN_DIGITS] = {0, 0, 0, 0, 0};
   bool bad = false;
-  for (int64_t k = tid; k < H; k += NT) {
-    const double p = (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k);
-    bad |= !win_add(dig, p, base);
+  // 8 consecutive k per thread and pass: the 16 loads of a pass are independent (the digit sums are exact,
+  // so the order of the additions does not matter); a product past H is zero, which adds nothing
+  constexpr int U = 8;
+  for (int64_t k0 = (int64_t)tid * U; k0 < H; k0 += (int64_t)NT * U) {
+    float xv[U], wv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = k0 + u < H;
+      xv[u] = in ? ld1<XB>(x, t * H + k0 + u) : 0.0f;
+      wv[u] = in ? ld1<WB>(w, e * H + k0 + u) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) bad |= !win_add(dig, (double)xv[u] * (double)wv[u], base);
   }
   if (bad) atomicOr(&L->bad, 1);
 #pragma unroll
@@ -207,7 +217,17 @@ __device__ float exact_logit_wg(const void* __restrict__ x, const void* __restri
     __syncthreads();
     int64_t loc[SA_NDIG];
     for (int q = 0; q < SA_NDIG; ++q) loc[q] = 0;
-    for (int64_t k = tid; k < H; k += NT) sa_add(loc, (double)ld1<XB>(x, t * H + k) * (double)ld1<WB>(w, e * H + k));
+    for (int64_t k0 = (int64_t)tid * U; k0 < H; k0 += (int64_t)NT * U) {
+      float xv[U], wv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool in = k0 + u < H;
+        xv[u] = in ? ld1<XB>(x, t * H + k0 + u) : 0.0f;
+        wv[u] = in ? ld1<WB>(w, e * H + k0 + u) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) sa_add(loc, (double)xv[u] * (double)wv[u]);
+    }
     for (int q = 0; q < SA_NDIG; ++q)
       if (loc[q]) atomicAdd(reinterpret_cast<unsigned long long*>(&L->sa[q]), (unsigned long long)loc[q]);
     __syncthreads();
