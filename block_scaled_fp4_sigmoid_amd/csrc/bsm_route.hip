@@ -48,6 +48,9 @@
 #ifndef BSM_ROUTE_I8
 #define BSM_ROUTE_I8 1
 #endif
+#ifndef BSM_ROUTE_I8_SMALL
+#define BSM_ROUTE_I8_SMALL 1  // small batches too (K cut into splits)
+#endif
 #ifndef BSM_SELECT_WAVE
 #define BSM_SELECT_WAVE 1
 #endif
@@ -74,8 +77,11 @@ constexpr int kI8ZeroRow = -4096; // exponent bound recorded for a row without f
 struct RouteWs {
   size_t norm, lsb, part, ulist, logits, blk, diag, total;  // norm, lsb, part, ulist: tiled path only
   size_t rexp, rres;  // int8 path: per-row exponent bound and truncation residual (dig shares part's space)
+  size_t dig, spart;  // int8 path: digits; small batches: per K split and logit an exact (hi, lo) partial
   bool i8ok;          // the int8 path fits this shape (the launch also needs bf16 x and w)
   int64_t ncp;        // int8 path: chunks of 32 k per row, rounded up to an even number of stages
+  int64_t s8, sps8;   // int8 path: K splits (1 at large batches) and stages per split (even)
+  int64_t nblk8;      // int8 path: workgroups that count list entries (the finalize kernel's at small batches)
   bool rb;    // small-batch kernel (full K per workgroup, lanes own K slices)
   int nadd;   // roundings along the longest summation path of one logit
   int64_t nblk;  // logits workgroups (one exact-recomputation count each)
@@ -100,26 +106,45 @@ RouteWs route_layout(int64_t T, int64_t H, int64_t E) {
   // tiled: an FMA chain of kBK per LDS step, added to the slice's running sum, then the slices
   // added in order
   L.nadd = L.rb ? (int)(((H + kRbK - 1) / kRbK) * 8 + 9) : (int)(kBK + sps + L.ks + 1);
+  // int8 path: small batches cut K into splits (an even number of stages each) so that the grid holds
+  // about 256 workgroups of at least 4 stages; their exact partials are added by k_fin_i8
+  L.i8ok = H % 16 == 0 && H <= kI8MaxH;
+  L.ncp = (((H + 31) / 32 + 2 * kI8Stage - 1) / (2 * kI8Stage)) * (2 * kI8Stage);  // an even number of stages
+  {
+    const int64_t nst8 = L.ncp / kI8Stage, nwg8 = ((T + kI8Rows - 1) / kI8Rows) * ((E + kI8Rows - 1) / kI8Rows);
+    int64_t s8 = L.rb ? (256 + nwg8 - 1) / (nwg8 > 0 ? nwg8 : 1) : 1;
+    const int64_t smax = nst8 / 4 > 1 ? nst8 / 4 : 1;
+    s8 = s8 < 1 ? 1 : s8 > smax ? smax : s8;
+    const int64_t pairs = nst8 / 2, ppers = (pairs + s8 - 1) / s8;
+    L.sps8 = 2 * ppers;
+    L.s8 = (nst8 + L.sps8 - 1) / L.sps8;
+    L.nblk8 = L.rb ? (T * E + 255) / 256 : nwg8;
+  }
+  const bool big = !L.rb, i8s = L.rb && L.i8ok;  // i8s: the small-batch int8 path may run
   L.nblk = L.rb ? ((T + kRbT - 1) / kRbT) * ((E + kRbE - 1) / kRbE) : tiles;
+  if (L.i8ok && L.nblk8 > L.nblk) L.nblk = L.nblk8;
   size_t o = 0;
   L.norm = o;
-  if (!L.rb) o += align256(sizeof(double) * (size_t)(T + E));
+  if (big || i8s) o += align256(sizeof(double) * (size_t)(T + E));
   L.lsb = o;
-  if (!L.rb) o += align256(sizeof(int) * (size_t)(T + E));
-  L.i8ok = !L.rb && H % 16 == 0 && H <= kI8MaxH;
-  L.ncp = (((H + 31) / 32 + 2 * kI8Stage - 1) / (2 * kI8Stage)) * (2 * kI8Stage);  // an even number of stages
+  if (big) o += align256(sizeof(int) * (size_t)(T + E));
   L.part = o;  // binary64 partial sums, or the int8 path's digits of every row of x and w
-  if (!L.rb) {
+  const size_t db = L.i8ok ? (size_t)(T + E) * (size_t)L.ncp * kI8ChunkB : 0;
+  if (big) {
     const size_t pb = sizeof(double) * (size_t)L.ks * (size_t)T * (size_t)E;
-    const size_t db = L.i8ok ? (size_t)(T + E) * (size_t)L.ncp * kI8ChunkB : 0;
     o += align256(pb > db ? pb : db);
+  } else if (i8s) {
+    o += align256(db);
   }
+  L.dig = L.part;
+  L.spart = o;
+  if (i8s) o += align256(2 * sizeof(int64_t) * (size_t)L.s8 * (size_t)T * (size_t)E);
   L.rexp = o;
   if (L.i8ok) o += align256(sizeof(int) * (size_t)(T + E));
   L.rres = o;
   if (L.i8ok) o += align256(sizeof(double) * (size_t)(T + E));
   L.ulist = o;  // count, then the flat indices of the logits left for exact recomputation
-  if (!L.rb) o += align256(sizeof(int) * (size_t)(T * E + 1));
+  if (big || i8s) o += align256(sizeof(int) * (size_t)(T * E + 1));
   L.logits = o;
   o += align256(sizeof(float) * (size_t)T * (size_t)E);
   L.blk = o;
@@ -760,9 +785,10 @@ __device__ inline uint32_t max_mag16(const uint32_t* u) {
   return mx;
 }
 
-// NC > 0: the row (at most 64 NC half chunks) stays in registers between the
-// exponent pass and the digit pass; NC == 0: the digit pass reads it again.
-template <int NC>
+// WPR waves share a row (1, or 4 when there are few rows); NC > 0: the row
+// (at most 64 WPR NC half chunks) stays in registers between the exponent pass
+// and the digit pass; NC == 0: the digit pass reads it again.
+template <int NC, int WPR>
 __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                 int64_t T, int64_t E, int64_t H, int64_t ncp,
                                                 int8_t* __restrict__ dig, int* __restrict__ rexp,
@@ -773,10 +799,15 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
     if (tid == 0) *ulist = 0;
     else diag[tid] = 0;
   }
-  const int64_t r = (int64_t)blockIdx.x * 4 + (tid >> 6);
-  if (r >= T + E) return;
+  __shared__ uint32_t s_mx[4];
+  __shared__ double s_res[4];
+  const int sub = (tid >> 6) % WPR;  // this wave's share of the row
+  const int64_t r = (int64_t)blockIdx.x * (4 / WPR) + (tid >> 6) / WPR;
+  if (WPR == 1 && r >= T + E) return;  // WPR > 1: one row per workgroup, the grid holds exactly T + E
   const uint16_t* p = r < T ? x + r * H : w + (r - T) * H;
   const int nh = (int)(H / 16), nhp = (int)(ncp * 2);
+  const int lj = sub * 64 + lane;  // first half chunk of this lane; then every 64 WPR
+  constexpr int JS = 64 * WPR;
   auto load16 = [&](int j, uint32_t* u) {
     const uint4 q0 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j);
     const uint4 q1 = *reinterpret_cast<const uint4*>(p + 16 * (int64_t)j + 8);
@@ -789,7 +820,7 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
   if constexpr (NC > 0) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {  // clamped loads: no load under a branch
-      const int j = lane + 64 * c;
+      const int j = lj + JS * c;
       load16(j < nh ? j : nh - 1, cu[c]);
       if (j >= nh)
 #pragma unroll
@@ -797,13 +828,18 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
       mx = max(mx, max_mag16(cu[c]));
     }
   } else {
-    for (int j = lane; j < nh; j += 64) {
+    for (int j = lj; j < nh; j += JS) {
       load16(j, cu[0]);
       mx = max(mx, max_mag16(cu[0]));
     }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  if constexpr (WPR > 1) {
+    if (lane == 0) s_mx[tid >> 6] = mx;
+    __syncthreads();
+    mx = max(max(s_mx[0], s_mx[1]), max(s_mx[2], s_mx[3]));
+  }
   const bool bad = mx >= 0x7F80u;  // Inf or NaN in the row
   const int meb = (int)(mx >> 7);
   const int ex = mx == 0u ? kI8ZeroRow : meb ? meb - 126 : -133 + (32 - __builtin_clz(mx));
@@ -821,23 +857,28 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
 #pragma unroll
     for (int a = 0; a < 4; ++a) o[a] = make_uint4(o4[a][0], o4[a][1], o4[a][2], o4[a][3]);
   };
-  int j0 = lane;
+  int j0 = lj;
   if constexpr (NC > 0) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int j = lane + 64 * c;
+      const int j = lj + JS * c;
       if (j < nhp) emit(j, cu[c], j < nh);
     }
-    j0 = lane + 64 * NC;
+    j0 = lj + JS * NC;
   }
-  for (int j = j0; j < nhp; j += 64) {  // NC == 0: every half chunk; NC > 0: the zero padding past them
+  for (int j = j0; j < nhp; j += JS) {  // NC == 0: every half chunk; NC > 0: the zero padding past them
     const bool data = j < nh;
     if (data) load16(j, cu[0]);
     emit(j, cu[0], data);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) res += __shfl_xor(res, o, 64);
-  if (lane == 0) {
+  if constexpr (WPR > 1) {
+    if (lane == 0) s_res[tid >> 6] = res;
+    __syncthreads();
+    res = ((s_res[0] + s_res[1]) + s_res[2]) + s_res[3];
+  }
+  if (lane == 0 && sub == 0) {
     rexp[r] = ex;
     // fewer than 2^15 nonnegative terms: the binary64 sum is within a factor 1 + 2^-30 of the exact one
     rres[r] = bad ? (double)INFINITY : res * (1.0 + 0x1p-30);
@@ -859,6 +900,19 @@ __device__ inline float round_i128_f32(int64_t hi, int64_t lo, int base) {
   return round_u64_to_f32(W, (ml << lz) != 0ull, base + 64 - lz, neg);
 }
 
+// The logit from its exact digit sum hi 2^48 + lo (in units of 2^(Xx - 30) 2^(Xw - 30)) and the two rows'
+// exponent bounds and residuals; NaN when a residual leaves the binary32 rounding unproven.
+__device__ inline float i8_round(int64_t hi, int64_t lo, int xe, int we, double rx, double rw) {
+  const int base = (xe - 30) + (we - 30);
+  if (rx == 0.0 && rw == 0.0) return round_i128_f32(hi, lo, base);
+  const int64_t c = lo >> 48;  // hi 2^48 + lo = (hi + c) 2^48 + (lo - c 2^48), the second part in [0, 2^48)
+  const double S = ldexp((double)(hi + c), base + 48) + ldexp((double)(lo - c * (1ll << 48)), base);  // one rounding
+  const double err = rx * ldexp(1.0, we) + ldexp(1.0, xe) * rw + fabs(S) * 0x1p-52;
+  float r;
+  if (!f32_certified(S, err, &r)) r = __builtin_nanf("");
+  return r;
+}
+
 typedef int i8x16_t __attribute__((ext_vector_type(4)));   // 16 int8 digits
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
@@ -869,11 +923,15 @@ typedef int i32x16_t __attribute__((ext_vector_type(16)));
 // chunk (the same k for both operands, which is all the sum needs); result
 // register 4q + i of lane l is token row 8q + 4 (l / 32) + i, expert l % 32.
 // With a multiple of 8 workgroups, the expert tiles of one token tile run on
-// one XCD, so the token digits are read from HBM once.
+// one XCD, so the token digits are read from HBM once.  SPLIT (small
+// batches): blockIdx.y takes sps stages of K and the workgroup stores its
+// exact partial (hi, lo) of every logit for k_fin_i8.
+template <bool SPLIT>
 __global__ __launch_bounds__(256, 2) void k_logits_i8(const int8_t* __restrict__ dig, int64_t T, int64_t E,
-                                                      int64_t ncp, const int* __restrict__ rexp,
+                                                      int64_t ncp, int64_t sps, const int* __restrict__ rexp,
                                                       const double* __restrict__ rres, float* __restrict__ logits,
-                                                      int* __restrict__ ulist, int* __restrict__ blk) {
+                                                      int* __restrict__ ulist, int* __restrict__ blk,
+                                                      int64_t* __restrict__ spart) {
   __shared__ __attribute__((aligned(16))) int8_t tl[2][2][kI8Rows * kI8Ld];  // [buffer][x, w]
   __shared__ int n_unc;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -897,8 +955,10 @@ __global__ __launch_bounds__(256, 2) void k_logits_i8(const int8_t* __restrict__
   // the last stage are clamped (those loads are never stored), so no load sits under a branch
   i8x16_t ga[8], gb[8];
   const int64_t nst = ncp / kI8Stage;  // even
+  const int64_t sb = SPLIT ? (int64_t)blockIdx.y * sps : 0;
+  const int64_t se = SPLIT ? (sb + sps < nst ? sb + sps : nst) : nst;  // stages [sb, se), an even count
   auto gload = [&](i8x16_t* g, int64_t s) {
-    const int64_t sc = s < nst ? s : nst - 1;
+    const int64_t sc = s < se ? s : se - 1;
 #pragma unroll
     for (int q = 0; q < 8; ++q) g[q] = *reinterpret_cast<const i8x16_t*>(src[q] + sc * (kI8Stage * kI8ChunkB));
   };
@@ -930,11 +990,11 @@ __global__ __launch_bounds__(256, 2) void k_logits_i8(const int8_t* __restrict__
           acc[d1 + d2] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[d1], bb[d2], acc[d1 + d2], 0, 0, 0);
     }
   };
-  gload(ga, 0);
-  gload(gb, 1);
+  gload(ga, sb);
+  gload(gb, sb + 1);
   lstore(ga, 0);
   __syncthreads();
-  for (int64_t s = 0; s < nst; s += 2) {
+  for (int64_t s = sb; s < se; s += 2) {
     gload(ga, s + 2);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiplies
     multiply(0);
@@ -961,27 +1021,57 @@ __global__ __launch_bounds__(256, 2) void k_logits_i8(const int8_t* __restrict__
       const int64_t hi = D0 + (D1 >> 8) + (D2 >> 16) + (D3 >> 24);
       const int64_t lo = (int64_t)acc[6][g] + ((int64_t)acc[5][g] << 8) + ((int64_t)acc[4][g] << 16) +
                          ((D3 & 0xFFFFFF) << 24) + ((D2 & 0xFFFF) << 32) + ((D1 & 0xFF) << 40);
-      const int xe = rexp[t], we = rexp[T + e];
-      const double rx = rres[t], rw = rres[T + e];
-      const int base = (xe - 30) + (we - 30);
-      float r;
-      if (rx == 0.0 && rw == 0.0) {
-        r = round_i128_f32(hi, lo, base);
+      if constexpr (SPLIT) {
+        int64_t* o = spart + 2 * (((int64_t)blockIdx.y * T + t) * E + e);
+        o[0] = hi;
+        o[1] = lo;
       } else {
-        const double S = ldexp((double)hi, base + 48) + ldexp((double)lo, base);  // one rounding
-        const double err = rx * ldexp(1.0, we) + ldexp(1.0, xe) * rw + fabs(S) * 0x1p-52;
-        if (!f32_certified(S, err, &r)) r = __builtin_nanf("");
-      }
-      logits[t * E + e] = r;
-      if (r != r) {
-        ++nu;
-        ulist[1 + atomicAdd(ulist, 1)] = (int)(t * E + e);
+        const float r = i8_round(hi, lo, rexp[t], rexp[T + e], rres[t], rres[T + e]);
+        logits[t * E + e] = r;
+        if (r != r) {
+          ++nu;
+          ulist[1 + atomicAdd(ulist, 1)] = (int)(t * E + e);
+        }
       }
     }
   }
-  if (nu) atomicAdd(&n_unc, nu);
+  if constexpr (!SPLIT) {
+    if (nu) atomicAdd(&n_unc, nu);
+    __syncthreads();
+    if (tid == 0) blk[b] = n_unc;
+  }
+}
+
+// Small batches: one thread per logit adds the K splits' exact partials (in
+// int64: |hi| < 2^26 and |lo| < 2^51 per split, at most 2^10 splits) and
+// rounds them; the unproven go to the list.
+__global__ __launch_bounds__(256) void k_fin_i8(int64_t T, int64_t E, int64_t s8,
+                                                const int64_t* __restrict__ spart, const int* __restrict__ rexp,
+                                                const double* __restrict__ rres, float* __restrict__ logits,
+                                                int* __restrict__ ulist, int* __restrict__ blk) {
+  __shared__ int n_unc;
+  const int tid = threadIdx.x;
+  if (tid == 0) n_unc = 0;
   __syncthreads();
-  if (tid == 0) blk[b] = n_unc;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + tid;
+  if (idx < T * E) {
+    const int64_t t = idx / E, e = idx % E;
+    int64_t hi = 0, lo = 0;
+#pragma unroll 8
+    for (int64_t z = 0; z < s8; ++z) {  // unrolled: the loads of 8 splits are in flight together
+      const int64_t* pz = spart + 2 * (z * T * E + idx);
+      hi += pz[0];
+      lo += pz[1];
+    }
+    const float r = i8_round(hi, lo, rexp[t], rexp[T + e], rres[t], rres[T + e]);
+    logits[idx] = r;
+    if (r != r) {
+      atomicAdd(&n_unc, 1);
+      ulist[1 + atomicAdd(ulist, 1)] = (int)idx;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) blk[blockIdx.x] = n_unc;
 }
 
 // The listed logits, exactly: each workgroup takes list entries blockIdx.x,
@@ -1196,20 +1286,29 @@ __global__ __launch_bounds__(64 * kSel4Tokens) void k_select256(
 
 void launch_slice8(const uint16_t* x, const uint16_t* w, int64_t T, int64_t E, int64_t H, int64_t ncp, int8_t* dig,
                    int* rexp, double* rres, double* norm, int* ulist, int* diag, hipStream_t st) {
-  const unsigned g = (unsigned)((T + E + 3) / 4);
-  const int64_t nc = (H / 16 + 63) / 64;  // half chunks per lane
-#define BSM_SLICE8(N) k_slice8<N><<<g, 256, 0, st>>>(x, w, T, E, H, ncp, dig, rexp, rres, norm, ulist, diag)
-  switch (nc) {
-    case 1: BSM_SLICE8(1); break;
-    case 2: BSM_SLICE8(2); break;
-    case 3: BSM_SLICE8(3); break;
-    case 4: BSM_SLICE8(4); break;
-    case 5: BSM_SLICE8(5); break;
-    case 6: BSM_SLICE8(6); break;
-    case 7: BSM_SLICE8(7); break;
-    case 8: BSM_SLICE8(8); break;
-    default: BSM_SLICE8(0); break;
+  // fewer rows than waves in flight on the chip: four waves per row
+  const bool few = T + E < 4096;
+  const unsigned g = (unsigned)(few ? T + E : (T + E + 3) / 4);
+  const int64_t nc = (H / 16 + (few ? 255 : 63)) / (few ? 256 : 64);  // half chunks per lane
+#define BSM_SLICE8(N, W) k_slice8<N, W><<<g, 256, 0, st>>>(x, w, T, E, H, ncp, dig, rexp, rres, norm, ulist, diag)
+#define BSM_SLICE8_NC(W)       \
+  switch (nc) {                \
+    case 1: BSM_SLICE8(1, W); break; \
+    case 2: BSM_SLICE8(2, W); break; \
+    case 3: BSM_SLICE8(3, W); break; \
+    case 4: BSM_SLICE8(4, W); break; \
+    case 5: BSM_SLICE8(5, W); break; \
+    case 6: BSM_SLICE8(6, W); break; \
+    case 7: BSM_SLICE8(7, W); break; \
+    case 8: BSM_SLICE8(8, W); break; \
+    default: BSM_SLICE8(0, W); break; \
   }
+  if (few) {
+    BSM_SLICE8_NC(4)
+  } else {
+    BSM_SLICE8_NC(1)
+  }
+#undef BSM_SLICE8_NC
 #undef BSM_SLICE8
 }
 
@@ -1241,20 +1340,34 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   const dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
   const dim3 glz(gl.x, gl.y, (unsigned)L.ks);
   // bf16 x and w at large batches: exact integer dot products on the int8 matrix cores
-  const bool i8 = BSM_ROUTE_I8 && L.i8ok && xb && wb;
-  int8_t* dig = reinterpret_cast<int8_t*>(ws + L.part);
+  const bool i8 = BSM_ROUTE_I8 && L.i8ok && xb && wb && (!L.rb || BSM_ROUTE_I8_SMALL);
+  int8_t* dig = reinterpret_cast<int8_t*>(ws + L.dig);
+  int64_t* spart = reinterpret_cast<int64_t*>(ws + L.spart);
   int* rexp = L.i8ok ? reinterpret_cast<int*>(ws + L.rexp) : nullptr;
   double* rres = L.i8ok ? reinterpret_cast<double*>(ws + L.rres) : nullptr;
+  if (i8) {  // the small-batch int8 path needs the norms and the list too
+    norm = reinterpret_cast<double*>(ws + L.norm);
+    ulist = reinterpret_cast<int*>(ws + L.ulist);
+  }
+  // workgroups whose list counts the selection kernel adds up
+  const int64_t nblk_used = i8 ? L.nblk8 : L.rb ? (int64_t)nrb : (int64_t)gl.x * gl.y;
   // one wave per token needs 256 experts, groups of a multiple of 4 and an aligned scores row
   const bool sel4 = BSM_SELECT_WAVE && E == 256 && (E / n_group) % 4 == 0 && topk <= 64 &&
                     ((uintptr_t)scores & 15) == 0;
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
-  if (L.rb) {                                                                                              \
+  if (i8 && L.rb) {                                                                                        \
+    launch_slice8(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), T, E, H, L.ncp,  \
+                  dig, rexp, rres, norm, ulist, diag, st);                                                 \
+    k_logits_i8<true><<<dim3(gl.x * gl.y, (unsigned)L.s8), 256, 0, st>>>(dig, T, E, L.ncp, L.sps8, rexp,     \
+                                                                         rres, logits, ulist, blk, spart); \
+    k_fin_i8<<<(unsigned)L.nblk8, 256, 0, st>>>(T, E, L.s8, spart, rexp, rres, logits, ulist, blk);          \
+  } else if (L.rb) {                                                                                       \
     k_logits_rb<XB, WB><<<nrb, 256, 0, st>>>(x, w, T, E, H, L.nadd, logits, blk, diag);                    \
   } else if (i8) {                                                                                         \
     launch_slice8(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), T, E, H, L.ncp,  \
                   dig, rexp, rres, norm, ulist, diag, st);                                                 \
-    k_logits_i8<<<gl.x * gl.y, 256, 0, st>>>(dig, T, E, L.ncp, rexp, rres, logits, ulist, blk);             \
+    k_logits_i8<false><<<gl.x * gl.y, 256, 0, st>>>(dig, T, E, L.ncp, L.sps8, rexp, rres, logits, ulist, blk, \
+                                                     nullptr);                                              \
   } else {                                                                                                 \
     if (vec)                                                                                               \
       k_rowstats<XB, WB, true><<<nrs, 256, 0, st>>>(x, w, T, E, H, norm, lsb);                             \
@@ -1267,13 +1380,13 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
     k_logits_fin<<<gl, 256, 0, st>>>(T, E, L.ks, part, norm, lsb, L.nadd, logits, ulist, blk, diag);        \
   }                                                                                                        \
   stage_mark(1, 1, st);                                                                                    \
-  if (!L.rb) k_exact_list<XB, WB><<<kExactWgs, 128, 0, st>>>(x, w, E, H, norm, T, ulist, logits);          \
+  if (!L.rb || i8) k_exact_list<XB, WB><<<kExactWgs, 128, 0, st>>>(x, w, E, H, norm, T, ulist, logits);    \
   if (sel4)                                                                                                \
     k_select256<<<(unsigned)((T + kSel4Tokens - 1) / kSel4Tokens), 64 * kSel4Tokens, 0, st>>>(                \
-        logits, T, (int)(E / n_group) / 4, topk_group, topk, ids, wts, scores, blk, L.nblk, diag);             \
+        logits, T, (int)(E / n_group) / 4, topk_group, topk, ids, wts, scores, blk, nblk_used, diag);          \
   else                                                                                                     \
     k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores,     \
-                                                  blk, L.nblk, diag);
+                                                  blk, nblk_used, diag);
   if (xb && wb) {
     BSM_ROUTE_DISPATCH(true, true)
   } else if (xb && !wb) {

@@ -128,14 +128,14 @@ def test_route_256_experts_group_sizes(gpu_lib, G, kg, k):
     _check(_run(gpu_lib, x, wr, G, kg, k), x, wr, G, kg, k)
 
 
-@pytest.mark.parametrize("H", [272, 1024])
-def test_route_int8_digit_path_edges(gpu_lib, H):
-    """bf16 x and w with at least 128 tiles of 64 x 64 take the int8 digit path: H with a zero-padded last chunk
-    (272) and without (1024), a ragged last token tile, all-zero token and expert rows, bf16 subnormals, rows
-    whose values span more than the 30-bit digit window (truncation residuals: the rounding proven by the bound or
-    the logit recomputed exactly) and cancelling rows."""
+@pytest.mark.parametrize("T,E,H", [(2050, 256, 272), (2050, 256, 1024), (37, 64, 528), (64, 256, 2048)])
+def test_route_int8_digit_path_edges(gpu_lib, T, E, H):
+    """bf16 x and w take the int8 digit path (at least 128 tiles of 64 x 64: one pass over K; fewer: K cut into
+    splits whose exact partials are added afterwards): H with a zero-padded last chunk (272, 528) and without,
+    ragged token and expert tiles, all-zero token and expert rows, bf16 subnormals, rows whose values span more
+    than the 30-bit digit window (truncation residuals: the rounding proven by the bound or the logit recomputed
+    exactly) and cancelling rows."""
     rng = np.random.default_rng(H)
-    T, E = 2050, 256
     x = W.to_bf16_f32(rng.standard_normal((T, H)).astype(np.float32))
     w = W.to_bf16_f32((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
     x[3] = 0.0
@@ -145,7 +145,7 @@ def test_route_int8_digit_path_edges(gpu_lib, H):
     x[13, 7] = 2.0 ** -40          # one value below the window of an otherwise ordinary row
     w[30, 0] = 2.0 ** 9
     w[41, 2] = 2.0 ** -50
-    rows = np.arange(100, T, 211)
+    rows = np.arange(20, T, 211)
     x[rows, 0] = 2.0 ** 20
     x[rows, 1] = -(2.0 ** 20)
     w[:, 0] = w[:, 1] = 1.0
