@@ -132,8 +132,8 @@ def test_route_256_experts_group_sizes(gpu_lib, G, kg, k):
 def test_route_int8_digit_path_edges(gpu_lib, T, E, H):
     """bf16 x and w take the int8 digit path (at least 128 tiles of 64 x 64: one pass over K; fewer: K cut into
     splits whose exact partials are added afterwards): H with a zero-padded last chunk (272, 528) and without,
-    ragged token and expert tiles, all-zero token and expert rows, bf16 subnormals, rows whose values span more
-    than the 30-bit digit window (truncation residuals: the rounding proven by the bound or the logit recomputed
+    ragged token and expert tiles, all-zero token and expert rows, bf16 subnormals, rows below 2^-100 (digits from
+    the integer fields) and near 2^100, rows whose values span more than the 30-bit digit window (truncation residuals: the rounding proven by the bound or the logit recomputed
     exactly) and cancelling rows."""
     rng = np.random.default_rng(H)
     x = W.to_bf16_f32(rng.standard_normal((T, H)).astype(np.float32))
@@ -145,6 +145,9 @@ def test_route_int8_digit_path_edges(gpu_lib, T, E, H):
     x[13, 7] = 2.0 ** -40          # one value below the window of an otherwise ordinary row
     w[30, 0] = 2.0 ** 9
     w[41, 2] = 2.0 ** -50
+    x[15] = W.to_bf16_f32(rng.standard_normal(H).astype(np.float32) * np.float32(2.0 ** -118))  # integer digits
+    w[43] = W.to_bf16_f32(rng.standard_normal(H).astype(np.float32) * np.float32(2.0 ** -110))
+    x[17] = W.to_bf16_f32(rng.standard_normal(H).astype(np.float32) * np.float32(2.0 ** 100))   # huge logits
     rows = np.arange(20, T, 211)
     x[rows, 0] = 2.0 ** 20
     x[rows, 1] = -(2.0 ** 20)
