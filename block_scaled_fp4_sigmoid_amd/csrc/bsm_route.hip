@@ -68,7 +68,7 @@ constexpr int kExactWgs = 1024;  // workgroups sharing the list of logits recomp
 
 // bf16 x bf16 tiled path on the int8 matrix cores (see k_slice8 below)
 constexpr int kI8Rows = 64;       // tokens and experts per workgroup
-constexpr int kI8ChunkB = 128;    // digit bytes per row and chunk of 32 k: [half of 16 k][digit][16 values]
+constexpr int kI8ChunkB = 128;    // digit bytes per row and chunk of 32 k (4 digits x 32 values)
 constexpr int kI8Stage = 2;       // chunks per LDS stage
 constexpr int kI8Ld = kI8Stage * kI8ChunkB + 16;  // LDS bytes per row and stage (16-byte pad)
 constexpr int kI8MaxH = 16384;    // keeps every int32 diagonal sum below 2^31
@@ -715,8 +715,10 @@ __global__ __launch_bounds__(256) void k_logits_fin(int64_t T, int64_t E, int ks
 // One wave per row (x rows 0..T-1, then w rows): the row's exponent bound X
 // (from the largest magnitude's bits: bf16 magnitudes order like their bit
 // patterns), its residual, a norm bound sqrt(H) max|v| (for the exact
-// recomputation), and its digits, laid out per chunk of 32 k as
-// [half of 16 k][digit][16 values], ncp chunks per row (zero past H).
+// recomputation), and its digits: a row is ncp / 2 stage blocks of 64 k, each
+// [digit][4 half chunks of 16 k][16 values] (zero past H).  A stage block is
+// what the logits kernel loads as one contiguous 256 bytes, and each store
+// instruction of a wave here writes runs of 64 bytes.
 // N = trunc(v 2^(30 - X)) comes from a binary32 scaling (exact: the result is
 // below 2^30) and a truncating conversion; v - N 2^(X - 30) is exact in
 // binary32 (the low bits of v's 8-bit significand), so a nonzero difference
@@ -853,9 +855,10 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
 #pragma unroll
       for (int c = 0; c < 4; ++c) o4[a][c] = 0u;
     if (data && live) slice16(u, ex, flt, res, o4);
-    uint4* o = reinterpret_cast<uint4*>(drow + 64 * (int64_t)j);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) o[a] = make_uint4(o4[a][0], o4[a][1], o4[a][2], o4[a][3]);
+    for (int a = 0; a < 4; ++a)
+      *reinterpret_cast<uint4*>(drow + 256 * (int64_t)(j >> 2) + 64 * a + 16 * (j & 3)) =
+          make_uint4(o4[a][0], o4[a][1], o4[a][2], o4[a][3]);
   };
   int j0 = lj;
   if constexpr (NC > 0) {
@@ -919,7 +922,7 @@ typedef int i32x16_t __attribute__((ext_vector_type(16)));
 // A workgroup owns 64 tokens x 64 experts, each of its 4 waves 32 x 32 on
 // v_mfma_i32_32x32x32_i8 with seven accumulators (one per digit diagonal j).
 // K goes in stages of two chunks through double-buffered LDS (rows padded by
-// 16 bytes).  Lane l of an operand carries row l % 32 and half l / 32 of a
+// 16 bytes; a stage block's [digit][half chunk] pieces stored as [half chunk][digit]).  Lane l of an operand carries row l % 32 and half l / 32 of a
 // chunk (the same k for both operands, which is all the sum needs); result
 // register 4q + i of lane l is token row 8q + 4 (l / 32) + i, expert l % 32.
 // With a multiple of 8 workgroups, the expert tiles of one token tile run on
@@ -940,16 +943,18 @@ __global__ __launch_bounds__(256, 2) void k_logits_i8(const int8_t* __restrict__
   const int64_t lt = (nwg % 8 == 0) ? (b % 8) * (nwg / 8) + b / 8 : b;
   const int64_t t0 = (lt / ne) * kI8Rows, e0 = (lt % ne) * kI8Rows;
   if (tid == 0) n_unc = 0;
-  // staging: 8 loads of 16 bytes per thread and stage; rows past T or E repeat the last row
+  // staging: 8 loads of 16 bytes per thread and stage (piece seg of the stage block: digit seg / 4, half
+  // chunk seg % 4); rows past T or E repeat the last row
   const int64_t rowb = ncp * kI8ChunkB;
   const int8_t* src[8];
   int dst[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int idx = q * 256 + tid, op = idx >> 10, rr = (idx >> 4) & 63, seg = idx & 15;
+    const int d = seg >> 2, hj = seg & 3;
     const int64_t row = op == 0 ? (t0 + rr < T ? t0 + rr : T - 1) : T + (e0 + rr < E ? e0 + rr : E - 1);
     src[q] = dig + row * rowb + seg * 16;
-    dst[q] = op * (kI8Rows * kI8Ld) + rr * kI8Ld + seg * 16;
+    dst[q] = op * (kI8Rows * kI8Ld) + rr * kI8Ld + (hj >> 1) * kI8ChunkB + (hj & 1) * 64 + d * 16;
   }
   // two register sets: a stage's digits are loaded two stages before they are multiplied; indices past
   // the last stage are clamped (those loads are never stored), so no load sits under a branch
