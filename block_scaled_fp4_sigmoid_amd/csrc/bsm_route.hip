@@ -1095,15 +1095,31 @@ __global__ __launch_bounds__(128) void k_exact_list(const void* __restrict__ x, 
   }
 }
 
+// Wave-wide maximum of a 64-bit key, returned to every lane.  Data-parallel
+// primitive moves: swaps within quads (lane ^ 1, lane ^ 2), mirrors within 8
+// and 16 lanes (after the quad steps each mirror pairs lanes of different
+// halves), then row broadcasts of lane 15 into rows 1 and 3 and of lane 31
+// into rows 2 and 3, which leaves the maximum in lane 63; lanes a step does
+// not write keep their own key (max with itself).
+template <int CTRL, int ROWS>
+__device__ inline uint64_t dpp_max_step(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false);
+  const uint64_t u = ((uint64_t)ohi << 32) | olo;
+  return u > v ? u : v;
+}
+
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    const uint64_t u = ((uint64_t)hi << 32) | lo;
-    v = u > v ? u : v;
-  }
-  return v;
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 constexpr int kMaxE = 1024;
