@@ -12,7 +12,7 @@
 // exactly rounded binary32 value of the exact dot product, and a score the
 // exactly rounded binary32 value of 1/(1+exp(-l)):
 //
-//   k_logits_rb   small batches: 4 tokens x 8 experts per workgroup over the
+//   k_logits_rb   small batches, fp32 x or w: 4 tokens x 8 experts per workgroup over the
 //                 whole row (lanes own K slices); binary64 FMA accumulation of
 //                 products that are exact in binary64, and binary64 sums of
 //                 squares of the workgroup's rows (an upper bound of each
@@ -21,25 +21,25 @@
 //                 for the rest, by exactness (lowest set bits of its two
 //                 rows); failing both, the workgroup recomputes it
 //                 exactly (fixed-point window / superaccumulator, rounded once)
-//   k_rowstats    large batches: per row of x and w, an upper bound of the
+//   k_rowstats    large batches, fp32 x or w: per row of x and w, an upper bound of the
 //                 2-norm and the lowest set-bit exponent of its nonzero entries
 //   k_logits      large batches: 64x64 double-buffered LDS tiles, 8x4 logits
 //                 per thread, K cut into slices (binary64 partial sums)
 //   k_logits_fin  large batches: adds the slices in order, tries exactness
 //                 first, then the error bound, and lists the rest
-//   k_exact_list  large batches: the listed logits recomputed exactly, one
+//   k_exact_list  the listed logits (tiled binary64 and int8 paths) recomputed exactly, one
 //                 workgroup per logit
 //   k_select      one workgroup per token: certified binary64 sigmoid
 //                 (double-double fallback), group top-2 sums, group
 //                 selection, iterative 64-bit (score, index) argmax,
 //                 normalization.
-//   k_slice8      large batches, bf16 x and w: per row an exponent bound, a
-//                 truncation residual, a norm bound, and four int8 digits of
-//                 every value
-//   k_logits_i8   large batches, bf16 x and w: the dot products as exact
-//                 int32 digit sums on the int8 matrix cores, rounded once;
-//                 rows with a residual prove the rounding by a bound or list
-//                 the logit for k_exact_list
+//   k_slice8      bf16 x and w: per row an exponent bound, a truncation
+//                 residual, a norm bound, and four int8 digits of every value
+//   k_logits_i8   bf16 x and w: the dot products as exact int32 digit sums on
+//                 the int8 matrix cores, rounded once; rows with a residual
+//                 prove the rounding by a bound or list the logit for
+//                 k_exact_list.  Small batches cut K into splits and store
+//                 exact partials, which k_fin_i8 adds and rounds
 //   k_select256   256 experts: the same selection, one wave per token with
 //                 four experts per lane and shuffles in place of LDS.
 
@@ -693,8 +693,8 @@ __global__ __launch_bounds__(256) void k_logits_fin(int64_t T, int64_t E, int ks
 }
 
 // ---------------------------------------------------------------------------
-// Large batches with bf16 x and w: the dot products in exact integer
-// arithmetic on the int8 matrix cores.
+// bf16 x and w: the dot products in exact integer arithmetic on the int8
+// matrix cores (fp32 inputs take the binary64 kernels above).
 //
 // Every bf16 value is m * 2^l with an integer m < 2^8.  For a row (of x or of
 // w) with every |v_k| < 2^X, N_k = trunc(v_k * 2^(30 - X)) is an integer with
@@ -712,7 +712,7 @@ __global__ __launch_bounds__(256) void k_logits_fin(int64_t T, int64_t E, int ks
 // exact-recomputation list like the binary64 path's.
 // ---------------------------------------------------------------------------
 
-// One wave per row (x rows 0..T-1, then w rows): the row's exponent bound X
+// One wave per row (four when rows are few; x rows 0..T-1, then w rows): the row's exponent bound X
 // (from the largest magnitude's bits: bf16 magnitudes order like their bit
 // patterns), its residual, a norm bound sqrt(H) max|v| (for the exact
 // recomputation), and its digits: a row is ncp / 2 stage blocks of 64 k, each
