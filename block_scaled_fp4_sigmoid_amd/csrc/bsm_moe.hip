@@ -122,7 +122,8 @@ __device__ inline void wg_amax_atomic(float hmax, uint32_t* h_amax) {
 // ---------------------------------------------------------------------------
 // One workgroup per 64-token chunk: every (token, slot) pair ORs its token bit
 // into the chunk's LDS mask of its expert (order independent), then the masks
-// and their popcounts are written out.
+// ([expert][chunk]) and their popcounts ([chunk][expert], so that the scan's
+// loads of one chunk are contiguous over the experts) are written out.
 __global__ __launch_bounds__(256) void k_perm_masks(const int32_t* __restrict__ ids, int64_t T, int topk, int64_t E,
                                                     int64_t nc, uint64_t* __restrict__ masks,
                                                     int* __restrict__ cnt) {
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void k_perm_masks(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e < E; e += 256) {
     const uint64_t m = lm[e];
     masks[e * nc + c] = m;
-    cnt[e * nc + c] = __popcll(m);
+    cnt[c * E + e] = __popcll(m);
   }
 }
 
@@ -163,16 +164,15 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int* __restrict__ cnt,
   int total = 0;
   if (e < E) {
     // 32 chunk counts in flight per batch (independent loads, clamped in range), then their prefix
-    const int* ce = cnt + (int64_t)e * nc;
-    int* be = base + (int64_t)e * nc;
+    // counts and bases are [chunk][expert]: each load and store of a wave covers 64 consecutive experts
     for (int64_t c0 = 0; c0 < nc; c0 += 32) {
       int v[32];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) v[q] = ce[c0 + q < nc ? c0 + q : nc - 1];
+      for (int q = 0; q < 32; ++q) v[q] = cnt[(c0 + q < nc ? c0 + q : nc - 1) * E + e];
 #pragma unroll
       for (int q = 0; q < 32; ++q) {
         if (c0 + q < nc) {
-          be[c0 + q] = total;
+          base[(c0 + q) * E + e] = total;
           total += v[q];
         }
       }
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int* __restrict__ cnt,
   if (e == 0) *h_amax = 0u;
 }
 
-__global__ __launch_bounds__(256) void k_perm_rows(const int32_t* __restrict__ ids, int64_t P, int topk, int64_t nc,
+__global__ __launch_bounds__(256) void k_perm_rows(const int32_t* __restrict__ ids, int64_t P, int topk, int64_t E, int64_t nc,
                                                    const uint64_t* __restrict__ masks, const int* __restrict__ base,
                                                    const int* __restrict__ offsets, int* __restrict__ row_pair,
                                                    int* __restrict__ pair_row) {
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void k_perm_rows(const int32_t* __restrict__ i
   const int64_t c = t / kChunk;
   const uint32_t bit = (uint32_t)(t % kChunk);
   const uint64_t below = bit ? (masks[e * nc + c] & ((1ull << bit) - 1ull)) : 0ull;
-  const int pos = offsets[e] + base[e * nc + c] + __popcll(below);
+  const int pos = offsets[e] + base[c * E + e] + __popcll(below);
   row_pair[pos] = (int)p;
   pair_row[p] = pos;
 }
@@ -1973,7 +1973,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     k_perm_masks<<<(unsigned)L.n_chunks, 256, 0, st>>>(a.ids, a.T, a.topk, a.E, L.n_chunks, masks, ccnt);
     k_perm_scan<<<1, 1024, 0, st>>>(ccnt, a.E, L.n_chunks, cbase, counts, offsets, tiles, ntiles, tiles_w, ntiles_w,
                                      h_amax);
-    k_perm_rows<<<(unsigned)((L.P + 255) / 256), 256, 0, st>>>(a.ids, L.P, a.topk, L.n_chunks, masks, cbase,
+    k_perm_rows<<<(unsigned)((L.P + 255) / 256), 256, 0, st>>>(a.ids, L.P, a.topk, a.E, L.n_chunks, masks, cbase,
                                                                 offsets, row_pair, pair_row);
   }
 #ifndef BSM_SKINNY_NT
