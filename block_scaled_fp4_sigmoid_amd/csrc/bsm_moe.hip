@@ -18,11 +18,9 @@
 // FP16 (weight-only W4A16: BF16) and run FP16 MFMA with FP32 accumulation
 // (16x16x32 in the few-row kernels, 32x32x16 in the many-row one); the global
 // scales (NVFP4) or the per-row x per-column scales (FP8) multiply the FP32
-// accumulator in the epilogue.  One exception: the FP8 down projection of
-// many-row experts runs the FP8 matrix cores on the raw E4M3 codes.  Their
-// block accumulation is not exact (about 2^-13 relative per 64 products), which
-// y, never re-quantized, absorbs; the gate/up projection, whose h is
-// re-quantized, stays on FP16.
+// accumulator in the epilogue.  gfx950's FP8/FP4 matrix cores are not used:
+// their scaled MFMA adds each group of products with a fixed-point alignment
+// to the largest one, which is not an FP32 accumulation.
 //
 // Pipeline (all on the caller's stream, no host synchronization):
 //   k_perm_masks   per 64-token chunk: LDS bit mask of the chunk's tokens for
@@ -44,8 +42,8 @@
 //   k_dense_f8<G1> FP8 with one expert and at most 64 rows (dense layers)
 //   h quantize     NVFP4 with one global scale over all rows / FP8 per row,
 //                  plus the FP16 decoded copy the down GEMM reads
-//   k_skinny_rows<!G1> / k_skinny<!G1>, k_gemm_big<!G1> (FP8: k_gemm_f8_down3)
-//                  down projection -> y (FP32)
+//   k_skinny_rows<!G1> / k_skinny<!G1>, k_gemm_big<!G1> (k_gemm_wide when
+//                  I % 256 != 0): down projection -> y (FP32)
 //   k_combine      out[t] = scale * sum_j w[t,j] * y[row(t,j)] (binary64 sum
 //                  in slot order, rounded once)
 //
@@ -55,11 +53,6 @@
 #include <algorithm>
 
 #include "bsm_internal.h"
-
-// skinny kernel: 16-row weight tiles per wave (2 x 16 rows = 32 weight rows)
-#ifndef BSM_SKINNY_NT
-#define BSM_SKINNY_NT 2
-#endif
 
 namespace bsm {
 
@@ -71,6 +64,14 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerTile = 16;
 constexpr int kChunk = 64;  // tokens per permutation chunk
+// Few-row (skinny) kernels: each wave owns kSkNT tiles of 16 weight rows; K is walked in super-steps of
+// 4 x kNvKB (NVFP4) or 4 x kF8KB (FP8) values; FP8 keeps kSkDepthF8 super-steps of codes in flight per
+// lane (NVFP4 one).  Measured at decode-64: NVFP4 gate/up 0.62 ms at depth 1 against 0.66 ms at depth 2
+// (occupancy 3 -> 2 workgroups per CU); FP8 1.01 -> 0.995 ms with depth 2.
+constexpr int kSkNT = 2;
+constexpr int kNvKB = 128;
+constexpr int kF8KB = 64;
+constexpr int kSkDepthF8 = 2;
 
 // FP16 high bytes of the E2M1 magnitudes {0, .5, 1, 1.5 | 2, 3, 4, 6}
 __device__ inline h2v scale_pair(uint32_t code) {
@@ -602,7 +603,7 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
     const float* __restrict__ a_rs, const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc,
     const float* __restrict__ wgs, const int4* __restrict__ tiles, const int* __restrict__ ntiles, int64_t K, int64_t H,
     int64_t I, float* __restrict__ out, uint32_t* __restrict__ h_amax) {
-  constexpr int KB = NV ? 128 : 64;
+  constexpr int KB = NV ? kNvKB : kF8KB;
   constexpr int KS = 4 * KB;  // k per super-step
   constexpr int VPU = SkGeom<NV>::VPU;
   constexpr int kSV = KB / 32;
@@ -1149,9 +1150,6 @@ __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict
 // 8q + 4 (l / 32) + j, column l % 32.
 // ---------------------------------------------------------------------------
 constexpr int kGBM = 128, kGBN = 256, kGBK = 64;
-#ifndef BSM_BIG_ADMA
-#define BSM_BIG_ADMA 1  // activation tiles by direct-to-LDS loads (0: through registers)
-#endif
 template <bool NV>
 struct BigB {
   static constexpr int kRow = NV ? 36 : 72;  // LDS bytes per weight row and K step (+4 / +8 pad)
@@ -1186,7 +1184,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   // row r stored at chunk c ^ ((r >> 1) & 7), which keeps the fragment reads of 16 consecutive rows
   // on distinct banks.  FP8 (measured slower that way) stages it through registers into padded rows.
   // Two separate arrays, so the compiler sees that loads into one do not alias reads of the other.
-  constexpr bool kAdma = BSM_BIG_ADMA && NV;
+  constexpr bool kAdma = NV;
   constexpr int kAS = kAdma ? kGBK : kGBK + 8;  // LDS row stride (f16)
   __shared__ __attribute__((aligned(16))) _Float16 As0[kGBM][kAS];
   __shared__ __attribute__((aligned(16))) _Float16 As1[kGBM][kAS];
@@ -1427,260 +1425,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// FP8_DYNAMIC down projection for many rows per expert on the FP8 matrix
-// cores ("f8"): the E4M3 codes of h and of the weights go into
-// v_mfma_scale_f32_32x32x64_f8f6f4 as they are (both operands E4M3, block
-// scale 2^0), and the per-row and per-channel scales multiply the FP32 result
-// in the epilogue, where they factor out of the sum.  Products of two E4M3
-// values are exact; the matrix core adds each group of 64 of them with a
-// fixed-point alignment to the largest before the FP32 accumulator, which
-// carries more rounding than an FP32 chain (relative L2 about 1.4e-5 per
-// 64-product block on normal data).  y is combined, never requantized, so
-// that error reaches the layer output unamplified.  (The gate/up projection
-// stays on exactly decoded FP16 operands: h is requantized to E4M3 per row,
-// and an error of that size flips codes near rounding boundaries, each by up
-// to 1/8 of the value.)  128 rows x 256 weight rows per workgroup, 4 waves of
-// 128 rows x 64 weight rows (4 x 2 tiles of 32 x 32), K in steps of 64 (one
-// MFMA K) through double-buffered LDS.  Operand layout: lane l carries row /
-// column l % 32 and k bytes 32 (l / 32) .. +31 of the step.
-// ---------------------------------------------------------------------------
-typedef int i8v __attribute__((ext_vector_type(8)));
-constexpr int kF8Row = 80;  // LDS bytes per row and K step: 64 + 16 pad (conflict-free 16-byte reads)
-
-__global__ __launch_bounds__(256, 2) void k_gemm_f8_down(const uint8_t* __restrict__ ac, const float* __restrict__ a_rs,
-                                                         const uint8_t* __restrict__ wc, const float* __restrict__ wsc,
-                                                         const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-                                                         int64_t K, int64_t H, float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][kGBM][kF8Row];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kGBN][kF8Row];
-  if ((int)blockIdx.y >= *ntiles) return;
-  const int4 ti = tiles[blockIdx.y];
-  const int e = ti.x, row0 = ti.y, nrows = ti.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, lh = lane >> 5;
-  const int64_t c0 = (int64_t)blockIdx.x * kGBN;
-  // staging: 4 lanes per 64-byte row segment; h rows 64 i + tid / 4 (i < 2), weight rows 64 i + tid / 4 (i < 4)
-  const int part = tid & 3, srow = tid >> 2;
-  auto arow = [&](int i) -> const uint8_t* {
-    const int r = 64 * i + srow;
-    const int ar = r < nrows ? r : nrows - 1;
-    return ac + (int64_t)(row0 + ar) * K + 16 * part;
-  };
-  const uint8_t *as0 = arow(0), *as1 = arow(1);
-  const uint8_t* bbase = wc + ((int64_t)e * H + c0) * K + 16 * part;
-  auto boff = [&](int i) -> uint32_t { return (uint32_t)((64 * i + srow) * K); };
-  const uint32_t bo0 = boff(0), bo1 = boff(1), bo2 = boff(2), bo3 = boff(3);
-  uint4 ra0, ra1, rb0, rb1, rb2, rb3;
-  auto gload = [&](int s) {
-    const int64_t k0 = (int64_t)s * kGBK;
-    ra0 = *reinterpret_cast<const uint4*>(as0 + k0);
-    ra1 = *reinterpret_cast<const uint4*>(as1 + k0);
-    const uint8_t* bs = bbase + k0;
-    rb0 = *reinterpret_cast<const uint4*>(bs + bo0);
-    rb1 = *reinterpret_cast<const uint4*>(bs + bo1);
-    rb2 = *reinterpret_cast<const uint4*>(bs + bo2);
-    rb3 = *reinterpret_cast<const uint4*>(bs + bo3);
-  };
-  auto lstore = [&](int buf) {
-    *reinterpret_cast<uint4*>(&As[buf][srow][16 * part]) = ra0;
-    *reinterpret_cast<uint4*>(&As[buf][64 + srow][16 * part]) = ra1;
-    *reinterpret_cast<uint4*>(&Bs[buf][srow][16 * part]) = rb0;
-    *reinterpret_cast<uint4*>(&Bs[buf][64 + srow][16 * part]) = rb1;
-    *reinterpret_cast<uint4*>(&Bs[buf][128 + srow][16 * part]) = rb2;
-    *reinterpret_cast<uint4*>(&Bs[buf][192 + srow][16 * part]) = rb3;
-  };
-  auto frag = [](const uint8_t* p) -> i8v {
-    const uint4 u0 = *reinterpret_cast<const uint4*>(p);
-    const uint4 u1 = *reinterpret_cast<const uint4*>(p + 16);
-    i8v v;
-    v[0] = (int)u0.x; v[1] = (int)u0.y; v[2] = (int)u0.z; v[3] = (int)u0.w;
-    v[4] = (int)u1.x; v[5] = (int)u1.y; v[6] = (int)u1.z; v[7] = (int)u1.w;
-    return v;
-  };
-  // LDS weight row of this wave's N tile t
-  auto brow0 = [&](int t) -> int { return 64 * wave + 32 * t; };
-
-  f16v acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[mt][t][q] = 0.0f;
-
-  const int nk = (int)(K / kGBK);
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
-    i8v a[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) a[mt] = frag(&As[buf][mt * 32 + l32][32 * lh]);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const i8v b = frag(&Bs[buf][brow0(t) + l32][32 * lh]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt], b, acc[mt][t], 0, 0, 0, 127, 0, 127);
-    }
-    if (ks + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ro = mt * 32 + 8 * q + 4 * lh + j;
-        if (ro >= nrows) continue;
-        const int r = 4 * q + j;
-        float* yr = out + (int64_t)(row0 + ro) * H;
-        const float* ws = wsc + (int64_t)e * H;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int64_t col = c0 + 64 * wave + 32 * t + l32;
-          yr[col] = acc[mt][t][r] * a_rs[row0 + ro] * ws[col];
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// FP8 down projection, three-stage direct-to-LDS pipeline: the same tile,
-// waves and MFMA as k_gemm_f8_down, with each K step's E4M3 h rows (128 x 64 B)
-// and weight rows (256 x 64 B) loaded straight into LDS
-// (global_load_lds_dwordx4: a load fills 16 unpadded 64-byte rows) two steps
-// ahead, into three buffers.  Chunk c of row r sits at chunk c ^ ((r >> 2) & 3),
-// which keeps the 16-byte fragment reads of 16 consecutive rows on distinct
-// banks.  Each buffer is its own LDS array and a step's loads and multiplies
-// sit in one function with restrict-qualified tile pointers, so the compiler
-// sees that the loads do not alias the reads; the barriers are LDS-only and
-// the loads are waited for explicitly (a workgroup fence would wait for all).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void k_gemm_f8_down3(const uint8_t* __restrict__ ac, const float* __restrict__ a_rs,
-                                                          const uint8_t* __restrict__ wc, const float* __restrict__ wsc,
-                                                          const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-                                                          int64_t K, int64_t H, float* __restrict__ out) {
-  constexpr int kR = kGBK;  // LDS bytes per row and K step (unpadded)
-  __shared__ __attribute__((aligned(16))) uint8_t A0[kGBM * kR];
-  __shared__ __attribute__((aligned(16))) uint8_t A1[kGBM * kR];
-  __shared__ __attribute__((aligned(16))) uint8_t A2[kGBM * kR];
-  __shared__ __attribute__((aligned(16))) uint8_t B0[kGBN * kR];
-  __shared__ __attribute__((aligned(16))) uint8_t B1[kGBN * kR];
-  __shared__ __attribute__((aligned(16))) uint8_t B2[kGBN * kR];
-  if ((int)blockIdx.y >= *ntiles) return;
-  const int4 ti = tiles[blockIdx.y];
-  const int e = ti.x, row0 = ti.y, nrows = ti.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, lh = lane >> 5;
-  const int64_t c0 = (int64_t)blockIdx.x * kGBN;
-  // load i of wave w fills rows 16 (n w + i) .. + 15 (n = 2 for h, 4 for weights); lane l writes
-  // chunk l % 4 of row 16 (n w + i) + l / 4, which holds the row's logical chunk (l % 4) ^ ((row >> 2) & 3)
-  auto src_chunk = [&](int r) { return (lane & 3) ^ ((r >> 2) & 3); };
-  const uint8_t* ap[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 16 * (2 * wave + i) + (lane >> 2);
-    const int ar = r < nrows ? r : nrows - 1;
-    ap[i] = ac + (int64_t)(row0 + ar) * K + 16 * src_chunk(r);
-  }
-  const uint8_t* bp[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * (4 * wave + i) + (lane >> 2);
-    bp[i] = wc + ((int64_t)e * H + c0 + r) * K + 16 * src_chunk(r);
-  }
-  auto load = [&](int s, uint8_t* __restrict__ a, uint8_t* __restrict__ b) {
-    const int64_t k0 = (int64_t)s * kGBK;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(ap[i] + k0, a + 16 * (2 * wave + i) * kR, 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds(bp[i] + k0, b + 16 * (4 * wave + i) * kR, 16, 0, 0);
-  };
-  // fragment of row r: logical chunks 2 lh, 2 lh + 1 (32 bytes), swizzle (r >> 2) & 3 = (l32 >> 2) & 3
-  const int sw = (l32 >> 2) & 3;
-  const int p0 = 16 * ((2 * lh) ^ sw), p1 = 16 * ((2 * lh + 1) ^ sw);
-  auto frag = [&](const uint8_t* row) -> i8v {
-    const uint4 u0 = *reinterpret_cast<const uint4*>(row + p0);
-    const uint4 u1 = *reinterpret_cast<const uint4*>(row + p1);
-    i8v v;
-    v[0] = (int)u0.x; v[1] = (int)u0.y; v[2] = (int)u0.z; v[3] = (int)u0.w;
-    v[4] = (int)u1.x; v[5] = (int)u1.y; v[6] = (int)u1.z; v[7] = (int)u1.w;
-    return v;
-  };
-  f16v acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[mt][t][q] = 0.0f;
-  const int nk = (int)(K / kGBK);
-  // loads of step snext into (wa, wb), then the multiplies of step s from (ra, rb) unless s is past the end
-  auto step = [&](int s, int snext, uint8_t* __restrict__ wa, uint8_t* __restrict__ wb,
-                  const uint8_t* __restrict__ ra, const uint8_t* __restrict__ rb) {
-    load(snext < nk ? snext : nk - 1, wa, wb);
-    __builtin_amdgcn_sched_barrier(0);
-    if (s < nk) {
-      i8v a[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = frag(ra + (mt * 32 + l32) * kR);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const i8v b = frag(rb + (64 * wave + 32 * t + l32) * kR);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[mt], b, acc[mt][t], 0, 0, 0, 127, 0, 127);
-      }
-    }
-    // the loads of step s + 1 (issued one step earlier) are complete once at most this step's 6 are
-    // in flight; then the barrier publishes every wave's rows
-    __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6), expcnt and lgkmcnt not waited for
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  };
-  load(0, A0, B0);
-  load(1 < nk ? 1 : 0, A1, B1);
-  __builtin_amdgcn_s_waitcnt(0x0F76);  // step 0's loads complete
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  for (int s = 0; s < nk; s += 3) {
-    step(s, s + 2, A2, B2, A0, B0);
-    step(s + 1, s + 3, A0, B0, A1, B1);
-    step(s + 2, s + 4, A1, B1, A2, B2);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // no load in flight at the end
-
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ro = mt * 32 + 8 * q + 4 * lh + j;
-        if (ro >= nrows) continue;
-        const int r = 4 * q + j;
-        float* yr = out + (int64_t)(row0 + ro) * H;
-        const float* ws = wsc + (int64_t)e * H;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int64_t col = c0 + 64 * wave + 32 * t + l32;
-          yr[col] = acc[mt][t][r] * a_rs[row0 + ro] * ws[col];
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -1881,18 +1625,15 @@ hipError_t launch_fp8_linear(const uint8_t* xc, const float* xs, const uint8_t* 
   k_dense_tiles<<<1, 64, 0, st>>>(T, tiles_s, ntiles_s, tiles_w, ntiles_w, amax);
   const int64_t xblk = T * K / 16;
   k_decode_act<false><<<(unsigned)((xblk + 255) / 256), 256, 0, st>>>(xc, nullptr, xblk, act);
-#ifndef BSM_FP8_KB
-#define BSM_FP8_KB 64
-#endif
-  const dim3 gs((unsigned)(N / (64 * BSM_SKINNY_NT)), (unsigned)L.max_s);
+  const dim3 gs((unsigned)(N / (64 * kSkNT)), (unsigned)L.max_s);
   const dim3 gw((unsigned)(N / 128), (unsigned)(L.max_w > 0 ? L.max_w : 1));
   if (T <= kSkinnyMaxRows) {
-    if (K % (4 * BSM_FP8_KB) == 0)
-      k_skinny<false, false, BSM_FP8_KB, BSM_SKINNY_NT><<<gs, 256, 0, st>>>(
+    if (K % (4 * kF8KB) == 0)
+      k_skinny<false, false, kF8KB, kSkNT><<<gs, 256, 0, st>>>(
           act, nullptr, 1, nullptr, xs, wc, reinterpret_cast<const uint8_t*>(wsc), nullptr, tiles_s, ntiles_s, K, N, 0,
           out, amax);
     else
-      k_skinny<false, false, 32, BSM_SKINNY_NT><<<gs, 256, 0, st>>>(
+      k_skinny<false, false, 32, kSkNT><<<gs, 256, 0, st>>>(
           act, nullptr, 1, nullptr, xs, wc, reinterpret_cast<const uint8_t*>(wsc), nullptr, tiles_s, ntiles_s, K, N, 0,
           out, amax);
   } else {
@@ -1976,28 +1717,8 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     k_perm_rows<<<(unsigned)((L.P + 255) / 256), 256, 0, st>>>(a.ids, L.P, a.topk, a.E, L.n_chunks, masks, cbase,
                                                                 offsets, row_pair, pair_row);
   }
-#ifndef BSM_SKINNY_NT
-#define BSM_SKINNY_NT 2
-#endif
-// super-steps of weight codes in flight per lane (measured at decode-64: NVFP4 gate/up 0.62 ms at depth 1,
-// 0.66 ms at depth 2 with occupancy 3 -> 2; FP8 1.01 -> 0.995 ms with depth 2, occupancy 4 -> 3)
-#ifndef BSM_SKINNY_DEPTH
-#define BSM_SKINNY_DEPTH 1
-#endif
-#ifndef BSM_SKINNY_DEPTH_FP8
-#define BSM_SKINNY_DEPTH_FP8 2
-#endif
-#ifndef BSM_SKINNY_ROWS
-#define BSM_SKINNY_ROWS 1  // few-row experts: activation rows staged in chunks of K, no barrier per super-step
-#endif
-#ifndef BSM_SKR_DEPTH_FP8
-#define BSM_SKR_DEPTH_FP8 2  // FP8: super-steps of weight codes in flight per lane in k_skinny_rows
-#endif
-  const dim3 g1((unsigned)(a.I / (32 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 8*NT h columns
-  const dim3 g2((unsigned)(a.H / (64 * BSM_SKINNY_NT)), (unsigned)L.max_tiles);  // 4 waves x 16*NT y columns
-#ifndef BSM_PREFILL_BIG
-#define BSM_PREFILL_BIG 1  // many-row experts on the 32x32x16 kernel (0: the 16x16x32 one)
-#endif
+  const dim3 g1((unsigned)(a.I / (32 * kSkNT)), (unsigned)L.max_tiles);  // 4 waves x 8*NT h columns
+  const dim3 g2((unsigned)(a.H / (64 * kSkNT)), (unsigned)L.max_tiles);  // 4 waves x 16*NT y columns
   // One permutation chunk (T <= kChunk) counts an expert's rows over a kChunk-bit token mask, so no
   // expert exceeds kSkinnyMaxRows rows and the many-row kernels have no tiles: they are not launched.
   static_assert(kChunk <= kSkinnyMaxRows, "a single chunk never yields a many-row expert");
@@ -2005,10 +1726,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   // dense FP8 MLP (one expert, top-1, at most kDenseRows tokens): every workgroup covers all rows
   const bool dense = !a.nvfp4 && !a.a16 && a.E == 1 && a.topk == 1 && a.T <= kDenseRows;
   float* part = reinterpret_cast<float*>(ws + L.part);
-  // the NVFP4 many-row kernel reads weights in groups of 4 K steps (K % 256 == 0): always for the gate/up
+  // the many-row kernel reads weights in groups of 4 K steps (K % 256 == 0): always for the gate/up
   // projection (H % 256 == 0), for the down projection when I % 256 == 0 (else the 16x16x32 kernel)
-  const bool big_dn = BSM_PREFILL_BIG && a.I % 256 == 0;
-  const dim3 w1((unsigned)(a.I / (BSM_PREFILL_BIG ? kGBN / 2 : 64)), (unsigned)L.max_tiles_w);
+  const bool big_dn = a.I % 256 == 0;
+  const dim3 w1((unsigned)(a.I / (kGBN / 2)), (unsigned)L.max_tiles_w);
   const dim3 w2((unsigned)(a.H / (big_dn ? kGBN : 128)), (unsigned)L.max_tiles_w);
   _Float16* act = reinterpret_cast<_Float16*>(ws + L.act_f16);
   _Float16* hdec = reinterpret_cast<_Float16*>(ws + L.h_f16);
@@ -2024,127 +1745,80 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   const uint8_t* w13s = reinterpret_cast<const uint8_t*>(a.w13_scales);
   const uint8_t* w2s = reinterpret_cast<const uint8_t*>(a.w2_scales);
   const float* xrs = reinterpret_cast<const float*>(a.x_scales);
-#define BSM_G1(NV, KB)                                                                                          \
-  if (BSM_SKINNY_ROWS && KB == (NV ? 128 : BSM_FP8_KB))                                                        \
-    k_skinny_rows<NV, true, BSM_SKINNY_NT, false, NV ? 1 : BSM_SKR_DEPTH_FP8><<<g1, 256, 0, st>>>(                               \
-        act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32,    \
-        h_amax);                                                                                                \
-  else                                                                                                          \
-  k_skinny<NV, true, KB, BSM_SKINNY_NT, false, NV ? BSM_SKINNY_DEPTH : BSM_SKINNY_DEPTH_FP8><<<g1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes,  \
-                                                            w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I,     \
-                                                            h_f32, h_amax);                                   \
-  if (many) (BSM_PREFILL_BIG ? k_gemm_big<NV, true> : k_gemm_wide<NV, true>)<<<w1, 256, 0, st>>>(                      \
-      act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,                                        \
-                                            tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
-#define BSM_G2(NV, KB)                                                                                         \
-  if (BSM_SKINNY_ROWS && KB == (NV ? 128 : BSM_FP8_KB))                                                       \
-    k_skinny_rows<NV, false, BSM_SKINNY_NT, false, NV ? 1 : BSM_SKR_DEPTH_FP8><<<g2, 256, 0, st>>>(                             \
-        hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), a.w2_codes, w2s, a.w2_gs, tiles, \
-        ntiles, a.I, a.H, a.I, y, h_amax);                                                                     \
+  const float* hsc = reinterpret_cast<const float*>(h_scales);  // FP8: per-row h scales
+  // Few-row experts: k_skinny_rows when K is a multiple of its super-step (NVFP4 512, FP8 256 values),
+  // else k_skinny with 32-value quarters; many-row experts: k_gemm_big (k_gemm_wide for the down
+  // projection when I % 256 != 0).
+#define BSM_G1(NV)                                                                                             \
+  if (a.H % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                                   \
+    k_skinny_rows<NV, true, kSkNT, false, NV ? 1 : kSkDepthF8><<<g1, 256, 0, st>>>(                            \
+        act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32,  \
+        h_amax);                                                                                               \
   else                                                                                                         \
-  k_skinny<NV, false, KB, BSM_SKINNY_NT, false, NV ? BSM_SKINNY_DEPTH : BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales), \
-                                              a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
-  if (many) (big_dn ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                    \
-      hdec, row_pair, a.topk, h_gs, reinterpret_cast<const float*>(h_scales),                                \
-                                             a.w2_codes, w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
-#ifndef BSM_NV_KB
-#define BSM_NV_KB 128
-#endif
+    k_skinny<NV, true, 32, kSkNT, false, NV ? 1 : kSkDepthF8><<<g1, 256, 0, st>>>(                             \
+        act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32,  \
+        h_amax);                                                                                               \
+  if (many)                                                                                                    \
+    k_gemm_big<NV, true><<<w1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, \
+                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
+#define BSM_G2(NV, HSC)                                                                                        \
+  if (a.I % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                                   \
+    k_skinny_rows<NV, false, kSkNT, false, NV ? 1 : kSkDepthF8><<<g2, 256, 0, st>>>(                           \
+        hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
+  else                                                                                                         \
+    k_skinny<NV, false, 32, kSkNT, false, NV ? 1 : kSkDepthF8><<<g2, 256, 0, st>>>(                            \
+        hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
+  if (many)                                                                                                    \
+    (big_dn ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                             \
+        hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
   hipError_t err;
   if (a.a16) {
     // weight-only W4A16: BF16 activations, NVFP4 weights decoded to BF16, h rounded to BF16
-#define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K, KB)                                               \
-  if (BSM_SKINNY_ROWS && KB == 128)                                                                            \
-    k_skinny_rows<true, G, BSM_SKINNY_NT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS,   \
-                                                                      WGS, tiles, ntiles, K, a.H, a.I, OUT, h_amax); \
+#define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K)                                                   \
+  if (K % (4 * kNvKB) == 0)                                                                                    \
+    k_skinny_rows<true, G, kSkNT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS,    \
+                                                              tiles, ntiles, K, a.H, a.I, OUT, h_amax);        \
   else                                                                                                         \
-  k_skinny<true, G, KB, BSM_SKINNY_NT, true, BSM_SKINNY_DEPTH><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, \
-                                                                   tiles, ntiles, K, a.H, a.I, OUT, h_amax);   \
-  if (many) ((G ? BSM_PREFILL_BIG : big_dn) ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(        \
-      A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,                                                  \
-                                                    ntiles_w, K, a.H, a.I, OUT, h_amax)
-    if (a.H % (4 * BSM_NV_KB) == 0) {
-      BSM_A16_G(true, act, xrs, a.w13_codes, w13s, a.w13_gs, h_f32, g1, w1, a.H, BSM_NV_KB);
-    } else {
-      BSM_A16_G(true, act, xrs, a.w13_codes, w13s, a.w13_gs, h_f32, g1, w1, a.H, 32);
-    }
+    k_skinny<true, G, 32, kSkNT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS,     \
+                                                             tiles, ntiles, K, a.H, a.I, OUT, h_amax);         \
+  if (many)                                                                                                    \
+    ((G || big_dn) ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(           \
+        A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w, ntiles_w, K, a.H, a.I, OUT, h_amax)
+    BSM_A16_G(true, act, xrs, a.w13_codes, w13s, a.w13_gs, h_f32, g1, w1, a.H);
     stage_mark(0, 2, st);
     const int64_t n4 = L.P * a.I / 4;
     k_h_to_bf16<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(h_f32, n4, reinterpret_cast<uint16_t*>(hdec));
     stage_mark(0, 3, st);
-    if (a.I % (4 * BSM_NV_KB) == 0) {
-      BSM_A16_G(false, hdec, nullptr, a.w2_codes, w2s, a.w2_gs, y, g2, w2, a.I, BSM_NV_KB);
-    } else {
-      BSM_A16_G(false, hdec, nullptr, a.w2_codes, w2s, a.w2_gs, y, g2, w2, a.I, 32);
-    }
+    BSM_A16_G(false, hdec, nullptr, a.w2_codes, w2s, a.w2_gs, y, g2, w2, a.I);
 #undef BSM_A16_G
   } else if (a.nvfp4) {
-    if (a.H % (4 * BSM_NV_KB) == 0) {
-      BSM_G1(true, BSM_NV_KB);
-    } else {
-      BSM_G1(true, 32);
-    }
+    BSM_G1(true);
     stage_mark(0, 2, st);
     err = launch_nvfp4_quantize_from_amax(h_f32, false, 1, L.P, a.I, h_codes, h_scales, h_gs, h_amax,
                                           a.h_static ? a.h_gs_user : nullptr, st, hdec);
     if (err != hipSuccess) return err;
     if (!a.h_static && a.h_gs_user) k_copy_f32<<<1, 64, 0, st>>>(h_gs, a.h_gs_user);
     stage_mark(0, 3, st);
-    if (a.I % (4 * BSM_NV_KB) == 0) {
-      BSM_G2(true, BSM_NV_KB);
-    } else {
-      BSM_G2(true, 32);
-    }
+    BSM_G2(true, hsc);
   } else {
-#ifndef BSM_FP8_KB
-#define BSM_FP8_KB 64
-#endif
-#ifndef BSM_F8_DOWN3
-#define BSM_F8_DOWN3 1  // FP8 down projection: three-stage direct-to-LDS pipeline (0: register staging)
-#endif
-#ifndef BSM_FP8_MFMA
-#define BSM_FP8_MFMA 1  // down projection of many-row experts on the FP8 matrix cores (0: decoded to FP16)
-#endif
+    // FP8: E4M3 operands decoded exactly to FP16 in both projections (FP32 accumulation)
     const float* w13f = reinterpret_cast<const float*>(a.w13_scales);
     const float* w2f = reinterpret_cast<const float*>(a.w2_scales);
     if (dense) {
       err = launch_dense_f8<true>(a.x_codes, xrs, a.T, a.H, a.w13_codes, w13f, 0, a.I, h_f32, part, st);
       if (err != hipSuccess) return err;
-    } else if (a.H % (4 * BSM_FP8_KB) == 0) {
-      BSM_G1(false, BSM_FP8_KB);
     } else {
-      BSM_G1(false, 32);
+      BSM_G1(false);
     }
     stage_mark(0, 2, st);
     err = launch_fp8_quantize(h_f32, false, L.P, a.I, h_codes, reinterpret_cast<float*>(h_scales), st, hdec);
     if (err != hipSuccess) return err;
     stage_mark(0, 3, st);
     if (dense) {
-      err = launch_dense_f8<false>(h_codes, reinterpret_cast<const float*>(h_scales), L.P, a.I, a.w2_codes, w2f,
-                                   a.H, 0, y, part, st);
+      err = launch_dense_f8<false>(h_codes, hsc, L.P, a.I, a.w2_codes, w2f, a.H, 0, y, part, st);
       if (err != hipSuccess) return err;
-    } else if (!BSM_FP8_MFMA) {
-      if (a.I % (4 * BSM_FP8_KB) == 0) {
-        BSM_G2(false, BSM_FP8_KB);
-      } else {
-        BSM_G2(false, 32);
-      }
     } else {
-      // few-row experts: E4M3 decoded to FP16 next to the weight stream; many-row experts: FP8 matrix cores
-      const float* hsc = reinterpret_cast<const float*>(h_scales);
-      if (a.I % (4 * BSM_FP8_KB) == 0 && BSM_SKINNY_ROWS && BSM_FP8_KB == 64)
-        k_skinny_rows<false, false, BSM_SKINNY_NT, false, BSM_SKR_DEPTH_FP8><<<g2, 256, 0, st>>>(
-            hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
-      else if (a.I % (4 * BSM_FP8_KB) == 0)
-        k_skinny<false, false, BSM_FP8_KB, BSM_SKINNY_NT, false, BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(
-            hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
-      else
-        k_skinny<false, false, 32, BSM_SKINNY_NT, false, BSM_SKINNY_DEPTH_FP8><<<g2, 256, 0, st>>>(
-            hdec, row_pair, a.topk, h_gs, hsc, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax);
-      if (many)
-        (BSM_F8_DOWN3 ? k_gemm_f8_down3 : k_gemm_f8_down)<<<dim3((unsigned)(a.H / kGBN), (unsigned)L.max_tiles_w),
-                                                           256, 0, st>>>(h_codes, hsc, a.w2_codes, w2f, tiles_w,
-                                                                         ntiles_w, a.I, a.H, y);
+      BSM_G2(false, hsc);
     }
   }
 #undef BSM_G1

@@ -45,16 +45,6 @@
 
 #include "bsm_internal.h"
 
-#ifndef BSM_ROUTE_I8
-#define BSM_ROUTE_I8 1
-#endif
-#ifndef BSM_ROUTE_I8_SMALL
-#define BSM_ROUTE_I8_SMALL 1  // small batches too (K cut into splits)
-#endif
-#ifndef BSM_SELECT_WAVE
-#define BSM_SELECT_WAVE 1
-#endif
-
 namespace bsm {
 
 namespace {
@@ -1361,7 +1351,7 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   const dim3 gl((unsigned)((T + kTile - 1) / kTile), (unsigned)((E + kTile - 1) / kTile));
   const dim3 glz(gl.x, gl.y, (unsigned)L.ks);
   // bf16 x and w at large batches: exact integer dot products on the int8 matrix cores
-  const bool i8 = BSM_ROUTE_I8 && L.i8ok && xb && wb && (!L.rb || BSM_ROUTE_I8_SMALL);
+  const bool i8 = L.i8ok && xb && wb;
   int8_t* dig = reinterpret_cast<int8_t*>(ws + L.dig);
   int64_t* spart = reinterpret_cast<int64_t*>(ws + L.spart);
   int* rexp = L.i8ok ? reinterpret_cast<int*>(ws + L.rexp) : nullptr;
@@ -1373,7 +1363,7 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   // workgroups whose list counts the selection kernel adds up
   const int64_t nblk_used = i8 ? L.nblk8 : L.rb ? (int64_t)nrb : (int64_t)gl.x * gl.y;
   // one wave per token needs 256 experts, groups of a multiple of 4 and an aligned scores row
-  const bool sel4 = BSM_SELECT_WAVE && E == 256 && (E / n_group) % 4 == 0 && topk <= 64 &&
+  const bool sel4 = E == 256 && (E / n_group) % 4 == 0 && topk <= 64 &&
                     ((uintptr_t)scores & 15) == 0;
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
   if (i8 && L.rb) {                                                                                        \
