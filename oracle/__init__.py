@@ -30,6 +30,10 @@ Where the pages leave a step open the reading taken is stated in the function
 that implements it.  Floating point is evaluated in float64 (exact where the
 docstrings say so) and rounded to float32 where the method fixes FP32.
 
+``quant_c`` runs the quantizers of ``quant`` as plain C loops (``quant_c.c``,
+built by ``build_c``) for full-size tensors; it is pinned bit-identical to
+``quant``.
+
 Parity status of each function (what pins it) is listed in each module header.
 """
 

@@ -109,27 +109,45 @@ def combine_f32(y_pairs, w, scale):
 
 
 class NVFP4Expert:
-    """One expert's gate / up / down projections quantized to NVFP4 (RTN)."""
+    """One expert's gate / up / down projections quantized to NVFP4 (RTN).
 
-    def __init__(self, w_gate, w_up, w_down):
-        self.gate = quant.nvfp4_quantize(w_gate)
-        self.up = quant.nvfp4_quantize(w_up)
-        self.down = quant.nvfp4_quantize(w_down)
+    ``q``: the quantizer module, ``oracle.quant`` or its C transcription
+    ``oracle.quant_c`` (bit-identical, for full-size experts).
+    """
+
+    def __init__(self, w_gate, w_up, w_down, q=quant):
+        self.q = q
+        self.gate = q.nvfp4_quantize(w_gate)
+        self.up = q.nvfp4_quantize(w_up)
+        self.down = q.nvfp4_quantize(w_down)
+
+    def decoded_gate_up(self):
+        return tuple(self.q.nvfp4_dequantize_exact(*p) for p in (self.gate, self.up))
+
+    def decoded_down(self):
+        return self.q.nvfp4_dequantize_exact(*self.down)
 
     def decoded(self):
-        return tuple(quant.nvfp4_dequantize_exact(*p) for p in (self.gate, self.up, self.down))
+        return self.decoded_gate_up() + (self.decoded_down(),)
 
 
 class FP8Expert:
     """One expert's gate / up / down projections quantized per output channel."""
 
-    def __init__(self, w_gate, w_up, w_down):
-        self.gate = quant.fp8_quantize(w_gate)
-        self.up = quant.fp8_quantize(w_up)
-        self.down = quant.fp8_quantize(w_down)
+    def __init__(self, w_gate, w_up, w_down, q=quant):
+        self.q = q
+        self.gate = q.fp8_quantize(w_gate)
+        self.up = q.fp8_quantize(w_up)
+        self.down = q.fp8_quantize(w_down)
+
+    def decoded_gate_up(self):
+        return tuple(self.q.fp8_dequantize_exact(*p) for p in (self.gate, self.up))
+
+    def decoded_down(self):
+        return self.q.fp8_dequantize_exact(*self.down)
 
     def decoded(self):
-        return tuple(quant.fp8_dequantize_exact(*p) for p in (self.gate, self.up, self.down))
+        return self.decoded_gate_up() + (self.decoded_down(),)
 
 
 # --------------------------------------------------------------------------
@@ -137,7 +155,7 @@ class FP8Expert:
 # --------------------------------------------------------------------------
 
 
-def quantize_activations(x, fmt, global_scale=None):
+def quantize_activations(x, fmt, global_scale=None, q=quant):
     """Quantize activations and return (packed quantities, exact decoded float64).
 
     Weight-only W4A16 keeps the BF16 activations: (None, x) with x BF16-exact.
@@ -147,19 +165,21 @@ def quantize_activations(x, fmt, global_scale=None):
         assert np.array_equal(formats.bf16_round(x), x), "W4A16 activations must be BF16 values"
         return None, x.astype(np.float64)
     if fmt == "nvfp4":
-        q = quant.nvfp4_quantize(x, global_scale)
-        return q, quant.nvfp4_dequantize_exact(*q)
-    q = quant.fp8_quantize(x)
-    return q, quant.fp8_dequantize_exact(*q)
+        xq = q.nvfp4_quantize(x, global_scale)
+        return xq, q.nvfp4_dequantize_exact(*xq)
+    xq = q.fp8_quantize(x)
+    return xq, q.fp8_dequantize_exact(*xq)
 
 
-def moe_expert_mlp(x_hat, ids, w, experts, fmt, combine_scale=2.5, h_global_scale=None):
+def moe_expert_mlp(x_hat, ids, w, experts, fmt, combine_scale=2.5, h_global_scale=None, q=quant):
     """Expert MLP on decoded activations.
 
     x_hat: [T, H] exactly decoded (float64) quantized activations (W4A16: the
     BF16 activations).  ids, w: [T, k] router output.  experts: mapping
     e -> NVFP4Expert (NVFP4, W4A16) / FP8Expert (only the experts that appear
-    in ids are touched).  fmt: "nvfp4", "fp8" or "w4a16".
+    in ids are touched, each decoded once per projection pass).  fmt: "nvfp4",
+    "fp8" or "w4a16".  q: quantizer module for h (``oracle.quant`` or the
+    bit-identical ``oracle.quant_c``).
     Returns a dict with the stages in pair order p = t*k + j:
       g, u, h: [P, I] float32; hq: quantized h; y: [P, H] float32; out: [T, H].
     """
@@ -169,12 +189,9 @@ def moe_expert_mlp(x_hat, ids, w, experts, fmt, combine_scale=2.5, h_global_scal
     tok = np.repeat(np.arange(T), k)
     P = T * k
     g = u = y = None
-    hs = {}
-    decoded = {}
-    for e in np.unique(flat):
-        wg, wu, wd = experts[int(e)].decoded()
-        decoded[int(e)] = wd
-        rows = np.nonzero(flat == e)[0]
+    rows_of = {int(e): np.nonzero(flat == e)[0] for e in np.unique(flat)}
+    for e, rows in rows_of.items():
+        wg, wu = experts[e].decoded_gate_up()
         xe = x_hat[tok[rows]]
         ge = gemm_f32(xe, wg)
         ue = gemm_f32(xe, wu)
@@ -184,19 +201,18 @@ def moe_expert_mlp(x_hat, ids, w, experts, fmt, combine_scale=2.5, h_global_scal
             u = np.zeros((P, I), np.float32)
         g[rows] = ge
         u[rows] = ue
-        hs[int(e)] = rows
     h = swiglu_f32(g, u)
     if fmt == "nvfp4":
-        hq = quant.nvfp4_quantize(h, h_global_scale)
-        h_hat = quant.nvfp4_dequantize_exact(*hq)
+        hq = q.nvfp4_quantize(h, h_global_scale)
+        h_hat = q.nvfp4_dequantize_exact(*hq)
     elif fmt == "w4a16":
         hq = None
         h_hat = formats.bf16_round(h).astype(np.float64)
     else:
-        hq = quant.fp8_quantize(h)
-        h_hat = quant.fp8_dequantize_exact(*hq)
-    for e, rows in hs.items():
-        ye = gemm_f32(h_hat[rows], decoded[e])
+        hq = q.fp8_quantize(h)
+        h_hat = q.fp8_dequantize_exact(*hq)
+    for e, rows in rows_of.items():
+        ye = gemm_f32(h_hat[rows], experts[e].decoded_down())
         if y is None:
             y = np.zeros((P, ye.shape[1]), np.float32)
         y[rows] = ye
@@ -204,11 +220,11 @@ def moe_expert_mlp(x_hat, ids, w, experts, fmt, combine_scale=2.5, h_global_scal
     return {"g": g, "u": u, "h": h, "hq": hq, "y": y, "out": out}
 
 
-def moe_layer(x, w_router, experts, fmt, n_group, topk_group, topk, combine_scale=2.5):
+def moe_layer(x, w_router, experts, fmt, n_group, topk_group, topk, combine_scale=2.5, q=quant):
     """One MoE layer: route -> quantize x -> expert MLP.  x: [T, H] float32-exact."""
     ids, w, scores, rstats = _route(x, w_router, n_group, topk_group, topk)
-    xq, x_hat = quantize_activations(x, fmt)
-    res = moe_expert_mlp(x_hat, ids, w, experts, fmt, combine_scale)
+    xq, x_hat = quantize_activations(x, fmt, q=q)
+    res = moe_expert_mlp(x_hat, ids, w, experts, fmt, combine_scale, q=q)
     res.update(ids=ids, w=w, scores=scores, xq=xq, route_stats=rstats)
     return res
 
@@ -235,7 +251,7 @@ def scaled_residual_f32(x, m, k):
     return (np.float64(a) * np.asarray(x, np.float64) + np.float64(b) * np.asarray(m, np.float64)).astype(np.float32)
 
 
-def moe_stack(x1, layers, fmt, n_group, topk_group, topk, eps=1e-6, combine_scale=2.5):
+def moe_stack(x1, layers, fmt, n_group, topk_group, topk, eps=1e-6, combine_scale=2.5, q=quant):
     """Stack of MoE layers on a float32 residual stream (embedding = step 1).
 
     layers: list of (w_router, experts).  Layer i (1-based) is residual step i+1.
@@ -245,7 +261,7 @@ def moe_stack(x1, layers, fmt, n_group, topk_group, topk, eps=1e-6, combine_scal
     stages = []
     for i, (wr, experts) in enumerate(layers, start=1):
         n = rmsnorm_f32(xs[-1], eps)
-        res = moe_layer(n, wr, experts, fmt, n_group, topk_group, topk, combine_scale)
+        res = moe_layer(n, wr, experts, fmt, n_group, topk_group, topk, combine_scale, q=q)
         xs.append(scaled_residual_f32(xs[-1], res["out"], i + 1))
         res["normed"] = n
         stages.append(res)

@@ -142,6 +142,47 @@ def test_residual_weights_and_zero_sublayer_stack():
     assert np.allclose(x, x1 * np.sqrt(5), rtol=1e-6)
 
 
+def _zero_experts(E, H, I, fmt):
+    cls = M.FP8Expert if fmt == "fp8" else M.NVFP4Expert
+    z = np.zeros((I, H), np.float32)
+    ex = cls(z, z, np.zeros((H, I), np.float32))
+    return {e: ex for e in range(E)}
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_stack_step_indices(fmt):
+    """moe_stack: the embedding is residual step 1 and MoE layer i is step i + 1.
+
+    With every expert zero, each layer only rescales the stream: x_(i+1) = fl32(a_(i+1) x_i), so after
+    four layers x_5 = x_1 sqrt(1/5) up to four roundings.  With one non-zero layer j, its output m_j
+    reaches the final stream with weight b_(j+1) * prod_(k > j+1) a_k = 1/sqrt(5), the embedding's
+    weight too: x_5 = (x_1 + m_j) / sqrt(5).  A step index shifted by one breaks both (a_1 = 0 would
+    zero the stream; weights 1/2 instead of 1/sqrt(5)).
+    """
+    rng = np.random.default_rng(31)
+    T, H, I, E = 16, 64, 32, 8
+    x1 = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    zero = (wr, _zero_experts(E, H, I, fmt))
+    xs, stages = M.moe_stack(x1, [zero] * 4, fmt, 2, 1, 2)
+    for i in range(1, 5):
+        assert not stages[i - 1]["out"].any()
+        a, _ = M.residual_weights(i + 1)
+        assert np.array_equal(xs[i], (np.float64(a) * xs[i - 1].astype(np.float64)).astype(np.float32))
+    assert np.allclose(xs[4], x1 * np.sqrt(1 / 5), rtol=5 * 2 ** -23, atol=0)
+    # one non-zero layer (j = 2): identical experts, so m_2 does not depend on the routing
+    r2 = np.random.default_rng(32)
+    cls = M.FP8Expert if fmt == "fp8" else M.NVFP4Expert
+    same = cls(_bf16(r2.standard_normal((I, H)) * 0.3), _bf16(r2.standard_normal((I, H)) * 0.3),
+               _bf16(r2.standard_normal((H, I)) * 0.3))
+    live = (wr, {e: same for e in range(E)})
+    xs, stages = M.moe_stack(x1, [zero, live, zero, zero], fmt, 2, 1, 2)
+    m2 = stages[1]["out"].astype(np.float64)
+    assert np.abs(m2).max() > 0.1 * np.abs(x1).max()
+    ref = (x1.astype(np.float64) + m2) / np.sqrt(5)
+    assert np.allclose(xs[4], ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+
+
 def test_rmsnorm_unit_rms():
     rng = np.random.default_rng(7)
     x = (rng.standard_normal((8, 5120)) * 3).astype(np.float32)
