@@ -33,22 +33,24 @@ import numpy as np
 from . import moe, quant
 
 
-def fp8_linear(x, w):
-    """x [T, K], w [N, K] float32 values -> (x codes/scales, w codes/scales, y [T, N] float32)."""
-    xq = quant.fp8_quantize(x)
-    wq = quant.fp8_quantize(w)
-    y = moe.gemm_f32(quant.fp8_dequantize_exact(*xq), quant.fp8_dequantize_exact(*wq))
+def fp8_linear(x, w, q=quant):
+    """x [T, K], w [N, K] float32 values -> (x codes/scales, w codes/scales, y [T, N] float32).
+
+    q: quantizer module (``oracle.quant`` or the bit-identical ``oracle.quant_c``)."""
+    xq = q.fp8_quantize(x)
+    wq = q.fp8_quantize(w)
+    y = moe.gemm_f32(q.fp8_dequantize_exact(*xq), q.fp8_dequantize_exact(*wq))
     return xq, wq, y
 
 
-def fp8_dense_mlp(x, w_gate, w_up, w_down):
+def fp8_dense_mlp(x, w_gate, w_up, w_down, q=quant):
     """Dense FP8 SwiGLU MLP: one expert, every token routed to it with weight 1, scale 1."""
     T = x.shape[0]
-    ex = moe.FP8Expert(w_gate, w_up, w_down)
-    xq, xh = moe.quantize_activations(x, "fp8")
+    ex = moe.FP8Expert(w_gate, w_up, w_down, q=q)
+    xq, xh = moe.quantize_activations(x, "fp8", q=q)
     ids = np.zeros((T, 1), np.int32)
     wts = np.ones((T, 1), np.float32)
-    res = moe.moe_expert_mlp(xh, ids, wts, {0: ex}, "fp8", combine_scale=1.0)
+    res = moe.moe_expert_mlp(xh, ids, wts, {0: ex}, "fp8", combine_scale=1.0, q=q)
     res["xq"] = xq
     res["expert"] = ex
     return res

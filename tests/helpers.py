@@ -50,3 +50,46 @@ def ws_view(ws, lay, key, dtype, shape):
     itemsize = torch.tensor([], dtype=dtype).element_size()
     start = lay[key]
     return ws[start:start + n * itemsize].view(dtype).reshape(shape)
+
+
+def weights_match(gpu_w, experts, fmt, ids):
+    """The GPU-quantized weights of experts ``ids`` equal the oracle experts' codes, scales and global scales."""
+    for e in ids:
+        ex = experts[e]
+        if fmt == "nvfp4":
+            c13, s13, g13 = np_(gpu_w.w13_codes[e]), np_(gpu_w.w13_scales[e]), np_(gpu_w.w13_gs[e])
+            I = c13.shape[0] // 2
+            assert np.array_equal(c13[:I], ex.gate[0]) and np.array_equal(c13[I:], ex.up[0])
+            assert np.array_equal(s13[:I], ex.gate[1]) and np.array_equal(s13[I:], ex.up[1])
+            assert g13[0] == ex.gate[2] and g13[1] == ex.up[2]
+            assert np.array_equal(np_(gpu_w.w2_codes[e]), ex.down[0])
+            assert np.array_equal(np_(gpu_w.w2_scales[e]), ex.down[1]) and np_(gpu_w.w2_gs[e]) == ex.down[2]
+        else:
+            c13, s13 = np_(gpu_w.w13_codes[e]), np_(gpu_w.w13_scales[e])
+            I = c13.shape[0] // 2
+            assert np.array_equal(c13[:I], ex.gate[0]) and np.array_equal(c13[I:], ex.up[0])
+            assert np.array_equal(s13[:I], ex.gate[1]) and np.array_equal(s13[I:], ex.up[1])
+            assert np.array_equal(np_(gpu_w.w2_codes[e]), ex.down[0])
+            assert np.array_equal(np_(gpu_w.w2_scales[e]), ex.down[1])
+
+
+def moe_stages(gpu_lib, fmt, cfg, T, ws, P):
+    """The expert-MLP workspace's stage buffers (permutation, h, h codes and scales, y) on the host."""
+    lay = gpu_lib.moe_workspace_layout(fmt, cfg.E, cfg.H, cfg.I, T, cfg.topk)
+    I, H = cfg.I, cfg.H
+    st = {
+        "counts": np_(ws_view(ws, lay, "counts", torch.int32, (cfg.E,))),
+        "offsets": np_(ws_view(ws, lay, "offsets", torch.int32, (cfg.E + 1,))),
+        "row_pair": np_(ws_view(ws, lay, "row_pair", torch.int32, (P,))),
+        "pair_row": np_(ws_view(ws, lay, "pair_row", torch.int32, (P,))),
+        "h": np_(ws_view(ws, lay, "h_f32", torch.float32, (P, I))),
+        "y": np_(ws_view(ws, lay, "y_f32", torch.float32, (P, H))),
+    }
+    if fmt == "nvfp4":
+        st["hc"] = np_(ws_view(ws, lay, "h_codes", torch.uint8, (P, I // 2)))
+        st["hs"] = np_(ws_view(ws, lay, "h_scales", torch.uint8, (P, I // 16)))
+        st["hg"] = np_(ws_view(ws, lay, "h_gs", torch.float32, (1,)))[0]
+    else:
+        st["hc"] = np_(ws_view(ws, lay, "h_codes", torch.uint8, (P, I)))
+        st["hs"] = np_(ws_view(ws, lay, "h_scales", torch.float32, (P,)))
+    return st
