@@ -122,6 +122,7 @@ def check_layer(gpu_lib, fmt, cfg, x, wr, w13, w2, gw, label):
     del ws
     torch.cuda.empty_cache()
 
+    print(f"{label}: GPU layer done, oracle routing", flush=True)
     # routing, activation quantization: bit-exact
     oi, ow, _, _ = OR.route(x, wr, cfg.n_group, cfg.topk_group, cfg.topk)
     assert np.array_equal(np_(ids), oi), f"{label}: routing ids differ"
@@ -133,6 +134,7 @@ def check_layer(gpu_lib, fmt, cfg, x, wr, w13, w2, gw, label):
     assert np.array_equal(st["row_pair"], pair_of_row) and np.array_equal(st["counts"], counts)
 
     # the oracle's own layer on its own quantization of the same masters
+    print(f"{label}: oracle expert MLP over {int((counts > 0).sum())} experts", flush=True)
     experts = DeviceExperts(w13, w2, gw, fmt)
     ref = OM.moe_expert_mlp(x_hat, oi, ow, experts, fmt, cfg.combine_scale, q=QC)
     res = {"active": int((counts > 0).sum()), "max_rows": int(counts.max())}
@@ -149,6 +151,7 @@ def check_layer(gpu_lib, fmt, cfg, x, wr, w13, w2, gw, label):
         hq_g = QC.fp8_quantize(st["h"])
         hh = QC.fp8_dequantize_exact(*hq_g)
     assert np.array_equal(st["hc"], hq_g[0]) and np.array_equal(st["hs"], hq_g[1]), f"{label}: h codes differ"
+    print(f"{label}: oracle down projection from the GPU's h codes", flush=True)
     # stage 3: the down projection from those identical h codes, every row
     y_tf = np.zeros_like(st["y"])
     for e in np.nonzero(counts)[0]:
