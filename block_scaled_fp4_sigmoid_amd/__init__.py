@@ -76,6 +76,8 @@ def load():
         "bsm_moe_workspace_layout": (i32, [i32, i64, i64, i64, i64, i32, ctypes.POINTER(_WsLayout)]),
         "bsm_moe_expert_mlp": (i32, [ctypes.POINTER(_MoeWeights), ctypes.POINTER(_ActQ), i64, vp, vp, i32, f32, i32,
                                      vp, vp, vp, sz, vp]),
+        "bsm_moe_expert_mlp_noalloc": (i32, [ctypes.POINTER(_MoeWeights), ctypes.POINTER(_ActQ), i64, vp, vp, i32,
+                                             f32, i32, vp, vp, vp]),
         "bsm_moe_expert_mlp_w4a16": (i32, [ctypes.POINTER(_MoeWeights), vp, i64, vp, vp, i32, f32, vp, vp, sz, vp]),
         "bsm_fp8_linear_workspace_size": (sz, [i64, i64, i64]),
         "bsm_fp8_linear": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
@@ -305,20 +307,47 @@ def moe_workspace_layout(fmt, E, H, I, T, topk):
     return {n: getattr(lay, n) for n, _ in _WsLayout._fields_}
 
 
+def _routing_args(ids, wts):
+    _dev(ids, "ids")
+    _dev(wts, "wts")
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise BsmError("ids must be int32 [T, topk]")
+    if wts.dtype != torch.float32 or tuple(wts.shape) != tuple(ids.shape):
+        raise BsmError("wts must be float32 with the shape of ids")
+    return ids.shape
+
+
+def _act_struct(weights, xq, T):
+    fmt = weights.format
+    H = weights.H
+    if fmt == FMT_NVFP4:
+        codes, scales, gs = xq
+        if tuple(codes.shape) != (T, H // 2) or codes.dtype != torch.uint8:
+            raise BsmError(f"NVFP4 activation codes must be uint8 [{T}, {H // 2}]")
+        if tuple(scales.shape) != (T, H // 16) or scales.dtype != torch.uint8:
+            raise BsmError(f"NVFP4 activation scales must be uint8 [{T}, {H // 16}]")
+        if gs.numel() != 1 or gs.dtype != torch.float32:
+            raise BsmError("NVFP4 activation global scale must be one float32")
+        for t, n in ((codes, "codes"), (scales, "scales"), (gs, "global scale")):
+            _dev(t, n)
+        return _ActQ(fmt, codes.data_ptr(), scales.data_ptr(), gs.data_ptr())
+    codes, scales = xq
+    if tuple(codes.shape) != (T, H) or codes.dtype != torch.uint8:
+        raise BsmError(f"FP8 activation codes must be uint8 [{T}, {H}]")
+    if tuple(scales.shape) != (T,) or scales.dtype != torch.float32:
+        raise BsmError(f"FP8 activation scales must be float32 [{T}]")
+    _dev(codes, "codes")
+    _dev(scales, "scales")
+    return _ActQ(fmt, codes.data_ptr(), scales.data_ptr(), None)
+
+
 def moe_expert_mlp(weights: ExpertWeights, xq, ids, wts, combine_scale=2.5, h_global_scale=None, out=None, ws=None,
                    return_workspace=False):
     """Routed-expert MLP on quantized activations ``xq`` -> out f32 [T, H]."""
     lib = load()
-    _dev(ids, "ids")
-    _dev(wts, "wts")
-    T, topk = ids.shape
+    T, topk = _routing_args(ids, wts)
+    act = _act_struct(weights, xq, T)
     fmt = weights.format
-    if fmt == FMT_NVFP4:
-        codes, scales, gs = xq
-        act = _ActQ(fmt, codes.data_ptr(), scales.data_ptr(), gs.data_ptr())
-    else:
-        codes, scales = xq
-        act = _ActQ(fmt, codes.data_ptr(), scales.data_ptr(), None)
     if out is None:
         out = torch.empty((T, weights.H), dtype=torch.float32, device=ids.device)
     need = lib.bsm_moe_workspace_size(fmt, weights.E, weights.H, weights.I, T, topk)
@@ -332,18 +361,33 @@ def moe_expert_mlp(weights: ExpertWeights, xq, ids, wts, combine_scale=2.5, h_gl
     return (out, ws) if return_workspace else out
 
 
+def moe_expert_mlp_noalloc(weights: ExpertWeights, xq, ids, wts, out: torch.Tensor, combine_scale=2.5,
+                           h_global_scale=None):
+    """``moe_expert_mlp`` into the caller's ``out`` (f32 [T, H]) without any allocation: the library's static
+    per-GPU scratch replaces the workspace (calls on one GPU share it and must not overlap)."""
+    lib = load()
+    T, topk = _routing_args(ids, wts)
+    act = _act_struct(weights, xq, T)
+    _dev(out, "out")
+    if out.dtype != torch.float32 or tuple(out.shape) != (T, weights.H):
+        raise BsmError(f"out must be float32 [{T}, {weights.H}]")
+    mode = GS_STATIC if h_global_scale is not None else GS_DYNAMIC
+    wstruct = weights._struct()
+    _check(lib.bsm_moe_expert_mlp_noalloc(ctypes.byref(wstruct), ctypes.byref(act), T, _ptr(ids), _ptr(wts), topk,
+                                          float(combine_scale), mode, _ptr(h_global_scale), _ptr(out), _stream()))
+    return out
+
+
 def moe_expert_mlp_w4a16(weights: ExpertWeights, x, ids, wts, combine_scale=2.5, out=None, ws=None,
                          return_workspace=False):
     """Weight-only routed-expert MLP: NVFP4 ``weights``, BF16 activations ``x`` [T, H] -> out f32 [T, H]."""
     lib = load()
     _dev(x, "x")
-    _dev(ids, "ids")
-    _dev(wts, "wts")
-    if x.dtype != torch.bfloat16:
-        raise BsmError("the weight-only path takes BF16 activations")
+    T, topk = _routing_args(ids, wts)
+    if x.dtype != torch.bfloat16 or tuple(x.shape) != (T, weights.H):
+        raise BsmError(f"the weight-only path takes BF16 activations [{T}, {weights.H}]")
     if weights.format != FMT_NVFP4:
         raise BsmError("the weight-only path takes NVFP4 weights")
-    T, topk = ids.shape
     if out is None:
         out = torch.empty((T, weights.H), dtype=torch.float32, device=ids.device)
     need = lib.bsm_moe_workspace_size(FMT_W4A16, weights.E, weights.H, weights.I, T, topk)

@@ -6,10 +6,21 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/bsmoe.h"
 #include "bsm_internal.h"
 
+// Scratch of bsm_moe_expert_mlp_noalloc: a file-scope device array (each GPU the library runs on holds
+// its own copy until the process ends).  Every call on a GPU shares that GPU's copy.
+constexpr size_t kNoAllocScratchBytes = BSM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 thread_local char g_err[512] = {0};
 thread_local bsm::StageEvents g_stage[2];
@@ -41,6 +52,76 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   if (!ws) return fail(BSM_ERR_WORKSPACE, "workspace pointer is NULL (need %zu bytes)", need);
   if (!aligned(ws, 256)) return fail(BSM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (ws_bytes < need) return fail(BSM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return BSM_OK;
+}
+
+// Arguments of the routed-expert MLP, validated on the host (nothing is enqueued on error).  *empty:
+// T == 0, nothing to do.
+int moe_args(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T, const int32_t* topk_ids,
+             const float* topk_weights, int topk, float combine_scale, int h_gs_mode, float* h_global_scale,
+             float* out, bsm::MoeArgs* a, bool* empty) {
+  if (!w || !xq) return fail(BSM_ERR_INVALID_ARG, "NULL weights / activation descriptor");
+  if (w->format != BSM_FMT_NVFP4 && w->format != BSM_FMT_FP8) return fail(BSM_ERR_INVALID_ARG, "bad weight format");
+  if (xq->format != w->format) return fail(BSM_ERR_INVALID_ARG, "activation and weight formats differ");
+  const bool nv = w->format == BSM_FMT_NVFP4;
+  const int64_t E = w->E, H = w->H, I = w->I;
+  if (E <= 0 || H <= 0 || I <= 0 || T < 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
+  if (H % 256 != 0 || I % 128 != 0) return fail(BSM_ERR_UNSUPPORTED, "H must be a multiple of 256 and I of 128");
+  if (E > 1024) return fail(BSM_ERR_UNSUPPORTED, "E > 1024");
+  if (topk < 1 || topk > 32 || topk > E) return fail(BSM_ERR_INVALID_ARG, "topk must be in [1, min(32, E)]");
+  if (T * topk > 0x3FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "T * topk too large");
+  if (h_gs_mode != BSM_GS_DYNAMIC && h_gs_mode != BSM_GS_STATIC) return fail(BSM_ERR_INVALID_ARG, "bad h_gs_mode");
+  if (nv && h_gs_mode == BSM_GS_STATIC && !h_global_scale)
+    return fail(BSM_ERR_INVALID_ARG, "STATIC h global scale needs h_global_scale");
+  *empty = T == 0;
+  if (*empty) return BSM_OK;
+  if (!w->w13_codes || !w->w13_scales || !w->w2_codes || !w->w2_scales || !xq->codes || !xq->scales || !topk_ids ||
+      !topk_weights || !out)
+    return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (nv && (!w->w13_gs || !w->w2_gs || !xq->global_scale)) return fail(BSM_ERR_INVALID_ARG, "NULL global scale");
+  if (!aligned(w->w13_codes, 16) || !aligned(w->w2_codes, 16) || !aligned(xq->codes, 16) || !aligned(out, 16))
+    return fail(BSM_ERR_INVALID_ARG, "codes and out must be 16-byte aligned");
+  if (nv && (!aligned(w->w13_scales, 2) || !aligned(w->w2_scales, 2) || !aligned(xq->scales, 2)))
+    return fail(BSM_ERR_INVALID_ARG, "NVFP4 scales must be 2-byte aligned");
+  a->nvfp4 = nv;
+  a->E = E;
+  a->H = H;
+  a->I = I;
+  a->T = T;
+  a->topk = topk;
+  a->w13_codes = w->w13_codes;
+  a->w13_scales = w->w13_scales;
+  a->w13_gs = w->w13_gs;
+  a->w2_codes = w->w2_codes;
+  a->w2_scales = w->w2_scales;
+  a->w2_gs = w->w2_gs;
+  a->x_codes = xq->codes;
+  a->x_scales = xq->scales;
+  a->x_gs = xq->global_scale;
+  a->ids = topk_ids;
+  a->wts = topk_weights;
+  a->combine_scale = combine_scale;
+  a->h_static = h_gs_mode == BSM_GS_STATIC;
+  a->h_gs_user = h_global_scale;
+  a->out = out;
+  return BSM_OK;
+}
+
+// Device address of this GPU's copy of the static scratch (found once per device with that device
+// current, then kept): host code uses this address, never the array's name, which on the host is only
+// a stand-in for the symbol.
+int noalloc_scratch(void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(BSM_ERR_HIP, "bsm_moe_expert_mlp_noalloc: no usable current device (%d)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fail(BSM_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *p = g_scratch_ptr[dev];
   return BSM_OK;
 }
 
@@ -214,53 +295,36 @@ int bsm_moe_workspace_layout(int format, int64_t E, int64_t H, int64_t I, int64_
 int bsm_moe_expert_mlp(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T, const int32_t* topk_ids,
                        const float* topk_weights, int topk, float combine_scale, int h_gs_mode, float* h_global_scale,
                        float* out, void* ws, size_t ws_bytes, bsm_stream_t stream) {
-  if (!w || !xq) return fail(BSM_ERR_INVALID_ARG, "NULL weights / activation descriptor");
-  if (w->format != BSM_FMT_NVFP4 && w->format != BSM_FMT_FP8) return fail(BSM_ERR_INVALID_ARG, "bad weight format");
-  if (xq->format != w->format) return fail(BSM_ERR_INVALID_ARG, "activation and weight formats differ");
-  const bool nv = w->format == BSM_FMT_NVFP4;
-  const int64_t E = w->E, H = w->H, I = w->I;
-  if (E <= 0 || H <= 0 || I <= 0 || T < 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
-  if (H % 256 != 0 || I % 128 != 0) return fail(BSM_ERR_UNSUPPORTED, "H must be a multiple of 256 and I of 128");
-  if (E > 1024) return fail(BSM_ERR_UNSUPPORTED, "E > 1024");
-  if (topk < 1 || topk > 32 || topk > E) return fail(BSM_ERR_INVALID_ARG, "topk must be in [1, min(32, E)]");
-  if (T * topk > 0x3FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "T * topk too large");
-  if (h_gs_mode != BSM_GS_DYNAMIC && h_gs_mode != BSM_GS_STATIC) return fail(BSM_ERR_INVALID_ARG, "bad h_gs_mode");
-  if (nv && h_gs_mode == BSM_GS_STATIC && !h_global_scale)
-    return fail(BSM_ERR_INVALID_ARG, "STATIC h global scale needs h_global_scale");
-  if (T == 0) return ok();
-  if (!w->w13_codes || !w->w13_scales || !w->w2_codes || !w->w2_scales || !xq->codes || !xq->scales || !topk_ids ||
-      !topk_weights || !out)
-    return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
-  if (nv && (!w->w13_gs || !w->w2_gs || !xq->global_scale)) return fail(BSM_ERR_INVALID_ARG, "NULL global scale");
-  if (!aligned(w->w13_codes, 16) || !aligned(w->w2_codes, 16) || !aligned(xq->codes, 16) || !aligned(out, 16))
-    return fail(BSM_ERR_INVALID_ARG, "codes and out must be 16-byte aligned");
-  if (nv && (!aligned(w->w13_scales, 2) || !aligned(w->w2_scales, 2) || !aligned(xq->scales, 2)))
-    return fail(BSM_ERR_INVALID_ARG, "NVFP4 scales must be 2-byte aligned");
-  if (int r = check_ws(ws, ws_bytes, bsm::moe_layout(nv, E, H, I, T, topk).total)) return r;
   bsm::MoeArgs a;
-  a.nvfp4 = nv;
-  a.E = E;
-  a.H = H;
-  a.I = I;
-  a.T = T;
-  a.topk = topk;
-  a.w13_codes = w->w13_codes;
-  a.w13_scales = w->w13_scales;
-  a.w13_gs = w->w13_gs;
-  a.w2_codes = w->w2_codes;
-  a.w2_scales = w->w2_scales;
-  a.w2_gs = w->w2_gs;
-  a.x_codes = xq->codes;
-  a.x_scales = xq->scales;
-  a.x_gs = xq->global_scale;
-  a.ids = topk_ids;
-  a.wts = topk_weights;
-  a.combine_scale = combine_scale;
-  a.h_static = h_gs_mode == BSM_GS_STATIC;
-  a.h_gs_user = h_global_scale;
-  a.out = out;
+  bool empty = false;
+  if (int r = moe_args(w, xq, T, topk_ids, topk_weights, topk, combine_scale, h_gs_mode, h_global_scale, out, &a,
+                       &empty))
+    return r;
+  if (empty) return ok();
+  if (int r = check_ws(ws, ws_bytes, bsm::moe_layout(a.nvfp4, a.E, a.H, a.I, T, topk).total)) return r;
   a.ws = (uint8_t*)ws;
   return hip_status(bsm::launch_moe(a, (hipStream_t)stream), "bsm_moe_expert_mlp");
+}
+
+int bsm_moe_expert_mlp_noalloc(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T, const int32_t* topk_ids,
+                               const float* topk_weights, int topk, float combine_scale, int h_gs_mode,
+                               float* h_global_scale, float* out, bsm_stream_t stream) {
+  bsm::MoeArgs a;
+  bool empty = false;
+  if (int r = moe_args(w, xq, T, topk_ids, topk_weights, topk, combine_scale, h_gs_mode, h_global_scale, out, &a,
+                       &empty))
+    return r;
+  if (empty) return ok();
+  const size_t need = bsm::moe_layout(a.nvfp4, a.E, a.H, a.I, T, topk).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(BSM_ERR_UNSUPPORTED,
+                "bsm_moe_expert_mlp_noalloc: this call needs %zu bytes of scratch, the static scratch holds %zu "
+                "(use bsm_moe_expert_mlp with a workspace)",
+                need, kNoAllocScratchBytes);
+  void* sp = nullptr;
+  if (int r = noalloc_scratch(&sp)) return r;
+  a.ws = (uint8_t*)sp;
+  return hip_status(bsm::launch_moe(a, (hipStream_t)stream), "bsm_moe_expert_mlp_noalloc");
 }
 
 int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w, const void* x, int64_t T, const int32_t* topk_ids,

@@ -241,6 +241,29 @@ int bsm_moe_expert_mlp(const bsm_moe_weights* w /* host */, const bsm_act_q* xq 
                        bsm_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Routed-expert MLP without allocation or workspace argument
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, semantics, validation and results (bit-identical) as
+ * bsm_moe_expert_mlp, minus the workspace: the call uses a static device
+ * array of BSM_NOALLOC_SCRATCH_BYTES (32 MiB) that every GPU the library
+ * runs on holds until the process ends (a Beam decode layer of 64 tokens
+ * needs about 19.4 MiB in either format).  A call whose
+ * bsm_moe_workspace_size exceeds it returns BSM_ERR_UNSUPPORTED and enqueues
+ * nothing.  The call allocates nothing (no hipMalloc, no library allocation);
+ * the first call on a device looks up that device's copy of the array with
+ * the device current.  Every call on one GPU shares its scratch, which keeps
+ * the last call's contents (whatever must start at zero is cleared on the
+ * stream by the call's own kernels): calls that overlap on one GPU (on
+ * different streams, or from several threads without ordering) race.
+ * ------------------------------------------------------------------------ */
+#define BSM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int bsm_moe_expert_mlp_noalloc(const bsm_moe_weights* w /* host */, const bsm_act_q* xq /* host */, int64_t T,
+                               const int32_t* topk_ids, const float* topk_weights, int topk, float combine_scale,
+                               int h_gs_mode, float* h_global_scale, float* out, bsm_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Weight-only W4A16 routed-expert MLP [WO] [MOE] [NUM]
  *
  * w: NVFP4 weights in the canonical layout above (format BSM_FMT_NVFP4).

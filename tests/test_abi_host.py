@@ -99,6 +99,24 @@ def test_moe_validation(lib):
     assert all(getattr(lay, f) % 256 == 0 for f, _ in bsm._WsLayout._fields_)
 
 
+def test_moe_noalloc_validation(lib):
+    """The allocation-free MLP validates like the workspace one and refuses calls beyond its static scratch
+    (all of these fail before any device call)."""
+    w = bsm._MoeWeights(1, 256, 5120, 2560, 0x100000, 0x100000, 0x100000, 0x100000, 0x100000, 0x100000)
+    a = bsm._ActQ(1, 0x100000, 0x100000, 0x100000)
+    ref = ctypes.byref
+    f = lib.bsm_moe_expert_mlp_noalloc
+    assert lib.bsm_moe_workspace_size(1, 256, 5120, 2560, 64, 8) <= 32 << 20  # a Beam decode layer fits
+    assert f(ref(w), ref(a), 4096, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None) == 2  # 1.2 GB of scratch needed
+    assert "static scratch" in _err(lib)
+    bad = bsm._MoeWeights(1, 256, 5120, 2500, 0x100000, 0x100000, 0x100000, 0x100000, 0x100000, 0x100000)
+    assert f(ref(bad), ref(a), 64, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None) == 2
+    assert f(None, ref(a), 64, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None) == 1
+    assert f(ref(w), ref(a), 64, FAKE, FAKE, 8, 2.5, 1, None, FAKE, None) == 1  # STATIC without a scale
+    assert f(ref(w), ref(a), 64, FAKE, FAKE, 8, 2.5, 0, None, None, None) == 1  # NULL out
+    assert f(ref(w), ref(a), 0, None, None, 8, 2.5, 0, None, None, None) == 0   # empty batch
+
+
 def test_norm_validation(lib):
     assert lib.bsm_rmsnorm_f32(FAKE, 4, 0, 1e-6, FAKE, None) == 1
     assert lib.bsm_rmsnorm_f32(FAKE, 4, 16, -1.0, FAKE, None) == 1
