@@ -11,8 +11,14 @@ run also measures the 8192-token prefill layer (Zipf-skewed router) and reports
 it under ``prefill_8192``.  Per-kernel times come from hipEvents recorded at
 the library's stage boundaries on the launch stream.
 
+The default run also reports the FP8 layers (decode and prefill), the
+standalone 32768 x 5120 NVFP4 quantize, the 4-layer stack in both formats, the
+measured HBM-read and FP16-MFMA ceilings of this GPU, and the CPU oracle on
+bounded samples (all host threads and one thread).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--fmt nvfp4|fp8|w4a16]
-                       [--workload decode|prefill] [--no-prefill] [--no-cpu-baseline]
+                       [--workload decode|prefill|stack|dense-fp8] [--no-prefill] [--no-extras]
+                       [--no-cpu-baseline] [--ceilings]
 """
 
 import argparse
@@ -332,36 +338,117 @@ def layer_numbers(cfg, fmt, T, ms, stage_ms, g1_ms, counts):
     }
 
 
-def cpu_baseline(cfg, fmt, w13, w2, x_np, wr_np):
-    """The CPU oracle, timed on a bounded sample: the full routing of the batch plus the
-    expert MLP of the first token (its experts quantized by the oracle beforehand, untimed)."""
+def _blas_info():
+    """BLAS library, version and thread count numpy uses, and the numpy version."""
+    try:
+        import threadpoolctl
+        info = [d for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+        blas = {k: info[0].get(k) for k in ("internal_api", "version", "num_threads")} if info else None
+    except ImportError:
+        blas = None
+    return {"numpy": np.__version__, "blas": blas}
+
+
+def _thread_limit(n):
+    import contextlib
+    try:
+        import threadpoolctl
+        return threadpoolctl.threadpool_limits(n)
+    except ImportError:
+        return contextlib.nullcontext()
+
+
+def _oracle_decode_time(cfg, fmt, x_np, wr_np, ids, wts, experts, sample):
+    """Seconds the oracle takes for the whole decode layer: routing and activation quantization of every
+    token are timed whole; the expert MLP is timed on ``sample`` pairs (one token's first slots, one expert
+    each) and scaled by the layer's active experts, since the oracle's per-expert work (decoding the
+    expert's weights exactly, its GEMMs) dominates and does not depend on the rows at decode."""
     from oracle import moe as OM
     from oracle import route as OR
 
-    ids, wts, _, _ = OR.route(x_np, wr_np, cfg.n_group, cfg.topk_group, cfg.topk)
-    cls = OM.FP8Expert if fmt == "fp8" else OM.NVFP4Expert
-    tok = 1
-    need = sorted(set(int(e) for e in ids[:tok].ravel()))
-    experts = {}
-    for e in need:
-        experts[e] = cls(w13[e, :cfg.I].float().cpu().numpy(), w13[e, cfg.I:].float().cpu().numpy(),
-                         w2[e].float().cpu().numpy())
     t0 = time.perf_counter()
     OR.route(x_np, wr_np, cfg.n_group, cfg.topk_group, cfg.topk)
     t_route = time.perf_counter() - t0
-    t1 = time.perf_counter()
-    xq, xh = OM.quantize_activations(x_np[:tok], fmt)
-    OM.moe_expert_mlp(xh, ids[:tok], wts[:tok], experts, fmt, cfg.combine_scale)
-    t_mlp = time.perf_counter() - t1
-    per_token = t_route / x_np.shape[0] + t_mlp / tok
+    t0 = time.perf_counter()
+    OM.quantize_activations(x_np, fmt)
+    t_xq = time.perf_counter() - t0
+    _, xh = OM.quantize_activations(x_np[:1], fmt)
+    t0 = time.perf_counter()
+    OM.moe_expert_mlp(xh, ids[:1, :sample], wts[:1, :sample], experts, fmt, cfg.combine_scale)
+    t_mlp = time.perf_counter() - t0
+    n_act = len(np.unique(ids))
+    return t_route + t_xq + t_mlp / sample * n_act, (t_route, t_xq, t_mlp, n_act)
+
+
+def cpu_baseline(dev):
+    """The CPU oracle (NumPy, float64 GEMMs on exactly decoded operands) on the host cores of this machine, on
+    bounded samples, with all host threads and with one thread:
+
+    * decode-64 NVFP4 (the headline workload): routing and activation quantization of all 64 tokens
+      timed whole, the expert MLP timed on 4 experts and scaled per active expert (222);
+    * the tiny layer (64 tokens, hidden 256, 16 experts): the whole layer;
+    * the standalone 32768 x 5120 quantize: 512 rows, scaled by 64.
+
+    Weight quantization is offline (untimed), as on the GPU."""
+    from oracle import moe as OM
+    from oracle import quant as Q
+    from oracle import quant_c as QC
+    from oracle import route as OR
+
+    cfg = W.DECODE
+    x_np, wr_np = W.activations(cfg), W.router_weights(cfg)
+    ids, wts, _, _ = OR.route(x_np, wr_np, cfg.n_group, cfg.topk_group, cfg.topk)
+    sample = 4
+    es = [int(e) for e in ids[0, :sample]]
+    w13, w2 = W.expert_weights_device(cfg, device=dev, experts=es)
+    experts = {}
+    for i, e in enumerate(es):
+        bits = [t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                for t in (w13[i, :cfg.I], w13[i, cfg.I:], w2[i])]
+        ex = OM.NVFP4Expert(*bits, q=QC)  # offline quantization (untimed) by the oracle's C loops ...
+        ex.q = Q  # ... and the timed decoding by its NumPy definition
+        experts[e] = ex
+    del w13, w2
+    tcfg = W.TINY
+    tx, twr = W.activations(tcfg), W.router_weights(tcfg)
+    texperts = {e: OM.NVFP4Expert(*W.expert_weights_host(tcfg, e), q=QC) for e in range(tcfg.E)}
+    for ex in texperts.values():
+        ex.q = Q
+    qx = W.quant_tensor_host((512, 5120), seed=2)
+
+    def measure():
+        t_dec, parts = _oracle_decode_time(cfg, "nvfp4", x_np, wr_np, ids, wts, experts, sample)
+        t0 = time.perf_counter()
+        OM.moe_layer(tx, twr, texperts, "nvfp4", tcfg.n_group, tcfg.topk_group, tcfg.topk, tcfg.combine_scale)
+        t_tiny = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        Q.nvfp4_quantize(qx)
+        t_q = (time.perf_counter() - t0) * (W.QUANT_SHAPE[0] / qx.shape[0])
+        return {"decode_tokens_per_s": cfg.T / t_dec, "decode_s": t_dec,
+                "decode_parts_s": {"route": parts[0], "x_quant": parts[1], f"mlp_{sample}_experts": parts[2],
+                                   "active_experts": parts[3]},
+                "tiny_tokens_per_s": tcfg.T / t_tiny, "tiny_s": t_tiny,
+                "quantize_32768x5120_s": t_q, "quantize_gbps": 429.9e6 / t_q / 1e9}
+
     threads = len(os.sched_getaffinity(0))
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"routing of all {x_np.shape[0]} tokens ({t_route:.2f} s) + quantize and expert MLP of "
-                      f"{tok} token ({len(need)} experts, {t_mlp:.2f} s); numpy float64 on {threads} host threads"}
+    full = measure()
+    with _thread_limit(1):
+        one = measure()
+    def rnd(d):
+        return {k: (round(v, 4) if isinstance(v, float) else rnd(v) if isinstance(v, dict) else v)
+                for k, v in d.items()}
+
+    return {"value": round(full["decode_tokens_per_s"], 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"decode-64 NVFP4 layer: routing + activation quantization of all 64 tokens timed whole, "
+                       f"expert MLP of {sample} experts ({full['decode_parts_s'][f'mlp_{sample}_experts']:.2f} s) "
+                       f"scaled to the {full['decode_parts_s']['active_experts']} active experts; NumPy float64 "
+                       f"on {threads} host threads"),
+            "all_threads": rnd(full), "one_thread": rnd(one), **_blas_info()}
 
 
-def run_stack(args, dev):
-    """Four Beam-shaped MoE layers on a 4096-token FP32 stream, NVFP4 and FP8 side by side."""
+def stack_numbers(dev, steps, warmup):
+    """Four Beam-shaped MoE layers on a 4096-token FP32 stream (RMSNorm -> MoE -> depth-scaled residual),
+    NVFP4 and FP8 side by side; one step = the whole 4-layer stack."""
     cfg = W.STACK
     x1 = torch.from_numpy(W.activations(cfg)).to(dev)
     res = {}
@@ -373,23 +460,34 @@ def run_stack(args, dev):
             layers.append((wr, bsm.quantize_expert_weights(w13, w2, fmt)))
             del w13, w2
             torch.cuda.empty_cache()
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             bsm.moe_stack(x1, layers, cfg.n_group, cfg.topk_group, cfg.topk)
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         start.record()
-        for _ in range(args.steps):
+        for _ in range(steps):
             bsm.moe_stack(x1, layers, cfg.n_group, cfg.topk_group, cfg.topk)
         stop.record()
         torch.cuda.synchronize()
-        ms = start.elapsed_time(stop) / args.steps
+        ms = start.elapsed_time(stop) / steps
         flop = cfg.layers * (2.0 * cfg.T * cfg.topk * 3 * cfg.H * cfg.I + 2.0 * cfg.T * cfg.E * cfg.H)
+        wbytes = sum(sum(t.numel() * t.element_size() for t in (w.w13_codes, w.w13_scales, w.w2_codes, w.w2_scales))
+                     for _, w in layers)
         res[fmt] = {"tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
-                    "tflops": round(flop / (ms * 1e-3) / 1e12, 2)}
+                    "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                    "frac_f16_mfma_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["f16"], 4),
+                    "weight_gbps": round(wbytes / (ms * 1e-3) / 1e9, 1)}
         print(f"[bench] stack {fmt}: {ms:.3f} ms per 4-layer step", file=sys.stderr, flush=True)
         del layers
         torch.cuda.empty_cache()
+    return res
+
+
+def run_stack(args, dev):
+    """--workload stack: the 4-layer stack as the line's workload."""
+    cfg = W.STACK
+    res = stack_numbers(dev, args.steps, args.warmup)
     line = {
         "metric": METRIC, "value": res["nvfp4"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["nvfp4"]["ms_per_step"],
@@ -401,6 +499,68 @@ def run_stack(args, dev):
         "stack": res,
     }
     print(json.dumps(line))
+
+
+def quantize_numbers(dev, steps, warmup):
+    """The standalone NVFP4 quantize of a 32768 x 5120 bf16 tensor (Student-t with outlier rows): global
+    amax, per-16 E4M3 scales and E2M1 codes; algorithmic bytes 2 B read + 0.5625 B written per value."""
+    xs = [W.quant_tensor_device(device=dev), None]
+    xs[1] = xs[0].clone()
+    R, C = W.QUANT_SHAPE
+    codes = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((R, C // 16), dtype=torch.uint8, device=dev)
+    gs = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = None
+    for i in range(warmup):
+        ws = bsm.nvfp4_quantize_into(xs[i % 2], codes, scales, gs, ws)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        ws = bsm.nvfp4_quantize_into(xs[i % 2], codes, scales, gs, ws)
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) / steps * 1e3
+    alg = R * C * 2 + R * C // 2 + R * C // 16
+    return {"us": round(us, 2), "algorithmic_bytes": alg, "gbps": round(alg / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "floor_us": round(alg / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}
+
+
+def ceilings(dev, reps=10):
+    """Measured ceilings of this GPU: streaming HBM read (best over workgroup counts) and the FP16 MFMA
+    rate from registers (32x32x16 and 16x16x32, FP32 accumulation)."""
+    nbytes = 4 << 30
+    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(2)]
+    best = 0.0
+    for wgs in (1024, 2048, 4096, 8192):
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+        bsm.ceiling_hbm_read(bufs[0], wgs, sink)
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for r in range(reps):
+            bsm.ceiling_hbm_read(bufs[r % 2], wgs, sink)
+        stop.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes * reps / (start.elapsed_time(stop) * 1e-3) / 1e9)
+    del bufs
+    torch.cuda.empty_cache()
+    out = {"hbm_read_gbps": round(best, 1)}
+    wgs, iters = 2048, 4000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    for shape, name, fl in ((0, "mfma_f16_32x32x16_tflops", 32768), (1, "mfma_f16_16x16x32_tflops", 16384)):
+        bsm.ceiling_mfma_f16(shape, iters, wgs, sink)
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            bsm.ceiling_mfma_f16(shape, iters, wgs, sink)
+        stop.record()
+        torch.cuda.synchronize()
+        flop = wgs * 4 * iters * 8 * fl * reps
+        out[name] = round(flop / (start.elapsed_time(stop) * 1e-3) / 1e12, 1)
+    return out
 
 
 def run_dense_fp8(args, dev):
@@ -453,6 +613,31 @@ def run_dense_fp8(args, dev):
         "gbps_weights": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBS, 4), "weight_bytes": int(wbytes)}))
 
 
+def prefill_object(fmt, pn, pms, pst, psteps):
+    mm = {"nvfp4": "fp4", "fp8": "fp8", "w4a16": "f16"}[fmt]
+    return {
+        "tokens_per_s": round(pn["tokens_per_s"], 1), "ms_per_step": round(pms, 4),
+        "tflops": round(pn["tflops"], 2), "frac_fp4_or_fp8_peak": round(pn["tflops"] / PEAK_TFLOPS[mm], 4),
+        "frac_f16_mfma_peak": round(pn["tflops"] / PEAK_TFLOPS["f16"], 4), "gbps": round(pn["gbps"], 1),
+        "active_experts": pn["active_experts"], "max_expert_rows": pn["max_expert_rows"],
+        "stage_ms": {k: round(v, 4) for k, v in pst.items()},
+        "gemm1": {k: round(v, 3) for k, v in pn["gemm1"].items()},
+        "steps": psteps,
+    }
+
+
+def measure_layer(cfg, fmt, dev, steps, warmup):
+    x, wr, w13, w2, weights = build_layer(cfg, fmt, dev)
+    del w13, w2
+    torch.cuda.empty_cache()
+    ms, stage_ms, g1_ms, counts = run_steps(cfg, fmt, x, wr, weights, steps, warmup,
+                                            copies=[second_copy(x, wr, weights)])
+    del x, wr, weights
+    torch.cuda.empty_cache()
+    print(f"[bench] {cfg.name} {fmt}: {ms:.3f} ms/step, stages {stage_ms}", file=sys.stderr, flush=True)
+    return ms, stage_ms, g1_ms, layer_numbers(cfg, fmt, cfg.T, ms, stage_ms, g1_ms, counts)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -461,7 +646,10 @@ def main():
     ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "fp8", "w4a16"])
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "stack", "dense-fp8"])
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the FP8 layers, the standalone quantize, the stack and the ceilings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceilings", action="store_true", help="only measure the HBM read and FP16 MFMA ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB elementwise copy (reference for the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
@@ -490,6 +678,9 @@ def main():
     dev = torch.device("cuda:0")
     bsm.load()
 
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(dev)}))
+        return
     if args.workload == "stack":
         run_stack(args, dev)
         return
@@ -497,11 +688,7 @@ def main():
         run_dense_fp8(args, dev)
         return
     main_cfg = W.DECODE if args.workload == "decode" else W.PREFILL
-    x, wr, w13, w2, weights = build_layer(main_cfg, args.fmt, dev)
-    ms, stage_ms, g1_ms, counts = run_steps(main_cfg, args.fmt, x, wr, weights, args.steps, args.warmup,
-                                            copies=[second_copy(x, wr, weights)])
-    main_nums = layer_numbers(main_cfg, args.fmt, main_cfg.T, ms, stage_ms, g1_ms, counts)
-    print(f"[bench] {main_cfg.name} {args.fmt}: {ms:.3f} ms/step, stages {stage_ms}", file=sys.stderr, flush=True)
+    ms, stage_ms, g1_ms, main_nums = measure_layer(main_cfg, args.fmt, dev, args.steps, args.warmup)
 
     g1 = main_nums["gemm1"]
     traffic = measured_traffic() if (args.workload == "decode" and args.fmt == "nvfp4") else None
@@ -513,36 +700,41 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev)
 
+    extras = args.workload == "decode" and not args.no_extras
+    psteps = max(3, args.steps // 4)
     prefill = None
     if args.workload == "decode" and not args.no_prefill:
-        del weights, w13, w2
-        torch.cuda.empty_cache()
-        pcfg = W.PREFILL
-        px, pwr, pw13, pw2, pweights = build_layer(pcfg, args.fmt, dev)
-        psteps = max(3, args.steps // 4)
-        pms, pst, pg1, pcounts = run_steps(pcfg, args.fmt, px, pwr, pweights, psteps, 2,
-                                           copies=[second_copy(px, pwr, pweights)])
-        pn = layer_numbers(pcfg, args.fmt, pcfg.T, pms, pst, pg1, pcounts)
-        print(f"[bench] prefill {args.fmt}: {pms:.3f} ms/step, stages {pst}", file=sys.stderr, flush=True)
-        mm = {"nvfp4": "fp4", "fp8": "fp8", "w4a16": "f16"}[args.fmt]
-        prefill = {
-            "tokens_per_s": round(pn["tokens_per_s"], 1), "ms_per_step": round(pms, 4),
-            "tflops": round(pn["tflops"], 2), "frac_fp4_or_fp8_peak": round(pn["tflops"] / PEAK_TFLOPS[mm], 4),
-            "frac_f16_mfma_peak": round(pn["tflops"] / PEAK_TFLOPS["f16"], 4), "gbps": round(pn["gbps"], 1),
-            "active_experts": pn["active_experts"], "max_expert_rows": pn["max_expert_rows"],
-            "stage_ms": {k: round(v, 4) for k, v in pst.items()},
-            "gemm1": {k: round(v, 3) for k, v in pn["gemm1"].items()},
-            "steps": psteps,
-        }
-        del pweights, pw13, pw2
-        torch.cuda.empty_cache()
-        w13 = w2 = None
+        pms, pst, _, pn = measure_layer(W.PREFILL, args.fmt, dev, psteps, 2)
+        prefill = prefill_object(args.fmt, pn, pms, pst, psteps)
+
+    fp8_decode = fp8_prefill = quant = stack = ceil = None
+    if extras and args.fmt == "nvfp4":
+        fms, fst, _, fn = measure_layer(W.DECODE, "fp8", dev, args.steps, args.warmup)
+        fg1 = fn["gemm1"]
+        fp8_decode = {"tokens_per_s": round(fn["tokens_per_s"], 1), "ms_per_step": round(fms, 4),
+                      "gbps": round(fn["gbps"], 1), "hbm_frac": round(fn["hbm_frac"], 4),
+                      "active_experts": fn["active_experts"], "stage_ms": {k: round(v, 4) for k, v in fst.items()},
+                      "roofline_gate_up": {"bound": "hbm", "achieved": round(fg1["gbps"], 1), "peak": HBM_PEAK_GBS,
+                                           "frac": round(fg1["gbps"] / HBM_PEAK_GBS, 4),
+                                           "algorithmic_bytes_per_launch": int(fg1["bytes"]),
+                                           "avg_launch_ms": round(fg1["ms"], 4)}}
+        if not args.no_prefill:
+            qms, qst, _, qn = measure_layer(W.PREFILL, "fp8", dev, psteps, 2)
+            fp8_prefill = prefill_object("fp8", qn, qms, qst, psteps)
+    if extras:
+        quant = quantize_numbers(dev, args.steps, args.warmup)
+        print(f"[bench] quantize 32768x5120: {quant}", file=sys.stderr, flush=True)
+        stack = stack_numbers(dev, max(3, args.steps // 4), 2)
+        ceil = ceilings(dev)
+        print(f"[bench] ceilings: {ceil}", file=sys.stderr, flush=True)
+        roofline["frac_of_measured_read_ceiling"] = round(g1["gbps"] / ceil["hbm_read_gbps"], 4)
+        if prefill:
+            prefill["frac_of_measured_f16_mfma_ceiling"] = round(
+                prefill["tflops"] / ceil["mfma_f16_32x32x16_tflops"], 4)
 
     cpu = None
-    if not args.no_cpu_baseline and args.workload == "decode":
-        if w13 is None:
-            w13, w2 = W.expert_weights_device(main_cfg, device=dev)
-        cpu = cpu_baseline(main_cfg, args.fmt, w13, w2, W.activations(main_cfg), W.router_weights(main_cfg))
+    if not args.no_cpu_baseline and args.workload == "decode" and args.fmt == "nvfp4":
+        cpu = cpu_baseline(dev)
 
     line = {
         "metric": METRIC,
@@ -569,6 +761,11 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill_8192": prefill,
+        "fp8_decode_64": fp8_decode,
+        "fp8_prefill_8192": fp8_prefill,
+        "quantize_32768x5120": quant,
+        "stack_4x4096": stack,
+        "ceilings": ceil,
     }
     print(json.dumps(line))
 

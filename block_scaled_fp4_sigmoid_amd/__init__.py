@@ -65,7 +65,7 @@ def load():
         "bsm_last_error": (ctypes.c_char_p, []),
         "bsm_nvfp4_quantize_workspace_size": (sz, [i64, i64, i64]),
         "bsm_nvfp4_quantize": (i32, [vp, i32, i64, i64, i64, vp, vp, vp, i32, vp, sz, vp]),
-        "bsm_nvfp4_dequantize": (i32, [vp, vp, vp, i64, i64, i64, vp, vp]),
+        "bsm_nvfp4_dequantize": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp]),
         "bsm_local_hessian_blocks": (i32, [vp, i32, i64, i64, vp, vp]),
         "bsm_nvfp4_quantize_local_hessian": (i32, [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp, sz, vp]),
         "bsm_fp8_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
@@ -82,7 +82,10 @@ def load():
         "bsm_fp8_linear_workspace_size": (sz, [i64, i64, i64]),
         "bsm_fp8_linear": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         "bsm_set_stage_events": (i32, [i32, ctypes.POINTER(vp), i32]),
-        "bsm_rmsnorm_f32": (i32, [vp, i64, i64, f32, vp, vp]),
+        "bsm_rmsnorm_f32": (i32, [vp, i64, i64, f32, vp, vp, vp]),
+        "bsm_residual_step_weights": (i32, [i64, ctypes.POINTER(f32), ctypes.POINTER(f32)]),
+        "bsm_ceiling_hbm_read": (i32, [vp, sz, vp, i32, vp]),
+        "bsm_ceiling_mfma_f16": (i32, [i32, i64, vp, i32, vp]),
         "bsm_scaled_residual_f32": (i32, [vp, vp, f32, f32, i64, i64, vp]),
     }
     for name, (res, args) in sig.items():
@@ -160,16 +163,37 @@ def nvfp4_quantize(x: torch.Tensor, global_scale: Optional[torch.Tensor] = None)
     return codes, scales, gs
 
 
-def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor):
-    """float32 values fl32(fl32(q * s_b) * S_g) of NVFP4 tensors."""
+def nvfp4_quantize_into(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, gs: torch.Tensor,
+                        ws: Optional[torch.Tensor] = None):
+    """Dynamic NVFP4 of one tensor x [R, C] into caller buffers codes [R, C/2], scales [R, C/16], gs [1];
+    ``ws`` (returned) is reused when large enough."""
+    lib = load()
+    for t, n in ((x, "x"), (codes, "codes"), (scales, "scales"), (gs, "gs")):
+        _dev(t, n)
+    R, C = x.shape
+    if tuple(codes.shape) != (R, C // 2) or tuple(scales.shape) != (R, C // 16) or gs.numel() != 1:
+        raise BsmError("codes [R, C/2], scales [R, C/16] and gs [1] buffers required")
+    need = lib.bsm_nvfp4_quantize_workspace_size(1, R, C)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, x.device)
+    _check(lib.bsm_nvfp4_quantize(_ptr(x), _dtype_code(x), 1, R, C, _ptr(codes), _ptr(scales), _ptr(gs), GS_DYNAMIC,
+                                  _ptr(ws), ws.numel(), _stream()))
+    return ws
+
+
+def nvfp4_dequantize(codes: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor,
+                     out_dtype: torch.dtype = torch.float32):
+    """Values q * s_b * S_g of NVFP4 tensors, rounded once to ``out_dtype`` (float32 or bfloat16)."""
     lib = load()
     _dev(codes, "codes")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise BsmError("out_dtype must be torch.float32 or torch.bfloat16")
     squeeze = codes.dim() == 2
     c3 = codes.unsqueeze(0) if squeeze else codes
     B, R, C2 = c3.shape
-    out = torch.empty((B, R, C2 * 2), dtype=torch.float32, device=codes.device)
+    out = torch.empty((B, R, C2 * 2), dtype=out_dtype, device=codes.device)
     _check(lib.bsm_nvfp4_dequantize(_ptr(c3), _ptr(_dev(scales, "scales")), _ptr(_dev(global_scale, "gs")), B, R,
-                                    C2 * 2, _ptr(out), _stream()))
+                                    C2 * 2, _dtype_code(out), _ptr(out), _stream()))
     return out[0] if squeeze else out
 
 
@@ -452,35 +476,44 @@ def set_stage_events(which: int, handles):
 # ---------------------------------------------------------------------------
 
 
+def residual_step_weights(k: int):
+    """(a_k, b_k) of residual step k >= 2, from the library (fl32 of sqrt((k-1)/k) and 1/sqrt(k))."""
+    lib = load()
+    a, b = ctypes.c_float(), ctypes.c_float()
+    _check(lib.bsm_residual_step_weights(int(k), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
 def moe_stack(x1: torch.Tensor, layers, n_group, topk_group, topk, eps=1e-6, combine_scale=2.5, keep=False):
     """Stack of MoE layers on an FP32 residual stream whose input is residual step 1.
 
     Layer i (1-based) is residual step k = i + 1:  n = RMSNorm(x);  m = MoE_i(n);
-    x <- fl32(sqrt((k-1)/k) * x + (1/sqrt(k)) * m).  ``layers``: list of
+    x <- fl32(a_k * x + b_k * m) with (a_k, b_k) = residual_step_weights(k).  ``layers``: list of
     (w_router, ExpertWeights).  Returns the final stream (and, with keep=True, the
     per-layer (stream input, normed, ids, weights, moe output)).
     """
-    import math
-
     x = x1.clone().float().contiguous()
     trace = []
     for i, (wr, weights) in enumerate(layers, start=1):
-        k = i + 1
         n = rmsnorm(x, eps)
         m, ids, wts = moe_layer(n, wr, weights, n_group, topk_group, topk, combine_scale)
         if keep:
             trace.append((x.clone(), n, ids, wts, m))
-        a = float(torch.tensor(math.sqrt((k - 1) / k), dtype=torch.float32))
-        b = float(torch.tensor(1.0 / math.sqrt(k), dtype=torch.float32))
+        a, b = residual_step_weights(i + 1)
         scaled_residual_(x, m, a, b)
     return (x, trace) if keep else x
 
 
-def rmsnorm(x: torch.Tensor, eps=1e-6):
+def rmsnorm(x: torch.Tensor, eps=1e-6, gamma: Optional[torch.Tensor] = None):
+    """FP32 RMSNorm of the rows of x, times the gain ``gamma`` [H] if given (else gain 1)."""
     lib = load()
     _dev(x, "x")
+    if gamma is not None:
+        _dev(gamma, "gamma")
+        if gamma.dtype != torch.float32 or tuple(gamma.shape) != (x.shape[1],):
+            raise BsmError(f"gamma must be float32 [{x.shape[1]}]")
     y = torch.empty_like(x)
-    _check(lib.bsm_rmsnorm_f32(_ptr(x), x.shape[0], x.shape[1], float(eps), _ptr(y), _stream()))
+    _check(lib.bsm_rmsnorm_f32(_ptr(x), x.shape[0], x.shape[1], float(eps), _ptr(gamma), _ptr(y), _stream()))
     return y
 
 
@@ -491,3 +524,20 @@ def scaled_residual_(x: torch.Tensor, m: torch.Tensor, a: float, b: float):
     _dev(m, "m")
     _check(lib.bsm_scaled_residual_f32(_ptr(x), _ptr(m), float(a), float(b), x.shape[0], x.shape[1], _stream()))
     return x
+
+
+# ---------------------------------------------------------------------------
+# measurement aids
+# ---------------------------------------------------------------------------
+
+
+def ceiling_hbm_read(buf: torch.Tensor, wgs: int, sink: torch.Tensor):
+    """Enqueue one streaming read of ``buf`` (see bsm_ceiling_hbm_read); ``sink`` holds wgs * 256 words."""
+    lib = load()
+    _check(lib.bsm_ceiling_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(wgs), _stream()))
+
+
+def ceiling_mfma_f16(shape: int, iters: int, wgs: int, sink: torch.Tensor):
+    """Enqueue the FP16 MFMA loop (shape 0: 32x32x16, 1: 16x16x32); ``sink`` holds wgs * 256 floats."""
+    lib = load()
+    _check(lib.bsm_ceiling_mfma_f16(int(shape), int(iters), _ptr(sink), int(wgs), _stream()))

@@ -11,7 +11,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["bsm_abi.hip", "bsm_quant.hip", "bsm_route.hip", "bsm_moe.hip"]
+SOURCES = ["bsm_abi.hip", "bsm_quant.hip", "bsm_route.hip", "bsm_moe.hip", "bsm_ceil.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
          "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -2,6 +2,7 @@
 // argument validation on the host, workspace sizing, kernel launches.
 // Every check runs before anything is enqueued; on error nothing is launched.
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -200,14 +201,16 @@ int bsm_nvfp4_quantize_local_hessian(const void* w, int w_dtype, int64_t R, int6
 }
 
 int bsm_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale, int64_t B, int64_t R,
-                         int64_t C, float* out, bsm_stream_t stream) {
+                         int64_t C, int out_dtype, void* out, bsm_stream_t stream) {
+  if (!dtype_ok(out_dtype)) return fail(BSM_ERR_INVALID_ARG, "out_dtype must be BSM_BF16 or BSM_F32");
   if (B < 0 || R < 0 || C < 0) return fail(BSM_ERR_INVALID_ARG, "negative shape");
   if (C % 16 != 0) return fail(BSM_ERR_INVALID_ARG, "C (%lld) must be a multiple of 16", (long long)C);
   if (B > 65535) return fail(BSM_ERR_UNSUPPORTED, "B (%lld) > 65535", (long long)B);
   if (B * R * C == 0) return ok();
   if (!codes || !scales || !global_scale || !out) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
   if (!aligned(codes, 8) || !aligned(out, 16)) return fail(BSM_ERR_INVALID_ARG, "codes 8-byte / out 16-byte alignment");
-  return hip_status(bsm::launch_nvfp4_dequantize(codes, scales, global_scale, B, R, C, out, (hipStream_t)stream),
+  return hip_status(bsm::launch_nvfp4_dequantize(codes, scales, global_scale, B, R, C, out_dtype == BSM_BF16, out,
+                                                 (hipStream_t)stream),
                     "bsm_nvfp4_dequantize");
 }
 
@@ -405,12 +408,35 @@ int bsm_set_stage_events(int which, void* const* events, int n) {
   return ok();
 }
 
-int bsm_rmsnorm_f32(const float* x, int64_t T, int64_t H, float eps, float* y, bsm_stream_t stream) {
+int bsm_ceiling_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int wgs, bsm_stream_t stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || !aligned(buf, 16) || wgs < 1 || wgs > (1 << 20))
+    return fail(BSM_ERR_INVALID_ARG, "bsm_ceiling_hbm_read: buf 16-byte aligned, bytes a positive multiple of 16, "
+                                     "wgs in [1, 2^20], sink non-NULL");
+  return hip_status(bsm::launch_ceil_read(buf, bytes, sink, wgs, (hipStream_t)stream), "bsm_ceiling_hbm_read");
+}
+
+int bsm_ceiling_mfma_f16(int shape, int64_t iters, float* sink, int wgs, bsm_stream_t stream) {
+  if ((shape != 0 && shape != 1) || iters < 1 || !sink || wgs < 1 || wgs > (1 << 20))
+    return fail(BSM_ERR_INVALID_ARG, "bsm_ceiling_mfma_f16: shape 0 or 1, iters >= 1, wgs in [1, 2^20], sink "
+                                     "non-NULL");
+  return hip_status(bsm::launch_ceil_mfma(shape, iters, sink, wgs, (hipStream_t)stream), "bsm_ceiling_mfma_f16");
+}
+
+int bsm_rmsnorm_f32(const float* x, int64_t T, int64_t H, float eps, const float* gamma, float* y,
+                    bsm_stream_t stream) {
   if (T < 0 || H <= 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
   if (!(eps >= 0.0f)) return fail(BSM_ERR_INVALID_ARG, "eps must be >= 0");
   if (T == 0) return ok();
   if (!x || !y) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
-  return hip_status(bsm::launch_rmsnorm(x, T, H, eps, y, (hipStream_t)stream), "bsm_rmsnorm_f32");
+  return hip_status(bsm::launch_rmsnorm(x, T, H, eps, gamma, y, (hipStream_t)stream), "bsm_rmsnorm_f32");
+}
+
+int bsm_residual_step_weights(int64_t k, float* a, float* b) {
+  if (k < 2) return fail(BSM_ERR_INVALID_ARG, "residual step k must be >= 2 (the embedding is step 1)");
+  if (!a || !b) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  *a = (float)sqrt((double)(k - 1) / (double)k);
+  *b = (float)(1.0 / sqrt((double)k));
+  return ok();
 }
 
 int bsm_scaled_residual_f32(float* x, const float* m, float a, float b, int64_t T, int64_t H, bsm_stream_t stream) {

@@ -35,7 +35,7 @@ hipError_t launch_nvfp4_quantize_from_amax(const void* x, bool x_bf16, int64_t B
                                            const uint32_t* amax_bits, const float* static_gs,
                                            hipStream_t st, _Float16* dec16 = nullptr);
 hipError_t launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t B,
-                                   int64_t R, int64_t C, float* out, hipStream_t st);
+                                   int64_t R, int64_t C, bool bf16_out, void* out, hipStream_t st);
 // dec16 (optional): also writes the exact FP16 values of the E4M3 codes (row scale not applied)
 hipError_t launch_fp8_quantize(const void* x, bool x_bf16, int64_t R, int64_t C, uint8_t* codes, float* scales,
                                hipStream_t st, _Float16* dec16 = nullptr);
@@ -99,7 +99,11 @@ inline void stage_mark(int which, int i, hipStream_t st) {
 }
 
 // ---- norm / residual ------------------------------------------------------
-hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t H, float eps, float* y, hipStream_t st);
+// measurement aids: HBM read and FP16 MFMA ceilings
+hipError_t launch_ceil_read(const void* buf, size_t bytes, uint32_t* sink, int wgs, hipStream_t st);
+hipError_t launch_ceil_mfma(int shape, int64_t iters, float* sink, int wgs, hipStream_t st);
+hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t H, float eps, const float* gamma, float* y,
+                          hipStream_t st);
 hipError_t launch_residual(float* x, const float* m, float a, float b, int64_t n, hipStream_t st);
 
 }  // namespace bsm

@@ -1835,7 +1835,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 namespace {
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int64_t H, float eps,
-                                                 float* __restrict__ y) {
+                                                 const float* __restrict__ gamma, float* __restrict__ y) {
   __shared__ double part[4];
   const int64_t t = blockIdx.x;
   const float* xr = x + t * H;
@@ -1851,7 +1851,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, in
   const double tot = ((part[0] + part[1]) + part[2]) + part[3];
   const float ms = (float)(tot / (double)H);
   const float r = (float)(1.0 / sqrt((double)ms + (double)eps));
-  for (int64_t k = threadIdx.x; k < H; k += 256) y[t * H + k] = xr[k] * r;
+  if (gamma)
+    for (int64_t k = threadIdx.x; k < H; k += 256) y[t * H + k] = (xr[k] * r) * gamma[k];
+  else
+    for (int64_t k = threadIdx.x; k < H; k += 256) y[t * H + k] = xr[k] * r;
 }
 
 __global__ __launch_bounds__(256) void k_residual(float* __restrict__ x, const float* __restrict__ m, double a,
@@ -1861,9 +1864,10 @@ __global__ __launch_bounds__(256) void k_residual(float* __restrict__ x, const f
 }
 }  // namespace
 
-hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t H, float eps, float* y, hipStream_t st) {
+hipError_t launch_rmsnorm(const float* x, int64_t T, int64_t H, float eps, const float* gamma, float* y,
+                          hipStream_t st) {
   if (T == 0) return hipSuccess;
-  k_rmsnorm<<<(unsigned)T, 256, 0, st>>>(x, H, eps, y);
+  k_rmsnorm<<<(unsigned)T, 256, 0, st>>>(x, H, eps, gamma, y);
   return hipGetLastError();
 }
 

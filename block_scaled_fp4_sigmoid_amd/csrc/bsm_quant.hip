@@ -165,30 +165,55 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_encode(const void* __restric
   }
 }
 
+// out = the exact q * s_b * S_g rounded once: to binary32 (fl32 of an exact product: q * s_b is exact in
+// binary32) or to BF16 (from the exact binary64 product: rounded to odd at binary32, whose 24 bits leave
+// room for the single correct round to nearest even at BF16's 8 bits).
+template <bool BF16_OUT>
 __global__ __launch_bounds__(kThreads) void k_nvfp4_decode(const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
                                                            const float* __restrict__ gs, int64_t n_blk,
-                                                           float* __restrict__ out) {
+                                                           void* __restrict__ out) {
   const int b = blockIdx.y;
   const float S = gs[b];
   const uint8_t* cb = codes + (int64_t)b * n_blk * 8;
   const uint8_t* sb = scales + (int64_t)b * n_blk;
-  float* ob = out + (int64_t)b * n_blk * 16;
   for (int64_t f = (int64_t)blockIdx.x * kThreads + threadIdx.x; f < n_blk; f += (int64_t)gridDim.x * kThreads) {
     const uint2 c = *reinterpret_cast<const uint2*>(cb + f * 8);
     const float sv = e4m3_value_mag(sb[f]);
-    float o[16];
+    if constexpr (BF16_OUT) {
+      uint32_t o[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t w = i < 8 ? c.x : c.y;
-      const uint32_t q = (w >> (4 * (i & 7))) & 15u;
-      const float e = e2m1_value_mag(q & 7u) * sv;  // exact: <= 6 significant bits
-      const float r = e * S;
-      o[i] = (q & 8u) ? -r : r;
+      for (int i = 0; i < 16; i += 2) {
+        uint32_t h2 = 0;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t w = i + k < 8 ? c.x : c.y;
+          const uint32_t q = (w >> (4 * ((i + k) & 7))) & 15u;
+          const double d = (double)(e2m1_value_mag(q & 7u) * sv) * (double)S;  // exact: <= 30 significant bits
+          const float t = __double2float_rz(d);
+          const uint32_t u = f2u(t) | ((double)t != d ? 1u : 0u);  // round to odd at binary32
+          const uint32_t hb = ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16) | ((q & 8u) ? 0x8000u : 0u);
+          h2 |= hb << (16 * k);
+        }
+        o[i / 2] = h2;
+      }
+      uint4* op = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + ((int64_t)b * n_blk + f) * 16);
+      op[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      op[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+      float o[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t w = i < 8 ? c.x : c.y;
+        const uint32_t q = (w >> (4 * (i & 7))) & 15u;
+        const float e = e2m1_value_mag(q & 7u) * sv;  // exact: <= 6 significant bits
+        const float r = e * S;
+        o[i] = (q & 8u) ? -r : r;
+      }
+      float4* op = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + ((int64_t)b * n_blk + f) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) op[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
     }
-    float4* op = reinterpret_cast<float4*>(ob + f * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) op[i] = make_float4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
   }
 }
 
@@ -460,13 +485,16 @@ hipError_t launch_nvfp4_quantize_lh(const void* w, bool w_bf16, int64_t R, int64
 }
 
 hipError_t launch_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gs, int64_t B, int64_t R,
-                                   int64_t C, float* out, hipStream_t st) {
+                                   int64_t C, bool bf16_out, void* out, hipStream_t st) {
   const int64_t n_blk = R * C / 16;
   if (n_blk == 0 || B == 0) return hipSuccess;
   int64_t p = (n_blk + kThreads * 4 - 1) / (kThreads * 4);
   if (p > 4096) p = 4096;
   dim3 g((unsigned)p, (unsigned)B);
-  k_nvfp4_decode<<<g, kThreads, 0, st>>>(codes, scales, gs, n_blk, out);
+  if (bf16_out)
+    k_nvfp4_decode<true><<<g, kThreads, 0, st>>>(codes, scales, gs, n_blk, out);
+  else
+    k_nvfp4_decode<false><<<g, kThreads, 0, st>>>(codes, scales, gs, n_blk, out);
   return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define BSM_ABI_VERSION 1
+#define BSM_ABI_VERSION 2
 
 typedef struct ihipStream_t* bsm_stream_t; /* identical to hipStream_t */
 
@@ -133,9 +133,13 @@ int bsm_nvfp4_quantize_local_hessian(const void* w, int w_dtype, int64_t R, int6
                                      int radius, uint8_t* codes, uint8_t* scales, float* global_scale, void* ws,
                                      size_t ws_bytes, bsm_stream_t stream);
 
-/* Dequantize: out[b,r,c] = fl32(fl32(q*s_b) * S_g[b]) (q*s_b is exact), float32 output. */
+/* Dequantize [NVFP4]: out[b,r,c] = the exact value q * s_b * S_g[b] rounded once to out_dtype
+ * (nearest, ties to even): BSM_F32 gives fl32(fl32(q*s_b) * S_g) (q*s_b is exact in binary32),
+ * BSM_BF16 rounds the exact product (at most 30 significant bits) straight to BF16.
+ * codes [B,R,C/2], scales [B,R,C/16], global_scale [B] float, out [B,R,C] of out_dtype;
+ * C % 16 == 0; codes 8-byte and out 16-byte aligned. */
 int bsm_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
-                         int64_t B, int64_t R, int64_t C, float* out, bsm_stream_t stream);
+                         int64_t B, int64_t R, int64_t C, int out_dtype, void* out, bsm_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * FP8_DYNAMIC quantization, one scale per row [FP8]
@@ -323,14 +327,35 @@ int bsm_fp8_linear(const uint8_t* x_codes, const float* x_scales, const uint8_t*
 int bsm_set_stage_events(int which, void* const* events, int n);
 
 /* ------------------------------------------------------------------------
+ * Measurement aids (not part of the method): this GPU's achievable ceilings.
+ *
+ * bsm_ceiling_hbm_read: reads bytes (a multiple of 16, buf 16-byte aligned)
+ *   of buf once, 16-byte loads in 4 KB pieces per workgroup, with wgs
+ *   workgroups of 256 threads; writes one word per thread to sink (wgs * 256
+ *   uint32).  Bytes / time = the streaming read ceiling.
+ * bsm_ceiling_mfma_f16: wgs workgroups of 4 waves, each wave running iters
+ *   rounds of 8 independent FP16 MFMAs with FP32 accumulation on register
+ *   operands (shape 0: 32x32x16, 32768 flop each; shape 1: 16x16x32, 16384
+ *   flop each); writes one float per thread to sink (wgs * 256 floats).
+ * Both validate their arguments (BSM_ERR_INVALID_ARG) and enqueue on stream.
+ * ------------------------------------------------------------------------ */
+int bsm_ceiling_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int wgs, bsm_stream_t stream);
+int bsm_ceiling_mfma_f16(int shape, int64_t iters, float* sink, int wgs, bsm_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * FP32 RMSNorm and depth-scaled residual [NUM]
  *
- * bsm_rmsnorm_f32: y[t] = fl32(x[t] * r), r = fl32(1/sqrt(fl32(mean(x[t]^2)) + eps)),
- *   mean and root in float64; gain 1.
- * bsm_scaled_residual_f32: x <- fl32(a*x + b*m) in place (float64 evaluation);
- *   a = sqrt((k-1)/k), b = 1/sqrt(k) for residual step k.
+ * bsm_rmsnorm_f32: y[t] = fl32(fl32(x[t] * r) * gamma), r = fl32(1/sqrt(fl32(mean(x[t]^2)) + eps)),
+ *   mean and root in float64; gamma: device float [H], or NULL for gain 1 (the reading taken for the
+ *   synthetic stack: y = fl32(x[t] * r)).
+ * bsm_scaled_residual_f32: x <- fl32(a*x + b*m) in place (float64 evaluation).
+ * bsm_residual_step_weights: the weights of residual step k >= 2 (the embedding is step 1, MoE layer i
+ *   of a stack is step i + 1): *a = fl32(sqrt((k-1)/k)), *b = fl32(1/sqrt(k)), square roots in
+ *   float64; a and b are host pointers; no device work.
  * ------------------------------------------------------------------------ */
-int bsm_rmsnorm_f32(const float* x, int64_t T, int64_t H, float eps, float* y, bsm_stream_t stream);
+int bsm_rmsnorm_f32(const float* x, int64_t T, int64_t H, float eps, const float* gamma, float* y,
+                    bsm_stream_t stream);
+int bsm_residual_step_weights(int64_t k, float* a /* host */, float* b /* host */);
 int bsm_scaled_residual_f32(float* x, const float* m, float a, float b, int64_t T, int64_t H,
                             bsm_stream_t stream);
 

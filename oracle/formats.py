@@ -171,3 +171,18 @@ def bf16_round(a):
     keep_lsb = (b >> 16) & 1
     r = ((b + 0x7FFF + keep_lsb) >> 16) << 16
     return r.astype(np.uint32).view(np.float32)
+
+
+def bf16_round_exact(v):
+    """float64 values -> nearest BF16 value (ties to even), rounded once, returned as float64.
+
+    BF16 has 8 significant bits and binary32's exponent range (smallest subnormal
+    2^-133).  v = m * 2^e with m in [0.5, 1): the BF16 neighbours of v are the
+    multiples of 2^(e-8) (of 2^-133 below the normal range), so v / 2^q rounded
+    to the nearest integer with ties to even (numpy's rint) times 2^q is the
+    answer; both scalings are exact.  Finite inputs of BF16 range only.
+    """
+    v = np.asarray(v, np.float64)
+    _, e = np.frexp(v)
+    q = np.maximum(e - 8, -133)
+    return np.ldexp(np.rint(np.ldexp(v, -q)), q)

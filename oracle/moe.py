@@ -34,7 +34,8 @@ Readings (listed with the others in the design notes):
 * out[t] = fl32(2.5 * sum_j w[t, j] * y[t, j]) in float64, output float32;
 * rows of expert e are ordered by (token, slot) -- the stable order.
 * RMSNorm: ms = fl32(mean(x^2)) with the mean in float64, r = fl32(1 /
-  sqrt(ms + eps)) in float64, n = fl32(x * r), eps = 1e-6, gain 1.
+  sqrt(ms + eps)) in float64, n = fl32(x * r), eps = 1e-6, gain 1 (a given
+  gain gamma multiplies after that rounding: fl32(n * gamma)).
 * residual: x <- fl32(a_k * x + b_k * m), a_k = fl32(sqrt((k-1)/k)),
   b_k = fl32(1/sqrt(k)), evaluated in float64.
 
@@ -234,11 +235,15 @@ def moe_layer(x, w_router, experts, fmt, n_group, topk_group, topk, combine_scal
 # --------------------------------------------------------------------------
 
 
-def rmsnorm_f32(x, eps=1e-6):
+def rmsnorm_f32(x, eps=1e-6, gamma=None):
+    """n = fl32(x * r) (times the gain: fl32(fl32(x * r) * gamma) when gamma is given)."""
     x64 = np.asarray(x, np.float32).astype(np.float64)
     ms = np.mean(x64 * x64, axis=1).astype(np.float32).astype(np.float64)
     r = (1.0 / np.sqrt(ms + eps)).astype(np.float32)
-    return (np.asarray(x, np.float32) * r[:, None]).astype(np.float32)
+    n = (np.asarray(x, np.float32) * r[:, None]).astype(np.float32)
+    if gamma is not None:
+        n = (n * np.asarray(gamma, np.float32)[None, :]).astype(np.float32)
+    return n
 
 
 def residual_weights(k):

@@ -31,6 +31,7 @@ bounds, brute-force recomputation of single blocks).  The constants 6*448 and
 
 import numpy as np
 
+from . import formats
 from .formats import (
     e2m1_decode,
     e2m1_encode,
@@ -117,6 +118,12 @@ def nvfp4_dequantize_f32(codes, scales, S_g):
     R, C = q.shape
     v = (q.reshape(R, C // NVFP4_BLOCK, NVFP4_BLOCK) * sb[..., None]).reshape(R, C)
     return (v * F32(S_g)).astype(np.float32)
+
+
+def nvfp4_dequantize_bf16(codes, scales, S_g):
+    """Standalone dequantize to BF16: the exact q * s_b * S_g rounded once to BF16 (nearest, ties to even),
+    returned as float32 (BF16 values are exact in float32)."""
+    return formats.bf16_round_exact(nvfp4_dequantize_exact(codes, scales, S_g)).astype(np.float32)
 
 
 def fp8_quantize(x):

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import block_scaled_fp4_sigmoid_amd as bsm
@@ -30,7 +31,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsm_abi_version() == 1
+    assert lib.bsm_abi_version() == 2
     assert lib.bsm_status_str(0) == b"BSM_OK"
     assert lib.bsm_status_str(3) == b"BSM_ERR_WORKSPACE"
 
@@ -61,8 +62,9 @@ def test_fp8_and_dequant_validation(lib):
     assert lib.bsm_fp8_quantize(FAKE, 1, 4, 30, FAKE, FAKE, None) == 1
     assert lib.bsm_fp8_quantize(FAKE, 3, 4, 32, FAKE, FAKE, None) == 1
     assert lib.bsm_fp8_quantize(None, 1, 0, 32, None, None, None) == 0
-    assert lib.bsm_nvfp4_dequantize(FAKE, FAKE, FAKE, 1, 4, 24, FAKE, None) == 1
-    assert lib.bsm_nvfp4_dequantize(None, FAKE, FAKE, 1, 4, 32, FAKE, None) == 1
+    assert lib.bsm_nvfp4_dequantize(FAKE, FAKE, FAKE, 1, 4, 24, 2, FAKE, None) == 1
+    assert lib.bsm_nvfp4_dequantize(None, FAKE, FAKE, 1, 4, 32, 2, FAKE, None) == 1
+    assert lib.bsm_nvfp4_dequantize(FAKE, FAKE, FAKE, 1, 4, 32, 7, FAKE, None) == 1  # out_dtype
 
 
 @pytest.mark.parametrize("E,G,kg,k,code", [
@@ -118,10 +120,31 @@ def test_moe_noalloc_validation(lib):
 
 
 def test_norm_validation(lib):
-    assert lib.bsm_rmsnorm_f32(FAKE, 4, 0, 1e-6, FAKE, None) == 1
-    assert lib.bsm_rmsnorm_f32(FAKE, 4, 16, -1.0, FAKE, None) == 1
+    assert lib.bsm_rmsnorm_f32(FAKE, 4, 0, 1e-6, None, FAKE, None) == 1
+    assert lib.bsm_rmsnorm_f32(FAKE, 4, 16, -1.0, None, FAKE, None) == 1
     assert lib.bsm_scaled_residual_f32(None, FAKE, 1.0, 1.0, 4, 16, None) == 1
-    assert lib.bsm_rmsnorm_f32(None, 0, 16, 1e-6, None, None) == 0
+    assert lib.bsm_rmsnorm_f32(None, 0, 16, 1e-6, None, None, None) == 0
+
+
+def test_residual_step_weights_match_the_oracle(lib):
+    """The library's residual weights are the oracle's, bit for bit (host computation, no device work)."""
+    from oracle import moe as OM
+
+    a, b = ctypes.c_float(), ctypes.c_float()
+    for k in range(2, 200):
+        assert lib.bsm_residual_step_weights(k, ctypes.byref(a), ctypes.byref(b)) == 0
+        ra, rb = OM.residual_weights(k)
+        assert np.float32(a.value).view(np.uint32) == ra.view(np.uint32)
+        assert np.float32(b.value).view(np.uint32) == rb.view(np.uint32)
+    assert lib.bsm_residual_step_weights(1, ctypes.byref(a), ctypes.byref(b)) == 1
+    assert lib.bsm_residual_step_weights(3, None, ctypes.byref(b)) == 1
+
+
+def test_ceiling_validation(lib):
+    assert lib.bsm_ceiling_hbm_read(FAKE, 24, FAKE, 8, None) == 1        # bytes % 16
+    assert lib.bsm_ceiling_hbm_read(None, 4096, FAKE, 8, None) == 1
+    assert lib.bsm_ceiling_mfma_f16(2, 10, FAKE, 8, None) == 1           # shape
+    assert lib.bsm_ceiling_mfma_f16(0, 0, FAKE, 8, None) == 1            # iters
 
 
 def test_weight_only_moe_validation(lib):

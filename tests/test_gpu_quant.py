@@ -6,6 +6,8 @@ import torch
 
 import workloads as W
 from oracle import quant as Q
+from oracle import quant_c as QC
+from tests.fullsize import bf16_bits
 from tests.helpers import np_, to_dev_bf16, to_dev_f32
 
 pytestmark = pytest.mark.gpu
@@ -62,22 +64,36 @@ def test_nvfp4_dequantize_bitexact(gpu_lib):
     assert np.array_equal(np_(d).view(np.uint32), ref.view(np.uint32))
 
 
-def test_nvfp4_standalone_workload_full_size_sampled(gpu_lib):
-    """32768 x 5120 Student-t tensor with outlier rows: full GPU run, oracle on sampled rows."""
+def test_nvfp4_standalone_workload_full_size(gpu_lib):
+    """32768 x 5120 Student-t tensor with outlier rows: every code, block scale and dequantized value
+    (float32 and BF16 outputs) bit-exact against the oracle's own quantization of the same bf16 tensor."""
     x = W.quant_tensor_device()
     codes, scales, gs = gpu_lib.nvfp4_quantize(x)
-    d = gpu_lib.nvfp4_dequantize(codes, scales, gs)
+    d32 = gpu_lib.nvfp4_dequantize(codes, scales, gs)
     torch.cuda.synchronize()
-    amax = float(x.abs().max().float())
-    og = np.float32(np.float32(amax) / np.float32(2688))
-    assert np_(gs)[0] == og
-    rows = np.random.default_rng(8).choice(x.shape[0], 96, replace=False)
-    xs = x[torch.from_numpy(rows).cuda()].float().cpu().numpy()
-    oc, os_, _ = Q.nvfp4_quantize(xs, global_scale=og)
-    assert np.array_equal(np_(codes)[rows], oc)
-    assert np.array_equal(np_(scales)[rows], os_)
+    oc, os_, og = QC.nvfp4_quantize(bf16_bits(x))
+    assert np_(gs)[0].view(np.uint32) == og.view(np.uint32)
+    assert np.array_equal(np_(codes), oc)
+    assert np.array_equal(np_(scales), os_)
     ref = Q.nvfp4_dequantize_f32(oc, os_, og)
-    assert np.array_equal(np_(d)[rows].view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(np_(d32).view(np.uint32), ref.view(np.uint32))
+    del d32, ref
+    rows = slice(0, 4096)
+    d16 = gpu_lib.nvfp4_dequantize(codes[rows], scales[rows], gs, out_dtype=torch.bfloat16)
+    ref16 = Q.nvfp4_dequantize_bf16(oc[rows], os_[rows], og)
+    assert np.array_equal(np_(d16.float()).view(np.uint32), ref16.view(np.uint32))
+
+
+def test_nvfp4_dequantize_bf16_rounds_once(gpu_lib):
+    """BF16 output rounds the exact product q * s_b * S_g once: a global scale with a full 24-bit
+    significand makes most products inexact in BF16, and some land on or near BF16 midpoints."""
+    x = W.quant_tensor_host((256, 512), seed=9)
+    codes, scales, gs = gpu_lib.nvfp4_quantize(to_dev_bf16(x))
+    for g in (np_(gs)[0], np.float32(1.0 + 2.0 ** -9 + 2.0 ** -23), np.float32(3.0e-39)):
+        gt = torch.tensor([g], dtype=torch.float32, device="cuda")
+        d16 = gpu_lib.nvfp4_dequantize(codes, scales, gt, out_dtype=torch.bfloat16)
+        ref = Q.nvfp4_dequantize_bf16(np_(codes), np_(scales), g)
+        assert np.array_equal(np_(d16.float()).view(np.uint32), ref.view(np.uint32))
 
 
 @pytest.mark.parametrize("R,C,bf16", [(1, 4, True), (64, 5120, True), (33, 2560, False), (7, 100, False)])

@@ -40,6 +40,18 @@ def _tiny_layers(gpu_lib, fmt, n_layers, seed_base=10):
     return layers_gpu, layers_orc
 
 
+def test_rmsnorm_with_gain(gpu_lib):
+    """RMSNorm with a gain vector: fl32(fl32(x * r) * gamma), within 1 ulp of the oracle (r exactly rounded
+    on both sides; the gain product is one binary32 multiply)."""
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal((37, 5120)) * 3).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(5120)).astype(np.float32)
+    y = np_(gpu_lib.rmsnorm(to_dev_f32(x), 1e-6, gamma=to_dev_f32(g)))
+    assert _ulps(y, OM.rmsnorm_f32(x, 1e-6, gamma=g)).max() <= 1
+    y1 = np_(gpu_lib.rmsnorm(to_dev_f32(x), 1e-6))
+    assert _ulps(y1, OM.rmsnorm_f32(x, 1e-6)).max() <= 1
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
 def test_stack_tiny_teacher_forced(gpu_lib, fmt):
     cfg = W.TINY

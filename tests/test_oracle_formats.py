@@ -151,3 +151,28 @@ def test_bf16_round_matches_torch_and_ties_to_even():
     # tie cases by hand: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> the even 1.0
     assert F.bf16_round(np.float32([1 + 2.0 ** -8]))[0] == 1.0
     assert F.bf16_round(np.float32([1 + 3 * 2.0 ** -8]))[0] == np.float32(1 + 2 * 2.0 ** -7)
+
+
+def test_bf16_round_exact_is_the_nearest_bf16():
+    """Brute force: every BF16 value between 1/4 and 4 and near the subnormal floor, each exact midpoint
+    between neighbours (ties to the even significand), and points just off the midpoints."""
+    ranges = [np.arange(0x3E80, 0x4081), np.arange(0x0000, 0x0100)]  # [1/4, 4] and the subnormal floor
+    tables = [(r.astype(np.uint32) << 16).view(np.float32).astype(np.float64) for r in ranges]
+    vals = np.concatenate(tables)
+    mids = np.concatenate([(t[:-1] + t[1:]) / 2 for t in tables])  # midpoints inside each range only
+    off = np.concatenate([mids * (1 + 2.0 ** -40), mids * (1 - 2.0 ** -40)])
+    off = off[off > 0]
+    for v in (vals, mids, off, -mids):
+        got = F.bf16_round_exact(v)
+        # nearest table entry by brute force, ties to the even bit pattern
+        a = np.abs(v)[:, None]
+        d = np.abs(a - vals[None, :])
+        best = d.min(axis=1, keepdims=True)
+        cand = np.where(d == best, vals[None, :], np.nan)
+        lo, hi = np.nanmin(cand, axis=1), np.nanmax(cand, axis=1)
+        even_lo = ((lo.astype(np.float32).view(np.uint32) >> 16) & 1) == 0
+        want = np.where(lo == hi, lo, np.where(even_lo, lo, hi)) * np.sign(v)
+        assert np.array_equal(got, want)
+    # on float32-exact inputs it is the pinned binary32 -> BF16 rounding
+    x = np.random.default_rng(5).standard_normal(100000).astype(np.float32)
+    assert np.array_equal(F.bf16_round_exact(x.astype(np.float64)), F.bf16_round(x).astype(np.float64))
