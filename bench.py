@@ -207,6 +207,47 @@ def summarize_pmc(fetch_csv, write_csv, command, bench_json=None):
     print(json.dumps(res, indent=1))
 
 
+def summarize_counters(title, command, kernel_filter, csvs):
+    """Per-kernel averages of rocprofv3 --pmc runs (several counters per run), for the library kernels
+    whose label contains ``kernel_filter``, with the derived ratios used in the design notes."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(list)
+    for path in csvs:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = _kernel_label(r["Kernel_Name"])
+                if not k or kernel_filter not in k:
+                    continue
+                vals[(k, r["Counter_Name"])].append(float(r["Counter_Value"]))
+    kernels = sorted({k for k, _ in vals})
+    print(f"# {title}")
+    print(f"# command (one run per counter set): {command}")
+    print("# rocprofv3 --pmc counter collection, averages per dispatch (counters summed over the chip)")
+    for k in kernels:
+        c = {n: float(np.mean(v)) for (kk, n), v in vals.items() if kk == k}
+        n_disp = max(len(v) for (kk, _), v in vals.items() if kk == k)
+        print(f"\n## {k}  ({n_disp} dispatches)")
+        for n in sorted(c):
+            print(f"{n:32s} {c[n]:20.6g}")
+        d = {}
+        if "SQ_INSTS_VALU" in c and "SQ_INSTS_MFMA" in c and c["SQ_INSTS_MFMA"]:
+            d["VALU instructions per MFMA"] = c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]
+        if "SQ_INSTS_LDS" in c and "SQ_INSTS_MFMA" in c and c["SQ_INSTS_MFMA"]:
+            d["LDS instructions per MFMA"] = c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"]
+        if "SQ_WAVE_CYCLES" in c and c["SQ_WAVE_CYCLES"]:
+            for n in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU",
+                      "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_ANY"):
+                if n in c:
+                    d[f"{n} / SQ_WAVE_CYCLES"] = c[n] / c["SQ_WAVE_CYCLES"]
+        if "SQ_LDS_BANK_CONFLICT" in c and "SQ_ACTIVE_INST_LDS" in c and c["SQ_ACTIVE_INST_LDS"]:
+            d["LDS bank-conflict cycles / LDS active cycles"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]
+        if d:
+            print("# derived")
+            for n, v in d.items():
+                print(f"{n:48s} {v:10.4f}")
+
+
 def measured_traffic():
     """HBM bytes per gate/up launch from the committed counter runs, if they match this kernel source."""
     try:
@@ -655,6 +696,9 @@ def main():
     ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
                     help="FETCH_CSV WRITE_CSV COMMAND [BENCH_JSON]: write the gate/up GEMM HBM traffic from two "
                          "rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="TITLE COMMAND KERNEL_FILTER CSV [CSV ...]: print per-kernel averages of rocprofv3 --pmc "
+                         "counter CSVs and exit")
     ap.add_argument("--summarize-trace", nargs="+", metavar="ARG",
                     help="KERNEL_TRACE_CSV TITLE COMMAND [NOTE ...]: print the kernel summary of a rocprofv3 "
                          "--kernel-trace run and exit")
@@ -663,6 +707,12 @@ def main():
         if len(args.summarize_pmc) not in (3, 4):
             ap.error("--summarize-pmc needs FETCH_CSV WRITE_CSV COMMAND [BENCH_JSON]")
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_counters:
+        if len(args.summarize_counters) < 4:
+            ap.error("--summarize-counters needs TITLE COMMAND KERNEL_FILTER CSV [CSV ...]")
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.summarize_counters[2],
+                           args.summarize_counters[3:])
         return
     if args.summarize_trace:
         if len(args.summarize_trace) < 3:

@@ -106,7 +106,13 @@ __device__ inline float wave_max_f(float v) {
   return v;
 }
 
-__device__ inline float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
+// SwiGLU product h = silu(g) * u = g * u / (1 + e^-g) in binary32: e^-g as 2^(-g log2 e) on the
+// hardware exp2, and the hardware reciprocal (1 ulp each; the product is within a few ulp of the
+// exactly rounded value).  Large negative g gives 2^x = inf, a reciprocal of 0 and h = +-0.
+__device__ inline float silu_mul(float g, float u) {
+  const float t = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return (g * u) * __builtin_amdgcn_rcpf(1.0f + t);
+}
 
 // max |h| of a 256-thread workgroup into the global amax word with one atomic (order independent).
 // One atomic per wave had cost the decode gate/up GEMM about 16 us of contention on that word.
@@ -1378,43 +1384,56 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   }
 #undef BSM_BIG_BROW
 
+  // Epilogue.  Accumulator register 4q + j of m tile mt is row mt * 32 + 8q + 4 (lane / 32) + j and
+  // column lane % 32 of the wave's 32-column tile: one base address per lane, and every other element
+  // sits a wave-uniform number of rows further.  Full tiles skip the row checks.
   float hmax = 0.0f;
+  const int64_t ld = G1 ? I : H;
+  float* const obase = out + (int64_t)(row0 + 4 * lh) * ld + (G1 ? c0 + 32 * wave + l32 : c0 + 64 * wave + l32);
+  const bool full = nrows == kGBM;
+  float sg = 0.0f, su = 0.0f, sy = 0.0f;  // NVFP4: the product of the global scales
+  if constexpr (NV) {
+    const float ag = A16 ? 1.0f : a_gs[0];  // weight-only: BF16 activations carry no scale
+    if (G1) {
+      sg = ag * wgs[2 * e];
+      su = ag * wgs[2 * e + 1];
+    } else {
+      sy = ag * wgs[e];
+    }
+  }
+  const float* wsf = reinterpret_cast<const float*>(wsc);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int ro = mt * 32 + 8 * q + 4 * lh + j;
-        if (ro >= nrows) continue;
+        const int rr = mt * 32 + 8 * q + j;  // row offset from this lane's base row
+        if (!full && rr + 4 * lh >= nrows) continue;
         const int r = 4 * q + j;
+        float* const p = obase + (int64_t)rr * ld;
         if (G1) {
-          float* hr = out + (int64_t)(row0 + ro) * I;
-          const int64_t col = c0 + 32 * wave + l32;
-          float sg, su;
+          float g = acc[mt][0][r], u = acc[mt][1][r];
           if (NV) {
-            const float ag = A16 ? 1.0f : a_gs[0];
-            sg = ag * wgs[2 * e];
-            su = ag * wgs[2 * e + 1];
+            g *= sg;
+            u *= su;
           } else {
-            const float sx = a_rs[row_pair[row0 + ro] / topk];
-            const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * 2 * I;
-            sg = sx * ws[col];
-            su = sx * ws[I + col];
+            const int64_t col = c0 + 32 * wave + l32;
+            const float sx = a_rs[row_pair[row0 + rr + 4 * lh] / topk];
+            g *= sx * wsf[(int64_t)e * 2 * I + col];
+            u *= sx * wsf[(int64_t)e * 2 * I + I + col];
           }
-          const float h = silu_mul(acc[mt][0][r] * sg, acc[mt][1][r] * su);
-          hr[col] = h;
+          const float h = silu_mul(g, u);
+          p[0] = h;
           hmax = fmaxf(hmax, fabsf(h));
         } else {
-          float* yr = out + (int64_t)(row0 + ro) * H;
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const int64_t col = c0 + 64 * wave + 32 * t + l32;
             if (NV) {
-              yr[col] = acc[mt][t][r] * ((A16 ? 1.0f : a_gs[0]) * wgs[e]);
+              p[32 * t] = acc[mt][t][r] * sy;
             } else {
-              const float* ws = reinterpret_cast<const float*>(wsc) + (int64_t)e * H;
-              yr[col] = acc[mt][t][r] * a_rs[row0 + ro] * ws[col];
+              const int64_t col = c0 + 64 * wave + 32 * t + l32;
+              p[32 * t] = acc[mt][t][r] * a_rs[row0 + rr + 4 * lh] * wsf[(int64_t)e * H + col];
             }
           }
         }
