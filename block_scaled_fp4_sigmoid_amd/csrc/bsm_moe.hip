@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void k_perm_masks(const int32_t* __restrict__ 
   for (int64_t i = threadIdx.x; i < tn * topk; i += 256) {
     const int64_t t = t0 + i / topk;
     const int e = ids[t0 * topk + i];
-    atomicOr(&lm[e], 1ull << (t - t0));
+    if ((uint32_t)e < (uint32_t)E) atomicOr(&lm[e], 1ull << (t - t0));  // ids outside [0, E) are dropped
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) {
@@ -232,6 +232,10 @@ __global__ __launch_bounds__(256) void k_perm_rows(const int32_t* __restrict__ i
   if (p >= P) return;
   const int64_t t = p / topk;
   const int e = ids[p];
+  if ((uint32_t)e >= (uint32_t)E) {  // a dropped pair: no row, nothing combined
+    pair_row[p] = -1;
+    return;
+  }
   const int64_t c = t / kChunk;
   const uint32_t bit = (uint32_t)(t % kChunk);
   const uint64_t below = bit ? (masks[e * nc + c] & ((1ull << bit) - 1ull)) : 0ull;
@@ -321,8 +325,12 @@ __global__ __launch_bounds__(256) void k_decode_act(const uint8_t* __restrict__ 
 // order.  NVFP4 block scales: lane g holds the whole scale span of its row for
 // super-step 4q+g (the 4 lanes of a row together hold one cache line per 4
 // super-steps); at super-step 4q+i every lane fetches its scale bytes from
-// lane group i with ds_bpermute, and group i then loads its span of
-// super-step 4q+4+i.  The next super-step's codes are loaded while the
+// lane group i with ds_bpermute.  At super-step 4q+3, when all four spans are
+// used, the four groups load the next line's spans together, so a row's
+// line is requested once: loaded one span at a time, a line was evicted from
+// L2 between the requests (each XCD streams about 3.4 MB of weights per
+// super-step through its 4 MB L2) and fetched again, 8.5 % more HBM reads at
+// decode.  The next super-step's codes are loaded while the
 // current one is multiplied (two register sets).
 // ---------------------------------------------------------------------------
 
@@ -501,13 +509,13 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny(const _Float
   {                                                                                                       \
     const bool more = (ST) + 1 < nsteps;                                                                  \
     if constexpr (NV) {                                                                                   \
-      /* every lane takes its scale bytes of this super-step from lane group gi, which then */           \
-      /* loads its span of super-step ST + 4 (needed four super-steps later) */                          \
+      /* every lane takes its scale bytes of this super-step from lane group gi; after the */            \
+      /* fourth, the four groups load the next line of scale spans together */                           \
       const int gi = (ST) & 3;                                                                            \
       _Pragma("unroll") for (int j = 0; j < NT; ++j) s_fetch<KB>(sc[j], (m + 16 * gi) * 4, ghi, sdw[j]);  \
-      if (g == gi && (ST) + 4 < nsteps) {                                                                 \
+      if (gi == 3 && (ST) + 1 < nsteps) { /* the next line: span of super-step ST + 1 + g per group */    \
         _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                   \
-          s_load<KB>(srow[j] + (int64_t)((ST) + 4 - g) * sstep, true, sc[j]);                             \
+          s_load<KB>(srow[j] + (int64_t)((ST) + 1) * sstep, (ST) + 1 + g < nsteps, sc[j]);                \
       }                                                                                                   \
     }                                                                                                     \
     if (more) {                                                                                           \
@@ -660,16 +668,16 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
 #pragma unroll
     for (int j = 0; j < NT; ++j) s_load<KB>(srow[j], g < nsteps, sc[j]);
   }
-  // one super-step: NVFP4 scale bytes from lane group (ST & 3) (which reloads its span for ST + 4), the
-  // codes of super-step ST + DEPTH into BN, the multiplies from the staged rows
+  // one super-step: NVFP4 scale bytes from lane group (ST & 3) (after the fourth, every group loads its
+  // span of the next line), the codes of super-step ST + DEPTH into BN, the multiplies from the staged rows
 #define BSM_SKR_STEP(ST, BC, BN)                                                                       \
   {                                                                                                    \
     if constexpr (NV) {                                                                                \
       const int gi = (ST) & 3;                                                                         \
       _Pragma("unroll") for (int j = 0; j < NT; ++j) s_fetch<KB>(sc[j], (m + 16 * gi) * 4, ghi, sdw[j]); \
-      if (g == gi && (ST) + 4 < nsteps) {                                                              \
+      if (gi == 3 && (ST) + 1 < nsteps) { /* the next line: span of super-step ST + 1 + g per group */ \
         _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                \
-          s_load<KB>(srow[j] + (int64_t)((ST) + 4 - g) * sstep, true, sc[j]);                          \
+          s_load<KB>(srow[j] + (int64_t)((ST) + 1) * sstep, (ST) + 1 + g < nsteps, sc[j]);             \
       }                                                                                                \
     }                                                                                                  \
     if ((ST) + DEPTH < nsteps) {                                                                       \
@@ -1459,24 +1467,26 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
     // all row indices, then all y loads of up to 8 slots in flight; the sum stays in slot order
     int row[8];
     double w[8];
+    bool in[8];  // slot present and its pair not dropped (expert id outside [0, E))
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const bool in = j0 + q < topk;
-      row[q] = in ? pair_row[t * topk + j0 + q] : 0;
-      w[q] = in ? (double)wts[t * topk + j0 + q] : 0.0;
+      const bool slot = j0 + q < topk;
+      row[q] = slot ? pair_row[t * topk + j0 + q] : -1;
+      in[q] = row[q] >= 0;
+      w[q] = in[q] ? (double)wts[t * topk + j0 + q] : 0.0;
     }
     // y is read once: non-temporal loads keep it from displacing cached data (0.30 -> 0.25 ms at 8192 tokens)
     float4 v[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const f32x4_t z = (j0 + q < topk)
+      const f32x4_t z = in[q]
                             ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + (int64_t)row[q] * H + c4 * 4))
                             : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       v[q] = make_float4(z.x, z.y, z.z, z.w);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      if (j0 + q < topk) {
+      if (in[q]) {
         acc[0] += w[q] * (double)v[q].x;
         acc[1] += w[q] * (double)v[q].y;
         acc[2] += w[q] * (double)v[q].z;
@@ -1509,7 +1519,10 @@ __global__ __launch_bounds__(1024) void k_perm_small(const int32_t* __restrict__
   lm[e] = 0ull;
   __syncthreads();
   const int64_t P = T * topk;
-  for (int64_t p = threadIdx.x; p < P; p += 1024) atomicOr(&lm[ids[p]], 1ull << (p / topk));
+  for (int64_t p = threadIdx.x; p < P; p += 1024) {
+    const int ex = ids[p];
+    if ((uint32_t)ex < (uint32_t)E) atomicOr(&lm[ex], 1ull << (p / topk));  // ids outside [0, E) are dropped
+  }
   __syncthreads();
   const int total = (e < E) ? __popcll(lm[e]) : 0;
   if (e < E) counts[e] = total;
@@ -1552,6 +1565,10 @@ __global__ __launch_bounds__(1024) void k_perm_small(const int32_t* __restrict__
   __syncthreads();  // s_cnt holds inclusive prefix counts
   for (int64_t p = threadIdx.x; p < P; p += 1024) {
     const int ex = ids[p];
+    if ((uint32_t)ex >= (uint32_t)E) {
+      pair_row[p] = -1;
+      continue;
+    }
     const uint32_t bit = (uint32_t)(p / topk);
     const uint64_t below = bit ? (lm[ex] & ((1ull << bit) - 1ull)) : 0ull;
     const int pos = s_cnt[ex] - __popcll(lm[ex]) + __popcll(below);

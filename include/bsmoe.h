@@ -198,7 +198,10 @@ int bsm_route_diagnostics(const void* ws, int64_t T, int64_t H, int64_t E, int32
  *   y    = decoded h times down of e
  *   out[t] = combine_scale * sum_j topk_weights[t, j] * y(t, j)   (float [T, H])
  * Requirements: H % 256 == 0, I % 128 == 0,
- * topk <= 32, ids in [0, E) and distinct within a token.  h_global_scale: NVFP4 STATIC -> read; DYNAMIC ->
+ * topk <= 32, ids in [0, E) and distinct within a token (a pair whose id lies
+ * outside [0, E) is dropped: it gets no row and adds nothing to out, so no
+ * out-of-range access follows from it; the pair_row of a dropped pair reads -1;
+ * repeated ids within a token give unspecified values).  h_global_scale: NVFP4 STATIC -> read; DYNAMIC ->
  * written when non-NULL.  The layout of the workspace (stage buffers) is
  * reported by bsm_moe_workspace_layout for inspection.
  * ------------------------------------------------------------------------ */

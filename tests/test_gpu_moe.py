@@ -178,3 +178,32 @@ def _many_tokens(gpu_lib, cfg, fmt, T):
     e2e = rel_l2(np_(out), ref["out"])
     print(f"{cfg.name} {fmt} T={T}: max rows {counts.max()}, end-to-end rel L2 {e2e:.3e}")
     assert e2e <= 1e-3
+
+
+@pytest.mark.parametrize("T", [64, 300])
+def test_moe_out_of_range_ids_are_dropped(gpu_lib, T):
+    """Expert ids outside [0, E) are dropped, through the one-chunk (T = 64) and the chunked (T = 300)
+    permutation: no row, pair_row -1, nothing combined.  With a static h global scale the other rows do not
+    depend on which pairs exist, so the output equals the run where those pairs go to a valid expert with
+    weight 0, bit for bit."""
+    cfg = W.TINY
+    _, w13, w2 = host_masters(cfg)
+    gw = gpu_lib.quantize_expert_weights(w13, w2, "nvfp4")
+    xt = to_dev_bf16(W.activations(cfg, T=T))
+    ids, wts = gpu_lib.route(xt, to_dev_f32(W.router_weights(cfg)), cfg.n_group, cfg.topk_group, cfg.topk)
+    xq = gpu_lib.quantize_activations(xt, "nvfp4")
+    bad = ids.clone()
+    bad[3, 0] = -1
+    bad[T - 1, 1] = cfg.E + 5
+    bad[T // 2, 0] = 1 << 30
+    drop = bad != ids
+    fixed_w = wts.clone()
+    fixed_w[drop] = 0.0
+    hs = torch.tensor([0.002], dtype=torch.float32, device="cuda")
+    out_bad, ws = gpu_lib.moe_expert_mlp(gw, xq, bad, wts, h_global_scale=hs, return_workspace=True)
+    out_ref = gpu_lib.moe_expert_mlp(gw, xq, ids, fixed_w, h_global_scale=hs)
+    torch.cuda.synchronize()
+    st = moe_stages(gpu_lib, "nvfp4", cfg, T, ws, T * cfg.topk)
+    assert (st["pair_row"][np_(drop).ravel()] == -1).all()
+    assert st["counts"].sum() == T * cfg.topk - int(drop.sum())
+    assert torch.equal(out_bad, out_ref)
