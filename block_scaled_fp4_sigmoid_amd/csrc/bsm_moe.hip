@@ -2,8 +2,9 @@
 // GEMM with the SwiGLU product, re-quantization of h, grouped down GEMM and
 // the weighted combine.
 //
-// Method: each expert is a SwiGLU MLP; expert outputs are combined with the
-// normalized router weights and scaled by 2.5 ("Reflection releases Beam"
+// Method: the experts are SwiGLU MLPs; the layer output adds up the chosen
+// experts' outputs, each weighted by its router score over the sum of the
+// chosen scores, and multiplies the total by 2.5 ("Reflection releases Beam"
 // news page, "Mixture-of-Experts details"); the SwiGLU product is computed in
 // FP32 ("Residual stream and numerical decisions").  NVFP4 W4A4: both GEMM
 // operands are E2M1 with E4M3 per-16 scales and a per-tensor global scale

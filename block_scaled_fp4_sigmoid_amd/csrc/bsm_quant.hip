@@ -3,8 +3,8 @@
 // NVFP4 ("NVFP4 quantization" page, "Quantization scheme"): E2M1 elements,
 // one E4M3 scale per 16 consecutive values, one global scale per tensor.
 // FP8_DYNAMIC ("FP8 quantization" page, "Quantization scheme" and
-// "Quantization method"): one scale per row, values divided by the scale and
-// rounded to the nearest E4M3 value.
+// "Quantization method"): one scale per row; each quotient value / scale
+// becomes the closest E4M3 value.
 //
 // Arithmetic per tensor (binary32, round to nearest even, in this order):
 //   S_g = amax / 2688 ; s_b = E4M3(a_b / (6*S_g)) ; q = E2M1(x / (s_b*S_g))

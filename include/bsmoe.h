@@ -6,30 +6,32 @@
  *
  * Method sources (cited per function below):
  *   [NVFP4]  "NVFP4 quantization" page, section "Quantization scheme":
- *            W4A4; elements are 4-bit E2M1; each block of 16 values shares an
- *            FP8 E4M3 scale; each tensor has one more global scale; only the
+ *            W4A4; values are held as 4-bit E2M1 codes, every run of 16
+ *            values along a row carries its own FP8 E4M3 scale, and the
+ *            tensor as a whole one FP32 scale on top; only the
  *            routed experts' gate/up/down projections are quantized, router
  *            input and weights stay unquantized.
  *   [FP8]    "FP8 quantization" page, sections "Quantization scheme" and
- *            "Quantization method": FP8_DYNAMIC (W8A8), E4M3 weights with a
- *            fixed per-output-channel scale, activation scales computed per
- *            token at run time; values are divided by their scale and
- *            rounded to the nearest FP8 value.
+ *            "Quantization method": FP8_DYNAMIC (W8A8), E4M3 codes; a weight
+ *            row (output channel) has one fixed scale, an activation row
+ *            (token) one scale found at run time; each quotient
+ *            value / scale becomes the closest E4M3 value (RTN).
  *   [MOE]    "Reflection releases Beam" news page, section
  *            "Mixture-of-Experts details": sigmoid scores over 256 experts,
  *            8 groups of 32, keep the 4 groups with the largest sum of their
  *            two best scores, top 8 experts within them, SwiGLU experts with
- *            intermediate 2560, outputs combined with normalized router
- *            weights and scaled by 2.5.
+ *            intermediate 2560; the chosen experts' outputs are weighted by
+ *            their scores renormalized to sum to one, added, and the total
+ *            multiplied by 2.5.
  *   [WO]     "Beam-1.0 auf 4x NVIDIA RTX PRO 6000 Blackwell Server Edition"
  *            page, section "NVFP4 auf Blackwell gegen FP8 auf Hopper" (and
  *            the H100 line of the [NVFP4] page's "Hardware compatibility and
  *            serving"): without FP4 arithmetic the NVFP4 experts run
  *            weight-only, FP4 weights with BF16 activations (W4A16).
  *   [NUM]    same page as [MOE], section "Residual stream and numerical decisions":
- *            router, SwiGLU product and norms in FP32; residual step k adds
- *            the sublayer output with weight 1/sqrt(k) and keeps the stream
- *            with weight sqrt((k-1)/k).
+ *            router, SwiGLU product and norms in FP32; the embedding is
+ *            step 1, and step k scales the stream by sqrt((k-1)/k) before
+ *            adding the sublayer output scaled by 1/sqrt(k).
  *
  * Conventions (all functions):
  *   - Pointers named x, w*, codes, scales, out, ws ... are DEVICE pointers
@@ -109,9 +111,9 @@ int bsm_nvfp4_quantize(const void* x, int x_dtype, int64_t B, int64_t R, int64_t
 
 /* ------------------------------------------------------------------------
  * Local-Hessian block-scale search (offline weight quantizer) [NVFP4]
- * ("NVFP4 quantization" page, "Quantization method": per block, candidate
- * scales are searched and the one minimizing the Hessian-weighted error
- * dW^T H dW kept, H computed from the tokens routed to the expert).
+ * ("NVFP4 quantization" page, "Quantization method": each block's scale is
+ * the candidate with the smallest error dW^T H dW, where H comes from the
+ * inputs of the tokens that the router sends to that expert).
  *
  * bsm_local_hessian_blocks: x [N, C] (the inputs the weight multiplies, bf16
  *   or f32) -> hess_blocks double [C/16][16][16], block b = the 16 x 16
@@ -294,8 +296,9 @@ int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w /* host */, const void* x,
 /* ------------------------------------------------------------------------
  * Dense FP8_DYNAMIC (W8A8) linear projection [FP8]
  *
- * The FP8 checkpoint also quantizes the attention query, key, value, output
- * and gate projections and the dense MLPs ([FP8] "Quantization scheme").
+ * In the FP8 checkpoint the projections of attention (q, k, v, o and the
+ * head gate) and of the dense MLPs are FP8 as well ([FP8] "Quantization
+ * scheme").
  *   x_codes uint8 [T, K] E4M3, x_scales float [T]   (bsm_fp8_quantize of x)
  *   w_codes uint8 [N, K] E4M3, w_scales float [N]   (bsm_fp8_quantize of W)
  *   out[t, n] = x_scales[t] * w_scales[n] * sum_k q_x[t,k] q_w[n,k]

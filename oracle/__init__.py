@@ -8,19 +8,20 @@ package or its C library.
 
 Every function follows the method as the source pages state it:
 
-* "NVFP4 quantization" page, section "Quantization scheme": weights and input
-  activations are 4-bit E2M1 values, each block of 16 values shares one FP8
-  E4M3 scale, and each tensor carries one more global scale.
+* "NVFP4 quantization" page, section "Quantization scheme": expert weights
+  and expert inputs are held as 4-bit E2M1 codes; every run of 16 values has
+  its own FP8 E4M3 scale, and the tensor one FP32 scale on top of those.
 * "FP8 quantization" page, sections "Quantization scheme" and "Quantization
-  method": E4M3 weights with a fixed per-output-channel scale, activation
-  scales computed per token at run time, weights divided by their scales and
-  rounded to the nearest representable FP8 value.
+  method": E4M3 codes; a weight row (output channel) has one fixed scale, an
+  activation row (token) one scale found at run time; a value is divided by
+  its scale and the quotient becomes the closest E4M3 value (RTN).
 * "Reflection releases Beam" news page, section "Mixture-of-Experts details":
-  sigmoid scores over 256 experts, 8 groups of 32, the 4 best groups by the sum
-  of each group's two largest scores, top 8 experts inside them, outputs
-  combined with normalized router weights and scaled by 2.5; section "Residual
-  stream and numerical decisions": router, SwiGLU product and norms in FP32,
-  residual weights 1/sqrt(k) and sqrt((k-1)/k).
+  each of the 256 experts gets a sigmoid score; of the 8 groups of 32 experts
+  the 4 whose two highest scores add up to the most survive; the 8
+  highest-scoring experts of those are chosen, and their outputs are mixed
+  with the chosen scores renormalized to sum to one, the total times 2.5;
+  section "Residual stream and numerical decisions": router, SwiGLU product
+  and norms in FP32, residual weights 1/sqrt(k) and sqrt((k-1)/k).
 * "FP8 quantization" page, "Quantization scheme": the attention projections
   and the dense MLPs are FP8_DYNAMIC too (``linear``).
 * "NVFP4 quantization" page, "Quantization method": the Local Hessian

@@ -6,7 +6,7 @@ Sources:
 * "NVFP4 quantization" page, "Quantization scheme": elements are 4-bit E2M1,
   block scales are FP8 E4M3.
 * "FP8 quantization" page, "Quantization scheme" / "Quantization method": E4M3
-  elements, values rounded to the nearest representable FP8 value.
+  elements; a scaled value becomes the closest E4M3 value.
 
 The pages name the formats but print neither value grid.  The grids below are
 the formats' own definitions:

@@ -3,11 +3,10 @@
 TEST INFRASTRUCTURE ONLY -- part of the CPU oracle; never used by the product path.
 
 Source: "NVFP4 quantization" page, "Quantization method": post-training
-quantization with a Local Hessian calibration -- for each block the quantizer
-searches over candidate scales and keeps the one minimizing the
-Hessian-weighted error dW^T H dW, H computed from the tokens routed to the
-expert.  "Quantization scheme": E2M1 elements, one E4M3 scale per 16 values,
-one global scale per tensor.
+quantization calibrated with a Local Hessian -- each block's scale is the
+candidate with the smallest error dW^T H dW, where H comes from the inputs of
+the tokens that the router sends to that expert.  "Quantization scheme": E2M1
+elements, one E4M3 scale per 16 values, one global scale per tensor.
 
 Readings (the page names the objective, not the search):
 * H is the Gram matrix X^T X of the inputs X [N, C] the weight multiplies

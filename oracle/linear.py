@@ -3,17 +3,16 @@
 TEST INFRASTRUCTURE ONLY -- part of the CPU oracle; never used by the product path.
 
 Sources:
-* "FP8 quantization" page, "Quantization scheme": the FP8_DYNAMIC checkpoint
-  quantizes the attention query, key, value, output and gate projections and
-  the dense MLPs' gate, up and down projections; E4M3 weights with a fixed
-  scale per output channel, activation scales computed per token at run time.
-  "Quantization method": values are divided by their scale and rounded to the
-  nearest FP8 value (RTN).
+* "FP8 quantization" page, "Quantization scheme": in the FP8_DYNAMIC
+  checkpoint the attention projections (q, k, v, o and the head gate) and the
+  three projections of each dense MLP are FP8 too; a weight row has one fixed
+  E4M3 scale, an activation row a scale found per token at run time.
+  "Quantization method": RTN, the closest E4M3 value to value / scale.
 * "Reflection releases Beam" news page, "Model architecture and attention":
-  hidden 5120, 48 query heads and 8 key-value heads (head dimension 128 from
-  "Long context handling and cache growth"), a sigmoid gate per channel of
-  every head before the output projection; "Mixture-of-Experts details": the
-  first three layers are dense SwiGLU MLPs.
+  hidden 5120, 8 KV heads and 48 query heads (128 dimensions each, from "Long
+  context handling and cache growth"), and a per-channel sigmoid gate on each
+  head's output ahead of the o projection; "Mixture-of-Experts details":
+  layers 1 to 3 use dense SwiGLU MLPs instead of experts.
 
 Readings:
 * a linear y = x W^T on FP8 operands is y[t, n] = fl32(s_x[t] s_w[n] sum_k

@@ -3,15 +3,16 @@
 TEST INFRASTRUCTURE ONLY -- part of the CPU oracle; never used by the product path.
 
 Sources:
-* "Reflection releases Beam" news page, "Mixture-of-Experts details": each
-  expert is a SwiGLU MLP (hidden 5120, intermediate 2560); expert outputs are
-  combined with the normalized router weights and scaled by 2.5.
+* "Reflection releases Beam" news page, "Mixture-of-Experts details": the
+  experts are SwiGLU MLPs (hidden 5120, intermediate 2560); the layer output
+  is the sum of the chosen experts' outputs, each weighted by its score over
+  the sum of the chosen scores, times 2.5.
   "Residual stream and numerical decisions": the SwiGLU product and the norms
-  run in FP32; a sublayer output at step k is added with weight 1/sqrt(k) and
-  the stream kept with weight sqrt((k-1)/k), the embedding being step 1.
+  run in FP32; the embedding counts as step 1, and step k scales the stream by
+  sqrt((k-1)/k) before adding the sublayer output scaled by 1/sqrt(k).
 * "NVFP4 quantization" page, "Quantization scheme": W4A4 -- the expert
-  weights and the expert inputs are NVFP4; only the routed experts' gate, up
-  and down projections are quantized.
+  weights and the expert inputs are NVFP4; of the whole model, just the gate,
+  up and down matrices of the routed experts are NVFP4.
 * "FP8 quantization" page, "Quantization scheme": W8A8 with per-output-channel
   weight scales and per-token activation scales.
 * "Beam-1.0 auf 4x NVIDIA RTX PRO 6000 Blackwell Server Edition" page,

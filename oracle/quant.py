@@ -6,7 +6,7 @@ NVFP4 ("NVFP4 quantization" page, "Quantization scheme"): 4-bit E2M1 elements,
 one FP8 E4M3 scale per block of 16 values, one more global scale per tensor.
 FP8_DYNAMIC ("FP8 quantization" page, "Quantization scheme" and "Quantization
 method"): E4M3 elements, one scale per row (output channel for weights, token
-for activations), values divided by their scale and rounded to the nearest FP8
+for activations); each quotient value / scale becomes the closest E4M3
 value.
 
 Readings taken where the pages are silent (each one is a choice, listed with

@@ -13,8 +13,8 @@
  * Sources: "NVFP4 quantization" page, "Quantization scheme" (E2M1 elements,
  * one E4M3 scale per block of 16 values, one more global scale per tensor);
  * "FP8 quantization" page, "Quantization scheme" and "Quantization method"
- * (E4M3 values, one scale per row, values divided by their scale and rounded
- * to the nearest FP8 value).
+ * (E4M3 values, one scale per row; each quotient value / scale becomes the
+ * closest E4M3 value).
  *
  * Readings (the same as oracle/quant.py):
  *   S_g = fl32(amax / 2688); s_b = E4M3(fl32(a_b / fl32(6 S_g)));

@@ -3,11 +3,11 @@
 TEST INFRASTRUCTURE ONLY -- part of the CPU oracle; never used by the product path.
 
 Source: "Reflection releases Beam" news page, "Mixture-of-Experts details":
-every expert gets a sigmoid score, experts are split into 8 groups of 32, the 4
+every expert gets a sigmoid score, the experts form 8 groups of 32 each, the 4
 groups with the largest sum of their two best scores are kept, the top 8
-experts inside the kept groups are selected, and their outputs are combined
-with normalized router weights (the x2.5 is applied at the combine, see
-moe.py).  "Residual stream and numerical decisions": the router runs in FP32.
+experts inside the kept groups are selected, and each chosen expert's weight is
+its score over the sum of the chosen scores (the x2.5 is applied at the
+combine, see moe.py).  "Residual stream and numerical decisions": the router runs in FP32.
 The "NVFP4 quantization" page, "Quantization scheme", keeps router input and
 weights unquantized.
 

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = 1e-5  # FP32 accumulation of exactly decoded E4M3 products (about sqrt(K) * 2^-24 per element)
 
-# Beam attention projections: hidden 5120, 48 query heads and 8 key-value heads of 128, a per-channel head gate
+# Beam attention projections: hidden 5120, 8 KV heads and 48 query heads of 128 dimensions, a per-channel head gate
 SHAPES = {"q": (5120, 6144), "kv": (5120, 1024), "o": (6144, 5120), "gate": (5120, 6144)}
 
 

@@ -1,8 +1,8 @@
 """Pins for the oracle's expert MLP, combine, permutation, RMSNorm and residual.
 
-Method ("Reflection releases Beam" news page): SwiGLU experts, outputs combined
-with normalized router weights and scaled by 2.5 ("Mixture-of-Experts
-details"); residual weights 1/sqrt(k) and sqrt((k-1)/k) whose squares sum to
+Method ("Reflection releases Beam" news page): SwiGLU experts whose outputs
+are mixed with the chosen scores renormalized to one, the total times 2.5
+("Mixture-of-Experts details"); residual weights 1/sqrt(k) and sqrt((k-1)/k) whose squares sum to
 one ("Residual stream and numerical decisions").
 """
 

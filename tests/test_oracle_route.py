@@ -1,8 +1,8 @@
 """Pins for the oracle's group-limited sigmoid router.
 
 Rule ("Reflection releases Beam" news page, "Mixture-of-Experts details"):
-sigmoid scores, groups, keep the best groups by the sum of each group's top-2
-scores, top-k experts inside the kept groups, normalized weights.  Checked
+sigmoid scores, groups ranked by the total of their two highest scores, the
+best groups kept, the top-k experts inside them, weights renormalized to one.  Checked
 against a pairwise-dominance brute force, the textbook all-groups case, exact
 rationals and decimal arithmetic.
 """
