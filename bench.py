@@ -177,9 +177,18 @@ def summarize_pmc(fetch_csv, write_csv, command, bench_json=None):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)
     alg = None
-    if bench_json:
+    if bench_json and os.path.exists(bench_json):
         with open(bench_json) as f:
             alg = json.loads(f.readline())["roofline"]["algorithmic_bytes_per_launch"]
+    write_traffic_text(res, alg)
+    print(json.dumps(res, indent=1))
+
+
+def write_traffic_text(res, alg=None):
+    """The text summary beside the traffic record (``alg``: the algorithmic bytes per launch, if known)."""
+    command, label = res["command"], res["kernel"].split(" ")[0]
+    f_copy, w_copy, fb, wb = res["copy_counter_fetch"], res["copy_counter_write"], res["fetch_bytes_per_launch"], \
+        res["write_bytes_per_launch"]
     lines = [
         f"# HBM traffic of the gate/up GEMM ({label}) at decode-64 NVFP4, MI355X",
         "# command (two runs, one counter each):",
@@ -189,9 +198,9 @@ def summarize_pmc(fetch_csv, write_csv, command, bench_json=None):
         "'<command>' <bench.py output line>",
         "# scaling: the same counters on a 1 GiB elementwise copy (torch.add(src, 0, out=dst), 1 GiB read + 1 GiB "
         "written)",
-        f"copy kernel FETCH_SIZE counter      {f_copy:.1f}  -> {sf:.2f} bytes per unit",
-        f"copy kernel WRITE_SIZE counter      {w_copy:.1f}  -> {sw:.2f} bytes per unit",
-        f"gate/up dispatches measured          {len(fetch[gemm])}",
+        f"copy kernel FETCH_SIZE counter      {f_copy:.1f}  -> {res['scale_fetch']:.2f} bytes per unit",
+        f"copy kernel WRITE_SIZE counter      {w_copy:.1f}  -> {res['scale_write']:.2f} bytes per unit",
+        f"gate/up dispatches measured          {res['dispatches']}",
         f"fetched bytes per launch             {fb:.4g}",
         f"written bytes per launch             {wb:.4g}",
         f"HBM traffic per launch               {fb + wb:.4g}",
@@ -204,7 +213,6 @@ def summarize_pmc(fetch_csv, write_csv, command, bench_json=None):
                  "in it.")
     with open(TRAFFIC_FILE[:-len(".json")] + ".txt", "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(json.dumps(res, indent=1))
 
 
 def summarize_counters(title, command, kernel_filter, csvs):
