@@ -287,23 +287,29 @@ __device__ inline h8v dec_fp8x8(uint32_t w0, uint32_t w1) {
 }
 
 // Activations -> FP16 [T, H]: NVFP4 q * s_b (global scale applied later), FP8 q.
+// 16 consecutive activation values as exact FP16: NVFP4 the q * s_b of 8 code bytes and the block's E4M3
+// scale byte (the global scale stays in the epilogue), FP8 the E4M3 values of 16 code bytes.
+template <bool NV>
+__device__ inline void dec_act16(const uint8_t* __restrict__ c, const uint8_t* __restrict__ s, uint4& o0, uint4& o1) {
+  if constexpr (NV) {
+    const uint2 w = *reinterpret_cast<const uint2*>(c);
+    const h2v s2 = scale_pair_hw<0>(*s);
+    o0 = __builtin_bit_cast(uint4, dec_fp4x8(w.x, s2));
+    o1 = __builtin_bit_cast(uint4, dec_fp4x8(w.y, s2));
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(c);
+    o0 = __builtin_bit_cast(uint4, dec_fp8x8(w.x, w.y));
+    o1 = __builtin_bit_cast(uint4, dec_fp8x8(w.z, w.w));
+  }
+}
+
 template <bool NV>
 __global__ __launch_bounds__(256) void k_decode_act(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                                     int64_t n_blk, _Float16* __restrict__ out) {
   const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-value block
   if (f >= n_blk) return;
   uint4 o0, o1;
-  if (NV) {
-    const uint2 c = *reinterpret_cast<const uint2*>(codes + f * 8);
-    const h2v s2 = scale_pair_hw<0>(scales[f]);
-    const h8v a = dec_fp4x8(c.x, s2), b = dec_fp4x8(c.y, s2);
-    o0 = __builtin_bit_cast(uint4, a);
-    o1 = __builtin_bit_cast(uint4, b);
-  } else {
-    const uint4 c = *reinterpret_cast<const uint4*>(codes + f * 16);
-    o0 = __builtin_bit_cast(uint4, dec_fp8x8(c.x, c.y));
-    o1 = __builtin_bit_cast(uint4, dec_fp8x8(c.z, c.w));
-  }
+  dec_act16<NV>(codes + f * (NV ? 8 : 16), NV ? scales + f : nullptr, o0, o1);
   uint4* op = reinterpret_cast<uint4*>(out + f * 16);
   op[0] = o0;
   op[1] = o1;
@@ -675,12 +681,17 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny(const _Float
 // (kc from the rows and kRowsLds bytes of LDS; the whole K when the tile has
 // few rows, as at decode), so the waves run those super-steps without a
 // barrier: a wave waiting for its weights does not hold the other three.
+// QA: the rows are staged from their codes (acodes; NVFP4 with the block
+// scales ascales) and decoded to FP16 on the way into LDS, instead of being
+// read from an FP16 copy (act): each workgroup re-reads its rows, and the
+// codes are 3.6 (NVFP4) or 2 (FP8) times fewer bytes.
 // ---------------------------------------------------------------------------
 constexpr int kRowsLds = 44 * 1024;  // LDS bytes for the staged rows (three workgroups per CU)
 
-template <bool NV, bool G1, int NT, bool A16 = false, int DEPTH = 1>
+template <bool NV, bool G1, int NT, bool A16 = false, int DEPTH = 1, bool QA = false>
 __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
-    const _Float16* __restrict__ act, const int* __restrict__ row_pair, int topk, const float* __restrict__ a_gs,
+    const _Float16* __restrict__ act, const uint8_t* __restrict__ acodes, const uint8_t* __restrict__ ascales,
+    const int* __restrict__ row_pair, int topk, const float* __restrict__ a_gs,
     const float* __restrict__ a_rs, const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc,
     const float* __restrict__ wgs, const int4* __restrict__ tiles, const int* __restrict__ ntiles, int64_t K, int64_t H,
     int64_t I, float* __restrict__ out, uint32_t* __restrict__ h_amax) {
@@ -759,12 +770,26 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
     const int c1 = c0 + kc < nsteps ? c0 + kc : nsteps;
     // stage rows x [c0 KS, c1 KS): 16-byte pieces, consecutive threads along a row
     if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
-    const int pr = (c1 - c0) * KS / 8;  // pieces per row
-    for (int q = tid; q < nrows * pr; q += 256) {
-      const int r = q / pr, p = q - r * pr;
-      const _Float16* src = (G1 ? act + (int64_t)(row_pair[row0 + r] / topk) * K : act + (int64_t)(row0 + r) * K) +
-                            (int64_t)c0 * KS + 8 * p;
-      *reinterpret_cast<uint4*>(Ar + r * rstride + 8 * p) = *reinterpret_cast<const uint4*>(src);
+    if constexpr (QA) {  // 16-value blocks, consecutive threads along a row
+      const int pb = (c1 - c0) * KS / 16;  // blocks per row
+      for (int q = tid; q < nrows * pb; q += 256) {
+        const int r = q / pb, p = q - r * pb;
+        const int64_t f = (G1 ? (int64_t)(row_pair[row0 + r] / topk) : (int64_t)(row0 + r)) * (K / 16) +
+                          (int64_t)c0 * (KS / 16) + p;
+        uint4 o0, o1;
+        dec_act16<NV>(acodes + f * (NV ? 8 : 16), NV ? ascales + f : nullptr, o0, o1);
+        uint4* d = reinterpret_cast<uint4*>(Ar + r * rstride + 16 * p);
+        d[0] = o0;
+        d[1] = o1;
+      }
+    } else {  // 16-byte pieces, consecutive threads along a row
+      const int pr = (c1 - c0) * KS / 8;  // pieces per row
+      for (int q = tid; q < nrows * pr; q += 256) {
+        const int r = q / pr, p = q - r * pr;
+        const _Float16* src = (G1 ? act + (int64_t)(row_pair[row0 + r] / topk) * K : act + (int64_t)(row0 + r) * K) +
+                              (int64_t)c0 * KS + 8 * p;
+        *reinterpret_cast<uint4*>(Ar + r * rstride + 8 * p) = *reinterpret_cast<const uint4*>(src);
+      }
     }
     __syncthreads();
     if constexpr (DEPTH == 1) {
@@ -1840,25 +1865,34 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   _Float16* hdec = reinterpret_cast<_Float16*>(ws + L.h_f16);
   const int64_t xblk = a.T * a.H / 16;
   const unsigned gx = (unsigned)((xblk + 255) / 256);
+  // Without many-row experts the few-row kernels stage their rows from the codes: x is not decoded to FP16
+  // first (qa1), and the h quantization writes no FP16 copy of h (qa2).
+  const int64_t ks_vals = 4 * (a.nvfp4 ? kNvKB : kF8KB);  // k_skinny_rows super-step
+  const bool qa1 = !many && a.H % ks_vals == 0, qa2 = !many && a.I % ks_vals == 0;
   if (a.a16)
     act = reinterpret_cast<_Float16*>(const_cast<uint8_t*>(a.x_codes));  // BF16 x, read as 16-bit containers
-  else if (a.nvfp4)
+  else if (a.nvfp4 && !qa1)
     k_decode_act<true><<<gx, 256, 0, st>>>(a.x_codes, reinterpret_cast<const uint8_t*>(a.x_scales), xblk, act);
-  else if (!dense)
+  else if (!a.nvfp4 && !dense && !qa1)
     k_decode_act<false><<<gx, 256, 0, st>>>(a.x_codes, nullptr, xblk, act);
   stage_mark(0, 1, st);
   const uint8_t* w13s = reinterpret_cast<const uint8_t*>(a.w13_scales);
   const uint8_t* w2s = reinterpret_cast<const uint8_t*>(a.w2_scales);
   const float* xrs = reinterpret_cast<const float*>(a.x_scales);
-  const float* hsc = reinterpret_cast<const float*>(h_scales);  // FP8: per-row h scales
+  const uint8_t* xsb = reinterpret_cast<const uint8_t*>(a.x_scales);  // NVFP4: E4M3 block scales
+  const float* hsc = reinterpret_cast<const float*>(h_scales);        // FP8: per-row h scales
   // Few-row experts: k_skinny_rows when K is a multiple of its super-step (NVFP4 512, FP8 256 values),
   // else k_skinny with 32-value quarters; many-row experts: k_gemm_big (k_gemm_wide for the down
   // projection when I % 256 != 0).
 #define BSM_G1(NV)                                                                                             \
-  if (a.H % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                                   \
+  if (qa1)                                                                                                     \
+    k_skinny_rows<NV, true, kSkNT, false, NV ? 1 : kSkDepthF8, true><<<g1, 256, 0, st>>>(                      \
+        nullptr, a.x_codes, NV ? xsb : nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,    \
+        tiles, ntiles, a.H, a.H, a.I, h_f32, h_amax);                                                          \
+  else if (a.H % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                              \
     k_skinny_rows<NV, true, kSkNT, false, NV ? 1 : kSkDepthF8><<<g1, 256, 0, st>>>(                            \
-        act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32,  \
-        h_amax);                                                                                               \
+        act, nullptr, nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, \
+        a.H, a.I, h_f32, h_amax);                                                                              \
   else                                                                                                         \
     k_skinny<NV, true, 32, kSkNT, false, NV ? 1 : kSkDepthF8><<<g1, 256, 0, st>>>(                             \
         act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32,  \
@@ -1867,9 +1901,14 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     k_gemm_big<NV, true><<<w1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, \
                                              tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
 #define BSM_G2(NV, HSC)                                                                                        \
-  if (a.I % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                                   \
+  if (qa2)                                                                                                     \
+    k_skinny_rows<NV, false, kSkNT, false, NV ? 1 : kSkDepthF8, true><<<g2, 256, 0, st>>>(                     \
+        nullptr, h_codes, NV ? h_scales : nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs,      \
+        tiles, ntiles, a.I, a.H, a.I, y, h_amax);                                                              \
+  else if (a.I % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                              \
     k_skinny_rows<NV, false, kSkNT, false, NV ? 1 : kSkDepthF8><<<g2, 256, 0, st>>>(                           \
-        hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
+        hdec, nullptr, nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I,     \
+        a.H, a.I, y, h_amax);                                                                                  \
   else                                                                                                         \
     k_skinny<NV, false, 32, kSkNT, false, NV ? 1 : kSkDepthF8><<<g2, 256, 0, st>>>(                            \
         hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
@@ -1881,8 +1920,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     // weight-only W4A16: BF16 activations, NVFP4 weights decoded to BF16, h rounded to BF16
 #define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K)                                                   \
   if (K % (4 * kNvKB) == 0)                                                                                    \
-    k_skinny_rows<true, G, kSkNT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS,    \
-                                                              tiles, ntiles, K, a.H, a.I, OUT, h_amax);        \
+    k_skinny_rows<true, G, kSkNT, true><<<GRID, 256, 0, st>>>(A, nullptr, nullptr, row_pair, a.topk, nullptr, \
+                                                              SC, W, WS, WGS, tiles, ntiles, K, a.H, a.I, OUT, \
+                                                              h_amax);                                         \
   else                                                                                                         \
     k_skinny<true, G, 32, kSkNT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS,     \
                                                              tiles, ntiles, K, a.H, a.I, OUT, h_amax);         \
@@ -1900,7 +1940,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     BSM_G1(true);
     stage_mark(0, 2, st);
     err = launch_nvfp4_quantize_from_amax(h_f32, false, 1, L.P, a.I, h_codes, h_scales, h_gs, h_amax,
-                                          a.h_static ? a.h_gs_user : nullptr, st, hdec);
+                                          a.h_static ? a.h_gs_user : nullptr, st, qa2 ? nullptr : hdec);
     if (err != hipSuccess) return err;
     if (!a.h_static && a.h_gs_user) k_copy_f32<<<1, 64, 0, st>>>(h_gs, a.h_gs_user);
     stage_mark(0, 3, st);
@@ -1916,7 +1956,8 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
       BSM_G1(false);
     }
     stage_mark(0, 2, st);
-    err = launch_fp8_quantize(h_f32, false, L.P, a.I, h_codes, reinterpret_cast<float*>(h_scales), st, hdec);
+    err = launch_fp8_quantize(h_f32, false, L.P, a.I, h_codes, reinterpret_cast<float*>(h_scales), st,
+                              qa2 || dense ? nullptr : hdec);
     if (err != hipSuccess) return err;
     stage_mark(0, 3, st);
     if (dense) {
