@@ -582,7 +582,7 @@ def ceilings(dev, reps=10):
     nbytes = 4 << 30
     bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(2)]
     best = 0.0
-    for wgs in (1024, 2048, 4096, 8192):
+    for wgs in (512, 768, 1024, 2048, 4096, 8192):
         sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
         bsm.ceiling_hbm_read(bufs[0], wgs, sink)
         torch.cuda.synchronize()

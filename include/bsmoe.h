@@ -336,7 +336,8 @@ int bsm_set_stage_events(int which, void* const* events, int n);
  * Measurement aids (not part of the method): this GPU's achievable ceilings.
  *
  * bsm_ceiling_hbm_read: reads bytes (a multiple of 16, buf 16-byte aligned)
- *   of buf once, 16-byte loads in 4 KB pieces per workgroup, with wgs
+ *   of buf once, non-temporal 16-byte loads in 4 KB pieces per workgroup
+ *   (each load instruction covers 8 whole 128-byte lines), with wgs
  *   workgroups of 256 threads; writes one word per thread to sink (wgs * 256
  *   uint32).  Bytes / time = the streaming read ceiling.
  * bsm_ceiling_mfma_f16: wgs workgroups of 4 waves, each wave running iters

@@ -22,7 +22,7 @@ def _grid():
     return out
 
 
-def test_e2m1_decode_matches_published_grid():
+def test_e2m1_decode_matches_format_grid():
     grid = _grid()
     assert len(grid) == 16
     dec = F.e2m1_decode(np.arange(16))
