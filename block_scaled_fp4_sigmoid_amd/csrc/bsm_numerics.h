@@ -100,6 +100,26 @@ BSM_HD uint32_t e4m3_code_mag(float a) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// The E2M1 code of fl32(a / d2) as comparisons of a.  e2m1_code_mag counts seven tests on the binary32
+// quotient q = fl32(a / d2): q > 0.25, q >= 0.75, q > 1.25, q >= 1.75, q > 2.5, q >= 3.5, q > 5.  Each
+// threshold t has an even last significand bit, so with ties to even a test on q is a test on the exact
+// quotient against the midpoint next to t: a / d2 > t + u/2 (the strict tests, i even) or a / d2 >= t - u/2
+// (i odd), u being the spacing of binary32 values at t (only 0.25, a strict one, is a power of two).  For
+// 0 < d2 <= FLT_MAX that is a > M d2 or a >= M d2, and M d2 is exact in binary64 (25 + 24 significant
+// bits).  e2m1_threshold(d2, i) is the smallest binary32 T with that property, so test i holds exactly
+// when a >= T (NaN a fails every test, as in e2m1_code_mag).  (M d2 itself is never a binary32 value: M's
+// significand has 25 bits ending in 1, so the strict and the other tests differ only in principle.)
+BSM_HD float e2m1_threshold(float d2, int i) {
+  const double M = i == 0 ? 0.25 + 0x1p-26 : i == 1 ? 0.75 - 0x1p-25 : i == 2 ? 1.25 + 0x1p-24
+                 : i == 3 ? 1.75 - 0x1p-24 : i == 4 ? 2.5 + 0x1p-23  : i == 5 ? 3.5 - 0x1p-23
+                 : 5.0 + 0x1p-22;
+  const double B = M * (double)d2;
+  float t = (float)B;
+  const bool bump = (i & 1) ? (double)t < B : (double)t <= B;
+  if (bump && t != __builtin_huge_valf()) t = u2f(f2u(t) + 1u);
+  return t;
+}
+
 // ---------------------------------------------------------------------------
 // binary64 -> binary32 rounding with a proof obligation.
 // Returns true when every real in [v - err, v + err] rounds to the same

@@ -90,9 +90,23 @@ __global__ __launch_bounds__(kThreads) void k_amax_parts(const void* __restrict_
   if (threadIdx.x == 0) parts[(int64_t)b * kAmaxMaxParts + blockIdx.x] = m;
 }
 
-// Encode one 16-value block with global scale S (S > 0, or S == 0 -> zero scales).
-__device__ inline void encode_block(const float* v, float S, float d1, uint8_t* codes_f, uint8_t* scale_f,
-                                    _Float16* dec_f) {
+// The E2M1 codes of a block without dividing (e2m1_threshold): the thresholds depend on the block scale
+// code only (d2 = fl32(E4M3(sc) * S)), so one table per tensor serves every block.  Row sc holds the 7
+// thresholds and, in [7], a flag for a d2 of 0 or inf, where the block divides instead.  The division costs
+// about ten instructions per element; the table, seven compares.
+__device__ inline void build_e2m1_thresholds(float S, float (*thr)[8]) {
+  for (int k = threadIdx.x; k < 127 * 8; k += kThreads) {
+    const int sc = k >> 3, i = k & 7;
+    const float d2 = e4m3_value_mag((uint32_t)sc) * S;
+    const bool ok = d2 > 0.0f && d2 <= 3.4028234663852886e38f;
+    thr[sc][i] = i == 7 ? (ok ? 0.0f : 1.0f) : ok ? e2m1_threshold(d2, i) : 0.0f;
+  }
+}
+
+// Encode one 16-value block with global scale S (S > 0, or S == 0 -> zero scales); thr from
+// build_e2m1_thresholds(S).
+__device__ inline void encode_block(const float* v, float S, float d1, const float (*thr)[8], uint8_t* codes_f,
+                                    uint8_t* scale_f, _Float16* dec_f) {
   float ab = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
@@ -100,12 +114,24 @@ __device__ inline void encode_block(const float* v, float S, float d1, uint8_t* 
   if (S != 0.0f) sc = e4m3_code_mag(ab / d1);
   const float sv = e4m3_value_mag(sc);
   const float d2 = sv * S;
+  const float4 t03 = *reinterpret_cast<const float4*>(&thr[sc][0]);
+  const float4 t47 = *reinterpret_cast<const float4*>(&thr[sc][4]);
   uint32_t q[16];
+  if (sv == 0.0f) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t sgn = (f2u(v[i]) >> 31) << 3;
-    const uint32_t mag = (sv == 0.0f) ? 0u : e2m1_code_mag(fabsf(v[i]) / d2);
-    q[i] = sgn | mag;
+    for (int i = 0; i < 16; ++i) q[i] = (f2u(v[i]) >> 31) << 3;
+  } else if (t47.w != 0.0f) {  // d2 of 0 or inf: divide
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = ((f2u(v[i]) >> 31) << 3) | e2m1_code_mag(fabsf(v[i]) / d2);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float a = fabsf(v[i]);
+      const uint32_t mag = (uint32_t)(a >= t03.x) + (uint32_t)(a >= t03.y) + (uint32_t)(a >= t03.z) +
+                           (uint32_t)(a >= t03.w) + (uint32_t)(a >= t47.x) + (uint32_t)(a >= t47.y) +
+                           (uint32_t)(a >= t47.z);
+      q[i] = ((f2u(v[i]) >> 31) << 3) | mag;
+    }
   }
   uint2 packed;
   packed.x = q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12) | (q[4] << 16) | (q[5] << 20) | (q[6] << 24) |
@@ -151,6 +177,9 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_encode(const void* __restric
   }
   if (gs && mode != 1 && blockIdx.x == 0 && threadIdx.x == 0) gs[b] = S;
   const float d1 = 6.0f * S;
+  __shared__ __attribute__((aligned(16))) float thr[128][8];
+  build_e2m1_thresholds(S, thr);
+  __syncthreads();
   const void* xb = BF16 ? (const void*)((const uint16_t*)x + (int64_t)b * n_blk * 16)
                         : (const void*)((const float*)x + (int64_t)b * n_blk * 16);
   uint8_t* cb = codes + (int64_t)b * n_blk * 8;
@@ -161,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_encode(const void* __restric
     const int64_t f = n_blk - 1 - g;
     float v[16];
     load16<BF16>(xb, f, v);
-    encode_block(v, S, d1, cb + f * 8, sb + f, dec16 ? dec16 + (int64_t)b * n_blk * 16 + f * 16 : nullptr);
+    encode_block(v, S, d1, thr, cb + f * 8, sb + f, dec16 ? dec16 + (int64_t)b * n_blk * 16 + f * 16 : nullptr);
   }
 }
 

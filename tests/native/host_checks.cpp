@@ -11,6 +11,15 @@ void hc_e4m3_code(const float* a, int64_t n, uint8_t* out) {
 void hc_e2m1_code(const float* a, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)bsm::e2m1_code_mag(a[i]);
 }
+
+// E2M1 magnitude code of fl32(a / d2) from the thresholds (0 < d2 <= FLT_MAX)
+void hc_e2m1_code_thr(const float* a, const float* d2, int64_t n, uint8_t* out) {
+  for (int64_t k = 0; k < n; ++k) {
+    uint32_t c = 0;
+    for (int i = 0; i < 7; ++i) c += (uint32_t)(a[k] >= bsm::e2m1_threshold(d2[k], i));
+    out[k] = (uint8_t)c;
+  }
+}
 void hc_e4m3_value(const uint8_t* c, int64_t n, float* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = bsm::e4m3_value_mag(c[i]);
 }

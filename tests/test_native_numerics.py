@@ -177,3 +177,39 @@ def test_exact_dot_nonfinite_inputs_stay_in_range(hc):
     ok = np.empty(3, np.int32)
     hc.hc_exact_dot(x, w, 3, 64, out)
     hc.hc_window_dot(x, w, 3, 64, out, ok)
+
+
+def test_e2m1_thresholds_equal_the_divided_encoding(hc):
+    """The gfx950 encoder's division-free E2M1 codes: a compared with e2m1_threshold(d2, i) must give the
+    oracle's code of the correctly rounded float32 quotient a / d2, for every block-scale value times
+    global scales across the range (subnormal, tiny and huge d2) and at every rounding midpoint of the
+    quotient, its float32 neighbours and random values."""
+    hc.hc_e2m1_code_thr.argtypes = [np.ctypeslib.ndpointer(np.float32), np.ctypeslib.ndpointer(np.float32),
+                                    ctypes.c_int64, np.ctypeslib.ndpointer(np.uint8)]
+    rng = np.random.default_rng(7)
+    sv = F.E4M3_MAGNITUDES[1:].astype(np.float32)
+    gs = np.float32([1.0, 1.0 / 6.0, 2.0 ** -20, 3.7e-3, 1.234567e-5, 2.0 ** -130, 1e-38, 5e30,
+                     3.4028235e38 / 448.0, *rng.uniform(1e-6, 1.0, 12)])
+    d2 = (sv[None, :] * gs[:, None]).astype(np.float32).ravel()
+    d2 = d2[(d2 > 0) & np.isfinite(d2)]
+    mids = np.float64([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    a_list, d_list = [], []
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        for d in d2:
+            b = (mids * np.float64(d)).astype(np.float32)  # the E2M1 decision points times d2, then +-2 ulps
+            near, up, lo = [b], b, b
+            for _ in range(2):
+                up, lo = np.nextafter(up, np.float32(np.inf)), np.nextafter(lo, np.float32(0))
+                near += [up, lo]
+            near.append(np.float32(rng.uniform(0, 7, 8) * d))
+            near.append(np.float32([0.0, np.inf, np.nan, 3.4028235e38, 2.0 ** -149]))
+            a = np.concatenate(near).astype(np.float32)
+            a_list.append(a)
+            d_list.append(np.full(a.size, d, np.float32))
+        a = np.concatenate(a_list)
+        dd = np.concatenate(d_list)
+        expect = F.e2m1_encode_magnitude((a / dd).astype(np.float32))
+    out = np.empty(a.size, np.uint8)
+    hc.hc_e2m1_code_thr(a, dd, a.size, out)
+    bad = np.nonzero(out != expect)[0]
+    assert bad.size == 0, [(float(a[i]), float(dd[i]), int(out[i]), int(expect[i])) for i in bad[:8]]
