@@ -72,19 +72,40 @@ __device__ inline void load16(const void* x, int64_t f, float* v) {
   }
 }
 
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+constexpr int kAmaxUnroll = 4;  // 16-byte pieces per lane and iteration
+
+// Pass 1 needs no block structure: consecutive lanes read consecutive 16-byte pieces, non-temporal, so
+// each load instruction covers 8 whole 128-byte lines.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_amax_parts(const void* __restrict__ x, int64_t n_blk,
                                                           float* __restrict__ parts, int nparts) {
   __shared__ float lds[kThreads / 64];
   const int b = blockIdx.y;
-  const void* xb = BF16 ? (const void*)((const uint16_t*)x + (int64_t)b * n_blk * 16)
-                        : (const void*)((const float*)x + (int64_t)b * n_blk * 16);
+  const u4v* xb = reinterpret_cast<const u4v*>(BF16 ? (const void*)((const uint16_t*)x + (int64_t)b * n_blk * 16)
+                                                    : (const void*)((const float*)x + (int64_t)b * n_blk * 16));
+  const int64_t np = n_blk * (BF16 ? 2 : 4);
   float m = 0.0f;
-  for (int64_t f = (int64_t)blockIdx.x * kThreads + threadIdx.x; f < n_blk; f += (int64_t)nparts * kThreads) {
-    float v[16];
-    load16<BF16>(xb, f, v);
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kAmaxUnroll + threadIdx.x; base < np;
+       base += (int64_t)nparts * kThreads * kAmaxUnroll) {
+    u4v v[kAmaxUnroll];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t i = base + (int64_t)u * kThreads;
+      v[u] = i < np ? __builtin_nontemporal_load(xb + i) : u4v{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (BF16) {
+          m = fmaxf(m, fabsf(u2f(v[u][i] << 16)));
+          m = fmaxf(m, fabsf(u2f(v[u][i] & 0xFFFF0000u)));
+        } else {
+          m = fmaxf(m, fabsf(u2f(v[u][i])));
+        }
+      }
+    }
   }
   m = block_max(m, lds);
   if (threadIdx.x == 0) parts[(int64_t)b * kAmaxMaxParts + blockIdx.x] = m;
@@ -126,11 +147,12 @@ __device__ inline void encode_block(const float* v, float S, float d1, const flo
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      // the number of thresholds at or below a, by binary search over the sorted T_0 <= ... <= T_6
       const float a = fabsf(v[i]);
-      const uint32_t mag = (uint32_t)(a >= t03.x) + (uint32_t)(a >= t03.y) + (uint32_t)(a >= t03.z) +
-                           (uint32_t)(a >= t03.w) + (uint32_t)(a >= t47.x) + (uint32_t)(a >= t47.y) +
-                           (uint32_t)(a >= t47.z);
-      q[i] = ((f2u(v[i]) >> 31) << 3) | mag;
+      const bool hi = a >= t03.w;
+      const bool mid = a >= (hi ? t47.y : t03.y);
+      const bool lo = a >= (hi ? (mid ? t47.z : t47.x) : (mid ? t03.z : t03.x));
+      q[i] = ((f2u(v[i]) >> 31) << 3) | (hi ? 4u : 0u) | (mid ? 2u : 0u) | (lo ? 1u : 0u);
     }
   }
   uint2 packed;
@@ -141,16 +163,15 @@ __device__ inline void encode_block(const float* v, float S, float d1, const flo
   *reinterpret_cast<uint2*>(codes_f) = packed;
   *scale_f = (uint8_t)sc;
   if (dec_f) {
-    // exact FP16 of q * s_b (at most 6 significant bits, within [2^-10, 2688])
-    _Float16 d[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float mag = e2m1_value_mag(q[i] & 7u) * sv;
-      d[i] = (_Float16)((q[i] & 8u) ? -mag : mag);
-    }
+    // exact FP16 of q * s_b (at most 6 significant bits, within [2^-10, 2688]): the hardware E2M1 -> FP16
+    // converter (unit scale) and one packed multiply by s_b, which FP16 holds exactly
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 s2 = {(_Float16)sv, (_Float16)sv};
+#define BSM_DEC2(W, K) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(W, 1.0f, K) * s2)
     uint4* dp = reinterpret_cast<uint4*>(dec_f);
-    dp[0] = __builtin_bit_cast(uint4, *reinterpret_cast<const _Float16(*)[8]>(d));
-    dp[1] = __builtin_bit_cast(uint4, *reinterpret_cast<const _Float16(*)[8]>(d + 8));
+    dp[0] = make_uint4(BSM_DEC2(packed.x, 0), BSM_DEC2(packed.x, 1), BSM_DEC2(packed.x, 2), BSM_DEC2(packed.x, 3));
+    dp[1] = make_uint4(BSM_DEC2(packed.y, 0), BSM_DEC2(packed.y, 1), BSM_DEC2(packed.y, 2), BSM_DEC2(packed.y, 3));
+#undef BSM_DEC2
   }
 }
 
