@@ -19,11 +19,12 @@ between them).
 import numpy as np
 import torch
 
+from oracle import formats as F
 from oracle import moe as OM
 from oracle import quant_c as QC
 from oracle import route as OR
 from oracle.quant import unpack_e2m1
-from tests.helpers import moe_stages, np_, rel_l2, to_dev_bf16, weights_match
+from tests.helpers import moe_stages, np_, rel_l2, to_dev_bf16, weights_match, ws_view
 
 STAGE_TOL = 1e-5
 LAYER_TOL = 1e-3
@@ -160,5 +161,52 @@ def check_layer(gpu_lib, fmt, cfg, x, wr, w13, w2, gw, label):
     # end to end
     res["out"] = rel_l2(out, ref["out"])
     print(f"{label}: layer output rel L2 {res['out']:.3e}", flush=True)
+    assert res["out"] <= LAYER_TOL, f"{label}: layer output rel L2 {res['out']:.3e}"
+    return res
+
+
+def check_layer_w4a16(gpu_lib, cfg, x, wr, w13, w2, gw, label):
+    """The weight-only layer (NVFP4 weights, BF16 x and h) on bf16 x against the oracle in full: routing
+    bit-exact; h of every row within 1e-5; y from the GPU's own h rounded to BF16 within 1e-5; the combine
+    of the GPU's y within 1e-6; the output within 1e-3 of the oracle's own end-to-end layer."""
+    T = x.shape[0]
+    xt = to_dev_bf16(x)
+    ids, wts = gpu_lib.route(xt, to_dev_bf16(wr), cfg.n_group, cfg.topk_group, cfg.topk)
+    out, ws = gpu_lib.moe_expert_mlp_w4a16(gw, xt, ids, wts, cfg.combine_scale, return_workspace=True)
+    torch.cuda.synchronize()
+    P = T * cfg.topk
+    lay = gpu_lib.moe_workspace_layout("w4a16", cfg.E, cfg.H, cfg.I, T, cfg.topk)
+    h = np_(ws_view(ws, lay, "h_f32", torch.float32, (P, cfg.I)))
+    y = np_(ws_view(ws, lay, "y_f32", torch.float32, (P, cfg.H)))
+    row_pair = np_(ws_view(ws, lay, "row_pair", torch.int32, (P,)))
+    out = np_(out)
+    del ws
+    torch.cuda.empty_cache()
+    print(f"{label}: GPU layer done, oracle routing", flush=True)
+    oi, ow, _, _ = OR.route(x, wr, cfg.n_group, cfg.topk_group, cfg.topk)
+    assert np.array_equal(np_(ids), oi), f"{label}: routing ids differ"
+    assert np.array_equal(np_(wts).view(np.uint32), ow.view(np.uint32)), f"{label}: routing weights differ"
+    counts, offsets, row_of_pair, pair_of_row = OM.permute(oi, cfg.E)
+    assert np.array_equal(row_pair, pair_of_row)
+    print(f"{label}: oracle expert MLP over {int((counts > 0).sum())} experts", flush=True)
+    experts = DeviceExperts(w13, w2, gw, "nvfp4")
+    ref = OM.moe_expert_mlp(x.astype(np.float64), oi, ow, experts, "w4a16", cfg.combine_scale, q=QC)
+    res = {"active": int((counts > 0).sum()), "max_rows": int(counts.max())}
+    res["h"] = rel_l2(h[row_of_pair], ref["h"])
+    assert res["h"] <= STAGE_TOL, f"{label}: h rel L2 {res['h']:.3e}"
+    hb = F.bf16_round(h).astype(np.float64)
+    y_tf = np.zeros_like(y)
+    for e in np.nonzero(counts)[0]:
+        rows = np.arange(offsets[e], offsets[e + 1])
+        y_tf[rows] = OM.gemm_f32(hb[rows], experts[e].decoded_down())
+    del hb
+    res["y"] = rel_l2(y, y_tf)
+    assert res["y"] <= STAGE_TOL, f"{label}: y rel L2 {res['y']:.3e}"
+    del y_tf
+    comb = OM.combine_f32(y[row_of_pair].reshape(T, cfg.topk, -1), ow, cfg.combine_scale)
+    res["combine"] = rel_l2(out, comb)
+    assert res["combine"] <= 1e-6, f"{label}: combine rel L2 {res['combine']:.3e}"
+    res["out"] = rel_l2(out, ref["out"])
+    print(f"{label}: {res}", flush=True)
     assert res["out"] <= LAYER_TOL, f"{label}: layer output rel L2 {res['out']:.3e}"
     return res

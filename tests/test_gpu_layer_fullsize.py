@@ -4,7 +4,10 @@
 5120, 256 SwiGLU experts of intermediate 2560 in 8 groups of 32, the best 4
 groups by their top-2 score sums, top 8 experts, normalized weights, x2.5.
 NVFP4 ("NVFP4 quantization" page, "Quantization scheme") and FP8_DYNAMIC
-("FP8 quantization" page, "Quantization scheme") weights and activations.
+("FP8 quantization" page, "Quantization scheme") weights and activations, and
+the weight-only variant (NVFP4 weights, BF16 activations: "Beam-1.0 auf 4x
+NVIDIA RTX PRO 6000 Blackwell Server Edition", "NVFP4 auf Blackwell gegen FP8
+auf Hopper").
 
 Decode: 64 tokens (about 222 active experts).  Prefill: 8192 tokens with the
 Zipf-like router skew (67 active experts, the largest above 4000 rows).  The
@@ -17,7 +20,7 @@ import pytest
 import torch
 
 import workloads as W
-from tests.fullsize import check_layer
+from tests.fullsize import check_layer, check_layer_w4a16
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -42,3 +45,12 @@ def test_layer_decode64_full(gpu_lib, fmt):
 def test_layer_prefill8192_full(gpu_lib, fmt):
     res = _layer(gpu_lib, W.PREFILL, fmt)
     assert res["max_rows"] > 1000
+
+
+@pytest.mark.parametrize("cfg", [W.DECODE, W.PREFILL], ids=["decode64", "prefill8192"])
+def test_layer_w4a16_full(gpu_lib, cfg):
+    x, wr = W.activations(cfg), W.router_weights(cfg)
+    w13, w2 = W.expert_weights_device(cfg)
+    gw = gpu_lib.quantize_expert_weights(w13, w2, "nvfp4")
+    res = check_layer_w4a16(gpu_lib, cfg, x, wr, w13, w2, gw, f"{cfg.name}-{cfg.T} w4a16")
+    assert res["max_rows"] > (1000 if cfg.T > 64 else 1)
