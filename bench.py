@@ -765,7 +765,10 @@ def main():
         pms, pst, _, pn = measure_layer(W.PREFILL, args.fmt, dev, psteps, 2)
         prefill = prefill_object(args.fmt, pn, pms, pst, psteps)
 
-    fp8_decode = fp8_prefill = quant = stack = ceil = None
+    fp8_decode = fp8_prefill = quant = stack = ceil = uniform = None
+    if extras and not args.no_prefill:
+        ums, ust, _, un = measure_layer(W.PREFILL_UNIFORM, args.fmt, dev, psteps, 2)
+        uniform = prefill_object(args.fmt, un, ums, ust, psteps)
     if extras and args.fmt == "nvfp4":
         fms, fst, _, fn = measure_layer(W.DECODE, "fp8", dev, args.steps, args.warmup)
         fg1 = fn["gemm1"]
@@ -819,6 +822,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill_8192": prefill,
+        "prefill_8192_all_experts": uniform,
         "fp8_decode_64": fp8_decode,
         "fp8_prefill_8192": fp8_prefill,
         "quantize_32768x5120": quant,

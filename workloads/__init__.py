@@ -63,7 +63,10 @@ TINY = LayerConfig("tiny", 1, T=64, H=256, I=128, E=16, n_group=4, topk_group=2,
 DECODE = LayerConfig("decode", 3, T=64, H=5120, I=2560, E=256, n_group=8, topk_group=4, topk=8)
 PREFILL = LayerConfig("prefill", 4, T=8192, H=5120, I=2560, E=256, n_group=8, topk_group=4, topk=8, zipf_skew=True)
 STACK = LayerConfig("stack", 5, T=4096, H=5120, I=2560, E=256, n_group=8, topk_group=4, topk=8, layers=4)
-CONFIGS = {c.name: c for c in (TINY, DECODE, PREFILL, STACK)}
+# the prefill layer without the popularity skew: every expert active (about 256 rows each)
+PREFILL_UNIFORM = LayerConfig("prefill-uniform", 4, T=8192, H=5120, I=2560, E=256, n_group=8, topk_group=4,
+                              topk=8)
+CONFIGS = {c.name: c for c in (TINY, DECODE, PREFILL, STACK, PREFILL_UNIFORM)}
 
 QUANT_SHAPE = (32768, 5120)  # standalone quantize workload
 QUANT_OUTLIER_FRACTION = 0.01
