@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import workloads as W
+from oracle import formats as F
 from oracle import quant as Q
 from oracle import quant_c as QC
 from tests.fullsize import bf16_bits
@@ -48,6 +49,59 @@ def test_nvfp4_quantize_batched_and_static(gpu_lib):
     for b in range(3):
         oc, os_, og = Q.nvfp4_quantize(xs[b], global_scale=np.float32(np_(static)[b]))
         assert np.array_equal(np_(scales)[b], os_) and np.array_equal(np_(codes)[b], oc)
+
+
+def _nbrs(v, k=2):
+    """v and its float32 neighbours up to k ulps either way (positive v)."""
+    v = np.asarray(v, np.float32)
+    out, up, lo = [v], v, v
+    for _ in range(k):
+        up, lo = np.nextafter(up, np.float32(np.inf)), np.nextafter(lo, np.float32(0))
+        out += [up, lo]
+    return np.concatenate(out)
+
+
+def test_nvfp4_quantize_decision_points(gpu_lib):
+    """Values at and next to every decision point of the encoding, bit-exact against the oracle (f32
+    input, static global scales): every E2M1 rounding point of x / d2, d2 = s_b S_g, for block scales
+    across the E4M3 range and several global scales, and every E4M3 rounding point of the block scale."""
+    t = np.float64([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for S in (1.0, 1.0 / 6.0, 3.7e-3, 2.0 ** -20, 0.73):
+        S = np.float32(S)
+        # one block per scale code: element 0 sets the block maximum (the scale); the oracle's scale of
+        # that block gives the d2 whose decision points the other 15 elements then sit on
+        tops = (np.float32(6.0) * F.E4M3_MAGNITUDES[1:127].astype(np.float32) * S).astype(np.float32)
+        probe = np.zeros((len(tops), 16), np.float32)
+        probe[:, 0] = tops
+        sc = Q.nvfp4_quantize(probe, global_scale=S)[1].ravel()
+        rows = []
+        for top, code in zip(tops, sc):
+            d2 = np.float32(np.float32(F.E4M3_MAGNITUDES[code]) * S)
+            a = _nbrs((t * np.float64(d2)).astype(np.float32))
+            a = np.concatenate([a, -a])
+            a = a[np.abs(a) <= top]
+            for i in range(0, len(a), 15):
+                blk = np.zeros(16, np.float32)
+                blk[0] = top
+                blk[1:1 + len(a[i:i + 15])] = a[i:i + 15]
+                rows.append(blk)
+        n = len(rows) // 8 * 8
+        x = np.stack(rows[:n]).reshape(n // 8, 128)
+        codes, scales, _ = gpu_lib.nvfp4_quantize(to_dev_f32(x), global_scale=torch.tensor([S], device="cuda"))
+        oc, os_, _ = Q.nvfp4_quantize(x, global_scale=S)
+        assert np.array_equal(np_(scales), os_), S
+        assert np.array_equal(np_(codes), oc), S
+    # every E4M3 rounding point of the block scale: S = fl32(1/6) makes fl32(6 S) = 1
+    S = np.float32(1.0 / 6.0)
+    tab = F.E4M3_MAGNITUDES
+    amax = _nbrs(((tab[1:-1] + tab[2:]) / 2).astype(np.float32), 1)
+    x = np.zeros((len(amax), 16), np.float32)
+    x[:, 5] = amax
+    x[:, 9] = -amax * np.float32(0.37)
+    x = x[: len(amax) // 8 * 8].reshape(-1, 128)
+    codes, scales, _ = gpu_lib.nvfp4_quantize(to_dev_f32(x), global_scale=torch.tensor([S], device="cuda"))
+    oc, os_, _ = Q.nvfp4_quantize(x, global_scale=S)
+    assert np.array_equal(np_(scales), os_) and np.array_equal(np_(codes), oc)
 
 
 def test_nvfp4_zero_tensor(gpu_lib):
