@@ -693,7 +693,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "fp8", "w4a16"])
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "stack", "dense-fp8"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "prefill-uniform", "stack",
+                                                               "dense-fp8"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the FP8 layers, the standalone quantize, the stack and the ceilings")
@@ -745,7 +746,7 @@ def main():
     if args.workload == "dense-fp8":
         run_dense_fp8(args, dev)
         return
-    main_cfg = W.DECODE if args.workload == "decode" else W.PREFILL
+    main_cfg = {"decode": W.DECODE, "prefill": W.PREFILL, "prefill-uniform": W.PREFILL_UNIFORM}[args.workload]
     ms, stage_ms, g1_ms, main_nums = measure_layer(main_cfg, args.fmt, dev, args.steps, args.warmup)
 
     g1 = main_nums["gemm1"]

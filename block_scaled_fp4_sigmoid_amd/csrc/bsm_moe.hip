@@ -1258,6 +1258,10 @@ __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict
 // 8q + 4 (l / 32) + j, column l % 32.
 // ---------------------------------------------------------------------------
 constexpr int kGBM = 128, kGBN = 256, kGBK = 64;
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
 template <bool NV>
 struct BigB {
   static constexpr int kRow = NV ? 36 : 72;  // LDS bytes per weight row and K step (+4 / +8 pad)
@@ -1418,6 +1422,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mt][t][q] = 0.0f;
 
+  // The K loop is compiled for MT = 1..4 live 32-row sub-tiles (MT = ceil(nrows / 32), uniform per
+  // workgroup): the last, ragged row tile of an expert skips the multiplies and fragment reads of its
+  // empty sub-tiles.
+  auto kloop = [&](auto mtc) {
+  constexpr int MT = decltype(mtc)::value;
   // K step j of the current group from LDS buffer buf
   // rd: the activation tile of this K step (rows of kAS; swizzled chunks with direct-to-LDS staging)
   auto mma_step = [&](int j, const _Float16* __restrict__ rd) {
@@ -1425,7 +1434,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
     for (int k16 = 0; k16 < kGBK / 16; ++k16) {
       h8v a[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
         a[mt] = *reinterpret_cast<const h8v*>(
             rd + (mt * 32 + l32) * kAS + (kAdma ? 8 * ((2 * k16 + lh) ^ ((l32 >> 1) & 7)) : k16 * 16 + lh * 8));
 #pragma unroll
@@ -1444,7 +1453,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
           b = dec_fp8x8(w.x, w.y);
         }
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt][t] = mfma32<A16>(a[mt], b, acc[mt][t]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt][t] = mfma32<A16>(a[mt], b, acc[mt][t]);
       }
     }
   };
@@ -1484,6 +1493,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
       lds_barrier();
     }
   }
+  };
+  const int live = (nrows + 31) / 32;
+  if (live >= 4)
+    kloop(IntC<4>{});
+  else if (live == 3)
+    kloop(IntC<3>{});
+  else if (live == 2)
+    kloop(IntC<2>{});
+  else
+    kloop(IntC<1>{});
 #undef BSM_BIG_BROW
 
   // Epilogue.  Accumulator register 4q + j of m tile mt is row mt * 32 + 8q + 4 (lane / 32) + j and
