@@ -1426,73 +1426,73 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   // workgroup): the last, ragged row tile of an expert skips the multiplies and fragment reads of its
   // empty sub-tiles.
   auto kloop = [&](auto mtc) {
-  constexpr int MT = decltype(mtc)::value;
-  // K step j of the current group from LDS buffer buf
-  // rd: the activation tile of this K step (rows of kAS; swizzled chunks with direct-to-LDS staging)
-  auto mma_step = [&](int j, const _Float16* __restrict__ rd) {
+    constexpr int MT = decltype(mtc)::value;
+    // K step j of the current group from LDS buffer buf
+    // rd: the activation tile of this K step (rows of kAS; swizzled chunks with direct-to-LDS staging)
+    auto mma_step = [&](int j, const _Float16* __restrict__ rd) {
 #pragma unroll
-    for (int k16 = 0; k16 < kGBK / 16; ++k16) {
-      h8v a[4];
+      for (int k16 = 0; k16 < kGBK / 16; ++k16) {
+        h8v a[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        a[mt] = *reinterpret_cast<const h8v*>(
-            rd + (mt * 32 + l32) * kAS + (kAdma ? 8 * ((2 * k16 + lh) ^ ((l32 >> 1) & 7)) : k16 * 16 + lh * 8));
+        for (int mt = 0; mt < MT; ++mt)
+          a[mt] = *reinterpret_cast<const h8v*>(
+              rd + (mt * 32 + l32) * kAS + (kAdma ? 8 * ((2 * k16 + lh) ^ ((l32 >> 1) & 7)) : k16 * 16 + lh * 8));
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int brow = BSM_BIG_BROW(t) + l32;
-        h8v b;
-        if constexpr (NV) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(&Bg[brow][j * 32 + k16 * 8 + lh * 4]);
-          const h2v s2 = scale_pair_sel(Bsc[j][brow], (uint32_t)k16 * 0x0101u);
-          if constexpr (A16)
-            b = dec_fp4x8_bf16(w, (float)s2[0]);
-          else
-            b = dec_fp4x8(w, s2);
-        } else {
-          const uint2 w = *reinterpret_cast<const uint2*>(&Bg[brow][j * 64 + k16 * 16 + lh * 8]);
-          b = dec_fp8x8(w.x, w.y);
+        for (int t = 0; t < 2; ++t) {
+          const int brow = BSM_BIG_BROW(t) + l32;
+          h8v b;
+          if constexpr (NV) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(&Bg[brow][j * 32 + k16 * 8 + lh * 4]);
+            const h2v s2 = scale_pair_sel(Bsc[j][brow], (uint32_t)k16 * 0x0101u);
+            if constexpr (A16)
+              b = dec_fp4x8_bf16(w, (float)s2[0]);
+            else
+              b = dec_fp4x8(w, s2);
+          } else {
+            const uint2 w = *reinterpret_cast<const uint2*>(&Bg[brow][j * 64 + k16 * 16 + lh * 8]);
+            b = dec_fp8x8(w.x, w.y);
+          }
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][t] = mfma32<A16>(a[mt], b, acc[mt][t]);
         }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][t] = mfma32<A16>(a[mt], b, acc[mt][t]);
       }
-    }
-  };
+    };
 
-  // The K loop runs over weight groups with the group's steps unrolled, so no load sits under a
-  // branch (indices past the end are clamped to the last step or group and their data is never
-  // read) and the wait counts stay exact.  A step's activations load one step ahead; a group's
-  // weights load two steps ahead, after the activations of that step, so that the activation
-  // store of the step before the group boundary does not wait for them.
-  const int nk = (int)(K / kGBK), ng = nk / GS;
-  // The step's loads and multiplies in one function whose two tile pointers are restrict-qualified:
-  // the compiler then knows the direct-to-LDS writes into one buffer do not alias the reads of the
-  // other, and does not make the reads wait for the writes.
-  auto issue_and_multiply = [&](int j, int snext, int gnext, _Float16* __restrict__ wr,
-                                const _Float16* __restrict__ rd) {
-    aload(snext, wr);
-    if (j == GS - 2) bload(gnext);
-    __builtin_amdgcn_sched_barrier(0);  // the scheduler would otherwise sink the loads to their stores
-    mma_step(j, rd);
-  };
-  aload(0, Ab[0]);
-  bload(0);
-  bstore();
-  lstore(0, 0);
-  __syncthreads();
-  for (int gi = 0; gi < ng; ++gi) {
+    // The K loop runs over weight groups with the group's steps unrolled, so no load sits under a
+    // branch (indices past the end are clamped to the last step or group and their data is never
+    // read) and the wait counts stay exact.  A step's activations load one step ahead; a group's
+    // weights load two steps ahead, after the activations of that step, so that the activation
+    // store of the step before the group boundary does not wait for them.
+    const int nk = (int)(K / kGBK), ng = nk / GS;
+    // The step's loads and multiplies in one function whose two tile pointers are restrict-qualified:
+    // the compiler then knows the direct-to-LDS writes into one buffer do not alias the reads of the
+    // other, and does not make the reads wait for the writes.
+    auto issue_and_multiply = [&](int j, int snext, int gnext, _Float16* __restrict__ wr,
+                                  const _Float16* __restrict__ rd) {
+      aload(snext, wr);
+      if (j == GS - 2) bload(gnext);
+      __builtin_amdgcn_sched_barrier(0);  // the scheduler would otherwise sink the loads to their stores
+      mma_step(j, rd);
+    };
+    aload(0, Ab[0]);
+    bload(0);
+    bstore();
+    lstore(0, 0);
+    __syncthreads();
+    for (int gi = 0; gi < ng; ++gi) {
 #pragma unroll
-    for (int j = 0; j < GS; ++j) {
-      const int ks = gi * GS + j;  // GS is even, so ks & 1 == j & 1
-      issue_and_multiply(j, ks + 1 < nk ? ks + 1 : ks, gi + 1 < ng ? (gi + 1) * GS : gi * GS,
-                         Ab[(j & 1) ^ 1], Ab[j & 1]);
-      if (j == GS - 1) {  // next group: every wave has finished reading the current one
+      for (int j = 0; j < GS; ++j) {
+        const int ks = gi * GS + j;  // GS is even, so ks & 1 == j & 1
+        issue_and_multiply(j, ks + 1 < nk ? ks + 1 : ks, gi + 1 < ng ? (gi + 1) * GS : gi * GS,
+                           Ab[(j & 1) ^ 1], Ab[j & 1]);
+        if (j == GS - 1) {  // next group: every wave has finished reading the current one
+          lds_barrier();
+          bstore();
+        }
+        lstore((j & 1) ^ 1, j == GS - 2);
         lds_barrier();
-        bstore();
       }
-      lstore((j & 1) ^ 1, j == GS - 2);
-      lds_barrier();
     }
-  }
   };
   const int live = (nrows + 31) / 32;
   if (live >= 4)
