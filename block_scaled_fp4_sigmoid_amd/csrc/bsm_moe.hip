@@ -1430,6 +1430,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
     // K step j of the current group from LDS buffer buf
     // rd: the activation tile of this K step (rows of kAS; swizzled chunks with direct-to-LDS staging)
     auto mma_step = [&](int j, const _Float16* __restrict__ rd) {
+      // NVFP4: the step's four block scales of each weight row as FP16, two converts per row and step
+      h2v s01[2], s23[2];
+      if constexpr (NV) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t sw = Bsc[j][BSM_BIG_BROW(t) + l32];
+          s01[t] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+          s23[t] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
+        }
+      }
 #pragma unroll
       for (int k16 = 0; k16 < kGBK / 16; ++k16) {
         h8v a[4];
@@ -1443,9 +1453,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
           h8v b;
           if constexpr (NV) {
             const uint32_t w = *reinterpret_cast<const uint32_t*>(&Bg[brow][j * 32 + k16 * 8 + lh * 4]);
-            const h2v s2 = scale_pair_sel(Bsc[j][brow], (uint32_t)k16 * 0x0101u);
+            const _Float16 sk = k16 == 0 ? s01[t][0] : k16 == 1 ? s01[t][1] : k16 == 2 ? s23[t][0] : s23[t][1];
+            const h2v s2 = {sk, sk};
             if constexpr (A16)
-              b = dec_fp4x8_bf16(w, (float)s2[0]);
+              b = dec_fp4x8_bf16(w, (float)sk);
             else
               b = dec_fp4x8(w, s2);
           } else {
