@@ -473,12 +473,26 @@ __device__ inline void sk_mma_step(const _Float16* arow, const BRegs<NV, KB>* b,
   if constexpr (J + 1 < KB / 8) sk_mma_step<NV, KB, NT, J + 1, A16>(arow, b, sdw, selA, selB, acc);
 }
 
+// Piece J from the lane's scale pairs (sp[q]: the two FP16 block scales of scale dword q that this lane's
+// group uses; the piece takes one of them, broadcast within the packed multiply).
+template <bool NV, int KB, int J, bool A16>
+__device__ inline h8v dec_piece_sp(uint4 c, const h2v* sp) {
+  constexpr int SPU = SkGeom<NV>::SPU;
+  if constexpr (NV) {
+    const uint32_t w = (J & 3) == 0 ? c.x : (J & 3) == 1 ? c.y : (J & 3) == 2 ? c.z : c.w;
+    const _Float16 sk = ((J & 3) >> 1) ? sp[J / SPU][1] : sp[J / SPU][0];
+    if constexpr (A16) return dec_fp4x8_bf16(w, (float)sk);
+    return dec_fp4x8(w, h2v{sk, sk});
+  } else {
+    return (J & 1) ? dec_fp8x8(c.z, c.w) : dec_fp8x8(c.x, c.y);
+  }
+}
+
 // The same steps from whole-line loads: piece i of every tile is moved into the MFMA lane layout just
 // before its first step (4 registers per tile live instead of the whole super-step).
 template <bool NV, int KB, int NT, int J, bool A16>
 __device__ inline void sk_mma_step_lines(const _Float16* arow, const Lines* r, int m, int g,
-                                         const uint32_t (*sdw)[KB / 32 > 0 ? KB / 32 : 1], uint32_t selA,
-                                         uint32_t selB, f4v* acc, uint4* cur) {
+                                         const h2v (*sp)[KB / 32 > 0 ? KB / 32 : 1], f4v* acc, uint4* cur) {
   constexpr int VPU = SkGeom<NV>::VPU, SPU = SkGeom<NV>::SPU;
   constexpr int col = (J / SPU) * 4 * VPU + (J % SPU) * 8;  // plus g * VPU, folded into arow
   if constexpr (J % SPU == 0) {
@@ -487,9 +501,8 @@ __device__ inline void sk_mma_step_lines(const _Float16* arow, const Lines* r, i
   }
   const h8v a = *reinterpret_cast<const h8v*>(arow + col);
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    acc[t] = mfma_ab<A16>(a, dec_piece<NV, KB, J, A16>(cur[t], sdw[t], selA, selB), acc[t]);
-  if constexpr (J + 1 < KB / 8) sk_mma_step_lines<NV, KB, NT, J + 1, A16>(arow, r, m, g, sdw, selA, selB, acc, cur);
+  for (int t = 0; t < NT; ++t) acc[t] = mfma_ab<A16>(a, dec_piece_sp<NV, KB, J, A16>(cur[t], sp[t]), acc[t]);
+  if constexpr (J + 1 < KB / 8) sk_mma_step_lines<NV, KB, NT, J + 1, A16>(arow, r, m, g, sp, acc, cur);
 }
 
 template <bool NV, bool G1, int KB, int NT, bool A16 = false, int DEPTH = 1>
@@ -735,6 +748,7 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
   uint4 cur[NT];                                 // the current piece of every tile in the MFMA lane layout
   SRegs<KB> sc[NT];
   uint32_t sdw[NT][kSV > 0 ? kSV : 1];
+  h2v sp[NT][kSV > 0 ? kSV : 1];  // NVFP4: this lane's two FP16 block scales of each scale dword
 #pragma unroll
   for (int j = 0; j < NT; ++j) b_load_lines(trow[j], cbytes, lane, b0[j]);
   if constexpr (DEPTH > 1) {
@@ -754,7 +768,14 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
   {                                                                                                    \
     if constexpr (NV) {                                                                                \
       const int gi = (ST) & 3;                                                                         \
-      _Pragma("unroll") for (int j = 0; j < NT; ++j) s_fetch<KB>(sc[j], (m + 16 * gi) * 4, ghi, sdw[j]); \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                  \
+        s_fetch<KB>(sc[j], (m + 16 * gi) * 4, ghi, sdw[j]);                                            \
+        _Pragma("unroll") for (int q = 0; q < kSV; ++q) {                                              \
+          const h2v p01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sdw[j][q], 1.0f, false);            \
+          const h2v p23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sdw[j][q], 1.0f, true);             \
+          sp[j][q] = (g & 1) ? p23 : p01;                                                              \
+        }                                                                                              \
+      }                                                                                                \
       if (gi == 3 && (ST) + 1 < nsteps) { /* the next line: span of super-step ST + 1 + g per group */ \
         _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                \
           s_load<KB>(srow[j] + (int64_t)((ST) + 1) * sstep, (ST) + 1 + g < nsteps, sc[j]);             \
@@ -764,7 +785,7 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
       _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                  \
         b_load_lines(trow[j] + ((ST) + DEPTH) * (int64_t)cstep, cbytes, lane, BN[j]);                  \
     }                                                                                                  \
-    sk_mma_step_lines<NV, KB, NT, 0, A16>(arow + ((ST) - c0) * KS, BC, m, g, sdw, selA, selB, acc, cur); \
+    sk_mma_step_lines<NV, KB, NT, 0, A16>(arow + ((ST) - c0) * KS, BC, m, g, sp, acc, cur);           \
   }
   for (int c0 = 0; c0 < nsteps; c0 += kc) {
     const int c1 = c0 + kc < nsteps ? c0 + kc : nsteps;
