@@ -1279,6 +1279,9 @@ __global__ __launch_bounds__(256, 3) void k_gemm_wide(const _Float16* __restrict
 // 8q + 4 (l / 32) + j, column l % 32.
 // ---------------------------------------------------------------------------
 constexpr int kGBM = 128, kGBN = 256, kGBK = 64;
+// Fourth word of a raw buffer descriptor (stride 0, byte offsets): 32-bit data format, as the buffer
+// instructions of gfx9-family GPUs expect; records up to 2^31 bytes from the base, far beyond one expert.
+constexpr int kBufDword3 = 0x00020000;
 template <int N>
 struct IntC {
   static constexpr int value = N;
@@ -1353,16 +1356,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
     return (int64_t)e * H + c0 + r;
   };
   const int64_t cbytes = NV ? K / 2 : K;
-  // weight rows as 32-bit byte offsets from the tile's first row (within one expert)
-  const uint8_t* bbase = wc + wrow_of(0) * cbytes + 16 * bpart;
+  // Weight (and scale) loads are buffer loads: a descriptor of the tile's first weight row (uniform), a
+  // 32-bit per-lane byte offset (within one expert) and the K step's offset in a scalar register, so no
+  // vector instruction computes an address inside the K loop.
+  const uint8_t* bbase = wc + wrow_of(0) * cbytes;
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bbase), (short)0,
+                                                                       0x7FFFFFFF, kBufDword3);
   auto boff_of = [&](int i) -> uint32_t {
-    return (uint32_t)((wrow_of((256 / kBP) * i + tid / kBP) - wrow_of(0)) * cbytes);
+    return (uint32_t)((wrow_of((256 / kBP) * i + tid / kBP) - wrow_of(0)) * cbytes + 16 * bpart);
   };
   uint32_t bo[kBI];
 #pragma unroll
   for (int i = 0; i < kBI; ++i) bo[i] = boff_of(i);
   // scale bytes: thread tid holds weight row tid; 16 bytes (the 4 K steps of a group) per load
-  const uint8_t* ssrc = NV ? wsc + wrow_of(tid) * (K / 16) : nullptr;
+  const uint8_t* sbase = NV ? wsc + wrow_of(0) * (K / 16) : wc;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sbase), (short)0,
+                                                                       0x7FFFFFFF, kBufDword3);
+  const uint32_t soff = NV ? (uint32_t)((wrow_of(tid) - wrow_of(0)) * (K / 16)) : 0u;
 
   uint4 ra0, ra1, ra2, ra3, rb[kBI], sc4 = make_uint4(0, 0, 0, 0);
   auto aload = [&](int s, _Float16* __restrict__ wr) {  // activations of K step s (into LDS tile wr)
@@ -1379,10 +1389,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
     }
   };
   auto bload = [&](int s) {  // weight codes (and NVFP4 scale bytes) of the group that starts at K step s
-    const uint8_t* bs = bbase + s * kSB;
 #pragma unroll
-    for (int i = 0; i < kBI; ++i) rb[i] = *reinterpret_cast<const uint4*>(bs + bo[i]);
-    if constexpr (NV) sc4 = *reinterpret_cast<const uint4*>(ssrc + 4 * s);
+    for (int i = 0; i < kBI; ++i)
+      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brs, bo[i], s * kSB, 0));
+    if constexpr (NV) sc4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(srs, soff, 4 * s, 0));
   };
   auto bstore = [&]() {  // weight registers of a group into the group buffer, scale dwords by K step
 #pragma unroll
