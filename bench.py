@@ -294,7 +294,9 @@ def run_steps(cfg, fmt, x, wr, weights, steps, warmup, copies=None):
     GEMM (its per-launch duration, for the roofline) on its launch stream.  A
     second, untimed pass records every stage boundary for the per-stage
     breakdown (each recorded event costs a few microseconds of GPU time).
-    Returns (ms per step, per-stage ms, gate/up GEMM ms in the timed pass, counts).
+    Returns (ms per step, per-stage ms, gate/up GEMM ms in the timed pass, counts); the per-stage
+    dict also carries ``host_submit``, the host time per timed step spent submitting the work (a step
+    whose GPU time is close to it is bound by the host).
     """
     T = x.shape[0]
     out = torch.empty((T, cfg.H), dtype=torch.float32, device=x.device)
@@ -323,9 +325,11 @@ def run_steps(cfg, fmt, x, wr, weights, steps, warmup, copies=None):
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
+    h0 = time.perf_counter()
     for i in range(steps):
         bsm.set_stage_events(0, [None, ev.ev[2 * i], ev.ev[2 * i + 1], None, None, None])
         ids = step()
+    host_ms = (time.perf_counter() - h0) * 1e3 / steps
     stop.record()
     torch.cuda.synchronize()
     bsm.set_stage_events(0, [])
@@ -354,7 +358,9 @@ def run_steps(cfg, fmt, x, wr, weights, steps, warmup, copies=None):
         stages["combine"].append(ev.ms(b + 4, b + 5))
     ev.close()
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=cfg.E)
-    return total_ms / steps, {k: float(np.mean(v)) for k, v in stages.items()}, g1_ms, counts
+    stage_ms = {k: float(np.mean(v)) for k, v in stages.items()}
+    stage_ms["host_submit"] = host_ms  # host time to submit one timed step (not a GPU stage)
+    return total_ms / steps, stage_ms, g1_ms, counts
 
 
 def layer_numbers(cfg, fmt, T, ms, stage_ms, g1_ms, counts):

@@ -42,6 +42,9 @@
 //                 exact partials, which k_fin_i8 adds and rounds
 //   k_select256   256 experts: the same selection, one wave per token with
 //                 four experts per lane and shuffles in place of LDS.
+//   k_select256_fin  256 experts, bf16 x and w at small batches: k_fin_i8's
+//                 rounding, the exact recomputation of what it leaves
+//                 unproven, and k_select256's selection in one kernel
 
 #include "bsm_internal.h"
 
@@ -789,7 +792,7 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
   const int tid = threadIdx.x, lane = tid & 63;
   if (blockIdx.x == 0 && tid < 4) {  // the list filled by k_logits_i8; the selection kernel's counters
     if (tid == 0) *ulist = 0;
-    else diag[tid] = 0;
+    diag[tid] = 0;
   }
   __shared__ uint32_t s_mx[4];
   __shared__ double s_res[4];
@@ -1218,25 +1221,12 @@ __device__ inline void top2_merge(float& a1, float& a2, float b1, float b2) {
   a2 = n2;
 }
 
-__global__ __launch_bounds__(64 * kSel4Tokens) void k_select256(
-    const float* __restrict__ logits, int64_t T, int lpg, int topk_group, int topk, int32_t* __restrict__ ids,
-    float* __restrict__ wts, float* __restrict__ scores, const int* __restrict__ blk, int64_t nblk,
-    int* __restrict__ diag) {
+// The selection of token t by one wave from its 256 logits, four consecutive experts per lane (l4).
+__device__ inline void select256_wave(float4 l4, int64_t t, int lpg, int topk_group, int topk,
+                                      int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ scores,
+                                      int* __restrict__ diag) {
   constexpr int64_t E = 256;
-  __shared__ int s_cnt;
-  const int tid = threadIdx.x, lane = tid & 63;
-  if (blockIdx.x == 0) {  // diagnostics: exact recomputations of all logits workgroups
-    if (tid == 0) s_cnt = 0;
-    __syncthreads();
-    int c = 0;
-    for (int64_t i = tid; i < nblk; i += 64 * kSel4Tokens) c += blk[i];
-    if (c) atomicAdd(&s_cnt, c);
-    __syncthreads();
-    if (tid == 0) diag[0] = s_cnt;
-  }
-  const int64_t t = (int64_t)blockIdx.x * kSel4Tokens + (tid >> 6);
-  if (t >= T) return;  // whole waves leave; no barrier follows
-  const float4 l4 = *reinterpret_cast<const float4*>(logits + t * E + 4 * lane);
+  const int lane = threadIdx.x & 63;
   bool f0, f1, f2, f3;
   float sv[4] = {sigmoid_f32_exact(l4.x, &f0), sigmoid_f32_exact(l4.y, &f1), sigmoid_f32_exact(l4.z, &f2),
                  sigmoid_f32_exact(l4.w, &f3)};
@@ -1293,6 +1283,78 @@ __global__ __launch_bounds__(64 * kSel4Tokens) void k_select256(
     ids[t * topk + lane] = my_id;
     wts[t * topk + lane] = my_s / ssum;
   }
+}
+
+__global__ __launch_bounds__(64 * kSel4Tokens) void k_select256(
+    const float* __restrict__ logits, int64_t T, int lpg, int topk_group, int topk, int32_t* __restrict__ ids,
+    float* __restrict__ wts, float* __restrict__ scores, const int* __restrict__ blk, int64_t nblk,
+    int* __restrict__ diag) {
+  constexpr int64_t E = 256;
+  __shared__ int s_cnt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (blockIdx.x == 0) {  // diagnostics: exact recomputations of all logits workgroups
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    int c = 0;
+    for (int64_t i = tid; i < nblk; i += 64 * kSel4Tokens) c += blk[i];
+    if (c) atomicAdd(&s_cnt, c);
+    __syncthreads();
+    if (tid == 0) diag[0] = s_cnt;
+  }
+  const int64_t t = (int64_t)blockIdx.x * kSel4Tokens + (tid >> 6);
+  if (t >= T) return;  // whole waves leave; no barrier follows
+  select256_wave(*reinterpret_cast<const float4*>(logits + t * E + 4 * lane), t, lpg, topk_group, topk, ids, wts,
+                 scores, diag);
+}
+
+// bf16 router on the int8 matrix cores with K cut into splits (small batches), 256 experts: the
+// selection kernel also finishes the logits, in place of the finalize and exact-list kernels.  One
+// token per workgroup: thread e adds the splits' exact partials of logit (t, e) in int64 and rounds them
+// once (the arithmetic of k_fin_i8).  Logits whose rounding the bound left unproven (NaN) are then
+// recomputed exactly by the whole workgroup, one after another (exact_logit_wg), and counted in
+// diag[0]; then wave 0 selects.  (At large batches the exact recomputation stays in k_exact_list: its
+// slow path needs per-lane scratch, which would limit how many selection workgroups run at once.)
+__global__ __launch_bounds__(256) void k_select256_fin(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int64_t H,
+    const int64_t* __restrict__ spart, int64_t s8, const int* __restrict__ rexp, const double* __restrict__ rres,
+    const double* __restrict__ norm, float* __restrict__ logits, int lpg, int topk_group, int topk,
+    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ scores, int* __restrict__ diag) {
+  constexpr int64_t E = 256;
+  __shared__ __attribute__((aligned(16))) float s_log[E];
+  __shared__ int s_list[E];
+  __shared__ int s_n;
+  __shared__ ExactLds xl;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t t = blockIdx.x, e = tid;
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  int64_t hi = 0, lo = 0;
+#pragma unroll 8
+  for (int64_t z = 0; z < s8; ++z) {  // unrolled: the loads of 8 splits are in flight together
+    const int64_t* pz = spart + 2 * ((z * T + t) * E + e);
+    hi += pz[0];
+    lo += pz[1];
+  }
+  const float r = i8_round(hi, lo, rexp[t], rexp[T + e], rres[t], rres[T + e]);
+  s_log[e] = r;
+  logits[t * E + e] = r;
+  if (r != r) s_list[atomicAdd(&s_n, 1)] = (int)e;
+  __syncthreads();
+  const int n = s_n;  // the same in every thread
+  for (int u = 0; u < n; ++u) {
+    const int ee = s_list[u];
+    const float v = exact_logit_wg<true, true, 256>(x, w, t, ee, H, abs_bound(norm[t], norm[T + ee]), &xl);
+    if (tid == 0) {
+      s_log[ee] = v;
+      logits[t * E + ee] = v;
+    }
+  }
+  if (n) {
+    if (tid == 0) atomicAdd(&diag[0], n);
+    __syncthreads();
+  }
+  if (tid >= 64) return;  // wave 0 selects; no barrier follows
+  select256_wave(*reinterpret_cast<const float4*>(&s_log[4 * lane]), t, lpg, topk_group, topk, ids, wts, scores, diag);
 }
 
 void launch_slice8(const uint16_t* x, const uint16_t* w, int64_t T, int64_t E, int64_t H, int64_t ncp, int8_t* dig,
@@ -1366,6 +1428,17 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   const bool sel4 = E == 256 && (E / n_group) % 4 == 0 && topk <= 64 &&
                     ((uintptr_t)scores & 15) == 0;
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
+  if (i8 && L.rb && sel4) { /* the selection kernel finishes the logits */                                  \
+    launch_slice8(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), T, E, H, L.ncp,  \
+                  dig, rexp, rres, norm, ulist, diag, st);                                                 \
+    k_logits_i8<true><<<dim3(gl.x * gl.y, (unsigned)L.s8), 256, 0, st>>>(dig, T, E, L.ncp, L.sps8, rexp,     \
+                                                                         rres, logits, ulist, blk, spart); \
+    stage_mark(1, 1, st);                                                                                  \
+    k_select256_fin<<<(unsigned)T, 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x),                      \
+                                                 reinterpret_cast<const uint16_t*>(w), T, H, spart, L.s8, rexp, \
+                                                 rres, norm, logits, (int)(E / n_group) / 4, topk_group,   \
+                                                 topk, ids, wts, scores, diag);                            \
+  } else {                                                                                                 \
   if (i8 && L.rb) {                                                                                        \
     launch_slice8(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), T, E, H, L.ncp,  \
                   dig, rexp, rres, norm, ulist, diag, st);                                                 \
@@ -1397,7 +1470,8 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
         logits, T, (int)(E / n_group) / 4, topk_group, topk, ids, wts, scores, blk, nblk_used, diag);          \
   else                                                                                                     \
     k_select<<<(unsigned)T, kSelThreads, 0, st>>>(logits, E, n_group, topk_group, topk, ids, wts, scores,     \
-                                                  blk, nblk_used, diag);
+                                                  blk, nblk_used, diag);                                    \
+  }
   if (xb && wb) {
     BSM_ROUTE_DISPATCH(true, true)
   } else if (xb && !wb) {
