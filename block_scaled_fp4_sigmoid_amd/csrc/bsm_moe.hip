@@ -33,7 +33,10 @@
 //   k_perm_rows    row of every (token, slot) pair; rows of an expert are in
 //                  token order (stable)
 //   k_perm_small   all three in one workgroup when the batch is one chunk
-//   k_decode_act   activation codes -> FP16 q * s_b (once per call)
+//   k_decode_act   activation codes -> FP16 q * s_b (once per call), where a
+//                  GEMM reads FP16 activations: NVFP4 gate/up with many-row
+//                  experts, K not a multiple of the few-row super-step
+//                  (k_skinny), the dense FP8 linear
 //   k_skinny_rows<G1> (k_skinny<G1> when K is not a multiple of the super-step)
 //                  gate/up for 16-row tiles: epilogue h = silu(g) * u (FP32)
 //                  to the workspace, max |h| into one atomicMax word (order
@@ -41,8 +44,9 @@
 //   k_gemm_big<G1> the same for 128-row tiles (128 x 256 per workgroup,
 //                  32x32x16 MFMA; k_gemm_wide is the 16x16x32 fallback)
 //   k_dense_f8<G1> FP8 with one expert and at most 64 rows (dense layers)
-//   h quantize     NVFP4 with one global scale over all rows / FP8 per row,
-//                  plus the FP16 decoded copy the down GEMM reads
+//   h quantize     NVFP4 with one global scale over all rows / FP8 per row
+//                  (plus an FP16 decoded copy only for k_skinny and k_gemm_wide,
+//                  the fallbacks for I not a multiple of 512 or 256)
 //   k_skinny_rows<!G1> / k_skinny<!G1>, k_gemm_big<!G1> (k_gemm_wide when
 //                  I % 256 != 0): down projection -> y (FP32)
 //   k_combine      out[t] = scale * sum_j w[t,j] * y[row(t,j)] (binary64 sum
@@ -1299,14 +1303,15 @@ __device__ inline f16v mfma32(h8v a, h8v b, f16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-template <bool NV, bool G1, bool A16 = false>
+template <bool NV, bool G1, bool A16 = false, bool QA = false>
 __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict__ act, const int* __restrict__ row_pair,
                                                      int topk, const float* __restrict__ a_gs,
                                                      const float* __restrict__ a_rs, const uint8_t* __restrict__ wc,
                                                      const uint8_t* __restrict__ wsc, const float* __restrict__ wgs,
                                                      const int4* __restrict__ tiles, const int* __restrict__ ntiles,
                                                      int64_t K, int64_t H, int64_t I, float* __restrict__ out,
-                                                     uint32_t* __restrict__ h_amax) {
+                                                     uint32_t* __restrict__ h_amax, const uint8_t* __restrict__ acodes,
+                                                     const uint8_t* __restrict__ ascales) {
   constexpr int kBRow = BigB<NV>::kRow;
   // Weights come in groups of GS K steps, 128 code bytes per row (one cache line, loaded by 8 lanes;
   // NVFP4 4 steps with K % 256 == 0, FP8 2 steps with K % 128 == 0), into one LDS buffer that the
@@ -1319,8 +1324,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   // bytes at base + 16 l, so a load fills 8 whole 128-byte rows): unpadded rows, 16-byte chunk c of
   // row r stored at chunk c ^ ((r >> 1) & 7), which keeps the fragment reads of 16 consecutive rows
   // on distinct banks.  FP8 (measured slower that way) stages it through registers into padded rows.
+  // QA: the tile is staged from the activation codes (NVFP4 codes and block scales, FP8 codes; acodes,
+  // ascales) and decoded to FP16 on the way into LDS, through registers: thread t takes 32 values of row
+  // t / 2, so no FP16 copy of the activations is read (or written before).
   // Two separate arrays, so the compiler sees that loads into one do not alias reads of the other.
-  constexpr bool kAdma = NV;
+  constexpr bool kAdma = NV && !QA;
   constexpr int kAS = kAdma ? kGBK : kGBK + 8;  // LDS row stride (f16)
   __shared__ __attribute__((aligned(16))) _Float16 As0[kGBM][kAS];
   __shared__ __attribute__((aligned(16))) _Float16 As1[kGBM][kAS];
@@ -1349,7 +1357,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
     const int c = kAdma ? (lane & 7) ^ ((r >> 1) & 7) : apart;
     return (G1 ? act + (int64_t)(row_pair[row0 + ar] / topk) * K : act + (int64_t)(row0 + ar) * K) + 8 * c;
   };
-  const _Float16 *as0 = arow(0), *as1 = arow(1), *as2 = arow(2), *as3 = arow(3);
+  const _Float16 *as0 = QA ? nullptr : arow(0), *as1 = QA ? nullptr : arow(1), *as2 = QA ? nullptr : arow(2),
+                 *as3 = QA ? nullptr : arow(3);
+  // QA: row qr = tid / 2, values 32 qh .. +31 of each K step (qh = tid % 2)
+  const int qr = tid >> 1, qh = tid & 1;
+  const uint8_t *qc = nullptr, *qs = nullptr;
+  if constexpr (QA) {
+    const int ar = qr < nrows ? qr : nrows - 1;
+    const int64_t ri = G1 ? (int64_t)(row_pair[row0 + ar] / topk) : (int64_t)(row0 + ar);
+    qc = acodes + ri * (NV ? K / 2 : K) + (NV ? 16 : 32) * qh;
+    qs = NV ? ascales + ri * (K / 16) : nullptr;
+  }
+  uint4 qa0 = make_uint4(0, 0, 0, 0), qa1 = make_uint4(0, 0, 0, 0);
+  uint32_t qsw = 0;
   // weight row r of the tile: GEMM1 gate rows c0.. then the matching up rows
   auto wrow_of = [&](int r) -> int64_t {
     if (G1) return (int64_t)e * 2 * I + (r < kGBN / 2 ? c0 + r : I + c0 + (r - kGBN / 2));
@@ -1376,7 +1396,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
 
   uint4 ra0, ra1, ra2, ra3, rb[kBI], sc4 = make_uint4(0, 0, 0, 0);
   auto aload = [&](int s, _Float16* __restrict__ wr) {  // activations of K step s (into LDS tile wr)
-    if constexpr (kAdma) {
+    if constexpr (QA) {
+      (void)wr;
+      if constexpr (NV) {
+        qa0 = *reinterpret_cast<const uint4*>(qc + (int64_t)s * (kGBK / 2));
+        qsw = *reinterpret_cast<const uint32_t*>(qs + (int64_t)s * (kGBK / 16));
+      } else {
+        qa0 = *reinterpret_cast<const uint4*>(qc + (int64_t)s * kGBK);
+        qa1 = *reinterpret_cast<const uint4*>(qc + (int64_t)s * kGBK + 16);
+      }
+    } else if constexpr (kAdma) {
       __builtin_amdgcn_global_load_lds(as0 + s * kGBK, wr + (32 * wave) * kGBK, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(as1 + s * kGBK, wr + (32 * wave + 8) * kGBK, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(as2 + s * kGBK, wr + (32 * wave + 16) * kGBK, 16, 0, 0);
@@ -1414,7 +1443,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   // complete in issue order); the barrier after it publishes every wave's rows.  Through
   // registers: the activation registers into LDS tile buf.
   auto lstore = [&](int buf, int n) {
-    if constexpr (kAdma) {
+    if constexpr (QA) {  // decode the row's 32 values: NVFP4 two blocks (scale bytes 2 qh, 2 qh + 1)
+      (void)n;
+      uint4 o[4];
+      if constexpr (NV) {
+        const uint32_t sa = (uint32_t)(2 * qh) * 0x0101u, sb = sa + 0x0101u;
+        const h2v s2a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(qsw, qsw, sa), 1.0f, false);
+        const h2v s2b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(qsw, qsw, sb), 1.0f, false);
+        o[0] = __builtin_bit_cast(uint4, dec_fp4x8(qa0.x, s2a));
+        o[1] = __builtin_bit_cast(uint4, dec_fp4x8(qa0.y, s2a));
+        o[2] = __builtin_bit_cast(uint4, dec_fp4x8(qa0.z, s2b));
+        o[3] = __builtin_bit_cast(uint4, dec_fp4x8(qa0.w, s2b));
+      } else {
+        o[0] = __builtin_bit_cast(uint4, dec_fp8x8(qa0.x, qa0.y));
+        o[1] = __builtin_bit_cast(uint4, dec_fp8x8(qa0.z, qa0.w));
+        o[2] = __builtin_bit_cast(uint4, dec_fp8x8(qa1.x, qa1.y));
+        o[3] = __builtin_bit_cast(uint4, dec_fp8x8(qa1.z, qa1.w));
+      }
+      uint4* d = reinterpret_cast<uint4*>(Ab[buf] + qr * kAS + 32 * qh);
+      d[0] = o[0];
+      d[1] = o[1];
+      d[2] = o[2];
+      d[3] = o[3];
+    } else if constexpr (kAdma) {
       if (n == 0)
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited for
       else
@@ -1926,10 +1977,16 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   _Float16* hdec = reinterpret_cast<_Float16*>(ws + L.h_f16);
   const int64_t xblk = a.T * a.H / 16;
   const unsigned gx = (unsigned)((xblk + 255) / 256);
-  // Without many-row experts the few-row kernels stage their rows from the codes: x is not decoded to FP16
-  // first (qa1), and the h quantization writes no FP16 copy of h (qa2).
+  // The GEMMs stage their activation rows from the codes (the few-row kernels when K is a multiple of their
+  // super-step; k_gemm_big): x is not decoded to FP16 first (qa1), and the h quantization writes no FP16
+  // copy of h (qa2; not when the down projection of many-row experts falls back to k_gemm_wide).  NVFP4
+  // gate/up with many-row experts keeps the FP16 copy of x, which k_gemm_big stages with direct-to-LDS
+  // loads: staging x from its codes measured slower there (prefill-8192 gate/up 2.99 -> 3.11 ms, against
+  // 0.02 ms saved by not decoding x).  The NVFP4 down projection went 1.59-1.62 -> 1.60-1.67 ms and the h
+  // quantization 0.19-0.21 -> 0.15 ms without the FP16 copy (layer unchanged within the spread of runs);
+  // FP8: gate/up 3.55 -> 3.43 ms, down 1.85 -> 1.75 ms, layer 6.30 -> 6.01 ms.
   const int64_t ks_vals = 4 * (a.nvfp4 ? kNvKB : kF8KB);  // k_skinny_rows super-step
-  const bool qa1 = !many && a.H % ks_vals == 0, qa2 = !many && a.I % ks_vals == 0;
+  const bool qa1 = a.H % ks_vals == 0 && (!many || !a.nvfp4), qa2 = a.I % ks_vals == 0 && (!many || big_dn);
   if (a.a16)
     act = reinterpret_cast<_Float16*>(const_cast<uint8_t*>(a.x_codes));  // BF16 x, read as 16-bit containers
   else if (a.nvfp4 && !qa1)
@@ -1958,9 +2015,13 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     k_skinny<NV, true, 32, kSkNT, false, NV ? 1 : kSkDepthF8><<<g1, 256, 0, st>>>(                             \
         act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32,  \
         h_amax);                                                                                               \
-  if (many)                                                                                                    \
+  if (many && qa1)                                                                                             \
+    k_gemm_big<NV, true, false, true><<<w1, 256, 0, st>>>(nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, \
+                                                          w13s, a.w13_gs, tiles_w, ntiles_w, a.H, a.H, a.I,    \
+                                                          h_f32, h_amax, a.x_codes, NV ? xsb : nullptr);       \
+  else if (many)                                                                                               \
     k_gemm_big<NV, true><<<w1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, \
-                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax)
+                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax, nullptr, nullptr)
 #define BSM_G2(NV, HSC)                                                                                        \
   if (qa2)                                                                                                     \
     k_skinny_rows<NV, false, kSkNT, false, NV ? 1 : kSkDepthF8, true><<<g2, 256, 0, st>>>(                     \
@@ -1973,9 +2034,16 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   else                                                                                                         \
     k_skinny<NV, false, 32, kSkNT, false, NV ? 1 : kSkDepthF8><<<g2, 256, 0, st>>>(                            \
         hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I, a.H, a.I, y, h_amax); \
-  if (many)                                                                                                    \
-    (big_dn ? k_gemm_big<NV, false> : k_gemm_wide<NV, false>)<<<w2, 256, 0, st>>>(                             \
-        hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
+  if (many && qa2)                                                                                             \
+    k_gemm_big<NV, false, false, true><<<w2, 256, 0, st>>>(nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes,  \
+                                                           w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y,  \
+                                                           h_amax, h_codes, NV ? h_scales : nullptr);          \
+  else if (many && big_dn)                                                                                     \
+    k_gemm_big<NV, false><<<w2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs,     \
+                                              tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax, nullptr, nullptr);  \
+  else if (many)                                                                                               \
+    k_gemm_wide<NV, false><<<w2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs,    \
+                                               tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
   hipError_t err;
   if (a.a16) {
     // weight-only W4A16: BF16 activations, NVFP4 weights decoded to BF16, h rounded to BF16
@@ -1987,9 +2055,12 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   else                                                                                                         \
     k_skinny<true, G, 32, kSkNT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS,     \
                                                              tiles, ntiles, K, a.H, a.I, OUT, h_amax);         \
-  if (many)                                                                                                    \
-    ((G || big_dn) ? k_gemm_big<true, G, true> : k_gemm_wide<true, G, true>)<<<WGRID, 256, 0, st>>>(           \
-        A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w, ntiles_w, K, a.H, a.I, OUT, h_amax)
+  if (many && (G || big_dn))                                                                                   \
+    k_gemm_big<true, G, true><<<WGRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,    \
+                                                     ntiles_w, K, a.H, a.I, OUT, h_amax, nullptr, nullptr);    \
+  else if (many)                                                                                               \
+    k_gemm_wide<true, G, true><<<WGRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,   \
+                                                      ntiles_w, K, a.H, a.I, OUT, h_amax)
     BSM_A16_G(true, act, xrs, a.w13_codes, w13s, a.w13_gs, h_f32, g1, w1, a.H);
     stage_mark(0, 2, st);
     const int64_t n4 = L.P * a.I / 4;
