@@ -719,8 +719,23 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
   constexpr int cstep = NV ? KS / 2 : KS, sstep = KS / 16;  // code (NVFP4: and scale) bytes per row and super-step
   constexpr int kU = DEPTH + 1;  // super-steps per unrolled iteration (one per register set)
   __shared__ __attribute__((aligned(16))) _Float16 Ar[kRowsLds / 2];
-  if ((int)blockIdx.y >= *ntiles) return;
-  const int4 ti = tiles[blockIdx.y];
+  // Gate/up: workgroup i runs on XCD i % 8 (the dispatcher deals workgroups out round robin), so the live
+  // workgroups are renumbered to give each XCD one contiguous run of (row tile, column block) items in
+  // column order.  The column blocks of a row tile then run on one XCD at about the same time, and its
+  // L2 fetches the tile's activation rows once instead of once per XCD and again after eviction.
+  int bx = (int)blockIdx.x, by = (int)blockIdx.y;
+  if constexpr (G1) {
+    const int gx = (int)gridDim.x, live = *ntiles * gx, lin = by * gx + bx;
+    if (lin >= live) return;
+    int pre = 0;  // live workgroups on the XCDs before this one: those with index i (mod 8), i < lin % 8
+    for (int i = 0; i < (lin & 7); ++i) pre += (live - i + 7) >> 3;
+    const int q = pre + (lin >> 3);
+    by = q / gx;
+    bx = q - by * gx;
+  } else {
+    if (by >= *ntiles) return;
+  }
+  const int4 ti = tiles[by];
   const int e = ti.x, row0 = ti.y, nrows = ti.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, g = lane >> 4;
@@ -732,7 +747,7 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
   const int rstride = kc * KS + 8;  // f16
   // this lane's A row (rows past nrows read the last real row: their outputs are never stored)
   const _Float16* arow = Ar + (m < nrows ? m : nrows - 1) * rstride + VPU * g;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * (G1 ? 8 * NT : 16 * NT);
+  const int64_t n0 = ((int64_t)bx * 4 + wave) * (G1 ? 8 * NT : 16 * NT);
   const int64_t cbytes = NV ? K / 2 : K;
   const uint8_t* trow[NT];  // first weight row of each tile (its 16 rows are consecutive)
   const uint8_t* srow[NT];
