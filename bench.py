@@ -270,7 +270,8 @@ def build_layer(cfg, fmt, dev):
     x = torch.from_numpy(W.activations(cfg)).to(dev, torch.bfloat16)
     wr = torch.from_numpy(W.router_weights(cfg)).to(dev, torch.bfloat16)
     w13, w2 = W.expert_weights_device(cfg, device=dev)
-    weights = bsm.quantize_expert_weights(w13, w2, "fp8" if fmt == "fp8" else "nvfp4")
+    # quantized offline, then the codes put in the pair layout the expert GEMMs read directly (same codes)
+    weights = bsm.to_pair_layout(bsm.quantize_expert_weights(w13, w2, "fp8" if fmt == "fp8" else "nvfp4"))
     torch.cuda.synchronize()
     return x, wr, w13, w2, weights
 
@@ -512,7 +513,7 @@ def stack_numbers(dev, steps, warmup):
         for li in range(cfg.layers):
             w13, w2 = W.expert_weights_device(cfg, layer=li, device=dev)
             wr = torch.from_numpy(W.router_weights(cfg, layer=li)).to(dev, torch.bfloat16)
-            layers.append((wr, bsm.quantize_expert_weights(w13, w2, fmt)))
+            layers.append((wr, bsm.to_pair_layout(bsm.quantize_expert_weights(w13, w2, fmt))))
             del w13, w2
             torch.cuda.empty_cache()
         for _ in range(warmup):

@@ -26,6 +26,7 @@ BSM_OK = 0
 BSM_BF16, BSM_F32 = 1, 2
 FMT_NVFP4, FMT_FP8, FMT_W4A16 = 1, 2, 3
 GS_DYNAMIC, GS_STATIC = 0, 1
+LAYOUT_ROWS, LAYOUT_PAIRS = 0, 1
 
 _lib = None
 
@@ -37,7 +38,8 @@ class BsmError(RuntimeError):
 class _MoeWeights(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int), ("E", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
                 ("w13_codes", ctypes.c_void_p), ("w13_scales", ctypes.c_void_p), ("w13_gs", ctypes.c_void_p),
-                ("w2_codes", ctypes.c_void_p), ("w2_scales", ctypes.c_void_p), ("w2_gs", ctypes.c_void_p)]
+                ("w2_codes", ctypes.c_void_p), ("w2_scales", ctypes.c_void_p), ("w2_gs", ctypes.c_void_p),
+                ("layout", ctypes.c_int)]
 
 
 class _ActQ(ctypes.Structure):
@@ -79,6 +81,7 @@ def load():
         "bsm_moe_expert_mlp_noalloc": (i32, [ctypes.POINTER(_MoeWeights), ctypes.POINTER(_ActQ), i64, vp, vp, i32,
                                              f32, i32, vp, vp, vp]),
         "bsm_moe_expert_mlp_w4a16": (i32, [ctypes.POINTER(_MoeWeights), vp, i64, vp, vp, i32, f32, vp, vp, sz, vp]),
+        "bsm_codes_to_pairs": (i32, [vp, vp, i64, i64, vp]),
         "bsm_fp8_linear_workspace_size": (sz, [i64, i64, i64]),
         "bsm_fp8_linear": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         "bsm_set_stage_events": (i32, [i32, ctypes.POINTER(vp), i32]),
@@ -277,7 +280,8 @@ def route_diagnostics(ws, T, H, E):
 
 @dataclass
 class ExpertWeights:
-    """Quantized routed-expert weights in the library's canonical layout."""
+    """Quantized routed-expert weights: codes in the canonical row-major layout (``LAYOUT_ROWS``) or in the
+    pair layout (``LAYOUT_PAIRS``, from ``to_pair_layout``); the scales are row-major either way."""
     format: int
     E: int
     H: int
@@ -288,11 +292,35 @@ class ExpertWeights:
     w2_codes: torch.Tensor
     w2_scales: torch.Tensor
     w2_gs: Optional[torch.Tensor]
+    layout: int = LAYOUT_ROWS
 
     def _struct(self):
         return _MoeWeights(self.format, self.E, self.H, self.I, self.w13_codes.data_ptr(), self.w13_scales.data_ptr(),
                            None if self.w13_gs is None else self.w13_gs.data_ptr(), self.w2_codes.data_ptr(),
-                           self.w2_scales.data_ptr(), None if self.w2_gs is None else self.w2_gs.data_ptr())
+                           self.w2_scales.data_ptr(), None if self.w2_gs is None else self.w2_gs.data_ptr(),
+                           self.layout)
+
+
+def codes_to_pairs(codes: torch.Tensor) -> torch.Tensor:
+    """Pair layout of weight codes [..., rows, row_bytes] (uint8; rows a multiple of 16 in total, row_bytes of 64),
+    out of place: in every block of 16 rows, rows p and p + 8 share each 128-byte line, 64 bytes each."""
+    lib = load()
+    _dev(codes, "codes")
+    if codes.dtype != torch.uint8:
+        raise BsmError("codes must be uint8")
+    rb = codes.shape[-1]
+    rows = codes.numel() // rb if rb else 0
+    out = torch.empty_like(codes)
+    _check(lib.bsm_codes_to_pairs(_ptr(codes), _ptr(out), rows, rb, _stream()))
+    return out
+
+
+def to_pair_layout(w: "ExpertWeights") -> "ExpertWeights":
+    """The same weights with both code tensors in the pair layout (new tensors; scales shared)."""
+    if w.layout == LAYOUT_PAIRS:
+        return w
+    return ExpertWeights(w.format, w.E, w.H, w.I, codes_to_pairs(w.w13_codes), w.w13_scales, w.w13_gs,
+                         codes_to_pairs(w.w2_codes), w.w2_scales, w.w2_gs, LAYOUT_PAIRS)
 
 
 def quantize_expert_weights(w13: torch.Tensor, w2: torch.Tensor, fmt: str) -> ExpertWeights:

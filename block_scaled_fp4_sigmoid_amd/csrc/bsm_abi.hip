@@ -56,6 +56,20 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   return BSM_OK;
 }
 
+// Layout of the weight codes: the pair layout is read by the kernels that take a whole K step of the few-row
+// GEMM (NVFP4 and W4A16: 512 values, FP8: 256) and by the many-row GEMM with I % 256 == 0, not by the
+// fallbacks for other shapes or by the dense FP8 path (one expert, top-1, T <= 64).
+static int check_layout(const bsm_moe_weights* w, bool nv, bool a16, int64_t T, int topk) {
+  if (w->layout == BSM_LAYOUT_ROWS) return BSM_OK;
+  if (w->layout != BSM_LAYOUT_PAIRS) return fail(BSM_ERR_INVALID_ARG, "bad weight layout %d", w->layout);
+  const int64_t ks = nv ? 512 : 256;
+  if (w->H % ks != 0 || w->I % ks != 0 || w->I % 256 != 0)
+    return fail(BSM_ERR_UNSUPPORTED, "pair layout needs H and I multiples of %lld and I of 256", (long long)ks);
+  if (!nv && !a16 && w->E == 1 && topk == 1 && T <= 64)
+    return fail(BSM_ERR_UNSUPPORTED, "pair layout: not taken by the dense FP8 path (E = 1, topk = 1, T <= 64)");
+  return BSM_OK;
+}
+
 // Arguments of the routed-expert MLP, validated on the host (nothing is enqueued on error).  *empty:
 // T == 0, nothing to do.
 int moe_args(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T, const int32_t* topk_ids,
@@ -72,6 +86,7 @@ int moe_args(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T, const int
   if (topk < 1 || topk > 32 || topk > E) return fail(BSM_ERR_INVALID_ARG, "topk must be in [1, min(32, E)]");
   if (T * topk > 0x3FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "T * topk too large");
   if (h_gs_mode != BSM_GS_DYNAMIC && h_gs_mode != BSM_GS_STATIC) return fail(BSM_ERR_INVALID_ARG, "bad h_gs_mode");
+  if (int r = check_layout(w, nv, false, T, topk)) return r;
   if (nv && h_gs_mode == BSM_GS_STATIC && !h_global_scale)
     return fail(BSM_ERR_INVALID_ARG, "STATIC h global scale needs h_global_scale");
   *empty = T == 0;
@@ -105,6 +120,7 @@ int moe_args(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T, const int
   a->h_static = h_gs_mode == BSM_GS_STATIC;
   a->h_gs_user = h_global_scale;
   a->out = out;
+  a->pairs = w->layout == BSM_LAYOUT_PAIRS;
   return BSM_OK;
 }
 
@@ -341,6 +357,7 @@ int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w, const void* x, int64_t T,
   if (E > 1024) return fail(BSM_ERR_UNSUPPORTED, "E > 1024");
   if (topk < 1 || topk > 32 || topk > E) return fail(BSM_ERR_INVALID_ARG, "topk must be in [1, min(32, E)]");
   if (T * topk > 0x3FFFFFFF) return fail(BSM_ERR_UNSUPPORTED, "T * topk too large");
+  if (int r = check_layout(w, true, true, T, topk)) return r;
   if (T == 0) return ok();
   if (!w->w13_codes || !w->w13_scales || !w->w2_codes || !w->w2_scales || !w->w13_gs || !w->w2_gs || !x ||
       !topk_ids || !topk_weights || !out)
@@ -373,8 +390,20 @@ int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w, const void* x, int64_t T,
   a.h_static = false;
   a.h_gs_user = nullptr;
   a.out = out;
+  a.pairs = w->layout == BSM_LAYOUT_PAIRS;
   a.ws = reinterpret_cast<uint8_t*>(ws);
   return hip_status(bsm::launch_moe(a, (hipStream_t)stream), "bsm_moe_expert_mlp_w4a16");
+}
+
+int bsm_codes_to_pairs(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, bsm_stream_t stream) {
+  if (rows < 0 || row_bytes < 0 || rows % 16 != 0 || row_bytes % 64 != 0)
+    return fail(BSM_ERR_INVALID_ARG, "rows must be a multiple of 16 and row_bytes of 64");
+  if (rows == 0 || row_bytes == 0) return ok();
+  if (!in || !out) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(in, 16) || !aligned(out, 16)) return fail(BSM_ERR_INVALID_ARG, "in and out must be 16-byte aligned");
+  const uint8_t *ie = in + rows * row_bytes, *oe = out + rows * row_bytes;
+  if (in < oe && out < ie) return fail(BSM_ERR_INVALID_ARG, "in and out overlap");
+  return hip_status(bsm::launch_codes_to_pairs(in, out, rows, row_bytes, (hipStream_t)stream), "bsm_codes_to_pairs");
 }
 
 size_t bsm_fp8_linear_workspace_size(int64_t T, int64_t K, int64_t N) {

@@ -73,6 +73,7 @@ struct MoeArgs {
   const float* x_gs;
   const int32_t* ids;
   const float* wts;
+  bool pairs = false;  // weight codes in the pair layout (launch_codes_to_pairs)
   float combine_scale;
   bool h_static;
   float* h_gs_user;
@@ -80,6 +81,8 @@ struct MoeArgs {
   uint8_t* ws;
 };
 hipError_t launch_moe(const MoeArgs& a, hipStream_t st);
+// weight codes [rows, row_bytes] (rows % 16 == 0, row_bytes % 64 == 0) -> pair layout, out of place
+hipError_t launch_codes_to_pairs(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, hipStream_t st);
 
 // ---- dense FP8 linear ------------------------------------------------------
 size_t fp8_linear_ws(int64_t T, int64_t K, int64_t N);

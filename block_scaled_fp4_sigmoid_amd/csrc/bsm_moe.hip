@@ -387,6 +387,20 @@ __device__ inline void b_load_lines(const uint8_t* span, int64_t cbytes, int lan
   r.v[3] = nt_load16(p + 8 * cbytes + 128);
 }
 
+// Pair layout of the weight codes (bsm_codes_to_pairs): in every block of 16 rows, rows p and p + 8 (p < 8)
+// form one double row of 2 * cbytes bytes whose 128-byte lines hold 64 bytes of row p, then the same 64
+// bytes of row p + 8.  Lane (m, g) then loads its pieces of a super-step straight in the MFMA lane layout
+// (piece i: bytes i * 64 + g * 16 of row m's span, at byte offset soff of the row), and each load
+// instruction still covers 8 whole lines, one in each double row.  tile: the block's first byte.
+__device__ inline void b_load_pairs(const uint8_t* tile, int64_t cbytes, int64_t soff, int lane, Lines& r) {
+  const int m = lane & 15, g = lane >> 4;
+  const uint8_t* p = tile + (int64_t)(m & 7) * 2 * cbytes + 2 * soff + (m >> 3) * 64 + g * 16;
+  r.v[0] = nt_load16(p);
+  r.v[1] = nt_load16(p + 128);
+  r.v[2] = nt_load16(p + 256);
+  r.v[3] = nt_load16(p + 384);
+}
+
 // Piece i (0..3) of the lane layout of b_load from whole-line loads: lane (m, g) takes bytes i * 64 + g * 16
 // of row m, that is half i / 2, 16-byte piece (i % 2) * 4 + g of it, held by lane (m % 8) * 8 + (i % 2) * 4
 // + g in Lines.v[2 (m / 8) + i / 2].  Every lane takes both candidates with ds_bpermute and keeps its own.
@@ -493,20 +507,21 @@ __device__ inline h8v dec_piece_sp(uint4 c, const h2v* sp) {
 }
 
 // The same steps from whole-line loads: piece i of every tile is moved into the MFMA lane layout just
-// before its first step (4 registers per tile live instead of the whole super-step).
-template <bool NV, int KB, int NT, int J, bool A16>
+// before its first step (4 registers per tile live instead of the whole super-step).  PAIRS: the loads
+// already hold piece i in register i (pair layout), nothing is moved.
+template <bool NV, int KB, int NT, int J, bool A16, bool PAIRS>
 __device__ inline void sk_mma_step_lines(const _Float16* arow, const Lines* r, int m, int g,
                                          const h2v (*sp)[KB / 32 > 0 ? KB / 32 : 1], f4v* acc, uint4* cur) {
   constexpr int VPU = SkGeom<NV>::VPU, SPU = SkGeom<NV>::SPU;
   constexpr int col = (J / SPU) * 4 * VPU + (J % SPU) * 8;  // plus g * VPU, folded into arow
   if constexpr (J % SPU == 0) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) cur[t] = piece_from_lines(r[t], m, g, J / SPU);
+    for (int t = 0; t < NT; ++t) cur[t] = PAIRS ? r[t].v[J / SPU] : piece_from_lines(r[t], m, g, J / SPU);
   }
   const h8v a = *reinterpret_cast<const h8v*>(arow + col);
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = mfma_ab<A16>(a, dec_piece_sp<NV, KB, J, A16>(cur[t], sp[t]), acc[t]);
-  if constexpr (J + 1 < KB / 8) sk_mma_step_lines<NV, KB, NT, J + 1, A16>(arow, r, m, g, sp, acc, cur);
+  if constexpr (J + 1 < KB / 8) sk_mma_step_lines<NV, KB, NT, J + 1, A16, PAIRS>(arow, r, m, g, sp, acc, cur);
 }
 
 template <bool NV, bool G1, int KB, int NT, bool A16 = false, int DEPTH = 1>
@@ -705,7 +720,7 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny(const _Float
 // ---------------------------------------------------------------------------
 constexpr int kRowsLds = 44 * 1024;  // LDS bytes for the staged rows (three workgroups per CU)
 
-template <bool NV, bool G1, int NT, bool A16 = false, int DEPTH = 1, bool QA = false>
+template <bool NV, bool G1, int NT, bool A16 = false, int DEPTH = 1, bool QA = false, bool PAIRS = false>
 __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
     const _Float16* __restrict__ act, const uint8_t* __restrict__ acodes, const uint8_t* __restrict__ ascales,
     const int* __restrict__ row_pair, int topk, const float* __restrict__ a_gs,
@@ -769,11 +784,21 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
   uint32_t sdw[NT][kSV > 0 ? kSV : 1];
   h2v sp[NT][kSV > 0 ? kSV : 1];  // NVFP4: this lane's two FP16 block scales of each scale dword
 #pragma unroll
-  for (int j = 0; j < NT; ++j) b_load_lines(trow[j], cbytes, lane, b0[j]);
+  for (int j = 0; j < NT; ++j) {
+    if constexpr (PAIRS)
+      b_load_pairs(trow[j], cbytes, 0, lane, b0[j]);
+    else
+      b_load_lines(trow[j], cbytes, lane, b0[j]);
+  }
   if constexpr (DEPTH > 1) {
     if (nsteps > 1) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b_load_lines(trow[j] + cstep, cbytes, lane, b1[j]);
+      for (int j = 0; j < NT; ++j) {
+        if constexpr (PAIRS)
+          b_load_pairs(trow[j], cbytes, cstep, lane, b1[j]);
+        else
+          b_load_lines(trow[j] + cstep, cbytes, lane, b1[j]);
+      }
     }
   }
   if constexpr (NV) {
@@ -801,10 +826,14 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
       }                                                                                                \
     }                                                                                                  \
     if ((ST) + DEPTH < nsteps) {                                                                       \
-      _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                  \
-        b_load_lines(trow[j] + ((ST) + DEPTH) * (int64_t)cstep, cbytes, lane, BN[j]);                  \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                \
+        if constexpr (PAIRS)                                                                           \
+          b_load_pairs(trow[j], cbytes, ((ST) + DEPTH) * (int64_t)cstep, lane, BN[j]);                 \
+        else                                                                                           \
+          b_load_lines(trow[j] + ((ST) + DEPTH) * (int64_t)cstep, cbytes, lane, BN[j]);                \
+      }                                                                                                \
     }                                                                                                  \
-    sk_mma_step_lines<NV, KB, NT, 0, A16>(arow + ((ST) - c0) * KS, BC, m, g, sp, acc, cur);           \
+    sk_mma_step_lines<NV, KB, NT, 0, A16, PAIRS>(arow + ((ST) - c0) * KS, BC, m, g, sp, acc, cur);    \
   }
   for (int c0 = 0; c0 < nsteps; c0 += kc) {
     const int c1 = c0 + kc < nsteps ? c0 + kc : nsteps;
@@ -1326,7 +1355,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
                                                      const int4* __restrict__ tiles, const int* __restrict__ ntiles,
                                                      int64_t K, int64_t H, int64_t I, float* __restrict__ out,
                                                      uint32_t* __restrict__ h_amax, const uint8_t* __restrict__ acodes,
-                                                     const uint8_t* __restrict__ ascales) {
+                                                     const uint8_t* __restrict__ ascales, int pairs) {
   constexpr int kBRow = BigB<NV>::kRow;
   // Weights come in groups of GS K steps, 128 code bytes per row (one cache line, loaded by 8 lanes;
   // NVFP4 4 steps with K % 256 == 0, FP8 2 steps with K % 128 == 0), into one LDS buffer that the
@@ -1397,7 +1426,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   const uint8_t* bbase = wc + wrow_of(0) * cbytes;
   const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(bbase), (short)0,
                                                                        0x7FFFFFFF, kBufDword3);
+  // Pair layout (pairs != 0; 16-row blocks of double rows, see b_load_pairs): load i of lane tid takes the
+  // 16-byte part tid % 8 of line (256 i + tid) / 8 of the group, which holds 64 bytes of row p and then of
+  // row p + 8 of a 16-row block.  Its row in the tile is 32 i + brow0 and its bytes in the row's group
+  // bcol .. +15 (canonical rows: row 32 i + tid / 8, part tid % 8); the group of K step s starts at byte
+  // s * kSB of a row, at 2 s * kSB of a double row.
+  const int brow0 = pairs ? 16 * (tid >> 7) + ((tid >> 4) & 7) + (((tid & 7) >> 2) << 3) : tid / kBP;
+  const int bcol = pairs ? ((tid >> 3) & 1) * 64 + (tid & 3) * 16 : 16 * bpart;
+  const int smul = pairs ? 2 : 1;
   auto boff_of = [&](int i) -> uint32_t {
+    if (pairs)
+      return (uint32_t)((wrow_of(32 * i + 16 * (tid >> 7)) - wrow_of(0)) * cbytes + ((tid >> 4) & 7) * 2 * cbytes +
+                        ((tid >> 3) & 1) * 128 + ((tid & 7) >> 2) * 64 + (tid & 3) * 16);
     return (uint32_t)((wrow_of((256 / kBP) * i + tid / kBP) - wrow_of(0)) * cbytes + 16 * bpart);
   };
   uint32_t bo[kBI];
@@ -1435,13 +1475,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   auto bload = [&](int s) {  // weight codes (and NVFP4 scale bytes) of the group that starts at K step s
 #pragma unroll
     for (int i = 0; i < kBI; ++i)
-      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brs, bo[i], s * kSB, 0));
+      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brs, bo[i], s * kSB * smul, 0));
     if constexpr (NV) sc4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(srs, soff, 4 * s, 0));
   };
   auto bstore = [&]() {  // weight registers of a group into the group buffer, scale dwords by K step
 #pragma unroll
     for (int i = 0; i < kBI; ++i) {
-      uint32_t* d = reinterpret_cast<uint32_t*>(&Bg[(256 / kBP) * i + tid / kBP][16 * bpart]);
+      uint32_t* d = reinterpret_cast<uint32_t*>(&Bg[32 * i + brow0][bcol]);
       d[0] = rb[i].x;
       d[1] = rb[i].y;
       d[2] = rb[i].z;
@@ -1941,6 +1981,38 @@ MoeLayout moe_layout(bool nvfp4, int64_t E, int64_t H, int64_t I, int64_t T, int
   return L;
 }
 
+namespace {
+
+// Pair layout of weight codes, out of place: 16-byte unit u of row r goes to block r / 16, double row
+// (r % 16) % 8, 128-byte line u / 4 of it, half (r % 16) / 8, unit u % 4 (see b_load_pairs).
+__global__ __launch_bounds__(256) void k_codes_to_pairs(const uint4* __restrict__ in, uint4* __restrict__ out,
+                                                        int64_t n, int64_t ru) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-byte unit of the input
+  if (i >= n) return;
+  const int64_t r = i / ru, u = i - r * ru;
+  const int64_t m = r & 15;
+  out[(r - m) * ru + (m & 7) * 2 * ru + (u >> 2) * 8 + (m >> 3) * 4 + (u & 3)] = in[i];
+}
+
+// k_skinny_rows for the canonical or the pair layout of the weight codes
+template <bool NV, bool G1, bool A16, int DEPTH, bool QA, typename... Args>
+void launch_skr(bool pairs, dim3 grid, hipStream_t st, Args... args) {
+  if (pairs)
+    k_skinny_rows<NV, G1, kSkNT, A16, DEPTH, QA, true><<<grid, 256, 0, st>>>(args...);
+  else
+    k_skinny_rows<NV, G1, kSkNT, A16, DEPTH, QA, false><<<grid, 256, 0, st>>>(args...);
+}
+
+}  // namespace
+
+hipError_t launch_codes_to_pairs(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, hipStream_t st) {
+  const int64_t ru = row_bytes / 16, n = rows * ru;
+  if (n == 0) return hipSuccess;
+  k_codes_to_pairs<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(reinterpret_cast<const uint4*>(in),
+                                                                 reinterpret_cast<uint4*>(out), n, ru);
+  return hipGetLastError();
+}
+
 hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   const MoeLayout L = moe_layout(a.nvfp4, a.E, a.H, a.I, a.T, a.topk);
   if (a.T == 0) return hipSuccess;
@@ -2019,11 +2091,11 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   // projection when I % 256 != 0).
 #define BSM_G1(NV)                                                                                             \
   if (qa1)                                                                                                     \
-    k_skinny_rows<NV, true, kSkNT, false, NV ? 1 : kSkDepthF8, true><<<g1, 256, 0, st>>>(                      \
+    launch_skr<NV, true, false, NV ? 1 : kSkDepthF8, true>(a.pairs, g1, st,                                    \
         nullptr, a.x_codes, NV ? xsb : nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,    \
         tiles, ntiles, a.H, a.H, a.I, h_f32, h_amax);                                                          \
   else if (a.H % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                              \
-    k_skinny_rows<NV, true, kSkNT, false, NV ? 1 : kSkDepthF8><<<g1, 256, 0, st>>>(                            \
+    launch_skr<NV, true, false, NV ? 1 : kSkDepthF8, false>(a.pairs, g1, st,                                   \
         act, nullptr, nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, \
         a.H, a.I, h_f32, h_amax);                                                                              \
   else                                                                                                         \
@@ -2033,17 +2105,19 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   if (many && qa1)                                                                                             \
     k_gemm_big<NV, true, false, true><<<w1, 256, 0, st>>>(nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, \
                                                           w13s, a.w13_gs, tiles_w, ntiles_w, a.H, a.H, a.I,    \
-                                                          h_f32, h_amax, a.x_codes, NV ? xsb : nullptr);       \
+                                                          h_f32, h_amax, a.x_codes, NV ? xsb : nullptr,        \
+                                                          a.pairs ? 1 : 0);                                    \
   else if (many)                                                                                               \
     k_gemm_big<NV, true><<<w1, 256, 0, st>>>(act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, \
-                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax, nullptr, nullptr)
+                                             tiles_w, ntiles_w, a.H, a.H, a.I, h_f32, h_amax, nullptr, nullptr,  \
+                                             a.pairs ? 1 : 0)
 #define BSM_G2(NV, HSC)                                                                                        \
   if (qa2)                                                                                                     \
-    k_skinny_rows<NV, false, kSkNT, false, NV ? 1 : kSkDepthF8, true><<<g2, 256, 0, st>>>(                     \
+    launch_skr<NV, false, false, NV ? 1 : kSkDepthF8, true>(a.pairs, g2, st,                                   \
         nullptr, h_codes, NV ? h_scales : nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs,      \
         tiles, ntiles, a.I, a.H, a.I, y, h_amax);                                                              \
   else if (a.I % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                              \
-    k_skinny_rows<NV, false, kSkNT, false, NV ? 1 : kSkDepthF8><<<g2, 256, 0, st>>>(                           \
+    launch_skr<NV, false, false, NV ? 1 : kSkDepthF8, false>(a.pairs, g2, st,                                  \
         hdec, nullptr, nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I,     \
         a.H, a.I, y, h_amax);                                                                                  \
   else                                                                                                         \
@@ -2052,10 +2126,12 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   if (many && qa2)                                                                                             \
     k_gemm_big<NV, false, false, true><<<w2, 256, 0, st>>>(nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes,  \
                                                            w2s, a.w2_gs, tiles_w, ntiles_w, a.I, a.H, a.I, y,  \
-                                                           h_amax, h_codes, NV ? h_scales : nullptr);          \
+                                                           h_amax, h_codes, NV ? h_scales : nullptr,           \
+                                                           a.pairs ? 1 : 0);                                   \
   else if (many && big_dn)                                                                                     \
     k_gemm_big<NV, false><<<w2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs,     \
-                                              tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax, nullptr, nullptr);  \
+                                              tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax, nullptr, nullptr,   \
+                                              a.pairs ? 1 : 0);                                                \
   else if (many)                                                                                               \
     k_gemm_wide<NV, false><<<w2, 256, 0, st>>>(hdec, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs,    \
                                                tiles_w, ntiles_w, a.I, a.H, a.I, y, h_amax)
@@ -2064,15 +2140,15 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
     // weight-only W4A16: BF16 activations, NVFP4 weights decoded to BF16, h rounded to BF16
 #define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K)                                                   \
   if (K % (4 * kNvKB) == 0)                                                                                    \
-    k_skinny_rows<true, G, kSkNT, true><<<GRID, 256, 0, st>>>(A, nullptr, nullptr, row_pair, a.topk, nullptr, \
-                                                              SC, W, WS, WGS, tiles, ntiles, K, a.H, a.I, OUT, \
-                                                              h_amax);                                         \
+    launch_skr<true, G, true, 1, false>(a.pairs, GRID, st, A, nullptr, nullptr, row_pair, a.topk, nullptr, SC,  \
+                                        W, WS, WGS, tiles, ntiles, K, a.H, a.I, OUT, h_amax);                  \
   else                                                                                                         \
     k_skinny<true, G, 32, kSkNT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS,     \
                                                              tiles, ntiles, K, a.H, a.I, OUT, h_amax);         \
   if (many && (G || big_dn))                                                                                   \
     k_gemm_big<true, G, true><<<WGRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,    \
-                                                     ntiles_w, K, a.H, a.I, OUT, h_amax, nullptr, nullptr);    \
+                                                     ntiles_w, K, a.H, a.I, OUT, h_amax, nullptr, nullptr,     \
+                                                     a.pairs ? 1 : 0);                                         \
   else if (many)                                                                                               \
     k_gemm_wide<true, G, true><<<WGRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,   \
                                                       ntiles_w, K, a.H, a.I, OUT, h_amax)

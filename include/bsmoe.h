@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define BSM_ABI_VERSION 2
+#define BSM_ABI_VERSION 3
 
 typedef struct ihipStream_t* bsm_stream_t; /* identical to hipStream_t */
 
@@ -77,6 +77,8 @@ enum bsm_status {
 enum bsm_dtype { BSM_BF16 = 1, BSM_F32 = 2 };
 enum bsm_format { BSM_FMT_NVFP4 = 1, BSM_FMT_FP8 = 2, BSM_FMT_W4A16 = 3 /* workspace sizing only */ };
 enum bsm_gs_mode { BSM_GS_DYNAMIC = 0, BSM_GS_STATIC = 1 };
+/* Order of the expert weight codes in memory (bsm_moe_weights.layout); the codes themselves are the same. */
+enum bsm_layout { BSM_LAYOUT_ROWS = 0 /* canonical, row-major */, BSM_LAYOUT_PAIRS = 1 /* bsm_codes_to_pairs */ };
 
 /* Library version (BSM_ABI_VERSION). */
 int bsm_abi_version(void);
@@ -216,6 +218,10 @@ typedef struct bsm_moe_weights {
   const uint8_t* w2_codes;
   const void* w2_scales;
   const float* w2_gs;
+  int layout; /* BSM_LAYOUT_ROWS, or BSM_LAYOUT_PAIRS for w13_codes and w2_codes from bsm_codes_to_pairs
+                 (the scales stay row-major).  PAIRS needs H and I multiples of the few-row GEMM's K step
+                 (NVFP4 and W4A16: 512 values, FP8: 256) and I a multiple of 256, and is not taken by the
+                 dense FP8 path (E = 1, topk = 1, T <= 64): BSM_ERR_UNSUPPORTED otherwise. */
 } bsm_moe_weights;
 
 typedef struct bsm_act_q {
@@ -292,6 +298,17 @@ int bsm_moe_expert_mlp_noalloc(const bsm_moe_weights* w /* host */, const bsm_ac
 int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w /* host */, const void* x, int64_t T,
                              const int32_t* topk_ids, const float* topk_weights, int topk, float combine_scale,
                              float* out, void* ws, size_t ws_bytes, bsm_stream_t stream);
+
+/* Pair layout of routed-expert weight codes (BSM_LAYOUT_PAIRS), out of place.  The codes are those of the
+ * canonical layout (NVFP4: E2M1 pairs per byte; FP8: E4M3 bytes; "NVFP4 quantization" and "FP8
+ * quantization" pages, "Quantization scheme"); only their order changes: in every block of 16 rows, rows
+ * p and p + 8 (p < 8) become one double row of 2 * row_bytes bytes whose 128-byte lines hold 64 bytes of
+ * row p, then the same 64 bytes of row p + 8.  The few-row expert GEMM then loads each lane's operand
+ * pieces directly while every load instruction still reads whole cache lines.
+ * in, out: device pointers to [rows, row_bytes] bytes (w13_codes: rows = E * 2I; w2_codes: rows = E * H),
+ * 16-byte aligned, not overlapping; rows % 16 == 0, row_bytes % 64 == 0 (BSM_ERR_INVALID_ARG otherwise).
+ * Enqueued on stream; the caller owns both buffers. */
+int bsm_codes_to_pairs(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, bsm_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Dense FP8_DYNAMIC (W8A8) linear projection [FP8]

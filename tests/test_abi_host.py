@@ -31,7 +31,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsm_abi_version() == 2
+    assert lib.bsm_abi_version() == 3
     assert lib.bsm_status_str(0) == b"BSM_OK"
     assert lib.bsm_status_str(3) == b"BSM_ERR_WORKSPACE"
 
@@ -99,6 +99,39 @@ def test_moe_validation(lib):
     assert lay.total == lib.bsm_moe_workspace_size(1, 256, 5120, 2560, 64, 8)
     assert lay.y_f32 >= lay.h_f32 + 512 * 2560 * 4
     assert all(getattr(lay, f) % 256 == 0 for f, _ in bsm._WsLayout._fields_)
+
+
+def test_moe_weight_layout_validation(lib):
+    """The pair layout of the weight codes is checked on the host: an unknown layout, shapes its kernels do not
+    take, and the dense FP8 path are refused before any device call."""
+    ref = ctypes.byref
+    a = bsm._ActQ(1, 0x100000, 0x100000, 0x100000)
+    P = 0x100000
+    unknown = bsm._MoeWeights(1, 256, 5120, 2560, P, P, P, P, P, P, 7)
+    assert lib.bsm_moe_expert_mlp(ref(unknown), ref(a), 64, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None, 0, None) == 1
+    assert "layout" in _err(lib)
+    # NVFP4 pairs need H and I multiples of 512 (I = 384: fine for rows, not for pairs)
+    odd = bsm._MoeWeights(1, 256, 5120, 384, P, P, P, P, P, P, bsm.LAYOUT_PAIRS)
+    assert lib.bsm_moe_expert_mlp(ref(odd), ref(a), 64, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None, 0, None) == 2
+    assert "pair layout" in _err(lib)
+    rows = bsm._MoeWeights(1, 256, 5120, 384, P, P, P, P, P, P, bsm.LAYOUT_ROWS)
+    assert lib.bsm_moe_expert_mlp(ref(rows), ref(a), 64, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None, 0, None) == 3
+    # FP8 dense path (one expert, top-1, at most 64 tokens) reads the canonical layout only
+    dense = bsm._MoeWeights(2, 1, 5120, 2560, P, P, None, P, P, None, bsm.LAYOUT_PAIRS)
+    a8 = bsm._ActQ(2, 0x100000, 0x100000, None)
+    assert lib.bsm_moe_expert_mlp(ref(dense), ref(a8), 64, FAKE, FAKE, 1, 1.0, 0, None, FAKE, None, 0, None) == 2
+    # W4A16 takes the same rule
+    assert lib.bsm_moe_expert_mlp_w4a16(ref(odd), FAKE, 64, FAKE, FAKE, 8, 2.5, FAKE, None, 0, None) == 2
+
+
+def test_codes_to_pairs_validation(lib):
+    f = lib.bsm_codes_to_pairs
+    assert f(FAKE, ctypes.c_void_p(0x200000), 24, 64, None) == 1  # rows % 16
+    assert f(FAKE, ctypes.c_void_p(0x200000), 32, 96, None) == 1  # row_bytes % 64
+    assert f(None, ctypes.c_void_p(0x200000), 32, 64, None) == 1
+    assert f(FAKE, ctypes.c_void_p(0x100010), 32, 64, None) == 1  # out overlaps in
+    assert f(FAKE, ctypes.c_void_p(0x200008), 32, 64, None) == 1  # misaligned
+    assert f(None, None, 0, 64, None) == 0
 
 
 def test_moe_noalloc_validation(lib):
