@@ -39,7 +39,7 @@ class _MoeWeights(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int), ("E", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
                 ("w13_codes", ctypes.c_void_p), ("w13_scales", ctypes.c_void_p), ("w13_gs", ctypes.c_void_p),
                 ("w2_codes", ctypes.c_void_p), ("w2_scales", ctypes.c_void_p), ("w2_gs", ctypes.c_void_p),
-                ("layout", ctypes.c_int)]
+                ("layout", ctypes.c_int), ("w13_scales_lanes", ctypes.c_void_p), ("w2_scales_lanes", ctypes.c_void_p)]
 
 
 class _ActQ(ctypes.Structure):
@@ -82,6 +82,7 @@ def load():
                                              f32, i32, vp, vp, vp]),
         "bsm_moe_expert_mlp_w4a16": (i32, [ctypes.POINTER(_MoeWeights), vp, i64, vp, vp, i32, f32, vp, vp, sz, vp]),
         "bsm_codes_to_pairs": (i32, [vp, vp, i64, i64, vp]),
+        "bsm_scales_to_lanes": (i32, [vp, vp, i64, i64, vp]),
         "bsm_fp8_linear_workspace_size": (sz, [i64, i64, i64]),
         "bsm_fp8_linear": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         "bsm_set_stage_events": (i32, [i32, ctypes.POINTER(vp), i32]),
@@ -281,7 +282,8 @@ def route_diagnostics(ws, T, H, E):
 @dataclass
 class ExpertWeights:
     """Quantized routed-expert weights: codes in the canonical row-major layout (``LAYOUT_ROWS``) or in the
-    pair layout (``LAYOUT_PAIRS``, from ``to_pair_layout``); the scales are row-major either way."""
+    pair layout (``LAYOUT_PAIRS``, from ``to_pair_layout``); the scales are row-major either way, and NVFP4
+    pair-layout weights also carry lane-ordered copies of the block scales (``*_scales_lanes``)."""
     format: int
     E: int
     H: int
@@ -293,12 +295,15 @@ class ExpertWeights:
     w2_scales: torch.Tensor
     w2_gs: Optional[torch.Tensor]
     layout: int = LAYOUT_ROWS
+    w13_scales_lanes: Optional[torch.Tensor] = None
+    w2_scales_lanes: Optional[torch.Tensor] = None
 
     def _struct(self):
         return _MoeWeights(self.format, self.E, self.H, self.I, self.w13_codes.data_ptr(), self.w13_scales.data_ptr(),
                            None if self.w13_gs is None else self.w13_gs.data_ptr(), self.w2_codes.data_ptr(),
                            self.w2_scales.data_ptr(), None if self.w2_gs is None else self.w2_gs.data_ptr(),
-                           self.layout)
+                           self.layout, None if self.w13_scales_lanes is None else self.w13_scales_lanes.data_ptr(),
+                           None if self.w2_scales_lanes is None else self.w2_scales_lanes.data_ptr())
 
 
 def codes_to_pairs(codes: torch.Tensor) -> torch.Tensor:
@@ -315,12 +320,29 @@ def codes_to_pairs(codes: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def scales_to_lanes(scales: torch.Tensor) -> torch.Tensor:
+    """Lane order of NVFP4 block scales [..., rows, row_bytes] (uint8; rows a multiple of 16 in total, row_bytes
+    of 32), out of place: per 16-row block and 512-value span, each row's 32 bytes reordered for the lanes."""
+    lib = load()
+    _dev(scales, "scales")
+    if scales.dtype != torch.uint8:
+        raise BsmError("scales must be uint8")
+    rb = scales.shape[-1]
+    rows = scales.numel() // rb if rb else 0
+    out = torch.empty_like(scales)
+    _check(lib.bsm_scales_to_lanes(_ptr(scales), _ptr(out), rows, rb, _stream()))
+    return out
+
+
 def to_pair_layout(w: "ExpertWeights") -> "ExpertWeights":
-    """The same weights with both code tensors in the pair layout (new tensors; scales shared)."""
+    """The same weights in the pair layout: both code tensors through codes_to_pairs (new tensors; the scales
+    are shared) and, for NVFP4, lane-ordered copies of both block-scale tensors through scales_to_lanes."""
     if w.layout == LAYOUT_PAIRS:
         return w
+    nv = w.format == FMT_NVFP4
     return ExpertWeights(w.format, w.E, w.H, w.I, codes_to_pairs(w.w13_codes), w.w13_scales, w.w13_gs,
-                         codes_to_pairs(w.w2_codes), w.w2_scales, w.w2_gs, LAYOUT_PAIRS)
+                         codes_to_pairs(w.w2_codes), w.w2_scales, w.w2_gs, LAYOUT_PAIRS,
+                         scales_to_lanes(w.w13_scales) if nv else None, scales_to_lanes(w.w2_scales) if nv else None)
 
 
 def quantize_expert_weights(w13: torch.Tensor, w2: torch.Tensor, fmt: str) -> ExpertWeights:

@@ -67,6 +67,10 @@ static int check_layout(const bsm_moe_weights* w, bool nv, bool a16, int64_t T, 
     return fail(BSM_ERR_UNSUPPORTED, "pair layout needs H and I multiples of %lld and I of 256", (long long)ks);
   if (!nv && !a16 && w->E == 1 && topk == 1 && T <= 64)
     return fail(BSM_ERR_UNSUPPORTED, "pair layout: not taken by the dense FP8 path (E = 1, topk = 1, T <= 64)");
+  if (nv && T > 0 && (!w->w13_scales_lanes || !w->w2_scales_lanes))
+    return fail(BSM_ERR_INVALID_ARG, "NVFP4 pair layout needs the lane-ordered scales");
+  if (nv && T > 0 && (!aligned(w->w13_scales_lanes, 16) || !aligned(w->w2_scales_lanes, 16)))
+    return fail(BSM_ERR_INVALID_ARG, "lane-ordered scales must be 16-byte aligned");
   return BSM_OK;
 }
 
@@ -121,6 +125,8 @@ int moe_args(const bsm_moe_weights* w, const bsm_act_q* xq, int64_t T, const int
   a->h_gs_user = h_global_scale;
   a->out = out;
   a->pairs = w->layout == BSM_LAYOUT_PAIRS;
+  a->w13_scales_lanes = w->w13_scales_lanes;
+  a->w2_scales_lanes = w->w2_scales_lanes;
   return BSM_OK;
 }
 
@@ -391,8 +397,21 @@ int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w, const void* x, int64_t T,
   a.h_gs_user = nullptr;
   a.out = out;
   a.pairs = w->layout == BSM_LAYOUT_PAIRS;
+  a.w13_scales_lanes = w->w13_scales_lanes;
+  a.w2_scales_lanes = w->w2_scales_lanes;
   a.ws = reinterpret_cast<uint8_t*>(ws);
   return hip_status(bsm::launch_moe(a, (hipStream_t)stream), "bsm_moe_expert_mlp_w4a16");
+}
+
+int bsm_scales_to_lanes(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, bsm_stream_t stream) {
+  if (rows < 0 || row_bytes < 0 || rows % 16 != 0 || row_bytes % 32 != 0)
+    return fail(BSM_ERR_INVALID_ARG, "rows must be a multiple of 16 and row_bytes of 32");
+  if (rows == 0 || row_bytes == 0) return ok();
+  if (!in || !out) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(in, 16) || !aligned(out, 16)) return fail(BSM_ERR_INVALID_ARG, "in and out must be 16-byte aligned");
+  const uint8_t *ie = in + rows * row_bytes, *oe = out + rows * row_bytes;
+  if (in < oe && out < ie) return fail(BSM_ERR_INVALID_ARG, "in and out overlap");
+  return hip_status(bsm::launch_scales_to_lanes(in, out, rows, row_bytes, (hipStream_t)stream), "bsm_scales_to_lanes");
 }
 
 int bsm_codes_to_pairs(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, bsm_stream_t stream) {

@@ -74,6 +74,8 @@ struct MoeArgs {
   const int32_t* ids;
   const float* wts;
   bool pairs = false;  // weight codes in the pair layout (launch_codes_to_pairs)
+  const uint8_t* w13_scales_lanes = nullptr;  // NVFP4 pairs: lane-ordered block scales (few-row GEMMs)
+  const uint8_t* w2_scales_lanes = nullptr;
   float combine_scale;
   bool h_static;
   float* h_gs_user;
@@ -83,6 +85,8 @@ struct MoeArgs {
 hipError_t launch_moe(const MoeArgs& a, hipStream_t st);
 // weight codes [rows, row_bytes] (rows % 16 == 0, row_bytes % 64 == 0) -> pair layout, out of place
 hipError_t launch_codes_to_pairs(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, hipStream_t st);
+// NVFP4 block scales [rows, row_bytes] (rows % 16 == 0, row_bytes % 32 == 0) -> lane order, out of place
+hipError_t launch_scales_to_lanes(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, hipStream_t st);
 
 // ---- dense FP8 linear ------------------------------------------------------
 size_t fp8_linear_ws(int64_t T, int64_t K, int64_t N);

@@ -733,6 +733,8 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
   constexpr int kSV = KB / 32;
   constexpr int cstep = NV ? KS / 2 : KS, sstep = KS / 16;  // code (NVFP4: and scale) bytes per row and super-step
   constexpr int kU = DEPTH + 1;  // super-steps per unrolled iteration (one per register set)
+  static_assert(!(NV && PAIRS) || DEPTH == 1, "lane-ordered NVFP4 scales: two register sets, depth 1");
+  static_assert(!(NV && PAIRS) || KS == 512, "lane-ordered NVFP4 scales: 32 per row and super-step");
   __shared__ __attribute__((aligned(16))) _Float16 Ar[kRowsLds / 2];
   // Gate/up: workgroup i runs on XCD i % 8 (the dispatcher deals workgroups out round robin), so the live
   // workgroups are renumbered to give each XCD one contiguous run of (row tile, column block) items in
@@ -766,12 +768,18 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
   const int64_t cbytes = NV ? K / 2 : K;
   const uint8_t* trow[NT];  // first weight row of each tile (its 16 rows are consecutive)
   const uint8_t* srow[NT];
+  const uint8_t* stile[NT];
+  // NVFP4 with the pair layout: the lane-ordered scales (bsm_scales_to_lanes) of a super-step are one 8-byte
+  // load per lane and tile (the two blocks of each of its 4 pieces), two sets: super-step s + 1 loads while
+  // s is multiplied
+  uint2 q0[NT], q1[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int64_t r0 = G1 ? (int64_t)e * 2 * I + (j >= NT / 2 ? I : 0) + n0 + 16 * (j % (NT / 2))
                           : (int64_t)e * H + n0 + 16 * j;
     trow[j] = wc + r0 * cbytes;
     srow[j] = NV ? wsc + (r0 + m) * (K / 16) + (int64_t)sstep * g : nullptr;  // lane g: super-step 4q + g
+    stile[j] = NV ? wsc + r0 * (K / 16) : nullptr;  // lane-ordered scales: the 16-row block's first byte
   }
   f4v acc[NT];
 #pragma unroll
@@ -803,14 +811,27 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
   }
   if constexpr (NV) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) s_load<KB>(srow[j], g < nsteps, sc[j]);
+    for (int j = 0; j < NT; ++j) {
+      if constexpr (PAIRS)
+        q0[j] = *reinterpret_cast<const uint2*>(stile[j] + m * 32 + g * 8);
+      else
+        s_load<KB>(srow[j], g < nsteps, sc[j]);
+    }
   }
-  // one super-step: NVFP4 scale bytes from lane group (ST & 3) (after the fourth, every group loads its
-  // span of the next line), the whole-line codes of super-step ST + DEPTH into BN, the codes of ST from BC
-  // into the MFMA lane layout, the multiplies from the staged rows
-#define BSM_SKR_STEP(ST, BC, BN)                                                                       \
+  // one super-step: NVFP4 scale bytes (pair layout: the lane's own 8 bytes from SC; canonical: from lane
+  // group (ST & 3), and after the fourth every group loads its span of the next line), the whole-line codes
+  // (and lane-ordered scales into SN) of super-step ST + DEPTH into BN, the codes of ST from BC into the
+  // MFMA lane layout, the multiplies from the staged rows
+#define BSM_SKR_STEP(ST, BC, BN, SC, SN)                                                               \
   {                                                                                                    \
-    if constexpr (NV) {                                                                                \
+    if constexpr (NV && PAIRS) {                                                                       \
+      _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                  \
+        sp[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SC[j].x, 1.0f, false);                      \
+        sp[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SC[j].x, 1.0f, true);                       \
+        sp[j][2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SC[j].y, 1.0f, false);                      \
+        sp[j][3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(SC[j].y, 1.0f, true);                       \
+      }                                                                                                \
+    } else if constexpr (NV) {                                                                         \
       const int gi = (ST) & 3;                                                                         \
       _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                  \
         s_fetch<KB>(sc[j], (m + 16 * gi) * 4, ghi, sdw[j]);                                            \
@@ -826,6 +847,10 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
       }                                                                                                \
     }                                                                                                  \
     if ((ST) + DEPTH < nsteps) {                                                                       \
+      if constexpr (NV && PAIRS) {                                                                     \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j)                                                \
+          SN[j] = *reinterpret_cast<const uint2*>(stile[j] + ((ST) + DEPTH) * 512 + m * 32 + g * 8);   \
+      }                                                                                                \
       _Pragma("unroll") for (int j = 0; j < NT; ++j) {                                                \
         if constexpr (PAIRS)                                                                           \
           b_load_pairs(trow[j], cbytes, ((ST) + DEPTH) * (int64_t)cstep, lane, BN[j]);                 \
@@ -863,14 +888,14 @@ __global__ __launch_bounds__(256, DEPTH == 1 ? 3 : 2) void k_skinny_rows(
     __syncthreads();
     if constexpr (DEPTH == 1) {
       for (int st = c0; st < c1; st += 2) {
-        BSM_SKR_STEP(st, b0, b1)
-        if (st + 1 < c1) BSM_SKR_STEP(st + 1, b1, b0)
+        BSM_SKR_STEP(st, b0, b1, q0, q1)
+        if (st + 1 < c1) BSM_SKR_STEP(st + 1, b1, b0, q1, q0)
       }
     } else {  // super-step st multiplies set st % 3 and loads st + 2 into set (st + 2) % 3
       for (int st = c0; st < c1; st += 3) {
-        BSM_SKR_STEP(st, b0, b2)
-        if (st + 1 < c1) BSM_SKR_STEP(st + 1, b1, b0)
-        if (st + 2 < c1) BSM_SKR_STEP(st + 2, b2, b1)
+        BSM_SKR_STEP(st, b0, b2, q0, q1)  /* NVFP4 runs depth 1: the scale sets are unused here */
+        if (st + 1 < c1) BSM_SKR_STEP(st + 1, b1, b0, q0, q1)
+        if (st + 2 < c1) BSM_SKR_STEP(st + 2, b2, b1, q0, q1)
       }
     }
   }
@@ -1447,6 +1472,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   const uint8_t* sbase = NV ? wsc + wrow_of(0) * (K / 16) : wc;
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sbase), (short)0,
                                                                        0x7FFFFFFF, kBufDword3);
+  // (the block scales are row-major in both code layouts: the lane-ordered copy is the few-row GEMM's)
   const uint32_t soff = NV ? (uint32_t)((wrow_of(tid) - wrow_of(0)) * (K / 16)) : 0u;
 
   uint4 ra0, ra1, ra2, ra3, rb[kBI], sc4 = make_uint4(0, 0, 0, 0);
@@ -1994,6 +2020,32 @@ __global__ __launch_bounds__(256) void k_codes_to_pairs(const uint4* __restrict_
   out[(r - m) * ru + (m & 7) * 2 * ru + (u >> 2) * 8 + (m >> 3) * 4 + (u & 3)] = in[i];
 }
 
+// Lane order of NVFP4 block scales, out of place: row r's 32 scale bytes of super-step st (512 values) go to
+// 16-row block r / 16, super-step st, row r % 16, block b to byte ((b >> 1) & 3) * 8 + (b >> 3) * 2 + (b & 1):
+// lane group g of the few-row GEMM finds the two blocks of each of its four pieces as 8 consecutive bytes
+// (one load; two dword loads per lane measured slower, decode-64 0.865 -> 0.90 ms).  The many-row GEMM keeps
+// the row-major scales: its weight groups take 16 blocks of a row at a time (prefill-8192 gate/up 3.03 ->
+// 3.16 ms reading this order).
+__global__ __launch_bounds__(256) void k_scales_to_lanes(const uint8_t* __restrict__ in, uint8_t* __restrict__ out,
+                                                         int64_t n, int64_t nst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, super-step) span of 32 bytes
+  if (i >= n) return;
+  const int64_t r = i / nst, st = i - r * nst;
+  const uint4* src = reinterpret_cast<const uint4*>(in + (r * nst + st) * 32);
+  const uint4 a = src[0], c = src[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+  uint32_t o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int b = 0; b < 32; ++b) {
+    const uint32_t v = (w[b >> 2] >> (8 * (b & 3))) & 0xFFu;
+    const int q = ((b >> 1) & 3) * 8 + (b >> 3) * 2 + (b & 1);
+    o[q >> 2] |= v << (8 * (q & 3));
+  }
+  uint4* dst = reinterpret_cast<uint4*>(out + (((r >> 4) * nst + st) * 16 + (r & 15)) * 32);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // k_skinny_rows for the canonical or the pair layout of the weight codes
 template <bool NV, bool G1, bool A16, int DEPTH, bool QA, typename... Args>
 void launch_skr(bool pairs, dim3 grid, hipStream_t st, Args... args) {
@@ -2004,6 +2056,13 @@ void launch_skr(bool pairs, dim3 grid, hipStream_t st, Args... args) {
 }
 
 }  // namespace
+
+hipError_t launch_scales_to_lanes(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, hipStream_t st) {
+  const int64_t nst = row_bytes / 32, n = rows * nst;
+  if (n == 0) return hipSuccess;
+  k_scales_to_lanes<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(in, out, n, nst);
+  return hipGetLastError();
+}
 
 hipError_t launch_codes_to_pairs(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, hipStream_t st) {
   const int64_t ru = row_bytes / 16, n = rows * ru;
@@ -2083,6 +2142,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   stage_mark(0, 1, st);
   const uint8_t* w13s = reinterpret_cast<const uint8_t*>(a.w13_scales);
   const uint8_t* w2s = reinterpret_cast<const uint8_t*>(a.w2_scales);
+  // the few-row GEMMs' NVFP4 block scales: lane-ordered with the pair layout, else row-major
+  const uint8_t* w13sk = a.pairs && a.nvfp4 ? reinterpret_cast<const uint8_t*>(a.w13_scales_lanes) : w13s;
+  const uint8_t* w2sk = a.pairs && a.nvfp4 ? reinterpret_cast<const uint8_t*>(a.w2_scales_lanes) : w2s;
   const float* xrs = reinterpret_cast<const float*>(a.x_scales);
   const uint8_t* xsb = reinterpret_cast<const uint8_t*>(a.x_scales);  // NVFP4: E4M3 block scales
   const float* hsc = reinterpret_cast<const float*>(h_scales);        // FP8: per-row h scales
@@ -2092,12 +2154,12 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #define BSM_G1(NV)                                                                                             \
   if (qa1)                                                                                                     \
     launch_skr<NV, true, false, NV ? 1 : kSkDepthF8, true>(a.pairs, g1, st,                                    \
-        nullptr, a.x_codes, NV ? xsb : nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs,    \
+        nullptr, a.x_codes, NV ? xsb : nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13sk, a.w13_gs,   \
         tiles, ntiles, a.H, a.H, a.I, h_f32, h_amax);                                                          \
   else if (a.H % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                              \
     launch_skr<NV, true, false, NV ? 1 : kSkDepthF8, false>(a.pairs, g1, st,                                   \
-        act, nullptr, nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, \
-        a.H, a.I, h_f32, h_amax);                                                                              \
+        act, nullptr, nullptr, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13sk, a.w13_gs, tiles, ntiles,    \
+        a.H, a.H, a.I, h_f32, h_amax);                                                                              \
   else                                                                                                         \
     k_skinny<NV, true, 32, kSkNT, false, NV ? 1 : kSkDepthF8><<<g1, 256, 0, st>>>(                             \
         act, row_pair, a.topk, a.x_gs, xrs, a.w13_codes, w13s, a.w13_gs, tiles, ntiles, a.H, a.H, a.I, h_f32,  \
@@ -2114,11 +2176,11 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
 #define BSM_G2(NV, HSC)                                                                                        \
   if (qa2)                                                                                                     \
     launch_skr<NV, false, false, NV ? 1 : kSkDepthF8, true>(a.pairs, g2, st,                                   \
-        nullptr, h_codes, NV ? h_scales : nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs,      \
+        nullptr, h_codes, NV ? h_scales : nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2sk, a.w2_gs,     \
         tiles, ntiles, a.I, a.H, a.I, y, h_amax);                                                              \
   else if (a.I % (4 * (NV ? kNvKB : kF8KB)) == 0)                                                              \
     launch_skr<NV, false, false, NV ? 1 : kSkDepthF8, false>(a.pairs, g2, st,                                  \
-        hdec, nullptr, nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2s, a.w2_gs, tiles, ntiles, a.I,     \
+        hdec, nullptr, nullptr, row_pair, a.topk, h_gs, HSC, a.w2_codes, w2sk, a.w2_gs, tiles, ntiles, a.I,    \
         a.H, a.I, y, h_amax);                                                                                  \
   else                                                                                                         \
     k_skinny<NV, false, 32, kSkNT, false, NV ? 1 : kSkDepthF8><<<g2, 256, 0, st>>>(                            \
@@ -2138,10 +2200,10 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   hipError_t err;
   if (a.a16) {
     // weight-only W4A16: BF16 activations, NVFP4 weights decoded to BF16, h rounded to BF16
-#define BSM_A16_G(G, A, SC, W, WS, WGS, OUT, GRID, WGRID, K)                                                   \
+#define BSM_A16_G(G, A, SC, W, WS, WSK, WGS, OUT, GRID, WGRID, K)                                                 \
   if (K % (4 * kNvKB) == 0)                                                                                    \
     launch_skr<true, G, true, 1, false>(a.pairs, GRID, st, A, nullptr, nullptr, row_pair, a.topk, nullptr, SC,  \
-                                        W, WS, WGS, tiles, ntiles, K, a.H, a.I, OUT, h_amax);                  \
+                                        W, WSK, WGS, tiles, ntiles, K, a.H, a.I, OUT, h_amax);                 \
   else                                                                                                         \
     k_skinny<true, G, 32, kSkNT, true><<<GRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS,     \
                                                              tiles, ntiles, K, a.H, a.I, OUT, h_amax);         \
@@ -2152,12 +2214,12 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t st) {
   else if (many)                                                                                               \
     k_gemm_wide<true, G, true><<<WGRID, 256, 0, st>>>(A, row_pair, a.topk, nullptr, SC, W, WS, WGS, tiles_w,   \
                                                       ntiles_w, K, a.H, a.I, OUT, h_amax)
-    BSM_A16_G(true, act, xrs, a.w13_codes, w13s, a.w13_gs, h_f32, g1, w1, a.H);
+    BSM_A16_G(true, act, xrs, a.w13_codes, w13s, w13sk, a.w13_gs, h_f32, g1, w1, a.H);
     stage_mark(0, 2, st);
     const int64_t n4 = L.P * a.I / 4;
     k_h_to_bf16<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(h_f32, n4, reinterpret_cast<uint16_t*>(hdec));
     stage_mark(0, 3, st);
-    BSM_A16_G(false, hdec, nullptr, a.w2_codes, w2s, a.w2_gs, y, g2, w2, a.I);
+    BSM_A16_G(false, hdec, nullptr, a.w2_codes, w2s, w2sk, a.w2_gs, y, g2, w2, a.I);
 #undef BSM_A16_G
   } else if (a.nvfp4) {
     BSM_G1(true);

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define BSM_ABI_VERSION 3
+#define BSM_ABI_VERSION 4
 
 typedef struct ihipStream_t* bsm_stream_t; /* identical to hipStream_t */
 
@@ -78,7 +78,10 @@ enum bsm_dtype { BSM_BF16 = 1, BSM_F32 = 2 };
 enum bsm_format { BSM_FMT_NVFP4 = 1, BSM_FMT_FP8 = 2, BSM_FMT_W4A16 = 3 /* workspace sizing only */ };
 enum bsm_gs_mode { BSM_GS_DYNAMIC = 0, BSM_GS_STATIC = 1 };
 /* Order of the expert weight codes in memory (bsm_moe_weights.layout); the codes themselves are the same. */
-enum bsm_layout { BSM_LAYOUT_ROWS = 0 /* canonical, row-major */, BSM_LAYOUT_PAIRS = 1 /* bsm_codes_to_pairs */ };
+enum bsm_layout {
+  BSM_LAYOUT_ROWS = 0, /* canonical, row-major */
+  BSM_LAYOUT_PAIRS = 1 /* codes from bsm_codes_to_pairs (NVFP4: and lane-ordered copies of the block scales) */
+};
 
 /* Library version (BSM_ABI_VERSION). */
 int bsm_abi_version(void);
@@ -219,9 +222,14 @@ typedef struct bsm_moe_weights {
   const void* w2_scales;
   const float* w2_gs;
   int layout; /* BSM_LAYOUT_ROWS, or BSM_LAYOUT_PAIRS for w13_codes and w2_codes from bsm_codes_to_pairs
-                 (the scales stay row-major).  PAIRS needs H and I multiples of the few-row GEMM's K step
-                 (NVFP4 and W4A16: 512 values, FP8: 256) and I a multiple of 256, and is not taken by the
-                 dense FP8 path (E = 1, topk = 1, T <= 64): BSM_ERR_UNSUPPORTED otherwise. */
+                 (the scales above stay as they are).  PAIRS needs H and I multiples of the few-row GEMM's
+                 K step (NVFP4 and W4A16: 512 values, FP8: 256) and I a multiple of 256, and is not taken
+                 by the dense FP8 path (E = 1, topk = 1, T <= 64): BSM_ERR_UNSUPPORTED otherwise. */
+  /* NVFP4 with BSM_LAYOUT_PAIRS only (else ignored): w13_scales and w2_scales through bsm_scales_to_lanes,
+     same shapes, 16-byte aligned, read by the GEMM of experts with few rows (the one of experts with many
+     rows reads the row-major scales); NULL or misaligned -> BSM_ERR_INVALID_ARG. */
+  const uint8_t* w13_scales_lanes;
+  const uint8_t* w2_scales_lanes;
 } bsm_moe_weights;
 
 typedef struct bsm_act_q {
@@ -309,6 +317,18 @@ int bsm_moe_expert_mlp_w4a16(const bsm_moe_weights* w /* host */, const void* x,
  * 16-byte aligned, not overlapping; rows % 16 == 0, row_bytes % 64 == 0 (BSM_ERR_INVALID_ARG otherwise).
  * Enqueued on stream; the caller owns both buffers. */
 int bsm_codes_to_pairs(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, bsm_stream_t stream);
+
+/* Lane order of NVFP4 block scales (the E4M3 scale of each block of 16 values, "NVFP4 quantization" page,
+ * "Quantization scheme"), out of place, for the *_scales_lanes copies of BSM_LAYOUT_PAIRS weights: the same
+ * bytes, reordered.  Row r's
+ * 32 scale bytes of each span of 512 values (super-step st) go to 16-row block r / 16, super-step st,
+ * row r % 16 (32 bytes each, so a block's super-step is 512 contiguous bytes), block b of the span to
+ * byte ((b >> 1) & 3) * 8 + (b >> 3) * 2 + (b & 1): each lane of the few-row GEMM finds its 8 scale bytes
+ * of a super-step together, and each 128-byte line holds 4 rows' bytes of one super-step only.
+ * in, out: device pointers to [rows, row_bytes] bytes (w13_scales: rows = E * 2I, row_bytes = H / 16;
+ * w2_scales: rows = E * H, row_bytes = I / 16), 16-byte aligned, not overlapping; rows % 16 == 0,
+ * row_bytes % 32 == 0 (BSM_ERR_INVALID_ARG otherwise).  Enqueued on stream; the caller owns both. */
+int bsm_scales_to_lanes(const uint8_t* in, uint8_t* out, int64_t rows, int64_t row_bytes, bsm_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Dense FP8_DYNAMIC (W8A8) linear projection [FP8]

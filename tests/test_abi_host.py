@@ -31,7 +31,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsm_abi_version() == 3
+    assert lib.bsm_abi_version() == 4
     assert lib.bsm_status_str(0) == b"BSM_OK"
     assert lib.bsm_status_str(3) == b"BSM_ERR_WORKSPACE"
 
@@ -122,6 +122,17 @@ def test_moe_weight_layout_validation(lib):
     assert lib.bsm_moe_expert_mlp(ref(dense), ref(a8), 64, FAKE, FAKE, 1, 1.0, 0, None, FAKE, None, 0, None) == 2
     # W4A16 takes the same rule
     assert lib.bsm_moe_expert_mlp_w4a16(ref(odd), FAKE, 64, FAKE, FAKE, 8, 2.5, FAKE, None, 0, None) == 2
+    # NVFP4 pairs need the lane-ordered copies of the block scales, 16-byte aligned (FP8 pairs do not)
+    bare = bsm._MoeWeights(1, 256, 5120, 2560, P, P, P, P, P, P, bsm.LAYOUT_PAIRS)
+    assert lib.bsm_moe_expert_mlp(ref(bare), ref(a), 64, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None, 0, None) == 1
+    assert "lane-ordered" in _err(lib)
+    assert lib.bsm_moe_expert_mlp_w4a16(ref(bare), FAKE, 64, FAKE, FAKE, 8, 2.5, FAKE, None, 0, None) == 1
+    skew = bsm._MoeWeights(1, 256, 5120, 2560, P, P, P, P, P, P, bsm.LAYOUT_PAIRS, P, P + 8)
+    assert lib.bsm_moe_expert_mlp(ref(skew), ref(a), 64, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None, 0, None) == 1
+    full = bsm._MoeWeights(1, 256, 5120, 2560, P, P, P, P, P, P, bsm.LAYOUT_PAIRS, P, P)
+    assert lib.bsm_moe_expert_mlp(ref(full), ref(a), 64, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None, 0, None) == 3
+    fp8 = bsm._MoeWeights(2, 256, 5120, 2560, P, P, None, P, P, None, bsm.LAYOUT_PAIRS)
+    assert lib.bsm_moe_expert_mlp(ref(fp8), ref(a8), 64, FAKE, FAKE, 8, 2.5, 0, None, FAKE, None, 0, None) == 3
 
 
 def test_codes_to_pairs_validation(lib):
@@ -132,6 +143,12 @@ def test_codes_to_pairs_validation(lib):
     assert f(FAKE, ctypes.c_void_p(0x100010), 32, 64, None) == 1  # out overlaps in
     assert f(FAKE, ctypes.c_void_p(0x200008), 32, 64, None) == 1  # misaligned
     assert f(None, None, 0, 64, None) == 0
+    g = lib.bsm_scales_to_lanes
+    assert g(FAKE, ctypes.c_void_p(0x200000), 24, 32, None) == 1  # rows % 16
+    assert g(FAKE, ctypes.c_void_p(0x200000), 32, 48, None) == 1  # row_bytes % 32
+    assert g(None, ctypes.c_void_p(0x200000), 32, 32, None) == 1
+    assert g(FAKE, ctypes.c_void_p(0x100010), 32, 32, None) == 1  # out overlaps in
+    assert g(None, None, 0, 32, None) == 0
 
 
 def test_moe_noalloc_validation(lib):

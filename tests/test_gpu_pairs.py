@@ -1,8 +1,9 @@
-"""GPU: the pair layout of the expert weight codes (bsm_codes_to_pairs).
+"""GPU: the pair layout of the expert weights (bsm_codes_to_pairs, and for NVFP4 the lane-ordered copies of
+the block scales from bsm_scales_to_lanes).
 
 The codes are the canonical NVFP4 / FP8 codes ("NVFP4 quantization" and "FP8 quantization" pages,
 "Quantization scheme"); only their order in memory changes.  Checked here:
-  - the permutation against its definition, written independently as a reshape and transpose;
+  - both permutations against their definitions, written independently (reshape, transpose, byte order);
   - the routed-expert MLP on pair-layout weights gives the same output, bit for bit, as on the canonical
     layout (the kernels feed the same operands to the same MFMA lanes in the same order), at a mid shape
     with few-row and many-row experts and at the Beam decode and prefill shapes, in NVFP4, FP8 and W4A16.
@@ -37,6 +38,29 @@ def test_codes_to_pairs_definition(gpu_lib, rows, rb):
     assert not np.array_equal(got, c)
 
 
+def _lanes_reference(scales):
+    """Per 16-row block and 32-byte span st (512 values): the block's 16 rows in order, each row's block b
+    at byte 8 * (lane group) + 2 * (piece) + (block of the piece), with piece b // 8 and lane group
+    (b // 2) % 4."""
+    rows, rb = scales.shape
+    x = scales.reshape(rows // 16, 16, rb // 32, 32).transpose(0, 2, 1, 3)  # block, span, row, byte
+    pos = np.array([8 * ((b // 2) % 4) + 2 * (b // 8) + b % 2 for b in range(32)])
+    out = np.empty_like(x)
+    out[..., pos] = x
+    return np.ascontiguousarray(out).reshape(rows, rb)
+
+
+@pytest.mark.parametrize("rows,rb", [(16, 32), (48, 64), (5120, 320), (5120, 160)])
+def test_scales_to_lanes_definition(gpu_lib, rows, rb):
+    rng = np.random.default_rng(7 * rows + rb)
+    s = rng.integers(0, 127, size=(rows, rb), dtype=np.uint8)
+    out = gpu_lib.scales_to_lanes(torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    got = np_(out)
+    assert np.array_equal(got, _lanes_reference(s))
+    assert np.array_equal(np.sort(got, axis=None), np.sort(s, axis=None))
+
+
 def _outputs(gpu_lib, cfg, fmt, T, w13, w2):
     """Layer output on the canonical and on the pair layout of the same quantized weights."""
     x, wr = W.activations(cfg, T=T), W.router_weights(cfg)
@@ -46,6 +70,7 @@ def _outputs(gpu_lib, cfg, fmt, T, w13, w2):
     gw = gpu_lib.quantize_expert_weights(w13, w2, "nvfp4" if fmt == "w4a16" else fmt)
     gp = gpu_lib.to_pair_layout(gw)
     assert gp.layout == gpu_lib.LAYOUT_PAIRS and gp.w13_scales is gw.w13_scales
+    assert (gp.w13_scales_lanes is None) == (fmt == "fp8")
     if fmt == "w4a16":
         o_rows = gpu_lib.moe_expert_mlp_w4a16(gw, xt, ids, wts, cfg.combine_scale)
         o_pairs = gpu_lib.moe_expert_mlp_w4a16(gp, xt, ids, wts, cfg.combine_scale)
