@@ -309,12 +309,16 @@ def run_steps(cfg, fmt, x, wr, weights, steps, warmup, copies=None):
         nonlocal ws
         x, wr, weights = sets[it[0] % len(sets)]
         it[0] += 1
-        ids, wts = bsm.route(x, wr, cfg.n_group, cfg.topk_group, cfg.topk)
+        if fmt == "nvfp4":  # routing and the quantization of x in one call (one pass of max|x| fewer)
+            ids, wts, xq = bsm.route_nvfp4_quantize(x, wr, cfg.n_group, cfg.topk_group, cfg.topk)
+        else:
+            ids, wts = bsm.route(x, wr, cfg.n_group, cfg.topk_group, cfg.topk)
         if fmt == "w4a16":  # weight-only: the BF16 activations go in as they are
             o, ws = bsm.moe_expert_mlp_w4a16(weights, x, ids, wts, cfg.combine_scale, out=out, ws=ws,
                                              return_workspace=True)
             return ids
-        xq = bsm.quantize_activations(x, fmt)
+        if fmt != "nvfp4":
+            xq = bsm.quantize_activations(x, fmt)
         o, ws = bsm.moe_expert_mlp(weights, xq, ids, wts, cfg.combine_scale, out=out, ws=ws, return_workspace=True)
         return ids
 

@@ -73,6 +73,9 @@ def load():
         "bsm_fp8_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
         "bsm_route_workspace_size": (sz, [i64, i64, i64]),
         "bsm_route": (i32, [vp, i32, i64, i64, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "bsm_route_nvfp4_quantize_workspace_size": (sz, [i64, i64, i64]),
+        "bsm_route_nvfp4_quantize": (i32, [vp, i32, i64, i64, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                           vp, sz, vp]),
         "bsm_route_diagnostics": (i32, [vp, i64, i64, i64, vp, vp]),
         "bsm_moe_workspace_size": (sz, [i32, i64, i64, i64, i64, i32]),
         "bsm_moe_workspace_layout": (i32, [i32, i64, i64, i64, i64, i32, ctypes.POINTER(_WsLayout)]),
@@ -263,6 +266,32 @@ def route(x, w_router, n_group, topk_group, topk, return_scores=False, return_wo
         out.append(scores)
     if return_workspace:
         out.append(ws)
+    return tuple(out)
+
+
+def route_nvfp4_quantize(x, w_router, n_group, topk_group, topk, return_scores=False, ws=None):
+    """Routing and NVFP4 quantization of the same x in one call -> (ids, weights, (codes, scales, gs[1])[, scores]);
+    the same values as ``route`` and ``nvfp4_quantize``."""
+    lib = load()
+    _dev(x, "x")
+    _dev(w_router, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    ids = torch.empty((T, topk), dtype=torch.int32, device=x.device)
+    wts = torch.empty((T, topk), dtype=torch.float32, device=x.device)
+    scores = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_scores else None
+    codes = torch.empty((T, H // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((T, H // 16), dtype=torch.uint8, device=x.device)
+    gs = torch.empty(1, dtype=torch.float32, device=x.device)
+    need = lib.bsm_route_nvfp4_quantize_workspace_size(T, H, E)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, x.device)
+    _check(lib.bsm_route_nvfp4_quantize(_ptr(x), _dtype_code(x), T, H, _ptr(w_router), _dtype_code(w_router), E,
+                                        n_group, topk_group, topk, _ptr(ids), _ptr(wts), _ptr(scores), _ptr(codes),
+                                        _ptr(scales), _ptr(gs), _ptr(ws), ws.numel(), _stream()))
+    out = [ids, wts, (codes, scales, gs)]
+    if return_scores:
+        out.append(scores)
     return tuple(out)
 
 
@@ -505,10 +534,12 @@ def fp8_dense_mlp(weights: ExpertWeights, x, out=None):
 
 
 def moe_layer(x, w_router, weights: ExpertWeights, n_group, topk_group, topk, combine_scale=2.5):
-    """Route -> quantize activations -> expert MLP.  Returns (out, ids, wts)."""
-    ids, wts = route(x, w_router, n_group, topk_group, topk)
-    fmt = "nvfp4" if weights.format == FMT_NVFP4 else "fp8"
-    xq = quantize_activations(x, fmt)
+    """Route -> quantize activations (NVFP4: in the same call) -> expert MLP.  Returns (out, ids, wts)."""
+    if weights.format == FMT_NVFP4:
+        ids, wts, xq = route_nvfp4_quantize(x, w_router, n_group, topk_group, topk)
+    else:
+        ids, wts = route(x, w_router, n_group, topk_group, topk)
+        xq = quantize_activations(x, "fp8")
     out = moe_expert_mlp(weights, xq, ids, wts, combine_scale)
     return out, ids, wts
 

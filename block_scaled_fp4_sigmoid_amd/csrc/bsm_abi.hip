@@ -284,6 +284,29 @@ int bsm_route(const void* x, int x_dtype, int64_t T, int64_t H, const void* w_ro
                     "bsm_route");
 }
 
+size_t bsm_route_nvfp4_quantize_workspace_size(int64_t T, int64_t H, int64_t E) {
+  if (T < 0 || H <= 0 || E <= 0) return 0;
+  return bsm::route_q_ws(T, H, E);
+}
+
+int bsm_route_nvfp4_quantize(const void* x, int x_dtype, int64_t T, int64_t H, const void* w_router, int w_dtype,
+                             int64_t E, int n_group, int topk_group, int topk, int32_t* topk_ids,
+                             float* topk_weights, float* scores, uint8_t* codes, uint8_t* scales,
+                             float* global_scale, void* ws, size_t ws_bytes, bsm_stream_t stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype)) return fail(BSM_ERR_INVALID_ARG, "dtype must be BSM_BF16 or BSM_F32");
+  if (int r = route_checks(T, H, E, n_group, topk_group, topk)) return r;
+  if (H % 16 != 0) return fail(BSM_ERR_INVALID_ARG, "H (%lld) must be a multiple of 16", (long long)H);
+  if (T == 0) return ok();
+  if (!x || !w_router || !topk_ids || !topk_weights || !codes || !scales || !global_scale)
+    return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(x, 32) || !aligned(codes, 8)) return fail(BSM_ERR_INVALID_ARG, "x must be 32-byte and codes 8-byte aligned");
+  if (int r = check_ws(ws, ws_bytes, bsm::route_q_ws(T, H, E))) return r;
+  return hip_status(bsm::launch_route_nvfp4_quantize(x, x_dtype == BSM_BF16, T, H, w_router, w_dtype == BSM_BF16, E,
+                                                     n_group, topk_group, topk, topk_ids, topk_weights, scores,
+                                                     codes, scales, global_scale, ws, (hipStream_t)stream),
+                    "bsm_route_nvfp4_quantize");
+}
+
 int bsm_route_diagnostics(const void* ws, int64_t T, int64_t H, int64_t E, int32_t* diag, bsm_stream_t stream) {
   if (T < 0 || H <= 0 || E <= 0) return fail(BSM_ERR_INVALID_ARG, "bad shape");
   if (!ws || !diag) return fail(BSM_ERR_INVALID_ARG, "NULL pointer argument");

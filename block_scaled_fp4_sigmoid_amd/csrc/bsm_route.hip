@@ -780,21 +780,38 @@ __device__ inline uint32_t max_mag16(const uint32_t* u) {
   return mx;
 }
 
+// The same over the values that are not NaN (patterns above 0x7F80): max|x| as the NVFP4 global scale takes it.
+__device__ inline uint32_t max_fin16(const uint32_t* u) {
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo = u[i] & 0x7FFFu, hi = (u[i] >> 16) & 0x7FFFu;
+    mx = max(mx, max(lo > 0x7F80u ? 0u : lo, hi > 0x7F80u ? 0u : hi));
+  }
+  return mx;
+}
+
 // WPR waves share a row (1, or 4 when there are few rows); NC > 0: the row
 // (at most 64 WPR NC half chunks) stays in registers between the exponent pass
-// and the digit pass; NC == 0: the digit pass reads it again.
+// and the digit pass; NC == 0: the digit pass reads it again.  rowam (optional,
+// WPR > 1 only): for each row of x, the bit pattern of its largest magnitude that
+// is not NaN, as a binary32 (the selection kernel folds these into *xam, zeroed here).
 template <int NC, int WPR>
 __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                 int64_t T, int64_t E, int64_t H, int64_t ncp,
                                                 int8_t* __restrict__ dig, int* __restrict__ rexp,
                                                 double* __restrict__ rres, double* __restrict__ norm,
-                                                int* __restrict__ ulist, int* __restrict__ diag) {
+                                                int* __restrict__ ulist, int* __restrict__ diag,
+                                                uint32_t* __restrict__ rowam, uint32_t* __restrict__ xam) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (blockIdx.x == 0 && tid < 4) {  // the list filled by k_logits_i8; the selection kernel's counters
-    if (tid == 0) *ulist = 0;
+    if (tid == 0) {
+      *ulist = 0;
+      if (xam) *xam = 0u;
+    }
     diag[tid] = 0;
   }
-  __shared__ uint32_t s_mx[4];
+  __shared__ uint32_t s_mx[4], s_fm[4];
   __shared__ double s_res[4];
   const int sub = (tid >> 6) % WPR;  // this wave's share of the row
   const int64_t r = (int64_t)blockIdx.x * (4 / WPR) + (tid >> 6) / WPR;
@@ -812,6 +829,8 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
   constexpr int NCC = NC > 0 ? NC : 1;
   uint32_t cu[NCC][8];
   uint32_t mx = 0u;  // largest magnitude bit pattern
+  uint32_t fm = 0u;  // the same without NaN (x rows, when rowam is given)
+  const bool want_fm = WPR > 1 && rowam && r < T;  // the same in the workgroup
   if constexpr (NC > 0) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {  // clamped loads: no load under a branch
@@ -821,19 +840,31 @@ __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, 
 #pragma unroll
         for (int i = 0; i < 8; ++i) cu[c][i] = 0u;
       mx = max(mx, max_mag16(cu[c]));
+      if constexpr (WPR > 1)
+        if (want_fm) fm = max(fm, max_fin16(cu[c]));
     }
   } else {
     for (int j = lj; j < nh; j += JS) {
       load16(j, cu[0]);
       mx = max(mx, max_mag16(cu[0]));
+      if constexpr (WPR > 1)
+        if (want_fm) fm = max(fm, max_fin16(cu[0]));
     }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
   if constexpr (WPR > 1) {
-    if (lane == 0) s_mx[tid >> 6] = mx;
+    if (want_fm)
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) fm = max(fm, (uint32_t)__shfl_xor((int)fm, o, 64));
+    if (lane == 0) {
+      s_mx[tid >> 6] = mx;
+      s_fm[tid >> 6] = fm;
+    }
     __syncthreads();
     mx = max(max(s_mx[0], s_mx[1]), max(s_mx[2], s_mx[3]));
+    fm = max(max(s_fm[0], s_fm[1]), max(s_fm[2], s_fm[3]));
+    if (want_fm && lane == 0 && sub == 0) rowam[r] = fm << 16;
   }
   const bool bad = mx >= 0x7F80u;  // Inf or NaN in the row
   const int meb = (int)(mx >> 7);
@@ -1318,7 +1349,8 @@ __global__ __launch_bounds__(256) void k_select256_fin(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int64_t H,
     const int64_t* __restrict__ spart, int64_t s8, const int* __restrict__ rexp, const double* __restrict__ rres,
     const double* __restrict__ norm, float* __restrict__ logits, int lpg, int topk_group, int topk,
-    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ scores, int* __restrict__ diag) {
+    int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ scores, int* __restrict__ diag,
+    const uint32_t* __restrict__ rowam, uint32_t* __restrict__ xam) {
   constexpr int64_t E = 256;
   __shared__ __attribute__((aligned(16))) float s_log[E];
   __shared__ int s_list[E];
@@ -1326,7 +1358,10 @@ __global__ __launch_bounds__(256) void k_select256_fin(
   __shared__ ExactLds xl;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t t = blockIdx.x, e = tid;
-  if (tid == 0) s_n = 0;
+  if (tid == 0) {
+    s_n = 0;
+    if (xam) atomicMax(xam, rowam[t]);  // max|x| over the tokens (order independent)
+  }
   __syncthreads();
   int64_t hi = 0, lo = 0;
 #pragma unroll 8
@@ -1357,13 +1392,18 @@ __global__ __launch_bounds__(256) void k_select256_fin(
   select256_wave(*reinterpret_cast<const float4*>(&s_log[4 * lane]), t, lpg, topk_group, topk, ids, wts, scores, diag);
 }
 
+// fewer rows than waves in flight on the chip: four waves per row
+bool slice8_few(int64_t T, int64_t E) { return T + E < 4096; }
+
+// rowam and xam are taken with four waves per row only (slice8_few)
 void launch_slice8(const uint16_t* x, const uint16_t* w, int64_t T, int64_t E, int64_t H, int64_t ncp, int8_t* dig,
-                   int* rexp, double* rres, double* norm, int* ulist, int* diag, hipStream_t st) {
-  // fewer rows than waves in flight on the chip: four waves per row
-  const bool few = T + E < 4096;
+                   int* rexp, double* rres, double* norm, int* ulist, int* diag, hipStream_t st,
+                   uint32_t* rowam = nullptr, uint32_t* xam = nullptr) {
+  const bool few = slice8_few(T, E);
   const unsigned g = (unsigned)(few ? T + E : (T + E + 3) / 4);
   const int64_t nc = (H / 16 + (few ? 255 : 63)) / (few ? 256 : 64);  // half chunks per lane
-#define BSM_SLICE8(N, W) k_slice8<N, W><<<g, 256, 0, st>>>(x, w, T, E, H, ncp, dig, rexp, rres, norm, ulist, diag)
+#define BSM_SLICE8(N, W) \
+  k_slice8<N, W><<<g, 256, 0, st>>>(x, w, T, E, H, ncp, dig, rexp, rres, norm, ulist, diag, rowam, xam)
 #define BSM_SLICE8_NC(W)       \
   switch (nc) {                \
     case 1: BSM_SLICE8(1, W); break; \
@@ -1395,7 +1435,8 @@ size_t route_ws(int64_t T, int64_t H, int64_t E) { return route_layout(T, H, E).
 size_t route_diag_offset(int64_t T, int64_t H, int64_t E) { return route_layout(T, H, E).diag; }
 
 hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void* w, bool wb, int64_t E, int n_group,
-                        int topk_group, int topk, int32_t* ids, float* wts, float* scores, void* ws_, hipStream_t st) {
+                        int topk_group, int topk, int32_t* ids, float* wts, float* scores, void* ws_, hipStream_t st,
+                        uint32_t* rowam, uint32_t* xam, bool* xam_done) {
   const RouteWs L = route_layout(T, H, E);
   uint8_t* ws = reinterpret_cast<uint8_t*>(ws_);
   float* logits = reinterpret_cast<float*>(ws + L.logits);
@@ -1405,6 +1446,8 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   int* lsb = L.rb ? nullptr : reinterpret_cast<int*>(ws + L.lsb);
   double* part = L.rb ? nullptr : reinterpret_cast<double*>(ws + L.part);
   int* ulist = L.rb ? nullptr : reinterpret_cast<int*>(ws + L.ulist);
+  if (xam_done) *xam_done = false;
+  uint32_t* xamr = slice8_few(T, E) ? xam : nullptr;  // the row maxima come with four waves per row
   if (T == 0) return hipSuccess;
   stage_mark(1, 0, st);
   const unsigned nrs = (unsigned)((T + E + 3) / 4);
@@ -1430,14 +1473,15 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
   if (i8 && L.rb && sel4) { /* the selection kernel finishes the logits */                                  \
     launch_slice8(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), T, E, H, L.ncp,  \
-                  dig, rexp, rres, norm, ulist, diag, st);                                                 \
+                  dig, rexp, rres, norm, ulist, diag, st, xamr ? rowam : nullptr, xamr);                   \
     k_logits_i8<true><<<dim3(gl.x * gl.y, (unsigned)L.s8), 256, 0, st>>>(dig, T, E, L.ncp, L.sps8, rexp,     \
                                                                          rres, logits, ulist, blk, spart); \
     stage_mark(1, 1, st);                                                                                  \
     k_select256_fin<<<(unsigned)T, 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x),                      \
                                                  reinterpret_cast<const uint16_t*>(w), T, H, spart, L.s8, rexp, \
                                                  rres, norm, logits, (int)(E / n_group) / 4, topk_group,   \
-                                                 topk, ids, wts, scores, diag);                            \
+                                                 topk, ids, wts, scores, diag, rowam, xamr);               \
+    if (xam_done) *xam_done = xamr != nullptr;                                                             \
   } else {                                                                                                 \
   if (i8 && L.rb) {                                                                                        \
     launch_slice8(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), T, E, H, L.ncp,  \
@@ -1484,6 +1528,40 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
 #undef BSM_ROUTE_DISPATCH
   stage_mark(1, 2, st);
   return hipGetLastError();
+}
+
+// Workspace of the routing + quantization call: the router's, then the max|x| word and the row maxima (when
+// the router's pass over x yields them), then the quantization's partial maxima (when it does not).
+namespace {
+struct RouteQWs {
+  size_t xam, rowam, parts, total;
+};
+RouteQWs route_q_layout(int64_t T, int64_t H, int64_t E) {
+  RouteQWs L;
+  L.xam = align256(route_ws(T, H, E));
+  L.rowam = L.xam + 256;
+  L.parts = L.rowam + align256(sizeof(uint32_t) * (size_t)(T > 0 ? T : 1));
+  L.total = L.parts + nvfp4_quant_ws(1, T, H);
+  return L;
+}
+}  // namespace
+
+size_t route_q_ws(int64_t T, int64_t H, int64_t E) { return route_q_layout(T, H, E).total; }
+
+hipError_t launch_route_nvfp4_quantize(const void* x, bool xb, int64_t T, int64_t H, const void* w, bool wb,
+                                       int64_t E, int n_group, int topk_group, int topk, int32_t* ids, float* wts,
+                                       float* scores, uint8_t* codes, uint8_t* scales, float* gs, void* ws_,
+                                       hipStream_t st) {
+  const RouteQWs L = route_q_layout(T, H, E);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(ws_);
+  uint32_t* xam = reinterpret_cast<uint32_t*>(ws + L.xam);
+  bool fused = false;
+  hipError_t err = launch_route(x, xb, T, H, w, wb, E, n_group, topk_group, topk, ids, wts, scores, ws_, st,
+                                reinterpret_cast<uint32_t*>(ws + L.rowam), xam, &fused);
+  if (err != hipSuccess) return err;
+  if (fused)  // S_g = max|x| / 2688 from the router's pass over x: the encoding pass only
+    return launch_nvfp4_quantize_from_amax(x, xb, 1, T, H, codes, scales, gs, xam, nullptr, st, nullptr);
+  return launch_nvfp4_quantize(x, xb, 1, T, H, codes, scales, gs, true, reinterpret_cast<float*>(ws + L.parts), st);
 }
 
 hipError_t launch_route_diag(const void* ws, int64_t T, int64_t H, int64_t E, int32_t* dst, hipStream_t st) {

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define BSM_ABI_VERSION 4
+#define BSM_ABI_VERSION 5
 
 typedef struct ihipStream_t* bsm_stream_t; /* identical to hipStream_t */
 
@@ -179,6 +179,21 @@ size_t bsm_route_workspace_size(int64_t T, int64_t H, int64_t E);
 int bsm_route(const void* x, int x_dtype, int64_t T, int64_t H, const void* w_router, int w_dtype, int64_t E,
               int n_group, int topk_group, int topk, int32_t* topk_ids, float* topk_weights, float* scores,
               void* ws, size_t ws_bytes, bsm_stream_t stream);
+
+/* Routing and NVFP4 quantization of the same activations in one call [MOE] [NVFP4]: the outputs of
+ * bsm_route(x, ..., topk_ids, topk_weights, scores) and of
+ * bsm_nvfp4_quantize(x, x_dtype, 1, T, H, codes, scales, global_scale, BSM_GS_DYNAMIC), bit for bit (the
+ * router's definition above; the quantization's in "NVFP4 quantization" page, "Quantization scheme").
+ * Where the router takes its int8 path for small batches (bf16 x and w_router, E = 256), its pass over x
+ * also yields max|x| (NaN excluded, as the quantization takes it), so the quantization does not read x
+ * twice.  Arguments and requirements: those of both calls (x 32-byte aligned, H % 16 == 0, codes [T, H/2]
+ * 8-byte aligned, scales [T, H/16], global_scale one float); ws of
+ * bsm_route_nvfp4_quantize_workspace_size bytes, 256-byte aligned.  Enqueued on stream; T == 0 does nothing. */
+size_t bsm_route_nvfp4_quantize_workspace_size(int64_t T, int64_t H, int64_t E);
+int bsm_route_nvfp4_quantize(const void* x, int x_dtype, int64_t T, int64_t H, const void* w_router, int w_dtype,
+                             int64_t E, int n_group, int topk_group, int topk, int32_t* topk_ids,
+                             float* topk_weights, float* scores, uint8_t* codes, uint8_t* scales,
+                             float* global_scale, void* ws, size_t ws_bytes, bsm_stream_t stream);
 
 /* Route diagnostics read back from the workspace of the last bsm_route call
  * enqueued with it: number of logits and scores that needed the exact

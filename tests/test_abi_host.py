@@ -31,7 +31,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bsm_abi_version() == 4
+    assert lib.bsm_abi_version() == 5
     assert lib.bsm_status_str(0) == b"BSM_OK"
     assert lib.bsm_status_str(3) == b"BSM_ERR_WORKSPACE"
 
@@ -79,6 +79,22 @@ def test_fp8_and_dequant_validation(lib):
 def test_route_validation(lib, E, G, kg, k, code):
     r = lib.bsm_route(FAKE, 1, 64, 5120, FAKE, 1, E, G, kg, k, FAKE, FAKE, None, None, 0, None)
     assert r == code, _err(lib)
+
+
+def test_route_nvfp4_quantize_validation(lib):
+    """The routing + quantization call takes both calls' rules, checked before anything is enqueued."""
+    f = lib.bsm_route_nvfp4_quantize
+    args = lambda T=64, H=5120, x=FAKE, E=256, G=8, codes=FAKE, ws=None, wsb=0: (
+        x, 1, T, H, FAKE, 1, E, G, 4, 8, FAKE, FAKE, None, codes, FAKE, FAKE, ws, wsb, None)
+    assert f(*args()) == 3  # valid, missing workspace
+    assert f(*args(G=7)) == 1  # E % n_group
+    assert f(*args(H=5128)) == 1  # H % 16
+    assert f(*args(x=ctypes.c_void_p(0x100010))) == 1  # x not 32-byte aligned
+    assert f(*args(codes=None)) == 1
+    need = lib.bsm_route_nvfp4_quantize_workspace_size(64, 5120, 256)
+    assert need >= lib.bsm_route_workspace_size(64, 5120, 256) + lib.bsm_nvfp4_quantize_workspace_size(1, 64, 5120)
+    assert f(*args(ws=ctypes.c_void_p(0x200000), wsb=need - 1)) == 3
+    assert f(*args(T=0)) == 0
 
 
 def test_moe_validation(lib):
