@@ -42,11 +42,13 @@ hipError_t launch_fp8_quantize(const void* x, bool x_bf16, int64_t R, int64_t C,
 
 // ---- router ---------------------------------------------------------------
 size_t route_ws(int64_t T, int64_t H, int64_t E);
-// rowam, xam (optional): when the path takes them (*xam_done), each x row's largest magnitude that is not NaN
-// (rowam[T], binary32 bits) and their maximum (*xam), for the NVFP4 quantization of the same x
+// rowam, xcodes, xscales, xgs (optional): when the path takes them (*x_done), the NVFP4 quantization of the
+// same x (DYNAMIC global scale) into xcodes, xscales, xgs, with each x row's largest magnitude that is not
+// NaN in rowam[T] (binary32 bits)
 hipError_t launch_route(const void* x, bool x_bf16, int64_t T, int64_t H, const void* w, bool w_bf16, int64_t E,
                         int n_group, int topk_group, int topk, int32_t* ids, float* wts, float* scores, void* ws,
-                        hipStream_t st, uint32_t* rowam = nullptr, uint32_t* xam = nullptr, bool* xam_done = nullptr);
+                        hipStream_t st, uint32_t* rowam = nullptr, uint8_t* xcodes = nullptr,
+                        uint8_t* xscales = nullptr, float* xgs = nullptr, bool* x_done = nullptr);
 // routing and NVFP4 quantization (DYNAMIC global scale) of the same x [T, H]
 size_t route_q_ws(int64_t T, int64_t H, int64_t E);
 hipError_t launch_route_nvfp4_quantize(const void* x, bool x_bf16, int64_t T, int64_t H, const void* w, bool w_bf16,

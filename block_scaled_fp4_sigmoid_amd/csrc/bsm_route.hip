@@ -795,20 +795,17 @@ __device__ inline uint32_t max_fin16(const uint32_t* u) {
 // (at most 64 WPR NC half chunks) stays in registers between the exponent pass
 // and the digit pass; NC == 0: the digit pass reads it again.  rowam (optional,
 // WPR > 1 only): for each row of x, the bit pattern of its largest magnitude that
-// is not NaN, as a binary32 (the selection kernel folds these into *xam, zeroed here).
+// is not NaN, as a binary32 (max|x| for the NVFP4 quantization of x).
 template <int NC, int WPR>
 __global__ __launch_bounds__(256) void k_slice8(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                 int64_t T, int64_t E, int64_t H, int64_t ncp,
                                                 int8_t* __restrict__ dig, int* __restrict__ rexp,
                                                 double* __restrict__ rres, double* __restrict__ norm,
                                                 int* __restrict__ ulist, int* __restrict__ diag,
-                                                uint32_t* __restrict__ rowam, uint32_t* __restrict__ xam) {
+                                                uint32_t* __restrict__ rowam) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (blockIdx.x == 0 && tid < 4) {  // the list filled by k_logits_i8; the selection kernel's counters
-    if (tid == 0) {
-      *ulist = 0;
-      if (xam) *xam = 0u;
-    }
+    if (tid == 0) *ulist = 0;
     diag[tid] = 0;
   }
   __shared__ uint32_t s_mx[4], s_fm[4];
@@ -1345,22 +1342,32 @@ __global__ __launch_bounds__(64 * kSel4Tokens) void k_select256(
 // recomputed exactly by the whole workgroup, one after another (exact_logit_wg), and counted in
 // diag[0]; then wave 0 selects.  (At large batches the exact recomputation stays in k_exact_list: its
 // slow path needs per-lane scratch, which would limit how many selection workgroups run at once.)
+// xcodes (optional): the workgroup also quantizes its token's row of x to NVFP4 ("NVFP4 quantization"
+// page, "Quantization scheme") while wave 0 selects: S_g = max|x| / 2688 from the row maxima of k_slice8
+// (rowam, T of them, reduced by every workgroup: no atomics), s_b = E4M3(a_b / (6 S_g)),
+// q = E2M1(fl32(x / (s_b S_g))) by the division itself; workgroup 0 writes S_g.
 __global__ __launch_bounds__(256) void k_select256_fin(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t T, int64_t H,
     const int64_t* __restrict__ spart, int64_t s8, const int* __restrict__ rexp, const double* __restrict__ rres,
     const double* __restrict__ norm, float* __restrict__ logits, int lpg, int topk_group, int topk,
     int32_t* __restrict__ ids, float* __restrict__ wts, float* __restrict__ scores, int* __restrict__ diag,
-    const uint32_t* __restrict__ rowam, uint32_t* __restrict__ xam) {
+    const uint32_t* __restrict__ rowam, uint8_t* __restrict__ xcodes, uint8_t* __restrict__ xscales,
+    float* __restrict__ xgs) {
   constexpr int64_t E = 256;
   __shared__ __attribute__((aligned(16))) float s_log[E];
   __shared__ int s_list[E];
   __shared__ int s_n;
+  __shared__ uint32_t s_am[4];
   __shared__ ExactLds xl;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t t = blockIdx.x, e = tid;
-  if (tid == 0) {
-    s_n = 0;
-    if (xam) atomicMax(xam, rowam[t]);  // max|x| over the tokens (order independent)
+  if (tid == 0) s_n = 0;
+  if (xcodes) {  // max|x|: the largest of the row maxima (non-negative binary32 bits order as their values)
+    uint32_t am = 0u;
+    for (int64_t i = tid; i < T; i += 256) am = max(am, rowam[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o, 64));
+    if (lane == 0) s_am[tid >> 6] = am;
   }
   __syncthreads();
   int64_t hi = 0, lo = 0;
@@ -1388,22 +1395,55 @@ __global__ __launch_bounds__(256) void k_select256_fin(
     if (tid == 0) atomicAdd(&diag[0], n);
     __syncthreads();
   }
-  if (tid >= 64) return;  // wave 0 selects; no barrier follows
+  if (tid >= 64) {  // waves 1-3 quantize the token's row while wave 0 selects; no barrier follows
+    if (xcodes) {
+      const float S = u2f(max(max(s_am[0], s_am[1]), max(s_am[2], s_am[3]))) / 2688.0f;
+      if (t == 0 && tid == 64) *xgs = S;
+      const float d1 = 6.0f * S;
+      const int64_t nb = H / 16;
+      for (int64_t j = tid - 64; j < nb; j += 192) {
+        const int64_t f = t * nb + j;
+        const uint4 q0 = *reinterpret_cast<const uint4*>(x + 16 * f);
+        const uint4 q1 = *reinterpret_cast<const uint4*>(x + 16 * f + 8);
+        const uint32_t u[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[2 * i] = u2f(u[i] << 16);
+          v[2 * i + 1] = u2f(u[i] & 0xFFFF0000u);
+        }
+        float ab = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
+        const uint32_t sc = S != 0.0f ? e4m3_code_mag(ab / d1) : 0u;
+        const float sv = e4m3_value_mag(sc), d2 = sv * S;
+        uint32_t c[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t q = ((f2u(v[i]) >> 31) << 3) | (sv != 0.0f ? e2m1_code_mag(fabsf(v[i]) / d2) : 0u);
+          c[i >> 3] |= q << (4 * (i & 7));
+        }
+        *reinterpret_cast<uint2*>(xcodes + 8 * f) = make_uint2(c[0], c[1]);
+        xscales[f] = (uint8_t)sc;
+      }
+    }
+    return;
+  }
   select256_wave(*reinterpret_cast<const float4*>(&s_log[4 * lane]), t, lpg, topk_group, topk, ids, wts, scores, diag);
 }
 
 // fewer rows than waves in flight on the chip: four waves per row
 bool slice8_few(int64_t T, int64_t E) { return T + E < 4096; }
 
-// rowam and xam are taken with four waves per row only (slice8_few)
+// rowam is taken with four waves per row only (slice8_few)
 void launch_slice8(const uint16_t* x, const uint16_t* w, int64_t T, int64_t E, int64_t H, int64_t ncp, int8_t* dig,
                    int* rexp, double* rres, double* norm, int* ulist, int* diag, hipStream_t st,
-                   uint32_t* rowam = nullptr, uint32_t* xam = nullptr) {
+                   uint32_t* rowam = nullptr) {
   const bool few = slice8_few(T, E);
   const unsigned g = (unsigned)(few ? T + E : (T + E + 3) / 4);
   const int64_t nc = (H / 16 + (few ? 255 : 63)) / (few ? 256 : 64);  // half chunks per lane
 #define BSM_SLICE8(N, W) \
-  k_slice8<N, W><<<g, 256, 0, st>>>(x, w, T, E, H, ncp, dig, rexp, rres, norm, ulist, diag, rowam, xam)
+  k_slice8<N, W><<<g, 256, 0, st>>>(x, w, T, E, H, ncp, dig, rexp, rres, norm, ulist, diag, rowam)
 #define BSM_SLICE8_NC(W)       \
   switch (nc) {                \
     case 1: BSM_SLICE8(1, W); break; \
@@ -1436,7 +1476,7 @@ size_t route_diag_offset(int64_t T, int64_t H, int64_t E) { return route_layout(
 
 hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void* w, bool wb, int64_t E, int n_group,
                         int topk_group, int topk, int32_t* ids, float* wts, float* scores, void* ws_, hipStream_t st,
-                        uint32_t* rowam, uint32_t* xam, bool* xam_done) {
+                        uint32_t* rowam, uint8_t* xcodes, uint8_t* xscales, float* xgs, bool* x_done) {
   const RouteWs L = route_layout(T, H, E);
   uint8_t* ws = reinterpret_cast<uint8_t*>(ws_);
   float* logits = reinterpret_cast<float*>(ws + L.logits);
@@ -1446,8 +1486,9 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   int* lsb = L.rb ? nullptr : reinterpret_cast<int*>(ws + L.lsb);
   double* part = L.rb ? nullptr : reinterpret_cast<double*>(ws + L.part);
   int* ulist = L.rb ? nullptr : reinterpret_cast<int*>(ws + L.ulist);
-  if (xam_done) *xam_done = false;
-  uint32_t* xamr = slice8_few(T, E) ? xam : nullptr;  // the row maxima come with four waves per row
+  if (x_done) *x_done = false;
+  // the row maxima come with four waves per row; the selection kernel reads a row as 16-value blocks
+  uint8_t* xc = slice8_few(T, E) && H % 16 == 0 ? xcodes : nullptr;
   if (T == 0) return hipSuccess;
   stage_mark(1, 0, st);
   const unsigned nrs = (unsigned)((T + E + 3) / 4);
@@ -1473,15 +1514,15 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
 #define BSM_ROUTE_DISPATCH(XB, WB)                                                                          \
   if (i8 && L.rb && sel4) { /* the selection kernel finishes the logits */                                  \
     launch_slice8(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), T, E, H, L.ncp,  \
-                  dig, rexp, rres, norm, ulist, diag, st, xamr ? rowam : nullptr, xamr);                   \
+                  dig, rexp, rres, norm, ulist, diag, st, xc ? rowam : nullptr);                           \
     k_logits_i8<true><<<dim3(gl.x * gl.y, (unsigned)L.s8), 256, 0, st>>>(dig, T, E, L.ncp, L.sps8, rexp,     \
                                                                          rres, logits, ulist, blk, spart); \
     stage_mark(1, 1, st);                                                                                  \
     k_select256_fin<<<(unsigned)T, 256, 0, st>>>(reinterpret_cast<const uint16_t*>(x),                      \
                                                  reinterpret_cast<const uint16_t*>(w), T, H, spart, L.s8, rexp, \
                                                  rres, norm, logits, (int)(E / n_group) / 4, topk_group,   \
-                                                 topk, ids, wts, scores, diag, rowam, xamr);               \
-    if (xam_done) *xam_done = xamr != nullptr;                                                             \
+                                                 topk, ids, wts, scores, diag, rowam, xc, xscales, xgs);   \
+    if (x_done) *x_done = xc != nullptr;                                                                   \
   } else {                                                                                                 \
   if (i8 && L.rb) {                                                                                        \
     launch_slice8(reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(w), T, E, H, L.ncp,  \
@@ -1530,16 +1571,15 @@ hipError_t launch_route(const void* x, bool xb, int64_t T, int64_t H, const void
   return hipGetLastError();
 }
 
-// Workspace of the routing + quantization call: the router's, then the max|x| word and the row maxima (when
-// the router's pass over x yields them), then the quantization's partial maxima (when it does not).
+// Workspace of the routing + quantization call: the router's, then the row maxima of x (when the router's
+// pass over x yields them), then the quantization's partial maxima (when it does not).
 namespace {
 struct RouteQWs {
-  size_t xam, rowam, parts, total;
+  size_t rowam, parts, total;
 };
 RouteQWs route_q_layout(int64_t T, int64_t H, int64_t E) {
   RouteQWs L;
-  L.xam = align256(route_ws(T, H, E));
-  L.rowam = L.xam + 256;
+  L.rowam = align256(route_ws(T, H, E));
   L.parts = L.rowam + align256(sizeof(uint32_t) * (size_t)(T > 0 ? T : 1));
   L.total = L.parts + nvfp4_quant_ws(1, T, H);
   return L;
@@ -1554,13 +1594,10 @@ hipError_t launch_route_nvfp4_quantize(const void* x, bool xb, int64_t T, int64_
                                        hipStream_t st) {
   const RouteQWs L = route_q_layout(T, H, E);
   uint8_t* ws = reinterpret_cast<uint8_t*>(ws_);
-  uint32_t* xam = reinterpret_cast<uint32_t*>(ws + L.xam);
   bool fused = false;
   hipError_t err = launch_route(x, xb, T, H, w, wb, E, n_group, topk_group, topk, ids, wts, scores, ws_, st,
-                                reinterpret_cast<uint32_t*>(ws + L.rowam), xam, &fused);
-  if (err != hipSuccess) return err;
-  if (fused)  // S_g = max|x| / 2688 from the router's pass over x: the encoding pass only
-    return launch_nvfp4_quantize_from_amax(x, xb, 1, T, H, codes, scales, gs, xam, nullptr, st, nullptr);
+                                reinterpret_cast<uint32_t*>(ws + L.rowam), codes, scales, gs, &fused);
+  if (err != hipSuccess || fused) return err;  // fused: the selection kernel quantized x
   return launch_nvfp4_quantize(x, xb, 1, T, H, codes, scales, gs, true, reinterpret_cast<float*>(ws + L.parts), st);
 }
 

@@ -185,8 +185,8 @@ int bsm_route(const void* x, int x_dtype, int64_t T, int64_t H, const void* w_ro
  * bsm_nvfp4_quantize(x, x_dtype, 1, T, H, codes, scales, global_scale, BSM_GS_DYNAMIC), bit for bit (the
  * router's definition above; the quantization's in "NVFP4 quantization" page, "Quantization scheme").
  * Where the router takes its int8 path for small batches (bf16 x and w_router, E = 256), its pass over x
- * also yields max|x| (NaN excluded, as the quantization takes it), so the quantization does not read x
- * twice.  Arguments and requirements: those of both calls (x 32-byte aligned, H % 16 == 0, codes [T, H/2]
+ * also yields max|x| (NaN excluded, as the quantization takes it) and its selection kernel quantizes each
+ * token's row while it selects, so the quantization launches nothing of its own.  Arguments and requirements: those of both calls (x 32-byte aligned, H % 16 == 0, codes [T, H/2]
  * 8-byte aligned, scales [T, H/16], global_scale one float); ws of
  * bsm_route_nvfp4_quantize_workspace_size bytes, 256-byte aligned.  Enqueued on stream; T == 0 does nothing. */
 size_t bsm_route_nvfp4_quantize_workspace_size(int64_t T, int64_t H, int64_t E);

@@ -74,6 +74,19 @@ def test_route_quant_special_rows(gpu_lib):
     assert gs[0] == np.float32(amax) / np.float32(2688.0)
 
 
+def test_route_quant_wide_range(gpu_lib):
+    """Blocks spread over 2^-12 .. 2^8 of each other: E4M3 block scales down to the subnormal codes and zero
+    scales, where the division by s_b S_g and the quantizer's threshold table must agree bit for bit."""
+    wr = W.router_weights(W.DECODE)
+    x = _x(64, 5120, 21)
+    t, j = np.meshgrid(np.arange(64), np.arange(5120 // 16), indexing="ij")
+    x *= np.repeat(np.exp2(((t * 7 + j * 3) % 21) - 12.0), 16, axis=1).astype(np.float32)
+    _, _, _, codes, scales, gs = _both(gpu_lib, to_dev_bf16(x), to_dev_bf16(wr), 8, 4, 8)
+    assert (scales < 8).any() and (scales == 0).any()  # subnormal and zero block scales occur
+    oc, osc, og = Q.nvfp4_quantize(x)
+    assert np.array_equal(codes, oc) and np.array_equal(scales, osc)
+
+
 def test_route_quant_all_zero(gpu_lib):
     wr = W.router_weights(W.DECODE)
     x = np.zeros((8, 5120), np.float32)
