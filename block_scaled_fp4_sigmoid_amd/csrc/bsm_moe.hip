@@ -1457,6 +1457,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   // bcol .. +15 (canonical rows: row 32 i + tid / 8, part tid % 8); the group of K step s starts at byte
   // s * kSB of a row, at 2 s * kSB of a double row.
   const int brow0 = pairs ? 16 * (tid >> 7) + ((tid >> 4) & 7) + (((tid & 7) >> 2) << 3) : tid / kBP;
+  // Weight row r of the tile sits in group-buffer row r ^ (bit 3 of r moved to bit 1): rows are 33 dwords
+  // apart, so a pair-layout store's rows p and p + 8 (same bytes of both) would share banks; permuted they
+  // fall on four different banks mod 4, and the fragment reads of 32 consecutive rows stay on 32 banks.
+  auto bg_row = [](int r) { return r ^ (((r >> 3) & 1) << 1); };
   const int bcol = pairs ? ((tid >> 3) & 1) * 64 + (tid & 3) * 16 : 16 * bpart;
   const int smul = pairs ? 2 : 1;
   auto boff_of = [&](int i) -> uint32_t {
@@ -1507,7 +1511,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
   auto bstore = [&]() {  // weight registers of a group into the group buffer, scale dwords by K step
 #pragma unroll
     for (int i = 0; i < kBI; ++i) {
-      uint32_t* d = reinterpret_cast<uint32_t*>(&Bg[32 * i + brow0][bcol]);
+      uint32_t* d = reinterpret_cast<uint32_t*>(&Bg[bg_row(32 * i + brow0)][bcol]);
       d[0] = rb[i].x;
       d[1] = rb[i].y;
       d[2] = rb[i].z;
@@ -1612,7 +1616,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(const _Float16* __restrict_
               rd + (mt * 32 + l32) * kAS + (kAdma ? 8 * ((2 * k16 + lh) ^ ((l32 >> 1) & 7)) : k16 * 16 + lh * 8));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int brow = BSM_BIG_BROW(t) + l32;
+          const int brow = bg_row(BSM_BIG_BROW(t) + l32);
           h8v b;
           if constexpr (NV) {
             const uint32_t w = *reinterpret_cast<const uint32_t*>(&Bg[brow][j * 32 + k16 * 8 + lh * 4]);
