@@ -117,8 +117,9 @@ MID = W.LayerConfig("mid", 7, T=700, H=1024, I=512, E=8, n_group=2, topk_group=1
 
 @pytest.mark.parametrize("fmt,T", [("nvfp4", 300), ("nvfp4", 1000), ("fp8", 300), ("fp8", 1000)])
 def test_moe_tiny_shapes_many_tokens(gpu_lib, fmt, T):
-    """Tiny layer with many tokens: experts with 33-64 rows (up to four 16-row tiles, T = 300) and above 64 rows
-    (LDS-tiled kernel, T = 1000) next to small ones, ragged tiles."""
+    """Tiny layer with many tokens (several permutation chunks): experts of at most 32 rows in 16-row tiles of
+    the few-row kernel, and above 32 rows in 128-row tiles of the many-row kernel (33-64 rows at T = 300:
+    one or two live 32-row sub-tiles; more at T = 1000), ragged tiles."""
     _many_tokens(gpu_lib, W.TINY, fmt, T)
 
 
@@ -128,17 +129,24 @@ def test_moe_mid_shapes_many_rows(gpu_lib, fmt):
     _many_tokens(gpu_lib, MID, fmt, MID.T)
 
 
-# Every expert has 35-61 rows here, so the few-row kernel gets full 16-row tiles; with K = 2048 (gate/up)
-# and 1024 (down) their staged activation rows come in several chunks of K (NVFP4: 2 super-steps of 512
-# per chunk at 16 rows, FP8: 3 of 256).
-SKC = W.LayerConfig("skinny-chunks", 8, T=200, H=2048, I=1024, E=8, n_group=2, topk_group=1, topk=2,
+# Few-row experts with full 16-row tiles; with K = 2048 (gate/up) and 1024 (down) their staged activation
+# rows come in several chunks of K (NVFP4: 2 super-steps of 512 per chunk at 16 rows, FP8: 3 of 256).
+# SKC: one permutation chunk (64 tokens, top-6 of 8), every expert at 42-52 rows, so up to four 16-row tiles
+# per expert.  SKM: two chunks (100 tokens, top-2), experts at 16-35 rows: up to 32 rows stay in the
+# few-row kernel (one or two 16-row tiles), the one above in the many-row kernel.
+SKC = W.LayerConfig("skinny-chunks", 8, T=64, H=2048, I=1024, E=8, n_group=2, topk_group=2, topk=6,
+                    router_fp32=True)
+SKM = W.LayerConfig("skinny-chunks", 8, T=100, H=2048, I=1024, E=8, n_group=2, topk_group=1, topk=2,
                     router_fp32=True)
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
-def test_moe_skinny_tiles_in_chunks(gpu_lib, fmt):
+@pytest.mark.parametrize("cfg", [SKC, SKM], ids=["one-chunk", "two-chunks"])
+def test_moe_skinny_tiles_in_chunks(gpu_lib, fmt, cfg):
     """Few-row experts with full 16-row tiles whose activation rows are staged in several chunks of K."""
-    _many_tokens(gpu_lib, SKC, fmt, SKC.T)
+    counts = _many_tokens(gpu_lib, cfg, fmt, cfg.T)
+    few = counts[counts <= (64 if cfg.T <= 64 else 32)]
+    assert few.size > 0 and few.max() > 16
 
 
 def _many_tokens(gpu_lib, cfg, fmt, T):
@@ -178,6 +186,7 @@ def _many_tokens(gpu_lib, cfg, fmt, T):
     e2e = rel_l2(np_(out), ref["out"])
     print(f"{cfg.name} {fmt} T={T}: max rows {counts.max()}, end-to-end rel L2 {e2e:.3e}")
     assert e2e <= 1e-3
+    return counts
 
 
 @pytest.mark.parametrize("T", [64, 300])
