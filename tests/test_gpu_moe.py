@@ -163,9 +163,16 @@ def _many_tokens(gpu_lib, cfg, fmt, T):
     assert np.array_equal(np_(ids), ref["ids"])
     counts = np.bincount(ref["ids"].ravel(), minlength=cfg.E)
     assert counts.max() > (64 if T >= 700 else 32)
+    _check_stages(gpu_lib, cfg, fmt, T, ref["ids"], experts, ref, out, ws)
+    return counts
+
+
+def _check_stages(gpu_lib, cfg, fmt, T, ids, experts, ref, out, ws):
+    """h of every row at the stage gate, h codes and scales bit-exact from the GPU's own h, y of every row
+    from those codes at the stage gate, and the layer output within 1e-3 of the oracle's."""
     P = T * cfg.topk
     st = moe_stages(gpu_lib, fmt, cfg, T, ws, P)
-    _, offsets, row_of_pair, _ = OM.permute(ref["ids"], cfg.E)
+    _, offsets, row_of_pair, _ = OM.permute(ids, cfg.E)
     h_err = rel_l2(st["h"][row_of_pair], ref["h"])
     print(f"{cfg.name} {fmt} T={T}: h rel L2 {h_err:.3e}")
     assert h_err <= STAGE_TOL
@@ -177,16 +184,52 @@ def _many_tokens(gpu_lib, cfg, fmt, T):
         hh = Q.fp8_dequantize_exact(oc, os_)
     assert np.array_equal(st["hc"], oc) and np.array_equal(st["hs"], os_)
     y_ref = np.zeros_like(st["y"])
-    for e in np.unique(ref["ids"]):
+    for e in np.unique(ids):
         rows = np.arange(offsets[e], offsets[e + 1])
         y_ref[rows] = OM.gemm_f32(hh[rows], experts[int(e)].decoded()[2])
     y_err = rel_l2(st["y"], y_ref)
     print(f"{cfg.name} {fmt} T={T}: y rel L2 {y_err:.3e}")
     assert y_err <= STAGE_TOL
     e2e = rel_l2(np_(out), ref["out"])
+    counts = np.bincount(np.asarray(ids).ravel(), minlength=cfg.E)
     print(f"{cfg.name} {fmt} T={T}: max rows {counts.max()}, end-to-end rel L2 {e2e:.3e}")
     assert e2e <= 1e-3
-    return counts
+
+
+# Experts whose row counts sit on each side of the kernel choices with several permutation chunks: 16 / 17
+# (one or two few-row tiles), 32 / 33 (few-row kernel / many-row kernel), 64 / 65 and 128 + 1 (a full
+# 128-row tile and a one-row ragged one); the last expert takes the remaining 44 rows.
+SPLIT = W.LayerConfig("split", 9, T=200, H=1024, I=512, E=8, n_group=2, topk_group=2, topk=2, router_fp32=True)
+SPLIT_ROWS = [16, 17, 32, 33, 64, 65, 129]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_moe_expert_split_boundaries(gpu_lib, fmt):
+    """Given ids (not routed) with the expert row counts above; every stage against the oracle's expert MLP."""
+    cfg = SPLIT
+    T, k, E = cfg.T, cfg.topk, cfg.E
+    counts = SPLIT_ROWS + [T * k - sum(SPLIT_ROWS)]
+    labels = np.repeat(np.arange(E), counts)  # sorted; slots t and t + T never share an expert (max 129 < T)
+    ids_np = np.stack([labels[:T], labels[T:]], axis=1).astype(np.int32)
+    rng = np.random.default_rng(11)
+    ids_np = ids_np[rng.permutation(T)]  # spread every expert's rows over the permutation chunks
+    w_np = rng.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)
+    w_np = (w_np / w_np.sum(axis=1, keepdims=True)).astype(np.float32)
+    x = W.activations(cfg, T=T)
+    masters, w13, w2 = host_masters(cfg)
+    gw = gpu_lib.quantize_expert_weights(w13, w2, fmt)
+    experts = oracle_experts(masters, fmt)
+    xt = to_dev_bf16(x)
+    xq = gpu_lib.quantize_activations(xt, fmt)
+    ids = torch.from_numpy(ids_np).cuda()
+    out, ws = gpu_lib.moe_expert_mlp(gw, xq, ids, torch.from_numpy(w_np).cuda(), cfg.combine_scale,
+                                     return_workspace=True)
+    torch.cuda.synchronize()
+    _, x_hat = OM.quantize_activations(x, fmt)
+    ref = OM.moe_expert_mlp(x_hat, ids_np, w_np, experts, fmt, cfg.combine_scale)
+    st = moe_stages(gpu_lib, fmt, cfg, T, ws, T * k)
+    assert np.array_equal(st["counts"], np.asarray(counts))
+    _check_stages(gpu_lib, cfg, fmt, T, ids_np, experts, ref, out, ws)
 
 
 @pytest.mark.parametrize("T", [64, 300])
