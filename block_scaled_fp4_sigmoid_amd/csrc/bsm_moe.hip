@@ -27,12 +27,13 @@
 //   k_perm_masks   per 64-token chunk: LDS bit mask of the chunk's tokens for
 //                  every expert (atomicOr, order independent) and its popcount
 //   k_perm_scan    per expert: prefix counts over chunks, counts, offsets, and
-//                  two device-side tile lists: experts with <= 64 rows get
+//                  two device-side tile lists: experts with <= 32 rows get
 //                  16-row tiles (skinny kernels), larger ones 128-row tiles
 //                  (many-row kernels); clears the h amax word
 //   k_perm_rows    row of every (token, slot) pair; rows of an expert are in
 //                  token order (stable)
 //   k_perm_small   all three in one workgroup when the batch is one chunk
+//                  (at most 64 tokens: every expert, up to 64 rows, in 16-row tiles)
 //   k_decode_act   activation codes -> FP16 q * s_b (once per call), where a
 //                  GEMM reads FP16 activations: NVFP4 gate/up with many-row
 //                  experts, K not a multiple of the few-row super-step

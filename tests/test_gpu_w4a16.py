@@ -58,7 +58,7 @@ def _check_layer(gpu_lib, cfg, T, x, wr, wr_dev, experts, gw):
 
 @pytest.mark.parametrize("T", [64, 37, 1000])
 def test_w4a16_tiny_layer(gpu_lib, T):
-    """Tiny layer: T = 64, a ragged T = 37, and T = 1000 (experts above 64 rows take the LDS-tiled kernel)."""
+    """Tiny layer: T = 64, a ragged T = 37, and T = 1000 (experts above 32 rows take the LDS-tiled kernel)."""
     cfg = W.TINY
     x, wr = W.activations(cfg, T=T), W.router_weights(cfg)
     masters, w13, w2 = host_masters(cfg)
