@@ -169,14 +169,39 @@ constexpr int kWideRows = 128;
 // (prefill-8192 NVFP4 5.59 -> 5.52 ms, FP8 6.28 -> 6.20 ms; a threshold of 16 gave the same).
 constexpr int kFewRowsMulti = 32;
 
+// Inclusive prefix sums of three per-thread counts over the 1024 threads of a workgroup (thread i's
+// values are item i's): within each wave by shuffles, then each wave adds the totals of the waves before
+// it from LDS.  One barrier instead of one pair per doubling step.
+__device__ inline void block_scan3_1024(int& a, int& b, int& c, int (*wt)[3]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ya = __shfl_up(a, o, 64), yb = __shfl_up(b, o, 64), yc = __shfl_up(c, o, 64);
+    if (lane >= o) {
+      a += ya;
+      b += yb;
+      c += yc;
+    }
+  }
+  if (lane == 63) {
+    wt[wv][0] = a;
+    wt[wv][1] = b;
+    wt[wv][2] = c;
+  }
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) {
+    a += wt[w][0];
+    b += wt[w][1];
+    c += wt[w][2];
+  }
+}
+
 __global__ __launch_bounds__(1024) void k_perm_scan(const int* __restrict__ cnt, int64_t E, int64_t nc,
                                                     int* __restrict__ base, int* __restrict__ counts,
                                                     int* __restrict__ offsets, int4* __restrict__ tiles_s,
                                                     int* __restrict__ ntiles_s, int4* __restrict__ tiles_w,
                                                     int* __restrict__ ntiles_w, uint32_t* __restrict__ h_amax) {
-  __shared__ int s_cnt[1024];
-  __shared__ int s_ts[1024];
-  __shared__ int s_tw[1024];
+  __shared__ int wtot[16][3];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
@@ -199,29 +224,17 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int* __restrict__ cnt,
   const bool skinny = total <= kFewRowsMulti;
   const int nts = (e < E && skinny) ? (total + kRowsPerTile - 1) / kRowsPerTile : 0;
   const int ntw = (e < E && !skinny) ? (total + kWideRows - 1) / kWideRows : 0;
-  s_cnt[e] = (e < E) ? total : 0;
-  s_ts[e] = nts;
-  s_tw[e] = ntw;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int a = (e >= o) ? s_cnt[e - o] : 0;
-    const int b = (e >= o) ? s_ts[e - o] : 0;
-    const int c = (e >= o) ? s_tw[e - o] : 0;
-    __syncthreads();
-    s_cnt[e] += a;
-    s_ts[e] += b;
-    s_tw[e] += c;
-    __syncthreads();
-  }
+  int sc = (e < E) ? total : 0, st = nts, sw = ntw;
+  block_scan3_1024(sc, st, sw, wtot);
   if (e < E) {
-    const int off = s_cnt[e] - total;
+    const int off = sc - total;
     offsets[e] = off;
     if (e == E - 1) {
-      offsets[E] = s_cnt[e];
-      *ntiles_s = s_ts[e];
-      *ntiles_w = s_tw[e];
+      offsets[E] = sc;
+      *ntiles_s = st;
+      *ntiles_w = sw;
     }
-    const int ts0 = s_ts[e] - nts, tw0 = s_tw[e] - ntw;
+    const int ts0 = st - nts, tw0 = sw - ntw;
     for (int i = 0; i < nts; ++i) {
       const int r = total - i * kRowsPerTile;
       tiles_s[ts0 + i] = make_int4(e, off + i * kRowsPerTile, r < kRowsPerTile ? r : kRowsPerTile, 0);
@@ -1809,8 +1822,7 @@ __global__ __launch_bounds__(1024) void k_perm_small(const int32_t* __restrict__
                                                      uint32_t* __restrict__ h_amax) {
   __shared__ unsigned long long lm[1024];
   __shared__ int s_cnt[1024];
-  __shared__ int s_ts[1024];
-  __shared__ int s_tw[1024];
+  __shared__ int wtot[16][3];
   const int e = threadIdx.x;
   lm[e] = 0ull;
   __syncthreads();
@@ -1825,29 +1837,18 @@ __global__ __launch_bounds__(1024) void k_perm_small(const int32_t* __restrict__
   const bool skinny = total <= kSkinnyMaxRows;
   const int nts = (e < E && skinny) ? (total + kRowsPerTile - 1) / kRowsPerTile : 0;
   const int ntw = (e < E && !skinny) ? (total + kWideRows - 1) / kWideRows : 0;
-  s_cnt[e] = total;
-  s_ts[e] = nts;
-  s_tw[e] = ntw;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int a = (e >= o) ? s_cnt[e - o] : 0;
-    const int b = (e >= o) ? s_ts[e - o] : 0;
-    const int c = (e >= o) ? s_tw[e - o] : 0;
-    __syncthreads();
-    s_cnt[e] += a;
-    s_ts[e] += b;
-    s_tw[e] += c;
-    __syncthreads();
-  }
+  int sc = total, st = nts, sw = ntw;
+  block_scan3_1024(sc, st, sw, wtot);
+  s_cnt[e] = sc;  // inclusive prefix counts, read by every thread below
   if (e < E) {
-    const int off = s_cnt[e] - total;
+    const int off = sc - total;
     offsets[e] = off;
     if (e == E - 1) {
-      offsets[E] = s_cnt[e];
-      *ntiles_s = s_ts[e];
-      *ntiles_w = s_tw[e];
+      offsets[E] = sc;
+      *ntiles_s = st;
+      *ntiles_w = sw;
     }
-    const int ts0 = s_ts[e] - nts, tw0 = s_tw[e] - ntw;
+    const int ts0 = st - nts, tw0 = sw - ntw;
     for (int i = 0; i < nts; ++i) {
       const int r = total - i * kRowsPerTile;
       tiles_s[ts0 + i] = make_int4(e, off + i * kRowsPerTile, r < kRowsPerTile ? r : kRowsPerTile, 0);
